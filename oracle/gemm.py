@@ -1,0 +1,100 @@
+"""fp64 oracle of the AllGather+GEMM workload -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg use
+this module; the GPU path never imports it.
+
+Followed passages: the HyperParallel RFC, section 十 ("fused_all_gather_matmul"),
+and "Triton-distributed Semantics", section "AllGather + GEMM Overlapping": W
+row shards A_w (m_local x K) are gathered into G (W*m_local x K) with shard w at
+rows [w*m_local, (w+1)*m_local); the consumer computes C = G @ B.
+
+Reading taken: the RFC's formula line also names a ReduceScatter, but its
+example returns an (m_total, n) product, which only C = G @ B has; the oracle
+computes C = G @ B with no reduction across ranks.
+
+bf16 inputs convert exactly to float64 (every bf16 value is a float64 value),
+so ``ref`` is the exact product up to float64 summation rounding.
+"""
+from __future__ import annotations
+
+from typing import List
+
+import numpy as np
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly: bf16 is the top half of a float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bit patterns, round to nearest with ties to even, in one rounding.
+
+    bf16 carries 8 significant bits.  With x = m * 2**k and 0.5 <= |m| < 1
+    (``frexp``), the nearest bf16 value is round_half_even(m * 256) / 256 * 2**k;
+    that value is exact in float32, whose top 16 bits are then the bf16 pattern.
+    Zero maps to +/-0.  Values below bf16's normal range or beyond its largest
+    finite value are rejected rather than guessed.
+    """
+    f = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(f)):
+        raise ValueError("only finite values are supported")
+    m, k = np.frexp(f)
+    q = np.round(m * 256.0)  # numpy rounds halves to even
+    v = np.ldexp(q / 256.0, k)
+    nz = v != 0.0
+    if np.any(np.abs(v[nz]) < 2.0 ** -126) or np.any(np.abs(v) > 3.3895313892515355e38):
+        raise ValueError("value outside bf16's normal range")
+    bits32 = v.astype(np.float32).view(np.uint32)
+    if np.any(bits32 & np.uint32(0xFFFF)):
+        raise AssertionError("rounded value is not a bf16 value")
+    out = (bits32 >> np.uint32(16)).astype(np.uint16)
+    # keep the sign of zero inputs
+    zero_neg = (f == 0.0) & np.signbit(f)
+    return np.where(zero_neg, np.uint16(0x8000), out).astype(np.uint16)
+
+
+def allgather_rows(shards: List[np.ndarray]) -> np.ndarray:
+    """G = shards stacked in rank order (shard w at rows [w*m, (w+1)*m))."""
+    return np.concatenate([np.asarray(s) for s in shards], axis=0)
+
+
+def ag_gemm_ref(shards_bits: List[np.ndarray], b_bits: np.ndarray) -> np.ndarray:
+    """C = AllGather(A) @ B in float64 from bf16 bit patterns."""
+    g = bf16_bits_to_f64(allgather_rows(shards_bits))
+    b = bf16_bits_to_f64(b_bits)
+    return g @ b
+
+
+def ag_gemm_rows_ref(shards_bits: List[np.ndarray], b_bits: np.ndarray,
+                     rows: np.ndarray) -> np.ndarray:
+    """Selected rows of C (for sampled checks at full size)."""
+    m_local = shards_bits[0].shape[0]
+    a = np.stack([bf16_bits_to_f64(shards_bits[int(r) // m_local][int(r) % m_local])
+                  for r in rows])
+    return a @ bf16_bits_to_f64(b_bits)
+
+
+def rel_error(c: np.ndarray, ref: np.ndarray) -> float:
+    """max_i |c_i - ref_i| / max(|ref_i|, tau), tau = 0.01 * RMS(ref).
+
+    The floor tau keeps entries whose exact value is close to 0 from turning an
+    absolute error at the level of bf16 output rounding into an unbounded ratio.
+    """
+    c = np.asarray(c, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    tau = 0.01 * float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    denom = np.maximum(np.abs(ref), tau)
+    if denom.size == 0:
+        return 0.0
+    denom = np.where(denom == 0.0, 1.0, denom)
+    return float(np.max(np.abs(c - ref) / denom))
+
+
+def normwise_error(c: np.ndarray, ref: np.ndarray) -> float:
+    """max |c - ref| / max |ref|."""
+    c = np.asarray(c, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    m = float(np.max(np.abs(ref))) if ref.size else 0.0
+    return float(np.max(np.abs(c - ref))) / (m if m else 1.0)

@@ -1,0 +1,96 @@
+"""Pins of the fp64 AllGather+GEMM oracle and its bf16 helpers.
+
+Pinned against: fixed bit patterns of the bf16 format, torch's own float32 ->
+bf16 conversion (a library routine), hand-worked ties, a brute-force triple
+loop on tiny shapes and exact integer products.
+"""
+import numpy as np
+import torch
+
+import oracle
+from oracle import gemm
+
+
+def test_bf16_decode_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x4049, 0x7F7F, 0x0080, 0x3C00],
+                    dtype=np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, 3.140625, 3.3895313892515355e38, 2.0 ** -126, 2.0 ** -7]
+    got = gemm.bf16_bits_to_f64(bits)
+    np.testing.assert_array_equal(got, np.array(want))
+    assert np.signbit(got[3])
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 2**16, size=10000, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # finite patterns
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64)
+    np.testing.assert_array_equal(gemm.bf16_bits_to_f64(bits), t.numpy())
+
+
+def test_rne_matches_torch_on_float32_values():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(gemm.f64_to_bf16_rne_bits(x.astype(np.float64)), ref)
+
+
+def test_rne_ties_and_single_rounding():
+    # 1 + 2**-8 is halfway between 1 and 1 + 2**-7: ties to even -> 1.0 (0x3F80)
+    # 1 + 3 * 2**-8 is halfway between 1 + 2**-7 and 1 + 2**-6: -> 1 + 2**-6 (0x3F82)
+    # 1 + 2**-8 + 2**-40 is above the tie -> 1 + 2**-7 (0x3F81); rounding through
+    # float32 first would land exactly on the tie and give 1.0 instead.
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, -0.0, 0.0, 7168.0])
+    np.testing.assert_array_equal(gemm.f64_to_bf16_rne_bits(x),
+                                  np.array([0x3F80, 0x3F82, 0x3F81, 0x8000, 0x0000, 0x45E0],
+                                           dtype=np.uint16))
+
+
+def test_gemm_matches_bruteforce_triple_loop():
+    rng = np.random.default_rng(2)
+    W, m, K, N = 3, 2, 5, 4
+    shards = [rng.integers(0, 2**16, size=(m, K), dtype=np.uint16) & 0xBFFF for _ in range(W)]
+    b = rng.integers(0, 2**16, size=(K, N), dtype=np.uint16) & 0xBFFF
+    ref = gemm.ag_gemm_ref(shards, b)
+    for w in range(W):
+        for i in range(m):
+            for n in range(N):
+                acc = 0.0
+                for k in range(K):
+                    a_val = float(gemm.bf16_bits_to_f64(shards[w][i:i + 1, k])[0])
+                    b_val = float(gemm.bf16_bits_to_f64(b[k:k + 1, n])[0])
+                    acc += a_val * b_val
+                assert abs(ref[w * m + i, n] - acc) <= 1e-12 * max(1.0, abs(acc))
+
+
+def test_gemm_integer_inputs_exact():
+    rng = np.random.default_rng(3)
+    W, m, K, N = 4, 3, 64, 5
+    ai = [rng.integers(-1, 2, size=(m, K)) for _ in range(W)]
+    bi = rng.integers(-1, 2, size=(K, N))
+    to_bits = lambda a: gemm.f64_to_bf16_rne_bits(a.astype(np.float64))
+    ref = gemm.ag_gemm_ref([to_bits(a) for a in ai], to_bits(bi))
+    np.testing.assert_array_equal(ref, (np.concatenate(ai) @ bi).astype(np.float64))
+
+
+def test_rows_ref_matches_full():
+    rng = np.random.default_rng(4)
+    shards = [rng.integers(0, 2**16, size=(4, 6), dtype=np.uint16) & 0xBFFF for _ in range(3)]
+    b = rng.integers(0, 2**16, size=(6, 5), dtype=np.uint16) & 0xBFFF
+    full = gemm.ag_gemm_ref(shards, b)
+    rows = np.array([0, 5, 11, 7])
+    np.testing.assert_array_equal(gemm.ag_gemm_rows_ref(shards, b, rows), full[rows])
+
+
+def test_rel_error_definition():
+    ref = np.array([1.0, -2.0, 0.0, 4.0])
+    tau = 0.01 * np.sqrt((1 + 4 + 0 + 16) / 4)
+    c = ref + np.array([0.01, 0.0, 0.001, 0.0])
+    assert abs(gemm.rel_error(c, ref) - max(0.01, 0.001 / tau)) < 1e-15
+    assert gemm.rel_error(ref, ref) == 0.0
+    assert abs(gemm.normwise_error(c, ref) - 0.01 / 4.0) < 1e-15
+
+
+def test_allgather_rows_is_oracle_allgather():
+    shards = [np.arange(12, dtype=np.uint16).reshape(3, 4) + 100 * w for w in range(4)]
+    np.testing.assert_array_equal(gemm.allgather_rows(shards), oracle.allgather(shards))

@@ -1,0 +1,101 @@
+"""Pins of the signal-protocol model: exhaustive interleavings, seeded schedules,
+closed-form final states, and negative controls that each turn one rule off.
+
+The negative controls are the failure modes the pages warn about: a launch
+without the host's signal reset ("Host Side Modifications"), a signal issued
+before the data is fenced (fence-before-signal in the RFC's put_with_signal),
+a producer that reuses a ring slot without waiting for the hand-back, and a
+producer piece that never arrives.
+"""
+import pytest
+
+import oracle
+from oracle.protocol import ADD, SET, ProtocolSpec, explore_all, run_random
+
+
+def ok_spec(protocol, **kw):
+    base = dict(W=2, nbs=3, nstreams=1, R=1, protocol=protocol, n_producers=2, n_consumers=2)
+    base.update(kw)
+    return ProtocolSpec(**base)
+
+
+@pytest.mark.parametrize("protocol", [ADD, SET])
+def test_exhaustive_no_violation_no_deadlock(protocol):
+    spec = ok_spec(protocol, nbs=2)
+    states, violations, deadlock = explore_all(spec)
+    assert states > 100
+    assert violations == []
+    assert not deadlock
+
+
+@pytest.mark.parametrize("protocol", [ADD, SET])
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_seeded_schedules_match_closed_forms(protocol, R):
+    spec = ok_spec(protocol, W=3, nbs=5, nstreams=2, R=R, n_producers=3, n_consumers=2)
+    want_sig = oracle.protocol.expected_final_signals(spec)
+    want_cred = oracle.protocol.expected_final_credits(spec)
+    for seed in range(200):
+        out = run_random(spec, seed)
+        assert out.completed and out.violations == []
+        assert out.signals == want_sig
+        assert out.credits == want_cred
+        assert all(v == k[2] for k, v in out.out.items())
+
+
+def test_closed_form_counts():
+    spec = ok_spec(ADD, W=8, nbs=8, nstreams=16, R=2)
+    sig = oracle.protocol.expected_final_signals(spec)
+    assert len(sig) == 8 * 8 * 16 and set(sig.values()) == {8}
+    spec = ok_spec(SET, W=2, nbs=1, nstreams=1, R=1)
+    sig = oracle.protocol.expected_final_signals(spec)
+    assert len(sig) == 4 and set(sig.values()) == {1}
+    cred = oracle.protocol.expected_final_credits(ok_spec(ADD, nbs=5, R=2))
+    assert sorted(set(cred.values())) == [2, 3]
+
+
+@pytest.mark.parametrize("protocol", [ADD, SET])
+def test_negative_skip_reset(protocol):
+    out = run_random(ok_spec(protocol, skip_reset=True), seed=0)
+    assert out.violations, "stale signals must let a consumer read unwritten data"
+
+
+@pytest.mark.parametrize("protocol", [ADD, SET])
+def test_negative_signal_before_fence(protocol):
+    _, violations, _ = explore_all(ok_spec(protocol, nbs=1, signal_before_fence=True))
+    assert any("read block" in v for v in violations)
+
+
+@pytest.mark.parametrize("protocol", [ADD, SET])
+def test_negative_skip_credit_wait(protocol):
+    _, violations, _ = explore_all(ok_spec(protocol, nbs=2, R=1, skip_credit_wait=True))
+    assert any("overwrite" in v or "read block" in v for v in violations)
+
+
+@pytest.mark.parametrize("protocol", [ADD, SET])
+def test_negative_missing_piece_times_out(protocol):
+    out = run_random(ok_spec(protocol, drop_piece=(1, 0, 1, 0)), seed=3)
+    assert not out.completed
+
+
+def test_signal_ops_and_predicates():
+    assert oracle.signal_apply(5, 1, "set") == 1
+    assert oracle.signal_apply(5, 3, "add") == 8
+    assert oracle.signal_apply(2**64 - 1, 1, "add") == 0
+    table = {"eq": (False, True, False), "ne": (True, False, True), "gt": (False, False, True),
+             "ge": (False, True, True), "lt": (True, False, False), "le": (True, True, False)}
+    for op, want in table.items():
+        assert tuple(oracle.compare(v, 4, op) for v in (3, 4, 5)) == want
+
+
+def test_symm_at():
+    base, stride, world = 1 << 40, 1 << 21, 4
+    p = base + 1234
+    assert oracle.symm_at(base, stride, world, p, 0) == p
+    assert oracle.symm_at(base, stride, world, p, 3) == p + 3 * stride
+    q = oracle.symm_at(base, stride, world, p, 2)
+    assert oracle.symm_at(base, stride, world, q, 1) == p + stride
+    assert oracle.symm_at(base, stride, world, q, 2) == q
+    assert oracle.symm_at(base, stride, world, p, 4) is None
+    assert oracle.symm_at(base, stride, world, p, -1) is None
+    assert oracle.symm_at(base, stride, world, base + world * stride, 0) is None
+    assert oracle.symm_at(base, stride, world, base - 1, 0) is None
