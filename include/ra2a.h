@@ -1,0 +1,297 @@
+/*
+ * ra2a -- Reverse All2All (EP-MoE combine) over a symmetric heap, MI355X (gfx950).
+ *
+ * C ABI of libra2a.so.  Plain pointers and sizes only; every call returns an int
+ * status (RA2A_OK or a negative RA2A_E* code) unless stated otherwise, and no C++
+ * exception crosses this boundary.  ra2a_last_error() returns a thread-local
+ * message describing the most recent failure on the calling thread.
+ *
+ * Simulated ranks.  W ranks live on one GPU as W equal slices of one device
+ * allocation (the symmetric heap).  Slice r is rank r's heap; a buffer has the
+ * same offset inside every slice, so rank r's copy of a buffer whose slice-0
+ * address is p is p + r * stride.  "Remote" stores are stores into another
+ * slice of the same HBM.
+ *
+ * Streams.  `stream` arguments are hipStream_t values passed as void*; NULL is
+ * the default stream.  Calls that take a stream only enqueue work: errors found
+ * before enqueueing are returned at once, asynchronous device-side errors (a
+ * bounded wait that timed out) are reported by ra2a_check().
+ *
+ * Device pointers.  Unless stated otherwise pointers are device addresses inside
+ * one heap created by ra2a_symm_heap_create (found by address; no handle is
+ * passed to the combine).  The library never frees memory it did not allocate.
+ */
+#ifndef RA2A_H_
+#define RA2A_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+#define RA2A_OK 0
+#define RA2A_EINVAL (-1)       /* bad argument (range, alignment, overlap, heap) */
+#define RA2A_ENOMEM (-2)       /* heap slice or device memory exhausted */
+#define RA2A_EHIP (-3)         /* a HIP runtime call failed (message has the HIP error) */
+#define RA2A_ETIMEOUT (-4)     /* a bounded device-side wait gave up */
+#define RA2A_EUNSUPPORTED (-5) /* combination not implemented */
+
+/* ---- signal operations ----------------------------------------------------
+ * "Distributed Architecture Design", section 2.3 (SignalOp SET / ADD) and the
+ * HyperParallel RFC, section 四 (shmem_signal_op).  The two pages number them
+ * differently (1/2 versus 0/1); the ABI uses these names, with SET = 0.       */
+#define RA2A_SIG_SET 0 /* signal := value */
+#define RA2A_SIG_ADD 1 /* signal += value (64-bit, wrapping) */
+
+/* ---- wait predicates ------------------------------------------------------
+ * "Distributed Architecture Design", section 6.3: eq, ne, gt, ge, lt, le
+ * (unsigned 64-bit comparison of the signal against the value).             */
+#define RA2A_CMP_EQ 0
+#define RA2A_CMP_NE 1
+#define RA2A_CMP_GT 2
+#define RA2A_CMP_GE 3
+#define RA2A_CMP_LT 4
+#define RA2A_CMP_LE 5
+
+/* ---- element types: the combine copies raw elements, only the size matters */
+#define RA2A_U8 0   /* 1 byte  */
+#define RA2A_BF16 1 /* 2 bytes */
+#define RA2A_F16 2  /* 2 bytes */
+#define RA2A_I32 3  /* 4 bytes */
+#define RA2A_F32 4  /* 4 bytes */
+#define RA2A_I64 5  /* 8 bytes */
+#define RA2A_F64 6  /* 8 bytes */
+
+/* One signal per 128-byte L2 line, so concurrent updates of neighbouring
+ * signals never share a line ("Wait/Notify Optimization": one cache line per
+ * signal slot; 128 B is gfx950's L2 line).  A signal array of n slots spans
+ * n * RA2A_SIG_STRIDE_BYTES bytes; slot i is the uint64_t at byte
+ * i * RA2A_SIG_STRIDE_BYTES.                                                   */
+#define RA2A_SIG_STRIDE_BYTES 128
+#define RA2A_SIG_STRIDE_U64 16
+
+typedef struct ra2a_heap ra2a_heap_t;
+
+/* ======================================================================== *
+ * Symmetric heap ("Distributed Architecture Design", sections 5.1-5.3;      *
+ * HyperParallel RFC, section 二).                                           *
+ * ======================================================================== */
+
+/* Create a heap of `world` slices of at least `slice_bytes` bytes each (the
+ * slice stride is slice_bytes rounded up to 2 MiB) with one hipMalloc on the
+ * current device.  The heap owns the memory; ra2a_symm_heap_destroy frees it.
+ * Errors: EINVAL (world < 1 or > 4096, slice_bytes == 0, out == NULL), ENOMEM,
+ * EHIP.                                                                        */
+int ra2a_symm_heap_create(int world, size_t slice_bytes, ra2a_heap_t **out);
+
+/* Adopt caller-owned device memory as a heap: `world` slices of `stride` bytes
+ * starting at `base` (base and stride multiples of 256).  The caller keeps
+ * ownership and must keep the memory alive until ra2a_symm_heap_destroy, which
+ * then only unregisters the heap.  Errors: EINVAL (alignment, NULL, world out
+ * of range, range overlapping a live heap), EHIP.                              */
+int ra2a_symm_heap_attach(void *base, int world, size_t stride, ra2a_heap_t **out);
+
+/* Free a heap and everything allocated from it (an attached heap's memory is
+ * left to its owner).  Waits for the device first.  Passing NULL is a no-op
+ * returning RA2A_OK.                                                            */
+int ra2a_symm_heap_destroy(ra2a_heap_t *heap);
+
+/* Symmetric allocation: reserve `bytes` at the same offset in every slice
+ * (bump allocator; `align` a power of two, 0 = 256).  The same-size,
+ * same-order rule of collective allocation holds trivially.  Returns the
+ * offset from the start of a slice.  Memory is not initialised.
+ * Errors: EINVAL, ENOMEM (slice exhausted).                                     */
+int ra2a_symm_malloc(ra2a_heap_t *heap, size_t bytes, size_t align, size_t *sym_offset);
+
+/* Base address, slice stride (bytes) and world size; any output may be NULL. */
+int ra2a_symm_heap_info(const ra2a_heap_t *heap, void **base, size_t *stride, int *world);
+
+/* The heap containing device address `ptr`, or NULL. */
+ra2a_heap_t *ra2a_symm_heap_find(const void *ptr);
+
+/* symm_at ("Distributed Architecture Design", section 5.3): the address of
+ * ptr's twin in rank `rank`'s slice, base + rank*stride + ((ptr - base) mod
+ * stride).  Pure host arithmetic, no device access.  Returns NULL if ptr is
+ * outside the heap or rank is outside [0, world).                              */
+void *ra2a_symm_at(const ra2a_heap_t *heap, const void *ptr, int rank);
+
+/* Timeout of every bounded device-side wait issued for this heap, in
+ * microseconds (default 5,000,000).  0 restores the default.                   */
+int ra2a_symm_heap_set_spin_timeout(ra2a_heap_t *heap, uint64_t timeout_us);
+
+/* ======================================================================== *
+ * One-sided primitives (HyperParallel RFC, sections 四 and 六; push mode,  *
+ * section 5.1).                                                             *
+ * ======================================================================== */
+
+/* put_with_signal: copy `bytes` from `src` (any device memory) to
+ * symm_at(dst_sym, target_rank), make the data visible device-wide, then apply
+ * `sig_op` with `value` to symm_at(sig_sym, target_rank).  The signal is never
+ * updated before the copy is complete and visible (fence before signal).
+ * Asynchronous on `stream`.  dst_sym and sig_sym must lie in `heap`, sig_sym
+ * 8-byte aligned; the destination range must not cross the end of the slice
+ * and must not overlap src.  bytes may be 0 (signal only).
+ * Errors: EINVAL, EHIP.                                                         */
+int ra2a_put_with_signal(const ra2a_heap_t *heap, void *dst_sym, const void *src, size_t bytes,
+                         uint64_t *sig_sym, uint64_t value, int sig_op, int target_rank,
+                         void *stream);
+
+/* put: the data part of put_with_signal alone (no signal).  Same rules.        */
+int ra2a_put(const ra2a_heap_t *heap, void *dst_sym, const void *src, size_t bytes,
+             int target_rank, void *stream);
+
+/* get: the pull direction ("Push 模式与 Pull 模式", section 5.2; shmem_get in
+ * section 四): copy `bytes` from symm_at(src_sym, source_rank) to `dst` (any
+ * device memory).  Same range and overlap rules as put.                        */
+int ra2a_get(const ra2a_heap_t *heap, void *dst, const void *src_sym, size_t bytes,
+             int source_rank, void *stream);
+
+/* signal_op: `sig_op` with `value` on symm_at(sig_sym, target_rank), ordered
+ * after all earlier work on `stream`.  Errors: EINVAL, EHIP.                    */
+int ra2a_signal_op(const ra2a_heap_t *heap, uint64_t *sig_sym, uint64_t value, int sig_op,
+                   int target_rank, void *stream);
+
+/* wait_for_signal: block `stream` until (*sig  cmp_op  cmp_value) holds
+ * (acquire: device memory written before the matching signal is visible to
+ * work enqueued after the wait).  Non-consuming: the signal is not modified,
+ * so several waiters on one slot are safe.  Bounded: after the heap's spin
+ * timeout the wait gives up, the heap's error word is set and the stream
+ * continues; ra2a_check() then returns ETIMEOUT.  sig must lie in `heap`.
+ * Errors: EINVAL, EHIP.                                                         */
+int ra2a_wait_signal(const ra2a_heap_t *heap, const uint64_t *sig, uint64_t cmp_value,
+                     int cmp_op, void *stream);
+
+/* Zero `n_slots` signal slots (RA2A_SIG_STRIDE_BYTES apart) starting at
+ * symm_at(sig_sym, r) for every rank r of the heap (the host-side reset before
+ * a launch, "Reverse All2All (EP MoE Distributed Kernel)", "Host Side
+ * Modifications").  Uses a kernel, not a memset node.  Errors: EINVAL, EHIP.    */
+int ra2a_signal_reset(const ra2a_heap_t *heap, uint64_t *sig_sym, int64_t n_slots,
+                      void *stream);
+
+/* ======================================================================== *
+ * Reverse All2All ("Reverse All2All (EP MoE Distributed Kernel)").          *
+ *                                                                           *
+ * For W ranks, rank r's input in_r has shape (S*W, H, D) and rank j's output *
+ * out_j has shape (S, H*W, D), both row-major, elements of the size fixed   *
+ * by `dtype`:                                                                *
+ *                                                                           *
+ *     out_j[s, r*H + h, d] = in_r[j*S + s, h, d]                            *
+ *                                                                           *
+ * (section "Reverse All2All Operator Semantics"; column r*H + h and row      *
+ * j*S + s as in the MTE listing).  `in`, `out` and `signals` are addresses   *
+ * inside one heap with world == W; rank r's buffers are their twins in slice *
+ * r.  Elements are moved as raw bytes, so the result is bit-exact for every  *
+ * type (NaN payloads, -0.0 and subnormals included).  in and out must not    *
+ * overlap in any slice; each of in/out must fit inside its slice.           *
+ * ======================================================================== */
+
+/* Signalling protocols of the pipelined combine (ra2a_opts_t.protocol). */
+#define RA2A_PROTO_ADD 1 /* push mode: W adds per tile, wait for W (default) */
+#define RA2A_PROTO_SET 2 /* one SET per (source, tile) piece, wait for 1 */
+
+/* Tiling and protocol of the signal-pipelined kernel (0 / -1 = default). */
+typedef struct ra2a_opts {
+    int64_t tile_s;     /* tokens per tile (default min(S, 64)) */
+    int64_t tile_h;     /* heads per tile (default 1) */
+    int64_t tile_d;     /* elements of D per tile (default D) */
+    int32_t protocol;   /* RA2A_PROTO_ADD (or 0, the default): one signal per tile (j,
+                         * s-block, head block, d block), each of the W sources adds 1, the
+                         * consumer waits for W.  RA2A_PROTO_SET: one signal per piece
+                         * (source r, tile), set to 1; the consumer waits for each piece. */
+    int32_t ring;       /* staging ring depth in S-blocks (default 2; >= number of
+                         * S-blocks means no slot is reused) */
+    int32_t wg_per_cu;  /* persistent workgroups per compute unit (default 2) */
+    int32_t producer_share; /* producers per 4 workgroups of a group, 1..3 (default 2) */
+    int32_t straggler_rank;   /* source slice whose producers are delayed, -1 = none */
+    uint32_t straggler_delay; /* busy-loop base n0: each delayed piece spins n0 + u
+                               * iterations, u uniform in [0, n0] from SplitMix64 */
+    uint64_t straggler_seed;  /* seed of that SplitMix64 sequence */
+    uint64_t *timestamps;     /* optional device array: per destination slice j, the
+                               * device real-time clock at which each consumer unit
+                               * finished, at timestamps[j * units + unit] */
+    int32_t consumer_lds;     /* 1: consumers copy through LDS; 0: through registers;
+                               * -1 or 0 in a zeroed struct: default */
+    int32_t consumer_split;   /* consumer workgroups sharing one unit, each copying a
+                               * contiguous part of it (default: about one per 128 KiB) */
+    int32_t producer_batch;   /* pieces a producer copies between two release fences
+                               * (default: about 64 KiB worth, at most 16) */
+    int32_t skip_reset;       /* 1: the caller has already zeroed both signal regions
+                               * (ra2a_signal_reset on the same stream); no reset launch */
+    int32_t reserved[2];      /* must be zero */
+} ra2a_opts_t;
+
+/* Number of signal slots the combine needs per slice: `tile_slots` data
+ * signals (region A: ADD, one per (s-block, head block, d block) in that
+ * order; SET, one per (s-block, head block, d block, source r)) followed by
+ * `credit_slots` ring hand-back counters (region B: ADD [ring][head block]
+ * [d block]; SET [ring][head block][d block][source]).  The `signals` array
+ * of a combine must hold tile_slots + credit_slots slots in every slice.
+ * opts may be NULL.                                                             */
+int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t D, int dtype,
+                                  const ra2a_opts_t *opts, int64_t *tile_slots,
+                                  int64_t *credit_slots);
+
+/* Staging bytes per slice the library reserves from the heap on first use
+ * (pipelined: the ring; two_phase != 0: a full (W, S, H, D) staging area).     */
+int ra2a_rev_all2all_workspace_bytes(int W, int64_t S, int64_t H, int64_t D, int dtype,
+                                     const ra2a_opts_t *opts, int two_phase, size_t *bytes);
+
+/* The combine with the signal-pipelined persistent kernel and default tiling:
+ * enqueues the reset of both signal regions, then one persistent launch whose
+ * producer workgroups copy pieces into the destination's staging ring with
+ * 16-byte stores, fence, and signal; consumer workgroups wait on their tile's
+ * signal, copy staging to out_j and hand the ring slot back.  Afterwards every
+ * region-A slot holds W (ADD) or 1 (SET) and every region-B slot the number of
+ * S-blocks that used it.  Staging comes from the heap (see workspace_bytes).
+ * Errors: EINVAL, ENOMEM (heap too small for the staging ring), EHIP.           */
+int ra2a_rev_all2all(const void *in, void *out, uint64_t *signals, int W, int64_t S, int64_t H,
+                     int64_t D, int dtype, void *stream);
+
+/* Same, with explicit tiling / protocol / straggler options (opts may be NULL). */
+int ra2a_rev_all2all_ex(const void *in, void *out, uint64_t *signals, int W, int64_t S,
+                        int64_t H, int64_t D, int dtype, const ra2a_opts_t *opts, void *stream);
+
+/* The two-phase variant ("UDMA Optimized Implementation": "Two-Phase Data
+ * Copy"): phase 1 copies every contiguous (S, H, D) segment in_r[j*S, (j+1)*S)
+ * into slot r of rank j's full-size staging area; stream order between the two
+ * launches is the barrier; phase 2 reorders staging into out_j.  `signals` is
+ * not used and may be NULL.  Errors: EINVAL, ENOMEM, EHIP.                      */
+int ra2a_rev_all2all_two_phase(const void *in, void *out, uint64_t *signals, int W, int64_t S,
+                               int64_t H, int64_t D, int dtype, void *stream);
+
+/* ---- diagnostics --------------------------------------------------------- */
+
+/* Wait for the device, then report and clear the heap's device error word:
+ * RA2A_ETIMEOUT if a bounded wait gave up since the last check, RA2A_EHIP if
+ * the device reported an error, else RA2A_OK.                                  */
+int ra2a_check(const ra2a_heap_t *heap);
+
+/* Host emulation of the signal-pipelined combine (no GPU needed): runs the
+ * kernel's own piece / work-item address arithmetic and launch partition for a
+ * device of `num_cus` compute units with `blocks_per_cu` resident workgroups,
+ * moving bytes between host copies of the heap in an order every wait of the
+ * protocol allows.  in[r] (rank r's input) and out[j] are host arrays of
+ * S*W*H*D elements; signals[j] (optional, may be NULL) receives the final
+ * tile_slots + credit_slots signal values of slice j (unstrided).  Returns
+ * EINVAL with a message if any access would leave its buffer, if the roles or
+ * work lists do not partition the work, or if a wait could not be satisfied.
+ * For checking the index arithmetic on a host; it is not a CPU fallback.      */
+int ra2a_debug_emulate_pipelined(const void *const *in, void *const *out,
+                                 uint64_t *const *signals, int W, int64_t S, int64_t H,
+                                 int64_t D, int dtype, const ra2a_opts_t *opts, int num_cus,
+                                 int blocks_per_cu);
+
+/* Message for the most recent failure on this thread ("" if none). */
+const char *ra2a_last_error(void);
+
+/* ABI version (major * 10000 + minor * 100 + patch). */
+int ra2a_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA2A_H_ */

@@ -1,0 +1,882 @@
+// C ABI of libra2a: symmetric heap, one-sided primitives and the Reverse All2All
+// combine (declarations and contracts in include/ra2a.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "combine_geom.h"
+#include "common.h"
+#include "launch.h"
+#include "ra2a.h"
+
+#define RA2A_API extern "C" __attribute__((visibility("default")))
+
+struct ra2a_heap {
+    int world = 0;
+    size_t stride = 0;
+    uint8_t* base = nullptr;
+    int device = 0;
+    size_t bump = 0;               // next free symmetric offset
+    uint32_t* err = nullptr;       // device error word (library-owned, outside the heap)
+    uint64_t timeout_us = 0;       // 0 = default
+    bool owned = true;             // false: attached caller memory
+    size_t ring_off = 0, ring_bytes = 0;   // cached staging ring (pipelined combine)
+    size_t full_off = 0, full_bytes = 0;   // cached full staging (two-phase combine)
+    std::mutex mu;
+};
+
+namespace {
+
+constexpr size_t kSliceAlign = size_t(2) << 20;
+constexpr uint64_t kDefaultTimeoutUs = 5000000ull;
+thread_local std::string g_err;
+std::mutex g_reg_mu;
+std::vector<ra2a_heap*> g_heaps;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(RA2A_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+int ok() {
+    return RA2A_OK;
+}
+
+int elem_bytes(int dtype) {
+    switch (dtype) {
+        case RA2A_U8: return 1;
+        case RA2A_BF16:
+        case RA2A_F16: return 2;
+        case RA2A_I32:
+        case RA2A_F32: return 4;
+        case RA2A_I64:
+        case RA2A_F64: return 8;
+        default: return 0;
+    }
+}
+
+ra2a_heap* find_heap(const void* p) {
+    const uint8_t* q = static_cast<const uint8_t*>(p);
+    std::lock_guard<std::mutex> g(g_reg_mu);
+    for (ra2a_heap* h : g_heaps)
+        if (q >= h->base && q < h->base + h->stride * (size_t)h->world) return h;
+    return nullptr;
+}
+
+bool in_heap(const ra2a_heap* h, const void* p) {
+    const uint8_t* q = static_cast<const uint8_t*>(p);
+    return h && q >= h->base && q < h->base + h->stride * (size_t)h->world;
+}
+
+size_t sym_offset(const ra2a_heap* h, const void* p) {
+    return (size_t)(static_cast<const uint8_t*>(p) - h->base) % h->stride;
+}
+
+uint64_t timeout_ticks(const ra2a_heap* h) {
+    int khz = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz <= 0)
+        khz = 100000;  // gfx9 real-time clock: 100 MHz
+    const uint64_t us = h->timeout_us ? h->timeout_us : kDefaultTimeoutUs;
+    return us * (uint64_t)khz / 1000ull;
+}
+
+// The device error word of a heap, allocated on first use (so that a heap can
+// be attached and validated on a host without a GPU).
+int ensure_err(ra2a_heap* h) {
+    std::lock_guard<std::mutex> g(h->mu);
+    if (h->err) return RA2A_OK;
+    void* ew = nullptr;
+    hipError_t e = hipMalloc(&ew, 256);
+    if (e == hipSuccess) e = hipMemset(ew, 0, 256);
+    if (e != hipSuccess) {
+        if (ew) (void)hipFree(ew);
+        (void)hipGetLastError();
+        return hip_fail(e, "error word allocation");
+    }
+    h->err = static_cast<uint32_t*>(ew);
+    return RA2A_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int lowbit_vec(uint64_t m) {
+    if ((m & 15u) == 0) return 16;
+    if ((m & 7u) == 0) return 8;
+    if ((m & 3u) == 0) return 4;
+    if ((m & 1u) == 0) return 2;
+    return 1;
+}
+
+// Resolved tiling of one pipelined combine.
+struct Plan {
+    int64_t BS, TH, TD;
+    int nbs, nhb, ndb, R;
+    int protocol;
+    int64_t regionA, regionB;
+    int64_t ring_bytes;     // staging ring bytes per slice
+    int csplit, pbatch, wg_per_cu, pshare;
+    int64_t piece_bytes, unit_bytes;
+};
+
+int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* o, Plan* p) {
+    ra2a_opts_t z;
+    std::memset(&z, 0, sizeof z);
+    z.straggler_rank = -1;
+    if (!o) o = &z;
+    for (int i = 0; i < 2; ++i)
+        if (o->reserved[i]) return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
+    p->BS = o->tile_s > 0 ? o->tile_s : std::min<int64_t>(S, 64);
+    p->TH = o->tile_h > 0 ? o->tile_h : 1;
+    p->TD = o->tile_d > 0 ? o->tile_d : D;
+    if (o->tile_s < 0 || o->tile_h < 0 || o->tile_d < 0)
+        return fail(RA2A_EINVAL, "negative tile size");
+    p->BS = std::min(p->BS, std::max<int64_t>(S, 1));
+    p->TH = std::min(p->TH, H);
+    p->TD = std::min(p->TD, D);
+    if (o->protocol != 0 && o->protocol != RA2A_PROTO_ADD && o->protocol != RA2A_PROTO_SET)
+        return fail(RA2A_EINVAL, "protocol must be 0, RA2A_PROTO_ADD or RA2A_PROTO_SET");
+    p->protocol = o->protocol == RA2A_PROTO_SET ? RA2A_SIG_SET : RA2A_SIG_ADD;
+    p->nbs = (int)cdiv(S, p->BS);
+    p->nhb = (int)cdiv(H, p->TH);
+    p->ndb = (int)cdiv(D, p->TD);
+    if (o->ring < 0) return fail(RA2A_EINVAL, "ring depth must be >= 0");
+    int R = o->ring > 0 ? o->ring : 2;
+    p->R = std::max(1, std::min(R, std::max(p->nbs, 1)));
+    const int64_t perW = p->protocol == RA2A_SIG_SET ? W : 1;
+    p->regionA = (int64_t)p->nbs * p->nhb * p->ndb * perW;
+    p->regionB = (int64_t)p->R * p->nhb * p->ndb * perW;
+    p->ring_bytes = (int64_t)p->R * p->BS * H * W * D * e;
+    p->piece_bytes = p->BS * p->TH * p->TD * e;
+    p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);
+    if (o->consumer_split < 0 || o->producer_batch < 0 || o->wg_per_cu < 0 ||
+        o->producer_share < 0)
+        return fail(RA2A_EINVAL, "negative option");
+    p->csplit = o->consumer_split > 0
+                    ? o->consumer_split
+                    : (int)std::max<int64_t>(1, std::min<int64_t>(64, p->unit_bytes / (128 << 10)));
+    p->pbatch = o->producer_batch > 0
+                    ? o->producer_batch
+                    : (int)std::max<int64_t>(1, std::min<int64_t>(16, (64 << 10) / std::max<int64_t>(p->piece_bytes, 1)));
+    if (p->pbatch > ra2a::kThreads) return fail(RA2A_EINVAL, "producer_batch must be <= 256");
+    p->wg_per_cu = o->wg_per_cu > 0 ? o->wg_per_cu : 2;
+    p->pshare = o->producer_share > 0 ? o->producer_share : 2;
+    if (p->pshare > 3) return fail(RA2A_EINVAL, "producer_share must be 1..3");
+    // per-launch index arithmetic uses 32-bit vector counts inside one unit
+    if (p->unit_bytes >= (int64_t(1) << 31) - 65536) return fail(RA2A_EINVAL, "tile too large");
+    return RA2A_OK;
+}
+
+struct Checked {
+    ra2a_heap* h;
+    int e;
+    int64_t n_bytes;  // per-slice bytes of in and of out
+    size_t in_off, out_off, sig_off;
+};
+
+// Common validation of the combine's pointers and sizes.
+int check_combine(const void* in, const void* out, const void* signals, int W, int64_t S,
+                  int64_t H, int64_t D, int dtype, int64_t sig_slots, Checked* c) {
+    c->e = elem_bytes(dtype);
+    if (!c->e) return fail(RA2A_EINVAL, "unknown dtype %d", dtype);
+    if (W < 1) return fail(RA2A_EINVAL, "W must be >= 1");
+    if (S < 0 || H < 0 || D < 0) return fail(RA2A_EINVAL, "negative dimension");
+    if (!in || !out) return fail(RA2A_EINVAL, "in and out must be non-NULL");
+    c->h = find_heap(in);
+    if (!c->h) return fail(RA2A_EINVAL, "in is not inside a symmetric heap");
+    if (c->h->world != W)
+        return fail(RA2A_EINVAL, "W=%d but the heap has %d slices", W, c->h->world);
+    if (!in_heap(c->h, out)) return fail(RA2A_EINVAL, "out is not inside the heap of in");
+    const double nb = (double)S * (double)W * (double)H * (double)D * (double)c->e;
+    if (nb > 9.0e18) return fail(RA2A_EINVAL, "size overflow");
+    c->n_bytes = S * (int64_t)W * H * D * c->e;
+    c->in_off = sym_offset(c->h, in);
+    c->out_off = sym_offset(c->h, out);
+    if (c->in_off + (size_t)c->n_bytes > c->h->stride)
+        return fail(RA2A_EINVAL, "in crosses the end of its slice");
+    if (c->out_off + (size_t)c->n_bytes > c->h->stride)
+        return fail(RA2A_EINVAL, "out crosses the end of its slice");
+    if (c->n_bytes > 0 && c->in_off < c->out_off + (size_t)c->n_bytes &&
+        c->out_off < c->in_off + (size_t)c->n_bytes)
+        return fail(RA2A_EINVAL, "in and out overlap");
+    if (sig_slots > 0) {
+        if (!signals) return fail(RA2A_EINVAL, "signals must be non-NULL");
+        if (!in_heap(c->h, signals)) return fail(RA2A_EINVAL, "signals not inside the heap of in");
+        c->sig_off = sym_offset(c->h, signals);
+        if (c->sig_off % 8) return fail(RA2A_EINVAL, "signals must be 8-byte aligned");
+        const size_t sb = (size_t)sig_slots * RA2A_SIG_STRIDE_BYTES;
+        if (c->sig_off + sb > c->h->stride)
+            return fail(RA2A_EINVAL, "signals (%lld slots) cross the end of the slice",
+                        (long long)sig_slots);
+        if (c->n_bytes > 0 &&
+            ((c->sig_off < c->in_off + (size_t)c->n_bytes && c->in_off < c->sig_off + sb) ||
+             (c->sig_off < c->out_off + (size_t)c->n_bytes && c->out_off < c->sig_off + sb)))
+            return fail(RA2A_EINVAL, "signals overlap in or out");
+    }
+    return RA2A_OK;
+}
+
+// Bump allocation under the heap's lock.
+int heap_alloc(ra2a_heap* h, size_t bytes, size_t align, size_t* off) {
+    if (align == 0) align = 256;
+    if (align & (align - 1)) return fail(RA2A_EINVAL, "align must be a power of two");
+    const size_t start = (h->bump + align - 1) & ~(align - 1);
+    if (start > h->stride || bytes > h->stride - start)
+        return fail(RA2A_ENOMEM, "symmetric heap slice exhausted: need %zu bytes at offset %zu of %zu",
+                    bytes, start, h->stride);
+    h->bump = start + bytes;
+    *off = start;
+    return RA2A_OK;
+}
+
+// Staging area of at least `bytes` per slice, cached per heap.
+int staging(ra2a_heap* h, bool full, size_t bytes, size_t* off) {
+    std::lock_guard<std::mutex> g(h->mu);
+    size_t& co = full ? h->full_off : h->ring_off;
+    size_t& cb = full ? h->full_bytes : h->ring_bytes;
+    if (cb >= bytes && cb > 0) {
+        *off = co;
+        return RA2A_OK;
+    }
+    size_t o = 0;
+    int rc = heap_alloc(h, std::max<size_t>(bytes, 256), 256, &o);
+    if (rc) return fail(RA2A_ENOMEM, "staging of %zu bytes per slice does not fit the heap: %s",
+                        bytes, g_err.c_str());
+    co = o;
+    cb = std::max<size_t>(bytes, 256);
+    *off = o;
+    return RA2A_OK;
+}
+
+int device_cus(int* n) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+    return RA2A_OK;
+}
+
+int gcd_int(int a, int b) {
+    while (b) {
+        int t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+// Kernel arguments and launch shape of one pipelined combine (everything but the
+// device pointers, error word and clock), shared by the launch and the host
+// emulator.  Offsets are symmetric byte offsets inside a slice.
+int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan& pl,
+                      const ra2a_opts_t* opts, int64_t stride, size_t in_off, size_t out_off,
+                      size_t stg_off, size_t sig_off, int ncu, int blocks_per_cu,
+                      ra2a::PipeArgs* a, int* V, int* grid) {
+    *a = ra2a::PipeArgs{};
+    a->stride = stride;
+    a->in_off = (int64_t)in_off;
+    a->out_off = (int64_t)out_off;
+    a->stg_off = (int64_t)stg_off;
+    a->sig_off = (int64_t)sig_off;
+    a->S = S;
+    a->H = H;
+    a->D = D;
+    a->BS = pl.BS;
+    a->TH = pl.TH;
+    a->TD = pl.TD;
+    a->W = W;
+    a->e = e0;
+    a->nbs = pl.nbs;
+    a->nhb = pl.nhb;
+    a->ndb = pl.ndb;
+    a->R = pl.R;
+    a->protocol = pl.protocol;
+    const int nstreams = W * pl.nhb * pl.ndb;
+    const int per_cu = std::max(1, std::min(blocks_per_cu, pl.wg_per_cu));
+    a->q = 4;
+    // one group per XCD when the streams divide evenly; fewer on a small device
+    a->NG = gcd_int(ra2a::kNumXcd, nstreams);
+    while (a->NG > 1 && a->NG * a->q > per_cu * ncu) a->NG /= 2;
+    a->ns_g = nstreams / a->NG;
+    a->p = pl.pshare;
+    a->pbatch = pl.pbatch;
+    a->csplit = pl.csplit;
+    a->regionA = pl.regionA;
+    a->straggler = opts ? opts->straggler_rank : -1;
+    a->delay = opts ? opts->straggler_delay : 0;
+    a->seed = opts ? opts->straggler_seed : 0;
+    a->units_per_dest = pl.regionA;
+    // vector width: every offset, stride and run is a multiple of it
+    const uint64_t m = (uint64_t)(D * e0) | (uint64_t)(pl.TD * e0) | in_off | out_off | stg_off;
+    *V = lowbit_vec(m);
+    const int unit = a->NG * a->q;
+    *grid = (per_cu * ncu) / unit * unit;
+    if (*grid < unit) return fail(RA2A_EUNSUPPORTED, "device too small for %d workgroups", unit);
+    const int periods = *grid / unit;
+    a->nprod = a->p * periods;
+    a->ncons = (a->q - a->p) * periods;
+    return RA2A_OK;
+}
+
+int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64_t S, int64_t H,
+                      int64_t D, int dtype, const ra2a_opts_t* opts, void* stream) {
+    const int e0 = elem_bytes(dtype);
+    if (!e0) return fail(RA2A_EINVAL, "unknown dtype %d", dtype);
+    if (W < 1) return fail(RA2A_EINVAL, "W must be >= 1");
+    if (S < 0 || H < 0 || D < 0) return fail(RA2A_EINVAL, "negative dimension");
+    Plan pl{};
+    const bool empty = S == 0 || H == 0 || D == 0;
+    if (!empty) {
+        int rc = make_plan(W, S, H, D, e0, opts, &pl);
+        if (rc) return rc;
+    }
+    Checked c{};
+    int rc = check_combine(in, out, signals, W, S, H, D, dtype,
+                           empty ? 0 : pl.regionA + pl.regionB, &c);
+    if (rc) return rc;
+    if (empty) return ok();
+    if (opts && (opts->straggler_rank < -1 || opts->straggler_rank >= W))
+        return fail(RA2A_EINVAL, "straggler_rank out of range");
+    size_t stg = 0;
+    rc = staging(c.h, false, (size_t)pl.ring_bytes, &stg);
+    if (rc) return rc;
+    rc = ensure_err(c.h);
+    if (rc) return rc;
+
+    int ncu = 0;
+    rc = device_cus(&ncu);
+    if (rc) return rc;
+    const uint64_t m = (uint64_t)(D * e0) | (uint64_t)(pl.TD * e0) | c.in_off | c.out_off | stg;
+    int occ = 0;
+    hipError_t he = ra2a::pipelined_blocks_per_cu(lowbit_vec(m), &occ);
+    if (he != hipSuccess) return hip_fail(he, "occupancy query");
+    ra2a::PipeArgs a{};
+    int V = 16, grid = 0;
+    rc = prepare_pipelined(W, S, H, D, e0, pl, opts, (int64_t)c.h->stride, c.in_off, c.out_off,
+                           stg, c.sig_off, ncu, occ, &a, &V, &grid);
+    if (rc) return rc;
+    a.base = c.h->base;
+    a.err = c.h->err;
+    a.stamps = opts ? opts->timestamps : nullptr;
+    a.timeout = timeout_ticks(c.h);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!(opts && opts->skip_reset)) {
+        he = ra2a::launch_signal_reset(c.h->base, (int64_t)c.h->stride, W, (int64_t)c.sig_off,
+                                       pl.regionA + pl.regionB, st);
+        if (he != hipSuccess) return hip_fail(he, "signal reset launch");
+    }
+    if (opts && opts->timestamps) {
+        he = hipMemsetAsync(opts->timestamps, 0, sizeof(uint64_t) * (size_t)W * pl.regionA, st);
+        if (he != hipSuccess) return hip_fail(he, "timestamp reset");
+    }
+    he = ra2a::launch_pipelined(a, V, grid, st);
+    if (he != hipSuccess) return hip_fail(he, "pipelined combine launch");
+    return ok();
+}
+
+}  // namespace
+
+// ===========================================================================
+// heap
+
+RA2A_API int ra2a_symm_heap_create(int world, size_t slice_bytes, ra2a_heap_t** out) {
+    if (!out) return fail(RA2A_EINVAL, "out must be non-NULL");
+    *out = nullptr;
+    if (world < 1 || world > 4096) return fail(RA2A_EINVAL, "world must be in [1, 4096]");
+    if (slice_bytes == 0) return fail(RA2A_EINVAL, "slice_bytes must be > 0");
+    const size_t stride = (slice_bytes + kSliceAlign - 1) / kSliceAlign * kSliceAlign;
+    if (stride / kSliceAlign > (SIZE_MAX / kSliceAlign) / (size_t)world)
+        return fail(RA2A_EINVAL, "heap size overflow");
+    ra2a_heap* h = new (std::nothrow) ra2a_heap;
+    if (!h) return fail(RA2A_ENOMEM, "host allocation failed");
+    h->world = world;
+    h->stride = stride;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "hipGetDevice");
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, stride * (size_t)world);
+    if (e != hipSuccess) {
+        delete h;
+        (void)hipGetLastError();
+        return fail(e == hipErrorOutOfMemory ? RA2A_ENOMEM : RA2A_EHIP,
+                    "hipMalloc of %zu bytes: %s", stride * (size_t)world, hipGetErrorString(e));
+    }
+    h->base = static_cast<uint8_t*>(p);
+    {
+        std::lock_guard<std::mutex> g(g_reg_mu);
+        g_heaps.push_back(h);
+    }
+    *out = h;
+    return ok();
+}
+
+RA2A_API int ra2a_symm_heap_attach(void* base, int world, size_t stride, ra2a_heap_t** out) {
+    if (!out) return fail(RA2A_EINVAL, "out must be non-NULL");
+    *out = nullptr;
+    if (!base) return fail(RA2A_EINVAL, "base must be non-NULL");
+    if (world < 1 || world > 4096) return fail(RA2A_EINVAL, "world must be in [1, 4096]");
+    if (stride == 0 || stride % 256 || (uintptr_t)base % 256)
+        return fail(RA2A_EINVAL, "base and stride must be non-zero multiples of 256");
+    if (stride > SIZE_MAX / (size_t)world) return fail(RA2A_EINVAL, "heap size overflow");
+    const uint8_t* b = static_cast<const uint8_t*>(base);
+    {
+        std::lock_guard<std::mutex> g(g_reg_mu);
+        for (ra2a_heap* o : g_heaps)
+            if (b < o->base + o->stride * (size_t)o->world && o->base < b + stride * (size_t)world)
+                return fail(RA2A_EINVAL, "range overlaps a live heap");
+    }
+    ra2a_heap* h = new (std::nothrow) ra2a_heap;
+    if (!h) return fail(RA2A_ENOMEM, "host allocation failed");
+    h->world = world;
+    h->stride = stride;
+    h->base = static_cast<uint8_t*>(base);
+    h->owned = false;
+    {
+        std::lock_guard<std::mutex> g(g_reg_mu);
+        g_heaps.push_back(h);
+    }
+    *out = h;
+    return ok();
+}
+
+RA2A_API int ra2a_symm_heap_destroy(ra2a_heap_t* h) {
+    if (!h) return ok();
+    {
+        std::lock_guard<std::mutex> g(g_reg_mu);
+        auto it = std::find(g_heaps.begin(), g_heaps.end(), h);
+        if (it == g_heaps.end()) return fail(RA2A_EINVAL, "not a live heap");
+        g_heaps.erase(it);
+    }
+    const bool touched = h->owned || h->err;
+    hipError_t e = touched ? hipDeviceSynchronize() : hipSuccess;
+    hipError_t e1 = h->owned ? hipFree(h->base) : hipSuccess;
+    hipError_t e2 = h->err ? hipFree(h->err) : hipSuccess;
+    delete h;
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    if (e1 != hipSuccess) return hip_fail(e1, "hipFree(heap)");
+    if (e2 != hipSuccess) return hip_fail(e2, "hipFree(error word)");
+    return ok();
+}
+
+RA2A_API int ra2a_symm_malloc(ra2a_heap_t* h, size_t bytes, size_t align, size_t* sym_offset_out) {
+    if (!h || !sym_offset_out) return fail(RA2A_EINVAL, "heap and sym_offset must be non-NULL");
+    std::lock_guard<std::mutex> g(h->mu);
+    return heap_alloc(h, bytes, align, sym_offset_out);
+}
+
+RA2A_API int ra2a_symm_heap_info(const ra2a_heap_t* h, void** base, size_t* stride, int* world) {
+    if (!h) return fail(RA2A_EINVAL, "heap must be non-NULL");
+    if (base) *base = h->base;
+    if (stride) *stride = h->stride;
+    if (world) *world = h->world;
+    return ok();
+}
+
+RA2A_API ra2a_heap_t* ra2a_symm_heap_find(const void* ptr) { return find_heap(ptr); }
+
+RA2A_API void* ra2a_symm_at(const ra2a_heap_t* h, const void* ptr, int rank) {
+    if (!h || !in_heap(h, ptr) || rank < 0 || rank >= h->world) return nullptr;
+    return h->base + (size_t)rank * h->stride + sym_offset(h, ptr);
+}
+
+RA2A_API int ra2a_symm_heap_set_spin_timeout(ra2a_heap_t* h, uint64_t timeout_us) {
+    if (!h) return fail(RA2A_EINVAL, "heap must be non-NULL");
+    h->timeout_us = timeout_us;
+    return ok();
+}
+
+// ===========================================================================
+// primitives
+
+namespace {
+
+int check_remote(const ra2a_heap_t* h, const void* sym, size_t bytes, int rank, const char* what,
+                 uint8_t** dst) {
+    if (!h) return fail(RA2A_EINVAL, "heap must be non-NULL");
+    if (!sym || !in_heap(h, sym)) return fail(RA2A_EINVAL, "%s is not inside the heap", what);
+    if (rank < 0 || rank >= h->world)
+        return fail(RA2A_EINVAL, "target rank %d outside [0, %d)", rank, h->world);
+    const size_t off = sym_offset(h, sym);
+    if (bytes > h->stride - off) return fail(RA2A_EINVAL, "%s range crosses the end of the slice", what);
+    *dst = h->base + (size_t)rank * h->stride + off;
+    return RA2A_OK;
+}
+
+int check_sig(const ra2a_heap_t* h, const uint64_t* sig, int rank, uint64_t** out) {
+    uint8_t* p = nullptr;
+    int rc = check_remote(h, sig, 8, rank, "signal", &p);
+    if (rc) return rc;
+    if ((uintptr_t)p % 8) return fail(RA2A_EINVAL, "signal must be 8-byte aligned");
+    *out = reinterpret_cast<uint64_t*>(p);
+    return RA2A_OK;
+}
+
+}  // namespace
+
+RA2A_API int ra2a_put(const ra2a_heap_t* h, void* dst_sym, const void* src, size_t bytes,
+                      int target_rank, void* stream) {
+    uint8_t* dst = nullptr;
+    int rc = check_remote(h, dst_sym, bytes, target_rank, "dst", &dst);
+    if (rc) return rc;
+    if (bytes && !src) return fail(RA2A_EINVAL, "src must be non-NULL");
+    const uint8_t* s = static_cast<const uint8_t*>(src);
+    if (bytes && s < dst + bytes && dst < s + bytes) return fail(RA2A_EINVAL, "src and dst overlap");
+    hipError_t e = ra2a::launch_put(dst, s, (int64_t)bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "put launch");
+    return ok();
+}
+
+RA2A_API int ra2a_get(const ra2a_heap_t* h, void* dst, const void* src_sym, size_t bytes,
+                      int source_rank, void* stream) {
+    uint8_t* src = nullptr;
+    int rc = check_remote(h, src_sym, bytes, source_rank, "src", &src);
+    if (rc) return rc;
+    if (bytes && !dst) return fail(RA2A_EINVAL, "dst must be non-NULL");
+    uint8_t* d = static_cast<uint8_t*>(dst);
+    if (bytes && d < src + bytes && src < d + bytes) return fail(RA2A_EINVAL, "src and dst overlap");
+    hipError_t e = ra2a::launch_put(d, src, (int64_t)bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "get launch");
+    return ok();
+}
+
+RA2A_API int ra2a_put_with_signal(const ra2a_heap_t* h, void* dst_sym, const void* src, size_t bytes,
+                                  uint64_t* sig_sym, uint64_t value, int sig_op, int target_rank,
+                                  void* stream) {
+    uint8_t* dst = nullptr;
+    int rc = check_remote(h, dst_sym, bytes, target_rank, "dst", &dst);
+    if (rc) return rc;
+    uint64_t* sig = nullptr;
+    rc = check_sig(h, sig_sym, target_rank, &sig);
+    if (rc) return rc;
+    if (sig_op != RA2A_SIG_SET && sig_op != RA2A_SIG_ADD)
+        return fail(RA2A_EINVAL, "sig_op must be RA2A_SIG_SET or RA2A_SIG_ADD");
+    if (bytes && !src) return fail(RA2A_EINVAL, "src must be non-NULL");
+    const uint8_t* s = static_cast<const uint8_t*>(src);
+    if (bytes && s < dst + bytes && dst < s + bytes) return fail(RA2A_EINVAL, "src and dst overlap");
+    const uint8_t* sg = reinterpret_cast<const uint8_t*>(sig);
+    if (bytes && sg < dst + bytes && dst < sg + 8) return fail(RA2A_EINVAL, "signal inside dst range");
+    hipError_t e = ra2a::launch_put_with_signal(dst, s, (int64_t)bytes, sig, value, sig_op,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "put_with_signal launch");
+    return ok();
+}
+
+RA2A_API int ra2a_signal_op(const ra2a_heap_t* h, uint64_t* sig_sym, uint64_t value, int sig_op,
+                            int target_rank, void* stream) {
+    uint64_t* sig = nullptr;
+    int rc = check_sig(h, sig_sym, target_rank, &sig);
+    if (rc) return rc;
+    if (sig_op != RA2A_SIG_SET && sig_op != RA2A_SIG_ADD)
+        return fail(RA2A_EINVAL, "sig_op must be RA2A_SIG_SET or RA2A_SIG_ADD");
+    hipError_t e = ra2a::launch_signal_op(sig, value, sig_op, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "signal launch");
+    return ok();
+}
+
+RA2A_API int ra2a_wait_signal(const ra2a_heap_t* h, const uint64_t* sig, uint64_t cmp_value,
+                              int cmp_op, void* stream) {
+    if (!h) return fail(RA2A_EINVAL, "heap must be non-NULL");
+    if (!sig || !in_heap(h, sig)) return fail(RA2A_EINVAL, "signal is not inside the heap");
+    if ((uintptr_t)sig % 8) return fail(RA2A_EINVAL, "signal must be 8-byte aligned");
+    if (sym_offset(h, sig) + 8 > h->stride) return fail(RA2A_EINVAL, "signal crosses the slice end");
+    if (cmp_op < RA2A_CMP_EQ || cmp_op > RA2A_CMP_LE) return fail(RA2A_EINVAL, "bad cmp_op");
+    ra2a_heap* hh = const_cast<ra2a_heap*>(h);
+    int rc = ensure_err(hh);
+    if (rc) return rc;
+    hipError_t e = ra2a::launch_wait(sig, cmp_op, cmp_value, timeout_ticks(h), h->err,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "wait launch");
+    return ok();
+}
+
+RA2A_API int ra2a_signal_reset(const ra2a_heap_t* h, uint64_t* sig_sym, int64_t n_slots,
+                               void* stream) {
+    if (!h) return fail(RA2A_EINVAL, "heap must be non-NULL");
+    if (n_slots < 0) return fail(RA2A_EINVAL, "n_slots must be >= 0");
+    if (n_slots == 0) return ok();
+    if (!sig_sym || !in_heap(h, sig_sym)) return fail(RA2A_EINVAL, "signals not inside the heap");
+    const size_t off = sym_offset(h, sig_sym);
+    if (off % 8) return fail(RA2A_EINVAL, "signals must be 8-byte aligned");
+    if ((size_t)(n_slots - 1) > (h->stride - off - 8) / RA2A_SIG_STRIDE_BYTES || off + 8 > h->stride)
+        return fail(RA2A_EINVAL, "signal slots cross the end of the slice");
+    hipError_t e = ra2a::launch_signal_reset(h->base, (int64_t)h->stride, h->world, (int64_t)off,
+                                             n_slots, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "signal reset launch");
+    return ok();
+}
+
+// ===========================================================================
+// combine
+
+RA2A_API int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t D, int dtype,
+                                           const ra2a_opts_t* opts, int64_t* tile_slots,
+                                           int64_t* credit_slots) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(RA2A_EINVAL, "unknown dtype %d", dtype);
+    if (W < 1 || S < 0 || H < 0 || D < 0) return fail(RA2A_EINVAL, "bad dimensions");
+    int64_t a = 0, b = 0;
+    if (S > 0 && H > 0 && D > 0) {
+        Plan p{};
+        int rc = make_plan(W, S, H, D, e, opts, &p);
+        if (rc) return rc;
+        a = p.regionA;
+        b = p.regionB;
+    }
+    if (tile_slots) *tile_slots = a;
+    if (credit_slots) *credit_slots = b;
+    return ok();
+}
+
+RA2A_API int ra2a_rev_all2all_workspace_bytes(int W, int64_t S, int64_t H, int64_t D, int dtype,
+                                              const ra2a_opts_t* opts, int two_phase, size_t* bytes) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(RA2A_EINVAL, "unknown dtype %d", dtype);
+    if (W < 1 || S < 0 || H < 0 || D < 0 || !bytes) return fail(RA2A_EINVAL, "bad arguments");
+    if (S == 0 || H == 0 || D == 0) {
+        *bytes = 0;
+        return ok();
+    }
+    if (two_phase) {
+        *bytes = (size_t)(S * (int64_t)W * H * D * e);
+        return ok();
+    }
+    Plan p{};
+    int rc = make_plan(W, S, H, D, e, opts, &p);
+    if (rc) return rc;
+    *bytes = (size_t)p.ring_bytes;
+    return ok();
+}
+
+RA2A_API int ra2a_rev_all2all(const void* in, void* out, uint64_t* signals, int W, int64_t S,
+                              int64_t H, int64_t D, int dtype, void* stream) {
+    return combine_pipelined(in, out, signals, W, S, H, D, dtype, nullptr, stream);
+}
+
+RA2A_API int ra2a_rev_all2all_ex(const void* in, void* out, uint64_t* signals, int W, int64_t S,
+                                 int64_t H, int64_t D, int dtype, const ra2a_opts_t* opts,
+                                 void* stream) {
+    return combine_pipelined(in, out, signals, W, S, H, D, dtype, opts, stream);
+}
+
+RA2A_API int ra2a_rev_all2all_two_phase(const void* in, void* out, uint64_t* signals, int W,
+                                        int64_t S, int64_t H, int64_t D, int dtype, void* stream) {
+    (void)signals;
+    Checked c{};
+    int rc = check_combine(in, out, nullptr, W, S, H, D, dtype, 0, &c);
+    if (rc) return rc;
+    if (c.n_bytes == 0) return ok();
+    size_t stg = 0;
+    rc = staging(c.h, true, (size_t)c.n_bytes, &stg);
+    if (rc) return rc;
+    ra2a::TwoPhaseArgs a{};
+    a.base = c.h->base;
+    a.stride = (int64_t)c.h->stride;
+    a.in_off = (int64_t)c.in_off;
+    a.out_off = (int64_t)c.out_off;
+    a.stg_off = (int64_t)stg;
+    a.S = S;
+    a.H = H;
+    a.D = D;
+    a.W = W;
+    a.e = c.e;
+    const uint64_t m = (uint64_t)(H * D * c.e) | c.in_off | c.out_off | stg;
+    const int V = lowbit_vec(m);
+    if (c.n_bytes / V >= (int64_t(1) << 31))
+        return fail(RA2A_EUNSUPPORTED, "two-phase combine: more than 2^31 vectors per slice");
+    hipError_t e = ra2a::launch_two_phase(a, V, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "two-phase launch");
+    return ok();
+}
+
+// ===========================================================================
+// diagnostics
+
+RA2A_API int ra2a_check(const ra2a_heap_t* h) {
+    if (!h) return fail(RA2A_EINVAL, "heap must be non-NULL");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    if (!h->err) return ok();
+    uint32_t w = 0;
+    e = hipMemcpy(&w, h->err, sizeof w, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "reading the error word");
+    if (w) {
+        e = hipMemset(h->err, 0, sizeof w);
+        if (e != hipSuccess) return hip_fail(e, "clearing the error word");
+        return fail(RA2A_ETIMEOUT, "a bounded device-side wait timed out (error word 0x%x)", w);
+    }
+    return ok();
+}
+
+RA2A_API const char* ra2a_last_error(void) { return g_err.c_str(); }
+
+RA2A_API int ra2a_version(void) { return 100; }
+
+// ===========================================================================
+// host emulation of the pipelined combine's address arithmetic
+
+RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* out,
+                                          uint64_t* const* signals, int W, int64_t S, int64_t H,
+                                          int64_t D, int dtype, const ra2a_opts_t* opts,
+                                          int num_cus, int blocks_per_cu) {
+    const int e0 = elem_bytes(dtype);
+    if (!e0) return fail(RA2A_EINVAL, "unknown dtype %d", dtype);
+    if (W < 1 || S < 1 || H < 1 || D < 1 || !in || !out || num_cus < 1 || blocks_per_cu < 1)
+        return fail(RA2A_EINVAL, "bad arguments");
+    Plan pl{};
+    int rc = make_plan(W, S, H, D, e0, opts, &pl);
+    if (rc) return rc;
+    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t nb = S * (int64_t)W * H * D * e0;
+    const int64_t in_off = 0, out_off = al(nb), stg_off = al(out_off + nb);
+    const int64_t sig_off = al(stg_off + pl.ring_bytes);
+    const int64_t nsig = pl.regionA + pl.regionB;
+    const int64_t stride = al(sig_off + nsig * RA2A_SIG_STRIDE_BYTES);
+    if ((double)stride * W > 16.0e9) return fail(RA2A_EINVAL, "too large to emulate");
+    ra2a::PipeArgs a{};
+    int V = 16, grid = 0;
+    rc = prepare_pipelined(W, S, H, D, e0, pl, opts, stride, (size_t)in_off, (size_t)out_off,
+                           (size_t)stg_off, (size_t)sig_off, num_cus, blocks_per_cu, &a, &V, &grid);
+    if (rc) return rc;
+    std::vector<uint8_t> heap((size_t)(stride * W), 0xCD);
+    for (int r = 0; r < W; ++r) {
+        std::memcpy(&heap[(size_t)(r * stride + in_off)], in[r], (size_t)nb);
+        std::memset(&heap[(size_t)(r * stride + sig_off)], 0, (size_t)(nsig * RA2A_SIG_STRIDE_BYTES));
+    }
+    auto u64 = [&](int64_t off) { return reinterpret_cast<uint64_t*>(&heap[(size_t)off]); };
+    auto inside = [&](int64_t off, int64_t len, int slice, int64_t region, int64_t rlen) {
+        const int64_t lo = (int64_t)slice * stride + region;
+        return off >= lo && off + len <= lo + rlen;
+    };
+
+    // roles: every (group, index) pair exactly once
+    std::vector<int> seen_p((size_t)a.NG * a.nprod, 0), seen_c((size_t)a.NG * a.ncons, 0);
+    for (int wg = 0; wg < grid; ++wg) {
+        const ra2a::Role ro = ra2a::role_of(a, wg);
+        if (ro.g < 0 || ro.g >= a.NG) return fail(RA2A_EINVAL, "workgroup %d: bad group", wg);
+        if (ro.producer) {
+            if (ro.index < 0 || ro.index >= a.nprod) return fail(RA2A_EINVAL, "bad producer index");
+            seen_p[(size_t)ro.g * a.nprod + ro.index]++;
+        } else {
+            if (ro.index < 0 || ro.index >= a.ncons) return fail(RA2A_EINVAL, "bad consumer index");
+            seen_c[(size_t)ro.g * a.ncons + ro.index]++;
+        }
+    }
+    for (int x : seen_p)
+        if (x != 1) return fail(RA2A_EINVAL, "producer roles do not partition the grid");
+    for (int x : seen_c)
+        if (x != 1) return fail(RA2A_EINVAL, "consumer roles do not partition the grid");
+
+    // work lists exactly as the kernel walks them: every piece / item exactly once
+    const bool add = a.protocol == ra2a::kSigAdd;
+    const int64_t npieces = (int64_t)a.nbs * a.ns_g * a.W;
+    const int upb = add ? a.ns_g : a.ns_g * a.W;
+    const int64_t nitems = (int64_t)a.nbs * upb * a.csplit;
+    {
+        std::vector<uint8_t> cov((size_t)npieces, 0);
+        for (int i = 0; i < a.nprod; ++i)
+            for (int64_t first = (int64_t)i * a.pbatch; first < npieces;
+                 first += (int64_t)a.nprod * a.pbatch)
+                for (int64_t pc = first; pc < std::min(first + (int64_t)a.pbatch, npieces); ++pc)
+                    cov[(size_t)pc]++;
+        for (uint8_t x : cov)
+            if (x != 1) return fail(RA2A_EINVAL, "producer work lists do not partition the pieces");
+        std::vector<uint8_t> covi((size_t)nitems, 0);
+        for (int i = 0; i < a.ncons; ++i)
+            for (int64_t it = i; it < nitems; it += a.ncons) covi[(size_t)it]++;
+        for (uint8_t x : covi)
+            if (x != 1) return fail(RA2A_EINVAL, "consumer work lists do not partition the items");
+    }
+
+    // data movement in an order every wait allows: S-block by S-block, producers first
+    const int64_t sigA_len = pl.regionA * RA2A_SIG_STRIDE_BYTES;
+    for (int b = 0; b < a.nbs; ++b) {
+        for (int g = 0; g < a.NG; ++g) {
+            for (int64_t pc = (int64_t)b * a.ns_g * a.W; pc < (int64_t)(b + 1) * a.ns_g * a.W; ++pc) {
+                const ra2a::Piece p = ra2a::piece_of(a, g, pc);
+                if (p.b != b) return fail(RA2A_EINVAL, "piece %lld is not in block %d", (long long)pc, b);
+                if (p.b >= a.R) {
+                    if (!inside(p.credit, 8, p.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
+                        return fail(RA2A_EINVAL, "piece credit slot outside region B");
+                    if (*u64(p.credit) < p.credit_need)
+                        return fail(RA2A_EINVAL, "piece (g=%d, pc=%lld) would wait for a hand-back "
+                                    "that never comes (%llu < %llu)", g, (long long)pc,
+                                    (unsigned long long)*u64(p.credit),
+                                    (unsigned long long)p.credit_need);
+                }
+                const int vpr = p.pl.run / V;
+                const int BC = p.pl.B * p.pl.C;
+                const int nv = ra2a::plan_vectors(p.pl, V);
+                for (int v = 0; v < nv; ++v) {
+                    int64_t so, dofs;
+                    ra2a::plan_offsets(p.pl, V, vpr, BC, v, &so, &dofs);
+                    if (!inside(p.src + so, V, p.r, in_off, nb))
+                        return fail(RA2A_EINVAL, "piece reads outside in of rank %d", p.r);
+                    if (!inside(p.dst + dofs, V, p.j, stg_off, pl.ring_bytes))
+                        return fail(RA2A_EINVAL, "piece writes outside the staging of rank %d", p.j);
+                    std::memcpy(&heap[(size_t)(p.dst + dofs)], &heap[(size_t)(p.src + so)], (size_t)V);
+                }
+                if (!inside(p.sig, 8, p.j, sig_off, sigA_len))
+                    return fail(RA2A_EINVAL, "piece signal outside region A");
+                if (add)
+                    *u64(p.sig) += 1;
+                else
+                    *u64(p.sig) = 1;
+            }
+        }
+        for (int g = 0; g < a.NG; ++g) {
+            for (int64_t it = (int64_t)b * upb * a.csplit; it < (int64_t)(b + 1) * upb * a.csplit; ++it) {
+                const ra2a::Item q = ra2a::item_of(a, g, it, V);
+                if (q.b != b) return fail(RA2A_EINVAL, "item %lld is not in block %d", (long long)it, b);
+                if (!inside(q.sig, 8, q.j, sig_off, sigA_len))
+                    return fail(RA2A_EINVAL, "item signal outside region A");
+                if (*u64(q.sig) != q.sig_want)
+                    return fail(RA2A_EINVAL, "item (g=%d, it=%lld) would wait forever: signal %llu, "
+                                "wants %llu", g, (long long)it, (unsigned long long)*u64(q.sig),
+                                (unsigned long long)q.sig_want);
+                const int vpr = q.pl.run / V;
+                const int BC = q.pl.B * q.pl.C;
+                for (int v = q.lo; v < q.hi; ++v) {
+                    int64_t so, dofs;
+                    ra2a::plan_offsets(q.pl, V, vpr, BC, v, &so, &dofs);
+                    if (!inside(q.src + so, V, q.j, stg_off, pl.ring_bytes))
+                        return fail(RA2A_EINVAL, "item reads outside the staging of rank %d", q.j);
+                    if (!inside(q.dst + dofs, V, q.j, out_off, nb))
+                        return fail(RA2A_EINVAL, "item writes outside out of rank %d", q.j);
+                    std::memcpy(&heap[(size_t)(q.dst + dofs)], &heap[(size_t)(q.src + so)], (size_t)V);
+                }
+                if (!inside(q.credit, 8, q.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
+                    return fail(RA2A_EINVAL, "item credit slot outside region B");
+                *u64(q.credit) += 1;
+            }
+        }
+    }
+    for (int j = 0; j < W; ++j) {
+        std::memcpy(out[j], &heap[(size_t)(j * stride + out_off)], (size_t)nb);
+        if (signals && signals[j])
+            for (int64_t k = 0; k < nsig; ++k)
+                signals[j][k] = *u64(j * stride + sig_off + k * RA2A_SIG_STRIDE_BYTES);
+    }
+    return ok();
+}

@@ -1,0 +1,55 @@
+// Constants and launch-argument structs shared by the host code and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace ra2a {
+
+constexpr int kSigSet = 0;
+constexpr int kSigAdd = 1;
+constexpr int kCmpEq = 0, kCmpNe = 1, kCmpGt = 2, kCmpGe = 3, kCmpLt = 4, kCmpLe = 5;
+constexpr int kSigStrideU64 = 16;  // 128-byte signal slots
+constexpr uint32_t kErrTimeout = 1u;
+constexpr int kThreads = 256;      // workgroup size of every copy kernel
+constexpr int kNumXcd = 8;         // XCDs of an MI355X
+
+// Arguments of the signal-pipelined persistent combine.
+struct PipeArgs {
+    uint8_t* base;      // heap base (slice 0)
+    int64_t stride;     // slice stride, bytes
+    int64_t in_off;     // symmetric byte offsets of in, out, staging ring, signals
+    int64_t out_off;
+    int64_t stg_off;
+    int64_t sig_off;
+    uint32_t* err;      // device error word of the heap
+    uint64_t* stamps;   // optional per-unit completion clock
+    uint64_t timeout;   // spin timeout, device clock ticks
+    int64_t S, H, D;    // problem
+    int64_t BS, TH, TD; // tile (tokens, heads, d elements)
+    int32_t W, e;       // ranks, element bytes
+    int32_t nbs, nhb, ndb;     // blocks along S, H, D
+    int32_t R;          // ring depth (S-blocks)
+    int32_t protocol;   // kSigSet | kSigAdd
+    int32_t NG;         // stream groups (XCD groups)
+    int32_t ns_g;       // streams per group
+    int32_t q, p;       // role period and producers per period
+    int32_t nprod, ncons;   // producers / consumers per group
+    int32_t pbatch;     // pieces per producer turn
+    int32_t csplit;     // consumer workgroups sharing one unit
+    int64_t regionA;    // data-signal slots per slice (credits follow)
+    int32_t straggler;  // delayed source rank or -1
+    uint32_t delay;     // busy-loop base n0
+    uint64_t seed;      // SplitMix64 seed of the delays
+    int64_t units_per_dest;  // consumer units per destination (timestamps row)
+};
+
+// Arguments of the two-phase combine's two launches.
+struct TwoPhaseArgs {
+    uint8_t* base;
+    int64_t stride;
+    int64_t in_off, out_off, stg_off;
+    int64_t S, H, D;
+    int32_t W, e;
+};
+
+}  // namespace ra2a

@@ -1,0 +1,147 @@
+// Device-side building blocks shared by the gfx950 kernels: vector copies,
+// signal operations, bounded waits and the workgroup-level release/acquire.
+//
+// Memory-ordering model (gfx950, agent scope).  Each XCD has its own L2; a
+// store is visible to another XCD only after the writer's L2 has written the
+// line back, and a reader on another XCD must not hit a stale line of its own
+// L2.  The compiler's agent-scope fences do exactly that: a release fence is a
+// full L2 write-back plus a wait for the wave's own stores, an acquire fence
+// invalidates the non-coherent lines of L1/L2.  A fence only waits for the
+// memory operations of its own wave, so a workgroup that stored a tile with
+// all its waves publishes it as:  every wave fences (release) -> workgroup
+// barrier -> one lane updates the signal.  The consumer side mirrors it: one
+// lane spins with relaxed loads -> barrier -> every wave fences (acquire).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace ra2a {
+
+__device__ __forceinline__ uint64_t rtc_now() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ void fence_release_agent() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+__device__ __forceinline__ void fence_acquire_agent() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+__device__ __forceinline__ uint64_t sig_load(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Signal update, relaxed: callers order it after their data with a release
+// fence (see the header comment).
+__device__ __forceinline__ void sig_update(uint64_t* p, uint64_t v, int op) {
+    if (op == kSigSet)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool cmp_holds(uint64_t x, int op, uint64_t v) {
+    switch (op) {
+        case kCmpEq: return x == v;
+        case kCmpNe: return x != v;
+        case kCmpGt: return x > v;
+        case kCmpGe: return x >= v;
+        case kCmpLt: return x < v;
+        default: return x <= v;  // kCmpLe
+    }
+}
+
+// Bounded spin by one lane: relaxed polling with s_sleep back-off.  Gives up
+// (returns false) when the wait exceeds `timeout` ticks of the 100 MHz device
+// real-time clock -- then it also raises the error word so every other waiter
+// of the launch gives up promptly -- or when another waiter already did.
+__device__ __forceinline__ bool spin_until(const uint64_t* p, int op, uint64_t v,
+                                           uint64_t timeout, uint32_t* err) {
+    uint64_t x = sig_load(p);
+    if (cmp_holds(x, op, v)) return true;
+    const uint64_t t0 = rtc_now();
+    uint32_t n = 0;
+    while (true) {
+        __builtin_amdgcn_s_sleep(1);
+        x = sig_load(p);
+        if (cmp_holds(x, op, v)) return true;
+        if ((++n & 31u) == 0) {
+            if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                return false;
+            if (rtc_now() - t0 > timeout) {
+                __hip_atomic_fetch_or(err, kErrTimeout, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                return false;
+            }
+        }
+    }
+}
+
+// Workgroup-wide wait: lane 0 of the workgroup spins, everyone acquires.
+// Returns false (uniformly across the workgroup) if the wait gave up.
+__device__ __forceinline__ bool wg_wait(const uint64_t* p, int op, uint64_t v, uint64_t timeout,
+                                        uint32_t* err, int* lds_flag) {
+    if (threadIdx.x == 0) *lds_flag = spin_until(p, op, v, timeout, err) ? 1 : 0;
+    __syncthreads();
+    const bool ok = *lds_flag != 0;
+    fence_acquire_agent();
+    __syncthreads();  // lds_flag may be rewritten by the next wait
+    return ok;
+}
+
+// Workgroup-wide release: every wave's stores become visible device-wide
+// before any signal issued after this call by any lane of the workgroup.
+__device__ __forceinline__ void wg_release() {
+    fence_release_agent();
+    __syncthreads();
+}
+
+// ---- vector copies ---------------------------------------------------------
+
+// Native vector types (not HIP's struct wrappers), so copies stay in VGPRs.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int V> struct Vec;
+template <> struct Vec<16> { using T = u32x4; };
+template <> struct Vec<8> { using T = u32x2; };
+template <> struct Vec<4> { using T = uint32_t; };
+template <> struct Vec<2> { using T = uint16_t; };
+template <> struct Vec<1> { using T = uint8_t; };
+
+// Contiguous copy of `bytes` (a multiple of V) by threads [tid0, tid0 + nthr).
+// Full rounds keep U vectors per thread in flight (all loads, then all
+// stores, no bounds checks so the values stay in registers); the remainder
+// goes one vector at a time.
+template <int V, int U>
+__device__ __forceinline__ void copy_flat(const uint8_t* __restrict__ src,
+                                          uint8_t* __restrict__ dst, int64_t bytes, int64_t tid0,
+                                          int64_t nthr) {
+    using T = typename Vec<V>::T;
+    const int64_t total = bytes / V;
+    const T* s = reinterpret_cast<const T*>(src);
+    T* d = reinterpret_cast<T*>(dst);
+    int64_t idx = tid0;
+    for (; idx + (U - 1) * nthr < total; idx += U * nthr) {
+        T v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = s[idx + u * nthr];
+#pragma unroll
+        for (int u = 0; u < U; ++u) d[idx + u * nthr] = v[u];
+    }
+    for (; idx < total; idx += nthr) d[idx] = s[idx];
+}
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): the output for counter value x of a sequence
+// seeded with `seed`.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t x) {
+    uint64_t z = seed + (x + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+}  // namespace ra2a

@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI that need no GPU: exported symbols, heap
+registry and symm_at arithmetic on an attached (never dereferenced) address
+range, tiling queries, and argument validation before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_all2all_combine_amd as ra2a
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra2a.h")
+FAKE_BASE = 0x7E0000000000  # host-side bookkeeping only: never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra2a_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 20
+    L = ra2a.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/ra2a.h but not exported"
+
+
+def test_version():
+    assert ra2a.version() >= 100
+
+
+@pytest.fixture
+def fake_heap():
+    h = ra2a.symm_heap_attach(FAKE_BASE, 4, 4 << 20)
+    yield h
+    ra2a.symm_heap_destroy(h)
+
+
+def test_symm_at_matches_oracle(fake_heap):
+    base, stride, world = ra2a.symm_heap_info(fake_heap)
+    assert (base, stride, world) == (FAKE_BASE, 4 << 20, 4)
+    for off in (0, 8, 1234, stride - 1):
+        for k in range(world):
+            p = base + k * stride + off
+            for r in range(-1, world + 1):
+                want = oracle.symm_at(base, stride, world, p, r)
+                got = ra2a.symm_at(fake_heap, p, r)
+                assert got == want, (off, k, r)
+    assert ra2a.symm_at(fake_heap, base - 1, 0) is None
+    assert ra2a.symm_at(fake_heap, base + world * stride, 0) is None
+    assert ra2a.lib().ra2a_symm_heap_find(base + 3 * stride + 5) == fake_heap
+    assert ra2a.lib().ra2a_symm_heap_find(base + 4 * stride) is None
+
+
+def test_symm_malloc_bump_and_exhaustion(fake_heap):
+    a = ra2a.symm_malloc(fake_heap, 100)
+    b = ra2a.symm_malloc(fake_heap, 10, 4096)
+    assert a == 0 and b == 4096
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.symm_malloc(fake_heap, 4 << 20)
+    assert e.value.code == ra2a.ENOMEM
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.symm_malloc(fake_heap, 8, 3)
+    assert e.value.code == ra2a.EINVAL
+
+
+def test_attach_rejects_overlap_and_misalignment(fake_heap):
+    for args in [(FAKE_BASE + (4 << 20), 1, 4 << 20), (FAKE_BASE + 1, 1, 256), (FAKE_BASE, 0, 256),
+                 (FAKE_BASE + (64 << 20), 1, 100)]:
+        with pytest.raises(ra2a.Ra2aError) as e:
+            ra2a.symm_heap_attach(*args)
+        assert e.value.code == ra2a.EINVAL
+
+
+def test_signal_slots_and_workspace():
+    # 64-token x 1-head x 128 tiles, ADD: one slot per (S-block, head) per slice
+    a, b = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
+    assert (a, b) == (8 * 16, 2 * 16)
+    # SET: one per (S-block, head, source)
+    opts = ra2a.Opts(protocol=ra2a.PROTO_SET)
+    a, b = ra2a.rev_all2all_signal_slots(16, 2048, 32, 128, "f32", opts)
+    assert (a, b) == (32 * 32 * 16, 2 * 32 * 16)
+    # 32 x 7168 tiles: 128 S-blocks
+    a, b = ra2a.rev_all2all_signal_slots(8, 4096, 1, 7168, "bf16", ra2a.Opts(tile_s=32))
+    assert (a, b) == (128, 2)
+    # ragged: S=37 in tiles of 16 -> 3 blocks; D=40 in tiles of 16 -> 3 d blocks
+    a, b = ra2a.rev_all2all_signal_slots(3, 37, 2, 40, "bf16", ra2a.Opts(tile_s=16, tile_d=16))
+    assert (a, b) == (3 * 2 * 3, 2 * 2 * 3)
+    assert ra2a.rev_all2all_signal_slots(3, 0, 2, 40, "bf16") == (0, 0)
+    ring = ra2a.rev_all2all_workspace_bytes(8, 512, 16, 128, "bf16")
+    assert ring == 2 * 64 * 16 * 8 * 128 * 2
+    assert ra2a.rev_all2all_workspace_bytes(8, 512, 16, 128, "bf16", two_phase=True) == \
+        512 * 8 * 16 * 128 * 2
+
+
+@pytest.mark.parametrize("bad", [
+    dict(W=0), dict(S=-1), dict(dtype=99), dict(inp=FAKE_BASE - 4096), dict(W=3),
+    dict(out=FAKE_BASE + 1024), dict(out=FAKE_BASE + (4 << 20) - 1024), dict(out=0x1000),
+    dict(signals=FAKE_BASE + 3004), dict(signals=FAKE_BASE + 1024), dict(signals=FAKE_BASE + (4 << 20) - 128),
+])
+def test_combine_validation(fake_heap, bad):
+    args = dict(inp=FAKE_BASE, out=FAKE_BASE + (1 << 20), signals=FAKE_BASE + (2 << 20), W=4, S=8,
+                H=2, D=16, dtype="bf16")
+    args.update(bad)
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.rev_all2all(args["inp"], args["out"], args["signals"], args["W"], args["S"],
+                         args["H"], args["D"], args["dtype"])
+    assert e.value.code == ra2a.EINVAL, e.value
+
+
+def test_combine_valid_arguments_pass_validation(fake_heap):
+    """With no GPU, valid arguments get past every host check and fail only at HIP."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present; this checks the no-GPU path")
+    except ImportError:
+        pass
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.rev_all2all(FAKE_BASE, FAKE_BASE + (1 << 20), FAKE_BASE + (2 << 20), 4, 8, 2, 16,
+                         "bf16")
+    assert e.value.code == ra2a.EHIP
+
+
+def test_empty_combine_is_a_noop(fake_heap):
+    ra2a.rev_all2all(FAKE_BASE, FAKE_BASE + (1 << 20), FAKE_BASE + (2 << 20), 4, 0, 2, 16, "bf16")
+    ra2a.rev_all2all_two_phase(FAKE_BASE, FAKE_BASE + (1 << 20), None, 4, 5, 0, 16, "bf16")
+
+
+def test_primitive_validation(fake_heap):
+    L = ra2a.lib()
+    assert L.ra2a_put(None, FAKE_BASE, FAKE_BASE, 8, 0, None) == ra2a.EINVAL
+    assert L.ra2a_put(fake_heap, FAKE_BASE, 0x1000, 8, 4, None) == ra2a.EINVAL  # rank
+    assert L.ra2a_put(fake_heap, FAKE_BASE + (4 << 20) - 4, 0x1000, 8, 0, None) == ra2a.EINVAL
+    assert L.ra2a_put_with_signal(fake_heap, FAKE_BASE, 0x1000, 8, FAKE_BASE + 4, 1, 0, 0,
+                                  None) == ra2a.EINVAL  # unaligned signal
+    assert L.ra2a_put_with_signal(fake_heap, FAKE_BASE, 0x1000, 8, FAKE_BASE + 4096, 1, 7, 0,
+                                  None) == ra2a.EINVAL  # bad op
+    assert L.ra2a_wait_signal(fake_heap, FAKE_BASE, 1, 6, None) == ra2a.EINVAL
+    assert L.ra2a_wait_signal(fake_heap, 0x1000, 1, 0, None) == ra2a.EINVAL
+    assert L.ra2a_signal_reset(fake_heap, FAKE_BASE + (4 << 20) - 128, 2, None) == ra2a.EINVAL
+    assert L.ra2a_symm_heap_create(0, 1, ctypes.byref(ctypes.c_void_p())) == ra2a.EINVAL
+    assert ra2a.last_error() != ""

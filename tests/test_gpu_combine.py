@@ -1,0 +1,190 @@
+"""GPU parity of the Reverse All2All combine against the CPU oracle.
+
+Every case compares the HIP path (called through the C ABI) with the oracle
+byte for byte, and the final signal arrays with the protocol model's closed
+forms.  Sizes: small ragged cases that span several tiles with ragged tails,
+edge cases (W=1, one-byte elements, tiles larger than the problem, ring depth
+1), and the four combine workloads at their full sizes.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import moe_all2all_combine_amd as ra2a  # noqa: E402
+import oracle  # noqa: E402
+import synthgen  # noqa: E402
+import expected  # noqa: E402
+from combine_harness import CombineCase, opts_for, say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def expected_signal_array(wl, opts, csplit):
+    return expected.expected_signal_array(wl.W, wl.S, wl.H, wl.D, opts, csplit)
+
+
+def run_and_check(wl, opts, variant="pipelined", inputs=None, want=None, check_signals=True,
+                  csplit=None):
+    say(f"[case] {variant} {wl.name} W={wl.W} S={wl.S} H={wl.H} D={wl.D} {wl.dtype} "
+        f"tile=({opts.tile_s},{opts.tile_h},{opts.tile_d}) proto={opts.protocol} ring={opts.ring}")
+    case = CombineCase(wl, opts, two_phase=(variant == "two_phase"))
+    try:
+        ins = inputs if inputs is not None else synthgen.make_inputs(wl)
+        want = want if want is not None else oracle.combine(ins)
+        case.upload(ins)
+        case.fill_out(0xA5)
+        if variant == "two_phase":
+            case.run_two_phase()
+        else:
+            case.run_pipelined()
+        torch.cuda.synchronize()
+        case.check_device()
+        for j in range(wl.W):
+            got = case.download(j)
+            assert got.tobytes() == want[j].tobytes(), f"rank {j} differs from the oracle"
+        if variant == "pipelined" and check_signals:
+            cs = csplit if csplit is not None else opts.consumer_split
+            exp = expected_signal_array(wl, opts, cs)
+            for j in range(wl.W):
+                np.testing.assert_array_equal(case.signals(j), exp, err_msg=f"signals of rank {j}")
+    finally:
+        case.close()
+
+
+SMALL = [
+    # (W, S, H, D, dtype, tile, protocol, ring)
+    (2, 8, 4, 16, "i32", (8, 4, 16), synthgen.PROTOCOL_SET, 2),
+    (3, 37, 2, 40, "bf16", (16, 1, 16), synthgen.PROTOCOL_ADD, 2),
+    (3, 37, 2, 40, "bf16", (16, 1, 16), synthgen.PROTOCOL_SET, 1),
+    (4, 7, 3, 12, "bf16", (3, 2, 12), synthgen.PROTOCOL_ADD, 1),
+    (5, 33, 1, 24, "u8", (8, 1, 7), synthgen.PROTOCOL_ADD, 3),
+    (2, 65, 3, 5, "u8", (64, 3, 5), synthgen.PROTOCOL_SET, 2),
+    (1, 50, 2, 64, "f32", (16, 2, 64), synthgen.PROTOCOL_ADD, 2),
+    (8, 64, 4, 128, "bf16", (16, 1, 128), synthgen.PROTOCOL_ADD, 2),
+    (6, 20, 2, 8, "f64", (32, 4, 64), synthgen.PROTOCOL_ADD, 2),   # tiles larger than the problem
+    (4, 96, 2, 256, "bf16", (32, 2, 256), synthgen.PROTOCOL_ADD, 8),  # ring deeper than S-blocks
+    (16, 9, 3, 32, "f32", (4, 1, 32), synthgen.PROTOCOL_SET, 2),
+]
+
+
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
+@pytest.mark.parametrize("csplit", [1, 3])
+def test_small_pipelined(W, S, H, D, dtype, tile, proto, ring, csplit):
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S, tile=tile, protocol=proto)
+    opts = opts_for(wl, ring=ring, consumer_split=csplit, producer_batch=2)
+    run_and_check(wl, opts)
+
+
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
+def test_small_two_phase(W, S, H, D, dtype, tile, proto, ring):
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S, tile=tile, protocol=proto)
+    run_and_check(wl, opts_for(wl), variant="two_phase")
+
+
+def test_iota_w2_worked_case():
+    wl = synthgen.WORKLOADS["iota_w2_s8_h4_d16_i32"]
+    opts = opts_for(wl, consumer_split=1)
+    run_and_check(wl, opts)
+
+
+@pytest.mark.parametrize("knobs", [
+    dict(wg_per_cu=1, producer_share=1), dict(wg_per_cu=4, producer_share=3),
+    dict(producer_batch=1), dict(producer_batch=16, consumer_split=8),
+])
+def test_launch_shapes_do_not_change_results(knobs):
+    wl = synthgen.small_workload(8, 200, 3, 96, "bf16", seed=5, tile=(32, 1, 96),
+                                 protocol=synthgen.PROTOCOL_ADD)
+    opts = opts_for(wl, **knobs)
+    cs = knobs.get("consumer_split", 1)
+    if "consumer_split" not in knobs:
+        opts.consumer_split = 1
+    run_and_check(wl, opts, csplit=cs)
+
+
+def test_back_to_back_launches_reset_signals():
+    """A second launch on new data must not be satisfied by the first one's signals."""
+    wl = synthgen.small_workload(4, 64, 2, 64, "bf16", seed=1, tile=(16, 1, 64),
+                                 protocol=synthgen.PROTOCOL_ADD)
+    opts = opts_for(wl, consumer_split=2, ring=1)
+    case = CombineCase(wl, opts)
+    try:
+        for seed in (1, 2, 3):
+            say(f"[case] back-to-back seed={seed}")
+            wl2 = synthgen.small_workload(4, 64, 2, 64, "bf16", seed=seed, tile=(16, 1, 64))
+            ins = synthgen.make_inputs(wl2)
+            case.upload(ins)
+            case.run_pipelined()
+            torch.cuda.synchronize()
+            case.check_device()
+            want = oracle.combine(ins)
+            for j in range(wl.W):
+                assert case.download(j).tobytes() == want[j].tobytes()
+            exp = expected_signal_array(wl, opts, 2)
+            for j in range(wl.W):
+                np.testing.assert_array_equal(case.signals(j), exp)
+    finally:
+        case.close()
+
+
+def test_pipelined_equals_two_phase_bitwise():
+    """The barrier-synchronised variant as a differential for the signal-pipelined one."""
+    wl = synthgen.small_workload(8, 300, 4, 72, "f16", seed=9, tile=(24, 1, 72))
+    case = CombineCase(wl, opts_for(wl, consumer_split=2))
+    try:
+        ins = synthgen.make_inputs(wl)
+        case.upload(ins)
+        case.run_pipelined()
+        torch.cuda.synchronize()
+        case.check_device()
+        a = [case.download(j) for j in range(wl.W)]
+        case.fill_out(0)
+        case.run_two_phase()
+        torch.cuda.synchronize()
+        b = [case.download(j) for j in range(wl.W)]
+        for j in range(wl.W):
+            assert a[j].tobytes() == b[j].tobytes()
+    finally:
+        case.close()
+
+
+def test_special_float_payloads_survive():
+    """NaN payloads, -0.0, infinities and subnormals are moved as bytes."""
+    W, S, H, D = 4, 16, 2, 64
+    wl = synthgen.small_workload(W, S, H, D, "f32", seed=0, tile=(8, 1, 64))
+    specials = np.array([0x7FC00001, 0xFFC12345, 0x80000000, 0x7F800000, 0xFF800000, 0x00000001,
+                         0x807FFFFF, 0x7FA00000], dtype=np.uint32)
+    rng = np.random.default_rng(0)
+    ins = [specials[rng.integers(0, len(specials), size=(S * W, H, D))].view(np.float32)
+           for _ in range(W)]
+    run_and_check(wl, opts_for(wl, consumer_split=1), inputs=ins)
+    run_and_check(wl, opts_for(wl), variant="two_phase", inputs=ins)
+
+
+# ---- full-size workloads ------------------------------------------------------------
+
+def full_case(name, variant, **kw):
+    wl = synthgen.WORKLOADS[name]
+    say(f"[full] generating {name}")
+    ins = synthgen.make_inputs(wl)
+    say(f"[full] oracle {name}")
+    want = oracle.combine(ins)
+    opts = opts_for(wl, consumer_split=kw.pop("consumer_split", 1), **kw)
+    run_and_check(wl, opts, variant=variant, inputs=ins, want=want)
+
+
+@pytest.mark.parametrize("variant", ["pipelined", "two_phase"])
+def test_full_ep_combine_w8_bf16(variant):
+    full_case("ep_combine_w8_s512_h16_d128_bf16", variant)
+
+
+@pytest.mark.parametrize("variant", ["pipelined", "two_phase"])
+def test_full_moe_combine_w8_d7168(variant):
+    full_case("moe_combine_w8_s4096_h1_d7168_bf16", variant, consumer_split=4)
+
+
+@pytest.mark.parametrize("variant", ["pipelined", "two_phase"])
+def test_full_straggler_w16_f32(variant):
+    wl = synthgen.WORKLOADS["straggler_w16_s2048_h32_d128_f32"]
+    full_case("straggler_w16_s2048_h32_d128_f32", variant,
+              straggler_rank=synthgen.straggler_rank(wl), straggler_delay=200, straggler_seed=2)
