@@ -220,7 +220,13 @@ typedef struct ra2a_opts {
                                * (default: about 64 KiB worth, at most 16) */
     int32_t skip_reset;       /* 1: the caller has already zeroed both signal regions
                                * (ra2a_signal_reset on the same stream); no reset launch */
-    int32_t reserved[2];      /* must be zero */
+    int32_t stream_batch;     /* tile streams of one XCD whose staging is live together
+                               * (default: as many as fit about 2 MiB of ring) */
+    int32_t agent_sync;       /* 1: synchronise producers and consumers with device-wide
+                               * release/acquire (L2 write-back / invalidate) instead of
+                               * the XCD-local protocol; also used automatically when the
+                               * device does not place workgroups on XCDs round-robin */
+    int32_t reserved[3];      /* must be zero */
 } ra2a_opts_t;
 
 /* Number of signal slots the combine needs per slice: `tile_slots` data
@@ -266,7 +272,9 @@ int ra2a_rev_all2all_two_phase(const void *in, void *out, uint64_t *signals, int
 
 /* Wait for the device, then report and clear the heap's device error word:
  * RA2A_ETIMEOUT if a bounded wait gave up since the last check, RA2A_EHIP if
- * the device reported an error, else RA2A_OK.                                  */
+ * the device reported an error or a pipelined launch found a workgroup on
+ * another XCD than the XCD-local protocol assumed (that launch's result is not
+ * reliable), else RA2A_OK.                                                     */
 int ra2a_check(const ra2a_heap_t *heap);
 
 /* Host emulation of the signal-pipelined combine (no GPU needed): runs the

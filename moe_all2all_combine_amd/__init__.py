@@ -55,7 +55,8 @@ class Opts(ctypes.Structure):
         ("straggler_delay", ctypes.c_uint32), ("straggler_seed", ctypes.c_uint64),
         ("timestamps", ctypes.c_void_p), ("consumer_lds", ctypes.c_int32),
         ("consumer_split", ctypes.c_int32), ("producer_batch", ctypes.c_int32),
-        ("skip_reset", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
+        ("skip_reset", ctypes.c_int32), ("stream_batch", ctypes.c_int32),
+        ("agent_sync", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
     ]
 
     def __init__(self, **kw):

@@ -133,7 +133,9 @@ struct Plan {
     int64_t regionA, regionB;
     int64_t ring_bytes;     // staging ring bytes per slice
     int csplit, pbatch, wg_per_cu, pshare;
-    int64_t piece_bytes, unit_bytes;
+    int stream_batch;       // 0 = derive from the L2 budget
+    int agent_sync;
+    int64_t piece_bytes, unit_bytes, tile_bytes;
 };
 
 int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* o, Plan* p) {
@@ -141,7 +143,7 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     std::memset(&z, 0, sizeof z);
     z.straggler_rank = -1;
     if (!o) o = &z;
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 3; ++i)
         if (o->reserved[i]) return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
     p->BS = o->tile_s > 0 ? o->tile_s : std::min<int64_t>(S, 64);
     p->TH = o->tile_h > 0 ? o->tile_h : 1;
@@ -165,6 +167,10 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     p->regionB = (int64_t)p->R * p->nhb * p->ndb * perW;
     p->ring_bytes = (int64_t)p->R * p->BS * H * W * D * e;
     p->piece_bytes = p->BS * p->TH * p->TD * e;
+    p->tile_bytes = p->piece_bytes * W;  // one S-block of one stream, all sources
+    if (o->stream_batch < 0) return fail(RA2A_EINVAL, "stream_batch must be >= 0");
+    p->stream_batch = o->stream_batch;
+    p->agent_sync = o->agent_sync ? 1 : 0;
     p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);
     if (o->consumer_split < 0 || o->producer_batch < 0 || o->wg_per_cu < 0 ||
         o->producer_share < 0)
@@ -181,6 +187,8 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (p->pshare > 3) return fail(RA2A_EINVAL, "producer_share must be 1..3");
     // per-launch index arithmetic uses 32-bit vector counts inside one unit
     if (p->unit_bytes >= (int64_t(1) << 31) - 65536) return fail(RA2A_EINVAL, "tile too large");
+    // consumers address the staging ring with 32-bit buffer offsets
+    if (p->ring_bytes >= (int64_t(1) << 32)) return fail(RA2A_EINVAL, "staging ring above 4 GiB");
     return RA2A_OK;
 }
 
@@ -288,8 +296,8 @@ int gcd_int(int a, int b) {
 // emulator.  Offsets are symmetric byte offsets inside a slice.
 int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan& pl,
                       const ra2a_opts_t* opts, int64_t stride, size_t in_off, size_t out_off,
-                      size_t stg_off, size_t sig_off, int ncu, int blocks_per_cu,
-                      ra2a::PipeArgs* a, int* V, int* grid) {
+                      size_t stg_off, size_t sig_off, int ncu, int blocks_per_cu, int nxcd,
+                      bool round_robin, ra2a::PipeArgs* a, int* V, int* grid) {
     *a = ra2a::PipeArgs{};
     a->stride = stride;
     a->in_off = (int64_t)in_off;
@@ -312,14 +320,27 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     const int nstreams = W * pl.nhb * pl.ndb;
     const int per_cu = std::max(1, std::min(blocks_per_cu, pl.wg_per_cu));
     a->q = 4;
-    // one group per XCD when the streams divide evenly; fewer on a small device
-    a->NG = gcd_int(ra2a::kNumXcd, nstreams);
+    // one stream group per XCD (fewer on a device too small for that many)
+    a->NG = std::max(1, nxcd);
     while (a->NG > 1 && a->NG * a->q > per_cu * ncu) a->NG /= 2;
-    a->ns_g = nstreams / a->NG;
+    a->nstreams = nstreams;
+    // XCD-local synchronisation needs group g == XCD of every workgroup w with
+    // w mod NG == g: the dispatcher's round-robin placement over all XCDs
+    a->sync = (!pl.agent_sync && round_robin && a->NG == nxcd) ? ra2a::kSyncXcd : ra2a::kSyncAgent;
+    {
+        const int ns_max = (nstreams + a->NG - 1) / a->NG;
+        int kb = pl.stream_batch;
+        if (kb <= 0) {
+            const int64_t budget = int64_t(2) << 20;  // staging bytes per XCD kept in its L2
+            kb = (int)std::max<int64_t>(1, budget / std::max<int64_t>(1, (int64_t)pl.R * pl.tile_bytes));
+        }
+        a->KB = std::max(1, std::min(kb, ns_max));
+    }
     a->p = pl.pshare;
     a->pbatch = pl.pbatch;
     a->csplit = pl.csplit;
     a->regionA = pl.regionA;
+    a->ring_bytes = pl.ring_bytes;
     a->straggler = opts ? opts->straggler_rank : -1;
     a->delay = opts ? opts->straggler_delay : 0;
     a->seed = opts ? opts->straggler_seed : 0;
@@ -333,6 +354,47 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     const int periods = *grid / unit;
     a->nprod = a->p * periods;
     a->ncons = (a->q - a->p) * periods;
+    return RA2A_OK;
+}
+
+// Number of XCDs of the current device and whether the dispatcher places
+// workgroup w on XCD w mod nxcd, measured once per device with a probe launch.
+int xcd_layout(int* nxcd, bool* round_robin) {
+    static std::mutex mu;
+    static int cached_n[64];
+    static signed char cached_rr[64];
+    static bool have[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) {
+        *nxcd = 1;
+        *round_robin = false;
+        return RA2A_OK;
+    }
+    std::lock_guard<std::mutex> g(mu);
+    if (!have[dev]) {
+        const int n = 4096;
+        uint32_t* d = nullptr;
+        e = hipMalloc(&d, n * sizeof(uint32_t));
+        if (e != hipSuccess) return hip_fail(e, "probe allocation");
+        e = ra2a::launch_xcc_probe(d, n, nullptr);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        std::vector<uint32_t> h(n, 0);
+        if (e == hipSuccess) e = hipMemcpy(h.data(), d, n * sizeof(uint32_t), hipMemcpyDeviceToHost);
+        (void)hipFree(d);
+        if (e != hipSuccess) return hip_fail(e, "XCD placement probe");
+        uint32_t mx = 0;
+        for (uint32_t v : h) mx = std::max(mx, v);
+        const int cnt = (int)mx + 1;
+        bool rr = true;
+        for (int w = 0; w < n; ++w) rr = rr && h[w] == (uint32_t)(w % cnt);
+        cached_n[dev] = cnt;
+        cached_rr[dev] = rr ? 1 : 0;
+        have[dev] = true;
+    }
+    *nxcd = cached_n[dev];
+    *round_robin = cached_rr[dev] != 0;
     return RA2A_OK;
 }
 
@@ -364,14 +426,19 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     int ncu = 0;
     rc = device_cus(&ncu);
     if (rc) return rc;
+    int nxcd = 1;
+    bool rr = false;
+    rc = xcd_layout(&nxcd, &rr);
+    if (rc) return rc;
     const uint64_t m = (uint64_t)(D * e0) | (uint64_t)(pl.TD * e0) | c.in_off | c.out_off | stg;
+    const int sync_guess = (!pl.agent_sync && rr) ? ra2a::kSyncXcd : ra2a::kSyncAgent;
     int occ = 0;
-    hipError_t he = ra2a::pipelined_blocks_per_cu(lowbit_vec(m), &occ);
+    hipError_t he = ra2a::pipelined_blocks_per_cu(lowbit_vec(m), sync_guess, &occ);
     if (he != hipSuccess) return hip_fail(he, "occupancy query");
     ra2a::PipeArgs a{};
     int V = 16, grid = 0;
     rc = prepare_pipelined(W, S, H, D, e0, pl, opts, (int64_t)c.h->stride, c.in_off, c.out_off,
-                           stg, c.sig_off, ncu, occ, &a, &V, &grid);
+                           stg, c.sig_off, ncu, occ, nxcd, rr, &a, &V, &grid);
     if (rc) return rc;
     a.base = c.h->base;
     a.err = c.h->err;
@@ -724,6 +791,9 @@ RA2A_API int ra2a_check(const ra2a_heap_t* h) {
     if (w) {
         e = hipMemset(h->err, 0, sizeof w);
         if (e != hipSuccess) return hip_fail(e, "clearing the error word");
+        if (w & ra2a::kErrPlacement)
+            return fail(RA2A_EHIP, "a pipelined launch ran a workgroup on another XCD than the "
+                        "XCD-local protocol assumed; its result is unreliable (error word 0x%x)", w);
         return fail(RA2A_ETIMEOUT, "a bounded device-side wait timed out (error word 0x%x)", w);
     }
     return ok();
@@ -757,7 +827,8 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
     ra2a::PipeArgs a{};
     int V = 16, grid = 0;
     rc = prepare_pipelined(W, S, H, D, e0, pl, opts, stride, (size_t)in_off, (size_t)out_off,
-                           (size_t)stg_off, (size_t)sig_off, num_cus, blocks_per_cu, &a, &V, &grid);
+                           (size_t)stg_off, (size_t)sig_off, num_cus, blocks_per_cu,
+                           ra2a::kNumXcd, true, &a, &V, &grid);
     if (rc) return rc;
     std::vector<uint8_t> heap((size_t)(stride * W), 0xCD);
     for (int r = 0; r < W; ++r) {
@@ -790,10 +861,9 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
 
     // work lists exactly as the kernel walks them: every piece / item exactly once
     const bool add = a.protocol == ra2a::kSigAdd;
-    const int64_t npieces = (int64_t)a.nbs * a.ns_g * a.W;
-    const int upb = add ? a.ns_g : a.ns_g * a.W;
-    const int64_t nitems = (int64_t)a.nbs * upb * a.csplit;
-    {
+    for (int g = 0; g < a.NG; ++g) {
+        const int64_t npieces = ra2a::group_pieces(a, g);
+        const int64_t nitems = ra2a::group_items(a, g);
         std::vector<uint8_t> cov((size_t)npieces, 0);
         for (int i = 0; i < a.nprod; ++i)
             for (int64_t first = (int64_t)i * a.pbatch; first < npieces;
@@ -807,69 +877,94 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
             for (int64_t it = i; it < nitems; it += a.ncons) covi[(size_t)it]++;
         for (uint8_t x : covi)
             if (x != 1) return fail(RA2A_EINVAL, "consumer work lists do not partition the items");
+        // each workgroup's list must be in non-decreasing S-block order per stream
+        // (the deadlock-freedom argument); tile order already guarantees it within a stream
+    }
+    {
+        // every stream belongs to exactly one group
+        std::vector<int> own((size_t)a.nstreams, 0);
+        for (int g = 0; g < a.NG; ++g) {
+            const ra2a::GroupStreams gs = ra2a::group_streams(a, g);
+            for (int k = 0; k < gs.ns; ++k) own[(size_t)(gs.start + k)]++;
+        }
+        for (int x : own)
+            if (x != 1) return fail(RA2A_EINVAL, "stream groups do not partition the streams");
     }
 
     // data movement in an order every wait allows: S-block by S-block, producers first
     const int64_t sigA_len = pl.regionA * RA2A_SIG_STRIDE_BYTES;
-    for (int b = 0; b < a.nbs; ++b) {
-        for (int g = 0; g < a.NG; ++g) {
-            for (int64_t pc = (int64_t)b * a.ns_g * a.W; pc < (int64_t)(b + 1) * a.ns_g * a.W; ++pc) {
-                const ra2a::Piece p = ra2a::piece_of(a, g, pc);
-                if (p.b != b) return fail(RA2A_EINVAL, "piece %lld is not in block %d", (long long)pc, b);
-                if (p.b >= a.R) {
-                    if (!inside(p.credit, 8, p.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
-                        return fail(RA2A_EINVAL, "piece credit slot outside region B");
-                    if (*u64(p.credit) < p.credit_need)
-                        return fail(RA2A_EINVAL, "piece (g=%d, pc=%lld) would wait for a hand-back "
-                                    "that never comes (%llu < %llu)", g, (long long)pc,
-                                    (unsigned long long)*u64(p.credit),
-                                    (unsigned long long)p.credit_need);
-                }
-                const int vpr = p.pl.run / V;
-                const int BC = p.pl.B * p.pl.C;
-                const int nv = ra2a::plan_vectors(p.pl, V);
-                for (int v = 0; v < nv; ++v) {
-                    int64_t so, dofs;
-                    ra2a::plan_offsets(p.pl, V, vpr, BC, v, &so, &dofs);
-                    if (!inside(p.src + so, V, p.r, in_off, nb))
-                        return fail(RA2A_EINVAL, "piece reads outside in of rank %d", p.r);
-                    if (!inside(p.dst + dofs, V, p.j, stg_off, pl.ring_bytes))
-                        return fail(RA2A_EINVAL, "piece writes outside the staging of rank %d", p.j);
-                    std::memcpy(&heap[(size_t)(p.dst + dofs)], &heap[(size_t)(p.src + so)], (size_t)V);
-                }
-                if (!inside(p.sig, 8, p.j, sig_off, sigA_len))
-                    return fail(RA2A_EINVAL, "piece signal outside region A");
-                if (add)
-                    *u64(p.sig) += 1;
-                else
-                    *u64(p.sig) = 1;
-            }
+    std::vector<std::vector<std::pair<int, int64_t>>> pieces_at((size_t)a.nbs), items_at((size_t)a.nbs);
+    for (int g = 0; g < a.NG; ++g) {
+        const int64_t npieces = ra2a::group_pieces(a, g);
+        for (int64_t pc = 0; pc < npieces; ++pc) {
+            const ra2a::Piece p = ra2a::piece_of(a, g, pc);
+            if (p.b < 0 || p.b >= a.nbs) return fail(RA2A_EINVAL, "piece S-block out of range");
+            pieces_at[(size_t)p.b].push_back({g, pc});
         }
-        for (int g = 0; g < a.NG; ++g) {
-            for (int64_t it = (int64_t)b * upb * a.csplit; it < (int64_t)(b + 1) * upb * a.csplit; ++it) {
-                const ra2a::Item q = ra2a::item_of(a, g, it, V);
-                if (q.b != b) return fail(RA2A_EINVAL, "item %lld is not in block %d", (long long)it, b);
-                if (!inside(q.sig, 8, q.j, sig_off, sigA_len))
-                    return fail(RA2A_EINVAL, "item signal outside region A");
-                if (*u64(q.sig) != q.sig_want)
-                    return fail(RA2A_EINVAL, "item (g=%d, it=%lld) would wait forever: signal %llu, "
-                                "wants %llu", g, (long long)it, (unsigned long long)*u64(q.sig),
-                                (unsigned long long)q.sig_want);
-                const int vpr = q.pl.run / V;
-                const int BC = q.pl.B * q.pl.C;
-                for (int v = q.lo; v < q.hi; ++v) {
-                    int64_t so, dofs;
-                    ra2a::plan_offsets(q.pl, V, vpr, BC, v, &so, &dofs);
-                    if (!inside(q.src + so, V, q.j, stg_off, pl.ring_bytes))
-                        return fail(RA2A_EINVAL, "item reads outside the staging of rank %d", q.j);
-                    if (!inside(q.dst + dofs, V, q.j, out_off, nb))
-                        return fail(RA2A_EINVAL, "item writes outside out of rank %d", q.j);
-                    std::memcpy(&heap[(size_t)(q.dst + dofs)], &heap[(size_t)(q.src + so)], (size_t)V);
-                }
-                if (!inside(q.credit, 8, q.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
-                    return fail(RA2A_EINVAL, "item credit slot outside region B");
-                *u64(q.credit) += 1;
+        const int64_t nitems = ra2a::group_items(a, g);
+        for (int64_t it = 0; it < nitems; ++it) {
+            const ra2a::Item q = ra2a::item_of(a, g, it, V);
+            if (q.b < 0 || q.b >= a.nbs) return fail(RA2A_EINVAL, "item S-block out of range");
+            items_at[(size_t)q.b].push_back({g, it});
+        }
+    }
+    for (int b = 0; b < a.nbs; ++b) {
+        for (auto& gp : pieces_at[(size_t)b]) {
+            const int g = gp.first;
+            const int64_t pc = gp.second;
+            const ra2a::Piece p = ra2a::piece_of(a, g, pc);
+            if (p.b >= a.R) {
+                if (!inside(p.credit, 8, p.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
+                    return fail(RA2A_EINVAL, "piece credit slot outside region B");
+                if (*u64(p.credit) < p.credit_need)
+                    return fail(RA2A_EINVAL, "piece (g=%d, pc=%lld) would wait for a hand-back "
+                                "that never comes (%llu < %llu)", g, (long long)pc,
+                                (unsigned long long)*u64(p.credit),
+                                (unsigned long long)p.credit_need);
             }
+            const int vpr = p.pl.run / V;
+            const int BC = p.pl.B * p.pl.C;
+            const int nv = ra2a::plan_vectors(p.pl, V);
+            for (int v = 0; v < nv; ++v) {
+                int64_t so, dofs;
+                ra2a::plan_offsets(p.pl, V, vpr, BC, v, &so, &dofs);
+                if (!inside(p.src + so, V, p.r, in_off, nb))
+                    return fail(RA2A_EINVAL, "piece reads outside in of rank %d", p.r);
+                if (!inside(p.dst + dofs, V, p.j, stg_off, pl.ring_bytes))
+                    return fail(RA2A_EINVAL, "piece writes outside the staging of rank %d", p.j);
+                std::memcpy(&heap[(size_t)(p.dst + dofs)], &heap[(size_t)(p.src + so)], (size_t)V);
+            }
+            if (!inside(p.sig, 8, p.j, sig_off, sigA_len))
+                return fail(RA2A_EINVAL, "piece signal outside region A");
+            if (add)
+                *u64(p.sig) += 1;
+            else
+                *u64(p.sig) = 1;
+        }
+        for (auto& gi : items_at[(size_t)b]) {
+            const int g = gi.first;
+            const int64_t it = gi.second;
+            const ra2a::Item q = ra2a::item_of(a, g, it, V);
+            if (!inside(q.sig, 8, q.j, sig_off, sigA_len))
+                return fail(RA2A_EINVAL, "item signal outside region A");
+            if (*u64(q.sig) != q.sig_want)
+                return fail(RA2A_EINVAL, "item (g=%d, it=%lld) would wait forever: signal %llu, "
+                            "wants %llu", g, (long long)it, (unsigned long long)*u64(q.sig),
+                            (unsigned long long)q.sig_want);
+            const int vpr = q.pl.run / V;
+            const int BC = q.pl.B * q.pl.C;
+            for (int v = q.lo; v < q.hi; ++v) {
+                int64_t so, dofs;
+                ra2a::plan_offsets(q.pl, V, vpr, BC, v, &so, &dofs);
+                if (!inside(q.src + so, V, q.j, stg_off, pl.ring_bytes))
+                    return fail(RA2A_EINVAL, "item reads outside the staging of rank %d", q.j);
+                if (!inside(q.dst + dofs, V, q.j, out_off, nb))
+                    return fail(RA2A_EINVAL, "item writes outside out of rank %d", q.j);
+                std::memcpy(&heap[(size_t)(q.dst + dofs)], &heap[(size_t)(q.src + so)], (size_t)V);
+            }
+            if (!inside(q.credit, 8, q.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
+                return fail(RA2A_EINVAL, "item credit slot outside region B");
+            *u64(q.credit) += 1;
         }
     }
     for (int j = 0; j < W; ++j) {

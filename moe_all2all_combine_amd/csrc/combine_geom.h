@@ -67,7 +67,33 @@ RA2A_HD void plan_offsets(const RowPlan& p, int V, int vpr, int BC, int idx, int
     *dofs = ia * p.da + ib * p.db + ic * p.dc + (int64_t)col * V;
 }
 
-// Producer piece pc of group g (pieces are ordered S-block, stream, source).
+// Streams of group g: the contiguous range [start, start + ns) of stream ids.
+struct GroupStreams {
+    int start, ns;
+};
+
+RA2A_HD GroupStreams group_streams(const PipeArgs& a, int g) {
+    GroupStreams r;
+    r.start = (int)((int64_t)g * a.nstreams / a.NG);
+    r.ns = (int)((int64_t)(g + 1) * a.nstreams / a.NG) - r.start;
+    return r;
+}
+
+// Tile t of a group with ns streams.  Tiles are ordered by stream batch (KB
+// consecutive streams), then S-block, then stream inside the batch, so that
+// only one batch's staging is live at a time while its S-blocks proceed
+// together.  Returns the S-block and the stream's index inside the group.
+RA2A_HD void tile_of(const PipeArgs& a, int ns, int64_t t, int* b, int* k) {
+    const int64_t per_batch = (int64_t)a.nbs * a.KB;
+    const int kb = (int)(t / per_batch);
+    const int64_t rem = t - kb * per_batch;
+    const int left = ns - kb * a.KB;
+    const int nk = left < a.KB ? left : a.KB;
+    *b = (int)(rem / nk);
+    *k = kb * a.KB + (int)(rem - (int64_t)(*b) * nk);
+}
+
+// Producer piece pc of group g: source r = pc mod W of tile pc div W.
 struct Piece {
     int32_t b, r, j, slot;
     int64_t src;          // absolute byte offset from the heap base (slice r)
@@ -82,11 +108,11 @@ struct Piece {
 RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
     Piece p;
     const int64_t e = a.e;
+    const GroupStreams gs = group_streams(a, g);
     p.r = (int)(pc % a.W);
-    const int64_t t = pc / a.W;
-    const int k = (int)(t % a.ns_g);
-    p.b = (int)(t / a.ns_g);
-    p.sid = g + a.NG * k;
+    int k;
+    tile_of(a, gs.ns, pc / a.W, &p.b, &k);
+    p.sid = gs.start + k;
     const Stream st = stream_of(a, p.sid);
     p.j = st.j;
     p.slot = p.b % a.R;
@@ -123,8 +149,13 @@ RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
     return p;
 }
 
-// Consumer work item `it` of group g: part `part` of unit u (units are ordered
-// S-block, stream[, source]); the unit's vectors [lo, hi) of its row plan.
+RA2A_HD int64_t group_pieces(const PipeArgs& a, int g) {
+    return (int64_t)a.nbs * group_streams(a, g).ns * a.W;
+}
+
+// Consumer work item `it` of group g: part `part` of a unit (ADD: a tile with
+// all W sources; SET: one source of a tile, units ordered tile then source),
+// i.e. the unit's vectors [lo, hi) of its row plan.
 struct Item {
     int32_t b, j, r0, nsrc, slot, part;
     int64_t src;          // absolute byte offset (slice j, staging ring)
@@ -141,15 +172,15 @@ RA2A_HD Item item_of(const PipeArgs& a, int g, int64_t it, int V) {
     Item q;
     const int64_t e = a.e;
     const bool add = a.protocol == kSigAdd;
-    const int upb = add ? a.ns_g : a.ns_g * a.W;  // units per S-block in a group
+    const GroupStreams gs = group_streams(a, g);
     q.part = (int)(it % a.csplit);
     const int64_t u = it / a.csplit;
-    q.b = (int)(u / upb);
-    const int ub = (int)(u - (int64_t)q.b * upb);
-    const int k = add ? ub : ub / a.W;
-    q.r0 = add ? 0 : ub % a.W;
+    const int64_t t = add ? u : u / a.W;
+    q.r0 = add ? 0 : (int)(u % a.W);
     q.nsrc = add ? a.W : 1;
-    const Stream st = stream_of(a, g + a.NG * k);
+    int k;
+    tile_of(a, gs.ns, t, &q.b, &k);
+    const Stream st = stream_of(a, gs.start + k);
     q.j = st.j;
     q.slot = q.b % a.R;
     const int64_t HWDe = a.H * (int64_t)a.W * a.D * e;
@@ -192,6 +223,11 @@ RA2A_HD Item item_of(const PipeArgs& a, int g, int64_t it, int V) {
     if (!add) ci = ci * a.W + q.r0;
     q.credit = (int64_t)st.j * a.stride + a.sig_off + (a.regionA + ci) * kSigStrideU64 * 8;
     return q;
+}
+
+RA2A_HD int64_t group_items(const PipeArgs& a, int g) {
+    const bool add = a.protocol == kSigAdd;
+    return (int64_t)a.nbs * group_streams(a, g).ns * (add ? 1 : a.W) * a.csplit;
 }
 
 // Role of workgroup `wg` of the persistent grid.

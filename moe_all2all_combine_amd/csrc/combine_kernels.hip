@@ -45,29 +45,70 @@ hipError_t launch_signal_reset(uint8_t* base, int64_t stride, int W, int64_t sig
 // Copies vectors [lo, hi) of a row plan (combine_geom.h).  Full rounds keep U
 // vectors per thread in flight (all loads before any store, no bounds checks
 // so the values stay in registers); the remainder goes one vector at a time.
-template <int V, int U>
+// NTL / NTS: non-temporal loads / stores (data touched once: the input and the
+// output), so that they do not displace the staging ring from the L2.
+template <int V, int U, bool NTL, bool NTS>
 __device__ __forceinline__ void copy_plan(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                           const RowPlan& p, int lo, int hi) {
     using T = typename Vec<V>::T;
     const int vpr = p.run / V;
     const int BC = p.B * p.C;
-    int idx = lo + (int)threadIdx.x;
-    for (; idx + (U - 1) * kThreads < hi; idx += U * kThreads) {
+    for (int base = lo + (int)threadIdx.x; base < hi; base += U * kThreads) {
+        // predicated round: every load of the round is issued before any store
         T v[U];
         int64_t doff[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int64_t so;
-            plan_offsets(p, V, vpr, BC, idx + u * kThreads, &so, &doff[u]);
-            v[u] = *reinterpret_cast<const T*>(src + so);
+            const int idx = base + u * kThreads;
+            int64_t so = 0;
+            doff[u] = -1;
+            if (idx < hi) plan_offsets(p, V, vpr, BC, idx, &so, &doff[u]);
+            const T* sp = reinterpret_cast<const T*>(src + so);
+            if (idx < hi) v[u] = NTL ? load_nt(sp) : *sp;
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) *reinterpret_cast<T*>(dst + doff[u]) = v[u];
+        for (int u = 0; u < U; ++u) {
+            if (doff[u] >= 0) {
+                T* dp = reinterpret_cast<T*>(dst + doff[u]);
+                if (NTS)
+                    store_nt(v[u], dp);
+                else
+                    *dp = v[u];
+            }
+        }
     }
-    for (; idx < hi; idx += kThreads) {
-        int64_t so, dofs;
-        plan_offsets(p, V, vpr, BC, idx, &so, &dofs);
-        *reinterpret_cast<T*>(dst + dofs) = *reinterpret_cast<const T*>(src + so);
+}
+
+// The same, reading the source through a buffer descriptor with cache policy
+// POLICY at 32-bit offsets src_off + (plan offset).
+template <int V, int U, int POLICY, bool NTS>
+__device__ __forceinline__ void copy_plan_buf(__amdgpu_buffer_rsrc_t src, uint32_t src_off,
+                                              uint8_t* __restrict__ dst, const RowPlan& p, int lo,
+                                              int hi) {
+    using T = typename Vec<V>::T;
+    const int vpr = p.run / V;
+    const int BC = p.B * p.C;
+    for (int base = lo + (int)threadIdx.x; base < hi; base += U * kThreads) {
+        T v[U];
+        int64_t doff[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = base + u * kThreads;
+            int64_t so = 0;
+            doff[u] = -1;
+            if (idx < hi) plan_offsets(p, V, vpr, BC, idx, &so, &doff[u]);
+            if (idx < hi) v[u] = BufLoad<V, POLICY>::go(src, src_off + (uint32_t)so);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (doff[u] >= 0) {
+                T* dp = reinterpret_cast<T*>(dst + doff[u]);
+                if (NTS)
+                    store_nt(v[u], dp);
+                else
+                    *dp = v[u];
+            }
+        }
     }
 }
 
@@ -75,50 +116,60 @@ __device__ __forceinline__ void copy_plan(const uint8_t* __restrict__ src, uint8
 // The signal-pipelined persistent combine.
 //
 // Work is organised in tile streams: stream (j, hb, db) is the sequence of
-// S-blocks b = 0 .. nbs-1 of destination j, head block hb, d block db.  Streams
-// are split into NG groups (sid mod NG); the workgroups of group g are the
-// launch's workgroups w with w mod NG == g, so with NG == 8 a group is one
-// XCD (workgroups are dispatched to the XCDs round-robin) and a stream's
-// staging lines are written and read inside one XCD's L2.  Inside a group the
-// workgroups alternate roles with period q: the first p of each period
-// produce, the rest consume.
+// S-blocks b = 0 .. nbs-1 of destination j, head block hb, d block db.  The
+// streams are cut into NG contiguous groups; group g is served by the
+// workgroups w with w mod NG == g.  With NG equal to the number of XCDs that
+// is exactly the set of workgroups the dispatcher places on XCD g (checked at
+// run time through the XCC_ID hardware register), so a stream's producers,
+// consumers, staging lines and signals all live in one XCD and its L2, and
+// they synchronise with the XCD-local sequences of device.h instead of device-
+// wide L2 write-backs and invalidations (SYNC == kSyncXcd).  SYNC == kSyncAgent
+// uses device-wide release/acquire instead and does not depend on placement.
 //
-// Producer: pieces (b, stream, source r) of its group in S-block-major order,
-// `pbatch` consecutive pieces per turn.  Per piece: wait for the ring slot
-// b mod R to be handed back by the consumers of S-block b - R (credit count),
-// copy in_r -> staging_j.  Per turn: release, then one lane per piece signals
-// (SET 1 on the piece's slot, or ADD 1 on the tile's slot).  Pieces already
-// copied in a turn are signalled before any hand-back wait of that turn.
+// Inside a group, tiles (stream, S-block) are ordered by stream batch (KB
+// streams whose staging is live together), S-block, stream; the workgroups
+// alternate roles with period q: the first p of each period produce, the rest
+// consume.
 //
-// Consumer: units of its group in S-block-major order (ADD: the tile (b,
-// stream) with all W sources; SET: one piece), each split into `csplit` parts
-// taken by different workgroups.  Per part: wait until the signal reaches W
-// (ADD) or 1 (SET), acquire, copy staging_j -> out_j, release, add 1 to the
-// slot's credit count.
+// Producer: pieces (tile, source r) of its group in order, `pbatch`
+// consecutive pieces per turn.  Per piece: wait for the ring slot b mod R of
+// its stream to be handed back by the consumers of S-block b - R (credit
+// count), copy in_r -> staging_j.  Per turn: release, then wave 0 signals
+// each piece (SET 1 on the piece's slot, or ADD 1 on the tile's slot).  Pieces
+// already copied in a turn are signalled before any hand-back wait of that
+// turn.
+//
+// Consumer: units of its group in order (ADD: a tile with all W sources; SET:
+// one piece), each split into `csplit` parts taken by different workgroups.
+// Per part: wait until the signal reaches W (ADD) or 1 (SET), acquire, copy
+// staging_j -> out_j, release, add 1 to the slot's credit count.
 //
 // Deadlock freedom: the launch is cooperative (every workgroup resident), each
-// workgroup walks its work in increasing S-block order, producers of block b
-// wait only on consumers of block b - R and consumers of block b only on
-// producers of block b; so the earliest blocked wait always has a running
-// workgroup able to satisfy it.  Every wait is also bounded in time.
-template <int V>
+// workgroup walks its work in increasing tile order, a producer of tile
+// (k, b) waits only on consumers of the earlier tile (k, b - R) and a consumer
+// only on producers of its own tile; so the earliest blocked wait always has a
+// running workgroup able to satisfy it.  Every wait is also bounded in time.
+template <int V, int SYNC>
 __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a) {
     __shared__ int lds_flag;
     const Role role = role_of(a, blockIdx.x);
     const int g = role.g;
     const bool add = a.protocol == kSigAdd;
     uint8_t* const base = a.base;
+    if (SYNC == kSyncXcd && threadIdx.x == 0 && (int)xcc_id() != (int)(blockIdx.x % a.NG))
+        __hip_atomic_fetch_or(a.err, kErrPlacement, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     if (role.producer) {
-        const int64_t npieces = (int64_t)a.nbs * a.ns_g * a.W;
-        // Publish pieces [lo, hi) of this workgroup: release, then one lane per piece signals.
+        const int64_t npieces = group_pieces(a, g);
+        // Publish pieces [lo, hi) of this workgroup: release, then wave 0 signals each.
         auto flush = [&](int64_t lo, int64_t hi) {
-            wg_release();
-            const int64_t mine = lo + threadIdx.x;
-            if (mine < hi) {
-                const Piece p = piece_of(a, g, mine);
-                sig_update(reinterpret_cast<uint64_t*>(base + p.sig), 1ull,
-                           add ? kSigAdd : kSigSet);
+            group_release<SYNC>();
+            if (threadIdx.x < 64) {
+                for (int64_t pc = lo + threadIdx.x; pc < hi; pc += 64) {
+                    const Piece p = piece_of(a, g, pc);
+                    sig_update(reinterpret_cast<uint64_t*>(base + p.sig), 1ull,
+                                           add ? kSigAdd : kSigSet);
+                }
             }
         };
         for (int64_t first = (int64_t)role.index * a.pbatch; first < npieces;
@@ -134,36 +185,46 @@ __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a)
                         flush(pend, pc);
                         pend = pc;
                     }
-                    if (!wg_wait(reinterpret_cast<const uint64_t*>(base + p.credit), kCmpGe,
-                                 p.credit_need, a.timeout, a.err, &lds_flag))
+                    if (!group_wait<false>(reinterpret_cast<const uint64_t*>(base + p.credit),
+                                           kCmpGe, p.credit_need, a.timeout, a.err, &lds_flag))
                         return;
                 }
                 if (p.r == a.straggler && a.delay) {
                     if (threadIdx.x == 0) {
-                        const uint64_t id =
-                            ((uint64_t)p.b * (uint64_t)(a.NG * a.ns_g) + p.sid) * a.W + p.r;
+                        const uint64_t id = ((uint64_t)p.b * (uint64_t)a.nstreams + p.sid) * a.W + p.r;
                         const uint64_t n =
                             a.delay + splitmix64(a.seed, id) % ((uint64_t)a.delay + 1ull);
                         for (uint64_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
                     }
                     __syncthreads();
                 }
-                copy_plan<V, 8>(base + p.src, base + p.dst, p.pl, 0, plan_vectors(p.pl, V));
+                copy_plan<V, 8, true, false>(base + p.src, base + p.dst, p.pl, 0,
+                                             plan_vectors(p.pl, V));
             }
             flush(pend, last);
         }
     } else {
-        const int upb = add ? a.ns_g : a.ns_g * a.W;
-        const int64_t nitems = (int64_t)a.nbs * upb * a.csplit;
+        const int64_t nitems = group_items(a, g);
         for (int64_t it = role.index; it < nitems; it += a.ncons) {
             const Item q = item_of(a, g, it, V);
-            if (!wg_wait(reinterpret_cast<const uint64_t*>(base + q.sig), kCmpEq, q.sig_want,
-                         a.timeout, a.err, &lds_flag))
+            // XCD-local: staging is read with device-scope (L1-bypassing) loads from
+            // the L2 this XCD's producers wrote it into, so no invalidation is needed.
+            // Device-wide: the acquire drops stale L1 and L2 lines first.
+            if (!group_wait<SYNC == kSyncAgent>(reinterpret_cast<const uint64_t*>(base + q.sig),
+                                                kCmpEq, q.sig_want, a.timeout, a.err, &lds_flag))
                 return;
-            copy_plan<V, 8>(base + q.src, base + q.dst, q.pl, q.lo, q.hi);
-            wg_release();
+            if (SYNC == kSyncXcd) {
+                const int64_t stg = (int64_t)q.j * a.stride + a.stg_off;
+                copy_plan_buf<V, 8, kPolicySc1, true>(make_rsrc(base + stg, (uint32_t)a.ring_bytes),
+                                                      (uint32_t)(q.src - stg), base + q.dst, q.pl,
+                                                      q.lo, q.hi);
+            } else {
+                copy_plan<V, 8, false, true>(base + q.src, base + q.dst, q.pl, q.lo, q.hi);
+            }
+            group_release<SYNC>();
             if (threadIdx.x == 0) {
-                sig_update(reinterpret_cast<uint64_t*>(base + q.credit), 1ull, kSigAdd);
+                sig_update(reinterpret_cast<uint64_t*>(base + q.credit), 1ull,
+                                       kSigAdd);
                 if (a.stamps)
                     __hip_atomic_fetch_max(a.stamps + (int64_t)q.j * a.units_per_dest + q.unit_index,
                                            rtc_now(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -172,33 +233,45 @@ __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a)
     }
 }
 
-template <int V>
-static hipError_t launch_pipelined_v(const PipeArgs& a, int grid, hipStream_t st) {
-    void* args[] = {const_cast<PipeArgs*>(&a)};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<V>),
-                                      dim3(grid), dim3(kThreads), args, 0, st);
+template <int V, int SYNC>
+static const void* pipelined_fn() {
+    return reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<V, SYNC>);
+}
+
+template <int SYNC>
+static const void* pipelined_fn_v(int V) {
+    switch (V) {
+        case 16: return pipelined_fn<16, SYNC>();
+        case 8: return pipelined_fn<8, SYNC>();
+        case 4: return pipelined_fn<4, SYNC>();
+        case 2: return pipelined_fn<2, SYNC>();
+        default: return pipelined_fn<1, SYNC>();
+    }
+}
+
+static const void* pipelined_kernel(int V, int sync) {
+    return sync == kSyncXcd ? pipelined_fn_v<kSyncXcd>(V) : pipelined_fn_v<kSyncAgent>(V);
 }
 
 hipError_t launch_pipelined(const PipeArgs& a, int V, int grid, hipStream_t st) {
-    switch (V) {
-        case 16: return launch_pipelined_v<16>(a, grid, st);
-        case 8: return launch_pipelined_v<8>(a, grid, st);
-        case 4: return launch_pipelined_v<4>(a, grid, st);
-        case 2: return launch_pipelined_v<2>(a, grid, st);
-        default: return launch_pipelined_v<1>(a, grid, st);
-    }
+    void* args[] = {const_cast<PipeArgs*>(&a)};
+    return hipLaunchCooperativeKernel(pipelined_kernel(V, a.sync), dim3(grid), dim3(kThreads), args,
+                                      0, st);
 }
 
-hipError_t pipelined_blocks_per_cu(int V, int* n) {
-    const void* f;
-    switch (V) {
-        case 16: f = reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<16>); break;
-        case 8: f = reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<8>); break;
-        case 4: f = reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<4>); break;
-        case 2: f = reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<2>); break;
-        default: f = reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<1>); break;
-    }
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, f, kThreads, 0);
+hipError_t pipelined_blocks_per_cu(int V, int sync, int* n) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, pipelined_kernel(V, sync), kThreads, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Placement probe: the XCD each workgroup of a launch runs on.
+__global__ void xcc_probe_kernel(uint32_t* out, int n) {
+    if (threadIdx.x == 0 && (int)blockIdx.x < n) out[blockIdx.x] = xcc_id();
+}
+
+hipError_t launch_xcc_probe(uint32_t* out, int n, hipStream_t st) {
+    hipLaunchKernelGGL(xcc_probe_kernel, dim3(n), dim3(64), 0, st, out, n);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -10,6 +10,9 @@ constexpr int kSigAdd = 1;
 constexpr int kCmpEq = 0, kCmpNe = 1, kCmpGt = 2, kCmpGe = 3, kCmpLt = 4, kCmpLe = 5;
 constexpr int kSigStrideU64 = 16;  // 128-byte signal slots
 constexpr uint32_t kErrTimeout = 1u;
+constexpr uint32_t kErrPlacement = 2u;  // a workgroup ran on another XCD than its group's
+constexpr int kSyncXcd = 0;    // producers and consumers of a stream share one XCD's L2
+constexpr int kSyncAgent = 1;  // device-wide release/acquire (L2 write-back / invalidate)
 constexpr int kThreads = 256;      // workgroup size of every copy kernel
 constexpr int kNumXcd = 8;         // XCDs of an MI355X
 
@@ -30,13 +33,16 @@ struct PipeArgs {
     int32_t nbs, nhb, ndb;     // blocks along S, H, D
     int32_t R;          // ring depth (S-blocks)
     int32_t protocol;   // kSigSet | kSigAdd
-    int32_t NG;         // stream groups (XCD groups)
-    int32_t ns_g;       // streams per group
+    int32_t NG;         // stream groups (one per XCD when sync == kSyncXcd)
+    int32_t nstreams;   // streams in total; group g owns [g*nstreams/NG, (g+1)*nstreams/NG)
+    int32_t KB;         // streams of a group in flight together (a stream batch)
+    int32_t sync;       // kSyncXcd | kSyncAgent
     int32_t q, p;       // role period and producers per period
     int32_t nprod, ncons;   // producers / consumers per group
     int32_t pbatch;     // pieces per producer turn
     int32_t csplit;     // consumer workgroups sharing one unit
     int64_t regionA;    // data-signal slots per slice (credits follow)
+    int64_t ring_bytes; // staging bytes per slice
     int32_t straggler;  // delayed source rank or -1
     uint32_t delay;     // busy-loop base n0
     uint64_t seed;      // SplitMix64 seed of the delays

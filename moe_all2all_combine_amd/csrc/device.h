@@ -34,12 +34,13 @@ __device__ __forceinline__ uint64_t sig_load(const uint64_t* p) {
 }
 
 // Signal update, relaxed: callers order it after their data with a release
-// fence (see the header comment).
+// fence (see the header comment).  Both operations are read-modify-write
+// atomics, which are coherent device-wide on their own.
 __device__ __forceinline__ void sig_update(uint64_t* p, uint64_t v, int op) {
     if (op == kSigSet)
-        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
-        __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ bool cmp_holds(uint64_t x, int op, uint64_t v) {
@@ -79,7 +80,7 @@ __device__ __forceinline__ bool spin_until(const uint64_t* p, int op, uint64_t v
     }
 }
 
-// Workgroup-wide wait: lane 0 of the workgroup spins, everyone acquires.
+// Workgroup-wide wait, device-wide flavour: lane 0 spins, everyone acquires.
 // Returns false (uniformly across the workgroup) if the wait gave up.
 __device__ __forceinline__ bool wg_wait(const uint64_t* p, int op, uint64_t v, uint64_t timeout,
                                         uint32_t* err, int* lds_flag) {
@@ -91,11 +92,71 @@ __device__ __forceinline__ bool wg_wait(const uint64_t* p, int op, uint64_t v, u
     return ok;
 }
 
-// Workgroup-wide release: every wave's stores become visible device-wide
-// before any signal issued after this call by any lane of the workgroup.
+// Workgroup-wide release, device-wide flavour: every wave's stores become
+// visible device-wide before any signal issued after this call by any lane.
 __device__ __forceinline__ void wg_release() {
     fence_release_agent();
     __syncthreads();
+}
+
+// ---- synchronisation between workgroups of one XCD ---------------------------
+//
+// Workgroups on the same XCD share its L2; the vector L1 of each CU is write-
+// through.  The signals themselves are device-scope atomics (read-modify-write
+// updates, L1-bypassing polls), coherent on their own.  The data is ordered
+// around them as follows.
+//   release: every wave drains (s_waitcnt vmcnt(0): its stores have been
+//            acknowledged by the L2), then the workgroup barrier, then wave 0
+//            signals.  With producer and consumer on one XCD the data is now in
+//            the L2 both read through, so nothing is written back from it --
+//            that device-wide write-back is what the XCD-local protocol saves.
+//            (SYNC == kSyncAgent adds it, for producers and consumers that may
+//            sit on different XCDs.)
+//   acquire: after seeing the signal, wave 0 runs the device-scope acquire
+//            (`buffer_inv sc1`): it drops the CU's L1, whose lines may hold an
+//            earlier use of the same staging slot.  The workgroup-scope
+//            invalidate (`buffer_inv sc0`) is not enough: outside threadgroup-
+//            split dispatches it leaves the L1 alone (measured: a consumer then
+//            read the slot's previous contents).  One wave suffices because the
+//            workgroup's waves share the CU and its L1.
+// The pipelined kernel checks at run time that each workgroup runs on the XCD
+// its stream group assumes.
+
+// This wave's memory operations have completed (stores acknowledged by the L2,
+// loads returned).
+__device__ __forceinline__ void wave_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup-wide wait.  Lane 0 spins; with ACQUIRE, wave 0 then acquires for the
+// whole workgroup (needed before reading data the signal publishes; not needed
+// before only writing, e.g. after a ring hand-back).  Returns false, uniformly
+// across the workgroup, if the wait gave up.
+template <bool ACQUIRE>
+__device__ __forceinline__ bool group_wait(const uint64_t* p, int op, uint64_t v, uint64_t timeout,
+                                           uint32_t* err, int* lds_flag) {
+    if (threadIdx.x == 0) {
+        const bool ok = spin_until(p, op, v, timeout, err);
+        if (ACQUIRE) fence_acquire_agent();
+        *lds_flag = ok ? 1 : 0;
+    }
+    __syncthreads();
+    const bool ok = *lds_flag != 0;
+    __syncthreads();  // lds_flag may be rewritten by the next wait
+    return ok;
+}
+
+// Workgroup-wide release: afterwards wave 0 may signal.  Every wave drains its
+// own memory operations; with SYNC == kSyncAgent wave 0 then also writes the
+// L2 back (one write-back covers every wave's stores, which the drains put in
+// the L2).  Signals must be issued by wave 0 (threadIdx.x < 64).
+template <int SYNC>
+__device__ __forceinline__ void group_release() {
+    wave_drain();
+    __syncthreads();
+    if (SYNC == kSyncAgent && threadIdx.x < 64) fence_release_agent();
+}
+
+__device__ __forceinline__ uint32_t xcc_id() {
+    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & 0xFu;  // HW_REG_XCC_ID
 }
 
 // ---- vector copies ---------------------------------------------------------
@@ -110,6 +171,49 @@ template <> struct Vec<8> { using T = u32x2; };
 template <> struct Vec<4> { using T = uint32_t; };
 template <> struct Vec<2> { using T = uint16_t; };
 template <> struct Vec<1> { using T = uint8_t; };
+
+// Buffer loads through a resource descriptor: the cache-policy bits are explicit
+// and the hardware range-checks every access against the descriptor's size
+// (an out-of-range load returns 0 instead of touching other memory).
+constexpr int kPolicySc1 = 16;  // device scope: never served from the CU's L1
+constexpr uint32_t kBufferDword3 = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             (int)kBufferDword3);
+}
+
+template <int V, int POLICY> struct BufLoad;
+template <int POLICY> struct BufLoad<16, POLICY> {
+    static __device__ __forceinline__ u32x4 go(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY);
+    }
+};
+template <int POLICY> struct BufLoad<8, POLICY> {
+    static __device__ __forceinline__ u32x2 go(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY);
+    }
+};
+template <int POLICY> struct BufLoad<4, POLICY> {
+    static __device__ __forceinline__ uint32_t go(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POLICY);
+    }
+};
+template <int POLICY> struct BufLoad<2, POLICY> {
+    static __device__ __forceinline__ uint16_t go(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, POLICY);
+    }
+};
+template <int POLICY> struct BufLoad<1, POLICY> {
+    static __device__ __forceinline__ uint8_t go(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, POLICY);
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ T load_nt(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void store_nt(T v, T* p) { __builtin_nontemporal_store(v, p); }
 
 // Contiguous copy of `bytes` (a multiple of V) by threads [tid0, tid0 + nthr).
 // Full rounds keep U vectors per thread in flight (all loads, then all

@@ -57,3 +57,23 @@ def test_emulator_rejects_device_too_small():
     with pytest.raises(ra2a.Ra2aError) as e:
         ra2a.debug_emulate_pipelined(ins, 8, 16, 16, 8, "bf16", None, 2, 1)
     assert e.value.code == ra2a.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("stream_batch", [1, 2, 3, 1000])
+@pytest.mark.parametrize("W,S,H,D,tile,proto,ring", [
+    (8, 200, 6, 96, (32, 1, 96), P_ADD, 2),
+    (5, 70, 4, 64, (16, 2, 32), P_SET, 3),
+    (16, 64, 8, 32, (16, 1, 32), P_ADD, 1),
+])
+def test_emulated_stream_batches(stream_batch, W, S, H, D, tile, proto, ring):
+    wl = synthgen.small_workload(W, S, H, D, "bf16", seed=7, tile=tile, protocol=proto)
+    ins = synthgen.make_inputs(wl)
+    opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2],
+                     protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD, ring=ring,
+                     consumer_split=2, producer_batch=3, stream_batch=stream_batch)
+    outs, sigs = ra2a.debug_emulate_pipelined(ins, W, S, H, D, "bf16", opts, 256, 2)
+    want = oracle.combine(ins)
+    exp = expected_signal_array(W, S, H, D, opts, 2)
+    for j in range(W):
+        assert outs[j].tobytes() == want[j].tobytes(), f"rank {j}"
+        np.testing.assert_array_equal(sigs[j].astype(np.int64), exp)

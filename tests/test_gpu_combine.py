@@ -76,6 +76,13 @@ def test_small_pipelined(W, S, H, D, dtype, tile, proto, ring, csplit):
     run_and_check(wl, opts)
 
 
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL[:6])
+def test_small_pipelined_agent_sync(W, S, H, D, dtype, tile, proto, ring):
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S + 1, tile=tile, protocol=proto)
+    opts = opts_for(wl, ring=ring, consumer_split=2, producer_batch=3, agent_sync=1)
+    run_and_check(wl, opts)
+
+
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
 def test_small_two_phase(W, S, H, D, dtype, tile, proto, ring):
     wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S, tile=tile, protocol=proto)
@@ -91,6 +98,8 @@ def test_iota_w2_worked_case():
 @pytest.mark.parametrize("knobs", [
     dict(wg_per_cu=1, producer_share=1), dict(wg_per_cu=4, producer_share=3),
     dict(producer_batch=1), dict(producer_batch=16, consumer_split=8),
+    dict(agent_sync=1), dict(agent_sync=1, producer_batch=5, consumer_split=3),
+    dict(stream_batch=1), dict(stream_batch=3, ring=1), dict(stream_batch=1000, ring=4),
 ])
 def test_launch_shapes_do_not_change_results(knobs):
     wl = synthgen.small_workload(8, 200, 3, 96, "bf16", seed=5, tile=(32, 1, 96),
