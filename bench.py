@@ -1,20 +1,26 @@
 """Benchmark of the Reverse All2All combine on one MI355X.
 
-One step = one whole combine (signal reset + the signal-pipelined persistent
-kernel) over the EP-combine workload: W=8 simulated ranks, S=512 tokens, H=16
-heads, D=128, bf16 values uniform(-1, 1) from seed 0, 64 x 1 x 128 tiles with
-ADD-to-W tile signals.  Inputs are resident in HBM before timing starts.  To
-keep the 256 MiB working set from being served by the 256 MB Infinity Cache,
-consecutive steps rotate through several independent in/out buffer sets.
+One step = one whole combine: the signal reset, then the signal-pipelined
+persistent kernel (direct mode, the library default), over the EP-combine
+workload: W=8 simulated ranks (slices of one symmetric heap), S=512 tokens,
+H=16 heads, D=128, bf16 values uniform(-1, 1) from seed 0, 64 x 1 x 128
+signal tiles with ADD-to-W tile signals.  Inputs are resident in HBM before
+timing starts.  So that the 256 MiB working set is not served from the 256 MB
+Infinity Cache, consecutive steps rotate through several in/out buffer sets.
 
-Prints one JSON line (metric, value in GB/s of algorithmic bytes = every input
-element read once + every output element written once, roofline of the
-persistent kernel from HIP events around its launches, the two-phase variant
-and a plain device copy for context, and the CPU oracle's rate on the host).
+Prints one JSON line: metric and value (GB/s of algorithmic bytes: every input
+element read once and every output element written once, per step), the
+roofline of the persistent kernel from HIP events around its launches inside
+the timed region, and for context the staged mode, the two-phase variant, a
+plain copy of the same bytes with the library's put kernel, and the CPU
+oracle's rate on the host.
+
+``--legs main`` runs only the timed combine (for counter runs under rocprofv3).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,18 +32,39 @@ sys.path.insert(0, ROOT)
 WORKLOAD = "ep_combine_w8_s512_h16_d128_bf16"
 HBM_PEAK_GBS = 8000.0
 NSETS = 6
+KERNEL = "rev_a2a_pipelined_kernel (direct mode)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rev_a2a_pipelined_direct_ep_combine_w8.json")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The CPU oracle (single thread) on repeated full combines for about budget_s."""
-    import oracle
-    import synthgen
+def kernel_source_hash():
+    """Hash of the sources the persistent kernel is compiled from."""
+    h = hashlib.sha256()
+    for f in ("combine_kernels.hip", "combine_geom.h", "device.h", "common.h"):
+        with open(os.path.join(ROOT, "moe_all2all_combine_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
-    ins = synthgen.make_inputs(wl)
+
+def load_traffic():
+    """HBM bytes per launch of the persistent kernel from the committed rocprofv3
+    counter runs, if they were taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, ins, budget_s=12.0):
+    """The CPU oracle as it stands (one thread) on repeated full combines."""
+    import oracle
+
     oracle.combine(ins)  # warm
     reps = 0
     t0 = time.perf_counter()
@@ -49,24 +76,8 @@ def cpu_baseline(wl, budget_s=12.0):
             break
     gbs = wl.algorithmic_bytes * reps / el / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full combines of the {wl.name} workload, single thread, "
-                      f"{el:.1f} s"}
-
-
-def load_traffic():
-    """HBM traffic of the persistent kernel from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_rev_a2a_pipelined_ep_combine_w8.json")
-    if not os.path.exists(path):
-        return None
-    import hashlib
-    src = os.path.join(ROOT, "moe_all2all_combine_amd", "csrc", "combine_kernels.hip")
-    dev = os.path.join(ROOT, "moe_all2all_combine_amd", "csrc", "device.h")
-    h = hashlib.sha256(open(src, "rb").read() + open(dev, "rb").read()).hexdigest()[:16]
-    rec = json.load(open(path))
-    if rec.get("source_hash") != h:
-        return None
-    return rec.get("traffic_bytes_per_launch")
+            "sample": f"{reps} full combines of the {wl.name} workload "
+                      f"({wl.algorithmic_bytes >> 20} MiB moved each), one thread, {el:.1f} s"}
 
 
 def main():
@@ -75,11 +86,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--legs", choices=["all", "main"], default="all")
     ap.add_argument("--workload", default=WORKLOAD)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs the combine's W simulated ranks on one GPU; "
-              f"--gpus {args.gpus} is not supported (use --gpus 1)", file=sys.stderr)
+        print(f"bench.py: the combine's W ranks are simulated as W slices of one heap on one "
+              f"GPU; --gpus {args.gpus} is not supported (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -92,100 +104,70 @@ def main():
     W, S, H, D = wl.W, wl.S, wl.H, wl.D
     torch.cuda.set_device(0)
     proto = ra2a.PROTO_SET if wl.protocol == synthgen.PROTOCOL_SET else ra2a.PROTO_ADD
-    opts = ra2a.Opts(tile_s=wl.tile_s, tile_h=wl.tile_h, tile_d=wl.tile_d, protocol=proto)
-    opts_nr = ra2a.Opts(tile_s=wl.tile_s, tile_h=wl.tile_h, tile_d=wl.tile_d, protocol=proto,
-                        skip_reset=1)
-    n_tile, n_credit = ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, opts)
-    nsig = n_tile + n_credit
-    ring = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, opts)
+    tiles = dict(tile_s=wl.tile_s, tile_h=wl.tile_h, tile_d=wl.tile_d, protocol=proto)
+    opts = ra2a.Opts(skip_reset=1, **tiles)
+    opts_st = ra2a.Opts(skip_reset=1, mode=ra2a.MODE_STAGED, **tiles)
+    nsig = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o)) for o in (opts, opts_st))
+    ring = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, opts_st)
     full = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, None, True)
     nb = wl.bytes_per_rank
-    slice_bytes = NSETS * (2 * nb + nsig * 128 + 4096) + ring + full + (1 << 20)
+    slice_bytes = NSETS * (2 * nb + nsig * 128 + 4096) + ring + full + (4 << 20)
     heap = ra2a.SymmHeap(W, slice_bytes)
-    sets = []
-    for _ in range(NSETS):
-        sets.append((heap.alloc(nb), heap.alloc(nb), heap.alloc(nsig * 128)))
+    sets = [(heap.alloc(nb), heap.alloc(nb), heap.alloc(nsig * 128)) for _ in range(NSETS)]
     log(f"[bench] generating {wl.name}")
     ins = synthgen.make_inputs(wl)
     bits = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[wl.elem_bytes]
+    npbits = {1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64}[wl.elem_bytes]
     for (oi, _, _) in sets:
         for r in range(W):
-            heap.view(oi, (S * W, H, D), bits, r).copy_(
-                torch.from_numpy(ins[r].view({2: np.int16, 4: np.int32, 1: np.uint8,
-                                              8: np.int64}[wl.elem_bytes])))
+            heap.view(oi, (S * W, H, D), bits, r).copy_(torch.from_numpy(ins[r].view(npbits)))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     hs = heap.handle
 
-    def step(k, ev=None):
+    def step(k, o, ev=None):
         oi, oo, osg = sets[k % NSETS]
         ra2a.signal_reset(hs, heap.ptr(osg), nsig, stream)
         if ev is not None:
             ev[0].record(stream)
-        ra2a.rev_all2all_ex(heap.ptr(oi), heap.ptr(oo), heap.ptr(osg), W, S, H, D, wl.dtype,
-                            opts_nr, stream)
+        ra2a.rev_all2all_ex(heap.ptr(oi), heap.ptr(oo), heap.ptr(osg), W, S, H, D, wl.dtype, o,
+                            stream)
         if ev is not None:
             ev[1].record(stream)
 
-    log("[bench] warmup")
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
+    def timed(o, steps, warmup, events=False):
+        for k in range(warmup):
+            step(k, o)
+        torch.cuda.synchronize()
+        assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)] if events else [None] * steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step(k, o, evs[k])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
+        kern = float(np.mean([a.elapsed_time(b) for a, b in evs])) if events else None
+        return (t1 - t0) * 1e3 / steps, kern
 
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    log(f"[bench] {args.warmup} warmup + {args.steps} timed steps")
+    ms_per_step, kern_ms = timed(opts, args.steps, args.warmup, events=True)
 
-    # kernel-only durations (HIP events on the launch stream, around the persistent kernel)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for k in range(args.steps):
-        step(k, evs[k])
-    torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    def parity(k):
+        import oracle
+        want = oracle.combine(ins)
+        oo = sets[k % NSETS][1]
+        return all(heap.view(oo, (S, H * W, D), bits, j).cpu().numpy().tobytes() == want[j].tobytes()
+                   for j in range(W))
 
-    # parity spot check of the last set used against the oracle (full, W outputs)
-    import oracle
-    want = oracle.combine(ins)
-    oo = sets[(args.steps - 1) % NSETS][1]
-    parity = all(heap.view(oo, (S, H * W, D), bits, j).cpu().numpy().tobytes() == want[j].tobytes()
-                 for j in range(W))
-
-    # two-phase variant on the same rotation, for context
-    for k in range(args.warmup):
-        oi, oo, _ = sets[k % NSETS]
-        ra2a.rev_all2all_two_phase(heap.ptr(oi), heap.ptr(oo), None, W, S, H, D, wl.dtype, stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        oi, oo, _ = sets[k % NSETS]
-        ra2a.rev_all2all_two_phase(heap.ptr(oi), heap.ptr(oo), None, W, S, H, D, wl.dtype, stream)
-    torch.cuda.synchronize()
-    tp_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # a plain device-to-device copy of the same bytes (torch), for context
-    src = torch.empty(W * nb, dtype=torch.uint8, device="cuda")
-    dsts = [torch.empty_like(src) for _ in range(3)]
-    for k in range(3):
-        dsts[k].copy_(src)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        dsts[k % 3].copy_(src)
-    torch.cuda.synchronize()
-    copy_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-
+    ok = parity(args.steps - 1)
+    log(f"[bench] combine {ms_per_step * 1e3:.1f} us/step, kernel {kern_ms * 1e3:.1f} us, "
+        f"parity {ok}")
     alg = wl.algorithmic_bytes
     value = alg / (ms_per_step * 1e-3) / 1e9
     achieved = alg / (kern_ms * 1e-3) / 1e9
-    cpu = None if args.no_cpu else cpu_baseline(wl)
     rec = {
         "metric": "Reverse-All2All combine GB/s (read+write) and % of HBM peak, W=8 bf16",
         "value": round(value, 2),
@@ -200,21 +182,50 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "parity": parity,
+        "parity": ok,
         "config": {"workload": wl.name, "W": W, "S": S, "H": H, "D": D, "dtype": wl.dtype,
                    "tile": [wl.tile_s, wl.tile_h, wl.tile_d], "protocol": wl.protocol,
-                   "variant": "signal-pipelined persistent kernel", "buffer_sets": NSETS,
+                   "variant": "signal-pipelined persistent kernel, direct mode",
+                   "step": "signal reset + combine", "buffer_sets": NSETS,
                    "algorithmic_bytes": alg},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(), "kernel": "rev_a2a_pipelined_kernel",
+                     "traffic": load_traffic(), "kernel": KERNEL,
                      "kernel_ms": round(kern_ms, 5)},
-        "two_phase": {"ms_per_step": round(tp_ms, 5),
-                      "value": round(alg / (tp_ms * 1e-3) / 1e9, 2)},
-        "device_copy": {"bytes": 2 * W * nb, "ms": round(copy_ms, 5),
-                        "GBps": round(2 * W * nb / (copy_ms * 1e-3) / 1e9, 2)},
-        "cpu_baseline": cpu,
     }
+    if args.legs == "all":
+        st_ms, st_kern = timed(opts_st, args.steps, args.warmup, events=True)
+        st_ok = parity(args.steps - 1)
+        rec["staged"] = {"ms_per_step": round(st_ms, 5), "kernel_ms": round(st_kern, 5),
+                         "value": round(alg / (st_ms * 1e-3) / 1e9, 2), "parity": st_ok}
+
+        def two_phase(k):
+            oi, oo, _ = sets[k % NSETS]
+            ra2a.rev_all2all_two_phase(heap.ptr(oi), heap.ptr(oo), None, W, S, H, D, wl.dtype,
+                                       stream)
+
+        def put_copy(k):
+            # calibration copy: every in slice -> the out slot of the same slice
+            oi, oo, _ = sets[k % NSETS]
+            for r in range(W):
+                ra2a.put(hs, heap.ptr(oo), heap.ptr(oi, r), nb, r, stream)
+
+        ctx = {}
+        for name, fn in (("two_phase", two_phase), ("put_copy", put_copy)):
+            for k in range(args.warmup):
+                fn(k)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(args.steps):
+                fn(k)
+            torch.cuda.synchronize()
+            ctx[name] = (time.perf_counter() - t0) * 1e3 / args.steps
+        rec["two_phase"] = {"ms_per_step": round(ctx["two_phase"], 5),
+                            "value": round(alg / (ctx["two_phase"] * 1e-3) / 1e9, 2)}
+        rec["put_copy"] = {"bytes_moved": 2 * W * nb, "launches": W,
+                           "ms": round(ctx["put_copy"], 5),
+                           "GBps": round(2 * W * nb / (ctx["put_copy"] * 1e-3) / 1e9, 2)}
+    rec["cpu_baseline"] = None if args.no_cpu else cpu_baseline(wl, ins)
     heap.close()
     print(json.dumps(rec), flush=True)
 

@@ -192,7 +192,17 @@ int ra2a_signal_reset(const ra2a_heap_t *heap, uint64_t *sig_sym, int64_t n_slot
 #define RA2A_PROTO_ADD 1 /* push mode: W adds per tile, wait for W (default) */
 #define RA2A_PROTO_SET 2 /* one SET per (source, tile) piece, wait for 1 */
 
-/* Tiling and protocol of the signal-pipelined kernel (0 / -1 = default). */
+/* Where producers put their pieces (ra2a_opts_t.mode). */
+#define RA2A_MODE_DIRECT 1 /* push straight into out_j (default) */
+#define RA2A_MODE_STAGED 2 /* through a staging ring in slice j, reordered by consumers */
+
+/* Work-queue words the pipelined combine keeps after the hand-back counters
+ * (used in slice 0 only): per stream group (up to 8) a claim counter and a
+ * take-over counter, then a mask of fully claimed groups and a spare word.   */
+#define RA2A_QUEUE_SLOTS 18
+
+/* Tiling, protocol and launch options of the signal-pipelined kernel; a zeroed
+ * struct (with straggler_rank = -1) means every default.                     */
 typedef struct ra2a_opts {
     int64_t tile_s;     /* tokens per tile (default min(S, 64)) */
     int64_t tile_h;     /* heads per tile (default 1) */
@@ -201,57 +211,73 @@ typedef struct ra2a_opts {
                          * s-block, head block, d block), each of the W sources adds 1, the
                          * consumer waits for W.  RA2A_PROTO_SET: one signal per piece
                          * (source r, tile), set to 1; the consumer waits for each piece. */
-    int32_t ring;       /* staging ring depth in S-blocks (default 2; >= number of
-                         * S-blocks means no slot is reused) */
+    int32_t ring;       /* staged mode: staging ring depth in S-blocks (default 8; >= the
+                         * number of S-blocks means no slot is reused) */
     int32_t wg_per_cu;  /* persistent workgroups per compute unit (default 2) */
-    int32_t producer_share; /* producers per 4 workgroups of a group, 1..3 (default 2) */
+    int32_t lookahead;  /* staged mode: tiles whose pieces are queued ahead of a tile's
+                         * consumer work (0: default -- half of what the ring allows, or
+                         * every piece first when no slot is reused; -1: every piece
+                         * first); always capped so that no wait points forward */
     int32_t straggler_rank;   /* source slice whose producers are delayed, -1 = none */
     uint32_t straggler_delay; /* busy-loop base n0: each delayed piece spins n0 + u
                                * iterations, u uniform in [0, n0] from SplitMix64 */
     uint64_t straggler_seed;  /* seed of that SplitMix64 sequence */
     uint64_t *timestamps;     /* optional device array: per destination slice j, the
                                * device real-time clock at which each consumer unit
-                               * finished, at timestamps[j * units + unit] */
-    int32_t consumer_lds;     /* 1: consumers copy through LDS; 0: through registers;
-                               * -1 or 0 in a zeroed struct: default */
-    int32_t consumer_split;   /* consumer workgroups sharing one unit, each copying a
-                               * contiguous part of it (default: about one per 128 KiB) */
-    int32_t producer_batch;   /* pieces a producer copies between two release fences
-                               * (default: about 64 KiB worth, at most 16) */
-    int32_t skip_reset;       /* 1: the caller has already zeroed both signal regions
+                               * finished, at timestamps[j * tile_slots + unit] */
+    int32_t mode;             /* RA2A_MODE_DIRECT (or 0): producers store each piece
+                               * straight into its final place in out_j (a symmetric
+                               * buffer) and signal the tile; consumers only wait for
+                               * their tiles (and stamp them); no ring, no hand-back.
+                               * RA2A_MODE_STAGED: producers store into slice j's staging
+                               * ring (the pages' window layout), consumers wait, copy
+                               * ring -> out_j and hand the ring slot back. */
+    int32_t consumer_split;   /* staged mode: consumer work items sharing one unit, each
+                               * copying a contiguous part (default: one per 128 KiB) */
+    int32_t skip_reset;       /* 1: the caller has already zeroed every signal slot
                                * (ra2a_signal_reset on the same stream); no reset launch */
-    int32_t stream_batch;     /* tile streams of one XCD whose staging is live together
-                               * (default: as many as fit about 2 MiB of ring) */
+    int32_t stream_batch;     /* tile streams of one XCD in flight together (default: as
+                               * many as fit about 2 MiB of staging ring) */
     int32_t agent_sync;       /* 1: synchronise producers and consumers with device-wide
                                * release/acquire (L2 write-back / invalidate) instead of
-                               * the XCD-local protocol; also used automatically when the
-                               * device does not place workgroups on XCDs round-robin */
-    int32_t reserved[3];      /* must be zero */
+                               * the XCD-local protocol, and let every workgroup serve
+                               * every stream group */
+    int32_t head_merge;       /* signal tiles of adjacent head blocks moved together by one
+                               * piece / unit (each keeps its own signal); default, when a
+                               * tile spans all of D: runs of up to 4 KiB, halved until the
+                               * combine has at least 2048 pieces */
+    int32_t reserved[2];      /* must be zero */
 } ra2a_opts_t;
 
 /* Number of signal slots the combine needs per slice: `tile_slots` data
  * signals (region A: ADD, one per (s-block, head block, d block) in that
- * order; SET, one per (s-block, head block, d block, source r)) followed by
- * `credit_slots` ring hand-back counters (region B: ADD [ring][head block]
- * [d block]; SET [ring][head block][d block][source]).  The `signals` array
- * of a combine must hold tile_slots + credit_slots slots in every slice.
- * opts may be NULL.                                                             */
+ * order; SET, one per (s-block, head block, d block, source r)), then
+ * `credit_slots` ring hand-back counters (region B: ADD [ring slot][merged
+ * head block][d block]; SET [ring slot][merged head block][d block][source],
+ * where a merged head block is head_merge adjacent head blocks and the direct
+ * mode counts every S-block as a ring slot), then `queue_slots`
+ * (RA2A_QUEUE_SLOTS, or 0 for an empty problem) work-queue words.  The
+ * `signals` array of a combine must hold the sum of the three in every slice.
+ * opts may be NULL; any output pointer may be NULL.                          */
 int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t D, int dtype,
                                   const ra2a_opts_t *opts, int64_t *tile_slots,
-                                  int64_t *credit_slots);
+                                  int64_t *credit_slots, int64_t *queue_slots);
 
 /* Staging bytes per slice the library reserves from the heap on first use
  * (pipelined: the ring; two_phase != 0: a full (W, S, H, D) staging area).     */
 int ra2a_rev_all2all_workspace_bytes(int W, int64_t S, int64_t H, int64_t D, int dtype,
                                      const ra2a_opts_t *opts, int two_phase, size_t *bytes);
 
-/* The combine with the signal-pipelined persistent kernel and default tiling:
- * enqueues the reset of both signal regions, then one persistent launch whose
- * producer workgroups copy pieces into the destination's staging ring with
- * 16-byte stores, fence, and signal; consumer workgroups wait on their tile's
- * signal, copy staging to out_j and hand the ring slot back.  Afterwards every
- * region-A slot holds W (ADD) or 1 (SET) and every region-B slot the number of
- * S-blocks that used it.  Staging comes from the heap (see workspace_bytes).
+/* The combine with the signal-pipelined persistent kernel and default options:
+ * enqueues the reset of every signal slot, then one persistent launch.  Its
+ * workgroups take tasks from one work queue per XCD: producer pieces, which
+ * copy one source's part of a tile with 16-byte stores straight into out_j
+ * (direct mode, the default), release and signal the tile, and consumer work,
+ * which waits until the tile's signal is complete (in staged mode it then
+ * copies the staging ring into out_j and hands the ring slot back).
+ * Afterwards every region-A slot holds W (ADD) or 1 (SET) and every region-B
+ * slot the number of consumer work items that used it.  Staging (staged mode)
+ * comes from the heap (see workspace_bytes).
  * Errors: EINVAL, ENOMEM (heap too small for the staging ring), EHIP.           */
 int ra2a_rev_all2all(const void *in, void *out, uint64_t *signals, int W, int64_t S, int64_t H,
                      int64_t D, int dtype, void *stream);
@@ -272,21 +298,21 @@ int ra2a_rev_all2all_two_phase(const void *in, void *out, uint64_t *signals, int
 
 /* Wait for the device, then report and clear the heap's device error word:
  * RA2A_ETIMEOUT if a bounded wait gave up since the last check, RA2A_EHIP if
- * the device reported an error or a pipelined launch found a workgroup on
- * another XCD than the XCD-local protocol assumed (that launch's result is not
- * reliable), else RA2A_OK.                                                     */
+ * the device reported an error, else RA2A_OK.                                  */
 int ra2a_check(const ra2a_heap_t *heap);
 
 /* Host emulation of the signal-pipelined combine (no GPU needed): runs the
- * kernel's own piece / work-item address arithmetic and launch partition for a
+ * kernel's own piece / work-item address arithmetic and work queues for a
  * device of `num_cus` compute units with `blocks_per_cu` resident workgroups,
- * moving bytes between host copies of the heap in an order every wait of the
- * protocol allows.  in[r] (rank r's input) and out[j] are host arrays of
- * S*W*H*D elements; signals[j] (optional, may be NULL) receives the final
- * tile_slots + credit_slots signal values of slice j (unstrided).  Returns
- * EINVAL with a message if any access would leave its buffer, if the roles or
- * work lists do not partition the work, or if a wait could not be satisfied.
- * For checking the index arithmetic on a host; it is not a CPU fallback.      */
+ * executing each queue strictly in order on host copies of the heap.  in[r]
+ * (rank r's input) and out[j] are host arrays of S*W*H*D elements; signals[j]
+ * (optional, may be NULL) receives the final tile_slots + credit_slots +
+ * queue_slots signal values of slice j (unstrided; the queue words are not
+ * modelled and read 0).  Returns EINVAL with a message if any access would
+ * leave its buffer, if a queue does not hold every task once, or if a wait
+ * would not already hold when its task comes up in queue order (which would
+ * let the kernel deadlock).  For checking the index arithmetic on a host; it
+ * is not a CPU fallback.                                                       */
 int ra2a_debug_emulate_pipelined(const void *const *in, void *const *out,
                                  uint64_t *const *signals, int W, int64_t S, int64_t H,
                                  int64_t D, int dtype, const ra2a_opts_t *opts, int num_cus,

@@ -17,7 +17,8 @@ from typing import Optional, Sequence, Tuple
 
 __all__ = [
     "Ra2aError", "Opts", "SymmHeap", "lib", "OK", "EINVAL", "ENOMEM", "EHIP", "ETIMEOUT",
-    "EUNSUPPORTED", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
+    "EUNSUPPORTED", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "MODE_DIRECT", "MODE_STAGED",
+    "QUEUE_SLOTS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
     "CMP_LE", "SIG_STRIDE_BYTES", "DTYPES", "symm_heap_create", "symm_heap_attach",
     "symm_heap_destroy", "symm_malloc", "symm_heap_info", "symm_at", "put", "get",
     "put_with_signal", "signal_op", "wait_signal", "signal_reset", "rev_all2all",
@@ -31,6 +32,8 @@ LIB_PATH = os.path.join(HERE, "libra2a.so")
 OK, EINVAL, ENOMEM, EHIP, ETIMEOUT, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 SIG_SET, SIG_ADD = 0, 1
 PROTO_ADD, PROTO_SET = 1, 2
+MODE_DIRECT, MODE_STAGED = 1, 2
+QUEUE_SLOTS = 18
 CMP_EQ, CMP_NE, CMP_GT, CMP_GE, CMP_LT, CMP_LE = range(6)
 SIG_STRIDE_BYTES = 128
 SIG_STRIDE_U64 = 16
@@ -51,12 +54,12 @@ class Opts(ctypes.Structure):
     _fields_ = [
         ("tile_s", ctypes.c_int64), ("tile_h", ctypes.c_int64), ("tile_d", ctypes.c_int64),
         ("protocol", ctypes.c_int32), ("ring", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32),
-        ("producer_share", ctypes.c_int32), ("straggler_rank", ctypes.c_int32),
+        ("lookahead", ctypes.c_int32), ("straggler_rank", ctypes.c_int32),
         ("straggler_delay", ctypes.c_uint32), ("straggler_seed", ctypes.c_uint64),
-        ("timestamps", ctypes.c_void_p), ("consumer_lds", ctypes.c_int32),
-        ("consumer_split", ctypes.c_int32), ("producer_batch", ctypes.c_int32),
-        ("skip_reset", ctypes.c_int32), ("stream_batch", ctypes.c_int32),
-        ("agent_sync", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+        ("timestamps", ctypes.c_void_p), ("mode", ctypes.c_int32),
+        ("consumer_split", ctypes.c_int32), ("skip_reset", ctypes.c_int32),
+        ("stream_batch", ctypes.c_int32), ("agent_sync", ctypes.c_int32),
+        ("head_merge", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
     ]
 
     def __init__(self, **kw):
@@ -98,7 +101,7 @@ def lib():
         "ra2a_signal_op": (i32, [vp, vp, u64, i32, i32, vp]),
         "ra2a_wait_signal": (i32, [vp, vp, u64, i32, vp]),
         "ra2a_signal_reset": (i32, [vp, vp, i64, vp]),
-        "ra2a_rev_all2all_signal_slots": (i32, [i32, i64, i64, i64, i32, vp,
+        "ra2a_rev_all2all_signal_slots": (i32, [i32, i64, i64, i64, i32, vp, ctypes.POINTER(i64),
                                                 ctypes.POINTER(i64), ctypes.POINTER(i64)]),
         "ra2a_rev_all2all_workspace_bytes": (i32, [i32, i64, i64, i64, i32, vp, i32,
                                                    ctypes.POINTER(sz)]),
@@ -233,12 +236,15 @@ def check(heap: int) -> int:
 
 # ---- combine ------------------------------------------------------------------
 
-def rev_all2all_signal_slots(W: int, S: int, H: int, D: int, dtype, opts=None) -> Tuple[int, int]:
+def rev_all2all_signal_slots(W: int, S: int, H: int, D: int, dtype,
+                             opts=None) -> Tuple[int, int, int]:
+    """(data signals, hand-back counters, work-queue words) per slice."""
     a = ctypes.c_int64()
     b = ctypes.c_int64()
+    c = ctypes.c_int64()
     _ok(lib().ra2a_rev_all2all_signal_slots(W, S, H, D, _dtype(dtype), _opts(opts),
-                                            ctypes.byref(a), ctypes.byref(b)))
-    return a.value, b.value
+                                            ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
 
 
 def rev_all2all_workspace_bytes(W: int, S: int, H: int, D: int, dtype, opts=None,
@@ -272,12 +278,12 @@ def debug_emulate_pipelined(inputs, W: int, S: int, H: int, D: int, dtype, opts=
 
     ``inputs``: W C-contiguous numpy arrays of S*W*H*D elements.  Returns
     (outputs, signals): W output arrays shaped (S, H*W, D) and W uint64 arrays of
-    final signal values (data signals, then ring hand-back counters).
+    final signal values (data signals, ring hand-back counters, queue words).
     """
     import numpy as np
-    n_tile, n_credit = rev_all2all_signal_slots(W, S, H, D, dtype, opts)
+    n_tile, n_credit, n_queue = rev_all2all_signal_slots(W, S, H, D, dtype, opts)
     outs = [np.empty((S, H * W, D), dtype=inputs[0].dtype) for _ in range(W)]
-    sigs = [np.zeros(n_tile + n_credit, dtype=np.uint64) for _ in range(W)]
+    sigs = [np.zeros(n_tile + n_credit + n_queue, dtype=np.uint64) for _ in range(W)]
     vp = ctypes.c_void_p
     pin = (vp * W)(*[a.ctypes.data for a in inputs])
     pout = (vp * W)(*[a.ctypes.data for a in outs])

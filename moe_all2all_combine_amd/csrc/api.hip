@@ -129,12 +129,14 @@ int lowbit_vec(uint64_t m) {
 struct Plan {
     int64_t BS, TH, TD;
     int nbs, nhb, ndb, R;
+    int MH, nmhb;           // head blocks moved together, merged head blocks
     int protocol;
     int64_t regionA, regionB;
     int64_t ring_bytes;     // staging ring bytes per slice
-    int csplit, pbatch, wg_per_cu, pshare;
+    int csplit, wg_per_cu, lookahead;
     int stream_batch;       // 0 = derive from the L2 budget
     int agent_sync;
+    int direct;             // 1: direct push (no staging), 0: staged through the ring
     int64_t piece_bytes, unit_bytes, tile_bytes;
 };
 
@@ -143,8 +145,10 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     std::memset(&z, 0, sizeof z);
     z.straggler_rank = -1;
     if (!o) o = &z;
-    for (int i = 0; i < 3; ++i)
-        if (o->reserved[i]) return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
+    if (o->reserved[0] || o->reserved[1])
+        return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
+    if (o->mode != 0 && o->mode != RA2A_MODE_DIRECT && o->mode != RA2A_MODE_STAGED)
+        return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_DIRECT or RA2A_MODE_STAGED");
     p->BS = o->tile_s > 0 ? o->tile_s : std::min<int64_t>(S, 64);
     p->TH = o->tile_h > 0 ? o->tile_h : 1;
     p->TD = o->tile_d > 0 ? o->tile_d : D;
@@ -160,31 +164,51 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     p->nhb = (int)cdiv(H, p->TH);
     p->ndb = (int)cdiv(D, p->TD);
     if (o->ring < 0) return fail(RA2A_EINVAL, "ring depth must be >= 0");
-    int R = o->ring > 0 ? o->ring : 2;
+    int R = o->ring > 0 ? o->ring : 8;
     p->R = std::max(1, std::min(R, std::max(p->nbs, 1)));
+    if (o->head_merge < 0) return fail(RA2A_EINVAL, "head_merge must be >= 0");
+    if (o->head_merge > 0) {
+        p->MH = std::min(o->head_merge, p->nhb);
+    } else if (p->TD == D) {
+        // adjacent head blocks are contiguous: merge up to ~4 KiB runs, but keep at
+        // least kMinPieces pieces so that every persistent workgroup gets several
+        constexpr int64_t kMinPieces = 2048;
+        int64_t mh = std::max<int64_t>(1, std::min<int64_t>(p->nhb, 4096 / std::max<int64_t>(1, p->TH * D * e)));
+        const int64_t per_mh = (int64_t)W * p->nbs * W;  // pieces per merged head block
+        while (mh > 1 && per_mh * cdiv(p->nhb, mh) < kMinPieces) mh /= 2;
+        p->MH = (int)mh;
+    } else {
+        p->MH = 1;
+    }
+    p->nmhb = (p->nhb + p->MH - 1) / p->MH;
     const int64_t perW = p->protocol == RA2A_SIG_SET ? W : 1;
     p->regionA = (int64_t)p->nbs * p->nhb * p->ndb * perW;
-    p->regionB = (int64_t)p->R * p->nhb * p->ndb * perW;
+    p->regionB = (int64_t)p->R * p->nmhb * p->ndb * perW;
     p->ring_bytes = (int64_t)p->R * p->BS * H * W * D * e;
-    p->piece_bytes = p->BS * p->TH * p->TD * e;
+    p->piece_bytes = p->BS * std::min<int64_t>((int64_t)p->MH * p->TH, H) * p->TD * e;
     p->tile_bytes = p->piece_bytes * W;  // one S-block of one stream, all sources
     if (o->stream_batch < 0) return fail(RA2A_EINVAL, "stream_batch must be >= 0");
     p->stream_batch = o->stream_batch;
     p->agent_sync = o->agent_sync ? 1 : 0;
+    p->direct = o->mode == RA2A_MODE_STAGED ? 0 : 1;
     p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);
-    if (o->consumer_split < 0 || o->producer_batch < 0 || o->wg_per_cu < 0 ||
-        o->producer_share < 0)
+    if (o->consumer_split < 0 || o->wg_per_cu < 0 || o->lookahead < -1)
         return fail(RA2A_EINVAL, "negative option");
     p->csplit = o->consumer_split > 0
                     ? o->consumer_split
                     : (int)std::max<int64_t>(1, std::min<int64_t>(64, p->unit_bytes / (128 << 10)));
-    p->pbatch = o->producer_batch > 0
-                    ? o->producer_batch
-                    : (int)std::max<int64_t>(1, std::min<int64_t>(16, (64 << 10) / std::max<int64_t>(p->piece_bytes, 1)));
-    if (p->pbatch > ra2a::kThreads) return fail(RA2A_EINVAL, "producer_batch must be <= 256");
+    if (p->direct) {
+        // no staging: no ring to reuse (R = every S-block), one part per unit
+        p->R = std::max(p->nbs, 1);
+        p->regionB = (int64_t)p->R * p->nmhb * p->ndb * perW;
+        p->ring_bytes = 0;
+        p->csplit = 1;
+    }
     p->wg_per_cu = o->wg_per_cu > 0 ? o->wg_per_cu : 2;
-    p->pshare = o->producer_share > 0 ? o->producer_share : 2;
-    if (p->pshare > 3) return fail(RA2A_EINVAL, "producer_share must be 1..3");
+    p->lookahead = o->lookahead;
+    // the kernels index tiles, pieces and work items with 32-bit arithmetic
+    const double tasks = (double)W * p->nbs * p->nhb * p->ndb * ((double)W + p->csplit * W);
+    if (tasks >= 2147483647.0 - 65536.0) return fail(RA2A_EINVAL, "too many tiles");
     // per-launch index arithmetic uses 32-bit vector counts inside one unit
     if (p->unit_bytes >= (int64_t(1) << 31) - 65536) return fail(RA2A_EINVAL, "tile too large");
     // consumers address the staging ring with 32-bit buffer offsets
@@ -297,7 +321,7 @@ int gcd_int(int a, int b) {
 int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan& pl,
                       const ra2a_opts_t* opts, int64_t stride, size_t in_off, size_t out_off,
                       size_t stg_off, size_t sig_off, int ncu, int blocks_per_cu, int nxcd,
-                      bool round_robin, ra2a::PipeArgs* a, int* V, int* grid) {
+                      ra2a::PipeArgs* a, int* V, int* grid) {
     *a = ra2a::PipeArgs{};
     a->stride = stride;
     a->in_off = (int64_t)in_off;
@@ -315,18 +339,17 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     a->nbs = pl.nbs;
     a->nhb = pl.nhb;
     a->ndb = pl.ndb;
+    a->MH = pl.MH;
+    a->nmhb = pl.nmhb;
     a->R = pl.R;
     a->protocol = pl.protocol;
-    const int nstreams = W * pl.nhb * pl.ndb;
+    const int nstreams = W * pl.nmhb * pl.ndb;
     const int per_cu = std::max(1, std::min(blocks_per_cu, pl.wg_per_cu));
-    a->q = 4;
-    // one stream group per XCD (fewer on a device too small for that many)
-    a->NG = std::max(1, nxcd);
-    while (a->NG > 1 && a->NG * a->q > per_cu * ncu) a->NG /= 2;
+    // one stream group (and work queue) per XCD
+    a->NG = std::max(1, std::min(nxcd, ra2a::kNumXcd));
     a->nstreams = nstreams;
-    // XCD-local synchronisation needs group g == XCD of every workgroup w with
-    // w mod NG == g: the dispatcher's round-robin placement over all XCDs
-    a->sync = (!pl.agent_sync && round_robin && a->NG == nxcd) ? ra2a::kSyncXcd : ra2a::kSyncAgent;
+    // XCD-local sync needs one group per XCD (XCC_ID mod NG must identify the XCD)
+    a->sync = (pl.agent_sync || nxcd > ra2a::kNumXcd) ? ra2a::kSyncAgent : ra2a::kSyncXcd;
     {
         const int ns_max = (nstreams + a->NG - 1) / a->NG;
         int kb = pl.stream_batch;
@@ -336,11 +359,12 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
         }
         a->KB = std::max(1, std::min(kb, ns_max));
     }
-    a->p = pl.pshare;
-    a->pbatch = pl.pbatch;
     a->csplit = pl.csplit;
+    a->lookahead = pl.lookahead;
     a->regionA = pl.regionA;
+    a->regionB = pl.regionB;
     a->ring_bytes = pl.ring_bytes;
+    a->direct = pl.direct;
     a->straggler = opts ? opts->straggler_rank : -1;
     a->delay = opts ? opts->straggler_delay : 0;
     a->seed = opts ? opts->straggler_seed : 0;
@@ -348,32 +372,25 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     // vector width: every offset, stride and run is a multiple of it
     const uint64_t m = (uint64_t)(D * e0) | (uint64_t)(pl.TD * e0) | in_off | out_off | stg_off;
     *V = lowbit_vec(m);
-    const int unit = a->NG * a->q;
-    *grid = (per_cu * ncu) / unit * unit;
-    if (*grid < unit) return fail(RA2A_EUNSUPPORTED, "device too small for %d workgroups", unit);
-    const int periods = *grid / unit;
-    a->nprod = a->p * periods;
-    a->ncons = (a->q - a->p) * periods;
+    *grid = per_cu * ncu;
+    if (*grid < 1) return fail(RA2A_EUNSUPPORTED, "no compute units");
     return RA2A_OK;
 }
 
-// Number of XCDs of the current device and whether the dispatcher places
-// workgroup w on XCD w mod nxcd, measured once per device with a probe launch.
-int xcd_layout(int* nxcd, bool* round_robin) {
+// Number of XCDs of the current device (the largest XCC_ID a probe launch of
+// 4096 workgroups observed, plus one), measured once per device.
+int xcd_count(int* nxcd) {
     static std::mutex mu;
     static int cached_n[64];
-    static signed char cached_rr[64];
-    static bool have[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (dev < 0 || dev >= 64) {
         *nxcd = 1;
-        *round_robin = false;
         return RA2A_OK;
     }
     std::lock_guard<std::mutex> g(mu);
-    if (!have[dev]) {
+    if (!cached_n[dev]) {
         const int n = 4096;
         uint32_t* d = nullptr;
         e = hipMalloc(&d, n * sizeof(uint32_t));
@@ -383,18 +400,12 @@ int xcd_layout(int* nxcd, bool* round_robin) {
         std::vector<uint32_t> h(n, 0);
         if (e == hipSuccess) e = hipMemcpy(h.data(), d, n * sizeof(uint32_t), hipMemcpyDeviceToHost);
         (void)hipFree(d);
-        if (e != hipSuccess) return hip_fail(e, "XCD placement probe");
+        if (e != hipSuccess) return hip_fail(e, "XCD probe");
         uint32_t mx = 0;
         for (uint32_t v : h) mx = std::max(mx, v);
-        const int cnt = (int)mx + 1;
-        bool rr = true;
-        for (int w = 0; w < n; ++w) rr = rr && h[w] == (uint32_t)(w % cnt);
-        cached_n[dev] = cnt;
-        cached_rr[dev] = rr ? 1 : 0;
-        have[dev] = true;
+        cached_n[dev] = (int)mx + 1;
     }
     *nxcd = cached_n[dev];
-    *round_robin = cached_rr[dev] != 0;
     return RA2A_OK;
 }
 
@@ -412,14 +423,16 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     }
     Checked c{};
     int rc = check_combine(in, out, signals, W, S, H, D, dtype,
-                           empty ? 0 : pl.regionA + pl.regionB, &c);
+                           empty ? 0 : pl.regionA + pl.regionB + ra2a::kQueueSlots, &c);
     if (rc) return rc;
     if (empty) return ok();
     if (opts && (opts->straggler_rank < -1 || opts->straggler_rank >= W))
         return fail(RA2A_EINVAL, "straggler_rank out of range");
     size_t stg = 0;
-    rc = staging(c.h, false, (size_t)pl.ring_bytes, &stg);
-    if (rc) return rc;
+    if (!pl.direct) {
+        rc = staging(c.h, false, (size_t)pl.ring_bytes, &stg);
+        if (rc) return rc;
+    }
     rc = ensure_err(c.h);
     if (rc) return rc;
 
@@ -427,18 +440,17 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     rc = device_cus(&ncu);
     if (rc) return rc;
     int nxcd = 1;
-    bool rr = false;
-    rc = xcd_layout(&nxcd, &rr);
+    rc = xcd_count(&nxcd);
     if (rc) return rc;
     const uint64_t m = (uint64_t)(D * e0) | (uint64_t)(pl.TD * e0) | c.in_off | c.out_off | stg;
-    const int sync_guess = (!pl.agent_sync && rr) ? ra2a::kSyncXcd : ra2a::kSyncAgent;
     int occ = 0;
-    hipError_t he = ra2a::pipelined_blocks_per_cu(lowbit_vec(m), sync_guess, &occ);
+    hipError_t he = ra2a::pipelined_blocks_per_cu(
+        lowbit_vec(m), pl.agent_sync ? ra2a::kSyncAgent : ra2a::kSyncXcd, pl.direct, &occ);
     if (he != hipSuccess) return hip_fail(he, "occupancy query");
     ra2a::PipeArgs a{};
     int V = 16, grid = 0;
     rc = prepare_pipelined(W, S, H, D, e0, pl, opts, (int64_t)c.h->stride, c.in_off, c.out_off,
-                           stg, c.sig_off, ncu, occ, nxcd, rr, &a, &V, &grid);
+                           stg, c.sig_off, ncu, occ, nxcd, &a, &V, &grid);
     if (rc) return rc;
     a.base = c.h->base;
     a.err = c.h->err;
@@ -448,7 +460,7 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!(opts && opts->skip_reset)) {
         he = ra2a::launch_signal_reset(c.h->base, (int64_t)c.h->stride, W, (int64_t)c.sig_off,
-                                       pl.regionA + pl.regionB, st);
+                                       pl.regionA + pl.regionB + ra2a::kQueueSlots, st);
         if (he != hipSuccess) return hip_fail(he, "signal reset launch");
     }
     if (opts && opts->timestamps) {
@@ -699,7 +711,7 @@ RA2A_API int ra2a_signal_reset(const ra2a_heap_t* h, uint64_t* sig_sym, int64_t 
 
 RA2A_API int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t D, int dtype,
                                            const ra2a_opts_t* opts, int64_t* tile_slots,
-                                           int64_t* credit_slots) {
+                                           int64_t* credit_slots, int64_t* queue_slots) {
     const int e = elem_bytes(dtype);
     if (!e) return fail(RA2A_EINVAL, "unknown dtype %d", dtype);
     if (W < 1 || S < 0 || H < 0 || D < 0) return fail(RA2A_EINVAL, "bad dimensions");
@@ -713,6 +725,7 @@ RA2A_API int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t 
     }
     if (tile_slots) *tile_slots = a;
     if (credit_slots) *credit_slots = b;
+    if (queue_slots) *queue_slots = (a + b) > 0 ? ra2a::kQueueSlots : 0;
     return ok();
 }
 
@@ -791,9 +804,6 @@ RA2A_API int ra2a_check(const ra2a_heap_t* h) {
     if (w) {
         e = hipMemset(h->err, 0, sizeof w);
         if (e != hipSuccess) return hip_fail(e, "clearing the error word");
-        if (w & ra2a::kErrPlacement)
-            return fail(RA2A_EHIP, "a pipelined launch ran a workgroup on another XCD than the "
-                        "XCD-local protocol assumed; its result is unreliable (error word 0x%x)", w);
         return fail(RA2A_ETIMEOUT, "a bounded device-side wait timed out (error word 0x%x)", w);
     }
     return ok();
@@ -801,10 +811,38 @@ RA2A_API int ra2a_check(const ra2a_heap_t* h) {
 
 RA2A_API const char* ra2a_last_error(void) { return g_err.c_str(); }
 
-RA2A_API int ra2a_version(void) { return 100; }
+RA2A_API int ra2a_version(void) { return 200; }
 
 // ===========================================================================
 // host emulation of the pipelined combine's address arithmetic
+
+namespace {
+
+// The offsets of vectors [lo, hi) of a row plan as the kernels' threads walk
+// them (thread t: lo + t, lo + t + 256, ... with a cursor), each checked against
+// the direct decomposition of its index.
+int walk_plan(const ra2a::RowPlan& p, int V, int lo, int hi,
+              std::vector<std::pair<int64_t, int64_t>>* out) {
+    out->clear();
+    if (hi <= lo) return RA2A_OK;
+    const int vpr = p.run / V;
+    if (vpr < 1 || p.run % V) return fail(RA2A_EINVAL, "row of %d bytes is not a multiple of %d", p.run, V);
+    for (int t = 0; t < ra2a::kThreads && lo + t < hi; ++t) {
+        ra2a::PlanCursor c = ra2a::cursor_start(p, V, vpr, (uint32_t)(lo + t), ra2a::kThreads);
+        for (int idx = lo + t; idx < hi; idx += ra2a::kThreads) {
+            int64_t so, dofs;
+            ra2a::plan_offsets(p, V, vpr, (uint32_t)idx, &so, &dofs);
+            if (so != c.so || dofs != c.dofs)
+                return fail(RA2A_EINVAL, "cursor at vector %d: (%lld, %lld), direct (%lld, %lld)", idx,
+                            (long long)c.so, (long long)c.dofs, (long long)so, (long long)dofs);
+            out->push_back({so, dofs});
+            ra2a::cursor_advance(c, p, vpr);
+        }
+    }
+    return RA2A_OK;
+}
+
+}  // namespace
 
 RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* out,
                                           uint64_t* const* signals, int W, int64_t S, int64_t H,
@@ -821,14 +859,14 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
     const int64_t nb = S * (int64_t)W * H * D * e0;
     const int64_t in_off = 0, out_off = al(nb), stg_off = al(out_off + nb);
     const int64_t sig_off = al(stg_off + pl.ring_bytes);
-    const int64_t nsig = pl.regionA + pl.regionB;
+    const int64_t nsig = pl.regionA + pl.regionB + ra2a::kQueueSlots;
     const int64_t stride = al(sig_off + nsig * RA2A_SIG_STRIDE_BYTES);
     if ((double)stride * W > 16.0e9) return fail(RA2A_EINVAL, "too large to emulate");
     ra2a::PipeArgs a{};
     int V = 16, grid = 0;
     rc = prepare_pipelined(W, S, H, D, e0, pl, opts, stride, (size_t)in_off, (size_t)out_off,
                            (size_t)stg_off, (size_t)sig_off, num_cus, blocks_per_cu,
-                           ra2a::kNumXcd, true, &a, &V, &grid);
+                           ra2a::kNumXcd, &a, &V, &grid);
     if (rc) return rc;
     std::vector<uint8_t> heap((size_t)(stride * W), 0xCD);
     for (int r = 0; r < W; ++r) {
@@ -841,45 +879,6 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
         return off >= lo && off + len <= lo + rlen;
     };
 
-    // roles: every (group, index) pair exactly once
-    std::vector<int> seen_p((size_t)a.NG * a.nprod, 0), seen_c((size_t)a.NG * a.ncons, 0);
-    for (int wg = 0; wg < grid; ++wg) {
-        const ra2a::Role ro = ra2a::role_of(a, wg);
-        if (ro.g < 0 || ro.g >= a.NG) return fail(RA2A_EINVAL, "workgroup %d: bad group", wg);
-        if (ro.producer) {
-            if (ro.index < 0 || ro.index >= a.nprod) return fail(RA2A_EINVAL, "bad producer index");
-            seen_p[(size_t)ro.g * a.nprod + ro.index]++;
-        } else {
-            if (ro.index < 0 || ro.index >= a.ncons) return fail(RA2A_EINVAL, "bad consumer index");
-            seen_c[(size_t)ro.g * a.ncons + ro.index]++;
-        }
-    }
-    for (int x : seen_p)
-        if (x != 1) return fail(RA2A_EINVAL, "producer roles do not partition the grid");
-    for (int x : seen_c)
-        if (x != 1) return fail(RA2A_EINVAL, "consumer roles do not partition the grid");
-
-    // work lists exactly as the kernel walks them: every piece / item exactly once
-    const bool add = a.protocol == ra2a::kSigAdd;
-    for (int g = 0; g < a.NG; ++g) {
-        const int64_t npieces = ra2a::group_pieces(a, g);
-        const int64_t nitems = ra2a::group_items(a, g);
-        std::vector<uint8_t> cov((size_t)npieces, 0);
-        for (int i = 0; i < a.nprod; ++i)
-            for (int64_t first = (int64_t)i * a.pbatch; first < npieces;
-                 first += (int64_t)a.nprod * a.pbatch)
-                for (int64_t pc = first; pc < std::min(first + (int64_t)a.pbatch, npieces); ++pc)
-                    cov[(size_t)pc]++;
-        for (uint8_t x : cov)
-            if (x != 1) return fail(RA2A_EINVAL, "producer work lists do not partition the pieces");
-        std::vector<uint8_t> covi((size_t)nitems, 0);
-        for (int i = 0; i < a.ncons; ++i)
-            for (int64_t it = i; it < nitems; it += a.ncons) covi[(size_t)it]++;
-        for (uint8_t x : covi)
-            if (x != 1) return fail(RA2A_EINVAL, "consumer work lists do not partition the items");
-        // each workgroup's list must be in non-decreasing S-block order per stream
-        // (the deadlock-freedom argument); tile order already guarantees it within a stream
-    }
     {
         // every stream belongs to exactly one group
         std::vector<int> own((size_t)a.nstreams, 0);
@@ -891,81 +890,96 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
             if (x != 1) return fail(RA2A_EINVAL, "stream groups do not partition the streams");
     }
 
-    // data movement in an order every wait allows: S-block by S-block, producers first
+    // Each group's queue run strictly in queue order, one task at a time: every
+    // wait must already hold when its task comes up (the kernel's deadlock-
+    // freedom argument), and the queue must hold every piece and item once.
+    const bool add = a.protocol == ra2a::kSigAdd;
     const int64_t sigA_len = pl.regionA * RA2A_SIG_STRIDE_BYTES;
-    std::vector<std::vector<std::pair<int, int64_t>>> pieces_at((size_t)a.nbs), items_at((size_t)a.nbs);
     for (int g = 0; g < a.NG; ++g) {
+        const ra2a::GroupQueue Q = ra2a::group_queue(a, g);
         const int64_t npieces = ra2a::group_pieces(a, g);
-        for (int64_t pc = 0; pc < npieces; ++pc) {
-            const ra2a::Piece p = ra2a::piece_of(a, g, pc);
-            if (p.b < 0 || p.b >= a.nbs) return fail(RA2A_EINVAL, "piece S-block out of range");
-            pieces_at[(size_t)p.b].push_back({g, pc});
-        }
         const int64_t nitems = ra2a::group_items(a, g);
-        for (int64_t it = 0; it < nitems; ++it) {
-            const ra2a::Item q = ra2a::item_of(a, g, it, V);
-            if (q.b < 0 || q.b >= a.nbs) return fail(RA2A_EINVAL, "item S-block out of range");
-            items_at[(size_t)q.b].push_back({g, it});
-        }
-    }
-    for (int b = 0; b < a.nbs; ++b) {
-        for (auto& gp : pieces_at[(size_t)b]) {
-            const int g = gp.first;
-            const int64_t pc = gp.second;
-            const ra2a::Piece p = ra2a::piece_of(a, g, pc);
-            if (p.b >= a.R) {
-                if (!inside(p.credit, 8, p.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
-                    return fail(RA2A_EINVAL, "piece credit slot outside region B");
-                if (*u64(p.credit) < p.credit_need)
-                    return fail(RA2A_EINVAL, "piece (g=%d, pc=%lld) would wait for a hand-back "
-                                "that never comes (%llu < %llu)", g, (long long)pc,
-                                (unsigned long long)*u64(p.credit),
-                                (unsigned long long)p.credit_need);
+        if (Q.total != npieces + nitems || Q.L < 0 || Q.L > Q.ntiles)
+            return fail(RA2A_EINVAL, "group %d: queue of %lld tasks for %lld pieces and %lld items",
+                        g, (long long)Q.total, (long long)npieces, (long long)nitems);
+        std::vector<uint8_t> cov_p((size_t)npieces, 0), cov_i((size_t)nitems, 0);
+        for (int64_t pos = 0; pos < Q.total; ++pos) {
+            int64_t idx = -1;
+            if (ra2a::task_of(Q, pos, &idx)) {
+                if (idx < 0 || idx >= npieces) return fail(RA2A_EINVAL, "queue piece out of range");
+                cov_p[(size_t)idx]++;
+                const ra2a::Piece p = ra2a::piece_of(a, g, idx);
+                if (p.b < 0 || p.b >= a.nbs) return fail(RA2A_EINVAL, "piece S-block out of range");
+                if (p.b >= a.R) {
+                    if (!inside(p.credit, 8, p.j, sig_off + sigA_len,
+                                pl.regionB * RA2A_SIG_STRIDE_BYTES))
+                        return fail(RA2A_EINVAL, "piece credit slot outside region B");
+                    if (*u64(p.credit) < p.credit_need)
+                        return fail(RA2A_EINVAL, "group %d position %lld: piece %lld waits for a "
+                                    "hand-back queued after it (%llu < %llu)", g, (long long)pos,
+                                    (long long)idx, (unsigned long long)*u64(p.credit),
+                                    (unsigned long long)p.credit_need);
+                }
+                const int nv = ra2a::plan_vectors(p.pl, V);
+                std::vector<std::pair<int64_t, int64_t>> offs;
+                rc = walk_plan(p.pl, V, 0, nv, &offs);
+                if (rc) return rc;
+                for (const auto& o : offs) {
+                    const int64_t so = o.first, dofs = o.second;
+                    if (!inside(p.src + so, V, p.r, in_off, nb))
+                        return fail(RA2A_EINVAL, "piece reads outside in of rank %d", p.r);
+                    if (pl.direct ? !inside(p.dst + dofs, V, p.j, out_off, nb)
+                                  : !inside(p.dst + dofs, V, p.j, stg_off, pl.ring_bytes))
+                        return fail(RA2A_EINVAL, "piece writes outside its destination of rank %d",
+                                    p.j);
+                    std::memcpy(&heap[(size_t)(p.dst + dofs)], &heap[(size_t)(p.src + so)],
+                                (size_t)V);
+                }
+                for (int k = 0; k < p.nsig; ++k) {
+                    const int64_t sg = p.sig + k * p.sig_step;
+                    if (!inside(sg, 8, p.j, sig_off, sigA_len))
+                        return fail(RA2A_EINVAL, "piece signal outside region A");
+                    if (add)
+                        *u64(sg) += 1;
+                    else
+                        *u64(sg) = 1;
+                }
+            } else {
+                if (idx < 0 || idx >= nitems) return fail(RA2A_EINVAL, "queue item out of range");
+                cov_i[(size_t)idx]++;
+                const ra2a::Item q = ra2a::item_of(a, g, idx, V);
+                if (q.b < 0 || q.b >= a.nbs) return fail(RA2A_EINVAL, "item S-block out of range");
+                for (int k = 0; k < q.nsig; ++k) {
+                    const int64_t sg = q.sig + k * q.sig_step;
+                    if (!inside(sg, 8, q.j, sig_off, sigA_len))
+                        return fail(RA2A_EINVAL, "item signal outside region A");
+                    if (*u64(sg) != q.sig_want)
+                        return fail(RA2A_EINVAL, "group %d position %lld: item %lld waits for "
+                                    "pieces queued after it (signal %llu, wants %llu)", g,
+                                    (long long)pos, (long long)idx,
+                                    (unsigned long long)*u64(sg), (unsigned long long)q.sig_want);
+                }
+                std::vector<std::pair<int64_t, int64_t>> offs;
+                rc = walk_plan(q.pl, V, q.lo, q.hi, &offs);
+                if (rc) return rc;
+                for (const auto& o : offs) {
+                    const int64_t so = o.first, dofs = o.second;
+                    if (!inside(q.src + so, V, q.j, stg_off, pl.ring_bytes))
+                        return fail(RA2A_EINVAL, "item reads outside the staging of rank %d", q.j);
+                    if (!inside(q.dst + dofs, V, q.j, out_off, nb))
+                        return fail(RA2A_EINVAL, "item writes outside out of rank %d", q.j);
+                    std::memcpy(&heap[(size_t)(q.dst + dofs)], &heap[(size_t)(q.src + so)],
+                                (size_t)V);
+                }
+                if (!inside(q.credit, 8, q.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
+                    return fail(RA2A_EINVAL, "item credit slot outside region B");
+                *u64(q.credit) += 1;
             }
-            const int vpr = p.pl.run / V;
-            const int BC = p.pl.B * p.pl.C;
-            const int nv = ra2a::plan_vectors(p.pl, V);
-            for (int v = 0; v < nv; ++v) {
-                int64_t so, dofs;
-                ra2a::plan_offsets(p.pl, V, vpr, BC, v, &so, &dofs);
-                if (!inside(p.src + so, V, p.r, in_off, nb))
-                    return fail(RA2A_EINVAL, "piece reads outside in of rank %d", p.r);
-                if (!inside(p.dst + dofs, V, p.j, stg_off, pl.ring_bytes))
-                    return fail(RA2A_EINVAL, "piece writes outside the staging of rank %d", p.j);
-                std::memcpy(&heap[(size_t)(p.dst + dofs)], &heap[(size_t)(p.src + so)], (size_t)V);
-            }
-            if (!inside(p.sig, 8, p.j, sig_off, sigA_len))
-                return fail(RA2A_EINVAL, "piece signal outside region A");
-            if (add)
-                *u64(p.sig) += 1;
-            else
-                *u64(p.sig) = 1;
         }
-        for (auto& gi : items_at[(size_t)b]) {
-            const int g = gi.first;
-            const int64_t it = gi.second;
-            const ra2a::Item q = ra2a::item_of(a, g, it, V);
-            if (!inside(q.sig, 8, q.j, sig_off, sigA_len))
-                return fail(RA2A_EINVAL, "item signal outside region A");
-            if (*u64(q.sig) != q.sig_want)
-                return fail(RA2A_EINVAL, "item (g=%d, it=%lld) would wait forever: signal %llu, "
-                            "wants %llu", g, (long long)it, (unsigned long long)*u64(q.sig),
-                            (unsigned long long)q.sig_want);
-            const int vpr = q.pl.run / V;
-            const int BC = q.pl.B * q.pl.C;
-            for (int v = q.lo; v < q.hi; ++v) {
-                int64_t so, dofs;
-                ra2a::plan_offsets(q.pl, V, vpr, BC, v, &so, &dofs);
-                if (!inside(q.src + so, V, q.j, stg_off, pl.ring_bytes))
-                    return fail(RA2A_EINVAL, "item reads outside the staging of rank %d", q.j);
-                if (!inside(q.dst + dofs, V, q.j, out_off, nb))
-                    return fail(RA2A_EINVAL, "item writes outside out of rank %d", q.j);
-                std::memcpy(&heap[(size_t)(q.dst + dofs)], &heap[(size_t)(q.src + so)], (size_t)V);
-            }
-            if (!inside(q.credit, 8, q.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
-                return fail(RA2A_EINVAL, "item credit slot outside region B");
-            *u64(q.credit) += 1;
-        }
+        for (uint8_t x : cov_p)
+            if (x != 1) return fail(RA2A_EINVAL, "group %d: queue does not hold every piece once", g);
+        for (uint8_t x : cov_i)
+            if (x != 1) return fail(RA2A_EINVAL, "group %d: queue does not hold every item once", g);
     }
     for (int j = 0; j < W; ++j) {
         std::memcpy(out[j], &heap[(size_t)(j * stride + out_off)], (size_t)nb);

@@ -24,23 +24,43 @@ namespace ra2a {
 
 RA2A_HD int64_t geom_min(int64_t a, int64_t b) { return a < b ? a : b; }
 
+// A tile stream: the S-blocks b = 0 .. nbs-1 of destination j, merged head
+// block mhb (signal head blocks [hb0, hb0 + nh)), d block db.  Its data moves
+// in pieces / units spanning all nh signal tiles at once (their heads are
+// adjacent in the input, the staging ring and the output), while each signal
+// tile keeps its own signal.
 struct Stream {
-    int32_t j, hb, db;
+    int32_t j, mhb, db, hb0, nh;
     int64_t h0, th, d0, td;
 };
 
-// Stream sid = (j * nhb + hb) * ndb + db: destination j, head block hb, d block db.
+// Stream sid = (j * nmhb + mhb) * ndb + db.  (32-bit index arithmetic: the
+// host keeps every count of tiles, pieces and items below 2^31.)
 RA2A_HD Stream stream_of(const PipeArgs& a, int sid) {
     Stream s;
-    s.db = sid % a.ndb;
-    const int t = sid / a.ndb;
-    s.hb = t % a.nhb;
-    s.j = t / a.nhb;
-    s.h0 = (int64_t)s.hb * a.TH;
-    s.th = geom_min(a.TH, a.H - s.h0);
+    const uint32_t usid = (uint32_t)sid;
+    const uint32_t t = usid / (uint32_t)a.ndb;
+    s.db = (int)(usid - t * (uint32_t)a.ndb);
+    s.j = (int)(t / (uint32_t)a.nmhb);
+    s.mhb = (int)(t - (uint32_t)s.j * (uint32_t)a.nmhb);
+    s.hb0 = s.mhb * a.MH;
+    s.nh = (int)geom_min(a.MH, a.nhb - s.hb0);
+    s.h0 = (int64_t)s.hb0 * a.TH;
+    s.th = geom_min((int64_t)s.nh * a.TH, a.H - s.h0);
     s.d0 = (int64_t)s.db * a.TD;
     s.td = geom_min(a.TD, a.D - s.d0);
     return s;
+}
+
+// Signal slots of the signal tiles (b, hb0 .. hb0+nh-1, db) (and source r under
+// SET): byte offset of the first slot inside slice j's signal array and the
+// distance between consecutive head blocks' slots.
+RA2A_HD int64_t tile_slot(const PipeArgs& a, int b, int hb, int db, int r) {
+    int64_t si = ((int64_t)b * a.nhb + hb) * a.ndb + db;
+    return a.protocol == kSigAdd ? si : si * a.W + r;
+}
+RA2A_HD int64_t slot_step(const PipeArgs& a) {
+    return (int64_t)a.ndb * (a.protocol == kSigAdd ? 1 : a.W);
 }
 
 // A block of rows: row i (0 <= i < A*B*C) is (ia, ib, ic) and holds `run` bytes
@@ -54,17 +74,92 @@ struct RowPlan {
 
 RA2A_HD int plan_vectors(const RowPlan& p, int V) { return p.A * p.B * p.C * (p.run / V); }
 
+// Digits of vector index idx in the plan's mixed radix: idx = ((ia * B + ib) *
+// C + ic) * vpr + col, with vpr = run / V vectors per row.
+struct PlanDigits {
+    int col, ic, ib, ia;
+};
+
+RA2A_HD PlanDigits plan_digits(const RowPlan& p, int vpr, uint32_t idx) {
+    PlanDigits d;
+    const uint32_t row = idx / (uint32_t)vpr;
+    d.col = (int)(idx - row * (uint32_t)vpr);
+    const uint32_t BC = (uint32_t)p.B * (uint32_t)p.C;
+    d.ia = (int)(row / BC);
+    const uint32_t rem = row - (uint32_t)d.ia * BC;
+    d.ib = (int)(rem / (uint32_t)p.C);
+    d.ic = (int)(rem - (uint32_t)d.ib * (uint32_t)p.C);
+    return d;
+}
+
 // Byte offsets (source, destination) of vector `idx` of a row plan.
-RA2A_HD void plan_offsets(const RowPlan& p, int V, int vpr, int BC, int idx, int64_t* so,
+RA2A_HD void plan_offsets(const RowPlan& p, int V, int vpr, uint32_t idx, int64_t* so,
                           int64_t* dofs) {
-    const int row = idx / vpr;
-    const int col = idx - row * vpr;
-    const int ia = row / BC;
-    const int rem = row - ia * BC;
-    const int ib = rem / p.C;
-    const int ic = rem - ib * p.C;
-    *so = ia * p.sa + ib * p.sb + ic * p.sc + (int64_t)col * V;
-    *dofs = ia * p.da + ib * p.db + ic * p.dc + (int64_t)col * V;
+    const PlanDigits d = plan_digits(p, vpr, idx);
+    *so = d.ia * p.sa + d.ib * p.sb + d.ic * p.sc + (int64_t)d.col * V;
+    *dofs = d.ia * p.da + d.ib * p.db + d.ic * p.dc + (int64_t)d.col * V;
+}
+
+// Walks the vectors idx, idx + step, idx + 2 step, ... of a row plan and keeps
+// their source / destination offsets with additions and carries only (the
+// divisions happen once, in cursor_start).
+struct PlanCursor {
+    int col, ic, ib;            // digits of the current vector (ia lives in the offsets)
+    int scol, sic, sib;         // digits of the step
+    int64_t so, dofs;           // offsets of the current vector
+    int64_t dso, ddo;           // offsets added by one step before carries
+    int64_t cso1, cdo1;         // carry col -> ic
+    int64_t cso2, cdo2;         // carry ic -> ib
+    int64_t cso3, cdo3;         // carry ib -> ia
+};
+
+RA2A_HD PlanCursor cursor_start(const RowPlan& p, int V, int vpr, uint32_t idx, uint32_t step) {
+    PlanCursor c;
+    const PlanDigits at = plan_digits(p, vpr, idx);
+    const PlanDigits st = plan_digits(p, vpr, step);
+    c.col = at.col;
+    c.ic = at.ic;
+    c.ib = at.ib;
+    c.scol = st.col;
+    c.sic = st.ic;
+    c.sib = st.ib;
+    c.so = at.ia * p.sa + at.ib * p.sb + at.ic * p.sc + (int64_t)at.col * V;
+    c.dofs = at.ia * p.da + at.ib * p.db + at.ic * p.dc + (int64_t)at.col * V;
+    c.dso = st.ia * p.sa + st.ib * p.sb + st.ic * p.sc + (int64_t)st.col * V;
+    c.ddo = st.ia * p.da + st.ib * p.db + st.ic * p.dc + (int64_t)st.col * V;
+    c.cso1 = p.sc - (int64_t)vpr * V;
+    c.cdo1 = p.dc - (int64_t)vpr * V;
+    c.cso2 = p.sb - p.C * p.sc;
+    c.cdo2 = p.db - p.C * p.dc;
+    c.cso3 = p.sa - p.B * p.sb;
+    c.cdo3 = p.da - p.B * p.db;
+    return c;
+}
+
+// One step.  Each digit sum is below twice its radix, so one carry per digit suffices.
+RA2A_HD void cursor_advance(PlanCursor& c, const RowPlan& p, int vpr) {
+    c.so += c.dso;
+    c.dofs += c.ddo;
+    c.col += c.scol;
+    c.ic += c.sic;
+    c.ib += c.sib;
+    if (c.col >= vpr) {
+        c.col -= vpr;
+        c.ic += 1;
+        c.so += c.cso1;
+        c.dofs += c.cdo1;
+    }
+    if (c.ic >= p.C) {
+        c.ic -= p.C;
+        c.ib += 1;
+        c.so += c.cso2;
+        c.dofs += c.cdo2;
+    }
+    if (c.ib >= p.B) {
+        c.ib -= p.B;
+        c.so += c.cso3;
+        c.dofs += c.cdo3;
+    }
 }
 
 // Streams of group g: the contiguous range [start, start + ns) of stream ids.
@@ -84,22 +179,25 @@ RA2A_HD GroupStreams group_streams(const PipeArgs& a, int g) {
 // only one batch's staging is live at a time while its S-blocks proceed
 // together.  Returns the S-block and the stream's index inside the group.
 RA2A_HD void tile_of(const PipeArgs& a, int ns, int64_t t, int* b, int* k) {
-    const int64_t per_batch = (int64_t)a.nbs * a.KB;
-    const int kb = (int)(t / per_batch);
-    const int64_t rem = t - kb * per_batch;
-    const int left = ns - kb * a.KB;
-    const int nk = left < a.KB ? left : a.KB;
-    *b = (int)(rem / nk);
-    *k = kb * a.KB + (int)(rem - (int64_t)(*b) * nk);
+    const uint32_t per_batch = (uint32_t)a.nbs * (uint32_t)a.KB;
+    const uint32_t ut = (uint32_t)t;
+    const uint32_t kb = ut / per_batch;
+    const uint32_t rem = ut - kb * per_batch;
+    const uint32_t left = (uint32_t)ns - kb * (uint32_t)a.KB;
+    const uint32_t nk = left < (uint32_t)a.KB ? left : (uint32_t)a.KB;
+    const uint32_t bb = rem / nk;
+    *b = (int)bb;
+    *k = (int)(kb * (uint32_t)a.KB + (rem - bb * nk));
 }
 
 // Producer piece pc of group g: source r = pc mod W of tile pc div W.
 struct Piece {
-    int32_t b, r, j, slot;
+    int32_t b, r, j, slot, nsig;
     int64_t src;          // absolute byte offset from the heap base (slice r)
-    int64_t dst;          // absolute byte offset (slice j, staging ring)
+    int64_t dst;          // absolute byte offset (slice j: staging ring, or out if direct)
     RowPlan pl;
-    int64_t sig;          // absolute byte offset of its data signal (slice j)
+    int64_t sig;          // absolute byte offset of its first data signal (slice j)
+    int64_t sig_step;     // bytes to the next signal tile's slot
     int64_t credit;       // absolute byte offset of the ring hand-back counter (slice j)
     uint64_t credit_need; // wait until credit >= this (only if b >= R)
     int32_t sid;
@@ -109,21 +207,26 @@ RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
     Piece p;
     const int64_t e = a.e;
     const GroupStreams gs = group_streams(a, g);
-    p.r = (int)(pc % a.W);
+    const uint32_t tile = (uint32_t)pc / (uint32_t)a.W;
+    p.r = (int)((uint32_t)pc - tile * (uint32_t)a.W);
     int k;
-    tile_of(a, gs.ns, pc / a.W, &p.b, &k);
+    tile_of(a, gs.ns, tile, &p.b, &k);
     p.sid = gs.start + k;
     const Stream st = stream_of(a, p.sid);
     p.j = st.j;
-    p.slot = p.b % a.R;
+    const uint32_t cycle = (uint32_t)p.b / (uint32_t)a.R;  // uses of this ring slot before b
+    p.slot = (int)((uint32_t)p.b - cycle * (uint32_t)a.R);
     const bool add = a.protocol == kSigAdd;
     const int64_t HWDe = a.H * (int64_t)a.W * a.D * e;
     const int64_t s0 = (int64_t)p.b * a.BS;
     const int bs = (int)geom_min(a.BS, a.S - s0);
     p.src = (int64_t)p.r * a.stride + a.in_off + (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e +
             st.d0 * e;
-    p.dst = (int64_t)st.j * a.stride + a.stg_off + (int64_t)p.slot * a.BS * HWDe +
-            ((int64_t)p.r * a.H + st.h0) * a.D * e + st.d0 * e;
+    // staging ring slot, or (direct) the piece's final place in out_j: both are
+    // rows of [H*W][D] columns, the ring being a window of S-blocks of the output
+    p.dst = a.direct ? (int64_t)st.j * a.stride + a.out_off + s0 * HWDe
+                     : (int64_t)st.j * a.stride + a.stg_off + (int64_t)p.slot * a.BS * HWDe;
+    p.dst += ((int64_t)p.r * a.H + st.h0) * a.D * e + st.d0 * e;
     RowPlan& pl = p.pl;
     pl.A = bs;
     pl.sa = a.H * a.D * e;  // input token stride
@@ -139,13 +242,14 @@ RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
         pl.sb = pl.db = a.D * e;
         pl.run = (int)(st.td * e);
     }
-    int64_t si = ((int64_t)p.b * a.nhb + st.hb) * a.ndb + st.db;
-    if (!add) si = si * a.W + p.r;
-    p.sig = (int64_t)st.j * a.stride + a.sig_off + si * kSigStrideU64 * 8;
-    int64_t ci = ((int64_t)p.slot * a.nhb + st.hb) * a.ndb + st.db;
+    const int64_t sig_base = (int64_t)st.j * a.stride + a.sig_off;
+    p.nsig = st.nh;
+    p.sig = sig_base + tile_slot(a, p.b, st.hb0, st.db, p.r) * kSigStrideU64 * 8;
+    p.sig_step = slot_step(a) * kSigStrideU64 * 8;
+    int64_t ci = ((int64_t)p.slot * a.nmhb + st.mhb) * a.ndb + st.db;
     if (!add) ci = ci * a.W + p.r;
-    p.credit = (int64_t)st.j * a.stride + a.sig_off + (a.regionA + ci) * kSigStrideU64 * 8;
-    p.credit_need = (uint64_t)(p.b / a.R) * (uint64_t)a.csplit;
+    p.credit = sig_base + (a.regionA + ci) * kSigStrideU64 * 8;
+    p.credit_need = (uint64_t)cycle * (uint64_t)a.csplit;
     return p;
 }
 
@@ -155,17 +259,20 @@ RA2A_HD int64_t group_pieces(const PipeArgs& a, int g) {
 
 // Consumer work item `it` of group g: part `part` of a unit (ADD: a tile with
 // all W sources; SET: one source of a tile, units ordered tile then source),
-// i.e. the unit's vectors [lo, hi) of its row plan.
+// i.e. the unit's vectors [lo, hi) of its row plan.  A unit spans the nsig
+// signal tiles of its stream and may start once every one of them is complete.
 struct Item {
-    int32_t b, j, r0, nsrc, slot, part;
+    int32_t b, j, r0, nsrc, slot, part, nsig;
     int64_t src;          // absolute byte offset (slice j, staging ring)
     int64_t dst;          // absolute byte offset (slice j, out)
     RowPlan pl;
     int lo, hi;
-    int64_t sig;          // data signal to wait on
+    int64_t sig;          // first data signal to wait on
+    int64_t sig_step;     // bytes to the next signal tile's slot
     uint64_t sig_want;    // W (ADD) or 1 (SET)
     int64_t credit;       // hand-back counter to add 1 to
-    int64_t unit_index;   // data-signal slot index within slice j (timestamp row)
+    int64_t unit_index;   // first data-signal slot index within slice j (timestamp row)
+    int64_t unit_step;    // slot-index distance to the next signal tile
 };
 
 RA2A_HD Item item_of(const PipeArgs& a, int g, int64_t it, int V) {
@@ -173,16 +280,16 @@ RA2A_HD Item item_of(const PipeArgs& a, int g, int64_t it, int V) {
     const int64_t e = a.e;
     const bool add = a.protocol == kSigAdd;
     const GroupStreams gs = group_streams(a, g);
-    q.part = (int)(it % a.csplit);
-    const int64_t u = it / a.csplit;
-    const int64_t t = add ? u : u / a.W;
-    q.r0 = add ? 0 : (int)(u % a.W);
+    const uint32_t u = (uint32_t)it / (uint32_t)a.csplit;
+    q.part = (int)((uint32_t)it - u * (uint32_t)a.csplit);
+    const uint32_t t = add ? u : u / (uint32_t)a.W;
+    q.r0 = add ? 0 : (int)(u - t * (uint32_t)a.W);
     q.nsrc = add ? a.W : 1;
     int k;
     tile_of(a, gs.ns, t, &q.b, &k);
     const Stream st = stream_of(a, gs.start + k);
     q.j = st.j;
-    q.slot = q.b % a.R;
+    q.slot = (int)((uint32_t)q.b % (uint32_t)a.R);
     const int64_t HWDe = a.H * (int64_t)a.W * a.D * e;
     const int64_t s0 = (int64_t)q.b * a.BS;
     const int bs = (int)geom_min(a.BS, a.S - s0);
@@ -211,17 +318,19 @@ RA2A_HD Item item_of(const PipeArgs& a, int g, int64_t it, int V) {
         pl.sc = pl.dc = head;
         pl.run = (int)(st.td * e);
     }
-    const int nvec = plan_vectors(pl, V);
+    const int nvec = a.direct ? 0 : plan_vectors(pl, V);  // direct: nothing to move
     q.lo = (int)((int64_t)nvec * q.part / a.csplit);
     q.hi = (int)((int64_t)nvec * (q.part + 1) / a.csplit);
-    int64_t si = ((int64_t)q.b * a.nhb + st.hb) * a.ndb + st.db;
-    if (!add) si = si * a.W + q.r0;
-    q.unit_index = si;
-    q.sig = (int64_t)st.j * a.stride + a.sig_off + si * kSigStrideU64 * 8;
+    const int64_t sig_base = (int64_t)st.j * a.stride + a.sig_off;
+    q.nsig = st.nh;
+    q.unit_index = tile_slot(a, q.b, st.hb0, st.db, q.r0);
+    q.unit_step = slot_step(a);
+    q.sig = sig_base + q.unit_index * kSigStrideU64 * 8;
+    q.sig_step = q.unit_step * kSigStrideU64 * 8;
     q.sig_want = add ? (uint64_t)a.W : 1ull;
-    int64_t ci = ((int64_t)q.slot * a.nhb + st.hb) * a.ndb + st.db;
+    int64_t ci = ((int64_t)q.slot * a.nmhb + st.mhb) * a.ndb + st.db;
     if (!add) ci = ci * a.W + q.r0;
-    q.credit = (int64_t)st.j * a.stride + a.sig_off + (a.regionA + ci) * kSigStrideU64 * 8;
+    q.credit = sig_base + (a.regionA + ci) * kSigStrideU64 * 8;
     return q;
 }
 
@@ -230,22 +339,73 @@ RA2A_HD int64_t group_items(const PipeArgs& a, int g) {
     return (int64_t)a.nbs * group_streams(a, g).ns * (add ? 1 : a.W) * a.csplit;
 }
 
-// Role of workgroup `wg` of the persistent grid.
-struct Role {
-    int g;          // stream group
-    bool producer;
-    int index;      // producer index or consumer index inside the group
+// The work queue of group g.  Its tasks are the group's producer pieces and
+// consumer work items in one order in which every wait of a task is on a task
+// placed before it: the pieces of tile t + L, then the consumer items of tile
+// t, for t = 0, 1, ... (after the pieces of tiles 0 .. L-1).  A piece of tile
+// (k, b) waits for the hand-back of tile (k, b - R), which lies R * nk tiles
+// earlier in the same stream batch (nk streams), so L <= R * nk - 1 keeps that
+// dependency backwards; without ring reuse nothing waits on consumers and any
+// L is valid (direct mode: the whole group, all pieces first).  Workgroups claim tasks in queue order
+// and only ever wait on earlier tasks, each of which a running workgroup has
+// claimed; hence no deadlock, whatever the number of resident workgroups.
+struct GroupQueue {
+    int64_t ntiles;  // tiles of the group
+    int np, ni;      // pieces per tile (W), consumer items per tile
+    int64_t L;       // lookahead in tiles
+    int64_t total;   // tasks
 };
 
-RA2A_HD Role role_of(const PipeArgs& a, int wg) {
-    Role r;
-    r.g = wg % a.NG;
-    const int lg = wg / a.NG;
-    const int per = lg / a.q;
-    const int pos = lg - per * a.q;
-    r.producer = pos < a.p;
-    r.index = r.producer ? per * a.p + pos : per * (a.q - a.p) + (pos - a.p);
-    return r;
+RA2A_HD GroupQueue group_queue(const PipeArgs& a, int g) {
+    GroupQueue q;
+    const int ns = group_streams(a, g).ns;
+    q.ntiles = (int64_t)a.nbs * ns;
+    q.np = a.W;
+    q.ni = (a.protocol == kSigAdd ? 1 : a.W) * a.csplit;
+    if (a.direct || ns == 0) {
+        q.L = q.ntiles;
+    } else {
+        // smallest stream batch of the group (the last one may be partial)
+        const int nk_last = ns - ((ns - 1) / a.KB) * a.KB;
+        const int nk_min = nk_last < a.KB ? nk_last : a.KB;
+        const int64_t cap = (int64_t)a.R * nk_min - 1;
+        // default: half the run-ahead the ring allows, so that a piece's hand-back
+        // and a unit's pieces were both claimed well before they are needed
+        if (a.lookahead < 0 || (a.lookahead == 0 && a.R >= a.nbs))
+            q.L = q.ntiles;  // (no ring reuse: nothing waits on consumers)
+        else
+            q.L = a.lookahead > 0 ? a.lookahead : (cap + 1) / 2 > 1 ? (cap + 1) / 2 : 1;
+        if (a.R < a.nbs && q.L > cap) q.L = cap;  // ring reused: no wait may point forward
+        if (q.L > q.ntiles) q.L = q.ntiles;
+    }
+    q.total = q.ntiles * (q.np + q.ni);
+    return q;
+}
+
+// Task at queue position pos: returns true for a piece (index *idx into the
+// group's pieces) or false for a consumer item (index *idx into its items).
+RA2A_HD bool task_of(const GroupQueue& q, int64_t pos, int64_t* idx) {
+    const int64_t head = q.L * q.np;
+    if (pos < head) {
+        *idx = pos;
+        return true;
+    }
+    pos -= head;
+    const int64_t blk = q.np + q.ni;
+    const int64_t nfull = q.ntiles - q.L;  // blocks: pieces of tile t+L, items of tile t
+    if (pos < nfull * blk) {
+        const int64_t t = pos / blk;
+        const int64_t off = pos - t * blk;
+        if (off < q.np) {
+            *idx = (t + q.L) * q.np + off;
+            return true;
+        }
+        *idx = t * q.ni + (off - q.np);
+        return false;
+    }
+    pos -= nfull * blk;
+    *idx = nfull * q.ni + pos;  // items of the last L tiles
+    return false;
 }
 
 }  // namespace ra2a

@@ -42,29 +42,32 @@ hipError_t launch_signal_reset(uint8_t* base, int64_t stride, int W, int64_t sig
 }
 
 // ---------------------------------------------------------------------------
-// Copies vectors [lo, hi) of a row plan (combine_geom.h).  Full rounds keep U
-// vectors per thread in flight (all loads before any store, no bounds checks
-// so the values stay in registers); the remainder goes one vector at a time.
-// NTL / NTS: non-temporal loads / stores (data touched once: the input and the
-// output), so that they do not displace the staging ring from the L2.
+// Copies vectors [lo, hi) of a row plan (combine_geom.h).  Thread t takes the
+// vectors lo + t, lo + t + 256, ...; a cursor keeps their offsets without
+// divisions.  Each round keeps U vectors per thread in flight (all loads issued
+// before any store).  NTL / NTS: non-temporal loads / stores (data touched
+// once: the input and the output), so that they do not displace the staging
+// ring from the L2.
 template <int V, int U, bool NTL, bool NTS>
 __device__ __forceinline__ void copy_plan(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                           const RowPlan& p, int lo, int hi) {
     using T = typename Vec<V>::T;
     const int vpr = p.run / V;
-    const int BC = p.B * p.C;
-    for (int base = lo + (int)threadIdx.x; base < hi; base += U * kThreads) {
-        // predicated round: every load of the round is issued before any store
+    int idx = lo + (int)threadIdx.x;
+    if (idx >= hi) return;
+    PlanCursor c = cursor_start(p, V, vpr, (uint32_t)idx, kThreads);
+    for (; idx < hi; idx += U * kThreads) {
         T v[U];
         int64_t doff[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int idx = base + u * kThreads;
-            int64_t so = 0;
             doff[u] = -1;
-            if (idx < hi) plan_offsets(p, V, vpr, BC, idx, &so, &doff[u]);
-            const T* sp = reinterpret_cast<const T*>(src + so);
-            if (idx < hi) v[u] = NTL ? load_nt(sp) : *sp;
+            if (idx + u * kThreads < hi) {
+                const T* sp = reinterpret_cast<const T*>(src + c.so);
+                v[u] = NTL ? load_nt(sp) : *sp;
+                doff[u] = c.dofs;
+            }
+            cursor_advance(c, p, vpr);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -87,17 +90,20 @@ __device__ __forceinline__ void copy_plan_buf(__amdgpu_buffer_rsrc_t src, uint32
                                               int hi) {
     using T = typename Vec<V>::T;
     const int vpr = p.run / V;
-    const int BC = p.B * p.C;
-    for (int base = lo + (int)threadIdx.x; base < hi; base += U * kThreads) {
+    int idx = lo + (int)threadIdx.x;
+    if (idx >= hi) return;
+    PlanCursor c = cursor_start(p, V, vpr, (uint32_t)idx, kThreads);
+    for (; idx < hi; idx += U * kThreads) {
         T v[U];
         int64_t doff[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int idx = base + u * kThreads;
-            int64_t so = 0;
             doff[u] = -1;
-            if (idx < hi) plan_offsets(p, V, vpr, BC, idx, &so, &doff[u]);
-            if (idx < hi) v[u] = BufLoad<V, POLICY>::go(src, src_off + (uint32_t)so);
+            if (idx + u * kThreads < hi) {
+                v[u] = BufLoad<V, POLICY>::go(src, src_off + (uint32_t)c.so);
+                doff[u] = c.dofs;
+            }
+            cursor_advance(c, p, vpr);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -115,152 +121,322 @@ __device__ __forceinline__ void copy_plan_buf(__amdgpu_buffer_rsrc_t src, uint32
 // ---------------------------------------------------------------------------
 // The signal-pipelined persistent combine.
 //
-// Work is organised in tile streams: stream (j, hb, db) is the sequence of
-// S-blocks b = 0 .. nbs-1 of destination j, head block hb, d block db.  The
-// streams are cut into NG contiguous groups; group g is served by the
-// workgroups w with w mod NG == g.  With NG equal to the number of XCDs that
-// is exactly the set of workgroups the dispatcher places on XCD g (checked at
-// run time through the XCC_ID hardware register), so a stream's producers,
-// consumers, staging lines and signals all live in one XCD and its L2, and
-// they synchronise with the XCD-local sequences of device.h instead of device-
-// wide L2 write-backs and invalidations (SYNC == kSyncXcd).  SYNC == kSyncAgent
-// uses device-wide release/acquire instead and does not depend on placement.
+// Work is organised in tile streams: stream (j, merged head block, d block) is
+// the sequence of S-blocks b = 0 .. nbs-1 of destination j.  The streams are
+// cut into NG contiguous groups, one per XCD.  Each group has a work queue
+// (combine_geom.h: group_queue / task_of) holding its producer pieces (tile,
+// source r) and consumer work items (parts of a tile's unit) in an order in
+// which every wait points backwards.  Workgroups claim queue positions one at
+// a time with an atomic counter and run each task to completion, so the
+// earliest unfinished task can always proceed: no deadlock, whatever the
+// number of resident workgroups, and an ordinary launch suffices.
 //
-// Inside a group, tiles (stream, S-block) are ordered by stream batch (KB
-// streams whose staging is live together), S-block, stream; the workgroups
-// alternate roles with period q: the first p of each period produce, the rest
-// consume.
+// Placement (staged mode, SYNC == kSyncXcd).  A group's tasks must all run on one XCD, so
+// that producers and consumers meet in that XCD's L2 and synchronise with the
+// XCD-local sequences of device.h instead of device-wide L2 write-backs and
+// invalidations.  A workgroup reads the XCD it runs on from the XCC_ID
+// register and claims from its own XCD's group; once that queue is drained it
+// may take over a group whose home XCD has not claimed anything (a group whose
+// XCD received no workgroup, or received them late), and then only workgroups
+// of the taking XCD serve it.  So every group is served, by one XCD, whatever
+// the dispatcher does.  SYNC == kSyncAgent uses device-wide release/acquire
+// and lets every workgroup help every group; so does the direct mode, whose
+// consumers read no data during the launch (only the signals, which are
+// device-scope atomics): its stores become visible to later work in stream
+// order, when the launch completes.
 //
-// Producer: pieces (tile, source r) of its group in order, `pbatch`
-// consecutive pieces per turn.  Per piece: wait for the ring slot b mod R of
-// its stream to be handed back by the consumers of S-block b - R (credit
-// count), copy in_r -> staging_j.  Per turn: release, then wave 0 signals
-// each piece (SET 1 on the piece's slot, or ADD 1 on the tile's slot).  Pieces
-// already copied in a turn are signalled before any hand-back wait of that
-// turn.
+// Producer piece: wait until ring slot b mod R of its stream has been handed
+// back by the consumers of S-block b - R (credit count; never in direct mode
+// or when the ring is not reused), copy in_r -> staging_j (direct mode: ->
+// out_j), release, then wave 0 signals the piece's signal tiles (SET 1 on the
+// piece's slot, or ADD 1 on the tile's slot).
 //
-// Consumer: units of its group in order (ADD: a tile with all W sources; SET:
-// one piece), each split into `csplit` parts taken by different workgroups.
-// Per part: wait until the signal reaches W (ADD) or 1 (SET), acquire, copy
-// staging_j -> out_j, release, add 1 to the slot's credit count.
+// Consumer item: wait until each of its signal tiles reads W (ADD) or 1 (SET),
+// copy its part of the unit staging_j -> out_j (direct mode: nothing left to
+// move), release, add 1 to the slot's hand-back count, optionally stamp the
+// completion time.
 //
-// Deadlock freedom: the launch is cooperative (every workgroup resident), each
-// workgroup walks its work in increasing tile order, a producer of tile
-// (k, b) waits only on consumers of the earlier tile (k, b - R) and a consumer
-// only on producers of its own tile; so the earliest blocked wait always has a
-// running workgroup able to satisfy it.  Every wait is also bounded in time.
-template <int V, int SYNC>
+// Every wait is also bounded in time (spin_until).
+// A piece's copy in rounds, so that the first round of the next piece can be
+// loaded while the current one drains: start() positions the thread on the
+// piece's vectors, load() issues one round of U loads per thread (non-
+// temporal: the input is read once), store() issues that round's stores.
+template <int V, int U, bool NTS>
+struct PieceMover {
+    using T = typename Vec<V>::T;
+    const uint8_t* src;
+    uint8_t* dst;
+    RowPlan pl;
+    int vpr, idx, hi;
+    PlanCursor c;
+    T v[U];
+    int64_t doff[U];
+
+    __device__ __forceinline__ void start(const uint8_t* s, uint8_t* d, const RowPlan& p) {
+        src = s;
+        dst = d;
+        pl = p;
+        vpr = p.run / V;
+        idx = (int)threadIdx.x;
+        hi = plan_vectors(p, V);
+        c = cursor_start(pl, V, vpr, (uint32_t)idx, kThreads);
+    }
+    __device__ __forceinline__ bool more() const { return idx < hi; }
+    __device__ __forceinline__ void load() {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            doff[u] = -1;
+            if (idx + u * kThreads < hi) {
+                v[u] = load_nt(reinterpret_cast<const T*>(src + c.so));
+                doff[u] = c.dofs;
+            }
+            cursor_advance(c, pl, vpr);
+        }
+    }
+    __device__ __forceinline__ void store() {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (doff[u] >= 0) {
+                T* dp = reinterpret_cast<T*>(dst + doff[u]);
+                if (NTS)
+                    store_nt(v[u], dp);
+                else
+                    *dp = v[u];
+            }
+        }
+        idx += U * kThreads;
+    }
+};
+
+// Whether a piece must wait before its copy starts: for the hand-back of its
+// ring slot (staged mode, ring reused) or as a delayed (straggler) source.
+__device__ __forceinline__ bool piece_waits(const PipeArgs& a, const Piece& p) {
+    return p.b >= a.R || (p.r == a.straggler && a.delay);
+}
+
+// The waits of piece_waits; false if a bounded wait gave up.
+__device__ __forceinline__ bool piece_wait(const PipeArgs& a, const Piece& p, int* lds_flag) {
+    if (p.b >= a.R &&
+        !group_wait<false>(reinterpret_cast<const uint64_t*>(a.base + p.credit), kCmpGe,
+                           p.credit_need, a.timeout, a.err, lds_flag))
+        return false;
+    if (p.r == a.straggler && a.delay) {
+        if (threadIdx.x == 0) {
+            const uint64_t id = ((uint64_t)p.b * (uint64_t)a.nstreams + p.sid) * a.W + p.r;
+            const uint64_t n = a.delay + splitmix64(a.seed, id) % ((uint64_t)a.delay + 1ull);
+            for (uint64_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
+        }
+        __syncthreads();
+    }
+    return true;
+}
+
+// Wave 0 signals the signal tiles of a piece (after the release).
+__device__ __forceinline__ void piece_signal(const PipeArgs& a, int64_t sig, int64_t step, int n) {
+    const int op = a.protocol == kSigAdd ? kSigAdd : kSigSet;
+    for (int k = threadIdx.x; k < n && threadIdx.x < 64; k += 64)
+        sig_update(reinterpret_cast<uint64_t*>(a.base + sig + k * step), 1ull, op);
+}
+
+template <int V, int SYNC, bool DIRECT>
+__device__ __forceinline__ bool run_item(const PipeArgs& a, int g, int64_t it, int* lds_flag) {
+    uint8_t* const base = a.base;
+    const Item q = item_of(a, g, it, V);
+    // XCD-local: staging is read with device-scope (L1-bypassing) loads from the
+    // L2 this XCD's producers wrote it into, so no invalidation is needed.
+    // Device-wide: the acquire drops stale L1 and L2 lines first.
+    if (!group_wait_all<SYNC == kSyncAgent>(reinterpret_cast<const uint64_t*>(base + q.sig),
+                                            q.sig_step, q.nsig, kCmpEq, q.sig_want, a.timeout,
+                                            a.err, lds_flag))
+        return false;
+    if (!DIRECT && q.hi > q.lo) {
+        if (SYNC == kSyncXcd) {
+            const int64_t stg = (int64_t)q.j * a.stride + a.stg_off;
+            copy_plan_buf<V, 8, kPolicySc1, true>(make_rsrc(base + stg, (uint32_t)a.ring_bytes),
+                                                  (uint32_t)(q.src - stg), base + q.dst, q.pl, q.lo,
+                                                  q.hi);
+        } else {
+            copy_plan<V, 8, false, true>(base + q.src, base + q.dst, q.pl, q.lo, q.hi);
+        }
+    }
+    group_release<SYNC>();
+    if (threadIdx.x == 0) sig_update(reinterpret_cast<uint64_t*>(base + q.credit), 1ull, kSigAdd);
+    if (a.stamps && threadIdx.x < 64) {
+        const uint64_t now = rtc_now();
+        for (int k = threadIdx.x; k < q.nsig; k += 64)
+            __hip_atomic_fetch_max(a.stamps + (int64_t)q.j * a.units_per_dest + q.unit_index +
+                                       k * q.unit_step,
+                                   now, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return true;
+}
+
+// Queue words of group g (slice 0, after the hand-back counters): the claim
+// counter of its home XCD, whose top bit marks a group taken over by another
+// XCD (bits 32..39: that XCD + 1), and the claim counter of such a taker.
+constexpr uint64_t kTaken = 1ull << 63;
+constexpr uint64_t kOwnerMask = 0xFFull << 32;
+
+template <int V, int SYNC, bool DIRECT>
 __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a) {
     __shared__ int lds_flag;
-    const Role role = role_of(a, blockIdx.x);
-    const int g = role.g;
-    const bool add = a.protocol == kSigAdd;
-    uint8_t* const base = a.base;
-    if (SYNC == kSyncXcd && threadIdx.x == 0 && (int)xcc_id() != (int)(blockIdx.x % a.NG))
-        __hip_atomic_fetch_or(a.err, kErrPlacement, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-    if (role.producer) {
-        const int64_t npieces = group_pieces(a, g);
-        // Publish pieces [lo, hi) of this workgroup: release, then wave 0 signals each.
-        auto flush = [&](int64_t lo, int64_t hi) {
-            group_release<SYNC>();
-            if (threadIdx.x < 64) {
-                for (int64_t pc = lo + threadIdx.x; pc < hi; pc += 64) {
-                    const Piece p = piece_of(a, g, pc);
-                    sig_update(reinterpret_cast<uint64_t*>(base + p.sig), 1ull,
-                                           add ? kSigAdd : kSigSet);
-                }
+    __shared__ int64_t lds_pos[2];
+    constexpr bool kOwned = SYNC == kSyncXcd && !DIRECT;  // groups bound to one XCD
+    uint64_t* const qw = reinterpret_cast<uint64_t*>(a.base + a.sig_off) +
+                         (a.regionA + a.regionB) * kSigStrideU64;
+    uint64_t* const drained = qw + (int64_t)(2 * kNumXcd) * kSigStrideU64;
+    const uint32_t xcc = xcc_id();
+    const int home = SYNC == kSyncXcd ? (int)(xcc % (uint32_t)a.NG) : (int)(blockIdx.x % a.NG);
+    // thread 0's claim state
+    uint64_t* ctr = nullptr;  // the counter claims of the current group come from
+    uint64_t known = 0;       // groups known to be fully claimed (copy of `drained`)
+    bool stale = true;        // `known` may be out of date
+    int k = 0;
+    for (int gi = 0; gi < a.NG; ++gi) {
+        const int g = (home + gi) % a.NG;
+        uint64_t* const head = qw + (int64_t)(2 * g) * kSigStrideU64;
+        uint64_t* const taker = head + kSigStrideU64;
+        // First claim.  Staged mode with XCD-local sync: the home XCD claims
+        // directly (one atomic; the returned word says whether another XCD took
+        // the group over first); another XCD takes over a group only if its home
+        // XCD has not claimed anything yet.  Otherwise (device-wide sync, or the
+        // direct mode, where no workgroup reads data another one wrote during the
+        // launch) any workgroup claims from any group: home group first, then it
+        // helps the others.  Leaving a group, one load of `drained` tells which
+        // groups are still worth a visit.
+        if (threadIdx.x == 0) {
+            int64_t first = -1;
+            if (gi > 0 && stale) {
+                known = __hip_atomic_load(drained, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                stale = false;
             }
-        };
-        for (int64_t first = (int64_t)role.index * a.pbatch; first < npieces;
-             first += (int64_t)a.nprod * a.pbatch) {
-            const int64_t last = min(first + (int64_t)a.pbatch, npieces);
-            int64_t pend = first;  // first piece of this turn not yet signalled
-            for (int64_t pc = first; pc < last; ++pc) {
-                const Piece p = piece_of(a, g, pc);
-                if (p.b >= a.R) {
-                    // Signal what this turn already copied before blocking on a hand-back:
-                    // that hand-back may depend on those very pieces.
-                    if (pc > pend) {
-                        flush(pend, pc);
-                        pend = pc;
-                    }
-                    if (!group_wait<false>(reinterpret_cast<const uint64_t*>(base + p.credit),
-                                           kCmpGe, p.credit_need, a.timeout, a.err, &lds_flag))
-                        return;
-                }
-                if (p.r == a.straggler && a.delay) {
-                    if (threadIdx.x == 0) {
-                        const uint64_t id = ((uint64_t)p.b * (uint64_t)a.nstreams + p.sid) * a.W + p.r;
-                        const uint64_t n =
-                            a.delay + splitmix64(a.seed, id) % ((uint64_t)a.delay + 1ull);
-                        for (uint64_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
-                    }
-                    __syncthreads();
-                }
-                copy_plan<V, 8, true, false>(base + p.src, base + p.dst, p.pl, 0,
-                                             plan_vectors(p.pl, V));
-            }
-            flush(pend, last);
-        }
-    } else {
-        const int64_t nitems = group_items(a, g);
-        for (int64_t it = role.index; it < nitems; it += a.ncons) {
-            const Item q = item_of(a, g, it, V);
-            // XCD-local: staging is read with device-scope (L1-bypassing) loads from
-            // the L2 this XCD's producers wrote it into, so no invalidation is needed.
-            // Device-wide: the acquire drops stale L1 and L2 lines first.
-            if (!group_wait<SYNC == kSyncAgent>(reinterpret_cast<const uint64_t*>(base + q.sig),
-                                                kCmpEq, q.sig_want, a.timeout, a.err, &lds_flag))
-                return;
-            if (SYNC == kSyncXcd) {
-                const int64_t stg = (int64_t)q.j * a.stride + a.stg_off;
-                copy_plan_buf<V, 8, kPolicySc1, true>(make_rsrc(base + stg, (uint32_t)a.ring_bytes),
-                                                      (uint32_t)(q.src - stg), base + q.dst, q.pl,
-                                                      q.lo, q.hi);
+            if ((known >> g) & 1ull) {
+                // fully claimed: nothing to do here
+            } else if (!kOwned || gi == 0) {
+                const uint64_t h =
+                    __hip_atomic_fetch_add(head, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!(h & kTaken)) first = (int64_t)h;
+                ctr = head;
             } else {
-                copy_plan<V, 8, false, true>(base + q.src, base + q.dst, q.pl, q.lo, q.hi);
+                const uint64_t mine = kTaken | ((uint64_t)(xcc + 1u) << 32);
+                uint64_t cur = 0;
+                __hip_atomic_compare_exchange_strong(head, &cur, mine, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (cur == 0ull || (cur & (kTaken | kOwnerMask)) == mine) {
+                    first = (int64_t)__hip_atomic_fetch_add(taker, 1ull, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                    ctr = taker;
+                }
             }
-            group_release<SYNC>();
-            if (threadIdx.x == 0) {
-                sig_update(reinterpret_cast<uint64_t*>(base + q.credit), 1ull,
-                                       kSigAdd);
-                if (a.stamps)
-                    __hip_atomic_fetch_max(a.stamps + (int64_t)q.j * a.units_per_dest + q.unit_index,
-                                           rtc_now(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lds_pos[k & 1] = first;
+        }
+        __syncthreads();
+        // positions are wave-uniform: keep them (and all task geometry) scalar
+        int64_t pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
+        ++k;
+        if (pos < 0) continue;
+        const GroupQueue Q = group_queue(a, g);
+        if (threadIdx.x == 0) stale = true;
+        // Pieces are software-pipelined: once a piece's last stores are issued, the
+        // next task is looked up and, if it is a piece that need not wait, its
+        // first round of loads goes out before the release of the current piece
+        // (whose drain waits for both), so the two latencies overlap.
+        while (true) {
+            if (pos >= Q.total) {
+                // the group is fully claimed; the one workgroup whose claim landed
+                // exactly at the end says so (no wait: same-address atomics
+                // serialise, so they are kept few)
+                if (threadIdx.x == 0 && pos == Q.total)
+                    __hip_atomic_fetch_or(drained, 1ull << g, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            // claim the next position while this task runs (positions a workgroup
+            // claims increase, so it still runs its tasks in queue order)
+            uint64_t nxt = 0;
+            if (threadIdx.x == 0)
+                nxt = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int64_t idx = 0;
+            if (!task_of(Q, pos, &idx)) {
+                if (!run_item<V, SYNC, DIRECT>(a, g, idx, &lds_flag))
+                    return;  // a wait gave up: the error word is raised, everyone leaves
+                if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
+                __syncthreads();
+                pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
+                ++k;
+                continue;
+            }
+            // a run of pieces
+            PieceMover<V, 8, DIRECT> m;  // DIRECT: final place, stream stores past the L2
+            {
+                const Piece p = piece_of(a, g, idx);
+                if (!piece_wait(a, p, &lds_flag)) return;
+                m.start(a.base + p.src, a.base + p.dst, p.pl);
+                m.load();
+            }
+            while (true) {
+                const Piece p = piece_of(a, g, idx);
+                m.store();
+                while (m.more()) {
+                    m.load();
+                    m.store();
+                }
+                if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
+                __syncthreads();
+                pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
+                ++k;
+                bool next_loaded = false;
+                if (pos < Q.total && task_of(Q, pos, &idx)) {
+                    const Piece pn = piece_of(a, g, idx);
+                    if (!piece_waits(a, pn)) {
+                        m.start(a.base + pn.src, a.base + pn.dst, pn.pl);
+                        m.load();
+                        next_loaded = true;
+                    }
+                }
+                group_release<SYNC>();
+                piece_signal(a, p.sig, p.sig_step, p.nsig);
+                if (!next_loaded) break;
+                if (threadIdx.x == 0)
+                    nxt = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
 }
 
-template <int V, int SYNC>
+template <int V, int SYNC, bool DIRECT>
 static const void* pipelined_fn() {
-    return reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<V, SYNC>);
+    return reinterpret_cast<const void*>(&rev_a2a_pipelined_kernel<V, SYNC, DIRECT>);
 }
 
-template <int SYNC>
+template <int SYNC, bool DIRECT>
 static const void* pipelined_fn_v(int V) {
     switch (V) {
-        case 16: return pipelined_fn<16, SYNC>();
-        case 8: return pipelined_fn<8, SYNC>();
-        case 4: return pipelined_fn<4, SYNC>();
-        case 2: return pipelined_fn<2, SYNC>();
-        default: return pipelined_fn<1, SYNC>();
+        case 16: return pipelined_fn<16, SYNC, DIRECT>();
+        case 8: return pipelined_fn<8, SYNC, DIRECT>();
+        case 4: return pipelined_fn<4, SYNC, DIRECT>();
+        case 2: return pipelined_fn<2, SYNC, DIRECT>();
+        default: return pipelined_fn<1, SYNC, DIRECT>();
     }
 }
 
-static const void* pipelined_kernel(int V, int sync) {
-    return sync == kSyncXcd ? pipelined_fn_v<kSyncXcd>(V) : pipelined_fn_v<kSyncAgent>(V);
+static const void* pipelined_kernel(int V, int sync, int direct) {
+    if (direct)
+        return sync == kSyncXcd ? pipelined_fn_v<kSyncXcd, true>(V) : pipelined_fn_v<kSyncAgent, true>(V);
+    return sync == kSyncXcd ? pipelined_fn_v<kSyncXcd, false>(V) : pipelined_fn_v<kSyncAgent, false>(V);
 }
 
+// The work queues make the kernel deadlock-free at any residency: an ordinary launch.
 hipError_t launch_pipelined(const PipeArgs& a, int V, int grid, hipStream_t st) {
     void* args[] = {const_cast<PipeArgs*>(&a)};
-    return hipLaunchCooperativeKernel(pipelined_kernel(V, a.sync), dim3(grid), dim3(kThreads), args,
-                                      0, st);
+    return hipLaunchKernel(pipelined_kernel(V, a.sync, a.direct), dim3(grid), dim3(kThreads), args, 0,
+                           st);
 }
 
-hipError_t pipelined_blocks_per_cu(int V, int sync, int* n) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, pipelined_kernel(V, sync), kThreads, 0);
+hipError_t pipelined_blocks_per_cu(int V, int sync, int direct, int* n) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, pipelined_kernel(V, sync, direct), kThreads,
+                                                        0);
 }
 
 // ---------------------------------------------------------------------------

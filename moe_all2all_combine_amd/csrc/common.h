@@ -10,11 +10,13 @@ constexpr int kSigAdd = 1;
 constexpr int kCmpEq = 0, kCmpNe = 1, kCmpGt = 2, kCmpGe = 3, kCmpLt = 4, kCmpLe = 5;
 constexpr int kSigStrideU64 = 16;  // 128-byte signal slots
 constexpr uint32_t kErrTimeout = 1u;
-constexpr uint32_t kErrPlacement = 2u;  // a workgroup ran on another XCD than its group's
 constexpr int kSyncXcd = 0;    // producers and consumers of a stream share one XCD's L2
 constexpr int kSyncAgent = 1;  // device-wide release/acquire (L2 write-back / invalidate)
 constexpr int kThreads = 256;      // workgroup size of every copy kernel
-constexpr int kNumXcd = 8;         // XCDs of an MI355X
+constexpr int kNumXcd = 8;         // XCDs of an MI355X: at most this many stream groups
+// queue words: per group a claim counter and a take-over counter, then a mask
+// of groups whose queue is fully claimed, then one spare word
+constexpr int kQueueSlots = 2 * kNumXcd + 2;
 
 // Arguments of the signal-pipelined persistent combine.
 struct PipeArgs {
@@ -30,19 +32,22 @@ struct PipeArgs {
     int64_t S, H, D;    // problem
     int64_t BS, TH, TD; // tile (tokens, heads, d elements)
     int32_t W, e;       // ranks, element bytes
-    int32_t nbs, nhb, ndb;     // blocks along S, H, D
+    int32_t nbs, nhb, ndb;     // signal-tile blocks along S, H, D
+    int32_t MH;         // head blocks moved together (one piece / unit spans MH signal tiles)
+    int32_t nmhb;       // merged head blocks: ceil(nhb / MH)
     int32_t R;          // ring depth (S-blocks)
     int32_t protocol;   // kSigSet | kSigAdd
     int32_t NG;         // stream groups (one per XCD when sync == kSyncXcd)
     int32_t nstreams;   // streams in total; group g owns [g*nstreams/NG, (g+1)*nstreams/NG)
     int32_t KB;         // streams of a group in flight together (a stream batch)
     int32_t sync;       // kSyncXcd | kSyncAgent
-    int32_t q, p;       // role period and producers per period
-    int32_t nprod, ncons;   // producers / consumers per group
-    int32_t pbatch;     // pieces per producer turn
-    int32_t csplit;     // consumer workgroups sharing one unit
+    int32_t csplit;     // consumer work items per unit (each copies one contiguous part)
+    int32_t lookahead;  // tiles whose pieces precede a tile's consumer items in the queue
+                        // (-1: all pieces first)
     int64_t regionA;    // data-signal slots per slice (credits follow)
+    int64_t regionB;    // ring hand-back slots per slice (work counters follow, slice 0)
     int64_t ring_bytes; // staging bytes per slice
+    int32_t direct;     // 1: pieces go straight to out_j, no staging
     int32_t straggler;  // delayed source rank or -1
     uint32_t delay;     // busy-loop base n0
     uint64_t seed;      // SplitMix64 seed of the delays

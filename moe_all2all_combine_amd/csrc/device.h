@@ -112,15 +112,17 @@ __device__ __forceinline__ void wg_release() {
 //            that device-wide write-back is what the XCD-local protocol saves.
 //            (SYNC == kSyncAgent adds it, for producers and consumers that may
 //            sit on different XCDs.)
-//   acquire: after seeing the signal, wave 0 runs the device-scope acquire
-//            (`buffer_inv sc1`): it drops the CU's L1, whose lines may hold an
-//            earlier use of the same staging slot.  The workgroup-scope
-//            invalidate (`buffer_inv sc0`) is not enough: outside threadgroup-
-//            split dispatches it leaves the L1 alone (measured: a consumer then
-//            read the slot's previous contents).  One wave suffices because the
-//            workgroup's waves share the CU and its L1.
-// The pipelined kernel checks at run time that each workgroup runs on the XCD
-// its stream group assumes.
+//   acquire: none.  Consumers read the published data with device-scope loads
+//            (cache policy sc1), which are never served from the CU's L1 -- whose
+//            lines may hold an earlier use of the same staging slot -- and so
+//            read the L2 the producers' stores went to.  (The workgroup-scope
+//            invalidate `buffer_inv sc0` would not do: outside threadgroup-split
+//            dispatches it leaves the L1 alone; measured, a consumer then read
+//            the slot's previous contents.)  SYNC == kSyncAgent instead has wave
+//            0 run the device-scope acquire (`buffer_inv sc1`), dropping stale
+//            L1 and L2 lines, before plain loads.
+// The pipelined kernel guarantees the "same XCD" premise itself: a workgroup
+// serves only stream groups its own XCD owns (XCC_ID register).
 
 // This wave's memory operations have completed (stores acknowledged by the L2,
 // loads returned).
@@ -141,6 +143,26 @@ __device__ __forceinline__ bool group_wait(const uint64_t* p, int op, uint64_t v
     __syncthreads();
     const bool ok = *lds_flag != 0;
     __syncthreads();  // lds_flag may be rewritten by the next wait
+    return ok;
+}
+
+// The same for `n` signals `step` bytes apart, all of which must hold.
+template <bool ACQUIRE>
+__device__ __forceinline__ bool group_wait_all(const uint64_t* p, int64_t step, int n, int op,
+                                               uint64_t v, uint64_t timeout, uint32_t* err,
+                                               int* lds_flag) {
+    if (threadIdx.x == 0) {
+        bool ok = true;
+        for (int k = 0; k < n && ok; ++k)
+            ok = spin_until(reinterpret_cast<const uint64_t*>(
+                                reinterpret_cast<const uint8_t*>(p) + k * step),
+                            op, v, timeout, err);
+        if (ACQUIRE) fence_acquire_agent();
+        *lds_flag = ok ? 1 : 0;
+    }
+    __syncthreads();
+    const bool ok = *lds_flag != 0;
+    __syncthreads();
     return ok;
 }
 

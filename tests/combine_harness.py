@@ -35,11 +35,12 @@ class CombineCase:
         self.wl = wl
         self.opts = opts if opts is not None else opts_for(wl)
         W, S, H, D = wl.W, wl.S, wl.H, wl.D
-        self.n_tile, self.n_credit = ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, self.opts)
+        self.n_tile, self.n_credit, self.n_queue = ra2a.rev_all2all_signal_slots(
+            W, S, H, D, wl.dtype, self.opts)
         ring = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, self.opts)
         full = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, None, True) if two_phase else 0
         nb = wl.bytes_per_rank
-        sig_bytes = max(1, self.n_tile + self.n_credit) * ra2a.SIG_STRIDE_BYTES
+        sig_bytes = max(1, self.n_tile + self.n_credit + self.n_queue) * ra2a.SIG_STRIDE_BYTES
         slice_bytes = 2 * nb + ring + full + sig_bytes + 8 * 4096 + extra
         self.heap = ra2a.SymmHeap(W, slice_bytes)
         self.off_in = self.heap.alloc(max(nb, 1))
@@ -86,6 +87,13 @@ class CombineCase:
         n = self.n_tile + self.n_credit
         v = self.heap.view(self.off_sig, (max(n, 1), ra2a.SIG_STRIDE_U64), torch.int64, j)
         return v[:n, 0].cpu().numpy()
+
+    def queue_words(self) -> np.ndarray:
+        """The work-queue words of slice 0: per group (8) its claim counter and
+        take-over counter, then the mask of fully claimed groups and a spare."""
+        n0 = self.n_tile + self.n_credit
+        v = self.heap.view(self.off_sig, (n0 + self.n_queue, ra2a.SIG_STRIDE_U64), torch.int64, 0)
+        return v[n0:, 0].cpu().numpy()
 
     def run_pipelined(self, stream=None) -> None:
         wl = self.wl

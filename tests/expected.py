@@ -1,6 +1,7 @@
 """Expected final signal arrays of one slice, laid out as the combine lays them
-out (data signals, then ring hand-back counters), from the protocol model's
-closed forms in ``oracle.protocol``."""
+out (data signals, then ring hand-back counters; the work-queue words that
+follow are not part of the protocol), from the protocol model's closed forms in
+``oracle.protocol``."""
 import math
 
 import numpy as np
@@ -9,23 +10,36 @@ import moe_all2all_combine_amd as ra2a
 from oracle.protocol import ADD, SET, ProtocolSpec, expected_final_credits, expected_final_signals
 
 
-def expected_signal_array(W, S, H, D, opts, csplit):
+def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):
+    """Data signals (one per signal tile) then hand-back counters (one per ring
+    slot of each moved stream, a stream being head_merge adjacent head blocks)."""
     nbs = math.ceil(S / opts.tile_s)
     nhb = math.ceil(H / opts.tile_h)
     ndb = math.ceil(D / opts.tile_d)
-    R = min(opts.ring or 2, nbs)
+    direct = opts.mode != ra2a.MODE_STAGED
+    R = nbs if direct else min(opts.ring or 8, nbs)
+    if direct:
+        csplit = 1
     proto = SET if opts.protocol == ra2a.PROTO_SET else ADD
-    spec = ProtocolSpec(W=W, nbs=nbs, nstreams=nhb * ndb, R=R, protocol=proto)
-    ns = nhb * ndb
     per = W if proto == SET else 1
+    # merged head blocks: derived from the size of the hand-back region
+    _, n_credit, _ = ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)
+    nmhb = n_credit // (R * ndb * per)
+    assert nmhb * R * ndb * per == n_credit
+    # data signals: one per signal tile, the model's closed form
+    tiles = ProtocolSpec(W=W, nbs=nbs, nstreams=nhb * ndb, R=R, protocol=proto)
+    ns = nhb * ndb
     a = np.zeros(nbs * ns * per, dtype=np.int64)
-    for k, v in expected_final_signals(spec).items():
+    for k, v in expected_final_signals(tiles).items():
         if k[0] != 0:
             continue
         a[(k[2] * ns + k[1]) * per + (k[3] if proto == SET else 0)] = v
-    b = np.zeros(R * ns * per, dtype=np.int64)
-    for k, v in expected_final_credits(spec).items():
+    # hand-back counters: one per (ring slot, moved stream), the model's closed form
+    moved = ProtocolSpec(W=W, nbs=nbs, nstreams=nmhb * ndb, R=R, protocol=proto)
+    nm = nmhb * ndb
+    b = np.zeros(R * nm * per, dtype=np.int64)
+    for k, v in expected_final_credits(moved).items():
         if k[0] != 0:
             continue
-        b[(k[2] * ns + k[1]) * per + (k[3] if proto == SET else 0)] = v * csplit
+        b[(k[2] * nm + k[1]) * per + (k[3] if proto == SET else 0)] = v * csplit
     return np.concatenate([a, b])

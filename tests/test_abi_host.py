@@ -77,22 +77,40 @@ def test_attach_rejects_overlap_and_misalignment(fake_heap):
 
 
 def test_signal_slots_and_workspace():
+    Q = ra2a.QUEUE_SLOTS
     # 64-token x 1-head x 128 tiles, ADD: one slot per (S-block, head) per slice
-    a, b = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
+    a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
+    # direct mode (the default): every S-block is a ring slot; 256-B heads would
+    # merge 16 at a time into 4 KiB runs, but that leaves only 512 pieces, so
+    # 4 at a time (2048 pieces): 4 moved streams per destination
+    assert (a, b, q) == (8 * 16, 8 * 4, Q)
+    staged = ra2a.Opts(mode=ra2a.MODE_STAGED)  # ring of 8 = every S-block
+    a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", staged)
+    assert (a, b, q) == (8 * 16, 8 * 4, Q)
+    a, b, _ = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16",
+                                            ra2a.Opts(head_merge=1, ring=2, mode=ra2a.MODE_STAGED))
     assert (a, b) == (8 * 16, 2 * 16)
     # SET: one per (S-block, head, source)
-    opts = ra2a.Opts(protocol=ra2a.PROTO_SET)
-    a, b = ra2a.rev_all2all_signal_slots(16, 2048, 32, 128, "f32", opts)
-    assert (a, b) == (32 * 32 * 16, 2 * 32 * 16)
+    opts = ra2a.Opts(protocol=ra2a.PROTO_SET, head_merge=1, mode=ra2a.MODE_STAGED)
+    a, b, _ = ra2a.rev_all2all_signal_slots(16, 2048, 32, 128, "f32", opts)
+    assert (a, b) == (32 * 32 * 16, 8 * 32 * 16)
+    opts = ra2a.Opts(protocol=ra2a.PROTO_SET, mode=ra2a.MODE_STAGED)  # 512-B heads merge 8 at a time
+    a, b, _ = ra2a.rev_all2all_signal_slots(16, 2048, 32, 128, "f32", opts)
+    assert (a, b) == (32 * 32 * 16, 8 * 4 * 16)
     # 32 x 7168 tiles: 128 S-blocks
-    a, b = ra2a.rev_all2all_signal_slots(8, 4096, 1, 7168, "bf16", ra2a.Opts(tile_s=32))
-    assert (a, b) == (128, 2)
+    a, b, _ = ra2a.rev_all2all_signal_slots(8, 4096, 1, 7168, "bf16",
+                                            ra2a.Opts(tile_s=32, mode=ra2a.MODE_STAGED))
+    assert (a, b) == (128, 8)
+    a, b, _ = ra2a.rev_all2all_signal_slots(8, 4096, 1, 7168, "bf16", ra2a.Opts(tile_s=32))
+    assert (a, b) == (128, 128)
     # ragged: S=37 in tiles of 16 -> 3 blocks; D=40 in tiles of 16 -> 3 d blocks
-    a, b = ra2a.rev_all2all_signal_slots(3, 37, 2, 40, "bf16", ra2a.Opts(tile_s=16, tile_d=16))
-    assert (a, b) == (3 * 2 * 3, 2 * 2 * 3)
-    assert ra2a.rev_all2all_signal_slots(3, 0, 2, 40, "bf16") == (0, 0)
-    ring = ra2a.rev_all2all_workspace_bytes(8, 512, 16, 128, "bf16")
-    assert ring == 2 * 64 * 16 * 8 * 128 * 2
+    a, b, _ = ra2a.rev_all2all_signal_slots(3, 37, 2, 40, "bf16",
+                                            ra2a.Opts(tile_s=16, tile_d=16, mode=ra2a.MODE_STAGED))
+    assert (a, b) == (3 * 2 * 3, 3 * 2 * 3)  # tiles narrower than D: heads are not merged
+    assert ra2a.rev_all2all_signal_slots(3, 0, 2, 40, "bf16") == (0, 0, 0)
+    assert ra2a.rev_all2all_workspace_bytes(8, 512, 16, 128, "bf16") == 0  # direct: no ring
+    ring = ra2a.rev_all2all_workspace_bytes(8, 512, 16, 128, "bf16", staged)
+    assert ring == 8 * 64 * 16 * 8 * 128 * 2
     assert ra2a.rev_all2all_workspace_bytes(8, 512, 16, 128, "bf16", two_phase=True) == \
         512 * 8 * 16 * 128 * 2
 

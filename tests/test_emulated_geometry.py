@@ -1,8 +1,9 @@
-"""The pipelined kernel's own address arithmetic and launch partition, run on
-the host (``ra2a_debug_emulate_pipelined``): every access inside its buffer,
-roles and work lists partitioning the work, every wait satisfiable in
-S-block order, and the bytes moved equal to the oracle's combine, with the
-signal arrays equal to the protocol model's closed forms.  No GPU needed."""
+"""The pipelined kernel's own address arithmetic and work queues, run on the
+host (``ra2a_debug_emulate_pipelined``): every access inside its buffer, each
+queue holding every piece and consumer item once, every wait already holding
+when its task comes up in queue order (the kernel's deadlock-freedom
+argument), and the bytes moved equal to the oracle's combine, with the signal
+arrays equal to the protocol model's closed forms.  No GPU needed."""
 import numpy as np
 import pytest
 
@@ -15,7 +16,7 @@ P_ADD = synthgen.PROTOCOL_ADD
 P_SET = synthgen.PROTOCOL_SET
 
 CASES = [
-    # W, S, H, D, dtype, (tile_s, tile_h, tile_d), protocol, ring, csplit, pbatch
+    # W, S, H, D, dtype, (tile_s, tile_h, tile_d), protocol, ring, csplit, lookahead
     (2, 8, 4, 16, "i32", (8, 4, 16), P_SET, 2, 1, 1),
     (3, 37, 2, 40, "bf16", (16, 1, 16), P_ADD, 2, 3, 2),
     (3, 37, 2, 40, "bf16", (16, 1, 16), P_SET, 1, 2, 5),
@@ -34,29 +35,39 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring,csplit,pbatch", CASES)
-@pytest.mark.parametrize("cus,per_cu", [(256, 2), (256, 1), (8, 1)])
-def test_emulated_kernel_matches_oracle(W, S, H, D, dtype, tile, proto, ring, csplit, pbatch, cus,
-                                        per_cu):
-    wl = synthgen.small_workload(W, S, H, D, dtype, seed=S + W, tile=tile, protocol=proto)
+def staged_opts(tile, proto, **kw):
+    return ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2],
+                     protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD,
+                     mode=ra2a.MODE_STAGED, **kw)
+
+
+def check_emulation(W, S, H, D, dtype, opts, csplit, seed, cus=256, per_cu=2):
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=seed, tile=(opts.tile_s, opts.tile_h,
+                                                                     opts.tile_d))
     ins = synthgen.make_inputs(wl)
-    opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2],
-                     protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD, ring=ring,
-                     consumer_split=csplit, producer_batch=pbatch, wg_per_cu=per_cu)
     outs, sigs = ra2a.debug_emulate_pipelined(ins, W, S, H, D, dtype, opts, cus, per_cu)
     want = oracle.combine(ins)
-    exp = expected_signal_array(W, S, H, D, opts, csplit)
+    exp = expected_signal_array(W, S, H, D, opts, csplit, dtype)
     for j in range(W):
         assert outs[j].tobytes() == want[j].tobytes(), f"rank {j}"
-        np.testing.assert_array_equal(sigs[j].astype(np.int64), exp)
+        np.testing.assert_array_equal(sigs[j][:len(exp)].astype(np.int64), exp)
+        assert len(sigs[j]) == len(exp) + ra2a.QUEUE_SLOTS and not sigs[j][len(exp):].any()
 
 
-def test_emulator_rejects_device_too_small():
-    wl = synthgen.small_workload(8, 16, 16, 8, "bf16", tile=(8, 1, 8))
-    ins = synthgen.make_inputs(wl)
-    with pytest.raises(ra2a.Ra2aError) as e:
-        ra2a.debug_emulate_pipelined(ins, 8, 16, 16, 8, "bf16", None, 2, 1)
-    assert e.value.code == ra2a.EUNSUPPORTED
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring,csplit,lookahead", CASES)
+@pytest.mark.parametrize("cus,per_cu", [(256, 2), (256, 1), (8, 1)])
+def test_emulated_kernel_matches_oracle(W, S, H, D, dtype, tile, proto, ring, csplit, lookahead,
+                                        cus, per_cu):
+    opts = staged_opts(tile, proto, ring=ring, consumer_split=csplit, lookahead=lookahead,
+                       wg_per_cu=per_cu)
+    check_emulation(W, S, H, D, dtype, opts, csplit, seed=S + W, cus=cus, per_cu=per_cu)
+
+
+@pytest.mark.parametrize("cus,per_cu", [(1, 1), (2, 1), (3, 2)])
+def test_emulated_tiny_devices(cus, per_cu):
+    """The queues make any number of resident workgroups enough."""
+    opts = staged_opts((8, 1, 8), P_ADD, ring=1, consumer_split=2)
+    check_emulation(8, 16, 16, 8, "bf16", opts, 2, seed=4, cus=cus, per_cu=per_cu)
 
 
 @pytest.mark.parametrize("stream_batch", [1, 2, 3, 1000])
@@ -66,14 +77,47 @@ def test_emulator_rejects_device_too_small():
     (16, 64, 8, 32, (16, 1, 32), P_ADD, 1),
 ])
 def test_emulated_stream_batches(stream_batch, W, S, H, D, tile, proto, ring):
-    wl = synthgen.small_workload(W, S, H, D, "bf16", seed=7, tile=tile, protocol=proto)
-    ins = synthgen.make_inputs(wl)
+    opts = staged_opts(tile, proto, ring=ring, consumer_split=2, stream_batch=stream_batch)
+    check_emulation(W, S, H, D, "bf16", opts, 2, seed=7)
+
+
+@pytest.mark.parametrize("lookahead", [-1, 0, 1, 2, 5, 1000])
+@pytest.mark.parametrize("W,S,H,D,tile,proto,ring,stream_batch", [
+    (8, 200, 6, 96, (32, 1, 96), P_ADD, 2, 2),
+    (5, 70, 4, 64, (16, 2, 32), P_SET, 3, 1),
+    (16, 64, 8, 32, (16, 1, 32), P_ADD, 1, 3),
+])
+def test_emulated_lookahead(lookahead, W, S, H, D, tile, proto, ring, stream_batch):
+    """Any requested lookahead is capped so that no wait points forward."""
+    opts = staged_opts(tile, proto, ring=ring, consumer_split=3, lookahead=lookahead,
+                       stream_batch=stream_batch)
+    check_emulation(W, S, H, D, "bf16", opts, 3, seed=8)
+
+
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto", [
+    (3, 37, 2, 40, "bf16", (16, 1, 16), P_ADD), (3, 37, 2, 40, "bf16", (16, 1, 16), P_SET),
+    (8, 512, 16, 128, "bf16", (64, 1, 128), P_ADD), (16, 64, 32, 128, "f32", (64, 1, 128), P_SET),
+    (2, 8, 4, 16, "i32", (8, 4, 16), P_SET), (1, 9, 3, 7, "u8", (4, 2, 3), P_ADD),
+])
+def test_emulated_direct_mode(W, S, H, D, dtype, tile, proto):
     opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2],
-                     protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD, ring=ring,
-                     consumer_split=2, producer_batch=3, stream_batch=stream_batch)
-    outs, sigs = ra2a.debug_emulate_pipelined(ins, W, S, H, D, "bf16", opts, 256, 2)
-    want = oracle.combine(ins)
-    exp = expected_signal_array(W, S, H, D, opts, 2)
-    for j in range(W):
-        assert outs[j].tobytes() == want[j].tobytes(), f"rank {j}"
-        np.testing.assert_array_equal(sigs[j].astype(np.int64), exp)
+                     protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD)
+    assert opts.mode == 0  # the default is the direct mode
+    assert ra2a.rev_all2all_workspace_bytes(W, S, H, D, dtype, opts) == 0
+    check_emulation(W, S, H, D, dtype, opts, 1, seed=3)
+    opts.mode = ra2a.MODE_DIRECT
+    check_emulation(W, S, H, D, dtype, opts, 1, seed=3)
+
+
+@pytest.mark.parametrize("head_merge", [1, 2, 3, 16])
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,mode", [
+    (4, 70, 7, 64, "bf16", (16, 1, 64), P_ADD, ra2a.MODE_STAGED),
+    (3, 33, 6, 40, "bf16", (8, 2, 40), P_SET, ra2a.MODE_STAGED),
+    (4, 70, 7, 64, "bf16", (16, 1, 64), P_SET, ra2a.MODE_DIRECT),
+    (2, 20, 5, 48, "f32", (8, 1, 16), P_ADD, ra2a.MODE_STAGED),
+])
+def test_emulated_head_merge(head_merge, W, S, H, D, dtype, tile, proto, mode):
+    opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2],
+                     protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD, ring=2,
+                     consumer_split=2, head_merge=head_merge, mode=mode)
+    check_emulation(W, S, H, D, dtype, opts, 2, seed=11)

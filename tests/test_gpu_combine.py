@@ -4,7 +4,8 @@ Every case compares the HIP path (called through the C ABI) with the oracle
 byte for byte, and the final signal arrays with the protocol model's closed
 forms.  Sizes: small ragged cases that span several tiles with ragged tails,
 edge cases (W=1, one-byte elements, tiles larger than the problem, ring depth
-1), and the four combine workloads at their full sizes.
+1), and the four combine workloads at their full sizes, in the direct mode
+(the default), the staged mode and the two-phase variant.
 """
 import numpy as np
 import pytest
@@ -21,7 +22,27 @@ pytestmark = pytest.mark.gpu
 
 
 def expected_signal_array(wl, opts, csplit):
-    return expected.expected_signal_array(wl.W, wl.S, wl.H, wl.D, opts, csplit)
+    return expected.expected_signal_array(wl.W, wl.S, wl.H, wl.D, opts, csplit, wl.dtype)
+
+
+TAKEN = 1 << 63
+
+
+def check_queue_words(q, opts):
+    """Per group: the home claim counter moved, or (staged XCD-local mode only)
+    another XCD, named in bits 32..39, took the group over and its counter moved;
+    every group is marked fully claimed."""
+    q = q.astype(np.uint64)
+    assert len(q) == ra2a.QUEUE_SLOTS == 18
+    assert int(q[16]) == 0xFF and int(q[17]) == 0, q[16:]
+    for g, (head, taker) in enumerate(q[:16].reshape(8, 2)):
+        head, taker = int(head), int(taker)
+        if head & TAKEN:
+            assert not opts.agent_sync and opts.mode == ra2a.MODE_STAGED, \
+                f"group {g} taken over, but only the staged XCD-local mode binds groups to XCDs"
+            assert 1 <= (head >> 32) & 0xFF <= 8 and taker >= 1, (g, hex(head), taker)
+        else:
+            assert head >= 1 and taker == 0, (g, head, taker)
 
 
 def run_and_check(wl, opts, variant="pipelined", inputs=None, want=None, check_signals=True,
@@ -48,6 +69,7 @@ def run_and_check(wl, opts, variant="pipelined", inputs=None, want=None, check_s
             exp = expected_signal_array(wl, opts, cs)
             for j in range(wl.W):
                 np.testing.assert_array_equal(case.signals(j), exp, err_msg=f"signals of rank {j}")
+            check_queue_words(case.queue_words(), opts)
     finally:
         case.close()
 
@@ -70,16 +92,25 @@ SMALL = [
 
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
 @pytest.mark.parametrize("csplit", [1, 3])
-def test_small_pipelined(W, S, H, D, dtype, tile, proto, ring, csplit):
+def test_small_staged(W, S, H, D, dtype, tile, proto, ring, csplit):
     wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S, tile=tile, protocol=proto)
-    opts = opts_for(wl, ring=ring, consumer_split=csplit, producer_batch=2)
+    opts = opts_for(wl, ring=ring, consumer_split=csplit, mode=ra2a.MODE_STAGED)
     run_and_check(wl, opts)
 
 
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
+@pytest.mark.parametrize("agent", [0, 1])
+def test_small_direct(W, S, H, D, dtype, tile, proto, ring, agent):
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S + 2, tile=tile, protocol=proto)
+    opts = opts_for(wl, agent_sync=agent)
+    run_and_check(wl, opts, csplit=1)
+
+
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL[:6])
-def test_small_pipelined_agent_sync(W, S, H, D, dtype, tile, proto, ring):
+def test_small_staged_agent_sync(W, S, H, D, dtype, tile, proto, ring):
     wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S + 1, tile=tile, protocol=proto)
-    opts = opts_for(wl, ring=ring, consumer_split=2, producer_batch=3, agent_sync=1)
+    opts = opts_for(wl, ring=ring, consumer_split=2, lookahead=2, agent_sync=1,
+                    mode=ra2a.MODE_STAGED)
     run_and_check(wl, opts)
 
 
@@ -89,17 +120,24 @@ def test_small_two_phase(W, S, H, D, dtype, tile, proto, ring):
     run_and_check(wl, opts_for(wl), variant="two_phase")
 
 
-def test_iota_w2_worked_case():
+@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
+def test_iota_w2_worked_case(mode):
     wl = synthgen.WORKLOADS["iota_w2_s8_h4_d16_i32"]
-    opts = opts_for(wl, consumer_split=1)
+    opts = opts_for(wl, consumer_split=1, mode=mode)
     run_and_check(wl, opts)
 
 
+STAGED = ra2a.MODE_STAGED
+
+
 @pytest.mark.parametrize("knobs", [
-    dict(wg_per_cu=1, producer_share=1), dict(wg_per_cu=4, producer_share=3),
-    dict(producer_batch=1), dict(producer_batch=16, consumer_split=8),
-    dict(agent_sync=1), dict(agent_sync=1, producer_batch=5, consumer_split=3),
-    dict(stream_batch=1), dict(stream_batch=3, ring=1), dict(stream_batch=1000, ring=4),
+    dict(wg_per_cu=1, mode=STAGED), dict(wg_per_cu=4, mode=STAGED), dict(wg_per_cu=1),
+    dict(lookahead=1, mode=STAGED), dict(lookahead=-1, consumer_split=8, mode=STAGED),
+    dict(lookahead=1000, ring=3, mode=STAGED),
+    dict(agent_sync=1, mode=STAGED), dict(agent_sync=1, lookahead=1, consumer_split=3, mode=STAGED),
+    dict(stream_batch=1, mode=STAGED), dict(stream_batch=3, ring=1, mode=STAGED),
+    dict(stream_batch=1000, ring=4, mode=STAGED),
+    dict(head_merge=1, mode=STAGED), dict(head_merge=2, ring=1, mode=STAGED), dict(head_merge=3),
 ])
 def test_launch_shapes_do_not_change_results(knobs):
     wl = synthgen.small_workload(8, 200, 3, 96, "bf16", seed=5, tile=(32, 1, 96),
@@ -115,7 +153,7 @@ def test_back_to_back_launches_reset_signals():
     """A second launch on new data must not be satisfied by the first one's signals."""
     wl = synthgen.small_workload(4, 64, 2, 64, "bf16", seed=1, tile=(16, 1, 64),
                                  protocol=synthgen.PROTOCOL_ADD)
-    opts = opts_for(wl, consumer_split=2, ring=1)
+    opts = opts_for(wl, consumer_split=2, ring=1, mode=ra2a.MODE_STAGED)
     case = CombineCase(wl, opts)
     try:
         for seed in (1, 2, 3):
@@ -136,10 +174,11 @@ def test_back_to_back_launches_reset_signals():
         case.close()
 
 
-def test_pipelined_equals_two_phase_bitwise():
+@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
+def test_pipelined_equals_two_phase_bitwise(mode):
     """The barrier-synchronised variant as a differential for the signal-pipelined one."""
     wl = synthgen.small_workload(8, 300, 4, 72, "f16", seed=9, tile=(24, 1, 72))
-    case = CombineCase(wl, opts_for(wl, consumer_split=2))
+    case = CombineCase(wl, opts_for(wl, consumer_split=2, mode=mode))
     try:
         ins = synthgen.make_inputs(wl)
         case.upload(ins)
@@ -166,33 +205,46 @@ def test_special_float_payloads_survive():
     rng = np.random.default_rng(0)
     ins = [specials[rng.integers(0, len(specials), size=(S * W, H, D))].view(np.float32)
            for _ in range(W)]
-    run_and_check(wl, opts_for(wl, consumer_split=1), inputs=ins)
+    run_and_check(wl, opts_for(wl), inputs=ins)
+    run_and_check(wl, opts_for(wl, consumer_split=1, mode=ra2a.MODE_STAGED), inputs=ins)
     run_and_check(wl, opts_for(wl), variant="two_phase", inputs=ins)
 
 
 # ---- full-size workloads ------------------------------------------------------------
 
+_FULL_CACHE = {}
+
+
 def full_case(name, variant, **kw):
     wl = synthgen.WORKLOADS[name]
-    say(f"[full] generating {name}")
-    ins = synthgen.make_inputs(wl)
-    say(f"[full] oracle {name}")
-    want = oracle.combine(ins)
+    if name not in _FULL_CACHE:
+        _FULL_CACHE.clear()
+        say(f"[full] generating {name}")
+        ins = synthgen.make_inputs(wl)
+        say(f"[full] oracle {name}")
+        _FULL_CACHE[name] = (ins, oracle.combine(ins))
+    ins, want = _FULL_CACHE[name]
+    if variant == "staged":
+        kw["mode"] = ra2a.MODE_STAGED
+        variant = "pipelined"
+    else:
+        kw.pop("consumer_split", None)
     opts = opts_for(wl, consumer_split=kw.pop("consumer_split", 1), **kw)
-    run_and_check(wl, opts, variant=variant, inputs=ins, want=want)
+    run_and_check(wl, opts, variant=variant, inputs=ins, want=want,
+                  csplit=None if opts.mode == ra2a.MODE_STAGED else 1)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "two_phase"])
 def test_full_ep_combine_w8_bf16(variant):
     full_case("ep_combine_w8_s512_h16_d128_bf16", variant)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "two_phase"])
 def test_full_moe_combine_w8_d7168(variant):
     full_case("moe_combine_w8_s4096_h1_d7168_bf16", variant, consumer_split=4)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "two_phase"])
 def test_full_straggler_w16_f32(variant):
     wl = synthgen.WORKLOADS["straggler_w16_s2048_h32_d128_f32"]
     full_case("straggler_w16_s2048_h32_d128_f32", variant,
