@@ -294,6 +294,49 @@ int ra2a_rev_all2all_ex(const void *in, void *out, uint64_t *signals, int W, int
 int ra2a_rev_all2all_two_phase(const void *in, void *out, uint64_t *signals, int W, int64_t S,
                                int64_t H, int64_t D, int dtype, void *stream);
 
+/* ---- AllGather + GEMM ---------------------------------------------------- */
+/* ("Triton-distributed Semantics", sections "Producer-Consumer Model" and
+ * "AllGather + GEMM Overlapping"; HyperParallel RFC, section 十
+ * fused_all_gather_matmul, read as C = gather(A) @ B with no reduction.)
+ *
+ * W row shards A_w (m_local x K bf16, row-major; shard w is `a_shards`' twin
+ * in slice w) are gathered into G (W*m_local x K bf16; `gathered`'s twin in
+ * slice `rank`, shard w at rows [w*m_local, (w+1)*m_local)), and
+ *     C = G @ B      (B: K x N bf16 row-major, C: W*m_local x N bf16 row-major)
+ * with fp32 accumulation on the matrix cores and bf16 output rounded to
+ * nearest even.  One persistent launch: every tile of `tile_rows` rows of a
+ * shard is copied in parts into G and signalled (SET 1 on its slot once all
+ * parts are in); each 256 x 256 output tile waits only for the tiles covering
+ * its rows.  Signals live in slice `rank`: W*ntiles tile signals, then W*ntiles
+ * part counters, then RA2A_QUEUE_SLOTS queue words (ntiles =
+ * ceil(m_local / min(tile_rows, m_local))); ra2a_ag_gemm_signal_slots gives
+ * the three counts.  Afterwards every tile signal holds 1 and every counter
+ * its tile's number of parts.  `b` and `c` are device pointers the caller owns
+ * (16- and 2-byte aligned; they must not overlap each other or the heap
+ * buffers); the heap buffers must be 16-byte aligned and must not overlap.
+ * K and N must be multiples of 8.  flags: RA2A_AG_AGENT_SYNC (device-wide
+ * release/acquire instead of XCD-local), RA2A_AG_SKIP_RESET (the caller has
+ * zeroed the signals on the stream).
+ * Errors: EINVAL (arguments), EUNSUPPORTED, EHIP; a device-side wait that gives
+ * up surfaces through ra2a_check as ETIMEOUT.                                  */
+#define RA2A_AG_AGENT_SYNC 1
+#define RA2A_AG_SKIP_RESET 2
+
+int ra2a_ag_gemm_signal_slots(int W, int64_t m_local, int tile_rows, int64_t *tile_slots,
+                              int64_t *count_slots, int64_t *queue_slots);
+
+int ra2a_ag_gemm(const void *a_shards, void *gathered, const void *b, void *c, uint64_t *signals,
+                 int W, int rank, int64_t m_local, int64_t K, int64_t N, int tile_rows, int flags,
+                 void *stream);
+
+/* Host check of the AllGather+GEMM work queues for a device of `num_xcd` XCDs
+ * (no GPU needed): every part and GEMM tile queued exactly once, parts cover
+ * each shard's rows once without straddling tiles, and every GEMM tile queued
+ * after all parts of the tiles it waits for.  *tasks_per_group (may be NULL)
+ * receives the queue length.  Returns EINVAL with a message on a violation.   */
+int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t N, int tile_rows,
+                            int num_xcd, int64_t *tasks_per_group);
+
 /* ---- diagnostics --------------------------------------------------------- */
 
 /* Wait for the device, then report and clear the heap's device error word:

@@ -23,7 +23,8 @@ __all__ = [
     "symm_heap_destroy", "symm_malloc", "symm_heap_info", "symm_at", "put", "get",
     "put_with_signal", "signal_op", "wait_signal", "signal_reset", "rev_all2all",
     "rev_all2all_ex", "rev_all2all_two_phase", "rev_all2all_signal_slots",
-    "rev_all2all_workspace_bytes", "check", "last_error", "version",
+    "rev_all2all_workspace_bytes", "check", "last_error", "version", "ag_gemm",
+    "ag_gemm_signal_slots", "debug_ag_gemm_plan", "AG_AGENT_SYNC", "AG_SKIP_RESET",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +35,7 @@ SIG_SET, SIG_ADD = 0, 1
 PROTO_ADD, PROTO_SET = 1, 2
 MODE_DIRECT, MODE_STAGED = 1, 2
 QUEUE_SLOTS = 18
+AG_AGENT_SYNC, AG_SKIP_RESET = 1, 2
 CMP_EQ, CMP_NE, CMP_GT, CMP_GE, CMP_LT, CMP_LE = range(6)
 SIG_STRIDE_BYTES = 128
 SIG_STRIDE_U64 = 16
@@ -109,6 +111,10 @@ def lib():
         "ra2a_rev_all2all_ex": (i32, [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp]),
         "ra2a_rev_all2all_two_phase": (i32, [vp, vp, vp, i32, i64, i64, i64, i32, vp]),
         "ra2a_check": (i32, [vp]),
+        "ra2a_ag_gemm_signal_slots": (i32, [i32, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                            ctypes.POINTER(i64)]),
+        "ra2a_ag_gemm": (i32, [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp]),
+        "ra2a_debug_ag_gemm_plan": (i32, [i32, i32, i64, i64, i64, i32, i32, ctypes.POINTER(i64)]),
         "ra2a_debug_emulate_pipelined": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp),
                                                ctypes.POINTER(vp), i32, i64, i64, i64, i32, vp,
                                                i32, i32]),
@@ -291,6 +297,30 @@ def debug_emulate_pipelined(inputs, W: int, S: int, H: int, D: int, dtype, opts=
     _ok(lib().ra2a_debug_emulate_pipelined(pin, pout, psig, W, S, H, D, _dtype(dtype),
                                            _opts(opts), num_cus, blocks_per_cu))
     return outs, sigs
+
+
+# ---- AllGather + GEMM -----------------------------------------------------------
+
+def ag_gemm_signal_slots(W: int, m_local: int, tile_rows: int) -> Tuple[int, int, int]:
+    """(tile signals, part counters, queue words) in the gathering rank's slice."""
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _ok(lib().ra2a_ag_gemm_signal_slots(W, m_local, tile_rows, ctypes.byref(a), ctypes.byref(b),
+                                        ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def ag_gemm(a_shards: int, gathered: int, b: int, c: int, signals: int, W: int, rank: int,
+            m_local: int, K: int, N: int, tile_rows: int = 128, flags: int = 0, stream=None) -> None:
+    _ok(lib().ra2a_ag_gemm(a_shards, gathered, b, c, signals, W, rank, m_local, K, N, tile_rows,
+                           flags, _stream(stream)))
+
+
+def debug_ag_gemm_plan(W: int, rank: int, m_local: int, K: int, N: int, tile_rows: int,
+                       num_xcd: int = 8) -> int:
+    """Host check of the AllGather+GEMM work queues; returns the queue length per group."""
+    n = ctypes.c_int64()
+    _ok(lib().ra2a_debug_ag_gemm_plan(W, rank, m_local, K, N, tile_rows, num_xcd, ctypes.byref(n)))
+    return n.value
 
 
 # ---- torch-backed heap --------------------------------------------------------

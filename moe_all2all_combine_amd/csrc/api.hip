@@ -10,6 +10,7 @@
 #include <string>
 #include <vector>
 
+#include "ag_gemm_geom.h"
 #include "combine_geom.h"
 #include "common.h"
 #include "launch.h"
@@ -787,6 +788,172 @@ RA2A_API int ra2a_rev_all2all_two_phase(const void* in, void* out, uint64_t* sig
         return fail(RA2A_EUNSUPPORTED, "two-phase combine: more than 2^31 vectors per slice");
     hipError_t e = ra2a::launch_two_phase(a, V, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "two-phase launch");
+    return ok();
+}
+
+// ===========================================================================
+// AllGather + GEMM
+
+namespace {
+
+// Plan of one AllGather+GEMM: everything but the device pointers.
+int plan_ag_gemm(int W, int rank, int64_t m_local, int64_t K, int64_t N, int tile_rows, int nxcd,
+                 bool agent_sync, ra2a::AgGemmArgs* a) {
+    if (W < 1) return fail(RA2A_EINVAL, "W must be >= 1");
+    if (rank < 0 || rank >= W) return fail(RA2A_EINVAL, "rank %d out of [0, %d)", rank, W);
+    if (m_local < 1 || K < 1 || N < 1) return fail(RA2A_EINVAL, "m_local, K and N must be >= 1");
+    if (K % 8 || N % 8) return fail(RA2A_EINVAL, "K and N must be multiples of 8 (16-byte rows)");
+    if (tile_rows < 1) return fail(RA2A_EINVAL, "tile_rows must be >= 1");
+    *a = ra2a::AgGemmArgs{};
+    a->W = W;
+    a->rank = rank;
+    a->m_local = m_local;
+    a->K = K;
+    a->N = N;
+    const int64_t tr = std::min<int64_t>(tile_rows, m_local);
+    a->tile_rows = (int)tr;
+    a->ntiles = (int)cdiv(m_local, tr);
+    // AllGather parts of about 128 KiB, never straddling a tile
+    const int64_t row_bytes = K * 2;
+    const int64_t np0 = std::max<int64_t>(1, cdiv(tr * row_bytes, int64_t(128) << 10));
+    a->rpp = (int)cdiv(tr, np0);
+    a->np = (int)cdiv(tr, a->rpp);
+    const int64_t rows_last = m_local - (int64_t)(a->ntiles - 1) * tr;
+    a->np_last = (int)cdiv(rows_last, a->rpp);
+    a->nmb = (int)cdiv(m_local, ra2a::kGemmBM);
+    a->ncol = (int)cdiv(N, ra2a::kGemmBN);
+    a->NG = std::max(1, std::min(nxcd, ra2a::kNumXcd));
+    a->spg = (int)cdiv(W, a->NG);
+    a->sync = (agent_sync || nxcd > ra2a::kNumXcd) ? ra2a::kSyncAgent : ra2a::kSyncXcd;
+    a->ntasks_shard = ra2a::agg_tasks_per_shard(*a);
+    if ((double)a->ntasks_shard * a->spg >= 2147483647.0 - 65536.0 ||
+        (double)a->rpp * row_bytes >= 2147483647.0)
+        return fail(RA2A_EINVAL, "AllGather+GEMM too large for 32-bit task indices");
+    return RA2A_OK;
+}
+
+}  // namespace
+
+RA2A_API int ra2a_ag_gemm_signal_slots(int W, int64_t m_local, int tile_rows, int64_t* tile_slots,
+                                       int64_t* count_slots, int64_t* queue_slots) {
+    if (W < 1 || m_local < 1 || tile_rows < 1) return fail(RA2A_EINVAL, "bad arguments");
+    const int64_t tr = std::min<int64_t>(tile_rows, m_local);
+    const int64_t nt = (int64_t)W * cdiv(m_local, tr);
+    if (tile_slots) *tile_slots = nt;
+    if (count_slots) *count_slots = nt;
+    if (queue_slots) *queue_slots = ra2a::kQueueSlots;
+    return ok();
+}
+
+RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, void* c,
+                          uint64_t* signals, int W, int rank, int64_t m_local, int64_t K, int64_t N,
+                          int tile_rows, int flags, void* stream) {
+    if (flags & ~(RA2A_AG_AGENT_SYNC | RA2A_AG_SKIP_RESET)) return fail(RA2A_EINVAL, "unknown flags");
+    if (!a_shards || !gathered || !b || !c || !signals) return fail(RA2A_EINVAL, "NULL pointer");
+    ra2a_heap* h = find_heap(a_shards);
+    if (!h) return fail(RA2A_EINVAL, "a_shards is not inside a symmetric heap");
+    if (h->world != W) return fail(RA2A_EINVAL, "W=%d but the heap has %d slices", W, h->world);
+    if (!in_heap(h, gathered) || !in_heap(h, signals))
+        return fail(RA2A_EINVAL, "gathered and signals must be inside the heap of a_shards");
+    int nxcd = 1;
+    int rc = xcd_count(&nxcd);
+    if (rc) return rc;
+    ra2a::AgGemmArgs a{};
+    rc = plan_ag_gemm(W, rank, m_local, K, N, tile_rows, nxcd, (flags & RA2A_AG_AGENT_SYNC) != 0, &a);
+    if (rc) return rc;
+    const size_t a_off = sym_offset(h, a_shards), g_off = sym_offset(h, gathered);
+    const size_t s_off = sym_offset(h, signals);
+    const size_t shard_bytes = (size_t)(m_local * K * 2), g_bytes = (size_t)W * shard_bytes;
+    const int64_t nslots = ra2a::agg_queue_slot(a) + ra2a::kQueueSlots;
+    const size_t s_bytes = (size_t)nslots * RA2A_SIG_STRIDE_BYTES;
+    if (a_off % 16 || g_off % 16 || s_off % 8 || reinterpret_cast<uintptr_t>(b) % 16 ||
+        reinterpret_cast<uintptr_t>(c) % 2)
+        return fail(RA2A_EINVAL, "a_shards, gathered and b must be 16-byte aligned, signals 8, c 2");
+    if (a_off + shard_bytes > h->stride || g_off + g_bytes > h->stride || s_off + s_bytes > h->stride)
+        return fail(RA2A_EINVAL, "a shard, the gathered matrix or the signals cross the end of a slice");
+    auto overlap = [](size_t o1, size_t n1, size_t o2, size_t n2) { return o1 < o2 + n2 && o2 < o1 + n1; };
+    if (overlap(a_off, shard_bytes, g_off, g_bytes) || overlap(a_off, shard_bytes, s_off, s_bytes) ||
+        overlap(g_off, g_bytes, s_off, s_bytes))
+        return fail(RA2A_EINVAL, "a_shards, gathered and signals overlap");
+    rc = ensure_err(h);
+    if (rc) return rc;
+    a.base = h->base;
+    a.stride = (int64_t)h->stride;
+    a.a_off = (int64_t)a_off;
+    a.g_off = (int64_t)g_off;
+    a.sig_off = (int64_t)s_off;
+    a.b = static_cast<const uint16_t*>(b);
+    a.c = static_cast<uint16_t*>(c);
+    a.err = h->err;
+    a.timeout = timeout_ticks(h);
+    int ncu = 0;
+    rc = device_cus(&ncu);
+    if (rc) return rc;
+    int occ = 0;
+    hipError_t he = ra2a::ag_gemm_blocks_per_cu(a.sync, &occ);
+    if (he != hipSuccess) return hip_fail(he, "occupancy query");
+    if (occ < 1) return fail(RA2A_EUNSUPPORTED, "the AllGather+GEMM kernel does not fit a compute unit");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!(flags & RA2A_AG_SKIP_RESET)) {
+        he = ra2a::launch_signal_reset(h->base, (int64_t)h->stride, W, (int64_t)s_off, nslots, st);
+        if (he != hipSuccess) return hip_fail(he, "signal reset launch");
+    }
+    he = ra2a::launch_ag_gemm(a, occ * ncu, st);
+    if (he != hipSuccess) return hip_fail(he, "AllGather+GEMM launch");
+    return ok();
+}
+
+RA2A_API int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t N,
+                                     int tile_rows, int num_xcd, int64_t* tasks_per_group) {
+    ra2a::AgGemmArgs a{};
+    int rc = plan_ag_gemm(W, rank, m_local, K, N, tile_rows, num_xcd, false, &a);
+    if (rc) return rc;
+    if (tasks_per_group) *tasks_per_group = a.ntasks_shard * a.spg;
+    // every part of every shard exactly once, rows covering the shard; every GEMM
+    // tile exactly once and after every part of the tiles it waits for
+    for (int g = 0; g < a.NG; ++g) {
+        const int64_t total = a.ntasks_shard * a.spg;
+        for (int si = 0; si < a.spg; ++si) {
+            const int w = g + si * a.NG;
+            std::vector<int> row_hits((size_t)m_local, 0);
+            std::vector<int> parts_seen((size_t)a.ntiles, 0);
+            std::vector<int> gemm_seen((size_t)a.nmb * a.ncol, 0);
+            for (int64_t pos = (int64_t)si * a.ntasks_shard; pos < (int64_t)(si + 1) * a.ntasks_shard; ++pos) {
+                const ra2a::AgTask t = ra2a::agg_task_of(a, g, pos);
+                if (t.w != w) return fail(RA2A_EINVAL, "group %d position %lld: shard %d, expected %d", g, (long long)pos, t.w, w);
+                if (!t.gemm) {
+                    if (t.tile < 0 || t.tile >= a.ntiles || t.part < 0 || t.part >= ra2a::agg_parts_of_tile(a, t.tile) || t.rows < 1)
+                        return fail(RA2A_EINVAL, "bad AllGather part (tile %d part %d rows %lld)", t.tile, t.part, (long long)t.rows);
+                    if (t.row0 < (int64_t)t.tile * a.tile_rows || t.row0 + t.rows > std::min<int64_t>((int64_t)(t.tile + 1) * a.tile_rows, m_local))
+                        return fail(RA2A_EINVAL, "AllGather part straddles its tile");
+                    for (int64_t r = t.row0; r < t.row0 + t.rows; ++r) row_hits[(size_t)r]++;
+                    parts_seen[(size_t)t.tile]++;
+                } else {
+                    if (t.mb < 0 || t.mb >= a.nmb || t.nb < 0 || t.nb >= a.ncol)
+                        return fail(RA2A_EINVAL, "bad GEMM tile (%d, %d)", t.mb, t.nb);
+                    gemm_seen[(size_t)t.mb * a.ncol + t.nb]++;
+                    int first, last;
+                    ra2a::agg_block_tiles(a, t.mb, &first, &last);
+                    if (first < 0 || last > a.ntiles || first >= last)
+                        return fail(RA2A_EINVAL, "GEMM row block %d waits for tiles [%d, %d)", t.mb, first, last);
+                    for (int x = first; x < last; ++x)
+                        if (parts_seen[(size_t)x] != ra2a::agg_parts_of_tile(a, x))
+                            return fail(RA2A_EINVAL, "group %d position %lld: GEMM tile (%d, %d) waits for tile %d "
+                                        "whose parts are queued after it", g, (long long)pos, t.mb, t.nb, x);
+                    // its rows must lie inside the tiles it waits for
+                    const int64_t r0 = (int64_t)t.mb * ra2a::kGemmBM;
+                    const int64_t r1 = std::min<int64_t>(r0 + ra2a::kGemmBM, m_local);
+                    if (r0 < (int64_t)first * a.tile_rows || r1 > std::min<int64_t>((int64_t)last * a.tile_rows, m_local))
+                        return fail(RA2A_EINVAL, "GEMM row block %d is not covered by tiles [%d, %d)", t.mb, first, last);
+                }
+            }
+            for (int x : row_hits)
+                if (x != 1) return fail(RA2A_EINVAL, "shard %d: AllGather parts do not cover its rows once", w);
+            for (int x : gemm_seen)
+                if (x != 1) return fail(RA2A_EINVAL, "shard %d: GEMM tiles are not each queued once", w);
+        }
+        (void)total;
+    }
     return ok();
 }
 

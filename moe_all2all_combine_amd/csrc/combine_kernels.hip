@@ -11,6 +11,7 @@
 #include "common.h"
 #include "device.h"
 #include "launch.h"
+#include "queue.h"
 
 namespace ra2a {
 
@@ -271,91 +272,44 @@ __device__ __forceinline__ bool run_item(const PipeArgs& a, int g, int64_t it, i
     return true;
 }
 
-// Queue words of group g (slice 0, after the hand-back counters): the claim
-// counter of its home XCD, whose top bit marks a group taken over by another
-// XCD (bits 32..39: that XCD + 1), and the claim counter of such a taker.
-constexpr uint64_t kTaken = 1ull << 63;
-constexpr uint64_t kOwnerMask = 0xFFull << 32;
-
 template <int V, int SYNC, bool DIRECT>
 __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a) {
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
-    constexpr bool kOwned = SYNC == kSyncXcd && !DIRECT;  // groups bound to one XCD
+    // Staged mode with XCD-local sync binds each group to one XCD (queue.h).
+    // Otherwise (device-wide sync, or the direct mode, where no workgroup reads
+    // data another one wrote during the launch) any workgroup serves any group:
+    // its home group first, then it helps the others.
+    constexpr bool kOwned = SYNC == kSyncXcd && !DIRECT;
+    // queue words: slice 0, after the hand-back counters
     uint64_t* const qw = reinterpret_cast<uint64_t*>(a.base + a.sig_off) +
                          (a.regionA + a.regionB) * kSigStrideU64;
-    uint64_t* const drained = qw + (int64_t)(2 * kNumXcd) * kSigStrideU64;
     const uint32_t xcc = xcc_id();
     const int home = SYNC == kSyncXcd ? (int)(xcc % (uint32_t)a.NG) : (int)(blockIdx.x % a.NG);
-    // thread 0's claim state
-    uint64_t* ctr = nullptr;  // the counter claims of the current group come from
-    uint64_t known = 0;       // groups known to be fully claimed (copy of `drained`)
-    bool stale = true;        // `known` may be out of date
+    QueueClaim qc;  // thread 0's
     int k = 0;
     for (int gi = 0; gi < a.NG; ++gi) {
         const int g = (home + gi) % a.NG;
-        uint64_t* const head = qw + (int64_t)(2 * g) * kSigStrideU64;
-        uint64_t* const taker = head + kSigStrideU64;
-        // First claim.  Staged mode with XCD-local sync: the home XCD claims
-        // directly (one atomic; the returned word says whether another XCD took
-        // the group over first); another XCD takes over a group only if its home
-        // XCD has not claimed anything yet.  Otherwise (device-wide sync, or the
-        // direct mode, where no workgroup reads data another one wrote during the
-        // launch) any workgroup claims from any group: home group first, then it
-        // helps the others.  Leaving a group, one load of `drained` tells which
-        // groups are still worth a visit.
-        if (threadIdx.x == 0) {
-            int64_t first = -1;
-            if (gi > 0 && stale) {
-                known = __hip_atomic_load(drained, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                stale = false;
-            }
-            if ((known >> g) & 1ull) {
-                // fully claimed: nothing to do here
-            } else if (!kOwned || gi == 0) {
-                const uint64_t h =
-                    __hip_atomic_fetch_add(head, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (!(h & kTaken)) first = (int64_t)h;
-                ctr = head;
-            } else {
-                const uint64_t mine = kTaken | ((uint64_t)(xcc + 1u) << 32);
-                uint64_t cur = 0;
-                __hip_atomic_compare_exchange_strong(head, &cur, mine, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (cur == 0ull || (cur & (kTaken | kOwnerMask)) == mine) {
-                    first = (int64_t)__hip_atomic_fetch_add(taker, 1ull, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
-                    ctr = taker;
-                }
-            }
-            lds_pos[k & 1] = first;
-        }
+        if (threadIdx.x == 0) lds_pos[k & 1] = queue_first<kOwned>(qw, g, gi, xcc, qc);
         __syncthreads();
         // positions are wave-uniform: keep them (and all task geometry) scalar
         int64_t pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
         ++k;
         if (pos < 0) continue;
         const GroupQueue Q = group_queue(a, g);
-        if (threadIdx.x == 0) stale = true;
         // Pieces are software-pipelined: once a piece's last stores are issued, the
         // next task is looked up and, if it is a piece that need not wait, its
         // first round of loads goes out before the release of the current piece
         // (whose drain waits for both), so the two latencies overlap.
         while (true) {
             if (pos >= Q.total) {
-                // the group is fully claimed; the one workgroup whose claim landed
-                // exactly at the end says so (no wait: same-address atomics
-                // serialise, so they are kept few)
-                if (threadIdx.x == 0 && pos == Q.total)
-                    __hip_atomic_fetch_or(drained, 1ull << g, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+                if (threadIdx.x == 0) queue_drained(qw, g, pos, Q.total, qc);
                 break;
             }
             // claim the next position while this task runs (positions a workgroup
             // claims increase, so it still runs its tasks in queue order)
             uint64_t nxt = 0;
-            if (threadIdx.x == 0)
-                nxt = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (threadIdx.x == 0) nxt = queue_next(qc);
             int64_t idx = 0;
             if (!task_of(Q, pos, &idx)) {
                 if (!run_item<V, SYNC, DIRECT>(a, g, idx, &lds_flag))
@@ -397,9 +351,7 @@ __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a)
                 group_release<SYNC>();
                 piece_signal(a, p.sig, p.sig_step, p.nsig);
                 if (!next_loaded) break;
-                if (threadIdx.x == 0)
-                    nxt = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+                if (threadIdx.x == 0) nxt = queue_next(qc);
             }
         }
     }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ag_gemm_geom.h"
 #include "common.h"
 
 namespace ra2a {
@@ -14,6 +15,8 @@ hipError_t launch_pipelined(const PipeArgs& a, int V, int grid, hipStream_t st);
 hipError_t pipelined_blocks_per_cu(int V, int sync, int direct, int* n);
 hipError_t launch_xcc_probe(uint32_t* out, int n, hipStream_t st);
 hipError_t launch_two_phase(const TwoPhaseArgs& a, int V, hipStream_t st);
+hipError_t launch_ag_gemm(const AgGemmArgs& a, int grid, hipStream_t st);
+hipError_t ag_gemm_blocks_per_cu(int sync, int* n);
 
 // One-sided primitives.
 hipError_t launch_put(uint8_t* dst, const uint8_t* src, int64_t bytes, hipStream_t st);
