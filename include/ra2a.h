@@ -314,13 +314,17 @@ int ra2a_rev_all2all_two_phase(const void *in, void *out, uint64_t *signals, int
  * its tile's number of parts.  `b` and `c` are device pointers the caller owns
  * (16- and 2-byte aligned; they must not overlap each other or the heap
  * buffers); the heap buffers must be 16-byte aligned and must not overlap.
- * K and N must be multiples of 8.  flags: RA2A_AG_AGENT_SYNC (device-wide
- * release/acquire instead of XCD-local), RA2A_AG_SKIP_RESET (the caller has
- * zeroed the signals on the stream).
+ * K and N must be multiples of 8, and 512 * K below 2^32.  flags:
+ * RA2A_AG_AGENT_SYNC (device-wide release/acquire instead of XCD-local),
+ * RA2A_AG_SKIP_RESET (the caller has zeroed the signals on the stream),
+ * RA2A_AG_B_TRANSPOSED (see below).
  * Errors: EINVAL (arguments), EUNSUPPORTED, EHIP; a device-side wait that gives
  * up surfaces through ra2a_check as ETIMEOUT.                                  */
 #define RA2A_AG_AGENT_SYNC 1
 #define RA2A_AG_SKIP_RESET 2
+#define RA2A_AG_B_TRANSPOSED 4 /* `b` holds B^T (N x K row-major); otherwise the
+                                  library transposes B into a workspace it owns
+                                  (hipMalloc'd once per heap, freed with it) */
 
 int ra2a_ag_gemm_signal_slots(int W, int64_t m_local, int tile_rows, int64_t *tile_slots,
                               int64_t *count_slots, int64_t *queue_slots);

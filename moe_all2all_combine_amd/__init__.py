@@ -25,6 +25,7 @@ __all__ = [
     "rev_all2all_ex", "rev_all2all_two_phase", "rev_all2all_signal_slots",
     "rev_all2all_workspace_bytes", "check", "last_error", "version", "ag_gemm",
     "ag_gemm_signal_slots", "debug_ag_gemm_plan", "AG_AGENT_SYNC", "AG_SKIP_RESET",
+    "AG_B_TRANSPOSED",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +36,7 @@ SIG_SET, SIG_ADD = 0, 1
 PROTO_ADD, PROTO_SET = 1, 2
 MODE_DIRECT, MODE_STAGED = 1, 2
 QUEUE_SLOTS = 18
-AG_AGENT_SYNC, AG_SKIP_RESET = 1, 2
+AG_AGENT_SYNC, AG_SKIP_RESET, AG_B_TRANSPOSED = 1, 2, 4
 CMP_EQ, CMP_NE, CMP_GT, CMP_GE, CMP_LT, CMP_LE = range(6)
 SIG_STRIDE_BYTES = 128
 SIG_STRIDE_U64 = 16

@@ -24,7 +24,6 @@ namespace ra2a {
 
 constexpr int kGemmBM = 256;  // GEMM output tile rows
 constexpr int kGemmBN = 256;  // GEMM output tile columns
-constexpr int kGemmBK = 64;   // K per pipeline stage
 
 struct AgGemmArgs {
     uint8_t* base;        // heap base (slice 0)
@@ -32,7 +31,7 @@ struct AgGemmArgs {
     int64_t a_off;        // symmetric offset of the shards (shard w in slice w)
     int64_t g_off;        // symmetric offset of G (used in slice `rank`)
     int64_t sig_off;      // symmetric offset of the signals (used in slice `rank`)
-    const uint16_t* b;    // B, K x N row-major bf16
+    const uint16_t* bt;   // B^T, N x K row-major bf16 (B transposed)
     uint16_t* c;          // C, (W*m_local) x N row-major bf16
     uint32_t* err;
     uint64_t timeout;
@@ -58,28 +57,11 @@ AGG_HD int64_t agg_parts_before(const AgGemmArgs& a, int t) {
     return (int64_t)(a.ntiles - 1) * a.np + a.np_last;
 }
 
-// First AllGather tile whose first row is at or after row block i's first row.
-AGG_HD int agg_first_tile(const AgGemmArgs& a, int i) {
-    if (i >= a.nmb) return a.ntiles;
-    const int64_t row = (int64_t)i * kGemmBM;
-    const int64_t t = (row + a.tile_rows - 1) / a.tile_rows;
-    return t < a.ntiles ? (int)t : a.ntiles;
-}
-
-// Parts listed with row blocks [0, i): those of the tiles whose first row lies
-// before row block i.
-AGG_HD int64_t agg_block_parts(const AgGemmArgs& a, int i) {
-    return agg_parts_before(a, agg_first_tile(a, i));
-}
-
-// A shard's queue: the parts of row blocks 0 and 1, then for each row block i
-// its GEMM tiles followed by the parts of row block i + 2.  A GEMM tile of row
-// block i needs only tiles whose first row precedes row block i + 1, all of
-// them listed with row blocks <= i, i.e. earlier in the queue: every wait
-// points backwards.  Segment i starts at i * ncol + parts(row blocks < i + 2).
-AGG_HD int64_t agg_segment_base(const AgGemmArgs& a, int i) {
-    return (int64_t)i * a.ncol + agg_block_parts(a, i + 2 < a.nmb ? i + 2 : a.nmb);
-}
+// GEMM tiles are queued in groups of kColGroup column blocks: for each group,
+// every row block of the shard, then every column block of the group.  The
+// tiles a group keeps in flight on one XCD (its 32 compute units) then share
+// row blocks of G and column blocks of B in the XCD's L2.
+constexpr int kColGroup = 8;
 
 AGG_HD int64_t agg_tasks_per_shard(const AgGemmArgs& a) {
     return (int64_t)a.nmb * a.ncol + agg_parts_before(a, a.ntiles);
@@ -95,37 +77,32 @@ struct AgTask {
     int mb, nb;
 };
 
-// Task at position pos of group g's queue.
+// Task at position pos of group g's queue.  A shard's queue holds all its
+// AllGather parts (tile by tile), then its GEMM tiles in column-group order.
+// Every GEMM tile follows all parts it waits for: every wait points backwards.
+// (The parts are short copies; the GEMM tiles wait only for their own rows.)
 AGG_HD AgTask agg_task_of(const AgGemmArgs& a, int g, int64_t pos) {
     AgTask t;
     const int64_t si = pos / a.ntasks_shard;
-    int64_t r = pos - si * a.ntasks_shard;
+    const int64_t r = pos - si * a.ntasks_shard;
     t.w = g + (int)si * a.NG;
-    int64_t part = -1;
-    const int64_t head = agg_block_parts(a, a.nmb < 2 ? a.nmb : 2);
-    if (r < head) {
-        part = r;
-    } else {
-        // largest i with segment_base(i) <= r (bases increase with i)
-        int lo = 0, hi = a.nmb - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            if (agg_segment_base(a, mid) <= r)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int64_t off = r - agg_segment_base(a, lo);
-        if (off < a.ncol) {
-            t.gemm = true;
-            t.mb = lo;
-            t.nb = (int)off;
-            t.tile = t.part = 0;
-            t.row0 = t.rows = 0;
-            return t;
-        }
-        part = agg_block_parts(a, lo + 2 < a.nmb ? lo + 2 : a.nmb) + (off - a.ncol);
+    const int64_t nparts = agg_parts_before(a, a.ntiles);
+    if (r >= nparts) {
+        const int64_t q = r - nparts;
+        const int64_t per_group = (int64_t)a.nmb * kColGroup;
+        const int ngroups = (a.ncol + kColGroup - 1) / kColGroup;
+        int ng = (int)(q / per_group);
+        if (ng > ngroups - 1) ng = ngroups - 1;
+        const int64_t q1 = q - (int64_t)ng * per_group;
+        const int width = a.ncol - ng * kColGroup < kColGroup ? a.ncol - ng * kColGroup : kColGroup;
+        t.gemm = true;
+        t.mb = (int)(q1 / width);
+        t.nb = ng * kColGroup + (int)(q1 - (int64_t)t.mb * width);
+        t.tile = t.part = 0;
+        t.row0 = t.rows = 0;
+        return t;
     }
+    const int64_t part = r;
     t.gemm = false;
     t.mb = t.nb = 0;
     const int64_t full = (int64_t)(a.ntiles - 1) * a.np;

@@ -26,10 +26,11 @@ namespace ra2a {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// LDS tile rows are padded from 64 to 72 bf16 (144 bytes): the 16-byte reads of
-// 8 consecutive rows then start 4 banks apart and do not conflict.
-constexpr int kLdsStride = kGemmBK + 8;
-constexpr int kLdsOperand = kGemmBM * kLdsStride;  // bf16 elements of one operand stage
+constexpr int kGemmThreads = 256;  // 4 waves: 2 x 2 of 128 x 128 output elements each
+constexpr int kStageK = 32;        // k per pipeline stage
+constexpr int kStages = 4;         // LDS ring depth (3 stages in flight)
+constexpr int kStageElems = kGemmBM * kStageK;  // bf16 per operand per stage (16 KiB)
+constexpr int kDmaPerStage = 8;    // 16-byte LDS loads per thread per stage (4 A + 4 B)
 
 // float -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -38,139 +39,115 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-constexpr int kGemmThreads = 512;  // 8 waves: 2 (rows) x 4 (columns) of 128 x 64 each
+// LDS stage layout of an operand: 256 rows x 32 k (64 bytes per row, four 16-byte
+// chunks).  Chunk c of row r is stored at position c ^ g(r), g(r) = ((r >> 1) ^
+// (r >> 3)) & 3, so the 16-byte fragment reads of 8, and of 16, consecutive rows
+// at one chunk all land in different 16-byte bank groups (whether the LDS serves
+// 128 or 256 bytes per cycle).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
-// One pipeline stage's global loads per thread: 4 x 16 bytes of A (rows of G)
-// and a 4 (k) x 8 (n) block of B.
-struct StageRegs {
-    u32x4 a[4];
-    u32x4 b[4];
-};
+// Offset sent for a chunk that must read as zero: past any buffer's range.
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
-// Per-thread load cursor of a tile: thread t loads A rows t/8 + 64 i (i < 4),
-// 16-byte chunk t % 8 of the stage's 64 k, and B rows k 4 (t % 16) + i (i < 4)
-// at columns 8 (t / 16) .. +8.  Pointers advance by one stage per step.
-// Out-of-range rows / columns / k read as zero.
-struct StageCursor {
-    const uint16_t* a;  // A row t/8, k of chunk t % 8, this stage
-    const uint16_t* b;  // B row k 4 (t % 16), column 8 (t / 16), this stage
-    int64_t ka, kb;     // k of the A chunk / of the first B row, this stage
-    int arow;           // t / 8
-    bool bn;            // the thread's 8 B columns are inside N
-};
-
-__device__ __forceinline__ void stage_load(StageRegs& r, const StageCursor& c, int rows_valid,
-                                           int64_t K, int64_t N) {
+// Load one stage (k0 .. k0 + 32) of both operands straight into LDS.  Each wave
+// instruction fills 1 KiB of LDS, lane l landing at byte 16 l: 16 rows x 4
+// chunks; the lane therefore fetches the logical chunk that belongs at its
+// swizzled position.  Rows past the operand's buffer and k past K read as 0.
+__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                           uint16_t* lds_a, uint16_t* lds_b, int64_t K,
+                                           int64_t k0) {
+    const int w = (int)threadIdx.x >> 6;
+    const int l = (int)threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (c.arow + 64 * i < rows_valid && c.ka < K)
-            v = *reinterpret_cast<const u32x4*>(c.a + (int64_t)(64 * i) * K);
-        r.a[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (c.kb + i < K && c.bn) v = *reinterpret_cast<const u32x4*>(c.b + (int64_t)i * N);
-        r.b[i] = v;
+        const int rbase = 64 * w + 16 * i;
+        const int row = rbase + (l >> 2);
+        const int c = swz(row, l & 3);
+        const int64_t k = k0 + 8 * c;
+        const uint32_t off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(lds_a + rbase * kStageK), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(lds_b + rbase * kStageK), 16, off, 0, 0, 0);
     }
 }
 
-// Store a stage into LDS: A as loaded (row-major, k contiguous); B transposed
-// in registers so that each column n holds consecutive k (the matrix cores take
-// both operands k-contiguous): the 4 x 8 block becomes 8 columns of 4 k.
-__device__ __forceinline__ void stage_store(const StageRegs& r, uint16_t* __restrict__ lds_a,
-                                            uint16_t* __restrict__ lds_b) {
-    const int t = (int)threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (t >> 3) + 64 * i;
-        *reinterpret_cast<u32x4*>(lds_a + row * kLdsStride + 8 * (t & 7)) = r.a[i];
-    }
-    // r.b[kk] holds B[k = 4 (t%16) + kk][n = 8 (t/16) .. +8]: dword j packs columns 2j, 2j+1.
-    // Column nn packs (k 0, k 1) in its first dword and (k 2, k 3) in its second.
-    const int nbase = 8 * (t >> 4);
-    const int kofs = 4 * (t & 15);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        u32x2 lo, hi;  // columns 2j and 2j + 1
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            lo[q] = __builtin_amdgcn_perm(r.b[2 * q + 1][j], r.b[2 * q][j], 0x05040100u);
-            hi[q] = __builtin_amdgcn_perm(r.b[2 * q + 1][j], r.b[2 * q][j], 0x07060302u);
-        }
-        *reinterpret_cast<u32x2*>(lds_b + (nbase + 2 * j) * kLdsStride + kofs) = lo;
-        *reinterpret_cast<u32x2*>(lds_b + (nbase + 2 * j + 1) * kLdsStride + kofs) = hi;
-    }
+// Wait until at most n of this wave's vector memory operations are outstanding
+// (they complete in issue order): the LDS loads of the stages issued after the
+// one about to be read.
+__device__ __forceinline__ void wait_stages_after(int n) {
+    if (n >= 2)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (n == 1)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // One stage of matrix-core work: wave (wm, wn) owns rows 128 wm .. +128 and
-// columns 64 wn .. +64 of the tile as 4 x 2 blocks of 32 x 32; each k16 step
-// reads 4 A and 2 B fragments (16 bytes per lane) and issues 8 MFMAs.
-__device__ __forceinline__ void stage_mma(f32x16 (&acc)[4][2], const uint16_t* __restrict__ lds_a,
-                                          const uint16_t* __restrict__ lds_b) {
-    const int lane = (int)threadIdx.x & 63;
-    const int wave = (int)threadIdx.x >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
-    const int r = lane & 31;
-    const int kh = 8 * (lane >> 5);
+// columns 128 wn .. +128 of the tile as 4 x 4 blocks of 32 x 32; each k16 step
+// reads 4 A and 4 B fragments (16 bytes per lane) and issues 16 MFMAs
+// (v_mfma_f32_32x32x16_bf16: lane l supplies row / column l % 32, k 8 (l / 32) .. +8).
+__device__ __forceinline__ void stage_mma(f32x16 (&acc)[4][4], const uint16_t* lds_a,
+                                          const uint16_t* lds_b) {
+    const int l = (int)threadIdx.x & 63;
+    const int w = (int)threadIdx.x >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int r = l & 31;
 #pragma unroll
-    for (int kk = 0; kk < kGemmBK / 16; ++kk) {
-        bf16x8 fa[4], fb[2];
+    for (int kk = 0; kk < kStageK / 16; ++kk) {
+        const int c = 2 * kk + (l >> 5);
+        bf16x8 fa[4], fb[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int ra = 128 * wm + 32 * x + r;
+            const int rb = 128 * wn + 32 * x + r;
+            fa[x] = *reinterpret_cast<const bf16x8*>(lds_a + ra * kStageK + 8 * swz(ra, c));
+            fb[x] = *reinterpret_cast<const bf16x8*>(lds_b + rb * kStageK + 8 * swz(rb, c));
+        }
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-            fa[x] = *reinterpret_cast<const bf16x8*>(lds_a + (128 * wm + 32 * x + r) * kLdsStride + 16 * kk + kh);
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
-            fb[y] = *reinterpret_cast<const bf16x8*>(lds_b + (64 * wn + 32 * y + r) * kLdsStride + 16 * kk + kh);
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y)
+            for (int y = 0; y < 4; ++y)
                 acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
 }
 
-// C[rows, cols] of one 256 x 256 output tile; rows of G start at g_rows.
-__device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* __restrict__ g_rows,
-                                          int rows_valid, int64_t n0, uint16_t* __restrict__ c_rows,
-                                          uint16_t* __restrict__ lds) {
+// C[rows, cols] of one 256 x 256 output tile: rows of G from g_rows (rows_valid
+// of them), rows n0 .. of B^T (N x K), into c_rows.
+__device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g_rows,
+                                          int rows_valid, int64_t n0, uint16_t* c_rows,
+                                          uint16_t* lds) {
     // K and N opaque per tile: nothing derived from them is hoisted out of the
     // persistent task loop and kept alive across tiles.
     int64_t K = a.K, N = a.N;
     asm volatile("" : "+s"(K), "+s"(N));
-    f32x16 acc[4][2];
+    const int64_t cols_valid = N - n0 < kGemmBN ? N - n0 : kGemmBN;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(g_rows, (uint32_t)((int64_t)rows_valid * K * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bt + n0 * K, (uint32_t)(cols_valid * K * 2));
+    f32x16 acc[4][4];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
-    const int64_t nk = (K + kGemmBK - 1) / kGemmBK;
-    const int t = (int)threadIdx.x;
-    StageCursor cur;
-    cur.arow = t >> 3;
-    cur.ka = 8 * (t & 7);
-    cur.a = g_rows + (int64_t)cur.arow * K + cur.ka;
-    cur.kb = 4 * (t & 15);
-    const int64_t n = n0 + 8 * (t >> 4);
-    cur.bn = n < N;
-    cur.b = a.b + cur.kb * N + n;
-    StageRegs regs;
-    stage_load(regs, cur, rows_valid, K, N);
-    stage_store(regs, lds, lds + kLdsOperand);
-    __syncthreads();
+        for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
+    const int64_t nk = (K + kStageK - 1) / kStageK;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only this tile's LDS loads in flight below
+    for (int64_t s = 0; s < nk && s < kStages - 1; ++s) {
+        uint16_t* st = lds + (s % kStages) * 2 * kStageElems;
+        stage_load(ra, rb, st, st + kStageElems, K, s * kStageK);
+    }
     for (int64_t s = 0; s < nk; ++s) {
-        uint16_t* const cur_lds = lds + (s & 1) * 2 * kLdsOperand;
-        uint16_t* const nxt_lds = lds + ((s + 1) & 1) * 2 * kLdsOperand;
-        if (s + 1 < nk) {
-            cur.a += kGemmBK;
-            cur.ka += kGemmBK;
-            cur.b += kGemmBK * N;
-            cur.kb += kGemmBK;
-            stage_load(regs, cur, rows_valid, K, N);
+        const int64_t after = nk - 1 - s;
+        wait_stages_after(after < 2 ? (int)after : 2);
+        // every wave's loads of stage s have landed, and every wave is done with
+        // stage s - 1, whose slot the next load reuses
+        __builtin_amdgcn_s_barrier();
+        if (s + kStages - 1 < nk) {
+            uint16_t* st = lds + ((s + kStages - 1) % kStages) * 2 * kStageElems;
+            stage_load(ra, rb, st, st + kStageElems, K, (s + kStages - 1) * kStageK);
         }
-        stage_mma(acc, cur_lds, cur_lds + kLdsOperand);
-        if (s + 1 < nk) stage_store(regs, nxt_lds, nxt_lds + kLdsOperand);
-        __syncthreads();
+        const uint16_t* cur = lds + (s % kStages) * 2 * kStageElems;
+        stage_mma(acc, cur, cur + kStageElems);
     }
     // epilogue: accumulator register e of block (x, y) holds row 8 (e/4) + 4 (lane/32) + e%4,
     // column lane % 32 of the block.  (The empty asm makes the output pointer opaque
@@ -181,24 +158,59 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* _
     c_rows = reinterpret_cast<uint16_t*>(cbase);
     const int lane = (int)threadIdx.x & 63;
     const int wave = (int)threadIdx.x >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            const int64_t col = n0 + 64 * wn + 32 * y + (lane & 31);  // < N checked below
+        for (int y = 0; y < 4; ++y) {
+            const int64_t col = 128 * wn + 32 * y + (lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = 128 * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (row < rows_valid && col < N)
-                    c_rows[(int64_t)row * N + col] = (uint16_t)bf16_rne(acc[x][y][e]);
+                if (row < rows_valid && col < cols_valid)
+                    c_rows[(int64_t)row * N + n0 + col] = (uint16_t)bf16_rne(acc[x][y][e]);
             }
         }
+    __builtin_amdgcn_s_barrier();  // the LDS ring is free for the next tile
+}
+
+// B (K x N, row-major) -> B^T (N x K): each lane transposes one 8 x 8 block in
+// registers; a wave covers 8 x 8 blocks so that both its loads (rows of B) and
+// its stores (rows of B^T) are 128 contiguous bytes per group of 8 lanes.
+__global__ void __launch_bounds__(256) transpose_b_kernel(const uint16_t* __restrict__ b,
+                                                          uint16_t* __restrict__ bt, int64_t K,
+                                                          int64_t N) {
+    const int l = (int)threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwb = (N + 63) / 64;  // wave tiles along N
+    const int64_t k0 = (wave / nwb) * 64 + 8 * (l & 7);
+    const int64_t n0 = (wave % nwb) * 64 + 8 * (l >> 3);
+    if (k0 >= K || n0 >= N) return;
+    u32x4 in[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) in[kk] = *reinterpret_cast<const u32x4*>(b + (k0 + kk) * N + n0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u32x4 lo, hi;  // columns n0 + 2j and n0 + 2j + 1
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            lo[q] = __builtin_amdgcn_perm(in[2 * q + 1][j], in[2 * q][j], 0x05040100u);
+            hi[q] = __builtin_amdgcn_perm(in[2 * q + 1][j], in[2 * q][j], 0x07060302u);
+        }
+        *reinterpret_cast<u32x4*>(bt + (n0 + 2 * j) * K + k0) = lo;
+        *reinterpret_cast<u32x4*>(bt + (n0 + 2 * j + 1) * K + k0) = hi;
+    }
+}
+
+hipError_t launch_transpose_b(const uint16_t* b, uint16_t* bt, int64_t K, int64_t N, hipStream_t st) {
+    const int64_t waves = ((K + 63) / 64) * ((N + 63) / 64);
+    hipLaunchKernelGGL(transpose_b_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, b, bt, K, N);
+    return hipGetLastError();
 }
 
 template <int SYNC>
 __global__ void __launch_bounds__(kGemmThreads, 1) ag_gemm_kernel(AgGemmArgs a) {
-    __shared__ uint16_t lds[4 * kLdsOperand];  // 2 stages x (A, B^T), 147456 bytes
+    __shared__ uint16_t lds[kStages * 2 * kStageElems];  // 4 stages x (A, B^T), 128 KiB
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
     constexpr bool kOwned = SYNC == kSyncXcd;

@@ -29,6 +29,8 @@ struct ra2a_heap {
     bool owned = true;             // false: attached caller memory
     size_t ring_off = 0, ring_bytes = 0;   // cached staging ring (pipelined combine)
     size_t full_off = 0, full_bytes = 0;   // cached full staging (two-phase combine)
+    void* bt_ws = nullptr;         // B^T workspace of the AllGather+GEMM (library-owned)
+    size_t bt_bytes = 0;
     std::mutex mu;
 };
 
@@ -549,11 +551,13 @@ RA2A_API int ra2a_symm_heap_destroy(ra2a_heap_t* h) {
         if (it == g_heaps.end()) return fail(RA2A_EINVAL, "not a live heap");
         g_heaps.erase(it);
     }
-    const bool touched = h->owned || h->err;
+    const bool touched = h->owned || h->err || h->bt_ws;
     hipError_t e = touched ? hipDeviceSynchronize() : hipSuccess;
     hipError_t e1 = h->owned ? hipFree(h->base) : hipSuccess;
     hipError_t e2 = h->err ? hipFree(h->err) : hipSuccess;
+    hipError_t e3 = h->bt_ws ? hipFree(h->bt_ws) : hipSuccess;
     delete h;
+    if (e3 != hipSuccess) return hip_fail(e3, "hipFree(B^T workspace)");
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     if (e1 != hipSuccess) return hip_fail(e1, "hipFree(heap)");
     if (e2 != hipSuccess) return hip_fail(e2, "hipFree(error word)");
@@ -829,6 +833,9 @@ int plan_ag_gemm(int W, int rank, int64_t m_local, int64_t K, int64_t N, int til
     if ((double)a->ntasks_shard * a->spg >= 2147483647.0 - 65536.0 ||
         (double)a->rpp * row_bytes >= 2147483647.0)
         return fail(RA2A_EINVAL, "AllGather+GEMM too large for 32-bit task indices");
+    // a GEMM tile's operand rows are addressed with 32-bit buffer offsets
+    if ((double)ra2a::kGemmBM * row_bytes >= 4294967295.0 - 65536.0)
+        return fail(RA2A_EINVAL, "K too large for 32-bit operand offsets");
     return RA2A_OK;
 }
 
@@ -848,7 +855,8 @@ RA2A_API int ra2a_ag_gemm_signal_slots(int W, int64_t m_local, int tile_rows, in
 RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, void* c,
                           uint64_t* signals, int W, int rank, int64_t m_local, int64_t K, int64_t N,
                           int tile_rows, int flags, void* stream) {
-    if (flags & ~(RA2A_AG_AGENT_SYNC | RA2A_AG_SKIP_RESET)) return fail(RA2A_EINVAL, "unknown flags");
+    if (flags & ~(RA2A_AG_AGENT_SYNC | RA2A_AG_SKIP_RESET | RA2A_AG_B_TRANSPOSED))
+        return fail(RA2A_EINVAL, "unknown flags");
     if (!a_shards || !gathered || !b || !c || !signals) return fail(RA2A_EINVAL, "NULL pointer");
     ra2a_heap* h = find_heap(a_shards);
     if (!h) return fail(RA2A_EINVAL, "a_shards is not inside a symmetric heap");
@@ -882,7 +890,37 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
     a.a_off = (int64_t)a_off;
     a.g_off = (int64_t)g_off;
     a.sig_off = (int64_t)s_off;
-    a.b = static_cast<const uint16_t*>(b);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (flags & RA2A_AG_B_TRANSPOSED) {
+        a.bt = static_cast<const uint16_t*>(b);
+    } else {
+        // B^T into the heap's workspace (the matrix cores take both operands k-contiguous)
+        const size_t need = (size_t)(K * N * 2);
+        {
+            std::lock_guard<std::mutex> lk(h->mu);
+            if (h->bt_bytes < need) {
+                if (h->bt_ws) {
+                    hipError_t e = hipDeviceSynchronize();  // earlier launches may still read it
+                    if (e == hipSuccess) e = hipFree(h->bt_ws);
+                    h->bt_ws = nullptr;
+                    h->bt_bytes = 0;
+                    if (e != hipSuccess) return hip_fail(e, "B^T workspace release");
+                }
+                void* p = nullptr;
+                hipError_t e = hipMalloc(&p, need);
+                if (e != hipSuccess) {
+                    (void)hipGetLastError();
+                    return fail(RA2A_ENOMEM, "B^T workspace of %zu bytes: %s", need, hipGetErrorString(e));
+                }
+                h->bt_ws = p;
+                h->bt_bytes = need;
+            }
+        }
+        hipError_t e = ra2a::launch_transpose_b(static_cast<const uint16_t*>(b),
+                                                static_cast<uint16_t*>(h->bt_ws), K, N, st);
+        if (e != hipSuccess) return hip_fail(e, "B transpose launch");
+        a.bt = static_cast<const uint16_t*>(h->bt_ws);
+    }
     a.c = static_cast<uint16_t*>(c);
     a.err = h->err;
     a.timeout = timeout_ticks(h);
@@ -893,7 +931,6 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
     hipError_t he = ra2a::ag_gemm_blocks_per_cu(a.sync, &occ);
     if (he != hipSuccess) return hip_fail(he, "occupancy query");
     if (occ < 1) return fail(RA2A_EUNSUPPORTED, "the AllGather+GEMM kernel does not fit a compute unit");
-    hipStream_t st = static_cast<hipStream_t>(stream);
     if (!(flags & RA2A_AG_SKIP_RESET)) {
         he = ra2a::launch_signal_reset(h->base, (int64_t)h->stride, W, (int64_t)s_off, nslots, st);
         if (he != hipSuccess) return hip_fail(he, "signal reset launch");

@@ -17,6 +17,7 @@ hipError_t launch_xcc_probe(uint32_t* out, int n, hipStream_t st);
 hipError_t launch_two_phase(const TwoPhaseArgs& a, int V, hipStream_t st);
 hipError_t launch_ag_gemm(const AgGemmArgs& a, int grid, hipStream_t st);
 hipError_t ag_gemm_blocks_per_cu(int sync, int* n);
+hipError_t launch_transpose_b(const uint16_t* b, uint16_t* bt, int64_t K, int64_t N, hipStream_t st);
 
 // One-sided primitives.
 hipError_t launch_put(uint8_t* dst, const uint8_t* src, int64_t bytes, hipStream_t st);
