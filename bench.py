@@ -85,6 +85,55 @@ def cpu_baseline(wl, ins, budget_s=12.0):
                       f"({wl.algorithmic_bytes >> 20} MiB moved each), one thread, {el:.1f} s"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def ag_gemm_leg(steps):
+    """The AllGather+GEMM workload (W=8 shards of 1024 x 7168 gathered, times a
+    7168 x 4096 B; bf16 in, fp32 accumulation, bf16 out), for context: one call
+    = B transposed into the workspace + signal reset + the persistent launch."""
+    import numpy as np
+    import torch
+
+    import moe_all2all_combine_amd as ra2a
+    import synthgen
+
+    g = synthgen.AG_GEMM
+    W, m, K, N, tr = g.W, g.m_local, g.K, g.N, g.tile_rows
+    nsig = sum(ra2a.ag_gemm_signal_slots(W, m, tr))
+    sb = m * K * 2
+    heap = ra2a.SymmHeap(W, sb + W * sb + nsig * 128 + (1 << 16))
+    try:
+        oa, og, osg = heap.alloc(sb), heap.alloc(W * sb), heap.alloc(nsig * 128)
+        gen = torch.Generator(device="cuda").manual_seed(g.seed_a)
+        for w in range(W):
+            heap.view(oa, (m * K,), torch.bfloat16, w).copy_(
+                torch.randn(m * K, generator=gen, device="cuda") * g.std)
+        b = (torch.randn(K, N, generator=gen, device="cuda") * g.std).to(torch.bfloat16)
+        c = torch.empty(W * m, N, dtype=torch.bfloat16, device="cuda")
+        st = torch.cuda.current_stream()
+
+        def call():
+            ra2a.ag_gemm(heap.ptr(oa), heap.ptr(og), b.data_ptr(), c.data_ptr(), heap.ptr(osg),
+                         W, 0, m, K, N, tr, 0, st)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
+        flops = 2.0 * W * m * N * K
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"workload": g.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "calls": steps}
+    finally:
+        heap.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,8 +313,10 @@ def main():
         rec["put_copy"] = {"bytes_moved": 2 * W * nb, "launches": W,
                            "ms": round(ctx["put_copy"], 5),
                            "GBps": round(2 * W * nb / (ctx["put_copy"] * 1e-3) / 1e9, 2)}
-    rec["cpu_baseline"] = None if args.no_cpu else cpu_baseline(wl, ins)
     heap.close()
+    if args.legs == "all":
+        rec["ag_gemm"] = ag_gemm_leg(args.steps // 5 + 3)
+    rec["cpu_baseline"] = None if args.no_cpu else cpu_baseline(wl, ins)
     print(json.dumps(rec), flush=True)
 
 

@@ -201,9 +201,9 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
                     ? o->consumer_split
                     : (int)std::max<int64_t>(1, std::min<int64_t>(64, p->unit_bytes / (128 << 10)));
     if (p->direct) {
-        // no staging: no ring to reuse (R = every S-block), one part per unit
+        // no staging: no ring, no hand-back counters, no consumer work items
         p->R = std::max(p->nbs, 1);
-        p->regionB = (int64_t)p->R * p->nmhb * p->ndb * perW;
+        p->regionB = 0;
         p->ring_bytes = 0;
         p->csplit = 1;
     }
@@ -1094,12 +1094,46 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
             if (x != 1) return fail(RA2A_EINVAL, "stream groups do not partition the streams");
     }
 
-    // Each group's queue run strictly in queue order, one task at a time: every
-    // wait must already hold when its task comes up (the kernel's deadlock-
-    // freedom argument), and the queue must hold every piece and item once.
     const bool add = a.protocol == ra2a::kSigAdd;
     const int64_t sigA_len = pl.regionA * RA2A_SIG_STRIDE_BYTES;
-    for (int g = 0; g < a.NG; ++g) {
+    if (pl.direct) {
+        // Direct mode as the kernel runs it: every piece once in its global order,
+        // no waits, no hand-back counters.
+        const int64_t total = ra2a::total_pieces(a);
+        std::vector<int64_t> seen_g(a.NG, 0);
+        for (int64_t gp = 0; gp < total; ++gp) {
+            int g;
+            int64_t pc;
+            ra2a::global_piece(a, gp, &g, &pc);
+            if (g < 0 || g >= a.NG || pc < 0 || pc >= ra2a::group_pieces(a, g))
+                return fail(RA2A_EINVAL, "global piece %lld maps outside its group", (long long)gp);
+            seen_g[g]++;
+            const ra2a::Piece p = ra2a::piece_of(a, g, pc);
+            std::vector<std::pair<int64_t, int64_t>> offs;
+            rc = walk_plan(p.pl, V, 0, ra2a::plan_vectors(p.pl, V), &offs);
+            if (rc) return rc;
+            for (const auto& o : offs) {
+                if (!inside(p.src + o.first, V, p.r, in_off, nb))
+                    return fail(RA2A_EINVAL, "piece reads outside in of rank %d", p.r);
+                if (!inside(p.dst + o.second, V, p.j, out_off, nb))
+                    return fail(RA2A_EINVAL, "piece writes outside out of rank %d", p.j);
+                std::memcpy(&heap[(size_t)(p.dst + o.second)], &heap[(size_t)(p.src + o.first)], (size_t)V);
+            }
+            for (int k = 0; k < p.nsig; ++k) {
+                const int64_t sg = p.sig + k * p.sig_step;
+                if (!inside(sg, 8, p.j, sig_off, sigA_len))
+                    return fail(RA2A_EINVAL, "piece signal outside region A");
+                *u64(sg) = add ? *u64(sg) + 1 : 1;
+            }
+        }
+        for (int g = 0; g < a.NG; ++g)
+            if (seen_g[g] != ra2a::group_pieces(a, g))
+                return fail(RA2A_EINVAL, "group %d: direct schedule does not cover its pieces", g);
+    }
+    // Staged mode: each group's queue run strictly in queue order, one task at a
+    // time: every wait must already hold when its task comes up (the kernel's
+    // deadlock-freedom argument), and the queue must hold every piece and item once.
+    for (int g = 0; g < a.NG && !pl.direct; ++g) {
         const ra2a::GroupQueue Q = ra2a::group_queue(a, g);
         const int64_t npieces = ra2a::group_pieces(a, g);
         const int64_t nitems = ra2a::group_items(a, g);

@@ -201,6 +201,7 @@ struct Piece {
     int64_t credit;       // absolute byte offset of the ring hand-back counter (slice j)
     uint64_t credit_need; // wait until credit >= this (only if b >= R)
     int32_t sid;
+    int64_t unit_index;   // first data-signal slot index within slice j (timestamp row)
 };
 
 RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
@@ -244,7 +245,8 @@ RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
     }
     const int64_t sig_base = (int64_t)st.j * a.stride + a.sig_off;
     p.nsig = st.nh;
-    p.sig = sig_base + tile_slot(a, p.b, st.hb0, st.db, p.r) * kSigStrideU64 * 8;
+    p.unit_index = tile_slot(a, p.b, st.hb0, st.db, p.r);
+    p.sig = sig_base + p.unit_index * kSigStrideU64 * 8;
     p.sig_step = slot_step(a) * kSigStrideU64 * 8;
     int64_t ci = ((int64_t)p.slot * a.nmhb + st.mhb) * a.ndb + st.db;
     if (!add) ci = ci * a.W + p.r;
@@ -255,6 +257,24 @@ RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
 
 RA2A_HD int64_t group_pieces(const PipeArgs& a, int g) {
     return (int64_t)a.nbs * group_streams(a, g).ns * a.W;
+}
+
+// Direct mode: piece gp of the whole combine (groups in order, each group's
+// pieces in tile order); returns the group and the piece index inside it.
+RA2A_HD void global_piece(const PipeArgs& a, int64_t gp, int* g, int64_t* pc) {
+    int gg = 0;
+    int64_t n = group_pieces(a, 0);
+    while (gp >= n && gg + 1 < a.NG) {
+        gp -= n;
+        ++gg;
+        n = group_pieces(a, gg);
+    }
+    *g = gg;
+    *pc = gp;
+}
+
+RA2A_HD int64_t total_pieces(const PipeArgs& a) {
+    return (int64_t)a.nbs * a.nstreams * a.W;
 }
 
 // Consumer work item `it` of group g: part `part` of a unit (ADD: a tile with

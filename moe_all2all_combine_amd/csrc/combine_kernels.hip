@@ -56,6 +56,36 @@ __device__ __forceinline__ void copy_plan(const uint8_t* __restrict__ src, uint8
     const int vpr = p.run / V;
     int idx = lo + (int)threadIdx.x;
     if (idx >= hi) return;
+    if (p.B * p.C == 1 && lo == 0 && kThreads % vpr == 0) {
+        // one run per row and whole rows per step: each step moves kThreads / vpr
+        // rows down at the same column, so both offsets advance by constants
+        const int rows = kThreads / vpr;
+        const int row = idx / vpr, col = idx - row * vpr;
+        const uint8_t* s0 = src + row * p.sa + (int64_t)col * V;
+        uint8_t* d0 = dst + row * p.da + (int64_t)col * V;
+        const int64_t ds = rows * p.sa, dd = rows * p.da;
+        for (; idx < hi; idx += U * kThreads) {
+            T v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (idx + u * kThreads < hi) {
+                    const T* sp = reinterpret_cast<const T*>(s0 + u * ds);
+                    v[u] = NTL ? load_nt(sp) : *sp;
+                }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (idx + u * kThreads < hi) {
+                    T* dp = reinterpret_cast<T*>(d0 + u * dd);
+                    if (NTS)
+                        store_nt(v[u], dp);
+                    else
+                        *dp = v[u];
+                }
+            s0 += U * ds;
+            d0 += U * dd;
+        }
+        return;
+    }
     PlanCursor c = cursor_start(p, V, vpr, (uint32_t)idx, kThreads);
     for (; idx < hi; idx += U * kThreads) {
         T v[U];
@@ -123,99 +153,44 @@ __device__ __forceinline__ void copy_plan_buf(__amdgpu_buffer_rsrc_t src, uint32
 // The signal-pipelined persistent combine.
 //
 // Work is organised in tile streams: stream (j, merged head block, d block) is
-// the sequence of S-blocks b = 0 .. nbs-1 of destination j.  The streams are
-// cut into NG contiguous groups, one per XCD.  Each group has a work queue
-// (combine_geom.h: group_queue / task_of) holding its producer pieces (tile,
-// source r) and consumer work items (parts of a tile's unit) in an order in
-// which every wait points backwards.  Workgroups claim queue positions one at
-// a time with an atomic counter and run each task to completion, so the
+// the sequence of S-blocks b = 0 .. nbs-1 of destination j.  A producer piece
+// is one source r's part of a tile (stream, S-block).
+//
+// Direct mode (the default, direct_path below): producers store each piece into
+// its final place in out_j and signal it; nothing waits, the schedule is static.
+//
+// Staged mode: the streams are cut into NG contiguous groups, one per XCD.  Each
+// group has a work queue (combine_geom.h: group_queue / task_of) holding its
+// producer pieces and consumer work items (parts of a tile's unit) in an order
+// in which every wait points backwards.  Workgroups claim queue positions one
+// at a time with an atomic counter and run each task to completion, so the
 // earliest unfinished task can always proceed: no deadlock, whatever the
 // number of resident workgroups, and an ordinary launch suffices.
 //
-// Placement (staged mode, SYNC == kSyncXcd).  A group's tasks must all run on one XCD, so
-// that producers and consumers meet in that XCD's L2 and synchronise with the
-// XCD-local sequences of device.h instead of device-wide L2 write-backs and
-// invalidations.  A workgroup reads the XCD it runs on from the XCC_ID
-// register and claims from its own XCD's group; once that queue is drained it
-// may take over a group whose home XCD has not claimed anything (a group whose
-// XCD received no workgroup, or received them late), and then only workgroups
-// of the taking XCD serve it.  So every group is served, by one XCD, whatever
-// the dispatcher does.  SYNC == kSyncAgent uses device-wide release/acquire
-// and lets every workgroup help every group; so does the direct mode, whose
-// consumers read no data during the launch (only the signals, which are
-// device-scope atomics): its stores become visible to later work in stream
-// order, when the launch completes.
+// Placement (staged mode, SYNC == kSyncXcd).  A group's tasks must all run on
+// one XCD, so that producers and consumers meet in that XCD's L2 and
+// synchronise with the XCD-local sequences of device.h instead of device-wide
+// L2 write-backs and invalidations.  A workgroup reads the XCD it runs on from
+// the XCC_ID register and claims from its own XCD's group; once that queue is
+// drained it may take over a group whose home XCD has not claimed anything (a
+// group whose XCD received no workgroup, or received them late), and then only
+// workgroups of the taking XCD serve it.  So every group is served, by one XCD,
+// whatever the dispatcher does.  SYNC == kSyncAgent uses device-wide
+// release/acquire and lets every workgroup help every group.
 //
-// Producer piece: wait until ring slot b mod R of its stream has been handed
-// back by the consumers of S-block b - R (credit count; never in direct mode
-// or when the ring is not reused), copy in_r -> staging_j (direct mode: ->
-// out_j), release, then wave 0 signals the piece's signal tiles (SET 1 on the
-// piece's slot, or ADD 1 on the tile's slot).
+// Staged producer piece: wait until ring slot b mod R of its stream has been
+// handed back by the consumers of S-block b - R (credit count; never when the
+// ring is not reused), copy in_r -> staging_j, release, then wave 0 signals the
+// piece's signal tiles (SET 1 on the piece's slot, or ADD 1 on the tile's slot).
 //
-// Consumer item: wait until each of its signal tiles reads W (ADD) or 1 (SET),
-// copy its part of the unit staging_j -> out_j (direct mode: nothing left to
-// move), release, add 1 to the slot's hand-back count, optionally stamp the
-// completion time.
+// Staged consumer item: wait until each of its signal tiles reads W (ADD) or 1
+// (SET), copy its part of the unit staging_j -> out_j, release, add 1 to the
+// slot's hand-back count, optionally stamp the completion time.
 //
 // Every wait is also bounded in time (spin_until).
-// A piece's copy in rounds, so that the first round of the next piece can be
-// loaded while the current one drains: start() positions the thread on the
-// piece's vectors, load() issues one round of U loads per thread (non-
-// temporal: the input is read once), store() issues that round's stores.
-template <int V, int U, bool NTS>
-struct PieceMover {
-    using T = typename Vec<V>::T;
-    const uint8_t* src;
-    uint8_t* dst;
-    RowPlan pl;
-    int vpr, idx, hi;
-    PlanCursor c;
-    T v[U];
-    int64_t doff[U];
-
-    __device__ __forceinline__ void start(const uint8_t* s, uint8_t* d, const RowPlan& p) {
-        src = s;
-        dst = d;
-        pl = p;
-        vpr = p.run / V;
-        idx = (int)threadIdx.x;
-        hi = plan_vectors(p, V);
-        c = cursor_start(pl, V, vpr, (uint32_t)idx, kThreads);
-    }
-    __device__ __forceinline__ bool more() const { return idx < hi; }
-    __device__ __forceinline__ void load() {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            doff[u] = -1;
-            if (idx + u * kThreads < hi) {
-                v[u] = load_nt(reinterpret_cast<const T*>(src + c.so));
-                doff[u] = c.dofs;
-            }
-            cursor_advance(c, pl, vpr);
-        }
-    }
-    __device__ __forceinline__ void store() {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (doff[u] >= 0) {
-                T* dp = reinterpret_cast<T*>(dst + doff[u]);
-                if (NTS)
-                    store_nt(v[u], dp);
-                else
-                    *dp = v[u];
-            }
-        }
-        idx += U * kThreads;
-    }
-};
-
-// Whether a piece must wait before its copy starts: for the hand-back of its
-// ring slot (staged mode, ring reused) or as a delayed (straggler) source.
-__device__ __forceinline__ bool piece_waits(const PipeArgs& a, const Piece& p) {
-    return p.b >= a.R || (p.r == a.straggler && a.delay);
-}
-
-// The waits of piece_waits; false if a bounded wait gave up.
+// A piece's waits before its copy starts: for the hand-back of its ring slot
+// (staged mode, ring reused) and as a delayed (straggler) source.  False if a
+// bounded wait gave up.
 __device__ __forceinline__ bool piece_wait(const PipeArgs& a, const Piece& p, int* lds_flag) {
     if (p.b >= a.R &&
         !group_wait<false>(reinterpret_cast<const uint64_t*>(a.base + p.credit), kCmpGe,
@@ -239,7 +214,22 @@ __device__ __forceinline__ void piece_signal(const PipeArgs& a, int64_t sig, int
         sig_update(reinterpret_cast<uint64_t*>(a.base + sig + k * step), 1ull, op);
 }
 
-template <int V, int SYNC, bool DIRECT>
+// Staged mode, producer piece: wait for the ring slot's hand-back, copy in_r ->
+// staging_j (plain stores: the consumers read it back from this XCD's L2),
+// release, signal.
+template <int V, int SYNC>
+__device__ __forceinline__ bool run_piece(const PipeArgs& a, int g, int64_t pc, int* lds_flag) {
+    const Piece p = piece_of(a, g, pc);
+    if (!piece_wait(a, p, lds_flag)) return false;
+    copy_plan<V, 8, true, false>(a.base + p.src, a.base + p.dst, p.pl, 0, plan_vectors(p.pl, V));
+    group_release<SYNC>();
+    piece_signal(a, p.sig, p.sig_step, p.nsig);
+    return true;
+}
+
+// Staged mode, consumer item: wait for the unit's signal tiles, copy its part
+// staging_j -> out_j, release, hand the slot back.
+template <int V, int SYNC>
 __device__ __forceinline__ bool run_item(const PipeArgs& a, int g, int64_t it, int* lds_flag) {
     uint8_t* const base = a.base;
     const Item q = item_of(a, g, it, V);
@@ -250,7 +240,7 @@ __device__ __forceinline__ bool run_item(const PipeArgs& a, int g, int64_t it, i
                                             q.sig_step, q.nsig, kCmpEq, q.sig_want, a.timeout,
                                             a.err, lds_flag))
         return false;
-    if (!DIRECT && q.hi > q.lo) {
+    if (q.hi > q.lo) {
         if (SYNC == kSyncXcd) {
             const int64_t stg = (int64_t)q.j * a.stride + a.stg_off;
             copy_plan_buf<V, 8, kPolicySc1, true>(make_rsrc(base + stg, (uint32_t)a.ring_bytes),
@@ -272,15 +262,48 @@ __device__ __forceinline__ bool run_item(const PipeArgs& a, int g, int64_t it, i
     return true;
 }
 
+// Direct mode.  Producers store straight into out_j, so no consumer has data to
+// move: a tile is complete when its signal reaches W (ADD) or each of its W
+// slots reads 1 (SET), and the optional completion stamp of a tile is the
+// latest of its producers' stamps (an atomic max each).  Nothing waits on
+// anything, so a static schedule (piece gp to workgroup gp mod grid) is
+// deadlock-free at any residency and needs no queue; every atomic is issued
+// without a return value, so no drain waits for a round trip.  (Measured: issuing
+// the next piece's loads before this piece's release is slower here, not faster.)
+template <int V, int SYNC>
+__device__ __forceinline__ void direct_path(const PipeArgs& a, int* lds_flag) {
+    const int64_t total = total_pieces(a);
+    for (int64_t gp = blockIdx.x; gp < total; gp += gridDim.x) {
+        int g;
+        int64_t pc;
+        global_piece(a, gp, &g, &pc);
+        const Piece p = piece_of(a, g, pc);
+        if (!piece_wait(a, p, lds_flag)) return;
+        // final place: stream the stores past the L2
+        copy_plan<V, 8, true, true>(a.base + p.src, a.base + p.dst, p.pl, 0, plan_vectors(p.pl, V));
+        group_release<SYNC>();
+        piece_signal(a, p.sig, p.sig_step, p.nsig);
+        if (a.stamps && threadIdx.x < 64) {
+            const uint64_t now = rtc_now();
+            const int64_t step = slot_step(a);
+            for (int k = threadIdx.x; k < p.nsig; k += 64)
+                __hip_atomic_fetch_max(a.stamps + (int64_t)p.j * a.units_per_dest + p.unit_index + k * step,
+                                       now, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 template <int V, int SYNC, bool DIRECT>
 __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a) {
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
-    // Staged mode with XCD-local sync binds each group to one XCD (queue.h).
-    // Otherwise (device-wide sync, or the direct mode, where no workgroup reads
-    // data another one wrote during the launch) any workgroup serves any group:
-    // its home group first, then it helps the others.
-    constexpr bool kOwned = SYNC == kSyncXcd && !DIRECT;
+    if (DIRECT) {
+        direct_path<V, SYNC>(a, &lds_flag);
+        return;
+    }
+    // Staged mode.  XCD-local sync binds each group to one XCD (queue.h); with
+    // device-wide sync any workgroup serves any group, its home group first.
+    constexpr bool kOwned = SYNC == kSyncXcd;
     // queue words: slice 0, after the hand-back counters
     uint64_t* const qw = reinterpret_cast<uint64_t*>(a.base + a.sig_off) +
                          (a.regionA + a.regionB) * kSigStrideU64;
@@ -297,10 +320,6 @@ __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a)
         ++k;
         if (pos < 0) continue;
         const GroupQueue Q = group_queue(a, g);
-        // Pieces are software-pipelined: once a piece's last stores are issued, the
-        // next task is looked up and, if it is a piece that need not wait, its
-        // first round of loads goes out before the release of the current piece
-        // (whose drain waits for both), so the two latencies overlap.
         while (true) {
             if (pos >= Q.total) {
                 if (threadIdx.x == 0) queue_drained(qw, g, pos, Q.total, qc);
@@ -311,48 +330,13 @@ __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a)
             uint64_t nxt = 0;
             if (threadIdx.x == 0) nxt = queue_next(qc);
             int64_t idx = 0;
-            if (!task_of(Q, pos, &idx)) {
-                if (!run_item<V, SYNC, DIRECT>(a, g, idx, &lds_flag))
-                    return;  // a wait gave up: the error word is raised, everyone leaves
-                if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
-                __syncthreads();
-                pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
-                ++k;
-                continue;
-            }
-            // a run of pieces
-            PieceMover<V, 8, DIRECT> m;  // DIRECT: final place, stream stores past the L2
-            {
-                const Piece p = piece_of(a, g, idx);
-                if (!piece_wait(a, p, &lds_flag)) return;
-                m.start(a.base + p.src, a.base + p.dst, p.pl);
-                m.load();
-            }
-            while (true) {
-                const Piece p = piece_of(a, g, idx);
-                m.store();
-                while (m.more()) {
-                    m.load();
-                    m.store();
-                }
-                if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
-                __syncthreads();
-                pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
-                ++k;
-                bool next_loaded = false;
-                if (pos < Q.total && task_of(Q, pos, &idx)) {
-                    const Piece pn = piece_of(a, g, idx);
-                    if (!piece_waits(a, pn)) {
-                        m.start(a.base + pn.src, a.base + pn.dst, pn.pl);
-                        m.load();
-                        next_loaded = true;
-                    }
-                }
-                group_release<SYNC>();
-                piece_signal(a, p.sig, p.sig_step, p.nsig);
-                if (!next_loaded) break;
-                if (threadIdx.x == 0) nxt = queue_next(qc);
-            }
+            const bool ok = task_of(Q, pos, &idx) ? run_piece<V, SYNC>(a, g, idx, &lds_flag)
+                                                  : run_item<V, SYNC>(a, g, idx, &lds_flag);
+            if (!ok) return;  // a wait gave up: the error word is raised, everyone leaves
+            if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
+            __syncthreads();
+            pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
+            ++k;
         }
     }
 }

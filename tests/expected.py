@@ -24,6 +24,16 @@ def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):
     per = W if proto == SET else 1
     # merged head blocks: derived from the size of the hand-back region
     _, n_credit, _ = ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)
+    if direct:
+        # no ring and no consumer work: the data signals only
+        assert n_credit == 0
+        tiles = ProtocolSpec(W=W, nbs=nbs, nstreams=nhb * ndb, R=R, protocol=proto)
+        ns = nhb * ndb
+        a = np.zeros(nbs * ns * per, dtype=np.int64)
+        for k, v in expected_final_signals(tiles).items():
+            if k[0] == 0:
+                a[(k[2] * ns + k[1]) * per + (k[3] if proto == SET else 0)] = v
+        return a
     nmhb = n_credit // (R * ndb * per)
     assert nmhb * R * ndb * per == n_credit
     # data signals: one per signal tile, the model's closed form

@@ -80,11 +80,12 @@ def test_signal_slots_and_workspace():
     Q = ra2a.QUEUE_SLOTS
     # 64-token x 1-head x 128 tiles, ADD: one slot per (S-block, head) per slice
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
-    # direct mode (the default): every S-block is a ring slot; 256-B heads would
-    # merge 16 at a time into 4 KiB runs, but that leaves only 512 pieces, so
-    # 4 at a time (2048 pieces): 4 moved streams per destination
-    assert (a, b, q) == (8 * 16, 8 * 4, Q)
-    staged = ra2a.Opts(mode=ra2a.MODE_STAGED)  # ring of 8 = every S-block
+    # direct mode (the default): no ring, so no hand-back counters
+    assert (a, b, q) == (8 * 16, 0, Q)
+    # staged: ring of 8 = every S-block; 256-B heads would merge 16 at a time into
+    # 4 KiB runs, but that leaves only 512 pieces, so 4 at a time (2048 pieces):
+    # 4 moved streams per destination
+    staged = ra2a.Opts(mode=ra2a.MODE_STAGED)
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", staged)
     assert (a, b, q) == (8 * 16, 8 * 4, Q)
     a, b, _ = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16",
@@ -102,7 +103,7 @@ def test_signal_slots_and_workspace():
                                             ra2a.Opts(tile_s=32, mode=ra2a.MODE_STAGED))
     assert (a, b) == (128, 8)
     a, b, _ = ra2a.rev_all2all_signal_slots(8, 4096, 1, 7168, "bf16", ra2a.Opts(tile_s=32))
-    assert (a, b) == (128, 128)
+    assert (a, b) == (128, 0)
     # ragged: S=37 in tiles of 16 -> 3 blocks; D=40 in tiles of 16 -> 3 d blocks
     a, b, _ = ra2a.rev_all2all_signal_slots(3, 37, 2, 40, "bf16",
                                             ra2a.Opts(tile_s=16, tile_d=16, mode=ra2a.MODE_STAGED))

@@ -29,11 +29,15 @@ TAKEN = 1 << 63
 
 
 def check_queue_words(q, opts):
-    """Per group: the home claim counter moved, or (staged XCD-local mode only)
-    another XCD, named in bits 32..39, took the group over and its counter moved;
-    every group is marked fully claimed."""
+    """Staged mode, per group: the home claim counter moved, or (XCD-local sync
+    only) another XCD, named in bits 32..39, took the group over and its counter
+    moved; every group is marked fully claimed.  Direct mode: untouched."""
     q = q.astype(np.uint64)
     assert len(q) == ra2a.QUEUE_SLOTS == 18
+    if opts.mode != ra2a.MODE_STAGED:
+        # the direct mode runs a static schedule: no queue words are touched
+        assert not q.any(), q
+        return
     assert int(q[16]) == 0xFF and int(q[17]) == 0, q[16:]
     for g, (head, taker) in enumerate(q[:16].reshape(8, 2)):
         head, taker = int(head), int(taker)
