@@ -7,16 +7,19 @@ H=16 heads, D=128, bf16 values uniform(-1, 1) from seed 0, 64 x 1 x 128
 signal tiles with ADD-to-W tile signals.  Inputs are resident in HBM before
 timing starts.  So that the 256 MiB working set is not served from the 256 MB
 Infinity Cache, consecutive steps rotate through several in/out/signal buffer
-sets.  Two ways of issuing the steps are timed: serial (reset and combine back
-to back on one stream) and overlapped (a step's reset on a side stream, while
-the previous step's combine runs -- it touches only its own set's signals --
-and the step's combine waiting for it); `value` is the faster one, and both
-are reported.
+sets.  Three ways of issuing the steps are timed, every one of which zeroes a
+step's signals before any of its producers signals: in-launch (the library
+default: one launch per step, whose first workgroups zero the signals),
+serial (a reset launch, then the combine, on one stream) and overlapped (a
+step's reset launch on a side stream while the previous step's combine runs
+-- it touches only its own set's signals -- and the combine waiting for it);
+`value` is the fastest, and all three are reported.
 
 Prints one JSON line: metric and value (GB/s of algorithmic bytes: every input
 element read once and every output element written once, per step), the
-roofline of the persistent kernel from HIP events around its launches inside
-the timed region, and for context the staged mode, the two-phase variant, a
+roofline of the persistent kernel (its duration from HIP events around every
+launch, on the launch stream, in a separate pass over the same steps: events
+between kernels slow the steps themselves), and for context the staged mode, the two-phase variant, a
 plain copy of the same bytes with the library's put kernel, and the CPU
 oracle's rate on the host.
 
@@ -48,7 +51,7 @@ def log(msg):
 def kernel_source_hash():
     """Hash of the sources the persistent kernel is compiled from."""
     h = hashlib.sha256()
-    for f in ("combine_kernels.hip", "combine_geom.h", "device.h", "common.h"):
+    for f in ("combine_kernels.hip", "combine_geom.h", "device.h", "common.h", "queue.h"):
         with open(os.path.join(ROOT, "moe_all2all_combine_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -159,6 +162,7 @@ def main():
     torch.cuda.set_device(0)
     proto = ra2a.PROTO_SET if wl.protocol == synthgen.PROTOCOL_SET else ra2a.PROTO_ADD
     tiles = dict(tile_s=wl.tile_s, tile_h=wl.tile_h, tile_d=wl.tile_d, protocol=proto)
+    opts_lib = ra2a.Opts(**tiles)  # the library's own reset (in-launch in direct mode)
     opts = ra2a.Opts(skip_reset=1, **tiles)
     opts_st = ra2a.Opts(skip_reset=1, mode=ra2a.MODE_STAGED, **tiles)
     nsig = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o)) for o in (opts, opts_st))
@@ -186,9 +190,11 @@ def main():
     # resets its signals before its combine starts (event order).
     done = [None] * NSETS
 
-    def step(k, o, ev=None, overlap=True):
+    def step(k, o, overlap=True, reset=True):
         oi, oo, osg = sets[k % NSETS]
-        if overlap:
+        if not reset:
+            pass  # the combine zeroes its own signals
+        elif overlap:
             if done[k % NSETS] is not None:
                 side.wait_event(done[k % NSETS])
             ra2a.signal_reset(hs, heap.ptr(osg), nsig, side)
@@ -197,51 +203,57 @@ def main():
             stream.wait_event(ready)
         else:
             ra2a.signal_reset(hs, heap.ptr(osg), nsig, stream)
-        if ev is not None:
-            ev[0].record(stream)
         ra2a.rev_all2all_ex(heap.ptr(oi), heap.ptr(oo), heap.ptr(osg), W, S, H, D, wl.dtype, o,
                             stream)
-        if ev is not None:
-            ev[1].record(stream)
-        if overlap:
+        if overlap and reset:
             fin = torch.cuda.Event()
             fin.record(stream)
             done[k % NSETS] = fin
 
-    def timed(o, steps, warmup, events=False, overlap=True):
+    def timed(o, steps, warmup, overlap=True, reset=True):
+        """Wall-clock ms per step, and ms per step between two HIP events recorded
+        on the launch stream around the whole timed region."""
         for k in range(warmup):
-            step(k, o, overlap=overlap)
+            step(k, o, overlap=overlap, reset=reset)
         torch.cuda.synchronize()
         assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)] if events else [None] * steps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        e0.record(stream)
         for k in range(steps):
-            step(k, o, evs[k], overlap)
+            step(k, o, overlap, reset)
+        e1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
-        kern = float(np.mean([a.elapsed_time(b) for a, b in evs])) if events else None
-        return (t1 - t0) * 1e3 / steps, kern
+        return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
-    # Throughput passes record no timing events (a timestamped event between two
-    # kernels costs several microseconds per step on this stack); the kernel's
-    # duration comes from a third pass over the same steps with HIP events
-    # around every launch, on the launch stream.
+    # No timing events between launches (a timestamped event between two kernels
+    # costs microseconds per step on this stack).  An in-launch step is exactly
+    # one launch of the persistent kernel, so the events around its timed region
+    # give the kernel's average launch duration (launch to launch, gaps included).
     log(f"[bench] {args.warmup} warmup + {args.steps} timed steps")
+    inl_ms, kern_ms = timed(opts_lib, args.steps, args.warmup, overlap=False, reset=False)
     serial_ms, _ = timed(opts, args.steps, args.warmup, overlap=False)
     overlap_ms, _ = timed(opts, args.steps, args.warmup, overlap=True)
-    _, kern_ms = timed(opts, args.steps, args.warmup, events=True, overlap=False)
-    ms_per_step = min(serial_ms, overlap_ms)
-    mode_used = "overlapped" if overlap_ms < serial_ms else "serial"
+    variants = {"in_launch": inl_ms, "serial": serial_ms, "overlapped": overlap_ms}
+    mode_used = min(variants, key=variants.get)
+    ms_per_step = variants[mode_used]
+
+    n_tile = ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, opts)[0]
 
     def parity(k):
+        """Output of step k equals the oracle's, and (ADD) every tile signal reads W."""
         import oracle
         want = oracle.combine(ins)
-        oo = sets[k % NSETS][1]
-        return all(heap.view(oo, (S, H * W, D), bits, j).cpu().numpy().tobytes() == want[j].tobytes()
-                   for j in range(W))
+        _, oo, osg = sets[k % NSETS]
+        ok = all(heap.view(oo, (S, H * W, D), bits, j).cpu().numpy().tobytes() == want[j].tobytes()
+                 for j in range(W))
+        if wl.protocol != synthgen.PROTOCOL_SET:
+            ok = ok and all(bool((heap.view(osg, (n_tile, ra2a.SIG_STRIDE_U64), torch.int64, j)[:, 0]
+                                  == W).all()) for j in range(W))
+        return ok
 
     ok = parity(args.steps - 1)
     log(f"[bench] combine {ms_per_step * 1e3:.1f} us/step, kernel {kern_ms * 1e3:.1f} us, "
@@ -276,15 +288,17 @@ def main():
                      "kernel_ms": round(kern_ms, 5)},
     }
     rec["step_variants"] = {
+        "in_launch": {"ms_per_step": round(inl_ms, 5),
+                      "note": "one launch per step; its first workgroups zero the signals"},
         "serial": {"ms_per_step": round(serial_ms, 5),
-                   "note": "reset and combine back to back on one stream"},
+                   "note": "a reset launch and the combine back to back on one stream"},
         "overlapped": {"ms_per_step": round(overlap_ms, 5),
-                       "note": "each reset on a side stream during the previous step's combine"},
-        "kernel_timing_pass": "serial steps with HIP events around every combine launch"}
+                       "note": "each reset launch on a side stream during the previous step's combine"},
+        "kernel_timing": "HIP events on the launch stream around the in-launch timed region / launches"}
     if args.legs == "all":
-        st_ms, st_kern = timed(opts_st, args.steps, args.warmup, events=True)
+        st_ms, _ = timed(opts_st, args.steps, args.warmup, overlap=False)  # reset launch + combine
         st_ok = parity(args.steps - 1)
-        rec["staged"] = {"ms_per_step": round(st_ms, 5), "kernel_ms": round(st_kern, 5),
+        rec["staged"] = {"ms_per_step": round(st_ms, 5),
                          "value": round(alg / (st_ms * 1e-3) / 1e9, 2), "parity": st_ok}
 
         def two_phase(k):

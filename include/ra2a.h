@@ -197,9 +197,16 @@ int ra2a_signal_reset(const ra2a_heap_t *heap, uint64_t *sig_sym, int64_t n_slot
 #define RA2A_MODE_STAGED 2 /* through a staging ring in slice j, reordered by consumers */
 
 /* Work-queue words the pipelined combine keeps after the hand-back counters
- * (used in slice 0 only): per stream group (up to 8) a claim counter and a
- * take-over counter, then a mask of fully claimed groups and a spare word.   */
+ * (used in slice 0 only, staged mode only; direct mode leaves them 0): per
+ * stream group (up to 8) a claim counter and a take-over counter, then a mask
+ * of fully claimed groups and a spare word.                                   */
 #define RA2A_QUEUE_SLOTS 18
+
+/* Reset flags the pipelined combine keeps after the work-queue words (slice 0
+ * only): in direct mode the signal reset runs inside the combine launch
+ * (ra2a_rev_all2all), and zeroing workgroup k publishes its share by setting
+ * flag k to the launch's tag.  They are never cleared by that reset.         */
+#define RA2A_RESET_FLAGS 64
 
 /* Tiling, protocol and launch options of the signal-pipelined kernel; a zeroed
  * struct (with straggler_rank = -1) means every default.                     */
@@ -213,7 +220,8 @@ typedef struct ra2a_opts {
                          * (source r, tile), set to 1; the consumer waits for each piece. */
     int32_t ring;       /* staged mode: staging ring depth in S-blocks (default 8; >= the
                          * number of S-blocks means no slot is reused) */
-    int32_t wg_per_cu;  /* persistent workgroups per compute unit (default 2) */
+    int32_t wg_per_cu;  /* persistent workgroups per compute unit (default 2, capped
+                         * at the kernel's occupancy) */
     int32_t lookahead;  /* staged mode: tiles whose pieces are queued ahead of a tile's
                          * consumer work (0: default -- half of what the ring allows, or
                          * every piece first when no slot is reused; -1: every piece
@@ -222,20 +230,26 @@ typedef struct ra2a_opts {
     uint32_t straggler_delay; /* busy-loop base n0: each delayed piece spins n0 + u
                                * iterations, u uniform in [0, n0] from SplitMix64 */
     uint64_t straggler_seed;  /* seed of that SplitMix64 sequence */
-    uint64_t *timestamps;     /* optional device array: per destination slice j, the
-                               * device real-time clock at which each consumer unit
-                               * finished, at timestamps[j * tile_slots + unit] */
+    uint64_t *timestamps;     /* optional device array, zeroed by the caller: for each
+                               * destination slice j and data-signal slot u, the device
+                               * real-time clock at which that signal tile was complete,
+                               * at timestamps[j * tile_slots + u] (direct mode: the
+                               * latest of its pieces' signals; staged mode: the end of
+                               * its consumer copy) */
     int32_t mode;             /* RA2A_MODE_DIRECT (or 0): producers store each piece
                                * straight into its final place in out_j (a symmetric
-                               * buffer) and signal the tile; consumers only wait for
-                               * their tiles (and stamp them); no ring, no hand-back.
+                               * buffer) and signal the tile; out_j is complete once
+                               * every tile signal is; no ring, no consumer copy, no
+                               * hand-back, no work queue (a static schedule).
                                * RA2A_MODE_STAGED: producers store into slice j's staging
                                * ring (the pages' window layout), consumers wait, copy
                                * ring -> out_j and hand the ring slot back. */
     int32_t consumer_split;   /* staged mode: consumer work items sharing one unit, each
-                               * copying a contiguous part (default: one per 128 KiB) */
+                               * copying a contiguous part (default: one per 128 KiB;
+                               * at most 4096) */
     int32_t skip_reset;       /* 1: the caller has already zeroed every signal slot
-                               * (ra2a_signal_reset on the same stream); no reset launch */
+                               * (ra2a_signal_reset on the same stream); the combine
+                               * zeroes none (the timestamps, if any, it still zeroes) */
     int32_t stream_batch;     /* tile streams of one XCD in flight together (default: as
                                * many as fit about 2 MiB of staging ring) */
     int32_t agent_sync;       /* 1: synchronise producers and consumers with device-wide
@@ -245,18 +259,22 @@ typedef struct ra2a_opts {
     int32_t head_merge;       /* signal tiles of adjacent head blocks moved together by one
                                * piece / unit (each keeps its own signal); default, when a
                                * tile spans all of D: runs of up to 4 KiB, halved until the
-                               * combine has at least 2048 pieces */
-    int32_t reserved[2];      /* must be zero */
+                               * combine has at least 1024 pieces */
+    int32_t separate_reset;   /* 1: zero the signals with a launch of their own before the
+                               * combine's, also in direct mode (0, the default: direct
+                               * mode zeroes them inside the combine launch) */
+    int32_t reserved[1];      /* must be zero */
 } ra2a_opts_t;
 
 /* Number of signal slots the combine needs per slice: `tile_slots` data
  * signals (region A: ADD, one per (s-block, head block, d block) in that
  * order; SET, one per (s-block, head block, d block, source r)), then
- * `credit_slots` ring hand-back counters (region B: ADD [ring slot][merged
- * head block][d block]; SET [ring slot][merged head block][d block][source],
- * where a merged head block is head_merge adjacent head blocks and the direct
- * mode counts every S-block as a ring slot), then `queue_slots`
- * (RA2A_QUEUE_SLOTS, or 0 for an empty problem) work-queue words.  The
+ * `credit_slots` ring hand-back counters (region B, staged mode only, 0 in
+ * direct mode: ADD [ring slot][merged head block][d block]; SET [ring
+ * slot][merged head block][d block][source], where a merged head block is
+ * head_merge adjacent head blocks), then `queue_slots` control words
+ * (RA2A_QUEUE_SLOTS work-queue words, then RA2A_RESET_FLAGS reset flags; 0 for
+ * an empty problem).  The
  * `signals` array of a combine must hold the sum of the three in every slice.
  * opts may be NULL; any output pointer may be NULL.                          */
 int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t D, int dtype,
@@ -268,13 +286,19 @@ int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t D, int dt
 int ra2a_rev_all2all_workspace_bytes(int W, int64_t S, int64_t H, int64_t D, int dtype,
                                      const ra2a_opts_t *opts, int two_phase, size_t *bytes);
 
-/* The combine with the signal-pipelined persistent kernel and default options:
- * enqueues the reset of every signal slot, then one persistent launch.  Its
- * workgroups take tasks from one work queue per XCD: producer pieces, which
- * copy one source's part of a tile with 16-byte stores straight into out_j
- * (direct mode, the default), release and signal the tile, and consumer work,
- * which waits until the tile's signal is complete (in staged mode it then
- * copies the staging ring into out_j and hands the ring slot back).
+/* The combine with the signal-pipelined persistent kernel and default options.
+ * Every signal slot and work-queue word is zeroed before any producer of the
+ * launch signals ("Host Side Modifications").  In direct mode (the default)
+ * one launch does both: a few extra workgroups zero the slots and publish
+ * their share through the reset flags, and the persistent workgroups walk the
+ * producer pieces on a static schedule: each copies one source's part of a
+ * tile with 16-byte stores straight into out_j, releases it and, once the
+ * reset flags carry this launch's tag, signals the tile.  (Staged mode, or
+ * separate_reset, or an occupancy without room for the zeroing workgroups:
+ * the reset is a launch of its own before the combine's.)  In staged
+ * mode they take tasks from one work queue per XCD: producer pieces into the
+ * staging ring, and consumer work, which waits until its tile's signal is
+ * complete, copies the ring into out_j and hands the ring slot back.
  * Afterwards every region-A slot holds W (ADD) or 1 (SET) and every region-B
  * slot the number of consumer work items that used it.  Staging (staged mode)
  * comes from the heap (see workspace_bytes).
@@ -349,9 +373,10 @@ int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t
 int ra2a_check(const ra2a_heap_t *heap);
 
 /* Host emulation of the signal-pipelined combine (no GPU needed): runs the
- * kernel's own piece / work-item address arithmetic and work queues for a
- * device of `num_cus` compute units with `blocks_per_cu` resident workgroups,
- * executing each queue strictly in order on host copies of the heap.  in[r]
+ * kernel's own piece / work-item address arithmetic for a device of `num_cus`
+ * compute units with `blocks_per_cu` resident workgroups -- direct mode: every
+ * piece of the static schedule; staged mode: each work queue strictly in
+ * order -- on host copies of the heap.  in[r]
  * (rank r's input) and out[j] are host arrays of S*W*H*D elements; signals[j]
  * (optional, may be NULL) receives the final tile_slots + credit_slots +
  * queue_slots signal values of slice j (unstrided; the queue words are not

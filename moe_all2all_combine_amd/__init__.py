@@ -18,7 +18,7 @@ from typing import Optional, Sequence, Tuple
 __all__ = [
     "Ra2aError", "Opts", "SymmHeap", "lib", "OK", "EINVAL", "ENOMEM", "EHIP", "ETIMEOUT",
     "EUNSUPPORTED", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "MODE_DIRECT", "MODE_STAGED",
-    "QUEUE_SLOTS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
+    "QUEUE_SLOTS", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
     "CMP_LE", "SIG_STRIDE_BYTES", "DTYPES", "symm_heap_create", "symm_heap_attach",
     "symm_heap_destroy", "symm_malloc", "symm_heap_info", "symm_at", "put", "get",
     "put_with_signal", "signal_op", "wait_signal", "signal_reset", "rev_all2all",
@@ -36,6 +36,7 @@ SIG_SET, SIG_ADD = 0, 1
 PROTO_ADD, PROTO_SET = 1, 2
 MODE_DIRECT, MODE_STAGED = 1, 2
 QUEUE_SLOTS = 18
+RESET_FLAGS = 64
 AG_AGENT_SYNC, AG_SKIP_RESET, AG_B_TRANSPOSED = 1, 2, 4
 CMP_EQ, CMP_NE, CMP_GT, CMP_GE, CMP_LT, CMP_LE = range(6)
 SIG_STRIDE_BYTES = 128
@@ -62,7 +63,8 @@ class Opts(ctypes.Structure):
         ("timestamps", ctypes.c_void_p), ("mode", ctypes.c_int32),
         ("consumer_split", ctypes.c_int32), ("skip_reset", ctypes.c_int32),
         ("stream_batch", ctypes.c_int32), ("agent_sync", ctypes.c_int32),
-        ("head_merge", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
+        ("head_merge", ctypes.c_int32), ("separate_reset", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
     def __init__(self, **kw):

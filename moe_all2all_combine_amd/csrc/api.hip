@@ -3,10 +3,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <random>
 #include <string>
 #include <vector>
 
@@ -148,8 +151,9 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     std::memset(&z, 0, sizeof z);
     z.straggler_rank = -1;
     if (!o) o = &z;
-    if (o->reserved[0] || o->reserved[1])
-        return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
+    if (o->reserved[0]) return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
+    if (o->separate_reset != 0 && o->separate_reset != 1)
+        return fail(RA2A_EINVAL, "separate_reset must be 0 or 1");
     if (o->mode != 0 && o->mode != RA2A_MODE_DIRECT && o->mode != RA2A_MODE_STAGED)
         return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_DIRECT or RA2A_MODE_STAGED");
     p->BS = o->tile_s > 0 ? o->tile_s : std::min<int64_t>(S, 64);
@@ -174,8 +178,9 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
         p->MH = std::min(o->head_merge, p->nhb);
     } else if (p->TD == D) {
         // adjacent head blocks are contiguous: merge up to ~4 KiB runs, but keep at
-        // least kMinPieces pieces so that every persistent workgroup gets several
-        constexpr int64_t kMinPieces = 2048;
+        // least kMinPieces pieces, so that each of the (about 512) persistent
+        // workgroups gets two or more
+        constexpr int64_t kMinPieces = 1024;
         int64_t mh = std::max<int64_t>(1, std::min<int64_t>(p->nhb, 4096 / std::max<int64_t>(1, p->TH * D * e)));
         const int64_t per_mh = (int64_t)W * p->nbs * W;  // pieces per merged head block
         while (mh > 1 && per_mh * cdiv(p->nhb, mh) < kMinPieces) mh /= 2;
@@ -197,6 +202,8 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);
     if (o->consumer_split < 0 || o->wg_per_cu < 0 || o->lookahead < -1)
         return fail(RA2A_EINVAL, "negative option");
+    // the kernels split a unit's vectors with 32-bit products part * (nvec mod cs)
+    if (o->consumer_split > 4096) return fail(RA2A_EINVAL, "consumer_split above 4096");
     p->csplit = o->consumer_split > 0
                     ? o->consumer_split
                     : (int)std::max<int64_t>(1, std::min<int64_t>(64, p->unit_bytes / (128 << 10)));
@@ -412,6 +419,20 @@ int xcd_count(int* nxcd) {
     return RA2A_OK;
 }
 
+// Tag of one in-launch reset: a process-wide counter starting at a random
+// value, never 0, so a reset flag left by any earlier launch never matches.
+uint64_t next_reset_tag() {
+    static std::atomic<uint64_t> ctr{[] {
+        std::random_device rd;
+        const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull);
+    }()};
+    uint64_t t;
+    do t = ctr.fetch_add(1, std::memory_order_relaxed);
+    while (t == 0);
+    return t;
+}
+
 int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64_t S, int64_t H,
                       int64_t D, int dtype, const ra2a_opts_t* opts, void* stream) {
     const int e0 = elem_bytes(dtype);
@@ -426,7 +447,8 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     }
     Checked c{};
     int rc = check_combine(in, out, signals, W, S, H, D, dtype,
-                           empty ? 0 : pl.regionA + pl.regionB + ra2a::kQueueSlots, &c);
+                           empty ? 0 : pl.regionA + pl.regionB + ra2a::kQueueSlots + ra2a::kResetFlags,
+                           &c);
     if (rc) return rc;
     if (empty) return ok();
     if (opts && (opts->straggler_rank < -1 || opts->straggler_rank >= W))
@@ -459,15 +481,37 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     a.err = c.h->err;
     a.stamps = opts ? opts->timestamps : nullptr;
     a.timeout = timeout_ticks(c.h);
+    a.piece_grid = grid;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!(opts && opts->skip_reset)) {
-        he = ra2a::launch_signal_reset(c.h->base, (int64_t)c.h->stride, W, (int64_t)c.sig_off,
-                                       pl.regionA + pl.regionB + ra2a::kQueueSlots, st);
-        if (he != hipSuccess) return hip_fail(he, "signal reset launch");
-    }
-    if (opts && opts->timestamps) {
-        he = hipMemsetAsync(opts->timestamps, 0, sizeof(uint64_t) * (size_t)W * pl.regionA, st);
+    const bool skip = opts && opts->skip_reset;
+    const int64_t reset_slots = pl.regionA + pl.regionB + ra2a::kQueueSlots;
+    const int64_t nstamps = a.stamps ? (int64_t)W * pl.regionA : 0;
+    // In-launch reset: direct mode, unless asked for a separate launch, and only
+    // when the occupancy leaves room for the zeroing workgroups beside the
+    // persistent ones (they must run whatever those do).
+    const int per_cu = grid / std::max(1, ncu);
+    const bool in_launch = pl.direct && !(opts && opts->separate_reset) && occ > per_cu &&
+                           (!skip || nstamps > 0);
+    if (in_launch) {
+        // about 16 slots per thread and zeroing workgroup, at most kResetFlags of them
+        const int64_t work = (skip ? 0 : reset_slots * W) + nstamps;  // words to zero
+        const int64_t nz = std::max<int64_t>(
+            1, std::min<int64_t>(ra2a::kResetFlags, (work + 16 * ra2a::kThreads - 1) / (16 * ra2a::kThreads)));
+        a.reset_tag = next_reset_tag();
+        a.reset_nz = (int)nz;
+        a.reset_slots = skip ? 0 : reset_slots;  // skip_reset: the caller zeroed the signals
+        a.reset_chunk = (a.reset_slots + nz - 1) / nz;
+        a.stamp_chunk = (nstamps + nz - 1) / nz;
+        a.flag_off = (int64_t)c.sig_off + reset_slots * RA2A_SIG_STRIDE_BYTES;
+        grid += (int)nz;
+    } else {
+        if (!skip) {
+            he = ra2a::launch_signal_reset(c.h->base, (int64_t)c.h->stride, W, (int64_t)c.sig_off,
+                                           reset_slots, st);
+            if (he != hipSuccess) return hip_fail(he, "signal reset launch");
+        }
+        he = ra2a::launch_zero_u64(a.stamps, nstamps, st);
         if (he != hipSuccess) return hip_fail(he, "timestamp reset");
     }
     he = ra2a::launch_pipelined(a, V, grid, st);
@@ -730,7 +774,7 @@ RA2A_API int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t 
     }
     if (tile_slots) *tile_slots = a;
     if (credit_slots) *credit_slots = b;
-    if (queue_slots) *queue_slots = (a + b) > 0 ? ra2a::kQueueSlots : 0;
+    if (queue_slots) *queue_slots = (a + b) > 0 ? ra2a::kQueueSlots + ra2a::kResetFlags : 0;
     return ok();
 }
 
@@ -1063,7 +1107,7 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
     const int64_t nb = S * (int64_t)W * H * D * e0;
     const int64_t in_off = 0, out_off = al(nb), stg_off = al(out_off + nb);
     const int64_t sig_off = al(stg_off + pl.ring_bytes);
-    const int64_t nsig = pl.regionA + pl.regionB + ra2a::kQueueSlots;
+    const int64_t nsig = pl.regionA + pl.regionB + ra2a::kQueueSlots + ra2a::kResetFlags;
     const int64_t stride = al(sig_off + nsig * RA2A_SIG_STRIDE_BYTES);
     if ((double)stride * W > 16.0e9) return fail(RA2A_EINVAL, "too large to emulate");
     ra2a::PipeArgs a{};
@@ -1100,15 +1144,12 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
         // Direct mode as the kernel runs it: every piece once in its global order,
         // no waits, no hand-back counters.
         const int64_t total = ra2a::total_pieces(a);
-        std::vector<int64_t> seen_g(a.NG, 0);
+        std::vector<uint8_t> seen((size_t)total, 0);  // by (stream, S-block, source)
         for (int64_t gp = 0; gp < total; ++gp) {
-            int g;
-            int64_t pc;
-            ra2a::global_piece(a, gp, &g, &pc);
-            if (g < 0 || g >= a.NG || pc < 0 || pc >= ra2a::group_pieces(a, g))
-                return fail(RA2A_EINVAL, "global piece %lld maps outside its group", (long long)gp);
-            seen_g[g]++;
-            const ra2a::Piece p = ra2a::piece_of(a, g, pc);
+            const ra2a::Piece p = ra2a::direct_piece(a, gp);
+            if (p.sid < 0 || p.sid >= a.nstreams || p.b < 0 || p.b >= a.nbs || p.r < 0 || p.r >= W)
+                return fail(RA2A_EINVAL, "direct piece %lld out of range", (long long)gp);
+            seen[(size_t)(((int64_t)p.sid * a.nbs + p.b) * W + p.r)]++;
             std::vector<std::pair<int64_t, int64_t>> offs;
             rc = walk_plan(p.pl, V, 0, ra2a::plan_vectors(p.pl, V), &offs);
             if (rc) return rc;
@@ -1126,9 +1167,8 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
                 *u64(sg) = add ? *u64(sg) + 1 : 1;
             }
         }
-        for (int g = 0; g < a.NG; ++g)
-            if (seen_g[g] != ra2a::group_pieces(a, g))
-                return fail(RA2A_EINVAL, "group %d: direct schedule does not cover its pieces", g);
+        for (uint8_t x : seen)
+            if (x != 1) return fail(RA2A_EINVAL, "direct schedule does not hold every piece once");
     }
     // Staged mode: each group's queue run strictly in queue order, one task at a
     // time: every wait must already hold when its task comes up (the kernel's

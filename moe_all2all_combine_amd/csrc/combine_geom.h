@@ -167,10 +167,19 @@ struct GroupStreams {
     int start, ns;
 };
 
+// start(g) = floor(g * nstreams / NG), in 32-bit arithmetic: with nstreams =
+// q * NG + m, it is g * q + floor(g * m / NG) (g <= NG <= 8, so g * m < 64).
+RA2A_HD uint32_t group_start(const PipeArgs& a, uint32_t g) {
+    const uint32_t n = (uint32_t)a.nstreams, ng = (uint32_t)a.NG;
+    const uint32_t q = n / ng;
+    const uint32_t m = n - q * ng;
+    return g * q + g * m / ng;
+}
+
 RA2A_HD GroupStreams group_streams(const PipeArgs& a, int g) {
     GroupStreams r;
-    r.start = (int)((int64_t)g * a.nstreams / a.NG);
-    r.ns = (int)((int64_t)(g + 1) * a.nstreams / a.NG) - r.start;
+    r.start = (int)group_start(a, (uint32_t)g);
+    r.ns = (int)group_start(a, (uint32_t)g + 1u) - r.start;
     return r;
 }
 
@@ -204,15 +213,13 @@ struct Piece {
     int64_t unit_index;   // first data-signal slot index within slice j (timestamp row)
 };
 
-RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
+// The piece of source r in S-block b of stream sid.
+RA2A_HD Piece piece_at(const PipeArgs& a, int sid, int b, int r) {
     Piece p;
     const int64_t e = a.e;
-    const GroupStreams gs = group_streams(a, g);
-    const uint32_t tile = (uint32_t)pc / (uint32_t)a.W;
-    p.r = (int)((uint32_t)pc - tile * (uint32_t)a.W);
-    int k;
-    tile_of(a, gs.ns, tile, &p.b, &k);
-    p.sid = gs.start + k;
+    p.r = r;
+    p.b = b;
+    p.sid = sid;
     const Stream st = stream_of(a, p.sid);
     p.j = st.j;
     const uint32_t cycle = (uint32_t)p.b / (uint32_t)a.R;  // uses of this ring slot before b
@@ -255,22 +262,29 @@ RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
     return p;
 }
 
+// Staged mode: producer piece pc of group g, source r = pc mod W of the
+// group's tile pc div W (tile_of order).
+RA2A_HD Piece piece_of(const PipeArgs& a, int g, int64_t pc) {
+    const GroupStreams gs = group_streams(a, g);
+    const uint32_t tile = (uint32_t)pc / (uint32_t)a.W;
+    const int r = (int)((uint32_t)pc - tile * (uint32_t)a.W);
+    int b, k;
+    tile_of(a, gs.ns, tile, &b, &k);
+    return piece_at(a, gs.start + k, b, r);
+}
+
 RA2A_HD int64_t group_pieces(const PipeArgs& a, int g) {
     return (int64_t)a.nbs * group_streams(a, g).ns * a.W;
 }
 
-// Direct mode: piece gp of the whole combine (groups in order, each group's
-// pieces in tile order); returns the group and the piece index inside it.
-RA2A_HD void global_piece(const PipeArgs& a, int64_t gp, int* g, int64_t* pc) {
-    int gg = 0;
-    int64_t n = group_pieces(a, 0);
-    while (gp >= n && gg + 1 < a.NG) {
-        gp -= n;
-        ++gg;
-        n = group_pieces(a, gg);
-    }
-    *g = gg;
-    *pc = gp;
+// Direct mode: piece gp of the whole combine, in the order (stream, S-block,
+// source) with the source fastest, so that the pieces in flight together fill
+// a few destinations' outputs and read contiguous row ranges of every input.
+RA2A_HD Piece direct_piece(const PipeArgs& a, int64_t gp) {
+    const uint32_t t = (uint32_t)gp / (uint32_t)a.W;
+    const int r = (int)((uint32_t)gp - t * (uint32_t)a.W);
+    const uint32_t sid = t / (uint32_t)a.nbs;
+    return piece_at(a, (int)sid, (int)(t - sid * (uint32_t)a.nbs), r);
 }
 
 RA2A_HD int64_t total_pieces(const PipeArgs& a) {
@@ -338,9 +352,13 @@ RA2A_HD Item item_of(const PipeArgs& a, int g, int64_t it, int V) {
         pl.sc = pl.dc = head;
         pl.run = (int)(st.td * e);
     }
-    const int nvec = a.direct ? 0 : plan_vectors(pl, V);  // direct: nothing to move
-    q.lo = (int)((int64_t)nvec * q.part / a.csplit);
-    q.hi = (int)((int64_t)nvec * (q.part + 1) / a.csplit);
+    // part p of the unit's nvec vectors: [floor(nvec p / cs), floor(nvec (p+1) / cs)),
+    // in 32-bit arithmetic with nvec = qv * cs + mv
+    const uint32_t nvec = (uint32_t)plan_vectors(pl, V);
+    const uint32_t cs = (uint32_t)a.csplit, up = (uint32_t)q.part;
+    const uint32_t qv = nvec / cs, mv = nvec - qv * cs;
+    q.lo = (int)(up * qv + up * mv / cs);
+    q.hi = (int)((up + 1u) * qv + (up + 1u) * mv / cs);
     const int64_t sig_base = (int64_t)st.j * a.stride + a.sig_off;
     q.nsig = st.nh;
     q.unit_index = tile_slot(a, q.b, st.hb0, st.db, q.r0);
@@ -366,7 +384,7 @@ RA2A_HD int64_t group_items(const PipeArgs& a, int g) {
 // (k, b) waits for the hand-back of tile (k, b - R), which lies R * nk tiles
 // earlier in the same stream batch (nk streams), so L <= R * nk - 1 keeps that
 // dependency backwards; without ring reuse nothing waits on consumers and any
-// L is valid (direct mode: the whole group, all pieces first).  Workgroups claim tasks in queue order
+// L is valid.  Workgroups claim tasks in queue order
 // and only ever wait on earlier tasks, each of which a running workgroup has
 // claimed; hence no deadlock, whatever the number of resident workgroups.
 struct GroupQueue {
@@ -414,7 +432,7 @@ RA2A_HD bool task_of(const GroupQueue& q, int64_t pos, int64_t* idx) {
     const int64_t blk = q.np + q.ni;
     const int64_t nfull = q.ntiles - q.L;  // blocks: pieces of tile t+L, items of tile t
     if (pos < nfull * blk) {
-        const int64_t t = pos / blk;
+        const int64_t t = (uint32_t)pos / (uint32_t)blk;  // positions < 2^31
         const int64_t off = pos - t * blk;
         if (off < q.np) {
             *idx = (t + q.L) * q.np + off;

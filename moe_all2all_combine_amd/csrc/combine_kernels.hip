@@ -21,21 +21,34 @@ namespace ra2a {
 __global__ void __launch_bounds__(kThreads) signal_reset_kernel(uint8_t* base, int64_t stride,
                                                                 int W, int64_t sig_off,
                                                                 int64_t nslots) {
-    const int64_t total = (int64_t)W * nslots;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / nslots;
-        const int64_t k = i - r * nslots;
-        uint64_t* p = reinterpret_cast<uint64_t*>(base + r * stride + sig_off) + k * kSigStrideU64;
-        *p = 0ull;
+    // thread k zeroes slot k in every slice (no index divisions)
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nslots;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        uint8_t* p = base + sig_off + k * (kSigStrideU64 * 8);
+        for (int r = 0; r < W; ++r) *reinterpret_cast<uint64_t*>(p + r * stride) = 0ull;
     }
+}
+
+// Zero n contiguous 8-byte words (a kernel rather than a memset node, so that
+// callers may capture it in a graph).
+__global__ void __launch_bounds__(kThreads) zero_u64_kernel(uint64_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0ull;
+}
+
+hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, p, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_signal_reset(uint8_t* base, int64_t stride, int W, int64_t sig_off,
                                int64_t nslots, hipStream_t st) {
-    const int64_t total = (int64_t)W * nslots;
-    if (total <= 0) return hipSuccess;
-    int64_t blocks = (total + kThreads - 1) / kThreads;
+    if (W <= 0 || nslots <= 0) return hipSuccess;
+    int64_t blocks = (nslots + kThreads - 1) / kThreads;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(signal_reset_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, base,
                        stride, W, sig_off, nslots);
@@ -53,9 +66,24 @@ template <int V, int U, bool NTL, bool NTS>
 __device__ __forceinline__ void copy_plan(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                           const RowPlan& p, int lo, int hi) {
     using T = typename Vec<V>::T;
+    constexpr int kRound = U * kThreads;  // vectors per round
     const int vpr = p.run / V;
+    // Rounds lying wholly inside [lo, hi) run without per-lane range tests (the
+    // loop condition is uniform), so the compiler waits for each load just
+    // before its store instead of draining every access before the first
+    // store; one predicated round moves the tail.
+    const int nfull = hi > lo ? (hi - lo) / kRound : 0;
     int idx = lo + (int)threadIdx.x;
-    if (idx >= hi) return;
+    auto put = [](const T& v, uint8_t* d) {
+        if (NTS)
+            store_nt(v, reinterpret_cast<T*>(d));
+        else
+            *reinterpret_cast<T*>(d) = v;
+    };
+    auto get = [](const uint8_t* s) {
+        const T* sp = reinterpret_cast<const T*>(s);
+        return NTL ? load_nt(sp) : *sp;
+    };
     if (p.B * p.C == 1 && lo == 0 && kThreads % vpr == 0) {
         // one run per row and whole rows per step: each step moves kThreads / vpr
         // rows down at the same column, so both offsets advance by constants
@@ -64,52 +92,53 @@ __device__ __forceinline__ void copy_plan(const uint8_t* __restrict__ src, uint8
         const uint8_t* s0 = src + row * p.sa + (int64_t)col * V;
         uint8_t* d0 = dst + row * p.da + (int64_t)col * V;
         const int64_t ds = rows * p.sa, dd = rows * p.da;
-        for (; idx < hi; idx += U * kThreads) {
+        for (int k = 0; k < nfull; ++k) {
+            T v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = get(s0 + u * ds);
+#pragma unroll
+            for (int u = 0; u < U; ++u) put(v[u], d0 + u * dd);
+            s0 += U * ds;
+            d0 += U * dd;
+        }
+        idx += nfull * kRound;
+        if (idx < hi) {
             T v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (idx + u * kThreads < hi) {
-                    const T* sp = reinterpret_cast<const T*>(s0 + u * ds);
-                    v[u] = NTL ? load_nt(sp) : *sp;
-                }
+                if (idx + u * kThreads < hi) v[u] = get(s0 + u * ds);
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (idx + u * kThreads < hi) {
-                    T* dp = reinterpret_cast<T*>(d0 + u * dd);
-                    if (NTS)
-                        store_nt(v[u], dp);
-                    else
-                        *dp = v[u];
-                }
-            s0 += U * ds;
-            d0 += U * dd;
+                if (idx + u * kThreads < hi) put(v[u], d0 + u * dd);
         }
         return;
     }
     PlanCursor c = cursor_start(p, V, vpr, (uint32_t)idx, kThreads);
-    for (; idx < hi; idx += U * kThreads) {
+    for (int k = 0; k < nfull; ++k) {
         T v[U];
         int64_t doff[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            doff[u] = -1;
-            if (idx + u * kThreads < hi) {
-                const T* sp = reinterpret_cast<const T*>(src + c.so);
-                v[u] = NTL ? load_nt(sp) : *sp;
-                doff[u] = c.dofs;
-            }
+            v[u] = get(src + c.so);
+            doff[u] = c.dofs;
             cursor_advance(c, p, vpr);
         }
 #pragma unroll
+        for (int u = 0; u < U; ++u) put(v[u], dst + doff[u]);
+    }
+    idx += nfull * kRound;
+    if (idx < hi) {
+        T v[U];
+        int64_t doff[U];
+#pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (doff[u] >= 0) {
-                T* dp = reinterpret_cast<T*>(dst + doff[u]);
-                if (NTS)
-                    store_nt(v[u], dp);
-                else
-                    *dp = v[u];
-            }
+            if (idx + u * kThreads < hi) v[u] = get(src + c.so);
+            doff[u] = c.dofs;
+            cursor_advance(c, p, vpr);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (idx + u * kThreads < hi) put(v[u], dst + doff[u]);
     }
 }
 
@@ -120,32 +149,42 @@ __device__ __forceinline__ void copy_plan_buf(__amdgpu_buffer_rsrc_t src, uint32
                                               uint8_t* __restrict__ dst, const RowPlan& p, int lo,
                                               int hi) {
     using T = typename Vec<V>::T;
+    constexpr int kRound = U * kThreads;
     const int vpr = p.run / V;
+    const int nfull = hi > lo ? (hi - lo) / kRound : 0;
     int idx = lo + (int)threadIdx.x;
-    if (idx >= hi) return;
+    auto put = [](const T& v, uint8_t* d) {
+        if (NTS)
+            store_nt(v, reinterpret_cast<T*>(d));
+        else
+            *reinterpret_cast<T*>(d) = v;
+    };
     PlanCursor c = cursor_start(p, V, vpr, (uint32_t)idx, kThreads);
-    for (; idx < hi; idx += U * kThreads) {
+    for (int k = 0; k < nfull; ++k) {  // whole rounds: no per-lane tests
         T v[U];
         int64_t doff[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            doff[u] = -1;
-            if (idx + u * kThreads < hi) {
-                v[u] = BufLoad<V, POLICY>::go(src, src_off + (uint32_t)c.so);
-                doff[u] = c.dofs;
-            }
+            v[u] = BufLoad<V, POLICY>::go(src, src_off + (uint32_t)c.so);
+            doff[u] = c.dofs;
             cursor_advance(c, p, vpr);
         }
 #pragma unroll
+        for (int u = 0; u < U; ++u) put(v[u], dst + doff[u]);
+    }
+    idx += nfull * kRound;
+    if (idx < hi) {
+        T v[U];
+        int64_t doff[U];
+#pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (doff[u] >= 0) {
-                T* dp = reinterpret_cast<T*>(dst + doff[u]);
-                if (NTS)
-                    store_nt(v[u], dp);
-                else
-                    *dp = v[u];
-            }
+            if (idx + u * kThreads < hi) v[u] = BufLoad<V, POLICY>::go(src, src_off + (uint32_t)c.so);
+            doff[u] = c.dofs;
+            cursor_advance(c, p, vpr);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (idx + u * kThreads < hi) put(v[u], dst + doff[u]);
     }
 }
 
@@ -262,26 +301,77 @@ __device__ __forceinline__ bool run_item(const PipeArgs& a, int g, int64_t it, i
     return true;
 }
 
+// In-launch signal reset (direct mode; "Host Side Modifications": every signal
+// is zero before any producer of a launch signals).  Zeroing workgroup k
+// clears slots [k * reset_chunk, (k + 1) * reset_chunk) of every slice and its
+// share of the timestamps, releases device-wide (every wave's stores reach the
+// device-wide coherence point), then sets reset flag k to this launch's tag.
+// It waits on nothing, so it always finishes.
+__device__ __forceinline__ void reset_share(const PipeArgs& a, int k) {
+    const int64_t lo = (int64_t)k * a.reset_chunk;
+    const int64_t hi = geom_min(lo + a.reset_chunk, a.reset_slots);
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
+        uint8_t* p = a.base + a.sig_off + i * (kSigStrideU64 * 8);
+        for (int r = 0; r < a.W; ++r) *reinterpret_cast<uint64_t*>(p + r * a.stride) = 0ull;
+    }
+    if (a.stamps) {
+        const int64_t n = (int64_t)a.W * a.units_per_dest;
+        const int64_t slo = (int64_t)k * a.stamp_chunk;
+        const int64_t shi = geom_min(slo + a.stamp_chunk, n);
+        for (int64_t i = slo + threadIdx.x; i < shi; i += kThreads) a.stamps[i] = 0ull;
+    }
+    wg_release();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(a.base + a.flag_off) + (int64_t)k * kSigStrideU64,
+                           a.reset_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Before a workgroup's first signal: every reset flag carries this launch's tag
+// (lane k of wave 0 polls flag k), then wave 0 -- the one that signals and
+// stamps -- acquires.  False, uniformly, if a bounded wait gave up.
+__device__ __forceinline__ bool reset_published(const PipeArgs& a) {
+    bool ok = true;
+    if ((int)threadIdx.x < a.reset_nz)
+        ok = spin_until(reinterpret_cast<const uint64_t*>(a.base + a.flag_off) +
+                            (int64_t)threadIdx.x * kSigStrideU64,
+                        kCmpEq, a.reset_tag, a.timeout, a.err);
+    if (threadIdx.x < 64) fence_acquire_agent();
+    return __syncthreads_and(ok ? 1 : 0) != 0;
+}
+
 // Direct mode.  Producers store straight into out_j, so no consumer has data to
 // move: a tile is complete when its signal reaches W (ADD) or each of its W
 // slots reads 1 (SET), and the optional completion stamp of a tile is the
-// latest of its producers' stamps (an atomic max each).  Nothing waits on
-// anything, so a static schedule (piece gp to workgroup gp mod grid) is
-// deadlock-free at any residency and needs no queue; every atomic is issued
-// without a return value, so no drain waits for a round trip.  (Measured: issuing
-// the next piece's loads before this piece's release is slower here, not faster.)
+// latest of its producers' stamps (an atomic max each).  The only wait is for
+// the in-launch reset's flags (above), so a static schedule (workgroup k takes
+// pieces k, k + piece_grid, ... of the direct_piece order) needs no queue.  The
+// reset runs on reset_nz workgroups launched after the piece_grid ones, and the
+// host launches it only when the occupancy leaves room for them beside the
+// persistent workgroups: they run whatever those do and wait on nothing, so
+// the wait always ends.  Every atomic is issued without a return value, so no
+// drain waits for a round trip.  A piece's geometry is 32-bit scalar arithmetic: the inline 64-bit
+// division sequences it replaced delayed every piece's first load measurably.
+// (Measured too: issuing the next piece's loads before this piece's release is
+// slower here, not faster.)
 template <int V, int SYNC>
 __device__ __forceinline__ void direct_path(const PipeArgs& a, int* lds_flag) {
+    const int pg = a.piece_grid;
+    if ((int)blockIdx.x >= pg) {  // a zeroing workgroup of the in-launch reset
+        reset_share(a, (int)blockIdx.x - pg);
+        return;
+    }
+    bool published = a.reset_tag == 0ull;
     const int64_t total = total_pieces(a);
-    for (int64_t gp = blockIdx.x; gp < total; gp += gridDim.x) {
-        int g;
-        int64_t pc;
-        global_piece(a, gp, &g, &pc);
-        const Piece p = piece_of(a, g, pc);
+    for (int64_t gp = blockIdx.x; gp < total; gp += pg) {
+        const Piece p = direct_piece(a, gp);
         if (!piece_wait(a, p, lds_flag)) return;
         // final place: stream the stores past the L2
         copy_plan<V, 8, true, true>(a.base + p.src, a.base + p.dst, p.pl, 0, plan_vectors(p.pl, V));
         group_release<SYNC>();
+        if (!published) {
+            if (!reset_published(a)) return;
+            published = true;
+        }
         piece_signal(a, p.sig, p.sig_step, p.nsig);
         if (a.stamps && threadIdx.x < 64) {
             const uint64_t now = rtc_now();

@@ -17,6 +17,10 @@ constexpr int kNumXcd = 8;         // XCDs of an MI355X: at most this many strea
 // queue words: per group a claim counter and a take-over counter, then a mask
 // of groups whose queue is fully claimed, then one spare word
 constexpr int kQueueSlots = 2 * kNumXcd + 2;
+// reset flags of the combine's in-launch signal reset (slice 0, after the queue
+// words): flag k holds the tag of the last launch whose zeroing workgroup k
+// finished; never cleared by that reset itself
+constexpr int kResetFlags = 64;
 
 // Arguments of the signal-pipelined persistent combine.
 struct PipeArgs {
@@ -52,6 +56,15 @@ struct PipeArgs {
     uint32_t delay;     // busy-loop base n0
     uint64_t seed;      // SplitMix64 seed of the delays
     int64_t units_per_dest;  // consumer units per destination (timestamps row)
+    // in-launch signal reset (direct mode): reset_nz extra workgroups, after the
+    // piece_grid workgroups that move pieces, zero slots [0, reset_slots) of every
+    // slice (reset_chunk each) and their share of the timestamps (stamp_chunk
+    // each), then set their reset flag to reset_tag; 0 = no in-launch reset
+    uint64_t reset_tag;
+    int32_t reset_nz;
+    int32_t piece_grid;
+    int64_t reset_slots, reset_chunk, stamp_chunk;
+    int64_t flag_off;   // symmetric offset of reset flag 0 (used in slice 0)
 };
 
 // Arguments of the two-phase combine's two launches.

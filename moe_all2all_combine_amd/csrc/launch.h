@@ -11,6 +11,7 @@ namespace ra2a {
 
 hipError_t launch_signal_reset(uint8_t* base, int64_t stride, int W, int64_t sig_off,
                                int64_t nslots, hipStream_t st);
+hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t st);
 hipError_t launch_pipelined(const PipeArgs& a, int V, int grid, hipStream_t st);
 hipError_t pipelined_blocks_per_cu(int V, int sync, int direct, int* n);
 hipError_t launch_xcc_probe(uint32_t* out, int n, hipStream_t st);

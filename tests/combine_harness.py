@@ -88,12 +88,26 @@ class CombineCase:
         v = self.heap.view(self.off_sig, (max(n, 1), ra2a.SIG_STRIDE_U64), torch.int64, j)
         return v[:n, 0].cpu().numpy()
 
-    def queue_words(self) -> np.ndarray:
-        """The work-queue words of slice 0: per group (8) its claim counter and
-        take-over counter, then the mask of fully claimed groups and a spare."""
+    def control_words(self) -> np.ndarray:
+        """Slice 0's words after the data signals and hand-back counters."""
         n0 = self.n_tile + self.n_credit
         v = self.heap.view(self.off_sig, (n0 + self.n_queue, ra2a.SIG_STRIDE_U64), torch.int64, 0)
         return v[n0:, 0].cpu().numpy()
+
+    def queue_words(self) -> np.ndarray:
+        """The work-queue words of slice 0: per group (8) its claim counter and
+        take-over counter, then the mask of fully claimed groups and a spare."""
+        return self.control_words()[:ra2a.QUEUE_SLOTS]
+
+    def reset_flags(self) -> np.ndarray:
+        """The in-launch reset's flags (slice 0), after the work-queue words."""
+        return self.control_words()[ra2a.QUEUE_SLOTS:ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS]
+
+    def fill_signals(self, byte: int) -> None:
+        """Every signal-array byte of every slice (control words included) := byte."""
+        n = max(1, self.n_tile + self.n_credit + self.n_queue) * ra2a.SIG_STRIDE_BYTES
+        for r in range(self.wl.W):
+            self.heap.view(self.off_sig, (n,), torch.uint8, r).fill_(byte)
 
     def run_pipelined(self, stream=None) -> None:
         wl = self.wl

@@ -77,17 +77,17 @@ def test_attach_rejects_overlap_and_misalignment(fake_heap):
 
 
 def test_signal_slots_and_workspace():
-    Q = ra2a.QUEUE_SLOTS
+    Q = ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS  # control words: queue words, then reset flags
     # 64-token x 1-head x 128 tiles, ADD: one slot per (S-block, head) per slice
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
     # direct mode (the default): no ring, so no hand-back counters
     assert (a, b, q) == (8 * 16, 0, Q)
     # staged: ring of 8 = every S-block; 256-B heads would merge 16 at a time into
-    # 4 KiB runs, but that leaves only 512 pieces, so 4 at a time (2048 pieces):
-    # 4 moved streams per destination
+    # 4 KiB runs, but that leaves only 512 pieces, so 8 at a time (1024 pieces):
+    # 2 moved streams per destination
     staged = ra2a.Opts(mode=ra2a.MODE_STAGED)
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", staged)
-    assert (a, b, q) == (8 * 16, 8 * 4, Q)
+    assert (a, b, q) == (8 * 16, 8 * 2, Q)
     a, b, _ = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16",
                                             ra2a.Opts(head_merge=1, ring=2, mode=ra2a.MODE_STAGED))
     assert (a, b) == (8 * 16, 2 * 16)

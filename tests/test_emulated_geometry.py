@@ -51,7 +51,8 @@ def check_emulation(W, S, H, D, dtype, opts, csplit, seed, cus=256, per_cu=2):
     for j in range(W):
         assert outs[j].tobytes() == want[j].tobytes(), f"rank {j}"
         np.testing.assert_array_equal(sigs[j][:len(exp)].astype(np.int64), exp)
-        assert len(sigs[j]) == len(exp) + ra2a.QUEUE_SLOTS and not sigs[j][len(exp):].any()
+        assert len(sigs[j]) == len(exp) + ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS
+        assert not sigs[j][len(exp):].any()
 
 
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring,csplit,lookahead", CASES)

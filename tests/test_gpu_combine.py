@@ -178,6 +178,78 @@ def test_back_to_back_launches_reset_signals():
         case.close()
 
 
+DIRTY = 0x5A  # byte pattern left in the signal array before a launch
+
+
+@pytest.mark.parametrize("reset", ["in_launch", "separate", "no_room"])
+def test_direct_reset_clears_dirty_signals(reset):
+    """Direct mode zeroes the signals inside the combine launch (with
+    separate_reset, or when the occupancy leaves no room for the zeroing
+    workgroups, in a launch of its own): whatever the signal array held, the
+    data signals end at their counts and the queue words at 0, launch after
+    launch; each in-launch reset leaves its own tag in the reset flags."""
+    wl = synthgen.small_workload(8, 96, 4, 64, "bf16", seed=11, tile=(16, 1, 64),
+                                 protocol=synthgen.PROTOCOL_ADD)
+    knobs = {"in_launch": {}, "separate": dict(separate_reset=1), "no_room": dict(wg_per_cu=64)}
+    opts = opts_for(wl, **knobs[reset])
+    case = CombineCase(wl, opts)
+    dirty = int.from_bytes(bytes([DIRTY]) * 8, "little")
+    try:
+        tags = []
+        for seed in (11, 12, 13):
+            say(f"[case] direct reset={reset} seed={seed}")
+            case.fill_signals(DIRTY)
+            ins = synthgen.make_inputs(synthgen.small_workload(8, 96, 4, 64, "bf16", seed=seed,
+                                                               tile=(16, 1, 64)))
+            case.upload(ins)
+            case.run_pipelined()
+            torch.cuda.synchronize()
+            case.check_device()
+            want = oracle.combine(ins)
+            for j in range(wl.W):
+                assert case.download(j).tobytes() == want[j].tobytes()
+            exp = expected_signal_array(wl, opts, 1)
+            for j in range(wl.W):
+                np.testing.assert_array_equal(case.signals(j), exp, err_msg=f"signals of rank {j}")
+            assert not case.queue_words().any()
+            f = [int(x) & (2**64 - 1) for x in case.reset_flags()]
+            if reset == "in_launch":
+                nz = next((k for k in range(1, len(f)) if f[k] != f[0]), len(f))
+                assert f[0] not in (0, dirty), hex(f[0])
+                assert all(x == dirty for x in f[nz:]), "flags past the zeroing workgroups moved"
+                tags.append(f[0])
+            else:
+                assert all(x == dirty for x in f), "a separate reset launch leaves the flags alone"
+        if reset == "in_launch":
+            assert len(set(tags)) == len(tags), "every launch has a tag of its own"
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
+def test_straggler_timestamps(mode):
+    """Per-tile completion clocks under a delayed source: every tile is stamped
+    (garbage left in the stamp array is cleared by the combine), and under SET
+    (one signal per source and tile) the delayed source's tiles complete later
+    on average than the others'."""
+    W, S, H, D = 4, 128, 4, 64
+    wl = synthgen.small_workload(W, S, H, D, "f32", seed=21, tile=(16, 1, 64),
+                                 protocol=synthgen.PROTOCOL_SET)
+    lag = 1
+    opts = opts_for(wl, mode=mode, straggler_rank=lag, straggler_delay=400, straggler_seed=7,
+                    consumer_split=1)
+    nt = ra2a.rev_all2all_signal_slots(W, S, H, D, "f32", opts)[0]
+    stamps = torch.full((W * nt,), -1, dtype=torch.int64, device="cuda")
+    opts.timestamps = stamps.data_ptr()
+    say(f"[case] straggler timestamps mode={mode}")
+    run_and_check(wl, opts, csplit=1)
+    t = stamps.cpu().numpy().view(np.uint64).reshape(W, nt // W, W)  # [dest, tile, source]
+    assert (t > 0).all() and (t != np.uint64(2**64 - 1)).all(), "a tile was not stamped"
+    t = (t - t.min()).astype(np.float64)
+    others = [r for r in range(W) if r != lag]
+    assert t[:, :, lag].mean() > t[:, :, others].mean(), (t[:, :, lag].mean(), t[:, :, others].mean())
+
+
 @pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
 def test_pipelined_equals_two_phase_bitwise(mode):
     """The barrier-synchronised variant as a differential for the signal-pipelined one."""
