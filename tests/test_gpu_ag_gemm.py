@@ -35,9 +35,10 @@ def parts_per_tile(m_local, K, tile_rows):
 
 
 def run_ag_gemm(shards, b, tile_rows, rank=0, flags=0):
+    """b is B (K x N), or B^T (N x K) when flags has AG_B_TRANSPOSED."""
     W = len(shards)
     m_local, K = shards[0].shape
-    N = b.shape[1]
+    N = b.shape[0] if flags & ra2a.AG_B_TRANSPOSED else b.shape[1]
     nt, nc, nq = ra2a.ag_gemm_signal_slots(W, m_local, tile_rows)
     nsig = nt + nc + nq
     shard_bytes = m_local * K * 2
@@ -106,6 +107,19 @@ def test_normal_inputs_within_tolerance(flags):
     check_common(shards, b, 128, c, g, sig, counts)
     ref = gemm.ag_gemm_ref(shards, b)
     err = gemm.rel_error(gemm.bf16_bits_to_f64(c), ref)
+    assert err <= 1e-2, err
+
+
+def test_pre_transposed_b_matches():
+    """Passing B^T (N x K) with AG_B_TRANSPOSED gives the same bits as passing B."""
+    wl = synthgen.AG_GEMM
+    say("[case] ag_gemm B vs pre-transposed B^T, W=4 m=384 K=520 N=392")
+    shards, b = synthgen.make_ag_gemm_inputs(wl, m_local=384, K=520, N=392, W=4)
+    c0, g0, sig0, counts = run_ag_gemm(shards, b, 128, 2, 0)
+    c1, g1, sig1, _ = run_ag_gemm(shards, np.ascontiguousarray(b.T), 128, 2, ra2a.AG_B_TRANSPOSED)
+    check_common(shards, b, 128, c1, g1, sig1, counts)
+    np.testing.assert_array_equal(c0, c1)
+    err = gemm.rel_error(gemm.bf16_bits_to_f64(c1), gemm.ag_gemm_ref(shards, b))
     assert err <= 1e-2, err
 
 
