@@ -84,33 +84,71 @@ __device__ __forceinline__ void wait_stages_after(int n) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// One stage of matrix-core work: wave (wm, wn) owns rows 128 wm .. +128 and
-// columns 128 wn .. +128 of the tile as 4 x 4 blocks of 32 x 32; each k16 step
+// Matrix-core work of one stage: wave (wm, wn) owns rows 128 wm .. +128 and
+// columns 128 wn .. +128 of the tile as 4 x 4 blocks of 32 x 32.  A k16 step
 // reads 4 A and 4 B fragments (16 bytes per lane) and issues 16 MFMAs
 // (v_mfma_f32_32x32x16_bf16: lane l supplies row / column l % 32, k 8 (l / 32) .. +8).
-__device__ __forceinline__ void stage_mma(f32x16 (&acc)[4][4], const uint16_t* lds_a,
-                                          const uint16_t* lds_b) {
+struct Frags {
+    bf16x8 a[4], b[4];
+};
+
+// 16-byte LDS reads at addr + OFF (OFF an immediate).  Written as inline
+// assembly on purpose: the compiler cannot tell these reads apart from the LDS
+// slots still being filled by the direct loads of later stages, and before
+// every LDS read it would wait for all of those loads (vmcnt(0)), which
+// serialises the pipeline.  The stage being read is already complete for every
+// wave (wait_stages_after + barrier); the caller waits for the reads with
+// lds_wait.
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+// Wait until at most N of this wave's LDS reads are outstanding; the fragments
+// are tied to the wait so that no use of them is scheduled above it.
+template <int N>
+__device__ __forceinline__ void lds_wait(Frags& f) {
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
+                   "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3])
+                 : "i"(N));
+}
+
+// LDS byte address of a stage slot's first element.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+// Lane byte offsets, inside an operand's stage slot, of the lane's fragment of
+// block 0 for k16 step kk: row 128 w + (l mod 32) (w = wm for A, wn for B^T),
+// chunk swz(row, 2 kk + l / 32).  The swizzle depends only on the row mod 32, so
+// blocks 1..3 (rows + 32 x) sit at fixed offsets of 32 x 64 bytes.
+__device__ __forceinline__ uint32_t frag_offset(int w, int kk) {
     const int l = (int)threadIdx.x & 63;
-    const int w = (int)threadIdx.x >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    const int r = l & 31;
+    const int row = 128 * w + (l & 31);
+    return 2u * (uint32_t)(row * kStageK + 8 * swz(row, 2 * kk + (l >> 5)));
+}
+
+__device__ __forceinline__ void read_frags(Frags& f, uint32_t a_addr, uint32_t b_addr) {
+    constexpr int kBlk = 32 * kStageK * 2;  // bytes between fragment blocks
+    f.a[0] = lds_read16<0>(a_addr);
+    f.a[1] = lds_read16<kBlk>(a_addr);
+    f.a[2] = lds_read16<2 * kBlk>(a_addr);
+    f.a[3] = lds_read16<3 * kBlk>(a_addr);
+    f.b[0] = lds_read16<0>(b_addr);
+    f.b[1] = lds_read16<kBlk>(b_addr);
+    f.b[2] = lds_read16<2 * kBlk>(b_addr);
+    f.b[3] = lds_read16<3 * kBlk>(b_addr);
+}
+
+__device__ __forceinline__ void mma_frags(f32x16 (&acc)[4][4], const Frags& f) {
 #pragma unroll
-    for (int kk = 0; kk < kStageK / 16; ++kk) {
-        const int c = 2 * kk + (l >> 5);
-        bf16x8 fa[4], fb[4];
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int ra = 128 * wm + 32 * x + r;
-            const int rb = 128 * wn + 32 * x + r;
-            fa[x] = *reinterpret_cast<const bf16x8*>(lds_a + ra * kStageK + 8 * swz(ra, c));
-            fb[x] = *reinterpret_cast<const bf16x8*>(lds_b + rb * kStageK + 8 * swz(rb, c));
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y)
-                acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
-    }
+        for (int y = 0; y < 4; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
 }
 
 // C[rows, cols] of one 256 x 256 output tile: rows of G from g_rows (rows_valid
@@ -123,8 +161,8 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g
     int64_t K = a.K, N = a.N;
     asm volatile("" : "+s"(K), "+s"(N));
     const int64_t cols_valid = N - n0 < kGemmBN ? N - n0 : kGemmBN;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(g_rows, (uint32_t)((int64_t)rows_valid * K * 2));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bt + n0 * K, (uint32_t)(cols_valid * K * 2));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc_uniform(g_rows, (uint32_t)((int64_t)rows_valid * K * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc_uniform(a.bt + n0 * K, (uint32_t)(cols_valid * K * 2));
     f32x16 acc[4][4];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
@@ -136,18 +174,46 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g
         uint16_t* st = lds + (s % kStages) * 2 * kStageElems;
         stage_load(ra, rb, st, st + kStageElems, K, s * kStageK);
     }
+    // Software pipeline over stages, one stage of LDS loads ahead of the reads:
+    //   read f1(s) | MFMAs of f0(s) | wait stage s+1, barrier, refill the slot of
+    //   stage s with stage s+4, read f0(s+1) | MFMAs of f1(s)
+    // so the LDS latency of each half hides under the other half's MFMAs.  A
+    // slot is refilled only after the barrier that follows every wave's wait for
+    // its own reads of it.  (Stage s is in slot s mod kStages; the loads of the
+    // stages after s+1 that are already issued may stay in flight.)
+    auto slot = [&](int64_t s) { return lds + (s % kStages) * 2 * kStageElems; };
+    auto issued_after = [&](int64_t s, int64_t last) { return (int)(last - s); };
+    wait_stages_after(issued_after(0, nk - 1 < kStages - 2 ? nk - 1 : kStages - 2));
+    __builtin_amdgcn_s_barrier();
+    if (kStages - 1 < nk) stage_load(ra, rb, slot(kStages - 1), slot(kStages - 1) + kStageElems, K,
+                                     (int64_t)(kStages - 1) * kStageK);
+    const int wave = (int)threadIdx.x >> 6;
+    const uint32_t oa0 = frag_offset(wave >> 1, 0), oa1 = frag_offset(wave >> 1, 1);
+    const uint32_t ob0 = frag_offset(wave & 1, 0) + 2u * kStageElems;
+    const uint32_t ob1 = frag_offset(wave & 1, 1) + 2u * kStageElems;
+    Frags f0, f1;
+    read_frags(f0, lds_addr(slot(0)) + oa0, lds_addr(slot(0)) + ob0);
     for (int64_t s = 0; s < nk; ++s) {
-        const int64_t after = nk - 1 - s;
-        wait_stages_after(after < 2 ? (int)after : 2);
-        // every wave's loads of stage s have landed, and every wave is done with
-        // stage s - 1, whose slot the next load reuses
-        __builtin_amdgcn_s_barrier();
-        if (s + kStages - 1 < nk) {
-            uint16_t* st = lds + ((s + kStages - 1) % kStages) * 2 * kStageElems;
-            stage_load(ra, rb, st, st + kStageElems, K, (s + kStages - 1) * kStageK);
+        const uint32_t cur = lds_addr(slot(s));
+        read_frags(f1, cur + oa1, cur + ob1);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait<8>(f0);
+        mma_frags(acc, f0);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait<0>(f1);  // every read of stage s is in: its slot may be refilled
+        if (s + 1 < nk) {
+            // issued so far: stages up to min(nk - 1, s + kStages - 1)
+            const int64_t last = nk - 1 < s + kStages - 1 ? nk - 1 : s + kStages - 1;
+            wait_stages_after(issued_after(s + 1, last));
+            __builtin_amdgcn_s_barrier();
+            if (s + kStages < nk)
+                stage_load(ra, rb, slot(s), slot(s) + kStageElems, K, (s + kStages) * kStageK);
+            const uint32_t nxt = lds_addr(slot(s + 1));
+            read_frags(f0, nxt + oa0, nxt + ob0);
         }
-        const uint16_t* cur = lds + (s % kStages) * 2 * kStageElems;
-        stage_mma(acc, cur, cur + kStageElems);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags(acc, f1);
+        __builtin_amdgcn_sched_barrier(0);
     }
     // epilogue: accumulator register e of block (x, y) holds row 8 (e/4) + 4 (lane/32) + e%4,
     // column lane % 32 of the block.  (The empty asm makes the output pointer opaque
@@ -157,7 +223,6 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g
     asm volatile("" : "+v"(cbase));
     c_rows = reinterpret_cast<uint16_t*>(cbase);
     const int lane = (int)threadIdx.x & 63;
-    const int wave = (int)threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int x = 0; x < 4; ++x)

@@ -205,6 +205,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              (int)kBufferDword3);
 }
 
+// The same for a wave-uniform base and size, stated to the compiler: the
+// descriptor then lives in scalar registers.  (A descriptor the compiler cannot
+// prove uniform sits in vector registers, and every buffer instruction using it
+// is wrapped in a loop over its distinct values.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
+                     __builtin_amdgcn_readfirstlane(bytes));
+}
+
 template <int V, int POLICY> struct BufLoad;
 template <int POLICY> struct BufLoad<16, POLICY> {
     static __device__ __forceinline__ u32x4 go(__amdgpu_buffer_rsrc_t r, uint32_t off) {
