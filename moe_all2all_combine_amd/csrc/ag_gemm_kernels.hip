@@ -26,11 +26,17 @@ namespace ra2a {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmThreads = 256;  // 4 waves: 2 x 2 of 128 x 128 output elements each
+constexpr int kGemmWaves = 8;      // 2 per SIMD: one issues MFMAs while the other waits
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kWaveRows = 64;      // each wave owns 64 x 128 outputs of the tile:
+constexpr int kWaveCols = 128;     //   waves (wm, wn), wm = wave / 2, wn = wave mod 2
+constexpr int kBlkA = kWaveRows / 32;  // 32 x 32 MFMA blocks per wave along rows
+constexpr int kBlkB = kWaveCols / 32;  // ... and along columns
 constexpr int kStageK = 32;        // k per pipeline stage
 constexpr int kStages = 4;         // LDS ring depth (3 stages in flight)
 constexpr int kStageElems = kGemmBM * kStageK;  // bf16 per operand per stage (16 KiB)
-constexpr int kDmaPerStage = 8;    // 16-byte LDS loads per thread per stage (4 A + 4 B)
+constexpr int kRowsPerWave = kGemmBM / kGemmWaves;        // operand rows each wave loads
+constexpr int kDmaPerStage = 2 * (kRowsPerWave / 16);      // its LDS loads per stage (A and B)
 
 // float -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -40,11 +46,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 // LDS stage layout of an operand: 256 rows x 32 k (64 bytes per row, four 16-byte
-// chunks).  Chunk c of row r is stored at position c ^ g(r), g(r) = ((r >> 1) ^
-// (r >> 3)) & 3, so the 16-byte fragment reads of 8, and of 16, consecutive rows
-// at one chunk all land in different 16-byte bank groups (whether the LDS serves
-// 128 or 256 bytes per cycle).
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+// chunks).  Chunk c of row r is stored at position c ^ g(r), g(r) = (r >> 2) & 3.
+// Of the XOR patterns measured with the LDS bank-conflict counter on gfx950 for
+// these fragment reads (32 consecutive rows at one chunk, and the same rows at
+// the next chunk), this one is the only conflict-free one: (r >> 1) & 3 and
+// ((r >> 1) ^ (r >> 3)) & 3 stall 4 cycles per read, r & 3 and no swizzle 12.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 // Offset sent for a chunk that must read as zero: past any buffer's range.
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
@@ -59,8 +66,8 @@ __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_b
     const int w = (int)threadIdx.x >> 6;
     const int l = (int)threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rbase = 64 * w + 16 * i;
+    for (int i = 0; i < kRowsPerWave / 16; ++i) {
+        const int rbase = kRowsPerWave * w + 16 * i;
         const int row = rbase + (l >> 2);
         const int c = swz(row, l & 3);
         const int64_t k = k0 + 8 * c;
@@ -77,19 +84,20 @@ __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_b
 // one about to be read.
 __device__ __forceinline__ void wait_stages_after(int n) {
     if (n >= 2)
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * kDmaPerStage) : "memory");
     else if (n == 1)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kDmaPerStage) : "memory");
     else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Matrix-core work of one stage: wave (wm, wn) owns rows 128 wm .. +128 and
-// columns 128 wn .. +128 of the tile as 4 x 4 blocks of 32 x 32.  A k16 step
-// reads 4 A and 4 B fragments (16 bytes per lane) and issues 16 MFMAs
-// (v_mfma_f32_32x32x16_bf16: lane l supplies row / column l % 32, k 8 (l / 32) .. +8).
+// Matrix-core work: wave (wm, wn) owns rows kWaveRows wm .. + kWaveRows and
+// columns kWaveCols wn .. + kWaveCols of the tile as kBlkA x kBlkB blocks of
+// 32 x 32.  A k16 step reads kBlkA A and kBlkB B fragments (16 bytes per lane)
+// and issues kBlkA kBlkB MFMAs (v_mfma_f32_32x32x16_bf16: lane l supplies row /
+// column l % 32, k 8 (l / 32) .. +8).
 struct Frags {
-    bf16x8 a[4], b[4];
+    bf16x8 a[kBlkA], b[kBlkB];
 };
 
 // 16-byte LDS reads at addr + OFF (OFF an immediate).  Written as inline
@@ -110,9 +118,10 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
 // are tied to the wait so that no use of them is scheduled above it.
 template <int N>
 __device__ __forceinline__ void lds_wait(Frags& f) {
-    asm volatile("s_waitcnt lgkmcnt(%8)"
-                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
-                   "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3])
+    static_assert(kBlkA == 2 && kBlkB == 4, "lds_wait ties 2 + 4 fragments");
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]),
+                   "+v"(f.b[3])
                  : "i"(N));
 }
 
@@ -122,12 +131,12 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
 }
 
 // Lane byte offsets, inside an operand's stage slot, of the lane's fragment of
-// block 0 for k16 step kk: row 128 w + (l mod 32) (w = wm for A, wn for B^T),
-// chunk swz(row, 2 kk + l / 32).  The swizzle depends only on the row mod 32, so
-// blocks 1..3 (rows + 32 x) sit at fixed offsets of 32 x 64 bytes.
-__device__ __forceinline__ uint32_t frag_offset(int w, int kk) {
+// block 0 for k16 step kk: row row0 + (l mod 32), chunk swz(row, 2 kk + l / 32).
+// The swizzle depends only on the row mod 32, so the other blocks (rows + 32 x)
+// sit at fixed offsets of 32 x 64 bytes.
+__device__ __forceinline__ uint32_t frag_offset(int row0, int kk) {
     const int l = (int)threadIdx.x & 63;
-    const int row = 128 * w + (l & 31);
+    const int row = row0 + (l & 31);
     return 2u * (uint32_t)(row * kStageK + 8 * swz(row, 2 * kk + (l >> 5)));
 }
 
@@ -135,19 +144,17 @@ __device__ __forceinline__ void read_frags(Frags& f, uint32_t a_addr, uint32_t b
     constexpr int kBlk = 32 * kStageK * 2;  // bytes between fragment blocks
     f.a[0] = lds_read16<0>(a_addr);
     f.a[1] = lds_read16<kBlk>(a_addr);
-    f.a[2] = lds_read16<2 * kBlk>(a_addr);
-    f.a[3] = lds_read16<3 * kBlk>(a_addr);
     f.b[0] = lds_read16<0>(b_addr);
     f.b[1] = lds_read16<kBlk>(b_addr);
     f.b[2] = lds_read16<2 * kBlk>(b_addr);
     f.b[3] = lds_read16<3 * kBlk>(b_addr);
 }
 
-__device__ __forceinline__ void mma_frags(f32x16 (&acc)[4][4], const Frags& f) {
+__device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Frags& f) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < kBlkA; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
+        for (int y = 0; y < kBlkB; ++y)
             acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
 }
 
@@ -163,11 +170,11 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g
     const int64_t cols_valid = N - n0 < kGemmBN ? N - n0 : kGemmBN;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc_uniform(g_rows, (uint32_t)((int64_t)rows_valid * K * 2));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc_uniform(a.bt + n0 * K, (uint32_t)(cols_valid * K * 2));
-    f32x16 acc[4][4];
+    f32x16 acc[kBlkA][kBlkB];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < kBlkA; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
+        for (int y = 0; y < kBlkB; ++y) acc[x][y] = f32x16{};
     const int64_t nk = (K + kStageK - 1) / kStageK;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only this tile's LDS loads in flight below
     for (int64_t s = 0; s < nk && s < kStages - 1; ++s) {
@@ -188,16 +195,17 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g
     if (kStages - 1 < nk) stage_load(ra, rb, slot(kStages - 1), slot(kStages - 1) + kStageElems, K,
                                      (int64_t)(kStages - 1) * kStageK);
     const int wave = (int)threadIdx.x >> 6;
-    const uint32_t oa0 = frag_offset(wave >> 1, 0), oa1 = frag_offset(wave >> 1, 1);
-    const uint32_t ob0 = frag_offset(wave & 1, 0) + 2u * kStageElems;
-    const uint32_t ob1 = frag_offset(wave & 1, 1) + 2u * kStageElems;
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t oa0 = frag_offset(kWaveRows * wm, 0), oa1 = frag_offset(kWaveRows * wm, 1);
+    const uint32_t ob0 = frag_offset(kWaveCols * wn, 0) + 2u * kStageElems;
+    const uint32_t ob1 = frag_offset(kWaveCols * wn, 1) + 2u * kStageElems;
     Frags f0, f1;
     read_frags(f0, lds_addr(slot(0)) + oa0, lds_addr(slot(0)) + ob0);
     for (int64_t s = 0; s < nk; ++s) {
         const uint32_t cur = lds_addr(slot(s));
         read_frags(f1, cur + oa1, cur + ob1);
         __builtin_amdgcn_sched_barrier(0);
-        lds_wait<8>(f0);
+        lds_wait<kBlkA + kBlkB>(f0);
         mma_frags(acc, f0);
         __builtin_amdgcn_sched_barrier(0);
         lds_wait<0>(f1);  // every read of stage s is in: its slot may be refilled
@@ -223,15 +231,14 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g
     asm volatile("" : "+v"(cbase));
     c_rows = reinterpret_cast<uint16_t*>(cbase);
     const int lane = (int)threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < kBlkA; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int64_t col = 128 * wn + 32 * y + (lane & 31);
+        for (int y = 0; y < kBlkB; ++y) {
+            const int64_t col = kWaveCols * wn + 32 * y + (lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = 128 * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 if (row < rows_valid && col < cols_valid)
                     c_rows[(int64_t)row * N + n0 + col] = (uint16_t)bf16_rne(acc[x][y][e]);
             }
