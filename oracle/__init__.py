@@ -12,6 +12,9 @@ Contents and the passages they follow:
   Distributed Kernel)", section "Reverse All2All Operator Semantics", with the
   column order r*H + h and the row split j*S + s taken from the same page's
   MTE listing ("Triton-Distributed Reverse All2All Operator").
+* ``dispatch`` / ``dispatch_dest`` (C, ``combine.c``): the forward All2All read
+  as the combine's inverse, out_r[j*S+s, h, d] = in_j[s, r*H+h, d] (same page,
+  sections "Reverse All2All Operator Semantics" and "EP MoE Scenario").
 * ``source_of``: the same definition read backwards, for one output element.
 * ``symm_at``: "Distributed Architecture Design", section 5.3: the symmetric
   offset of a pointer inside its own heap, added to the target's heap base.
@@ -49,6 +52,9 @@ def _load():
         lib.oracle_combine_dest.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
                                             i64, i64, i64, i64, i64, i64]
         lib.oracle_combine_dest.restype = ctypes.c_int
+        lib.oracle_dispatch_dest.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                             i64, i64, i64, i64, i64, i64]
+        lib.oracle_dispatch_dest.restype = ctypes.c_int
         lib.oracle_source_of.argtypes = [i64] * 8 + [ctypes.POINTER(i64)] * 3
         lib.oracle_source_of.restype = None
         lib.oracle_allgather.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
@@ -94,6 +100,30 @@ def combine(inputs: Sequence[np.ndarray]) -> List[np.ndarray]:
     """All W outputs, each of shape (S, H*W, D)."""
     W = len(inputs)
     return [combine_dest(inputs, j) for j in range(W)]
+
+
+def dispatch_dest(inputs: Sequence[np.ndarray], r: int) -> np.ndarray:
+    """out_r of shape (S*W, H, D) from the W dispatch inputs, each (S, H*W, D)."""
+    W = len(inputs)
+    if W < 1:
+        raise ValueError("need at least one rank")
+    shape, dt = inputs[0].shape, inputs[0].dtype
+    if len(shape) != 3 or shape[1] % W:
+        raise ValueError(f"each dispatch input must be (S, H*W, D); got {shape} for W={W}")
+    for a in inputs:
+        if a.shape != shape or a.dtype != dt or not a.flags.c_contiguous:
+            raise ValueError("inputs must share one shape and dtype and be C-contiguous")
+    S, H, D = shape[0], shape[1] // W, shape[2]
+    out = np.empty((S * W, H, D), dtype=dt)
+    rc = _load().oracle_dispatch_dest(_ptrs(inputs), out.ctypes.data, r, W, S, H, D, dt.itemsize)
+    if rc:
+        raise ValueError("oracle_dispatch_dest rejected its arguments")
+    return out
+
+
+def dispatch(inputs: Sequence[np.ndarray]) -> List[np.ndarray]:
+    """All W dispatch outputs, each of shape (S*W, H, D): out_r[j*S+s, h, d] = in_j[s, r*H+h, d]."""
+    return [dispatch_dest(inputs, r) for r in range(len(inputs))]
 
 
 def source_of(j: int, s: int, c: int, d: int, W: int, S: int, H: int, D: int):

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the Reverse All2All (EP-MoE combine) -- TEST INFRASTRUCTURE ONLY.
+ * CPU oracle for the Reverse All2All (EP-MoE combine) and its inverse, the forward
+ * All2All (dispatch) -- TEST INFRASTRUCTURE ONLY.
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg load
  * this file's library.  The GPU path never links, includes or calls it.
@@ -57,6 +58,40 @@ int oracle_combine(const void *const *in, void *const *out, int64_t W, int64_t S
         int rc = oracle_combine_dest(in, out[j], j, W, S, H, D, e);
         if (rc) return rc;
     }
+    return 0;
+}
+
+/*
+ * Forward All2All (dispatch), read as the exact inverse of the combine.  The
+ * page's "EP MoE Scenario" sends tokens to the experts' ranks with the
+ * dispatch and brings the expert outputs back with the combine, so combine
+ * after dispatch returns every token to where it started.  (The page's shape
+ * line for the dispatch has the same form as the combine's; its "dimension
+ * swap" sentence and the round trip fix the direction.)  Rank j holds an input
+ * of shape (S, H*W, D); rank r receives an output of shape (S*W, H, D):
+ *
+ *       out_r[j*S + s, h, d] = in_j[s, r*H + h, d]
+ *
+ * for r, j in [0, W), s in [0, S), h in [0, H), d in [0, D).
+ */
+int oracle_dispatch_dest(const void *const *in, void *out_r, int64_t r, int64_t W,
+                         int64_t S, int64_t H, int64_t D, int64_t e)
+{
+    if (W < 1 || S < 0 || H < 1 || D < 1 || r < 0 || r >= W) return -1;
+    for (int64_t j = 0; j < W; ++j)
+        for (int64_t s = 0; s < S; ++s)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t d = 0; d < D; ++d) {
+                    const int64_t o = ((j * S + s) * H + h) * D + d;   /* out_r[j*S + s, h, d] */
+                    const int64_t i = (s * (H * W) + r * H + h) * D + d; /* in_j[s, r*H + h, d] */
+                    switch (e) {
+                    case 1: ((uint8_t *)out_r)[o] = ((const uint8_t *)in[j])[i]; break;
+                    case 2: ((uint16_t *)out_r)[o] = ((const uint16_t *)in[j])[i]; break;
+                    case 4: ((uint32_t *)out_r)[o] = ((const uint32_t *)in[j])[i]; break;
+                    case 8: ((uint64_t *)out_r)[o] = ((const uint64_t *)in[j])[i]; break;
+                    default: return -1;
+                    }
+                }
     return 0;
 }
 
