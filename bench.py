@@ -20,7 +20,8 @@ element read once and every output element written once, per step), the
 roofline of the persistent kernel (its duration from HIP events around every
 launch, on the launch stream, in a separate pass over the same steps: events
 between kernels slow the steps themselves), and for context the staged mode, the two-phase variant, a
-plain copy of the same bytes with the library's put kernel, and the CPU
+plain copy of the same bytes with the library's put kernel, the forward
+All2All (dispatch, the combine's inverse map) on the same buffers, and the CPU
 oracle's rate on the host.
 
 ``--legs main`` runs only the timed combine (for counter runs under rocprofv3).
@@ -196,7 +197,11 @@ def main():
     opts_lib = ra2a.Opts(**tiles)  # the library's own reset (in-launch in direct mode)
     opts = ra2a.Opts(skip_reset=1, **tiles)
     opts_st = ra2a.Opts(skip_reset=1, mode=ra2a.MODE_STAGED, **tiles)
-    nsig = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o)) for o in (opts, opts_st))
+    dopts = ra2a.Opts(direction=ra2a.DIR_DISPATCH, **tiles)  # forward All2All, same buffers
+    nsig = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
+               for o in (opts, opts_st, dopts))  # each set's signal array holds any of them
+    nsig_c = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
+                 for o in (opts, opts_st))  # what the combine's separate reset launch clears
     ring = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, opts_st)
     full = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, None, True)
     nb = wl.bytes_per_rank
@@ -228,12 +233,12 @@ def main():
         elif overlap:
             if done[k % NSETS] is not None:
                 side.wait_event(done[k % NSETS])
-            ra2a.signal_reset(hs, heap.ptr(osg), nsig, side)
+            ra2a.signal_reset(hs, heap.ptr(osg), nsig_c, side)
             ready = torch.cuda.Event()
             ready.record(side)
             stream.wait_event(ready)
         else:
-            ra2a.signal_reset(hs, heap.ptr(osg), nsig, stream)
+            ra2a.signal_reset(hs, heap.ptr(osg), nsig_c, stream)
         ra2a.rev_all2all_ex(heap.ptr(oi), heap.ptr(oo), heap.ptr(osg), W, S, H, D, wl.dtype, o,
                             stream)
         if overlap and reset:
@@ -331,6 +336,32 @@ def main():
         st_ok = parity(args.steps - 1)
         rec["staged"] = {"ms_per_step": round(st_ms, 5),
                          "value": round(alg / (st_ms * 1e-3) / 1e9, 2), "parity": st_ok}
+
+        # forward All2All (dispatch, the combine's inverse) on the same buffers
+        # (in_j read as (S, H*W, D), out_r written as (S*W, H, D)), in-launch reset
+
+        def dispatch(k):
+            oi, oo, osg = sets[k % NSETS]
+            ra2a.all2all_dispatch_ex(heap.ptr(oi), heap.ptr(oo), heap.ptr(osg), W, S, H, D,
+                                     wl.dtype, dopts, stream)
+
+        for k in range(args.warmup):
+            dispatch(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            dispatch(k)
+        torch.cuda.synchronize()
+        d_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
+        import oracle
+        d_want = oracle.dispatch([x.reshape(S, H * W, D) for x in ins])
+        d_oo = sets[(args.steps - 1) % NSETS][1]
+        d_ok = all(heap.view(d_oo, (S * W, H, D), bits, r).cpu().numpy().tobytes() ==
+                   d_want[r].tobytes() for r in range(W))
+        rec["dispatch"] = {"ms_per_step": round(d_ms, 5),
+                           "value": round(alg / (d_ms * 1e-3) / 1e9, 2), "parity": d_ok,
+                           "note": "forward All2All (the combine's inverse), one launch per step"}
 
         def two_phase(k):
             oi, oo, _ = sets[k % NSETS]

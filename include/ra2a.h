@@ -192,6 +192,10 @@ int ra2a_signal_reset(const ra2a_heap_t *heap, uint64_t *sig_sym, int64_t n_slot
 #define RA2A_PROTO_ADD 1 /* push mode: W adds per tile, wait for W (default) */
 #define RA2A_PROTO_SET 2 /* one SET per (source, tile) piece, wait for 1 */
 
+/* Which map a launch performs (ra2a_opts_t.direction). */
+#define RA2A_DIR_COMBINE 0  /* out_j[s, r*H + h, d] = in_r[j*S + s, h, d] */
+#define RA2A_DIR_DISPATCH 1 /* out_r[j*S + s, h, d] = in_j[s, r*H + h, d] (the inverse) */
+
 /* Where producers put their pieces (ra2a_opts_t.mode). */
 #define RA2A_MODE_DIRECT 1 /* push straight into out_j (default) */
 #define RA2A_MODE_STAGED 2 /* through a staging ring in slice j, reordered by consumers */
@@ -263,6 +267,8 @@ typedef struct ra2a_opts {
     int32_t separate_reset;   /* 1: zero the signals with a launch of their own before the
                                * combine's, also in direct mode (0, the default: direct
                                * mode zeroes them inside the combine launch) */
+    int32_t direction;        /* RA2A_DIR_COMBINE (0, the default) or RA2A_DIR_DISPATCH (the
+                               * inverse map; see ra2a_all2all_dispatch) */
     int32_t reserved[1];      /* must be zero */
 } ra2a_opts_t;
 
@@ -309,6 +315,26 @@ int ra2a_rev_all2all(const void *in, void *out, uint64_t *signals, int W, int64_
 /* Same, with explicit tiling / protocol / straggler options (opts may be NULL). */
 int ra2a_rev_all2all_ex(const void *in, void *out, uint64_t *signals, int W, int64_t S,
                         int64_t H, int64_t D, int dtype, const ra2a_opts_t *opts, void *stream);
+
+/* Forward All2All (dispatch), read as the exact inverse of the combine
+ * ("Reverse All2All (EP MoE Distributed Kernel)", sections "Reverse All2All
+ * Operator Semantics" and "EP MoE Scenario": the dispatch sends tokens to the
+ * experts' ranks and the combine brings the outputs back, so a combine after a
+ * dispatch returns every element to its place).  Rank j's input `in` (slice j)
+ * is (S, H*W, D); rank r's output `out` (slice r) is (S*W, H, D):
+ *     out_r[j*S + s, h, d] = in_j[s, r*H + h, d].
+ * Same buffers, heap, tiling options and in-launch reset as the direct-mode
+ * combine: the signal tile (source j's S-block b, head block, d block) of
+ * destination r has one slot per source (the SET layout,
+ * ra2a_rev_all2all_signal_slots with direction = RA2A_DIR_DISPATCH), and each
+ * ends at 1.  Staged mode is rejected (EINVAL).  _ex takes the combine's
+ * options (direction is forced to RA2A_DIR_DISPATCH).
+ * Errors: EINVAL, EHIP.                                                         */
+int ra2a_all2all_dispatch(const void *in, void *out, uint64_t *signals, int W, int64_t S,
+                          int64_t H, int64_t D, int dtype, void *stream);
+int ra2a_all2all_dispatch_ex(const void *in, void *out, uint64_t *signals, int W, int64_t S,
+                             int64_t H, int64_t D, int dtype, const ra2a_opts_t *opts,
+                             void *stream);
 
 /* The two-phase variant ("UDMA Optimized Implementation": "Two-Phase Data
  * Copy"): phase 1 copies every contiguous (S, H, D) segment in_r[j*S, (j+1)*S)

@@ -18,7 +18,7 @@ from typing import Optional, Sequence, Tuple
 __all__ = [
     "Ra2aError", "Opts", "SymmHeap", "lib", "OK", "EINVAL", "ENOMEM", "EHIP", "ETIMEOUT",
     "EUNSUPPORTED", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "MODE_DIRECT", "MODE_STAGED",
-    "QUEUE_SLOTS", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
+    "QUEUE_SLOTS", "DIR_COMBINE", "DIR_DISPATCH", "all2all_dispatch", "all2all_dispatch_ex", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
     "CMP_LE", "SIG_STRIDE_BYTES", "DTYPES", "symm_heap_create", "symm_heap_attach",
     "symm_heap_destroy", "symm_malloc", "symm_heap_info", "symm_at", "put", "get",
     "put_with_signal", "signal_op", "wait_signal", "signal_reset", "rev_all2all",
@@ -36,6 +36,8 @@ SIG_SET, SIG_ADD = 0, 1
 PROTO_ADD, PROTO_SET = 1, 2
 MODE_DIRECT, MODE_STAGED = 1, 2
 QUEUE_SLOTS = 18
+DIR_COMBINE = 0
+DIR_DISPATCH = 1
 RESET_FLAGS = 64
 AG_AGENT_SYNC, AG_SKIP_RESET, AG_B_TRANSPOSED = 1, 2, 4
 CMP_EQ, CMP_NE, CMP_GT, CMP_GE, CMP_LT, CMP_LE = range(6)
@@ -64,7 +66,7 @@ class Opts(ctypes.Structure):
         ("consumer_split", ctypes.c_int32), ("skip_reset", ctypes.c_int32),
         ("stream_batch", ctypes.c_int32), ("agent_sync", ctypes.c_int32),
         ("head_merge", ctypes.c_int32), ("separate_reset", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 1),
+        ("direction", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
     ]
 
     def __init__(self, **kw):
@@ -113,6 +115,8 @@ def lib():
         "ra2a_rev_all2all": (i32, [vp, vp, vp, i32, i64, i64, i64, i32, vp]),
         "ra2a_rev_all2all_ex": (i32, [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp]),
         "ra2a_rev_all2all_two_phase": (i32, [vp, vp, vp, i32, i64, i64, i64, i32, vp]),
+        "ra2a_all2all_dispatch": (i32, [vp, vp, vp, i32, i64, i64, i64, i32, vp]),
+        "ra2a_all2all_dispatch_ex": (i32, [vp, vp, vp, i32, i64, i64, i64, i32, vp, vp]),
         "ra2a_check": (i32, [vp]),
         "ra2a_ag_gemm_signal_slots": (i32, [i32, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                             ctypes.POINTER(i64)]),
@@ -273,6 +277,19 @@ def rev_all2all_ex(inp: int, out: int, signals: int, W: int, S: int, H: int, D: 
                    opts=None, stream=None) -> None:
     _ok(lib().ra2a_rev_all2all_ex(inp, out, signals, W, S, H, D, _dtype(dtype), _opts(opts),
                                   _stream(stream)))
+
+
+def all2all_dispatch(inp: int, out: int, signals: int, W: int, S: int, H: int, D: int, dtype,
+                     stream=None) -> None:
+    """Forward All2All: out_r[j*S+s, h, d] = in_j[s, r*H+h, d] (the combine's inverse)."""
+    _ok(lib().ra2a_all2all_dispatch(inp, out, signals, W, S, H, D, _dtype(dtype),
+                                    _stream(stream)))
+
+
+def all2all_dispatch_ex(inp: int, out: int, signals: int, W: int, S: int, H: int, D: int, dtype,
+                        opts=None, stream=None) -> None:
+    _ok(lib().ra2a_all2all_dispatch_ex(inp, out, signals, W, S, H, D, _dtype(dtype), _opts(opts),
+                                       _stream(stream)))
 
 
 def rev_all2all_two_phase(inp: int, out: int, signals: Optional[int], W: int, S: int, H: int,

@@ -143,6 +143,7 @@ struct Plan {
     int stream_batch;       // 0 = derive from the L2 budget
     int agent_sync;
     int direct;             // 1: direct push (no staging), 0: staged through the ring
+    int inverse;            // 1: the dispatch (the combine's inverse map)
     int64_t piece_bytes, unit_bytes, tile_bytes;
 };
 
@@ -152,6 +153,10 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     z.straggler_rank = -1;
     if (!o) o = &z;
     if (o->reserved[0]) return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
+    if (o->direction != RA2A_DIR_COMBINE && o->direction != RA2A_DIR_DISPATCH)
+        return fail(RA2A_EINVAL, "direction must be RA2A_DIR_COMBINE or RA2A_DIR_DISPATCH");
+    if (o->direction == RA2A_DIR_DISPATCH && o->mode == RA2A_MODE_STAGED)
+        return fail(RA2A_EINVAL, "the dispatch runs in direct mode only");
     if (o->separate_reset != 0 && o->separate_reset != 1)
         return fail(RA2A_EINVAL, "separate_reset must be 0 or 1");
     if (o->mode != 0 && o->mode != RA2A_MODE_DIRECT && o->mode != RA2A_MODE_STAGED)
@@ -166,7 +171,10 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     p->TD = std::min(p->TD, D);
     if (o->protocol != 0 && o->protocol != RA2A_PROTO_ADD && o->protocol != RA2A_PROTO_SET)
         return fail(RA2A_EINVAL, "protocol must be 0, RA2A_PROTO_ADD or RA2A_PROTO_SET");
-    p->protocol = o->protocol == RA2A_PROTO_SET ? RA2A_SIG_SET : RA2A_SIG_ADD;
+    p->inverse = o->direction == RA2A_DIR_DISPATCH ? 1 : 0;
+    // the dispatch fills each output tile from one source: one signal per
+    // (tile, source), set to 1 (the SET layout)
+    p->protocol = (o->protocol == RA2A_PROTO_SET || p->inverse) ? RA2A_SIG_SET : RA2A_SIG_ADD;
     p->nbs = (int)cdiv(S, p->BS);
     p->nhb = (int)cdiv(H, p->TH);
     p->ndb = (int)cdiv(D, p->TD);
@@ -375,6 +383,7 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     a->regionB = pl.regionB;
     a->ring_bytes = pl.ring_bytes;
     a->direct = pl.direct;
+    a->inverse = pl.inverse;
     a->straggler = opts ? opts->straggler_rank : -1;
     a->delay = opts ? opts->straggler_delay : 0;
     a->seed = opts ? opts->straggler_seed : 0;
@@ -807,6 +816,25 @@ RA2A_API int ra2a_rev_all2all_ex(const void* in, void* out, uint64_t* signals, i
                                  int64_t H, int64_t D, int dtype, const ra2a_opts_t* opts,
                                  void* stream) {
     return combine_pipelined(in, out, signals, W, S, H, D, dtype, opts, stream);
+}
+
+RA2A_API int ra2a_all2all_dispatch(const void* in, void* out, uint64_t* signals, int W, int64_t S,
+                                   int64_t H, int64_t D, int dtype, void* stream) {
+    return ra2a_all2all_dispatch_ex(in, out, signals, W, S, H, D, dtype, nullptr, stream);
+}
+
+RA2A_API int ra2a_all2all_dispatch_ex(const void* in, void* out, uint64_t* signals, int W,
+                                      int64_t S, int64_t H, int64_t D, int dtype,
+                                      const ra2a_opts_t* opts, void* stream) {
+    ra2a_opts_t o;
+    if (opts) {
+        o = *opts;
+    } else {
+        std::memset(&o, 0, sizeof o);
+        o.straggler_rank = -1;
+    }
+    o.direction = RA2A_DIR_DISPATCH;
+    return combine_pipelined(in, out, signals, W, S, H, D, dtype, &o, stream);
 }
 
 RA2A_API int ra2a_rev_all2all_two_phase(const void* in, void* out, uint64_t* signals, int W,

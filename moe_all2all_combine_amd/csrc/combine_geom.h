@@ -228,17 +228,28 @@ RA2A_HD Piece piece_at(const PipeArgs& a, int sid, int b, int r) {
     const int64_t HWDe = a.H * (int64_t)a.W * a.D * e;
     const int64_t s0 = (int64_t)p.b * a.BS;
     const int bs = (int)geom_min(a.BS, a.S - s0);
-    p.src = (int64_t)p.r * a.stride + a.in_off + (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e +
-            st.d0 * e;
-    // staging ring slot, or (direct) the piece's final place in out_j: both are
-    // rows of [H*W][D] columns, the ring being a window of S-blocks of the output
-    p.dst = a.direct ? (int64_t)st.j * a.stride + a.out_off + s0 * HWDe
-                     : (int64_t)st.j * a.stride + a.stg_off + (int64_t)p.slot * a.BS * HWDe;
-    p.dst += ((int64_t)p.r * a.H + st.h0) * a.D * e + st.d0 * e;
     RowPlan& pl = p.pl;
     pl.A = bs;
-    pl.sa = a.H * a.D * e;  // input token stride
-    pl.da = HWDe;           // staging token stride
+    if (a.inverse) {
+        // dispatch: source rank p.r sends in_r[s0.., j*H + h0.., d0..] (rows of
+        // [H*W][D] columns) to out_j[r*S + s0.., h0.., d0..] (rows of [H][D])
+        p.src = (int64_t)p.r * a.stride + a.in_off + s0 * HWDe + ((int64_t)st.j * a.H + st.h0) * a.D * e +
+                st.d0 * e;
+        p.dst = (int64_t)st.j * a.stride + a.out_off +
+                (((int64_t)p.r * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e;
+        pl.sa = HWDe;
+        pl.da = a.H * a.D * e;
+    } else {
+        p.src = (int64_t)p.r * a.stride + a.in_off + (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e +
+                st.d0 * e;
+        // staging ring slot, or (direct) the piece's final place in out_j: both are
+        // rows of [H*W][D] columns, the ring being a window of S-blocks of the output
+        p.dst = a.direct ? (int64_t)st.j * a.stride + a.out_off + s0 * HWDe
+                         : (int64_t)st.j * a.stride + a.stg_off + (int64_t)p.slot * a.BS * HWDe;
+        p.dst += ((int64_t)p.r * a.H + st.h0) * a.D * e + st.d0 * e;
+        pl.sa = a.H * a.D * e;  // input token stride
+        pl.da = HWDe;           // staging token stride
+    }
     pl.C = 1;
     pl.sc = pl.dc = 0;
     if (st.td == a.D) {     // the tile spans D: its heads form one run

@@ -20,7 +20,9 @@ def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):
     R = nbs if direct else min(opts.ring or 8, nbs)
     if direct:
         csplit = 1
-    proto = SET if opts.protocol == ra2a.PROTO_SET else ADD
+    # the dispatch fills each tile from one source: one slot per (tile, source), SET 1
+    dispatch = getattr(opts, "direction", 0) == ra2a.DIR_DISPATCH
+    proto = SET if (opts.protocol == ra2a.PROTO_SET or dispatch) else ADD
     per = W if proto == SET else 1
     # merged head blocks: derived from the size of the hand-back region
     _, n_credit, _ = ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)

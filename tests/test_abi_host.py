@@ -164,3 +164,32 @@ def test_primitive_validation(fake_heap):
     assert L.ra2a_signal_reset(fake_heap, FAKE_BASE + (4 << 20) - 128, 2, None) == ra2a.EINVAL
     assert L.ra2a_symm_heap_create(0, 1, ctypes.byref(ctypes.c_void_p())) == ra2a.EINVAL
     assert ra2a.last_error() != ""
+
+
+def test_opts_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of ra2a_opts_t has the C struct's size and field offsets."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    fields = [f[0] for f in ra2a.Opts._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "ra2a.h"', "int main(void) {",
+           '  printf("%zu\\n", sizeof(ra2a_opts_t));']
+    src += [f'  printf("%zu\\n", offsetof(ra2a_opts_t, {f}));' for f in fields]
+    src += ["  return 0;", "}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(root, "include"), str(c), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(ra2a.Opts)
+    assert got[1:] == [getattr(ra2a.Opts, f).offset for f in fields]
+
+
+def test_dispatch_signal_slots():
+    """One slot per (signal tile, source) in every slice; no hand-back counters."""
+    o = ra2a.Opts(direction=ra2a.DIR_DISPATCH)
+    assert ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", o) == (
+        8 * 16 * 8, 0, ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS)

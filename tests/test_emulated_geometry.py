@@ -122,3 +122,47 @@ def test_emulated_head_merge(head_merge, W, S, H, D, dtype, tile, proto, mode):
                      protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD, ring=2,
                      consumer_split=2, head_merge=head_merge, mode=mode)
     check_emulation(W, S, H, D, dtype, opts, 2, seed=11)
+
+
+# ---- the dispatch (the combine's inverse map) ------------------------------------
+
+DISPATCH_CASES = [
+    # W, S, H, D, dtype, (tile_s, tile_h, tile_d)
+    (2, 8, 4, 16, "i32", (8, 4, 16)),
+    (3, 37, 2, 40, "bf16", (16, 1, 16)),
+    (4, 7, 3, 12, "bf16", (3, 2, 12)),
+    (5, 33, 1, 24, "u8", (8, 1, 7)),
+    (1, 50, 2, 64, "f32", (16, 2, 64)),
+    (6, 20, 2, 8, "f64", (32, 4, 64)),
+    (16, 9, 3, 32, "f32", (4, 1, 32)),
+    (8, 512, 16, 128, "bf16", (64, 1, 128)),
+    (8, 128, 1, 7168, "bf16", (32, 1, 7168)),
+]
+
+
+@pytest.mark.parametrize("W,S,H,D,dtype,tile", DISPATCH_CASES)
+@pytest.mark.parametrize("head_merge", [0, 1, 3])
+def test_emulated_dispatch_matches_oracle(W, S, H, D, dtype, tile, head_merge):
+    """The kernel's dispatch geometry moves exactly the oracle's bytes, and every
+    (tile, source) signal ends at 1."""
+    opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2], head_merge=head_merge,
+                     direction=ra2a.DIR_DISPATCH)
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=S + 3 * W, tile=tile)
+    ins = [x.reshape(S, H * W, D) for x in synthgen.make_inputs(wl)]  # in_j: (S, H*W, D)
+    outs, sigs = ra2a.debug_emulate_pipelined(ins, W, S, H, D, dtype, opts)
+    want = oracle.dispatch(ins)
+    exp = expected_signal_array(W, S, H, D, opts, 1, dtype)
+    assert (exp == 1).all() and len(exp) == W * -(-S // tile[0]) * -(-H // tile[1]) * -(-D // tile[2])
+    for r in range(W):
+        assert outs[r].tobytes() == want[r].tobytes(), f"rank {r}"
+        np.testing.assert_array_equal(sigs[r][:len(exp)].astype(np.int64), exp)
+        assert not sigs[r][len(exp):].any()
+
+
+def test_dispatch_rejects_staged_mode():
+    opts = ra2a.Opts(direction=ra2a.DIR_DISPATCH, mode=ra2a.MODE_STAGED)
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", opts)
+    assert e.value.code == ra2a.EINVAL
+    with pytest.raises(ra2a.Ra2aError):
+        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", ra2a.Opts(direction=2))
