@@ -20,7 +20,8 @@ element read once and every output element written once, per step), the
 roofline of the persistent kernel (its duration from HIP events around every
 launch, on the launch stream, in a separate pass over the same steps: events
 between kernels slow the steps themselves), and for context the staged mode, the two-phase variant, a
-plain copy of the same bytes with the library's put kernel, the forward
+plain copy of the same bytes with the library's put kernel, the bulk mode
+(two-phase layout with per-(S-block, sender) signals), the forward
 All2All (dispatch, the combine's inverse map) on the same buffers, and the CPU
 oracle's rate on the host.
 
@@ -197,12 +198,15 @@ def main():
     opts_lib = ra2a.Opts(**tiles)  # the library's own reset (in-launch in direct mode)
     opts = ra2a.Opts(skip_reset=1, **tiles)
     opts_st = ra2a.Opts(skip_reset=1, mode=ra2a.MODE_STAGED, **tiles)
+    # two-phase layout with per-(S-block, sender) signals (forces the SET layout)
+    opts_bk = ra2a.Opts(skip_reset=1, mode=ra2a.MODE_BULK,
+                        **{k: v for k, v in tiles.items() if k != "protocol"})
     dopts = ra2a.Opts(direction=ra2a.DIR_DISPATCH, **tiles)  # forward All2All, same buffers
     nsig = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
-               for o in (opts, opts_st, dopts))  # each set's signal array holds any of them
+               for o in (opts, opts_st, opts_bk, dopts))  # each set's signal array holds any
     nsig_c = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
-                 for o in (opts, opts_st))  # what the combine's separate reset launch clears
-    ring = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, opts_st)
+                 for o in (opts, opts_st, opts_bk))  # what a separate reset launch clears
+    ring = sum(ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, o) for o in (opts_st, opts_bk))
     full = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, None, True)
     nb = wl.bytes_per_rank
     slice_bytes = NSETS * (2 * nb + nsig * 128 + 4096) + ring + full + (4 << 20)
@@ -279,14 +283,14 @@ def main():
 
     n_tile = ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, opts)[0]
 
-    def parity(k):
+    def parity(k, check_signals=True):
         """Output of step k equals the oracle's, and (ADD) every tile signal reads W."""
         import oracle
         want = oracle.combine(ins)
         _, oo, osg = sets[k % NSETS]
         ok = all(heap.view(oo, (S, H * W, D), bits, j).cpu().numpy().tobytes() == want[j].tobytes()
                  for j in range(W))
-        if wl.protocol != synthgen.PROTOCOL_SET:
+        if check_signals and wl.protocol != synthgen.PROTOCOL_SET:
             ok = ok and all(bool((heap.view(osg, (n_tile, ra2a.SIG_STRIDE_U64), torch.int64, j)[:, 0]
                                   == W).all()) for j in range(W))
         return ok
@@ -336,6 +340,11 @@ def main():
         st_ok = parity(args.steps - 1)
         rec["staged"] = {"ms_per_step": round(st_ms, 5),
                          "value": round(alg / (st_ms * 1e-3) / 1e9, 2), "parity": st_ok}
+        bk_ms, _ = timed(opts_bk, args.steps, args.warmup, overlap=False)  # reset launch + combine
+        rec["bulk"] = {"ms_per_step": round(bk_ms, 5),
+                       "value": round(alg / (bk_ms * 1e-3) / 1e9, 2),
+                       "parity": parity(args.steps - 1, check_signals=False),
+                       "note": "two-phase layout with per-(S-block, sender) signals"}
 
         # forward All2All (dispatch, the combine's inverse) on the same buffers
         # (in_j read as (S, H*W, D), out_r written as (S*W, H, D)), in-launch reset

@@ -199,6 +199,7 @@ int ra2a_signal_reset(const ra2a_heap_t *heap, uint64_t *sig_sym, int64_t n_slot
 /* Where producers put their pieces (ra2a_opts_t.mode). */
 #define RA2A_MODE_DIRECT 1 /* push straight into out_j (default) */
 #define RA2A_MODE_STAGED 2 /* through a staging ring in slice j, reordered by consumers */
+#define RA2A_MODE_BULK 3   /* two-phase layout with fine-grained signals (see below) */
 
 /* Work-queue words the pipelined combine keeps after the hand-back counters
  * (used in slice 0 only, staged mode only; direct mode leaves them 0): per
@@ -247,7 +248,18 @@ typedef struct ra2a_opts {
                                * hand-back, no work queue (a static schedule).
                                * RA2A_MODE_STAGED: producers store into slice j's staging
                                * ring (the pages' window layout), consumers wait, copy
-                               * ring -> out_j and hand the ring slot back. */
+                               * ring -> out_j and hand the ring slot back.
+                               * RA2A_MODE_BULK ("UDMA Optimized Implementation", section
+                               * "Wait/Notify Optimization"): the two-phase exchange with
+                               * per-(S-block, sender) signals instead of a barrier.  Source
+                               * r copies its segment in_r[j*S + b*tile_s ..] straight
+                               * into slice j's staging [W][S][H][D] at [r][b*tile_s ..]
+                               * (the input's own layout) and sets slot (b, r) of region A
+                               * (slot b*W + r with whole-row tiles; the SET layout is
+                               * forced); a consumer waits only for its sender's slot, then
+                               * reorders that block into out_j.  No ring, no hand-back
+                               * (region B is empty).  Staging of 4 GiB or more per slice
+                               * needs agent_sync (EINVAL otherwise). */
     int32_t consumer_split;   /* staged mode: consumer work items sharing one unit, each
                                * copying a contiguous part (default: one per 128 KiB;
                                * at most 4096) */

@@ -144,6 +144,7 @@ struct Plan {
     int agent_sync;
     int direct;             // 1: direct push (no staging), 0: staged through the ring
     int inverse;            // 1: the dispatch (the combine's inverse map)
+    int bulk;               // 1: two-phase staging layout with fine-grained signals
     int64_t piece_bytes, unit_bytes, tile_bytes;
 };
 
@@ -155,12 +156,13 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (o->reserved[0]) return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
     if (o->direction != RA2A_DIR_COMBINE && o->direction != RA2A_DIR_DISPATCH)
         return fail(RA2A_EINVAL, "direction must be RA2A_DIR_COMBINE or RA2A_DIR_DISPATCH");
-    if (o->direction == RA2A_DIR_DISPATCH && o->mode == RA2A_MODE_STAGED)
+    if (o->direction == RA2A_DIR_DISPATCH && (o->mode == RA2A_MODE_STAGED || o->mode == RA2A_MODE_BULK))
         return fail(RA2A_EINVAL, "the dispatch runs in direct mode only");
     if (o->separate_reset != 0 && o->separate_reset != 1)
         return fail(RA2A_EINVAL, "separate_reset must be 0 or 1");
-    if (o->mode != 0 && o->mode != RA2A_MODE_DIRECT && o->mode != RA2A_MODE_STAGED)
-        return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_DIRECT or RA2A_MODE_STAGED");
+    if (o->mode != 0 && o->mode != RA2A_MODE_DIRECT && o->mode != RA2A_MODE_STAGED &&
+        o->mode != RA2A_MODE_BULK)
+        return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_DIRECT, _STAGED or _BULK");
     p->BS = o->tile_s > 0 ? o->tile_s : std::min<int64_t>(S, 64);
     p->TH = o->tile_h > 0 ? o->tile_h : 1;
     p->TD = o->tile_d > 0 ? o->tile_d : D;
@@ -172,9 +174,12 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (o->protocol != 0 && o->protocol != RA2A_PROTO_ADD && o->protocol != RA2A_PROTO_SET)
         return fail(RA2A_EINVAL, "protocol must be 0, RA2A_PROTO_ADD or RA2A_PROTO_SET");
     p->inverse = o->direction == RA2A_DIR_DISPATCH ? 1 : 0;
-    // the dispatch fills each output tile from one source: one signal per
-    // (tile, source), set to 1 (the SET layout)
-    p->protocol = (o->protocol == RA2A_PROTO_SET || p->inverse) ? RA2A_SIG_SET : RA2A_SIG_ADD;
+    p->bulk = o->mode == RA2A_MODE_BULK ? 1 : 0;
+    // the dispatch fills each output tile from one source, and the bulk mode
+    // signals each (S-block, sender): one signal per (tile, source), set to 1
+    // (the SET layout)
+    p->protocol = (o->protocol == RA2A_PROTO_SET || p->inverse || p->bulk) ? RA2A_SIG_SET
+                                                                          : RA2A_SIG_ADD;
     p->nbs = (int)cdiv(S, p->BS);
     p->nhb = (int)cdiv(H, p->TH);
     p->ndb = (int)cdiv(D, p->TD);
@@ -206,7 +211,7 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (o->stream_batch < 0) return fail(RA2A_EINVAL, "stream_batch must be >= 0");
     p->stream_batch = o->stream_batch;
     p->agent_sync = o->agent_sync ? 1 : 0;
-    p->direct = o->mode == RA2A_MODE_STAGED ? 0 : 1;
+    p->direct = (o->mode == RA2A_MODE_STAGED || o->mode == RA2A_MODE_BULK) ? 0 : 1;
     p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);
     if (o->consumer_split < 0 || o->wg_per_cu < 0 || o->lookahead < -1)
         return fail(RA2A_EINVAL, "negative option");
@@ -222,6 +227,12 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
         p->ring_bytes = 0;
         p->csplit = 1;
     }
+    if (p->bulk) {
+        // every sender's whole segment has a place: no ring reuse, no hand-back
+        p->R = std::max(p->nbs, 1);
+        p->regionB = 0;
+        p->ring_bytes = (int64_t)W * S * H * D * e;
+    }
     p->wg_per_cu = o->wg_per_cu > 0 ? o->wg_per_cu : 2;
     p->lookahead = o->lookahead;
     // the kernels index tiles, pieces and work items with 32-bit arithmetic
@@ -230,7 +241,9 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     // per-launch index arithmetic uses 32-bit vector counts inside one unit
     if (p->unit_bytes >= (int64_t(1) << 31) - 65536) return fail(RA2A_EINVAL, "tile too large");
     // consumers address the staging ring with 32-bit buffer offsets
-    if (p->ring_bytes >= (int64_t(1) << 32)) return fail(RA2A_EINVAL, "staging ring above 4 GiB");
+    if (p->ring_bytes >= (int64_t(1) << 32) && !(p->bulk && p->agent_sync))
+        return fail(RA2A_EINVAL, "staging above 4 GiB per slice (the bulk mode allows it with "
+                                 "agent_sync)");
     return RA2A_OK;
 }
 
@@ -384,6 +397,7 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     a->ring_bytes = pl.ring_bytes;
     a->direct = pl.direct;
     a->inverse = pl.inverse;
+    a->bulk = pl.bulk;
     a->straggler = opts ? opts->straggler_rank : -1;
     a->delay = opts ? opts->straggler_delay : 0;
     a->seed = opts ? opts->straggler_seed : 0;
@@ -1277,9 +1291,12 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
                     std::memcpy(&heap[(size_t)(q.dst + dofs)], &heap[(size_t)(q.src + so)],
                                 (size_t)V);
                 }
-                if (!inside(q.credit, 8, q.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
-                    return fail(RA2A_EINVAL, "item credit slot outside region B");
-                *u64(q.credit) += 1;
+                if (!pl.bulk) {  // the bulk mode has no ring and no hand-back
+                    if (!inside(q.credit, 8, q.j, sig_off + sigA_len,
+                                pl.regionB * RA2A_SIG_STRIDE_BYTES))
+                        return fail(RA2A_EINVAL, "item credit slot outside region B");
+                    *u64(q.credit) += 1;
+                }
             }
         }
         for (uint8_t x : cov_p)

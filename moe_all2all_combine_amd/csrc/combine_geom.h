@@ -239,6 +239,14 @@ RA2A_HD Piece piece_at(const PipeArgs& a, int sid, int b, int r) {
                 (((int64_t)p.r * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e;
         pl.sa = HWDe;
         pl.da = a.H * a.D * e;
+    } else if (a.bulk) {
+        // bulk staging of destination j: sender r's segment in the input's own
+        // layout, [r][s][h][d], so both sides have rows of H*D elements
+        p.src = (int64_t)p.r * a.stride + a.in_off + (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e +
+                st.d0 * e;
+        p.dst = (int64_t)st.j * a.stride + a.stg_off +
+                (((int64_t)p.r * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e;
+        pl.sa = pl.da = a.H * a.D * e;
     } else {
         p.src = (int64_t)p.r * a.stride + a.in_off + (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e +
                 st.d0 * e;
@@ -339,12 +347,17 @@ RA2A_HD Item item_of(const PipeArgs& a, int g, int64_t it, int V) {
     const int64_t s0 = (int64_t)q.b * a.BS;
     const int bs = (int)geom_min(a.BS, a.S - s0);
     const int64_t col = ((int64_t)q.r0 * a.H + st.h0) * a.D * e + st.d0 * e;
-    q.src = (int64_t)st.j * a.stride + a.stg_off + (int64_t)q.slot * a.BS * HWDe + col;
+    // the ring holds rows of the output's layout; the bulk staging (one source
+    // per unit, the SET layout) holds sender r0's rows of H*D elements
+    q.src = a.bulk ? (int64_t)st.j * a.stride + a.stg_off +
+                         (((int64_t)q.r0 * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e
+                   : (int64_t)st.j * a.stride + a.stg_off + (int64_t)q.slot * a.BS * HWDe + col;
     q.dst = (int64_t)st.j * a.stride + a.out_off + s0 * HWDe + col;
     RowPlan& pl = q.pl;
     const int64_t head = a.D * e;
     pl.A = bs;
-    pl.sa = pl.da = HWDe;
+    pl.sa = a.bulk ? a.H * head : HWDe;
+    pl.da = HWDe;
     if (st.td == a.D && st.th == a.H) {  // whole rows of the sources: one run
         pl.B = 1;
         pl.C = 1;

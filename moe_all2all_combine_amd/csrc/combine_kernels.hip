@@ -290,7 +290,8 @@ __device__ __forceinline__ bool run_item(const PipeArgs& a, int g, int64_t it, i
         }
     }
     group_release<SYNC>();
-    if (threadIdx.x == 0) sig_update(reinterpret_cast<uint64_t*>(base + q.credit), 1ull, kSigAdd);
+    if (threadIdx.x == 0 && !a.bulk)  // the bulk mode has no ring to hand back
+        sig_update(reinterpret_cast<uint64_t*>(base + q.credit), 1ull, kSigAdd);
     if (a.stamps && threadIdx.x < 64) {
         const uint64_t now = rtc_now();
         for (int k = threadIdx.x; k < q.nsig; k += 64)

@@ -16,18 +16,19 @@ def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):
     nbs = math.ceil(S / opts.tile_s)
     nhb = math.ceil(H / opts.tile_h)
     ndb = math.ceil(D / opts.tile_d)
-    direct = opts.mode != ra2a.MODE_STAGED
-    R = nbs if direct else min(opts.ring or 8, nbs)
+    direct = opts.mode not in (ra2a.MODE_STAGED, ra2a.MODE_BULK)
+    bulk = opts.mode == ra2a.MODE_BULK  # staged, but no ring: data signals only
+    R = nbs if (direct or bulk) else min(opts.ring or 8, nbs)
     if direct:
         csplit = 1
     # the dispatch fills each tile from one source: one slot per (tile, source), SET 1
     dispatch = getattr(opts, "direction", 0) == ra2a.DIR_DISPATCH
-    proto = SET if (opts.protocol == ra2a.PROTO_SET or dispatch) else ADD
+    proto = SET if (opts.protocol == ra2a.PROTO_SET or dispatch or bulk) else ADD
     per = W if proto == SET else 1
     # merged head blocks: derived from the size of the hand-back region
     _, n_credit, _ = ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)
-    if direct:
-        # no ring and no consumer work: the data signals only
+    if direct or bulk:
+        # no ring (direct: no consumer work either): the data signals only
         assert n_credit == 0
         tiles = ProtocolSpec(W=W, nbs=nbs, nstreams=nhb * ndb, R=R, protocol=proto)
         ns = nhb * ndb

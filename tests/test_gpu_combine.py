@@ -34,7 +34,7 @@ def check_queue_words(q, opts):
     moved; every group is marked fully claimed.  Direct mode: untouched."""
     q = q.astype(np.uint64)
     assert len(q) == ra2a.QUEUE_SLOTS == 18
-    if opts.mode != ra2a.MODE_STAGED:
+    if opts.mode not in (ra2a.MODE_STAGED, ra2a.MODE_BULK):
         # the direct mode runs a static schedule: no queue words are touched
         assert not q.any(), q
         return
@@ -42,7 +42,7 @@ def check_queue_words(q, opts):
     for g, (head, taker) in enumerate(q[:16].reshape(8, 2)):
         head, taker = int(head), int(taker)
         if head & TAKEN:
-            assert not opts.agent_sync and opts.mode == ra2a.MODE_STAGED, \
+            assert not opts.agent_sync and opts.mode in (ra2a.MODE_STAGED, ra2a.MODE_BULK), \
                 f"group {g} taken over, but only the staged XCD-local mode binds groups to XCDs"
             assert 1 <= (head >> 32) & 0xFF <= 8 and taker >= 1, (g, hex(head), taker)
         else:
@@ -116,6 +116,16 @@ def test_small_staged_agent_sync(W, S, H, D, dtype, tile, proto, ring):
     opts = opts_for(wl, ring=ring, consumer_split=2, lookahead=2, agent_sync=1,
                     mode=ra2a.MODE_STAGED)
     run_and_check(wl, opts)
+
+
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
+@pytest.mark.parametrize("knobs", [dict(consumer_split=1), dict(consumer_split=2, lookahead=2),
+                                   dict(consumer_split=1, agent_sync=1)])
+def test_small_bulk(W, S, H, D, dtype, tile, proto, ring, knobs):
+    """Two-phase layout with per-(S-block, sender) signals."""
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S + 5, tile=tile, protocol=proto)
+    opts = opts_for(wl, mode=ra2a.MODE_BULK, **knobs)
+    run_and_check(wl, opts, csplit=knobs["consumer_split"])
 
 
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
@@ -226,7 +236,7 @@ def test_direct_reset_clears_dirty_signals(reset):
         case.close()
 
 
-@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
+@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED, ra2a.MODE_BULK])
 def test_straggler_timestamps(mode):
     """Per-tile completion clocks under a delayed source: every tile is stamped
     (garbage left in the stamp array is cleared by the combine), and under SET
@@ -300,27 +310,27 @@ def full_case(name, variant, **kw):
         say(f"[full] oracle {name}")
         _FULL_CACHE[name] = (ins, oracle.combine(ins))
     ins, want = _FULL_CACHE[name]
-    if variant == "staged":
-        kw["mode"] = ra2a.MODE_STAGED
+    if variant in ("staged", "bulk"):
+        kw["mode"] = ra2a.MODE_STAGED if variant == "staged" else ra2a.MODE_BULK
         variant = "pipelined"
     else:
         kw.pop("consumer_split", None)
     opts = opts_for(wl, consumer_split=kw.pop("consumer_split", 1), **kw)
     run_and_check(wl, opts, variant=variant, inputs=ins, want=want,
-                  csplit=None if opts.mode == ra2a.MODE_STAGED else 1)
+                  csplit=None if opts.mode in (ra2a.MODE_STAGED, ra2a.MODE_BULK) else 1)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "staged", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "two_phase"])
 def test_full_ep_combine_w8_bf16(variant):
     full_case("ep_combine_w8_s512_h16_d128_bf16", variant)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "staged", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "two_phase"])
 def test_full_moe_combine_w8_d7168(variant):
     full_case("moe_combine_w8_s4096_h1_d7168_bf16", variant, consumer_split=4)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "staged", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "two_phase"])
 def test_full_straggler_w16_f32(variant):
     wl = synthgen.WORKLOADS["straggler_w16_s2048_h32_d128_f32"]
     full_case("straggler_w16_s2048_h32_d128_f32", variant,
