@@ -1,4 +1,5 @@
-"""fp64 oracle of the AllGather+GEMM workload -- TEST INFRASTRUCTURE ONLY.
+"""fp64 oracles of the AllGather+GEMM and GEMM+ReduceScatter workloads -- TEST
+INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg use
 this module; the GPU path never imports it.
@@ -11,6 +12,13 @@ rows [w*m_local, (w+1)*m_local); the consumer computes C = G @ B.
 Reading taken: the RFC's formula line also names a ReduceScatter, but its
 example returns an (m_total, n) product, which only C = G @ B has; the oracle
 computes C = G @ B with no reduction across ranks.
+
+GEMM + ReduceScatter (the RFC, section 十, "fused_matmul_reduce_scatter"; and
+"Triton-distributed Semantics", section "GEMM + ReduceScatter Overlapping"):
+output = ReduceScatter(x1 @ x2).  Rank r holds x1_r (m x K) and x2_r (K x N);
+its product is an (m x N) partial; the ReduceScatter sums the W partials and
+gives rank j rows [j*m/W, (j+1)*m/W) of the sum (reading: an even row split, m
+divisible by W).
 
 bf16 inputs convert exactly to float64 (every bf16 value is a float64 value),
 so ``ref`` is the exact product up to float64 summation rounding.
@@ -74,6 +82,37 @@ def ag_gemm_rows_ref(shards_bits: List[np.ndarray], b_bits: np.ndarray,
     a = np.stack([bf16_bits_to_f64(shards_bits[int(r) // m_local][int(r) % m_local])
                   for r in rows])
     return a @ bf16_bits_to_f64(b_bits)
+
+
+def gemm_rs_ref(a_bits: List[np.ndarray], bt_bits: List[np.ndarray]) -> List[np.ndarray]:
+    """out_j = (sum_r x1_r @ x2_r)[j*m/W : (j+1)*m/W] in float64.
+
+    a_bits[r]: x1_r as bf16 bits (m x K); bt_bits[r]: x2_r transposed, bf16 bits
+    (N x K), so x2_r = bt_bits[r].T.
+    """
+    W = len(a_bits)
+    m = a_bits[0].shape[0]
+    if m % W:
+        raise ValueError("m must be divisible by W")
+    mj = m // W
+    total = None
+    for a, bt in zip(a_bits, bt_bits):
+        part = bf16_bits_to_f64(a) @ bf16_bits_to_f64(bt).T
+        total = part if total is None else total + part
+    return [total[j * mj:(j + 1) * mj] for j in range(W)]
+
+
+def gemm_rs_rows_ref(a_bits: List[np.ndarray], bt_bits: List[np.ndarray], j: int,
+                     rows: np.ndarray) -> np.ndarray:
+    """Selected rows of out_j (for sampled checks at full size)."""
+    W = len(a_bits)
+    mj = a_bits[0].shape[0] // W
+    idx = j * mj + np.asarray(rows, dtype=np.int64)
+    total = None
+    for a, bt in zip(a_bits, bt_bits):
+        part = bf16_bits_to_f64(a[idx]) @ bf16_bits_to_f64(bt).T
+        total = part if total is None else total + part
+    return total
 
 
 def rel_error(c: np.ndarray, ref: np.ndarray) -> float:

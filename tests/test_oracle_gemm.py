@@ -94,3 +94,95 @@ def test_rel_error_definition():
 def test_allgather_rows_is_oracle_allgather():
     shards = [np.arange(12, dtype=np.uint16).reshape(3, 4) + 100 * w for w in range(4)]
     np.testing.assert_array_equal(gemm.allgather_rows(shards), oracle.allgather(shards))
+
+
+# ---- GEMM + ReduceScatter --------------------------------------------------------
+
+def _bf16_ints(rng, shape, lo=-2, hi=3):
+    """Small integers as bf16 bit patterns (exact in bf16)."""
+    v = rng.integers(lo, hi, size=shape).astype(np.float64)
+    return gemm.f64_to_bf16_rne_bits(v)
+
+
+def test_gemm_rs_matches_bruteforce_loops():
+    """out_j[i, n] = sum_r sum_k x1_r[j*m/W + i, k] * x2_r[k, n], written out as loops."""
+    rng = np.random.default_rng(3)
+    W, m, K, N = 3, 6, 4, 5
+    a = [_bf16_ints(rng, (m, K)) for _ in range(W)]
+    bt = [_bf16_ints(rng, (N, K)) for _ in range(W)]
+    got = gemm.gemm_rs_ref(a, bt)
+    mj = m // W
+    for j in range(W):
+        for i in range(mj):
+            for n in range(N):
+                want = 0.0
+                for r in range(W):
+                    for k in range(K):
+                        want += (gemm.bf16_bits_to_f64(a[r][j * mj + i, k]) *
+                                 gemm.bf16_bits_to_f64(bt[r][n, k]))
+                assert got[j][i, n] == want
+
+
+def test_gemm_rs_w1_is_plain_matmul():
+    rng = np.random.default_rng(4)
+    a = _bf16_ints(rng, (7, 9))
+    bt = _bf16_ints(rng, (5, 9))
+    got = gemm.gemm_rs_ref([a], [bt])[0]
+    want = gemm.bf16_bits_to_f64(a) @ gemm.bf16_bits_to_f64(bt).T
+    np.testing.assert_array_equal(got, want)
+
+
+def test_gemm_rs_scatter_and_reduce_are_independent_of_each_other():
+    """Concatenating the scattered blocks gives the sum of the per-rank products;
+    scaling one rank's x2 scales only that rank's contribution."""
+    rng = np.random.default_rng(5)
+    W, m, K, N = 4, 8, 6, 3
+    a = [_bf16_ints(rng, (m, K)) for _ in range(W)]
+    bt = [_bf16_ints(rng, (N, K)) for _ in range(W)]
+    full = np.concatenate(gemm.gemm_rs_ref(a, bt), axis=0)
+    parts = [gemm.bf16_bits_to_f64(x) @ gemm.bf16_bits_to_f64(y).T for x, y in zip(a, bt)]
+    np.testing.assert_array_equal(full, sum(parts))
+    bt2 = list(bt)
+    bt2[1] = gemm.f64_to_bf16_rne_bits(2.0 * gemm.bf16_bits_to_f64(bt[1]))
+    full2 = np.concatenate(gemm.gemm_rs_ref(a, bt2), axis=0)
+    np.testing.assert_array_equal(full2 - full, parts[1])
+
+
+def test_gemm_rs_rows_ref_matches_full():
+    rng = np.random.default_rng(6)
+    W, m, K, N = 4, 12, 5, 7
+    a = [_bf16_ints(rng, (m, K)) for _ in range(W)]
+    bt = [_bf16_ints(rng, (N, K)) for _ in range(W)]
+    full = gemm.gemm_rs_ref(a, bt)
+    for j in range(W):
+        rows = np.array([0, 2, m // W - 1])
+        np.testing.assert_array_equal(gemm.gemm_rs_rows_ref(a, bt, j, rows), full[j][rows])
+
+
+def test_gemm_rs_rejects_uneven_rows():
+    import pytest
+    rng = np.random.default_rng(7)
+    with pytest.raises(ValueError):
+        gemm.gemm_rs_ref([_bf16_ints(rng, (5, 2))] * 2, [_bf16_ints(rng, (3, 2))] * 2)
+
+
+def test_gemm_rs_planted_mistakes_are_caught():
+    """Plausible slips in a ReduceScatter (wrong row block, missing rank, rows of the
+    destination's own input, transposed operand) all disagree with the loop pin."""
+    rng = np.random.default_rng(8)
+    W, m, K, N = 3, 6, 4, 5
+    a = [_bf16_ints(rng, (m, K)) for _ in range(W)]
+    bt = [_bf16_ints(rng, (N, K)) for _ in range(W)]
+    ok = gemm.gemm_rs_ref(a, bt)
+    f = gemm.bf16_bits_to_f64
+    mj = m // W
+    mutants = {
+        "row block of the next rank": [sum(f(x) @ f(y).T for x, y in zip(a, bt))[((j + 1) % W) * mj:((j + 1) % W + 1) * mj] for j in range(W)],
+        "a rank left out": [sum(f(x) @ f(y).T for x, y in list(zip(a, bt))[1:])[j * mj:(j + 1) * mj] for j in range(W)],
+        "only the destination's own partial": [(f(a[j]) @ f(bt[j]).T)[j * mj:(j + 1) * mj] for j in range(W)],
+        "x2 not transposed": [sum(f(x)[:, :N] @ f(y)[:, :N] for x, y in zip(a, bt))[j * mj:(j + 1) * mj] if K >= N else None for j in range(W)],
+    }
+    for name, outs in mutants.items():
+        differs = any(o is None or o.shape != ok[j].shape or not np.array_equal(o, ok[j])
+                      for j, o in enumerate(outs))
+        assert differs, f"mutant '{name}' agrees with the oracle"
