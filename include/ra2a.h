@@ -403,6 +403,53 @@ int ra2a_ag_gemm(const void *a_shards, void *gathered, const void *b, void *c, u
 int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t N, int tile_rows,
                             int num_xcd, int64_t *tasks_per_group);
 
+/* ---- GEMM + ReduceScatter -------------------------------------------------- */
+/* (HyperParallel RFC, section 十 fused_matmul_reduce_scatter; "Triton-distributed
+ * Semantics", section "GEMM + ReduceScatter Overlapping".)  output =
+ * ReduceScatter(x1 @ x2): rank r holds x1_r (m x K) and x2_r (K x N); rank j
+ * receives out_j = rows [j*m/W, (j+1)*m/W) of sum_r x1_r @ x2_r (m must be
+ * divisible by W).  One persistent launch: producer tasks compute 256 x 256
+ * tiles of rank r's partial product for destination j, store them in fp32 into
+ * j's receive area at slot r and SET the (tile, r) signal in j's slice; the
+ * receiver's reduce task waits for the W partials of its tile, adds them in
+ * rank order 0..W-1 in fp32 and stores bf16 (round to nearest even).  Producers
+ * for destination j visit the sources in the RFC's rotation ((j - t) mod W at
+ * step t, so rank r works for rank (r + t) mod W).  bf16 operands, fp32
+ * accumulation.  Every wait is bounded (ra2a_check reports RA2A_ETIMEOUT).    */
+#define RA2A_RS_AGENT_SYNC 1 /* device-wide release/acquire instead of the XCD-local protocol */
+#define RA2A_RS_SKIP_RESET 2 /* the caller zeroed the signals; no reset launch */
+
+/* Sizes for (W, m, K, N): `tile_slots` = (output tiles of out_j) * W signal slots
+ * per slice, then `queue_slots` (RA2A_QUEUE_SLOTS) queue words (slice 0); the
+ * `signals` array must hold their sum per slice.  `partial_bytes` = bytes of the
+ * receive area per slice: [W][m/W][N] fp32.  Any output pointer may be NULL.
+ * Errors: EINVAL.                                                              */
+int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int64_t *tile_slots,
+                       int64_t *queue_slots, size_t *partial_bytes);
+
+/* All five buffers are symmetric, inside one heap of W slices, at these
+ * offsets in every slice (row-major, bf16 unless stated):
+ *   x1      slice r: x1_r, m x K (16-byte aligned);
+ *   x2t     slice r: x2_r transposed, N x K (16-byte aligned);
+ *   partial slice j: the receive area, [W][m/W][N] fp32 (16-byte aligned);
+ *   out     slice j: out_j, m/W x N (8-byte aligned);
+ *   signals slice j: ra2a_gemm_rs_sizes' slots at 128-byte spacing (8-byte aligned).
+ * K must be a multiple of 8.  The signals are zeroed by a reset launch first
+ * unless RA2A_RS_SKIP_RESET.  After the call every tile slot holds 1.  The
+ * library owns the buffers until the stream reaches the end of the launch.
+ * Errors: EINVAL (shapes, flags, alignment, overlap, a buffer outside the heap
+ * or crossing the end of a slice, a receive area of 4 GiB or more), EHIP.      */
+int ra2a_gemm_rs(const void *x1, const void *x2t, void *partial, void *out, uint64_t *signals,
+                 int W, int64_t m, int64_t K, int64_t N, int flags, void *stream);
+
+/* Host check of the GEMM+ReduceScatter work queues for a device of num_xcd
+ * XCDs: every (destination, tile, source) GEMM task and every reduce task once,
+ * each reduce task after the W GEMM tasks it waits for.  tasks_per_group
+ * (optional) receives the queue length.  Returns EINVAL with a message on a
+ * violation.                                                                   */
+int ra2a_debug_gemm_rs_plan(int W, int64_t m, int64_t K, int64_t N, int num_xcd,
+                            int64_t *tasks_per_group);
+
 /* ---- diagnostics --------------------------------------------------------- */
 
 /* Wait for the device, then report and clear the heap's device error word:

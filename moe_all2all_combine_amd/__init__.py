@@ -18,7 +18,7 @@ from typing import Optional, Sequence, Tuple
 __all__ = [
     "Ra2aError", "Opts", "SymmHeap", "lib", "OK", "EINVAL", "ENOMEM", "EHIP", "ETIMEOUT",
     "EUNSUPPORTED", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "MODE_DIRECT", "MODE_STAGED",
-    "QUEUE_SLOTS", "MODE_BULK", "DIR_COMBINE", "DIR_DISPATCH", "all2all_dispatch", "all2all_dispatch_ex", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
+    "QUEUE_SLOTS", "RS_AGENT_SYNC", "RS_SKIP_RESET", "gemm_rs_sizes", "gemm_rs", "debug_gemm_rs_plan", "MODE_BULK", "DIR_COMBINE", "DIR_DISPATCH", "all2all_dispatch", "all2all_dispatch_ex", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
     "CMP_LE", "SIG_STRIDE_BYTES", "DTYPES", "symm_heap_create", "symm_heap_attach",
     "symm_heap_destroy", "symm_malloc", "symm_heap_info", "symm_at", "put", "get",
     "put_with_signal", "signal_op", "wait_signal", "signal_reset", "rev_all2all",
@@ -123,6 +123,10 @@ def lib():
                                             ctypes.POINTER(i64)]),
         "ra2a_ag_gemm": (i32, [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp]),
         "ra2a_debug_ag_gemm_plan": (i32, [i32, i32, i64, i64, i64, i32, i32, ctypes.POINTER(i64)]),
+        "ra2a_gemm_rs_sizes": (i32, [i32, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                     ctypes.POINTER(sz)]),
+        "ra2a_gemm_rs": (i32, [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp]),
+        "ra2a_debug_gemm_rs_plan": (i32, [i32, i64, i64, i64, i32, ctypes.POINTER(i64)]),
         "ra2a_debug_emulate_pipelined": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp),
                                                ctypes.POINTER(vp), i32, i64, i64, i64, i32, vp,
                                                i32, i32]),
@@ -391,3 +395,28 @@ class SymmHeap:
             self.close()
         except Exception:
             pass
+
+
+# ---- GEMM + ReduceScatter --------------------------------------------------------
+
+RS_AGENT_SYNC = 1
+RS_SKIP_RESET = 2
+
+
+def gemm_rs_sizes(W: int, m: int, K: int, N: int) -> Tuple[int, int, int]:
+    """(tile signal slots, queue words, receive-area bytes) per slice."""
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    _ok(lib().ra2a_gemm_rs_sizes(W, m, K, N, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def gemm_rs(x1: int, x2t: int, partial: int, out: int, signals: int, W: int, m: int, K: int,
+            N: int, flags: int = 0, stream=None) -> None:
+    """out_j = rows [j*m/W, (j+1)*m/W) of sum_r x1_r @ x2_r (x2 passed transposed)."""
+    _ok(lib().ra2a_gemm_rs(x1, x2t, partial, out, signals, W, m, K, N, flags, _stream(stream)))
+
+
+def debug_gemm_rs_plan(W: int, m: int, K: int, N: int, num_xcd: int = 8) -> int:
+    n = ctypes.c_int64()
+    _ok(lib().ra2a_debug_gemm_rs_plan(W, m, K, N, num_xcd, ctypes.byref(n)))
+    return n.value

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ag_gemm_geom.h"
+#include "gemm_rs_geom.h"
 #include "common.h"
 #include "device.h"
 #include "launch.h"
@@ -158,18 +159,19 @@ __device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Fra
             acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
 }
 
-// C[rows, cols] of one 256 x 256 output tile: rows of G from g_rows (rows_valid
-// of them), rows n0 .. of B^T (N x K), into c_rows.
-__device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g_rows,
-                                          int rows_valid, int64_t n0, uint16_t* c_rows,
-                                          uint16_t* lds) {
-    // K and N opaque per tile: nothing derived from them is hoisted out of the
+// One 256 x 256 output tile: C[i, n] = sum_k A[i, k] B^T[n, k] for the
+// rows_valid rows of A at a_rows and the cols_valid rows of B^T at bt_rows (both
+// K-contiguous bf16), stored at c (row stride ldc elements) as bf16 rounded to
+// nearest even, or (F32OUT) as the fp32 accumulators themselves.
+template <bool F32OUT>
+__device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid,
+                                          const uint16_t* bt_rows, int cols_valid, int64_t K,
+                                          void* c, int64_t ldc, uint16_t* lds) {
+    // K and ldc opaque per tile: nothing derived from them is hoisted out of the
     // persistent task loop and kept alive across tiles.
-    int64_t K = a.K, N = a.N;
-    asm volatile("" : "+s"(K), "+s"(N));
-    const int64_t cols_valid = N - n0 < kGemmBN ? N - n0 : kGemmBN;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc_uniform(g_rows, (uint32_t)((int64_t)rows_valid * K * 2));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc_uniform(a.bt + n0 * K, (uint32_t)(cols_valid * K * 2));
+    asm volatile("" : "+s"(K), "+s"(ldc));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc_uniform(a_rows, (uint32_t)((int64_t)rows_valid * K * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc_uniform(bt_rows, (uint32_t)((int64_t)cols_valid * K * 2));
     f32x16 acc[kBlkA][kBlkB];
 #pragma unroll
     for (int x = 0; x < kBlkA; ++x)
@@ -227,9 +229,8 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g
     // column lane % 32 of the block.  (The empty asm makes the output pointer opaque
     // here, so that the compiler does not hoist the epilogue's addresses above the
     // loop and keep them alive across it.)
-    uint64_t cbase = reinterpret_cast<uint64_t>(c_rows);
+    uint64_t cbase = reinterpret_cast<uint64_t>(c);
     asm volatile("" : "+v"(cbase));
-    c_rows = reinterpret_cast<uint16_t*>(cbase);
     const int lane = (int)threadIdx.x & 63;
 #pragma unroll
     for (int x = 0; x < kBlkA; ++x)
@@ -239,8 +240,13 @@ __device__ __forceinline__ void gemm_tile(const AgGemmArgs& a, const uint16_t* g
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (row < rows_valid && col < cols_valid)
-                    c_rows[(int64_t)row * N + n0 + col] = (uint16_t)bf16_rne(acc[x][y][e]);
+                if (row < rows_valid && col < cols_valid) {
+                    if (F32OUT)
+                        reinterpret_cast<float*>(cbase)[(int64_t)row * ldc + col] = acc[x][y][e];
+                    else
+                        reinterpret_cast<uint16_t*>(cbase)[(int64_t)row * ldc + col] =
+                            (uint16_t)bf16_rne(acc[x][y][e]);
+                }
             }
         }
     __builtin_amdgcn_s_barrier();  // the LDS ring is free for the next tile
@@ -336,7 +342,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) ag_gemm_kernel(AgGemmArgs a) 
                     const int64_t row0 = (int64_t)t.w * a.m_local + (int64_t)t.mb * kGemmBM;
                     int64_t rv = a.m_local - (int64_t)t.mb * kGemmBM;
                     const int rows_valid = rv < kGemmBM ? (int)rv : kGemmBM;
-                    gemm_tile(a, G + row0 * a.K, rows_valid, (int64_t)t.nb * kGemmBN, a.c + row0 * a.N, lds);
+                    const int64_t n0 = (int64_t)t.nb * kGemmBN;
+                    const int cols_valid = a.N - n0 < kGemmBN ? (int)(a.N - n0) : kGemmBN;
+                    gemm_tile<false>(G + row0 * a.K, rows_valid, a.bt + n0 * a.K, cols_valid, a.K,
+                                     a.c + row0 * a.N + n0, a.N, lds);
                 }
             }
             if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
@@ -345,6 +354,139 @@ __global__ void __launch_bounds__(kGemmThreads, 1) ag_gemm_kernel(AgGemmArgs a) 
             ++k;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM + ReduceScatter (gemm_rs_geom.h): one persistent launch over one work
+// queue per XCD.  Destination j's tasks form group j mod NG, bound to one XCD
+// like the AllGather's, so the partials a reduce task reads were written into
+// the L2 it reads through.
+
+// Reduce task: out_j tile = sum over r = 0..W-1 (in that order) of the fp32
+// partials partial_j[r] of the tile, rounded to bf16 (nearest even).  The
+// partials are read with device-scope loads (never from the CU's L1).
+__device__ __forceinline__ void rs_reduce_tile(const GemmRsArgs& a, int j, int tile) {
+    int mb, nb;
+    grs_tile(a, tile, &mb, &nb);
+    const int64_t row0 = (int64_t)mb * kRsTile, col0 = (int64_t)nb * kRsTile;
+    const int rows = a.mj - row0 < kRsTile ? (int)(a.mj - row0) : kRsTile;
+    const int cols = a.N - col0 < kRsTile ? (int)(a.N - col0) : kRsTile;
+    uint8_t* const slice = a.base + (int64_t)j * a.stride;
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc_uniform(slice + a.p_off, (uint32_t)((int64_t)a.W * a.mj * a.N * 4));
+    uint16_t* const out = reinterpret_cast<uint16_t*>(slice + a.out_off);
+    const uint32_t plane = (uint32_t)(a.mj * a.N * 4);  // bytes of one source's partial
+    if ((a.N & 3) == 0) {
+        // 4 columns per lane: 16-byte loads, 8-byte stores
+        const int vc = cols >> 2;
+        for (int i = threadIdx.x; i < rows * vc; i += kGemmThreads) {
+            const int r = i / vc;
+            const int c = (i - r * vc) << 2;
+            const uint32_t off = (uint32_t)(((row0 + r) * a.N + col0 + c) * 4);
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+            for (int src = 0; src < a.W; ++src) {
+                const u32x4 v = BufLoad<16, kPolicySc1>::go(rp, off + (uint32_t)src * plane);
+                s0 += __uint_as_float(v[0]);
+                s1 += __uint_as_float(v[1]);
+                s2 += __uint_as_float(v[2]);
+                s3 += __uint_as_float(v[3]);
+            }
+            u32x2 o;
+            o[0] = bf16_rne(s0) | (bf16_rne(s1) << 16);
+            o[1] = bf16_rne(s2) | (bf16_rne(s3) << 16);
+            *reinterpret_cast<u32x2*>(out + (row0 + r) * a.N + col0 + c) = o;
+        }
+    } else {
+        for (int i = threadIdx.x; i < rows * cols; i += kGemmThreads) {
+            const int r = i / cols;
+            const int c = i - r * cols;
+            const uint32_t off = (uint32_t)(((row0 + r) * a.N + col0 + c) * 4);
+            float sum = 0.f;
+            for (int src = 0; src < a.W; ++src)
+                sum += __uint_as_float(BufLoad<4, kPolicySc1>::go(rp, off + (uint32_t)src * plane));
+            out[(row0 + r) * a.N + col0 + c] = (uint16_t)bf16_rne(sum);
+        }
+    }
+}
+
+template <int SYNC>
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_rs_kernel(GemmRsArgs a) {
+    __shared__ uint16_t lds[kStages * 2 * kStageElems];
+    __shared__ int lds_flag;
+    __shared__ int64_t lds_pos[2];
+    constexpr bool kOwned = SYNC == kSyncXcd;
+    uint64_t* const qw = reinterpret_cast<uint64_t*>(a.base + a.sig_off) + grs_queue_slot(a) * kSigStrideU64;
+    const uint32_t xcc = xcc_id();
+    const int home = SYNC == kSyncXcd ? (int)(xcc % (uint32_t)a.NG) : (int)(blockIdx.x % a.NG);
+    const int64_t total = a.ntasks_dest * a.dpg;
+    QueueClaim qc;
+    int k = 0;
+    for (int gi = 0; gi < a.NG; ++gi) {
+        const int g = (home + gi) % a.NG;
+        if (threadIdx.x == 0) lds_pos[k & 1] = queue_first<kOwned>(qw, g, gi, xcc, qc);
+        __syncthreads();
+        int64_t pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
+        ++k;
+        if (pos < 0) continue;
+        while (true) {
+            // the group's queue: dpg destinations of ntasks_dest each (the last
+            // group may have fewer real destinations; their tasks are skipped)
+            if (pos >= total) {
+                if (threadIdx.x == 0) queue_drained(qw, g, pos, total, qc);
+                break;
+            }
+            uint64_t nxt = 0;
+            if (threadIdx.x == 0) nxt = queue_next(qc);
+            const RsTask t = grs_group_task(a, g, pos);
+            if (t.j < a.W) {
+                uint8_t* const dst_slice = a.base + (int64_t)t.j * a.stride;
+                uint64_t* const sig = reinterpret_cast<uint64_t*>(dst_slice + a.sig_off);
+                if (!t.reduce) {
+                    // rank r's partial of the tile: rows j*mj + mb*256 .. of x1_r,
+                    // rows nb*256 .. of x2_r^T, into slot r of j's receive area
+                    int mb, nb;
+                    grs_tile(a, t.tile, &mb, &nb);
+                    const int64_t row0 = (int64_t)mb * kRsTile, col0 = (int64_t)nb * kRsTile;
+                    const int rows = a.mj - row0 < kRsTile ? (int)(a.mj - row0) : kRsTile;
+                    const int cols = a.N - col0 < kRsTile ? (int)(a.N - col0) : kRsTile;
+                    const uint8_t* const src_slice = a.base + (int64_t)t.r * a.stride;
+                    const uint16_t* x1 = reinterpret_cast<const uint16_t*>(src_slice + a.a_off) +
+                                         ((int64_t)t.j * a.mj + row0) * a.K;
+                    const uint16_t* x2t = reinterpret_cast<const uint16_t*>(src_slice + a.bt_off) +
+                                          col0 * a.K;
+                    float* part = reinterpret_cast<float*>(dst_slice + a.p_off) +
+                                  ((int64_t)t.r * a.mj + row0) * a.N + col0;
+                    gemm_tile<true>(x1, rows, x2t, cols, a.K, part, a.N, lds);
+                    group_release<SYNC>();
+                    if (threadIdx.x == 0)
+                        sig_update(sig + grs_sig_slot(a, t.tile, t.r) * kSigStrideU64, 1ull, kSigSet);
+                } else {
+                    if (!group_wait_all<SYNC == kSyncAgent>(sig + grs_sig_slot(a, t.tile, 0) * kSigStrideU64,
+                                                            kSigStrideU64 * 8, a.W, kCmpEq, 1ull,
+                                                            a.timeout, a.err, &lds_flag))
+                        return;
+                    rs_reduce_tile(a, t.j, t.tile);
+                }
+            }
+            if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
+            __syncthreads();
+            pos = (int64_t)__builtin_amdgcn_readfirstlane((int)lds_pos[k & 1]);
+            ++k;
+        }
+    }
+}
+
+hipError_t launch_gemm_rs(const GemmRsArgs& a, int grid, hipStream_t st) {
+    void* args[] = {const_cast<GemmRsArgs*>(&a)};
+    const void* fn = a.sync == kSyncXcd ? reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncXcd>)
+                                        : reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncAgent>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kGemmThreads), args, 0, st);
+}
+
+hipError_t gemm_rs_blocks_per_cu(int sync, int* n) {
+    const void* fn = sync == kSyncXcd ? reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncXcd>)
+                                      : reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncAgent>);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, fn, kGemmThreads, 0);
 }
 
 hipError_t launch_ag_gemm(const AgGemmArgs& a, int grid, hipStream_t st) {

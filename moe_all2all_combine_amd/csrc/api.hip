@@ -1026,6 +1026,156 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
     return ok();
 }
 
+// ===========================================================================
+// GEMM + ReduceScatter
+
+namespace {
+
+int plan_gemm_rs(int W, int64_t m, int64_t K, int64_t N, int nxcd, bool agent_sync,
+                 ra2a::GemmRsArgs* a) {
+    if (W < 1) return fail(RA2A_EINVAL, "W must be >= 1");
+    if (m < 1 || K < 1 || N < 1) return fail(RA2A_EINVAL, "m, K and N must be >= 1");
+    if (m % W) return fail(RA2A_EINVAL, "m=%lld must be divisible by W=%d (each rank receives m/W rows)",
+                           (long long)m, W);
+    if (K % 8) return fail(RA2A_EINVAL, "K must be a multiple of 8 (16-byte rows)");
+    *a = ra2a::GemmRsArgs{};
+    a->W = W;
+    a->m = m;
+    a->mj = m / W;
+    a->K = K;
+    a->N = N;
+    a->ntm = (int)cdiv(a->mj, ra2a::kRsTile);
+    a->ntn = (int)cdiv(N, ra2a::kRsTile);
+    a->ntiles = a->ntm * a->ntn;
+    a->nblocks = (int)cdiv(a->ntiles, ra2a::kRsBlock);
+    a->NG = std::max(1, std::min(nxcd, ra2a::kNumXcd));
+    a->dpg = (int)cdiv(W, a->NG);
+    a->sync = (agent_sync || nxcd > ra2a::kNumXcd) ? ra2a::kSyncAgent : ra2a::kSyncXcd;
+    a->ntasks_dest = (int64_t)a->ntiles * (W + 1);
+    if ((double)a->ntasks_dest * a->dpg >= 2147483647.0 - 65536.0)
+        return fail(RA2A_EINVAL, "GEMM+ReduceScatter too large for 32-bit task indices");
+    // a GEMM tile's operand rows and the receive area are addressed with 32-bit buffer offsets
+    if ((double)ra2a::kRsTile * K * 2 >= 4294967295.0 - 65536.0)
+        return fail(RA2A_EINVAL, "K too large for 32-bit operand offsets");
+    if ((double)W * a->mj * N * 4 >= 4294967295.0 - 65536.0)
+        return fail(RA2A_EINVAL, "receive area of 4 GiB or more per slice");
+    return RA2A_OK;
+}
+
+}  // namespace
+
+RA2A_API int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int64_t* tile_slots,
+                                int64_t* queue_slots, size_t* partial_bytes) {
+    ra2a::GemmRsArgs a{};
+    int rc = plan_gemm_rs(W, m, K, N, ra2a::kNumXcd, false, &a);
+    if (rc) return rc;
+    if (tile_slots) *tile_slots = (int64_t)a.ntiles * W;
+    if (queue_slots) *queue_slots = ra2a::kQueueSlots;
+    if (partial_bytes) *partial_bytes = (size_t)W * (size_t)a.mj * (size_t)N * 4u;
+    return ok();
+}
+
+RA2A_API int ra2a_gemm_rs(const void* x1, const void* x2t, void* partial, void* out,
+                          uint64_t* signals, int W, int64_t m, int64_t K, int64_t N, int flags,
+                          void* stream) {
+    if (flags & ~(RA2A_RS_AGENT_SYNC | RA2A_RS_SKIP_RESET)) return fail(RA2A_EINVAL, "unknown flags");
+    if (!x1 || !x2t || !partial || !out || !signals) return fail(RA2A_EINVAL, "NULL pointer");
+    ra2a_heap* h = find_heap(x1);
+    if (!h) return fail(RA2A_EINVAL, "x1 is not inside a symmetric heap");
+    if (h->world != W) return fail(RA2A_EINVAL, "W=%d but the heap has %d slices", W, h->world);
+    if (!in_heap(h, x2t) || !in_heap(h, partial) || !in_heap(h, out) || !in_heap(h, signals))
+        return fail(RA2A_EINVAL, "x2t, partial, out and signals must be inside the heap of x1");
+    int nxcd = 1;
+    int rc = xcd_count(&nxcd);
+    if (rc) return rc;
+    ra2a::GemmRsArgs a{};
+    rc = plan_gemm_rs(W, m, K, N, nxcd, (flags & RA2A_RS_AGENT_SYNC) != 0, &a);
+    if (rc) return rc;
+    const size_t o_a = sym_offset(h, x1), o_b = sym_offset(h, x2t), o_p = sym_offset(h, partial);
+    const size_t o_o = sym_offset(h, out), o_s = sym_offset(h, signals);
+    const size_t n_a = (size_t)(m * K * 2), n_b = (size_t)(N * K * 2);
+    const size_t n_p = (size_t)W * (size_t)a.mj * (size_t)N * 4u, n_o = (size_t)(a.mj * N * 2);
+    const int64_t nslots = ra2a::grs_queue_slot(a) + ra2a::kQueueSlots;
+    const size_t n_s = (size_t)nslots * RA2A_SIG_STRIDE_BYTES;
+    if (o_a % 16 || o_b % 16 || o_p % 16 || o_o % 8 || o_s % 8)
+        return fail(RA2A_EINVAL, "x1, x2t and partial must be 16-byte aligned, out and signals 8");
+    const size_t offs[5] = {o_a, o_b, o_p, o_o, o_s}, lens[5] = {n_a, n_b, n_p, n_o, n_s};
+    for (int i = 0; i < 5; ++i) {
+        if (offs[i] + lens[i] > h->stride)
+            return fail(RA2A_EINVAL, "an operand, the receive area, out or the signals cross the "
+                                     "end of a slice");
+        for (int k2 = 0; k2 < i; ++k2)
+            if (offs[i] < offs[k2] + lens[k2] && offs[k2] < offs[i] + lens[i])
+                return fail(RA2A_EINVAL, "x1, x2t, partial, out and signals must not overlap");
+    }
+    rc = ensure_err(h);
+    if (rc) return rc;
+    a.base = h->base;
+    a.stride = (int64_t)h->stride;
+    a.a_off = (int64_t)o_a;
+    a.bt_off = (int64_t)o_b;
+    a.p_off = (int64_t)o_p;
+    a.out_off = (int64_t)o_o;
+    a.sig_off = (int64_t)o_s;
+    a.err = h->err;
+    a.timeout = timeout_ticks(h);
+    int ncu = 0;
+    rc = device_cus(&ncu);
+    if (rc) return rc;
+    int occ = 0;
+    hipError_t he = ra2a::gemm_rs_blocks_per_cu(a.sync, &occ);
+    if (he != hipSuccess) return hip_fail(he, "occupancy query");
+    if (occ < 1) return fail(RA2A_EUNSUPPORTED, "the GEMM+ReduceScatter kernel does not fit a compute unit");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!(flags & RA2A_RS_SKIP_RESET)) {
+        he = ra2a::launch_signal_reset(h->base, (int64_t)h->stride, W, (int64_t)o_s, nslots, st);
+        if (he != hipSuccess) return hip_fail(he, "signal reset launch");
+    }
+    he = ra2a::launch_gemm_rs(a, occ * ncu, st);
+    if (he != hipSuccess) return hip_fail(he, "GEMM+ReduceScatter launch");
+    return ok();
+}
+
+RA2A_API int ra2a_debug_gemm_rs_plan(int W, int64_t m, int64_t K, int64_t N, int num_xcd,
+                                     int64_t* tasks_per_group) {
+    ra2a::GemmRsArgs a{};
+    int rc = plan_gemm_rs(W, m, K, N, std::max(1, num_xcd), false, &a);
+    if (rc) return rc;
+    // every destination's queue: each (source, tile) GEMM task and each reduce task
+    // exactly once, and every reduce task after the W GEMM tasks it waits for
+    for (int g = 0; g < a.NG; ++g) {
+        const int64_t total = a.ntasks_dest * a.dpg;
+        std::vector<int> done((size_t)W * a.ntiles * W, 0), red((size_t)W * a.ntiles, 0);
+        for (int64_t pos = 0; pos < total; ++pos) {
+            const ra2a::RsTask t = ra2a::grs_group_task(a, g, pos);
+            if (t.j < 0 || t.tile < 0 || t.tile >= a.ntiles || t.r < 0 || t.r >= W ||
+                t.j % a.NG != g)
+                return fail(RA2A_EINVAL, "group %d position %lld: task out of range", g, (long long)pos);
+            if (t.j >= W) continue;  // padding of the last group
+            if (!t.reduce) {
+                int& d = done[((size_t)t.j * a.ntiles + t.tile) * W + t.r];
+                if (d++) return fail(RA2A_EINVAL, "GEMM task (j=%d, tile=%d, r=%d) twice", t.j, t.tile, t.r);
+            } else {
+                for (int r = 0; r < W; ++r)
+                    if (!done[((size_t)t.j * a.ntiles + t.tile) * W + r])
+                        return fail(RA2A_EINVAL, "group %d position %lld: reduce of tile %d waits for "
+                                    "a GEMM task queued after it", g, (long long)pos, t.tile);
+                if (red[(size_t)t.j * a.ntiles + t.tile]++)
+                    return fail(RA2A_EINVAL, "reduce task twice");
+            }
+        }
+        for (int j = g; j < W; j += a.NG)
+            for (int t = 0; t < a.ntiles; ++t) {
+                if (!red[(size_t)j * a.ntiles + t]) return fail(RA2A_EINVAL, "a reduce task is missing");
+                for (int r = 0; r < W; ++r)
+                    if (!done[((size_t)j * a.ntiles + t) * W + r])
+                        return fail(RA2A_EINVAL, "a GEMM task is missing");
+            }
+    }
+    if (tasks_per_group) *tasks_per_group = a.ntasks_dest * a.dpg;
+    return ok();
+}
+
 RA2A_API int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t N,
                                      int tile_rows, int num_xcd, int64_t* tasks_per_group) {
     ra2a::AgGemmArgs a{};

@@ -124,6 +124,28 @@ AG_GEMM = AgGemmWorkload("ag_gemm_w8_m1024_k7168_n4096_bf16", W=8, m_local=1024,
                          N=4096, tile_rows=128, seed_a=3, seed_b=4, std=0.02)
 
 
+@dataclasses.dataclass(frozen=True)
+class GemmRsWorkload:
+    """GEMM + ReduceScatter: rank r holds x1_r (m x K) and x2_r (K x N, passed
+    transposed); rank j receives rows [j*m/W, (j+1)*m/W) of sum_r x1_r @ x2_r."""
+
+    name: str
+    W: int
+    m: int
+    K: int
+    N: int
+    seed_a: int
+    seed_b: int
+    std: float
+
+
+# The ReduceScatter counterpart of the AllGather+GEMM workload: the same 8192 x
+# 4096 output and the same FLOPs, with K = 7168 split over the 8 ranks (each
+# rank's x1_r is its K-slice of the activations, x2_r its K-slice of the weight).
+GEMM_RS = GemmRsWorkload("gemm_rs_w8_m8192_k896_n4096_bf16", W=8, m=8192, K=896, N=4096,
+                         seed_a=6, seed_b=7, std=0.02)
+
+
 def small_workload(W: int, S: int, H: int, D: int, dtype: str = "bf16", seed: int = 0,
                    tile=(None, None, None), protocol: str = PROTOCOL_ADD,
                    dist: Optional[str] = None) -> CombineWorkload:
@@ -215,3 +237,28 @@ def make_integer_ag_gemm_inputs(W: int, m_local: int, K: int, N: int, seed: int 
     tb = torch.randint(-1, 2, (K, N), generator=g).to(torch.float32)
     b = tb.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     return shards, b
+
+
+def make_gemm_rs_inputs(wl: GemmRsWorkload = GEMM_RS, m: Optional[int] = None,
+                        K: Optional[int] = None, N: Optional[int] = None, W: Optional[int] = None,
+                        integer: bool = False):
+    """(list of W x1_r as bf16 bits (m, K), list of W x2_r^T as bf16 bits (N, K)).
+
+    Normal(0, std) values, or (integer=True) integers in {-1, 0, 1}."""
+    W = W or wl.W
+    m = m or wl.m
+    K = K or wl.K
+    N = N or wl.N
+
+    def draw(g, shape):
+        if integer:
+            t = torch.randint(-1, 2, shape, generator=g).to(torch.float32)
+        else:
+            t = torch.randn(shape, dtype=torch.float32, generator=g) * wl.std
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    ga = torch.Generator().manual_seed(wl.seed_a)
+    gb = torch.Generator().manual_seed(wl.seed_b)
+    a = [draw(ga, (m, K)) for _ in range(W)]
+    bt = [draw(gb, (N, K)) for _ in range(W)]
+    return a, bt

@@ -1,0 +1,45 @@
+"""Host checks of the GEMM+ReduceScatter work queues (no GPU): the kernel's own
+task decode (gemm_rs_geom.h) holds every (destination, tile, source) GEMM task
+and every reduce task once per queue, each reduce task after the W GEMM tasks it
+waits for (the deadlock-freedom argument), and the argument checks reject what
+the kernel cannot run."""
+import pytest
+
+import moe_all2all_combine_amd as ra2a
+
+SHAPES = [
+    # W, m, K, N
+    (8, 8192, 896, 4096),
+    (8, 512, 512, 512),
+    (3, 300, 72, 200),
+    (3, 300, 72, 202),
+    (1, 5, 8, 8),
+    (2, 2, 8, 3000),
+    (16, 2048, 64, 264),
+    (5, 5 * 700, 16, 1000),
+    (8, 8 * 257, 8, 257),
+]
+
+
+@pytest.mark.parametrize("W,m,K,N", SHAPES)
+@pytest.mark.parametrize("num_xcd", [8, 3, 1])
+def test_queues_hold_every_task_once_and_waits_point_backwards(W, m, K, N, num_xcd):
+    n = ra2a.debug_gemm_rs_plan(W, m, K, N, num_xcd)
+    tiles = -(-(m // W) // 256) * -(-N // 256)
+    groups = min(num_xcd, 8)
+    assert n == tiles * (W + 1) * -(-W // groups)
+
+
+def test_sizes():
+    t, q, p = ra2a.gemm_rs_sizes(8, 8192, 896, 4096)
+    assert (t, q, p) == (4 * 16 * 8, ra2a.QUEUE_SLOTS, 8 * 1024 * 4096 * 4)
+
+
+@pytest.mark.parametrize("args", [(3, 100, 8, 8),      # m not divisible by W
+                                  (2, 8, 12, 8),       # K not a multiple of 8
+                                  (0, 8, 8, 8), (2, 0, 8, 8), (2, 8, 8, 0),
+                                  (8, 8 * 20000, 8, 8192)])  # receive area above 4 GiB
+def test_rejected_shapes(args):
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.gemm_rs_sizes(*args)
+    assert e.value.code == ra2a.EINVAL
