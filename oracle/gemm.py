@@ -18,7 +18,10 @@ GEMM + ReduceScatter (the RFC, section 十, "fused_matmul_reduce_scatter"; and
 output = ReduceScatter(x1 @ x2).  Rank r holds x1_r (m x K) and x2_r (K x N);
 its product is an (m x N) partial; the ReduceScatter sums the W partials and
 gives rank j rows [j*m/W, (j+1)*m/W) of the sum (reading: an even row split, m
-divisible by W).
+divisible by W).  The pages do not fix the partials' type.  Reading taken: in
+framework semantics x1 @ x2 of bf16 tensors is itself a bf16 tensor, so the
+default GPU path rounds each partial to bf16 before the ReduceScatter adds them
+(``round_partials=True`` here); the exact partials are kept as an option.
 
 bf16 inputs convert exactly to float64 (every bf16 value is a float64 value),
 so ``ref`` is the exact product up to float64 summation rounding.
@@ -84,11 +87,23 @@ def ag_gemm_rows_ref(shards_bits: List[np.ndarray], b_bits: np.ndarray,
     return a @ bf16_bits_to_f64(b_bits)
 
 
-def gemm_rs_ref(a_bits: List[np.ndarray], bt_bits: List[np.ndarray]) -> List[np.ndarray]:
+def _partial(a: np.ndarray, bt: np.ndarray, round_partials: bool) -> np.ndarray:
+    """x1_r @ x2_r in float64; with round_partials, as the bf16 tensor a framework's
+    matmul of bf16 operands returns (the exact product rounded once to bf16,
+    nearest even)."""
+    p = bf16_bits_to_f64(a) @ bf16_bits_to_f64(bt).T
+    return bf16_bits_to_f64(f64_to_bf16_rne_bits(p)) if round_partials else p
+
+
+def gemm_rs_ref(a_bits: List[np.ndarray], bt_bits: List[np.ndarray],
+                round_partials: bool = False) -> List[np.ndarray]:
     """out_j = (sum_r x1_r @ x2_r)[j*m/W : (j+1)*m/W] in float64.
 
-    a_bits[r]: x1_r as bf16 bits (m x K); bt_bits[r]: x2_r transposed, bf16 bits
-    (N x K), so x2_r = bt_bits[r].T.
+    HyperParallel RFC, section 十, fused_matmul_reduce_scatter: output =
+    ReduceScatter(x1 @ x2).  a_bits[r]: x1_r as bf16 bits (m x K); bt_bits[r]:
+    x2_r transposed, bf16 bits (N x K), so x2_r = bt_bits[r].T.  The sum is taken
+    in float64 either over the exact per-rank products or (round_partials) over
+    the per-rank products rounded to bf16 first.
     """
     W = len(a_bits)
     m = a_bits[0].shape[0]
@@ -97,20 +112,20 @@ def gemm_rs_ref(a_bits: List[np.ndarray], bt_bits: List[np.ndarray]) -> List[np.
     mj = m // W
     total = None
     for a, bt in zip(a_bits, bt_bits):
-        part = bf16_bits_to_f64(a) @ bf16_bits_to_f64(bt).T
+        part = _partial(a, bt, round_partials)
         total = part if total is None else total + part
     return [total[j * mj:(j + 1) * mj] for j in range(W)]
 
 
 def gemm_rs_rows_ref(a_bits: List[np.ndarray], bt_bits: List[np.ndarray], j: int,
-                     rows: np.ndarray) -> np.ndarray:
+                     rows: np.ndarray, round_partials: bool = False) -> np.ndarray:
     """Selected rows of out_j (for sampled checks at full size)."""
     W = len(a_bits)
     mj = a_bits[0].shape[0] // W
     idx = j * mj + np.asarray(rows, dtype=np.int64)
     total = None
     for a, bt in zip(a_bits, bt_bits):
-        part = bf16_bits_to_f64(a[idx]) @ bf16_bits_to_f64(bt).T
+        part = _partial(a[idx], bt, round_partials)
         total = part if total is None else total + part
     return total
 

@@ -186,3 +186,59 @@ def test_gemm_rs_planted_mistakes_are_caught():
         differs = any(o is None or o.shape != ok[j].shape or not np.array_equal(o, ok[j])
                       for j, o in enumerate(outs))
         assert differs, f"mutant '{name}' agrees with the oracle"
+
+
+def _one_hot_rows(count, K):
+    """A 1 x K row of `count` ones then zeros, as bf16 bits."""
+    v = np.zeros((1, K))
+    v[0, :count] = 1.0
+    return gemm.f64_to_bf16_rne_bits(v)
+
+
+def test_gemm_rs_rounded_partials_hand_worked():
+    """W=2, m=2, N=1, K=264, x2 all ones.  Rank 0's partial for row 0 is 257, which
+    lies halfway between the bf16 neighbours 256 and 258 (spacing 2 on [256, 512))
+    and rounds to the even significand, 256; rank 1's partial is 1.  Rounded
+    partials: 256 + 1 = 257, stored as bf16 256 (0x4380).  Exact partials: 258,
+    a bf16 value (0x4381)."""
+    K = 264
+    ones = gemm.f64_to_bf16_rne_bits(np.ones((1, K)))
+    a = [np.concatenate([_one_hot_rows(257, K), _one_hot_rows(0, K)]),
+         np.concatenate([_one_hot_rows(1, K), _one_hot_rows(0, K)])]
+    bt = [ones, ones]
+    exact = gemm.gemm_rs_ref(a, bt)
+    rounded = gemm.gemm_rs_ref(a, bt, round_partials=True)
+    assert exact[0][0, 0] == 258.0 and rounded[0][0, 0] == 257.0
+    assert exact[1][0, 0] == 0.0 and rounded[1][0, 0] == 0.0
+    assert int(gemm.f64_to_bf16_rne_bits(rounded[0])[0, 0]) == 0x4380
+    assert int(gemm.f64_to_bf16_rne_bits(exact[0])[0, 0]) == 0x4381
+    np.testing.assert_array_equal(gemm.gemm_rs_rows_ref(a, bt, 0, np.array([0]), round_partials=True),
+                                  rounded[0])
+
+
+def test_gemm_rs_rounded_partials_equal_exact_when_partials_are_bf16_values():
+    """Integer partials of magnitude <= 256 are bf16 values: rounding changes nothing."""
+    rng = np.random.default_rng(9)
+    W, m, K, N = 4, 8, 64, 6  # |partial| <= 2 * 2 * 64 = 256
+    a = [_bf16_ints(rng, (m, K)) for _ in range(W)]
+    bt = [_bf16_ints(rng, (N, K)) for _ in range(W)]
+    for x, y in zip(gemm.gemm_rs_ref(a, bt), gemm.gemm_rs_ref(a, bt, round_partials=True)):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_gemm_rs_rounded_partials_match_torch_bf16_matmul():
+    """Each rounded partial equals torch's float64 product cast to bf16 (a library
+    conversion), summed over ranks."""
+    rng = np.random.default_rng(10)
+    W, m, K, N = 2, 4, 40, 5
+    a = [gemm.f64_to_bf16_rne_bits(rng.standard_normal((m, K))) for _ in range(W)]
+    bt = [gemm.f64_to_bf16_rne_bits(rng.standard_normal((N, K))) for _ in range(W)]
+    tot = 0
+    for x, y in zip(a, bt):
+        p = torch.from_numpy(gemm.bf16_bits_to_f64(x)) @ torch.from_numpy(gemm.bf16_bits_to_f64(y)).T
+        tot = tot + p.to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.concatenate(gemm.gemm_rs_ref(a, bt, round_partials=True))
+    # the float64 -> float32 -> bf16 double rounding can differ from one rounding
+    # only on the rare values within 2**-24 relative of a bf16 midpoint
+    assert np.mean(got == tot) > 0.99
+    np.testing.assert_allclose(got, tot, rtol=2 ** -7)
