@@ -165,13 +165,92 @@ def ag_gemm_leg(steps):
         heap.close()
 
 
+def gemm_rs_leg(steps):
+    """The GEMM + ReduceScatter workload (W=8 ranks, x1_r 8192 x 896, x2_r
+    896 x 4096; bf16 in, fp32 partials and sums, bf16 out): one call = signal
+    reset + the persistent launch; also timed with the partials rounded to bf16.  For context, the same product as a library
+    sequence without overlap: W torch.mm calls (bf16 out) then a sum over the
+    sources of each destination's rows."""
+    import torch
+
+    import moe_all2all_combine_amd as ra2a
+    import synthgen
+
+    g = synthgen.GEMM_RS
+    W, m, K, N = g.W, g.m, g.K, g.N
+    mj = m // W
+    nt, nq, pbytes = ra2a.gemm_rs_sizes(W, m, K, N)  # fp32 partials: the larger area
+    nsig = nt + nq
+    na, nb, no = m * K * 2, N * K * 2, mj * N * 2
+    heap = ra2a.SymmHeap(W, na + nb + pbytes + no + nsig * 128 + (1 << 16))
+    try:
+        oa, ob, op = heap.alloc(na), heap.alloc(nb), heap.alloc(pbytes)
+        oo, osg = heap.alloc(no), heap.alloc(nsig * 128)
+        gen = torch.Generator(device="cuda").manual_seed(g.seed_a)
+        for r in range(W):
+            heap.view(oa, (m, K), torch.bfloat16, r).copy_(
+                torch.randn(m, K, generator=gen, device="cuda") * g.std)
+            heap.view(ob, (N, K), torch.bfloat16, r).copy_(
+                torch.randn(N, K, generator=gen, device="cuda") * g.std)
+        st = torch.cuda.current_stream()
+
+        def call(flags=0):
+            ra2a.gemm_rs(heap.ptr(oa), heap.ptr(ob), heap.ptr(op), heap.ptr(oo), heap.ptr(osg),
+                         W, m, K, N, flags, st)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for _ in range(steps):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+
+        ms = timed(call)
+        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
+        bf16p_ms = timed(lambda: call(ra2a.RS_BF16_PARTIALS))
+        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
+        # the library sequence, on the same inputs
+        x1 = [heap.view(oa, (m, K), torch.bfloat16, r) for r in range(W)]
+        x2 = [heap.view(ob, (N, K), torch.bfloat16, r).t() for r in range(W)]
+        part = torch.empty(W, m, N, dtype=torch.bfloat16, device="cuda")
+        out = torch.empty(m, N, dtype=torch.float32, device="cuda")
+
+        def lib():
+            for r in range(W):
+                torch.mm(x1[r], x2[r], out=part[r])
+            torch.sum(part, dim=0, dtype=torch.float32, out=out)
+
+        lib_ms = timed(lib)
+        flops = 2.0 * W * m * N * K
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"workload": g.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "calls": steps,
+                "note": "one call = signal reset + persistent launch; fp32 partials",
+                "bf16_partials": {"ms": round(bf16p_ms, 4),
+                                  "TFLOP/s": round(flops / (bf16p_ms * 1e-3) / 1e12, 1)},
+                "library_sequence": {"ms": round(lib_ms, 4),
+                                     "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 1),
+                                     "what": "W torch.mm (bf16 out) + fp32 sum over sources"},
+                "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "kernel": "gemm_rs_kernel (reset + one launch per call)",
+                             "ms_per_call": round(ms, 4), "flop_per_launch": flops}}
+    finally:
+        heap.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--legs", choices=["all", "main", "ag_gemm"], default="all")
+    ap.add_argument("--legs", choices=["all", "main", "ag_gemm", "gemm_rs"], default="all")
     ap.add_argument("--workload", default=WORKLOAD)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -188,6 +267,10 @@ def main():
     if args.legs == "ag_gemm":  # only the AllGather+GEMM leg (for counter runs)
         torch.cuda.set_device(0)
         print(json.dumps({"ag_gemm": ag_gemm_leg(args.steps)}), flush=True)
+        return
+    if args.legs == "gemm_rs":  # only the GEMM+ReduceScatter leg (for counter runs)
+        torch.cuda.set_device(0)
+        print(json.dumps({"gemm_rs": gemm_rs_leg(args.steps)}), flush=True)
         return
 
     wl = synthgen.WORKLOADS[args.workload]
@@ -401,6 +484,7 @@ def main():
     heap.close()
     if args.legs == "all":
         rec["ag_gemm"] = ag_gemm_leg(args.steps // 5 + 3)
+        rec["gemm_rs"] = gemm_rs_leg(args.steps // 5 + 3)
     rec["cpu_baseline"] = None if args.no_cpu else cpu_baseline(wl, ins)
     print(json.dumps(rec), flush=True)
 

@@ -409,29 +409,38 @@ int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t
  * ReduceScatter(x1 @ x2): rank r holds x1_r (m x K) and x2_r (K x N); rank j
  * receives out_j = rows [j*m/W, (j+1)*m/W) of sum_r x1_r @ x2_r (m must be
  * divisible by W).  One persistent launch: producer tasks compute 256 x 256
- * tiles of rank r's partial product for destination j, store them in fp32 into
- * j's receive area at slot r and SET the (tile, r) signal in j's slice; the
+ * tiles of rank r's partial product for destination j, store them into j's
+ * receive area at slot r and SET the (tile, r) signal in j's slice; the
  * receiver's reduce task waits for the W partials of its tile, adds them in
- * rank order 0..W-1 in fp32 and stores bf16 (round to nearest even).  Producers
+ * rank order 0..W-1 in fp32 and stores bf16 (round to nearest even).  A partial
+ * is the fp32 accumulator tile of x1_r @ x2_r (one rounding in all, to bf16 at
+ * the end), or with RA2A_RS_BF16_PARTIALS that product as the bf16 tensor a
+ * framework's matmul returns (rounded to nearest even): half the receive area
+ * and its traffic, at the cost of W more roundings, so that where the partials
+ * cancel the elementwise error is no longer bounded by the result's magnitude
+ * but by 2^-8 * sum_r |partial_r|.  Producers
  * for destination j visit the sources in the RFC's rotation ((j - t) mod W at
  * step t, so rank r works for rank (r + t) mod W).  bf16 operands, fp32
  * accumulation.  Every wait is bounded (ra2a_check reports RA2A_ETIMEOUT).    */
 #define RA2A_RS_AGENT_SYNC 1 /* device-wide release/acquire instead of the XCD-local protocol */
 #define RA2A_RS_SKIP_RESET 2 /* the caller zeroed the signals; no reset launch */
+#define RA2A_RS_BF16_PARTIALS 4 /* partials rounded to bf16 instead of kept in fp32 */
 
 /* Sizes for (W, m, K, N): `tile_slots` = (output tiles of out_j) * W signal slots
  * per slice, then `queue_slots` (RA2A_QUEUE_SLOTS) queue words (slice 0); the
  * `signals` array must hold their sum per slice.  `partial_bytes` = bytes of the
- * receive area per slice: [W][m/W][N] fp32.  Any output pointer may be NULL.
- * Errors: EINVAL.                                                              */
-int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int64_t *tile_slots,
+ * receive area per slice: [W][m/W][N] fp32, or bf16 if `flags` holds
+ * RA2A_RS_BF16_PARTIALS (the other flags do not change the sizes).  Any output
+ * pointer may be NULL.  Errors: EINVAL.                                        */
+int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int flags, int64_t *tile_slots,
                        int64_t *queue_slots, size_t *partial_bytes);
 
 /* All five buffers are symmetric, inside one heap of W slices, at these
  * offsets in every slice (row-major, bf16 unless stated):
  *   x1      slice r: x1_r, m x K (16-byte aligned);
  *   x2t     slice r: x2_r transposed, N x K (16-byte aligned);
- *   partial slice j: the receive area, [W][m/W][N] fp32 (16-byte aligned);
+ *   partial slice j: the receive area, [W][m/W][N] fp32 or (RA2A_RS_BF16_PARTIALS)
+ *           bf16 (16-byte aligned);
  *   out     slice j: out_j, m/W x N (8-byte aligned);
  *   signals slice j: ra2a_gemm_rs_sizes' slots at 128-byte spacing (8-byte aligned).
  * K must be a multiple of 8.  The signals are zeroed by a reset launch first

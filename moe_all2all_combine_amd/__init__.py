@@ -18,7 +18,7 @@ from typing import Optional, Sequence, Tuple
 __all__ = [
     "Ra2aError", "Opts", "SymmHeap", "lib", "OK", "EINVAL", "ENOMEM", "EHIP", "ETIMEOUT",
     "EUNSUPPORTED", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "MODE_DIRECT", "MODE_STAGED",
-    "QUEUE_SLOTS", "RS_AGENT_SYNC", "RS_SKIP_RESET", "gemm_rs_sizes", "gemm_rs", "debug_gemm_rs_plan", "MODE_BULK", "DIR_COMBINE", "DIR_DISPATCH", "all2all_dispatch", "all2all_dispatch_ex", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
+    "QUEUE_SLOTS", "RS_AGENT_SYNC", "RS_SKIP_RESET", "RS_BF16_PARTIALS", "gemm_rs_sizes", "gemm_rs", "debug_gemm_rs_plan", "MODE_BULK", "DIR_COMBINE", "DIR_DISPATCH", "all2all_dispatch", "all2all_dispatch_ex", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
     "CMP_LE", "SIG_STRIDE_BYTES", "DTYPES", "symm_heap_create", "symm_heap_attach",
     "symm_heap_destroy", "symm_malloc", "symm_heap_info", "symm_at", "put", "get",
     "put_with_signal", "signal_op", "wait_signal", "signal_reset", "rev_all2all",
@@ -123,8 +123,8 @@ def lib():
                                             ctypes.POINTER(i64)]),
         "ra2a_ag_gemm": (i32, [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp]),
         "ra2a_debug_ag_gemm_plan": (i32, [i32, i32, i64, i64, i64, i32, i32, ctypes.POINTER(i64)]),
-        "ra2a_gemm_rs_sizes": (i32, [i32, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
-                                     ctypes.POINTER(sz)]),
+        "ra2a_gemm_rs_sizes": (i32, [i32, i64, i64, i64, i32, ctypes.POINTER(i64),
+                                     ctypes.POINTER(i64), ctypes.POINTER(sz)]),
         "ra2a_gemm_rs": (i32, [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp]),
         "ra2a_debug_gemm_rs_plan": (i32, [i32, i64, i64, i64, i32, ctypes.POINTER(i64)]),
         "ra2a_debug_emulate_pipelined": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp),
@@ -401,12 +401,14 @@ class SymmHeap:
 
 RS_AGENT_SYNC = 1
 RS_SKIP_RESET = 2
+RS_BF16_PARTIALS = 4
 
 
-def gemm_rs_sizes(W: int, m: int, K: int, N: int) -> Tuple[int, int, int]:
+def gemm_rs_sizes(W: int, m: int, K: int, N: int, flags: int = 0) -> Tuple[int, int, int]:
     """(tile signal slots, queue words, receive-area bytes) per slice."""
     a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
-    _ok(lib().ra2a_gemm_rs_sizes(W, m, K, N, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    _ok(lib().ra2a_gemm_rs_sizes(W, m, K, N, flags, ctypes.byref(a), ctypes.byref(b),
+                                 ctypes.byref(c)))
     return a.value, b.value, c.value
 
 

@@ -362,9 +362,58 @@ __global__ void __launch_bounds__(kGemmThreads, 1) ag_gemm_kernel(AgGemmArgs a) 
 // like the AllGather's, so the partials a reduce task reads were written into
 // the L2 it reads through.
 
-// Reduce task: out_j tile = sum over r = 0..W-1 (in that order) of the fp32
-// partials partial_j[r] of the tile, rounded to bf16 (nearest even).  The
-// partials are read with device-scope loads (never from the CU's L1).
+// Reduce task: out_j tile = sum over r = 0..W-1 (in that order) of the partials
+// partial_j[r] of the tile (bf16, or with F32P fp32), added in fp32 and rounded
+// to bf16 (nearest even).  The partials are read with device-scope loads (never
+// from the CU's L1).  V columns per lane: V partial elements form one load.
+template <bool F32P, int V>
+__device__ __forceinline__ void rs_reduce_cols(const GemmRsArgs& a, uint8_t* slice, int64_t row0,
+                                               int64_t col0, int rows, int cols) {
+    constexpr int E = F32P ? 4 : 2;  // bytes per partial element
+    using Load = BufLoad<V * E, kPolicySc1>;
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc_uniform(slice + a.p_off, (uint32_t)((int64_t)a.W * a.mj * a.N * E));
+    uint16_t* const out = reinterpret_cast<uint16_t*>(slice + a.out_off);
+    const uint32_t plane = (uint32_t)(a.mj * a.N * E);  // bytes of one source's partial
+    const int vc = cols / V;
+    for (int i = threadIdx.x; i < rows * vc; i += kGemmThreads) {
+        const int r = i / vc;
+        const int c = (i - r * vc) * V;
+        const int64_t el = (row0 + r) * a.N + col0 + c;
+        const uint32_t off = (uint32_t)(el * E);
+        float s[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) s[v] = 0.f;
+        for (int src = 0; src < a.W; ++src) {
+            const auto x = Load::go(rp, off + (uint32_t)src * plane);
+            if constexpr (V == 1) {
+                s[0] += F32P ? __uint_as_float((uint32_t)x) : __uint_as_float((uint32_t)x << 16);
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    if constexpr (F32P)
+                        s[v] += __uint_as_float(x[v]);
+                    else
+                        s[v] += __uint_as_float(v & 1 ? x[v >> 1] & 0xFFFF0000u : x[v >> 1] << 16);
+                }
+            }
+        }
+        if constexpr (V == 1) {
+            out[el] = (uint16_t)bf16_rne(s[0]);
+        } else {
+            // V bf16 results as V/4 8-byte stores (out is 8-byte aligned, V*2 bytes per lane)
+#pragma unroll
+            for (int q = 0; q < V / 4; ++q) {
+                u32x2 o;
+                o[0] = bf16_rne(s[4 * q]) | (bf16_rne(s[4 * q + 1]) << 16);
+                o[1] = bf16_rne(s[4 * q + 2]) | (bf16_rne(s[4 * q + 3]) << 16);
+                *reinterpret_cast<u32x2*>(out + el + 4 * q) = o;
+            }
+        }
+    }
+}
+
+template <bool F32P>
 __device__ __forceinline__ void rs_reduce_tile(const GemmRsArgs& a, int j, int tile) {
     int mb, nb;
     grs_tile(a, tile, &mb, &nb);
@@ -372,44 +421,15 @@ __device__ __forceinline__ void rs_reduce_tile(const GemmRsArgs& a, int j, int t
     const int rows = a.mj - row0 < kRsTile ? (int)(a.mj - row0) : kRsTile;
     const int cols = a.N - col0 < kRsTile ? (int)(a.N - col0) : kRsTile;
     uint8_t* const slice = a.base + (int64_t)j * a.stride;
-    const __amdgpu_buffer_rsrc_t rp =
-        make_rsrc_uniform(slice + a.p_off, (uint32_t)((int64_t)a.W * a.mj * a.N * 4));
-    uint16_t* const out = reinterpret_cast<uint16_t*>(slice + a.out_off);
-    const uint32_t plane = (uint32_t)(a.mj * a.N * 4);  // bytes of one source's partial
-    if ((a.N & 3) == 0) {
-        // 4 columns per lane: 16-byte loads, 8-byte stores
-        const int vc = cols >> 2;
-        for (int i = threadIdx.x; i < rows * vc; i += kGemmThreads) {
-            const int r = i / vc;
-            const int c = (i - r * vc) << 2;
-            const uint32_t off = (uint32_t)(((row0 + r) * a.N + col0 + c) * 4);
-            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-            for (int src = 0; src < a.W; ++src) {
-                const u32x4 v = BufLoad<16, kPolicySc1>::go(rp, off + (uint32_t)src * plane);
-                s0 += __uint_as_float(v[0]);
-                s1 += __uint_as_float(v[1]);
-                s2 += __uint_as_float(v[2]);
-                s3 += __uint_as_float(v[3]);
-            }
-            u32x2 o;
-            o[0] = bf16_rne(s0) | (bf16_rne(s1) << 16);
-            o[1] = bf16_rne(s2) | (bf16_rne(s3) << 16);
-            *reinterpret_cast<u32x2*>(out + (row0 + r) * a.N + col0 + c) = o;
-        }
-    } else {
-        for (int i = threadIdx.x; i < rows * cols; i += kGemmThreads) {
-            const int r = i / cols;
-            const int c = i - r * cols;
-            const uint32_t off = (uint32_t)(((row0 + r) * a.N + col0 + c) * 4);
-            float sum = 0.f;
-            for (int src = 0; src < a.W; ++src)
-                sum += __uint_as_float(BufLoad<4, kPolicySc1>::go(rp, off + (uint32_t)src * plane));
-            out[(row0 + r) * a.N + col0 + c] = (uint16_t)bf16_rne(sum);
-        }
-    }
+    // 16-byte loads where every row of a tile splits into whole vectors
+    constexpr int V = F32P ? 4 : 8;
+    if (a.N % V == 0)
+        rs_reduce_cols<F32P, V>(a, slice, row0, col0, rows, cols);
+    else
+        rs_reduce_cols<F32P, 1>(a, slice, row0, col0, rows, cols);
 }
 
-template <int SYNC>
+template <int SYNC, bool F32P>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_rs_kernel(GemmRsArgs a) {
     __shared__ uint16_t lds[kStages * 2 * kStageElems];
     __shared__ int lds_flag;
@@ -454,9 +474,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_rs_kernel(GemmRsArgs a) 
                                          ((int64_t)t.j * a.mj + row0) * a.K;
                     const uint16_t* x2t = reinterpret_cast<const uint16_t*>(src_slice + a.bt_off) +
                                           col0 * a.K;
-                    float* part = reinterpret_cast<float*>(dst_slice + a.p_off) +
-                                  ((int64_t)t.r * a.mj + row0) * a.N + col0;
-                    gemm_tile<true>(x1, rows, x2t, cols, a.K, part, a.N, lds);
+                    uint8_t* const part = dst_slice + a.p_off +
+                                          (((int64_t)t.r * a.mj + row0) * a.N + col0) * (F32P ? 4 : 2);
+                    gemm_tile<F32P>(x1, rows, x2t, cols, a.K, part, a.N, lds);
                     group_release<SYNC>();
                     if (threadIdx.x == 0)
                         sig_update(sig + grs_sig_slot(a, t.tile, t.r) * kSigStrideU64, 1ull, kSigSet);
@@ -465,7 +485,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_rs_kernel(GemmRsArgs a) 
                                                             kSigStrideU64 * 8, a.W, kCmpEq, 1ull,
                                                             a.timeout, a.err, &lds_flag))
                         return;
-                    rs_reduce_tile(a, t.j, t.tile);
+                    rs_reduce_tile<F32P>(a, t.j, t.tile);
                 }
             }
             if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
@@ -476,17 +496,21 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_rs_kernel(GemmRsArgs a) 
     }
 }
 
-hipError_t launch_gemm_rs(const GemmRsArgs& a, int grid, hipStream_t st) {
-    void* args[] = {const_cast<GemmRsArgs*>(&a)};
-    const void* fn = a.sync == kSyncXcd ? reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncXcd>)
-                                        : reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncAgent>);
-    return hipLaunchKernel(fn, dim3(grid), dim3(kGemmThreads), args, 0, st);
+static const void* gemm_rs_fn(int sync, bool f32p) {
+    if (sync == kSyncXcd)
+        return f32p ? reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncXcd, true>)
+                    : reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncXcd, false>);
+    return f32p ? reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncAgent, true>)
+                : reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncAgent, false>);
 }
 
-hipError_t gemm_rs_blocks_per_cu(int sync, int* n) {
-    const void* fn = sync == kSyncXcd ? reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncXcd>)
-                                      : reinterpret_cast<const void*>(&gemm_rs_kernel<kSyncAgent>);
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, fn, kGemmThreads, 0);
+hipError_t launch_gemm_rs(const GemmRsArgs& a, int grid, hipStream_t st) {
+    void* args[] = {const_cast<GemmRsArgs*>(&a)};
+    return hipLaunchKernel(gemm_rs_fn(a.sync, a.f32p != 0), dim3(grid), dim3(kGemmThreads), args, 0, st);
+}
+
+hipError_t gemm_rs_blocks_per_cu(int sync, bool f32p, int* n) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, gemm_rs_fn(sync, f32p), kGemmThreads, 0);
 }
 
 hipError_t launch_ag_gemm(const AgGemmArgs& a, int grid, hipStream_t st) {

@@ -1031,8 +1031,13 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
 
 namespace {
 
-int plan_gemm_rs(int W, int64_t m, int64_t K, int64_t N, int nxcd, bool agent_sync,
+// bytes per element of the receive area
+size_t gemm_rs_elem(const ra2a::GemmRsArgs& a) { return a.f32p ? 4u : 2u; }
+
+int plan_gemm_rs(int W, int64_t m, int64_t K, int64_t N, int nxcd, int flags,
                  ra2a::GemmRsArgs* a) {
+    if (flags & ~(RA2A_RS_AGENT_SYNC | RA2A_RS_SKIP_RESET | RA2A_RS_BF16_PARTIALS))
+        return fail(RA2A_EINVAL, "unknown flags");
     if (W < 1) return fail(RA2A_EINVAL, "W must be >= 1");
     if (m < 1 || K < 1 || N < 1) return fail(RA2A_EINVAL, "m, K and N must be >= 1");
     if (m % W) return fail(RA2A_EINVAL, "m=%lld must be divisible by W=%d (each rank receives m/W rows)",
@@ -1050,35 +1055,37 @@ int plan_gemm_rs(int W, int64_t m, int64_t K, int64_t N, int nxcd, bool agent_sy
     a->nblocks = (int)cdiv(a->ntiles, ra2a::kRsBlock);
     a->NG = std::max(1, std::min(nxcd, ra2a::kNumXcd));
     a->dpg = (int)cdiv(W, a->NG);
-    a->sync = (agent_sync || nxcd > ra2a::kNumXcd) ? ra2a::kSyncAgent : ra2a::kSyncXcd;
+    a->sync = ((flags & RA2A_RS_AGENT_SYNC) || nxcd > ra2a::kNumXcd) ? ra2a::kSyncAgent : ra2a::kSyncXcd;
+    a->f32p = (flags & RA2A_RS_BF16_PARTIALS) ? 0 : 1;
     a->ntasks_dest = (int64_t)a->ntiles * (W + 1);
     if ((double)a->ntasks_dest * a->dpg >= 2147483647.0 - 65536.0)
         return fail(RA2A_EINVAL, "GEMM+ReduceScatter too large for 32-bit task indices");
     // a GEMM tile's operand rows and the receive area are addressed with 32-bit buffer offsets
     if ((double)ra2a::kRsTile * K * 2 >= 4294967295.0 - 65536.0)
         return fail(RA2A_EINVAL, "K too large for 32-bit operand offsets");
-    if ((double)W * a->mj * N * 4 >= 4294967295.0 - 65536.0)
+    if ((double)W * a->mj * N * gemm_rs_elem(*a) >= 4294967295.0 - 65536.0)
         return fail(RA2A_EINVAL, "receive area of 4 GiB or more per slice");
     return RA2A_OK;
 }
 
 }  // namespace
 
-RA2A_API int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int64_t* tile_slots,
-                                int64_t* queue_slots, size_t* partial_bytes) {
+RA2A_API int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int flags,
+                                int64_t* tile_slots, int64_t* queue_slots, size_t* partial_bytes) {
     ra2a::GemmRsArgs a{};
-    int rc = plan_gemm_rs(W, m, K, N, ra2a::kNumXcd, false, &a);
+    int rc = plan_gemm_rs(W, m, K, N, ra2a::kNumXcd, flags, &a);
     if (rc) return rc;
     if (tile_slots) *tile_slots = (int64_t)a.ntiles * W;
     if (queue_slots) *queue_slots = ra2a::kQueueSlots;
-    if (partial_bytes) *partial_bytes = (size_t)W * (size_t)a.mj * (size_t)N * 4u;
+    if (partial_bytes) *partial_bytes = (size_t)W * (size_t)a.mj * (size_t)N * gemm_rs_elem(a);
     return ok();
 }
 
 RA2A_API int ra2a_gemm_rs(const void* x1, const void* x2t, void* partial, void* out,
                           uint64_t* signals, int W, int64_t m, int64_t K, int64_t N, int flags,
                           void* stream) {
-    if (flags & ~(RA2A_RS_AGENT_SYNC | RA2A_RS_SKIP_RESET)) return fail(RA2A_EINVAL, "unknown flags");
+    if (flags & ~(RA2A_RS_AGENT_SYNC | RA2A_RS_SKIP_RESET | RA2A_RS_BF16_PARTIALS))
+        return fail(RA2A_EINVAL, "unknown flags");
     if (!x1 || !x2t || !partial || !out || !signals) return fail(RA2A_EINVAL, "NULL pointer");
     ra2a_heap* h = find_heap(x1);
     if (!h) return fail(RA2A_EINVAL, "x1 is not inside a symmetric heap");
@@ -1089,12 +1096,12 @@ RA2A_API int ra2a_gemm_rs(const void* x1, const void* x2t, void* partial, void* 
     int rc = xcd_count(&nxcd);
     if (rc) return rc;
     ra2a::GemmRsArgs a{};
-    rc = plan_gemm_rs(W, m, K, N, nxcd, (flags & RA2A_RS_AGENT_SYNC) != 0, &a);
+    rc = plan_gemm_rs(W, m, K, N, nxcd, flags, &a);
     if (rc) return rc;
     const size_t o_a = sym_offset(h, x1), o_b = sym_offset(h, x2t), o_p = sym_offset(h, partial);
     const size_t o_o = sym_offset(h, out), o_s = sym_offset(h, signals);
     const size_t n_a = (size_t)(m * K * 2), n_b = (size_t)(N * K * 2);
-    const size_t n_p = (size_t)W * (size_t)a.mj * (size_t)N * 4u, n_o = (size_t)(a.mj * N * 2);
+    const size_t n_p = (size_t)W * (size_t)a.mj * (size_t)N * gemm_rs_elem(a), n_o = (size_t)(a.mj * N * 2);
     const int64_t nslots = ra2a::grs_queue_slot(a) + ra2a::kQueueSlots;
     const size_t n_s = (size_t)nslots * RA2A_SIG_STRIDE_BYTES;
     if (o_a % 16 || o_b % 16 || o_p % 16 || o_o % 8 || o_s % 8)
@@ -1123,7 +1130,7 @@ RA2A_API int ra2a_gemm_rs(const void* x1, const void* x2t, void* partial, void* 
     rc = device_cus(&ncu);
     if (rc) return rc;
     int occ = 0;
-    hipError_t he = ra2a::gemm_rs_blocks_per_cu(a.sync, &occ);
+    hipError_t he = ra2a::gemm_rs_blocks_per_cu(a.sync, a.f32p != 0, &occ);
     if (he != hipSuccess) return hip_fail(he, "occupancy query");
     if (occ < 1) return fail(RA2A_EUNSUPPORTED, "the GEMM+ReduceScatter kernel does not fit a compute unit");
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1139,7 +1146,7 @@ RA2A_API int ra2a_gemm_rs(const void* x1, const void* x2t, void* partial, void* 
 RA2A_API int ra2a_debug_gemm_rs_plan(int W, int64_t m, int64_t K, int64_t N, int num_xcd,
                                      int64_t* tasks_per_group) {
     ra2a::GemmRsArgs a{};
-    int rc = plan_gemm_rs(W, m, K, N, std::max(1, num_xcd), false, &a);
+    int rc = plan_gemm_rs(W, m, K, N, std::max(1, num_xcd), 0, &a);
     if (rc) return rc;
     // every destination's queue: each (source, tile) GEMM task and each reduce task
     // exactly once, and every reduce task after the W GEMM tasks it waits for

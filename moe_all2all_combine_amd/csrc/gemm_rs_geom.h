@@ -7,10 +7,11 @@
 // (m x K) and x2_r, passed transposed as x2_r^T (N x K); output =
 // ReduceScatter(x1 @ x2): rank j receives out_j = rows [j*mj, (j+1)*mj) of
 // sum_r x1_r @ x2_r, mj = m / W.  Producer tasks compute one 256 x 256 tile of
-// rank r's partial for destination j and store it in fp32 into j's receive
-// area (slot r), then set the (tile, r) signal; the receiver's reduce task waits
-// for the W partials of a tile, adds them in rank order in fp32 and stores the
-// bf16 result.  Sources are visited in the RFC's rotation: at step t the
+// rank r's partial for destination j and store it into j's receive area (slot
+// r), then set the (tile, r) signal; the receiver's reduce task waits for the W
+// partials of a tile, adds them in rank order in fp32 and stores the bf16 result.
+// A partial is the fp32 accumulator tile of x1_r @ x2_r, or optionally that
+// product rounded to bf16 (nearest even), the type a framework's matmul returns.  Sources are visited in the RFC's rotation: at step t the
 // producer for destination j is rank (j - t) mod W, so rank r works for rank
 // (r + t) mod W and no destination is the target of every rank at once.
 #pragma once
@@ -33,7 +34,7 @@ struct GemmRsArgs {
     int64_t stride;       // slice stride, bytes
     int64_t a_off;        // symmetric offset of x1 (x1_r in slice r), m x K bf16
     int64_t bt_off;       // symmetric offset of x2^T (x2_r^T in slice r), N x K bf16
-    int64_t p_off;        // symmetric offset of the receive area: [W][mj][N] fp32 in slice j
+    int64_t p_off;        // symmetric offset of the receive area: [W][mj][N] bf16 (f32p: fp32) in slice j
     int64_t out_off;      // symmetric offset of out (out_j in slice j), mj x N bf16
     int64_t sig_off;      // symmetric offset of the signals ([tile][source] in slice j)
     uint32_t* err;
@@ -46,6 +47,7 @@ struct GemmRsArgs {
     int32_t NG;           // stream groups (one per XCD)
     int32_t dpg;          // destinations per group: j = g, g + NG, ...
     int32_t sync;         // kSyncXcd | kSyncAgent
+    int32_t f32p;         // 1: partials kept in fp32; 0: rounded to bf16 (a framework matmul's type)
     int64_t ntasks_dest;  // queue tasks per destination: ntiles * (W + 1)
 };
 

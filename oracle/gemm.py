@@ -18,10 +18,10 @@ GEMM + ReduceScatter (the RFC, section 十, "fused_matmul_reduce_scatter"; and
 output = ReduceScatter(x1 @ x2).  Rank r holds x1_r (m x K) and x2_r (K x N);
 its product is an (m x N) partial; the ReduceScatter sums the W partials and
 gives rank j rows [j*m/W, (j+1)*m/W) of the sum (reading: an even row split, m
-divisible by W).  The pages do not fix the partials' type.  Reading taken: in
-framework semantics x1 @ x2 of bf16 tensors is itself a bf16 tensor, so the
-default GPU path rounds each partial to bf16 before the ReduceScatter adds them
-(``round_partials=True`` here); the exact partials are kept as an option.
+divisible by W).  The pages do not fix the partials' type.  Reading taken: the
+partials are exact (the GPU keeps them in fp32); as an option, each partial is
+the bf16 tensor a framework's matmul of bf16 operands returns, rounded before
+the ReduceScatter adds them (``round_partials=True`` here).
 
 bf16 inputs convert exactly to float64 (every bf16 value is a float64 value),
 so ``ref`` is the exact product up to float64 summation rounding.

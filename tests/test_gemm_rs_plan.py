@@ -33,6 +33,24 @@ def test_queues_hold_every_task_once_and_waits_point_backwards(W, m, K, N, num_x
 def test_sizes():
     t, q, p = ra2a.gemm_rs_sizes(8, 8192, 896, 4096)
     assert (t, q, p) == (4 * 16 * 8, ra2a.QUEUE_SLOTS, 8 * 1024 * 4096 * 4)
+    t, q, p = ra2a.gemm_rs_sizes(8, 8192, 896, 4096, ra2a.RS_BF16_PARTIALS)
+    assert (t, q, p) == (4 * 16 * 8, ra2a.QUEUE_SLOTS, 8 * 1024 * 4096 * 2)
+    # the sync and reset flags do not change the sizes
+    assert ra2a.gemm_rs_sizes(8, 8192, 896, 4096, ra2a.RS_AGENT_SYNC | ra2a.RS_SKIP_RESET)[2] == \
+        8 * 1024 * 4096 * 4
+
+
+def test_unknown_flags_rejected():
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.gemm_rs_sizes(8, 8192, 896, 4096, 8)
+    assert e.value.code == ra2a.EINVAL
+
+
+def test_f32_partials_hit_the_4gib_limit_first():
+    # 8 x 8000 x 24576 elements: 3.1 GB in bf16, 6.3 GB in fp32
+    ra2a.gemm_rs_sizes(8, 8 * 8000, 8, 24576, ra2a.RS_BF16_PARTIALS)
+    with pytest.raises(ra2a.Ra2aError):
+        ra2a.gemm_rs_sizes(8, 8 * 8000, 8, 24576)
 
 
 @pytest.mark.parametrize("args", [(3, 100, 8, 8),      # m not divisible by W
