@@ -21,7 +21,7 @@ roofline of the persistent kernel (its duration from HIP events around every
 launch, on the launch stream, in a separate pass over the same steps: events
 between kernels slow the steps themselves), and for context the staged mode, the two-phase variant, a
 plain copy of the same bytes with the library's put kernel, the bulk mode
-(two-phase layout with per-(S-block, sender) signals), the forward
+(two-phase layout with per-(S-block, sender) signals), the pull mode, the forward
 All2All (dispatch, the combine's inverse map) on the same buffers, and the CPU
 oracle's rate on the host.
 
@@ -284,11 +284,13 @@ def main():
     # two-phase layout with per-(S-block, sender) signals (forces the SET layout)
     opts_bk = ra2a.Opts(skip_reset=1, mode=ra2a.MODE_BULK,
                         **{k: v for k, v in tiles.items() if k != "protocol"})
+    opts_pl = ra2a.Opts(skip_reset=1, mode=ra2a.MODE_PULL,
+                        **{k: v for k, v in tiles.items() if k != "protocol"})
     dopts = ra2a.Opts(direction=ra2a.DIR_DISPATCH, **tiles)  # forward All2All, same buffers
     nsig = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
-               for o in (opts, opts_st, opts_bk, dopts))  # each set's signal array holds any
+               for o in (opts, opts_st, opts_bk, opts_pl, dopts))  # each set's signal array holds any
     nsig_c = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
-                 for o in (opts, opts_st, opts_bk))  # what a separate reset launch clears
+                 for o in (opts, opts_st, opts_bk, opts_pl))  # what a separate reset launch clears
     ring = sum(ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, o) for o in (opts_st, opts_bk))
     full = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, None, True)
     nb = wl.bytes_per_rank
@@ -428,6 +430,11 @@ def main():
                        "value": round(alg / (bk_ms * 1e-3) / 1e9, 2),
                        "parity": parity(args.steps - 1, check_signals=False),
                        "note": "two-phase layout with per-(S-block, sender) signals"}
+        pl_ms, _ = timed(opts_pl, args.steps, args.warmup, overlap=False)  # reset launch + combine
+        rec["pull"] = {"ms_per_step": round(pl_ms, 5),
+                       "value": round(alg / (pl_ms * 1e-3) / 1e9, 2),
+                       "parity": parity(args.steps - 1, check_signals=False),
+                       "note": "pull mode: senders stage in their own slice, receivers pull"}
 
         # forward All2All (dispatch, the combine's inverse) on the same buffers
         # (in_j read as (S, H*W, D), out_r written as (S*W, H, D)), in-launch reset

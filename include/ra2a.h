@@ -200,6 +200,7 @@ int ra2a_signal_reset(const ra2a_heap_t *heap, uint64_t *sig_sym, int64_t n_slot
 #define RA2A_MODE_DIRECT 1 /* push straight into out_j (default) */
 #define RA2A_MODE_STAGED 2 /* through a staging ring in slice j, reordered by consumers */
 #define RA2A_MODE_BULK 3   /* two-phase layout with fine-grained signals (see below) */
+#define RA2A_MODE_PULL 4   /* senders stage in their own slice, receivers pull (see below) */
 
 /* Work-queue words the pipelined combine keeps after the hand-back counters
  * (used in slice 0 only, staged mode only; direct mode leaves them 0): per
@@ -259,7 +260,17 @@ typedef struct ra2a_opts {
                                * forced); a consumer waits only for its sender's slot, then
                                * reorders that block into out_j.  No ring, no hand-back
                                * (region B is empty).  Staging of 4 GiB or more per slice
-                               * needs agent_sync (EINVAL otherwise). */
+                               * needs agent_sync (EINVAL otherwise).
+                               * RA2A_MODE_PULL (HyperParallel RFC, section 5.2, pull
+                               * mode): the sender first copies its segment for j into its
+                               * OWN slice's staging [W][S][H][D] at [j][b*tile_s ..] (the
+                               * same offset as its input rows) and sets slot (b, r) in
+                               * slice j; the receiver waits for that slot, then reads the
+                               * block from the sender's slice and reorders it into out_j.
+                               * Signals, staging size (workspace_bytes) and limits as
+                               * RA2A_MODE_BULK; slice r's copy of the staging holds
+                               * sender r's outgoing segments instead of receiver j's
+                               * incoming ones. */
     int32_t consumer_split;   /* staged mode: consumer work items sharing one unit, each
                                * copying a contiguous part (default: one per 128 KiB;
                                * at most 4096) */

@@ -145,6 +145,7 @@ struct Plan {
     int direct;             // 1: direct push (no staging), 0: staged through the ring
     int inverse;            // 1: the dispatch (the combine's inverse map)
     int bulk;               // 1: two-phase staging layout with fine-grained signals
+    int pull;               // 1 (with bulk): staging in the sender's slice, pulled by the receiver
     int64_t piece_bytes, unit_bytes, tile_bytes;
 };
 
@@ -156,13 +157,14 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (o->reserved[0]) return fail(RA2A_EINVAL, "ra2a_opts_t.reserved must be zero");
     if (o->direction != RA2A_DIR_COMBINE && o->direction != RA2A_DIR_DISPATCH)
         return fail(RA2A_EINVAL, "direction must be RA2A_DIR_COMBINE or RA2A_DIR_DISPATCH");
-    if (o->direction == RA2A_DIR_DISPATCH && (o->mode == RA2A_MODE_STAGED || o->mode == RA2A_MODE_BULK))
+    if (o->direction == RA2A_DIR_DISPATCH && (o->mode == RA2A_MODE_STAGED || o->mode == RA2A_MODE_BULK ||
+                                              o->mode == RA2A_MODE_PULL))
         return fail(RA2A_EINVAL, "the dispatch runs in direct mode only");
     if (o->separate_reset != 0 && o->separate_reset != 1)
         return fail(RA2A_EINVAL, "separate_reset must be 0 or 1");
     if (o->mode != 0 && o->mode != RA2A_MODE_DIRECT && o->mode != RA2A_MODE_STAGED &&
-        o->mode != RA2A_MODE_BULK)
-        return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_DIRECT, _STAGED or _BULK");
+        o->mode != RA2A_MODE_BULK && o->mode != RA2A_MODE_PULL)
+        return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_DIRECT, _STAGED, _BULK or _PULL");
     p->BS = o->tile_s > 0 ? o->tile_s : std::min<int64_t>(S, 64);
     p->TH = o->tile_h > 0 ? o->tile_h : 1;
     p->TD = o->tile_d > 0 ? o->tile_d : D;
@@ -174,7 +176,9 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (o->protocol != 0 && o->protocol != RA2A_PROTO_ADD && o->protocol != RA2A_PROTO_SET)
         return fail(RA2A_EINVAL, "protocol must be 0, RA2A_PROTO_ADD or RA2A_PROTO_SET");
     p->inverse = o->direction == RA2A_DIR_DISPATCH ? 1 : 0;
-    p->bulk = o->mode == RA2A_MODE_BULK ? 1 : 0;
+    // the pull mode is the bulk mode's protocol with the staging on the sender's side
+    p->pull = o->mode == RA2A_MODE_PULL ? 1 : 0;
+    p->bulk = (o->mode == RA2A_MODE_BULK || p->pull) ? 1 : 0;
     // the dispatch fills each output tile from one source, and the bulk mode
     // signals each (S-block, sender): one signal per (tile, source), set to 1
     // (the SET layout)
@@ -211,7 +215,7 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (o->stream_batch < 0) return fail(RA2A_EINVAL, "stream_batch must be >= 0");
     p->stream_batch = o->stream_batch;
     p->agent_sync = o->agent_sync ? 1 : 0;
-    p->direct = (o->mode == RA2A_MODE_STAGED || o->mode == RA2A_MODE_BULK) ? 0 : 1;
+    p->direct = (o->mode == RA2A_MODE_STAGED || p->bulk) ? 0 : 1;
     p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);
     if (o->consumer_split < 0 || o->wg_per_cu < 0 || o->lookahead < -1)
         return fail(RA2A_EINVAL, "negative option");
@@ -398,6 +402,7 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     a->direct = pl.direct;
     a->inverse = pl.inverse;
     a->bulk = pl.bulk;
+    a->pull = pl.pull;
     a->straggler = opts ? opts->straggler_rank : -1;
     a->delay = opts ? opts->straggler_delay : 0;
     a->seed = opts ? opts->straggler_seed : 0;
@@ -1405,10 +1410,12 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
                     const int64_t so = o.first, dofs = o.second;
                     if (!inside(p.src + so, V, p.r, in_off, nb))
                         return fail(RA2A_EINVAL, "piece reads outside in of rank %d", p.r);
+                    // the staging is the destination's, or (pull) the sender's own
+                    const int stg_rank = pl.pull ? p.r : p.j;
                     if (pl.direct ? !inside(p.dst + dofs, V, p.j, out_off, nb)
-                                  : !inside(p.dst + dofs, V, p.j, stg_off, pl.ring_bytes))
+                                  : !inside(p.dst + dofs, V, stg_rank, stg_off, pl.ring_bytes))
                         return fail(RA2A_EINVAL, "piece writes outside its destination of rank %d",
-                                    p.j);
+                                    pl.direct ? p.j : stg_rank);
                     std::memcpy(&heap[(size_t)(p.dst + dofs)], &heap[(size_t)(p.src + so)],
                                 (size_t)V);
                 }
@@ -1441,8 +1448,9 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
                 if (rc) return rc;
                 for (const auto& o : offs) {
                     const int64_t so = o.first, dofs = o.second;
-                    if (!inside(q.src + so, V, q.j, stg_off, pl.ring_bytes))
-                        return fail(RA2A_EINVAL, "item reads outside the staging of rank %d", q.j);
+                    const int stg_rank = pl.pull ? q.r0 : q.j;
+                    if (!inside(q.src + so, V, stg_rank, stg_off, pl.ring_bytes))
+                        return fail(RA2A_EINVAL, "item reads outside the staging of rank %d", stg_rank);
                     if (!inside(q.dst + dofs, V, q.j, out_off, nb))
                         return fail(RA2A_EINVAL, "item writes outside out of rank %d", q.j);
                     std::memcpy(&heap[(size_t)(q.dst + dofs)], &heap[(size_t)(q.src + so)],

@@ -241,11 +241,15 @@ RA2A_HD Piece piece_at(const PipeArgs& a, int sid, int b, int r) {
         pl.da = a.H * a.D * e;
     } else if (a.bulk) {
         // bulk staging of destination j: sender r's segment in the input's own
-        // layout, [r][s][h][d], so both sides have rows of H*D elements
+        // layout, [r][s][h][d], so both sides have rows of H*D elements.  Pull:
+        // the sender's own staging [j][s][h][d] in slice r, the same bytes at the
+        // same offset as its input rows for j (a local copy)
         p.src = (int64_t)p.r * a.stride + a.in_off + (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e +
                 st.d0 * e;
-        p.dst = (int64_t)st.j * a.stride + a.stg_off +
-                (((int64_t)p.r * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e;
+        p.dst = a.pull ? (int64_t)p.r * a.stride + a.stg_off +
+                             (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e
+                       : (int64_t)st.j * a.stride + a.stg_off +
+                             (((int64_t)p.r * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e;
         pl.sa = pl.da = a.H * a.D * e;
     } else {
         p.src = (int64_t)p.r * a.stride + a.in_off + (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e +
@@ -348,10 +352,13 @@ RA2A_HD Item item_of(const PipeArgs& a, int g, int64_t it, int V) {
     const int bs = (int)geom_min(a.BS, a.S - s0);
     const int64_t col = ((int64_t)q.r0 * a.H + st.h0) * a.D * e + st.d0 * e;
     // the ring holds rows of the output's layout; the bulk staging (one source
-    // per unit, the SET layout) holds sender r0's rows of H*D elements
-    q.src = a.bulk ? (int64_t)st.j * a.stride + a.stg_off +
+    // per unit, the SET layout) holds sender r0's rows of H*D elements, in slice
+    // j at [r0][s][h][d], or (pull) in sender r0's own slice at [j][s][h][d]
+    q.src = a.pull   ? (int64_t)q.r0 * a.stride + a.stg_off +
+                         (((int64_t)st.j * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e
+            : a.bulk ? (int64_t)st.j * a.stride + a.stg_off +
                          (((int64_t)q.r0 * a.S + s0) * a.H + st.h0) * a.D * e + st.d0 * e
-                   : (int64_t)st.j * a.stride + a.stg_off + (int64_t)q.slot * a.BS * HWDe + col;
+                     : (int64_t)st.j * a.stride + a.stg_off + (int64_t)q.slot * a.BS * HWDe + col;
     q.dst = (int64_t)st.j * a.stride + a.out_off + s0 * HWDe + col;
     RowPlan& pl = q.pl;
     const int64_t head = a.D * e;

@@ -281,7 +281,8 @@ __device__ __forceinline__ bool run_item(const PipeArgs& a, int g, int64_t it, i
         return false;
     if (q.hi > q.lo) {
         if (SYNC == kSyncXcd) {
-            const int64_t stg = (int64_t)q.j * a.stride + a.stg_off;
+            // the staging slice: the destination's, or (pull) the sender's
+            const int64_t stg = (int64_t)(a.pull ? q.r0 : q.j) * a.stride + a.stg_off;
             copy_plan_buf<V, 8, kPolicySc1, true>(make_rsrc_uniform(base + stg, (uint32_t)a.ring_bytes),
                                                   (uint32_t)(q.src - stg), base + q.dst, q.pl, q.lo,
                                                   q.hi);

@@ -54,6 +54,7 @@ struct PipeArgs {
     int32_t direct;     // 1: pieces go straight to out_j, no staging
     int32_t inverse;    // 1: the dispatch (the combine's inverse map), direct mode only
     int32_t bulk;       // 1: staging in the two-phase layout [W][S][H][D], no ring
+    int32_t pull;       // 1 (with bulk): the staging lives in the sender's slice, [j][S][H][D]
     int32_t straggler;  // delayed source rank or -1
     uint32_t delay;     // busy-loop base n0
     uint64_t seed;      // SplitMix64 seed of the delays

@@ -16,8 +16,8 @@ def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):
     nbs = math.ceil(S / opts.tile_s)
     nhb = math.ceil(H / opts.tile_h)
     ndb = math.ceil(D / opts.tile_d)
-    direct = opts.mode not in (ra2a.MODE_STAGED, ra2a.MODE_BULK)
-    bulk = opts.mode == ra2a.MODE_BULK  # staged, but no ring: data signals only
+    direct = opts.mode not in (ra2a.MODE_STAGED, ra2a.MODE_BULK, ra2a.MODE_PULL)
+    bulk = opts.mode in (ra2a.MODE_BULK, ra2a.MODE_PULL)  # staged, but no ring: data signals only
     R = nbs if (direct or bulk) else min(opts.ring or 8, nbs)
     if direct:
         csplit = 1

@@ -159,11 +159,14 @@ def test_emulated_dispatch_matches_oracle(W, S, H, D, dtype, tile, head_merge):
         assert not sigs[r][len(exp):].any()
 
 
-def test_dispatch_rejects_staged_mode():
-    opts = ra2a.Opts(direction=ra2a.DIR_DISPATCH, mode=ra2a.MODE_STAGED)
+@pytest.mark.parametrize("mode", [ra2a.MODE_STAGED, ra2a.MODE_BULK, ra2a.MODE_PULL])
+def test_dispatch_rejects_staged_mode(mode):
+    opts = ra2a.Opts(direction=ra2a.DIR_DISPATCH, mode=mode)
     with pytest.raises(ra2a.Ra2aError) as e:
         ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", opts)
     assert e.value.code == ra2a.EINVAL
+    with pytest.raises(ra2a.Ra2aError):
+        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", ra2a.Opts(mode=5))
     with pytest.raises(ra2a.Ra2aError):
         ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", ra2a.Opts(direction=2))
 
@@ -172,12 +175,14 @@ def test_dispatch_rejects_staged_mode():
 
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring,csplit,lookahead", CASES)
 @pytest.mark.parametrize("cus,per_cu", [(256, 2), (8, 1)])
+@pytest.mark.parametrize("mode", [ra2a.MODE_BULK, ra2a.MODE_PULL])
 def test_emulated_bulk_matches_oracle(W, S, H, D, dtype, tile, proto, ring, csplit, lookahead,
-                                      cus, per_cu):
-    """Every sender's segment lands in the [W][S][H][D] staging, each consumer
-    unit waits only for its (S-block, sender) signal, and the bytes equal the
-    oracle's; every region-A slot ends at 1 and there is no region B."""
-    opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2], mode=ra2a.MODE_BULK,
+                                      cus, per_cu, mode):
+    """Every sender's segment lands in the [W][S][H][D] staging (the receiver's,
+    or in pull mode the sender's own), each consumer unit waits only for its
+    (S-block, sender) signal, and the bytes equal the oracle's; every region-A
+    slot ends at 1 and there is no region B."""
+    opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2], mode=mode,
                      consumer_split=csplit, lookahead=lookahead, wg_per_cu=per_cu)
     nt, nc, _ = ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)
     assert nc == 0 and nt == W * -(-S // tile[0]) * -(-H // tile[1]) * -(-D // tile[2])
@@ -187,10 +192,11 @@ def test_emulated_bulk_matches_oracle(W, S, H, D, dtype, tile, proto, ring, cspl
     check_emulation(W, S, H, D, dtype, opts, csplit, seed=S + W + 1, cus=cus, per_cu=per_cu)
 
 
-def test_bulk_staging_over_4gib_needs_agent_sync():
+@pytest.mark.parametrize("mode", [ra2a.MODE_BULK, ra2a.MODE_PULL])
+def test_bulk_staging_over_4gib_needs_agent_sync(mode):
     big = (16, 16384, 32, 128, "f32")  # 16 senders x 16384 x 32 x 128 x 4 B = 4 GiB per slice
     with pytest.raises(ra2a.Ra2aError) as e:
-        ra2a.rev_all2all_signal_slots(*big, ra2a.Opts(mode=ra2a.MODE_BULK))
+        ra2a.rev_all2all_signal_slots(*big, ra2a.Opts(mode=mode))
     assert e.value.code == ra2a.EINVAL and "agent_sync" in str(e.value)
-    nt, nc, _ = ra2a.rev_all2all_signal_slots(*big, ra2a.Opts(mode=ra2a.MODE_BULK, agent_sync=1))
+    nt, nc, _ = ra2a.rev_all2all_signal_slots(*big, ra2a.Opts(mode=mode, agent_sync=1))
     assert nc == 0

@@ -26,6 +26,7 @@ def expected_signal_array(wl, opts, csplit):
 
 
 TAKEN = 1 << 63
+QUEUED = (ra2a.MODE_STAGED, ra2a.MODE_BULK, ra2a.MODE_PULL)  # modes with work queues
 
 
 def check_queue_words(q, opts):
@@ -34,7 +35,7 @@ def check_queue_words(q, opts):
     moved; every group is marked fully claimed.  Direct mode: untouched."""
     q = q.astype(np.uint64)
     assert len(q) == ra2a.QUEUE_SLOTS == 18
-    if opts.mode not in (ra2a.MODE_STAGED, ra2a.MODE_BULK):
+    if opts.mode not in QUEUED:
         # the direct mode runs a static schedule: no queue words are touched
         assert not q.any(), q
         return
@@ -42,7 +43,7 @@ def check_queue_words(q, opts):
     for g, (head, taker) in enumerate(q[:16].reshape(8, 2)):
         head, taker = int(head), int(taker)
         if head & TAKEN:
-            assert not opts.agent_sync and opts.mode in (ra2a.MODE_STAGED, ra2a.MODE_BULK), \
+            assert not opts.agent_sync and opts.mode in QUEUED, \
                 f"group {g} taken over, but only the staged XCD-local mode binds groups to XCDs"
             assert 1 <= (head >> 32) & 0xFF <= 8 and taker >= 1, (g, hex(head), taker)
         else:
@@ -121,10 +122,12 @@ def test_small_staged_agent_sync(W, S, H, D, dtype, tile, proto, ring):
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
 @pytest.mark.parametrize("knobs", [dict(consumer_split=1), dict(consumer_split=2, lookahead=2),
                                    dict(consumer_split=1, agent_sync=1)])
-def test_small_bulk(W, S, H, D, dtype, tile, proto, ring, knobs):
-    """Two-phase layout with per-(S-block, sender) signals."""
+@pytest.mark.parametrize("mode", [ra2a.MODE_BULK, ra2a.MODE_PULL])
+def test_small_bulk(W, S, H, D, dtype, tile, proto, ring, knobs, mode):
+    """Two-phase layout with per-(S-block, sender) signals; staged at the receiver
+    (bulk) or at the sender and pulled by the receiver (pull)."""
     wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S + 5, tile=tile, protocol=proto)
-    opts = opts_for(wl, mode=ra2a.MODE_BULK, **knobs)
+    opts = opts_for(wl, mode=mode, **knobs)
     run_and_check(wl, opts, csplit=knobs["consumer_split"])
 
 
@@ -236,7 +239,7 @@ def test_direct_reset_clears_dirty_signals(reset):
         case.close()
 
 
-@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED, ra2a.MODE_BULK])
+@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED, ra2a.MODE_BULK, ra2a.MODE_PULL])
 def test_straggler_timestamps(mode):
     """Per-tile completion clocks under a delayed source: every tile is stamped
     (garbage left in the stamp array is cleared by the combine), and under SET
@@ -310,27 +313,27 @@ def full_case(name, variant, **kw):
         say(f"[full] oracle {name}")
         _FULL_CACHE[name] = (ins, oracle.combine(ins))
     ins, want = _FULL_CACHE[name]
-    if variant in ("staged", "bulk"):
-        kw["mode"] = ra2a.MODE_STAGED if variant == "staged" else ra2a.MODE_BULK
+    if variant in ("staged", "bulk", "pull"):
+        kw["mode"] = {"staged": ra2a.MODE_STAGED, "bulk": ra2a.MODE_BULK, "pull": ra2a.MODE_PULL}[variant]
         variant = "pipelined"
     else:
         kw.pop("consumer_split", None)
     opts = opts_for(wl, consumer_split=kw.pop("consumer_split", 1), **kw)
     run_and_check(wl, opts, variant=variant, inputs=ins, want=want,
-                  csplit=None if opts.mode in (ra2a.MODE_STAGED, ra2a.MODE_BULK) else 1)
+                  csplit=None if opts.mode in QUEUED else 1)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "pull", "two_phase"])
 def test_full_ep_combine_w8_bf16(variant):
     full_case("ep_combine_w8_s512_h16_d128_bf16", variant)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "pull", "two_phase"])
 def test_full_moe_combine_w8_d7168(variant):
     full_case("moe_combine_w8_s4096_h1_d7168_bf16", variant, consumer_split=4)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "pull", "two_phase"])
 def test_full_straggler_w16_f32(variant):
     wl = synthgen.WORKLOADS["straggler_w16_s2048_h32_d128_f32"]
     full_case("straggler_w16_s2048_h32_d128_f32", variant,
