@@ -21,7 +21,9 @@ Contents and the passages they follow:
 * ``signal_apply`` / ``compare``: section 2.3 (SignalOp SET / ADD) and section
   6.3 (the six wait predicates) of the same page.
 * ``protocol``: the producer/consumer signal protocol (see its docstring).
-* ``gemm``: the fp64 AllGather+GEMM.
+* ``gemm``: the fp64 AllGather+GEMM and GEMM+ReduceScatter.
+* ``alltoallv``: the variable-size AllToAll (the HyperParallel RFC, section 十,
+  "AllToAll (Push mode)"), read as the frameworks' split-size all-to-all.
 
 Pins (what ties these to something other than themselves) live in
 ``tests/test_oracle_*.py`` and run with ``-m "not gpu"``.
@@ -34,7 +36,7 @@ from typing import List, Sequence
 
 import numpy as np
 
-from . import gemm, protocol  # noqa: F401
+from . import alltoallv, gemm, protocol  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "_oracle.so")

@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the Reverse All2All combine and the AllGather+GEMM workload.
+"""Seeded synthetic inputs for the Reverse All2All combine, the AllGather+GEMM and
+GEMM+ReduceScatter workloads and the variable-size AllToAll.
 
 This module holds the workload definitions (shapes, element types, value
 distributions, seeds and tiling) and the generators that turn them into host
@@ -262,3 +263,47 @@ def make_gemm_rs_inputs(wl: GemmRsWorkload = GEMM_RS, m: Optional[int] = None,
     a = [draw(ga, (m, K)) for _ in range(W)]
     bt = [draw(gb, (N, K)) for _ in range(W)]
     return a, bt
+
+
+@dataclasses.dataclass(frozen=True)
+class AllToAllvWorkload:
+    """Variable-size AllToAll: rank r holds `rows` rows of `row_bytes` bytes and
+    sends send_counts[r][j] of them to rank j, the counts of each rank a
+    multinomial draw over the W destinations with Dirichlet(alpha) weights (the
+    uneven token-to-expert routing of an MoE dispatch)."""
+
+    name: str
+    W: int
+    rows: int
+    row_bytes: int
+    seed: int
+    alpha: float
+
+
+# MoE-shaped: 32768 rows of 7168 bf16 per rank (the same bytes per rank as the
+# W=8, S=4096, H=1, D=7168 combine), routed unevenly.
+ALLTOALLV = AllToAllvWorkload("alltoallv_w8_rows32768_row14336B", W=8, rows=32768,
+                              row_bytes=7168 * 2, seed=12, alpha=4.0)
+
+
+def make_alltoallv_counts(W: int, rows: int, seed: int, alpha: float = 4.0,
+                          empty_pairs: int = 0) -> np.ndarray:
+    """send_counts (W x W int64): row r sums to `rows`; `empty_pairs` (r, j) pairs,
+    chosen by the same generator, are forced to 0 (their rows go to the next
+    destination)."""
+    rng = np.random.default_rng(seed)
+    c = np.zeros((W, W), dtype=np.int64)
+    for r in range(W):
+        p = rng.dirichlet(np.full(W, alpha))
+        c[r] = rng.multinomial(rows, p)
+    for _ in range(empty_pairs):
+        r, j = int(rng.integers(0, W)), int(rng.integers(0, W))
+        c[r, (j + 1) % W] += c[r, j]
+        c[r, j] = 0
+    return c
+
+
+def make_alltoallv_inputs(W: int, rows: int, row_bytes: int, seed: int) -> List[np.ndarray]:
+    """W arrays of (rows, row_bytes) uniform random bytes, rank 0 first."""
+    rng = np.random.default_rng(seed + 1000)
+    return [rng.integers(0, 256, size=(rows, row_bytes), dtype=np.uint8) for _ in range(W)]
