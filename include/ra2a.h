@@ -38,6 +38,7 @@ extern "C" {
 #define RA2A_EHIP (-3)         /* a HIP runtime call failed (message has the HIP error) */
 #define RA2A_ETIMEOUT (-4)     /* a bounded device-side wait gave up */
 #define RA2A_EUNSUPPORTED (-5) /* combination not implemented */
+#define RA2A_EDATA (-6)        /* a device-side check of device-resident data failed */
 
 /* ---- signal operations ----------------------------------------------------
  * "Distributed Architecture Design", section 2.3 (SignalOp SET / ADD) and the
@@ -470,9 +471,62 @@ int ra2a_gemm_rs(const void *x1, const void *x2t, void *partial, void *out, uint
 int ra2a_debug_gemm_rs_plan(int W, int64_t m, int64_t K, int64_t N, int num_xcd,
                             int64_t *tasks_per_group);
 
+/* ---- variable-size AllToAll (push) ------------------------------------------ */
+/* (HyperParallel RFC, section 十, "AllToAll (Push mode)".)  The split-size
+ * all-to-all: rank r's input is rows of row_bytes bytes cut, in destination
+ * order, into segments of send_counts_r[j] rows; rank j receives the
+ * concatenation, in source order r = 0 .. W-1, of the segments addressed to it.
+ * As on the page, the ranks first exchange metadata -- each sender puts its
+ * count into the destination's recv_counts and adds 1 to its count signal; each
+ * destination, once that reads W, hands every sender the row where its segment
+ * goes -- then every sender pushes its segments (in the rotation j = (r + t) mod
+ * W, t = 0 .. W-1, cut into chunks of chunk_bytes), and each destination's
+ * arrival signal accumulates to W.  One launch: the counts stay on the device,
+ * with no host round trip between metadata and data.  W <= 32.                */
+#define RA2A_A2V_SKIP_RESET 1 /* the caller zeroed the signals; no reset launch */
+
+/* Signal slots per slice (at 128-byte spacing): 2W + 3.  Errors: EINVAL.      */
+int ra2a_alltoallv_signal_slots(int W, int64_t *slots);
+
+/* All five buffers are symmetric, inside one heap of W slices, at these
+ * offsets in every slice:
+ *   in          slice r: in_rows rows of row_bytes bytes (16-byte aligned);
+ *   send_counts slice r: int64[W], rows rank r sends to each rank (8-byte aligned;
+ *               device memory, read by the kernel);
+ *   out         slice j: out_rows rows of row_bytes bytes (16-byte aligned);
+ *   recv_counts slice j: int64[W + 1]: [r] = rows received from rank r, [W] = the
+ *               total, written once every segment has arrived (8-byte aligned);
+ *   signals     slice j: ra2a_alltoallv_signal_slots' slots (8-byte aligned).
+ * chunk_bytes: bytes per data task (0: 256 KiB; else a positive multiple of 16).
+ * The signals are zeroed by a reset launch first unless RA2A_A2V_SKIP_RESET.
+ * Checked on the device (ra2a_check then reports RA2A_EDATA): a sender with a
+ * negative count, or more rows in total than in_rows, sends nothing (its counts
+ * read as 0); a segment that would run past out_rows is not copied.  Either way
+ * every signal still completes, so nothing waits out a timeout.  Afterwards the
+ * count and arrival signals of every slice read W.  The library owns the
+ * buffers until the stream reaches the end of the launch.
+ * Errors: EINVAL (shapes, flags, alignment, overlap, a buffer outside the heap
+ * or crossing the end of a slice), EHIP.                                     */
+int ra2a_alltoallv(const void *in, const int64_t *send_counts, void *out, int64_t *recv_counts,
+                   uint64_t *signals, int W, int64_t row_bytes, int64_t in_rows, int64_t out_rows,
+                   int64_t chunk_bytes, int flags, void *stream);
+
+/* Host emulation (no GPU needed) of the AllToAll's work queue, run strictly in
+ * queue order with the kernel's own decode: in[r] and out[j] are host arrays
+ * of in_rows / out_rows rows, send_counts W x W (row r = rank r's counts),
+ * recv_counts W x (W + 1), signals W x (2W + 3) final slot values, *err_word
+ * receives the device error bits.  Returns EINVAL if a task would wait for one
+ * queued after it or a segment's chunks are not each queued once; *tasks
+ * (optional) receives the queue length.                                      */
+int ra2a_debug_alltoallv_emulate(int W, int64_t row_bytes, int64_t in_rows, int64_t out_rows,
+                                 int64_t chunk_bytes, const void *const *in,
+                                 const int64_t *send_counts, void *const *out, int64_t *recv_counts,
+                                 uint64_t *signals, uint32_t *err_word, int64_t *tasks);
+
 /* ---- diagnostics --------------------------------------------------------- */
 
 /* Wait for the device, then report and clear the heap's device error word:
+ * RA2A_EDATA if a device-side data check failed (the AllToAll's counts),
  * RA2A_ETIMEOUT if a bounded wait gave up since the last check, RA2A_EHIP if
  * the device reported an error, else RA2A_OK.                                  */
 int ra2a_check(const ra2a_heap_t *heap);

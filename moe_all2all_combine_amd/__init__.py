@@ -17,7 +17,7 @@ from typing import Optional, Sequence, Tuple
 
 __all__ = [
     "Ra2aError", "Opts", "SymmHeap", "lib", "OK", "EINVAL", "ENOMEM", "EHIP", "ETIMEOUT",
-    "EUNSUPPORTED", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "MODE_DIRECT", "MODE_STAGED",
+    "EUNSUPPORTED", "EDATA", "A2V_SKIP_RESET", "alltoallv_signal_slots", "alltoallv", "debug_alltoallv_emulate", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "MODE_DIRECT", "MODE_STAGED",
     "QUEUE_SLOTS", "RS_AGENT_SYNC", "RS_SKIP_RESET", "RS_BF16_PARTIALS", "gemm_rs_sizes", "gemm_rs", "debug_gemm_rs_plan", "MODE_BULK", "MODE_PULL", "DIR_COMBINE", "DIR_DISPATCH", "all2all_dispatch", "all2all_dispatch_ex", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
     "CMP_LE", "SIG_STRIDE_BYTES", "DTYPES", "symm_heap_create", "symm_heap_attach",
     "symm_heap_destroy", "symm_malloc", "symm_heap_info", "symm_at", "put", "get",
@@ -31,7 +31,7 @@ __all__ = [
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libra2a.so")
 
-OK, EINVAL, ENOMEM, EHIP, ETIMEOUT, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+OK, EINVAL, ENOMEM, EHIP, ETIMEOUT, EUNSUPPORTED, EDATA = 0, -1, -2, -3, -4, -5, -6
 SIG_SET, SIG_ADD = 0, 1
 PROTO_ADD, PROTO_SET = 1, 2
 MODE_DIRECT, MODE_STAGED = 1, 2
@@ -128,6 +128,12 @@ def lib():
                                      ctypes.POINTER(i64), ctypes.POINTER(sz)]),
         "ra2a_gemm_rs": (i32, [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp]),
         "ra2a_debug_gemm_rs_plan": (i32, [i32, i64, i64, i64, i32, ctypes.POINTER(i64)]),
+        "ra2a_alltoallv_signal_slots": (i32, [i32, ctypes.POINTER(i64)]),
+        "ra2a_alltoallv": (i32, [vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, vp]),
+        "ra2a_debug_alltoallv_emulate": (i32, [i32, i64, i64, i64, i64, ctypes.POINTER(vp),
+                                               ctypes.POINTER(i64), ctypes.POINTER(vp),
+                                               ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_uint64),
+                                               ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(i64)]),
         "ra2a_debug_emulate_pipelined": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp),
                                                ctypes.POINTER(vp), i32, i64, i64, i64, i32, vp,
                                                i32, i32]),
@@ -249,7 +255,7 @@ def signal_reset(heap: int, sig_sym: int, n_slots: int, stream=None) -> None:
 
 
 def check(heap: int) -> int:
-    """Status of the heap's device-side waits (RA2A_OK or RA2A_ETIMEOUT), without raising."""
+    """Status of the heap's device-side checks (RA2A_OK, RA2A_ETIMEOUT or RA2A_EDATA), without raising."""
     return lib().ra2a_check(heap)
 
 
@@ -423,3 +429,46 @@ def debug_gemm_rs_plan(W: int, m: int, K: int, N: int, num_xcd: int = 8) -> int:
     n = ctypes.c_int64()
     _ok(lib().ra2a_debug_gemm_rs_plan(W, m, K, N, num_xcd, ctypes.byref(n)))
     return n.value
+
+
+# ---- variable-size AllToAll -------------------------------------------------------
+
+A2V_SKIP_RESET = 1
+
+
+def alltoallv_signal_slots(W: int) -> int:
+    n = ctypes.c_int64()
+    _ok(lib().ra2a_alltoallv_signal_slots(W, ctypes.byref(n)))
+    return n.value
+
+
+def alltoallv(inp: int, send_counts: int, out: int, recv_counts: int, signals: int, W: int,
+              row_bytes: int, in_rows: int, out_rows: int, chunk_bytes: int = 0, flags: int = 0,
+              stream=None) -> None:
+    """Split-size all-to-all of rows: out_j = concat over r of rank r's segment for j."""
+    _ok(lib().ra2a_alltoallv(inp, send_counts, out, recv_counts, signals, W, row_bytes, in_rows,
+                             out_rows, chunk_bytes, flags, _stream(stream)))
+
+
+def debug_alltoallv_emulate(ins, send_counts, out_rows: int, chunk_bytes: int = 0):
+    """Host emulation of the AllToAll's queue: (outs, recv_counts, signals, error bits, tasks).
+
+    ins: W uint8 arrays (in_rows, row_bytes); send_counts: W x W integers."""
+    import numpy as np
+    W = len(ins)
+    in_rows, row_bytes = ins[0].shape
+    ins = [np.ascontiguousarray(x, dtype=np.uint8) for x in ins]
+    outs = [np.zeros((out_rows, row_bytes), dtype=np.uint8) for _ in range(W)]
+    cnt = np.ascontiguousarray(np.asarray(send_counts, dtype=np.int64).reshape(W, W))
+    rc = np.zeros((W, W + 1), dtype=np.int64)
+    sig = np.zeros((W, 2 * W + 3), dtype=np.uint64)
+    err = ctypes.c_uint32()
+    tasks = ctypes.c_int64()
+    ip = (ctypes.c_void_p * W)(*[x.ctypes.data for x in ins])
+    op = (ctypes.c_void_p * W)(*[x.ctypes.data for x in outs])
+    _ok(lib().ra2a_debug_alltoallv_emulate(
+        W, row_bytes, in_rows, out_rows, chunk_bytes, ip,
+        cnt.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), op,
+        rc.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        sig.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), ctypes.byref(err), ctypes.byref(tasks)))
+    return outs, rc, sig, err.value, tasks.value

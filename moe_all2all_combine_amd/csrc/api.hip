@@ -1188,6 +1188,184 @@ RA2A_API int ra2a_debug_gemm_rs_plan(int W, int64_t m, int64_t K, int64_t N, int
     return ok();
 }
 
+// ===========================================================================
+// Variable-size AllToAll
+
+namespace {
+
+constexpr int64_t kA2vDefaultChunk = 256 << 10;
+
+int check_a2v_shape(int W, int64_t row_bytes, int64_t in_rows, int64_t out_rows, int64_t* chunk) {
+    if (W < 1 || W > ra2a::kA2vMaxW) return fail(RA2A_EINVAL, "W must be in 1..%d", ra2a::kA2vMaxW);
+    if (row_bytes < 1) return fail(RA2A_EINVAL, "row_bytes must be >= 1");
+    if (in_rows < 0 || out_rows < 0) return fail(RA2A_EINVAL, "row capacities must be >= 0");
+    if ((double)in_rows * row_bytes >= 4.6e18 || (double)out_rows * row_bytes >= 4.6e18)
+        return fail(RA2A_EINVAL, "buffers too large");
+    if (*chunk == 0) *chunk = kA2vDefaultChunk;
+    if (*chunk < 16 || *chunk % 16) return fail(RA2A_EINVAL, "chunk_bytes must be a positive multiple of 16");
+    // the queue positions of one launch: 3W + the chunks of every segment (each at most in_rows rows)
+    const double chunks = (double)W * W * ((double)in_rows * row_bytes / (double)*chunk + 1.0);
+    if (3.0 * W + chunks >= 9.0e18) return fail(RA2A_EINVAL, "too many chunks");
+    return RA2A_OK;
+}
+
+int a2v_vector(int64_t row_bytes) { return row_bytes % 16 == 0 ? 16 : row_bytes % 4 == 0 ? 4 : 1; }
+
+}  // namespace
+
+RA2A_API int ra2a_alltoallv_signal_slots(int W, int64_t* slots) {
+    if (W < 1 || W > ra2a::kA2vMaxW) return fail(RA2A_EINVAL, "W must be in 1..%d", ra2a::kA2vMaxW);
+    if (slots) *slots = ra2a::a2v_slots(W);
+    return ok();
+}
+
+RA2A_API int ra2a_alltoallv(const void* in, const int64_t* send_counts, void* out, int64_t* recv_counts,
+                            uint64_t* signals, int W, int64_t row_bytes, int64_t in_rows,
+                            int64_t out_rows, int64_t chunk_bytes, int flags, void* stream) {
+    if (flags & ~RA2A_A2V_SKIP_RESET) return fail(RA2A_EINVAL, "unknown flags");
+    if (!in || !send_counts || !out || !recv_counts || !signals) return fail(RA2A_EINVAL, "NULL pointer");
+    int64_t chunk = chunk_bytes;
+    int rc = check_a2v_shape(W, row_bytes, in_rows, out_rows, &chunk);
+    if (rc) return rc;
+    ra2a_heap* h = find_heap(in);
+    if (!h) return fail(RA2A_EINVAL, "in is not inside a symmetric heap");
+    if (h->world != W) return fail(RA2A_EINVAL, "W=%d but the heap has %d slices", W, h->world);
+    if (!in_heap(h, send_counts) || !in_heap(h, out) || !in_heap(h, recv_counts) || !in_heap(h, signals))
+        return fail(RA2A_EINVAL, "send_counts, out, recv_counts and signals must be inside the heap of in");
+    const size_t offs[5] = {sym_offset(h, in), sym_offset(h, send_counts), sym_offset(h, out),
+                            sym_offset(h, recv_counts), sym_offset(h, signals)};
+    const size_t lens[5] = {(size_t)(in_rows * row_bytes), (size_t)W * 8u, (size_t)(out_rows * row_bytes),
+                            (size_t)(W + 1) * 8u, (size_t)ra2a::a2v_slots(W) * RA2A_SIG_STRIDE_BYTES};
+    if (offs[0] % 16 || offs[2] % 16) return fail(RA2A_EINVAL, "in and out must be 16-byte aligned");
+    if (offs[1] % 8 || offs[3] % 8 || offs[4] % 8)
+        return fail(RA2A_EINVAL, "send_counts, recv_counts and signals must be 8-byte aligned");
+    for (int i = 0; i < 5; ++i) {
+        if (offs[i] + lens[i] > h->stride)
+            return fail(RA2A_EINVAL, "a buffer crosses the end of a slice");
+        for (int k = 0; k < i; ++k)
+            if (lens[i] && lens[k] && offs[i] < offs[k] + lens[k] && offs[k] < offs[i] + lens[i])
+                return fail(RA2A_EINVAL, "in, send_counts, out, recv_counts and signals must not overlap");
+    }
+    rc = ensure_err(h);
+    if (rc) return rc;
+    ra2a::A2vArgs a{};
+    a.base = h->base;
+    a.stride = (int64_t)h->stride;
+    a.in_off = (int64_t)offs[0];
+    a.cnt_off = (int64_t)offs[1];
+    a.out_off = (int64_t)offs[2];
+    a.rc_off = (int64_t)offs[3];
+    a.sig_off = (int64_t)offs[4];
+    a.err = h->err;
+    a.timeout = timeout_ticks(h);
+    a.W = W;
+    a.row_bytes = row_bytes;
+    a.in_rows = in_rows;
+    a.out_rows = out_rows;
+    a.chunk = chunk;
+    const int V = a2v_vector(row_bytes);
+    int ncu = 0;
+    rc = device_cus(&ncu);
+    if (rc) return rc;
+    int occ = 0;
+    hipError_t he = ra2a::alltoallv_blocks_per_cu(V, &occ);
+    if (he != hipSuccess) return hip_fail(he, "occupancy query");
+    if (occ < 1) return fail(RA2A_EUNSUPPORTED, "the AllToAll kernel does not fit a compute unit");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!(flags & RA2A_A2V_SKIP_RESET)) {
+        he = ra2a::launch_signal_reset(h->base, (int64_t)h->stride, W, (int64_t)offs[4],
+                                       ra2a::a2v_slots(W), st);
+        if (he != hipSuccess) return hip_fail(he, "signal reset launch");
+    }
+    he = ra2a::launch_alltoallv(a, V, std::min(occ, 4) * ncu, st);
+    if (he != hipSuccess) return hip_fail(he, "AllToAll launch");
+    return ok();
+}
+
+RA2A_API int ra2a_debug_alltoallv_emulate(int W, int64_t row_bytes, int64_t in_rows, int64_t out_rows,
+                                          int64_t chunk_bytes, const void* const* in,
+                                          const int64_t* send_counts, void* const* out,
+                                          int64_t* recv_counts, uint64_t* signals, uint32_t* err_word,
+                                          int64_t* tasks) {
+    int64_t chunk = chunk_bytes;
+    int rc = check_a2v_shape(W, row_bytes, in_rows, out_rows, &chunk);
+    if (rc) return rc;
+    if (!in || !send_counts || !out || !recv_counts || !signals || !err_word)
+        return fail(RA2A_EINVAL, "NULL pointer");
+    const int n = W * W;
+    const int64_t S = ra2a::a2v_slots(W);
+    // the kernel's own decode: usable counts, chunk table, queue positions
+    std::vector<int64_t> cnt(send_counts, send_counts + n);
+    std::vector<int> rank_ok((size_t)W);
+    for (int r = 0; r < W; ++r) rank_ok[(size_t)r] = ra2a::a2v_rank_ok(W, in_rows, cnt.data() + r * W) ? 1 : 0;
+    for (int i = 0; i < n; ++i)
+        if (!rank_ok[(size_t)(i / W)]) cnt[(size_t)i] = 0;
+    std::vector<int64_t> first((size_t)n + 1, 0);
+    for (int p = 0; p < n; ++p) {
+        const int r = p / W;
+        first[(size_t)p + 1] = first[(size_t)p] +
+                               ra2a::a2v_chunks(cnt[(size_t)(r * W + ra2a::a2v_dest(W, r, p - r * W))], row_bytes, chunk);
+    }
+    std::memset(signals, 0, sizeof(uint64_t) * (size_t)(W * S));
+    auto sig = [&](int slice, int64_t slot) -> uint64_t& { return signals[(size_t)(slice * S + slot)]; };
+    const int64_t total = ra2a::a2v_total(W, first.data());
+    std::vector<int64_t> seen_chunks((size_t)n, 0);
+    for (int64_t pos = 0; pos < total; ++pos) {
+        const ra2a::A2vTask t = ra2a::a2v_task(W, first.data(), pos);
+        if (t.kind == 0) {
+            for (int j = 0; j < W; ++j) recv_counts[(size_t)(j * (W + 1) + t.r)] = cnt[(size_t)(t.r * W + j)];
+            if (!rank_ok[(size_t)t.r]) *err_word |= ra2a::kErrCounts;
+            for (int j = 0; j < W; ++j) sig(j, ra2a::a2v_count_slot()) += 1;
+        } else if (t.kind == 1) {
+            if (sig(t.j, ra2a::a2v_count_slot()) != (uint64_t)W)
+                return fail(RA2A_EINVAL, "position %lld: offset task of %d waits for counts queued after it",
+                            (long long)pos, t.j);
+            int64_t run = 0;
+            for (int r = 0; r < W; ++r) {
+                sig(r, ra2a::a2v_offset_slot(t.j)) = (uint64_t)run + 1u;
+                run += recv_counts[(size_t)(t.j * (W + 1) + r)];
+            }
+        } else if (t.kind == 2) {
+            if (t.r < 0 || t.r >= W || t.j < 0 || t.j >= W) return fail(RA2A_EINVAL, "chunk task out of range");
+            const uint64_t o = sig(t.r, ra2a::a2v_offset_slot(t.j));
+            if (o == 0)
+                return fail(RA2A_EINVAL, "position %lld: chunk waits for an offset queued after it", (long long)pos);
+            const int64_t rows = cnt[(size_t)(t.r * W + t.j)];
+            const int64_t nch = ra2a::a2v_chunks(rows, row_bytes, chunk);
+            if (t.c < 0 || t.c >= nch || t.c != seen_chunks[(size_t)(t.r * W + t.j)]++)
+                return fail(RA2A_EINVAL, "chunk %lld of (%d, %d) out of order", (long long)t.c, t.r, t.j);
+            const int64_t dst_row = (int64_t)o - 1;
+            if (dst_row >= 0 && rows <= out_rows && dst_row <= out_rows - rows) {
+                int64_t lo, hi;
+                ra2a::a2v_chunk_range(rows, row_bytes, chunk, t.c, &lo, &hi);
+                const int64_t src_row = ra2a::a2v_send_offset(W, cnt.data(), t.r, t.j);
+                std::memcpy(static_cast<uint8_t*>(out[t.j]) + dst_row * row_bytes + lo,
+                            static_cast<const uint8_t*>(in[t.r]) + src_row * row_bytes + lo, (size_t)(hi - lo));
+            } else {
+                *err_word |= ra2a::kErrOverflow;
+            }
+            if (++sig(t.j, ra2a::a2v_chunk_slot(W, t.r)) == (uint64_t)nch) sig(t.j, ra2a::a2v_arrival_slot(W)) += 1;
+        } else if (t.kind == 3) {
+            if (sig(t.j, ra2a::a2v_arrival_slot(W)) != (uint64_t)W)
+                return fail(RA2A_EINVAL, "position %lld: receive task of %d waits for data queued after it",
+                            (long long)pos, t.j);
+            int64_t sum = 0;
+            for (int r = 0; r < W; ++r) sum += recv_counts[(size_t)(t.j * (W + 1) + r)];
+            recv_counts[(size_t)(t.j * (W + 1) + W)] = sum;
+        } else {
+            return fail(RA2A_EINVAL, "position %lld decodes to no task", (long long)pos);
+        }
+    }
+    for (int p = 0; p < n; ++p) {
+        const int r = p / W, j = p % W;
+        if (seen_chunks[(size_t)p] != ra2a::a2v_chunks(cnt[(size_t)p], row_bytes, chunk))
+            return fail(RA2A_EINVAL, "segment (%d, %d): not every chunk queued", r, j);
+    }
+    sig(0, ra2a::a2v_queue_slot(W)) = (uint64_t)total;
+    if (tasks) *tasks = total;
+    return ok();
+}
+
 RA2A_API int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t N,
                                      int tile_rows, int num_xcd, int64_t* tasks_per_group) {
     ra2a::AgGemmArgs a{};
@@ -1256,6 +1434,11 @@ RA2A_API int ra2a_check(const ra2a_heap_t* h) {
     if (w) {
         e = hipMemset(h->err, 0, sizeof w);
         if (e != hipSuccess) return hip_fail(e, "clearing the error word");
+        if (w & (ra2a::kErrCounts | ra2a::kErrOverflow))
+            return fail(RA2A_EDATA, "device-side data check failed (error word 0x%x:%s%s%s)", w,
+                        (w & ra2a::kErrCounts) ? " a sender's counts were unusable" : "",
+                        (w & ra2a::kErrOverflow) ? " a destination received more rows than it holds" : "",
+                        (w & ra2a::kErrTimeout) ? " a bounded wait timed out" : "");
         return fail(RA2A_ETIMEOUT, "a bounded device-side wait timed out (error word 0x%x)", w);
     }
     return ok();

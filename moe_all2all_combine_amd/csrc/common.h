@@ -10,6 +10,8 @@ constexpr int kSigAdd = 1;
 constexpr int kCmpEq = 0, kCmpNe = 1, kCmpGt = 2, kCmpGe = 3, kCmpLt = 4, kCmpLe = 5;
 constexpr int kSigStrideU64 = 16;  // 128-byte signal slots
 constexpr uint32_t kErrTimeout = 1u;
+constexpr uint32_t kErrCounts = 2u;    // AllToAll: a sender's counts were unusable
+constexpr uint32_t kErrOverflow = 4u;  // AllToAll: a destination received more rows than it holds
 constexpr int kSyncXcd = 0;    // producers and consumers of a stream share one XCD's L2
 constexpr int kSyncAgent = 1;  // device-wide release/acquire (L2 write-back / invalidate)
 constexpr int kThreads = 256;      // workgroup size of every copy kernel

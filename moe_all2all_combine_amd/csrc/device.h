@@ -253,7 +253,8 @@ __device__ __forceinline__ void store_nt(T v, T* p) { __builtin_nontemporal_stor
 // Full rounds keep U vectors per thread in flight (all loads, then all
 // stores, no bounds checks so the values stay in registers); the remainder
 // goes one vector at a time.
-template <int V, int U>
+// NT: non-temporal loads and stores (streamed past the caches).
+template <int V, int U, bool NT = false>
 __device__ __forceinline__ void copy_flat(const uint8_t* __restrict__ src,
                                           uint8_t* __restrict__ dst, int64_t bytes, int64_t tid0,
                                           int64_t nthr) {
@@ -265,11 +266,21 @@ __device__ __forceinline__ void copy_flat(const uint8_t* __restrict__ src,
     for (; idx + (U - 1) * nthr < total; idx += U * nthr) {
         T v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = s[idx + u * nthr];
+        for (int u = 0; u < U; ++u) v[u] = NT ? load_nt(s + idx + u * nthr) : s[idx + u * nthr];
 #pragma unroll
-        for (int u = 0; u < U; ++u) d[idx + u * nthr] = v[u];
+        for (int u = 0; u < U; ++u) {
+            if (NT)
+                store_nt(v[u], d + idx + u * nthr);
+            else
+                d[idx + u * nthr] = v[u];
+        }
     }
-    for (; idx < total; idx += nthr) d[idx] = s[idx];
+    for (; idx < total; idx += nthr) {
+        if (NT)
+            store_nt(load_nt(s + idx), d + idx);
+        else
+            d[idx] = s[idx];
+    }
 }
 
 // SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "ag_gemm_geom.h"
+#include "alltoallv_geom.h"
 #include "gemm_rs_geom.h"
 #include "common.h"
 
@@ -20,6 +21,8 @@ hipError_t launch_two_phase(const TwoPhaseArgs& a, int V, hipStream_t st);
 hipError_t launch_ag_gemm(const AgGemmArgs& a, int grid, hipStream_t st);
 hipError_t launch_gemm_rs(const GemmRsArgs& a, int grid, hipStream_t st);
 hipError_t gemm_rs_blocks_per_cu(int sync, bool f32p, int* n);
+hipError_t launch_alltoallv(const A2vArgs& a, int V, int grid, hipStream_t st);
+hipError_t alltoallv_blocks_per_cu(int V, int* n);
 hipError_t ag_gemm_blocks_per_cu(int sync, int* n);
 hipError_t launch_transpose_b(const uint16_t* b, uint16_t* bt, int64_t K, int64_t N, hipStream_t st);
 

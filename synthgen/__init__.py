@@ -306,4 +306,5 @@ def make_alltoallv_counts(W: int, rows: int, seed: int, alpha: float = 4.0,
 def make_alltoallv_inputs(W: int, rows: int, row_bytes: int, seed: int) -> List[np.ndarray]:
     """W arrays of (rows, row_bytes) uniform random bytes, rank 0 first."""
     rng = np.random.default_rng(seed + 1000)
-    return [rng.integers(0, 256, size=(rows, row_bytes), dtype=np.uint8) for _ in range(W)]
+    return [np.frombuffer(rng.bytes(rows * row_bytes), dtype=np.uint8).reshape(rows, row_bytes).copy()
+            for _ in range(W)]
