@@ -80,6 +80,27 @@ __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_b
     }
 }
 
+// One of the kDmaPerStage LDS loads of stage_load: part p = 2 i + (0: A, 1: B).
+template <int P>
+__device__ __forceinline__ void stage_load_part(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                                uint16_t* lds_a, uint16_t* lds_b, int64_t K,
+                                                int64_t k0) {
+    static_assert(P >= 0 && P < kDmaPerStage, "stage_load has kDmaPerStage parts");
+    const int w = (int)threadIdx.x >> 6;
+    const int l = (int)threadIdx.x & 63;
+    const int rbase = kRowsPerWave * w + 16 * (P >> 1);
+    const int row = rbase + (l >> 2);
+    const int c = swz(row, l & 3);
+    const int64_t k = k0 + 8 * c;
+    const uint32_t off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : kOutOfRange;
+    if (P & 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(lds_b + rbase * kStageK), 16, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(lds_a + rbase * kStageK), 16, off, 0, 0, 0);
+}
+
 // Wait until at most n of this wave's vector memory operations are outstanding
 // (they complete in issue order): the LDS loads of the stages issued after the
 // one about to be read.
@@ -151,6 +172,25 @@ __device__ __forceinline__ void read_frags(Frags& f, uint32_t a_addr, uint32_t b
     f.b[3] = lds_read16<3 * kBlk>(b_addr);
 }
 
+// Fragment I of read_frags alone (0, 1: A blocks; 2 .. 5: B blocks).
+template <int I>
+__device__ __forceinline__ void read_frag(Frags& f, uint32_t a_addr, uint32_t b_addr) {
+    constexpr int kBlk = 32 * kStageK * 2;
+    if (I < kBlkA)
+        f.a[I < kBlkA ? I : 0] = lds_read16<(I < kBlkA ? I : 0) * kBlk>(a_addr);
+    else
+        f.b[I >= kBlkA ? I - kBlkA : 0] = lds_read16<(I >= kBlkA ? I - kBlkA : 0) * kBlk>(b_addr);
+}
+
+// MFMA I of mma_frags alone (block x = I / kBlkB, y = I mod kBlkB).
+template <int I>
+__device__ __forceinline__ void mma_one(f32x16 (&acc)[kBlkA][kBlkB], const Frags& f) {
+    constexpr int x = I / kBlkB, y = I % kBlkB;
+    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
+}
+
+__device__ __forceinline__ void sb() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Frags& f) {
 #pragma unroll
     for (int x = 0; x < kBlkA; ++x)
@@ -179,18 +219,25 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
         for (int y = 0; y < kBlkB; ++y) acc[x][y] = f32x16{};
     const int64_t nk = (K + kStageK - 1) / kStageK;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only this tile's LDS loads in flight below
+    // Stage s lives in slot s mod kStages; only stages that exist are loaded.
     for (int64_t s = 0; s < nk && s < kStages - 1; ++s) {
-        uint16_t* st = lds + (s % kStages) * 2 * kStageElems;
+        uint16_t* st = lds + s * 2 * kStageElems;
         stage_load(ra, rb, st, st + kStageElems, K, s * kStageK);
     }
     // Software pipeline over stages, one stage of LDS loads ahead of the reads:
-    //   read f1(s) | MFMAs of f0(s) | wait stage s+1, barrier, refill the slot of
-    //   stage s with stage s+4, read f0(s+1) | MFMAs of f1(s)
-    // so the LDS latency of each half hides under the other half's MFMAs.  A
+    //   MFMAs of f0(s), each followed by one read of f1(s) | wait for f1(s),
+    //   wait for stage s+1, barrier | MFMAs of f1(s), each followed by one LDS
+    //   load refilling the slot of stage s with stage s+4 or one read of f0(s+1)
+    // so the LDS latency of each half hides under the other half's MFMAs, and the
+    // memory instructions issue while the matrix core works (one MFMA, then one
+    // memory instruction: the MFMA runs on while the next instruction issues).  A
     // slot is refilled only after the barrier that follows every wave's wait for
-    // its own reads of it.  (Stage s is in slot s mod kStages; the loads of the
-    // stages after s+1 that are already issued may stay in flight.)
+    // its own reads of it.  The last iteration reads f0 of a stage past the end
+    // (a slot's stale contents, never used): those reads are drained after the
+    // loop.  Every branch below is uniform and guards loads only, so the MFMA
+    // sequence is the same on every path.
     auto slot = [&](int64_t s) { return lds + (s % kStages) * 2 * kStageElems; };
+    // stages issued after stage s when the last one issued is `last`
     auto issued_after = [&](int64_t s, int64_t last) { return (int)(last - s); };
     wait_stages_after(issued_after(0, nk - 1 < kStages - 2 ? nk - 1 : kStages - 2));
     __builtin_amdgcn_s_barrier();
@@ -201,30 +248,41 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
     const uint32_t oa0 = frag_offset(kWaveRows * wm, 0), oa1 = frag_offset(kWaveRows * wm, 1);
     const uint32_t ob0 = frag_offset(kWaveCols * wn, 0) + 2u * kStageElems;
     const uint32_t ob1 = frag_offset(kWaveCols * wn, 1) + 2u * kStageElems;
+    static_assert(kBlkA * kBlkB == 8 && kBlkA + kBlkB == 6 && kDmaPerStage == 4,
+                  "the interleaving below pairs 8 MFMAs with 6 reads or 4 loads + 6 reads");
     Frags f0, f1;
     read_frags(f0, lds_addr(slot(0)) + oa0, lds_addr(slot(0)) + ob0);
     for (int64_t s = 0; s < nk; ++s) {
-        const uint32_t cur = lds_addr(slot(s));
-        read_frags(f1, cur + oa1, cur + ob1);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_wait<kBlkA + kBlkB>(f0);
-        mma_frags(acc, f0);
-        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t ca = lds_addr(slot(s)) + oa1, cb = lds_addr(slot(s)) + ob1;
+        lds_wait<0>(f0);  // the only LDS reads in flight here are f0(s)'s
+        sb();
+        mma_one<0>(acc, f0); sb(); read_frag<0>(f1, ca, cb); sb();
+        mma_one<1>(acc, f0); sb(); read_frag<1>(f1, ca, cb); sb();
+        mma_one<2>(acc, f0); sb(); read_frag<2>(f1, ca, cb); sb();
+        mma_one<3>(acc, f0); sb(); read_frag<3>(f1, ca, cb); sb();
+        mma_one<4>(acc, f0); sb(); read_frag<4>(f1, ca, cb); sb();
+        mma_one<5>(acc, f0); sb(); read_frag<5>(f1, ca, cb); sb();
+        mma_one<6>(acc, f0); sb();
+        mma_one<7>(acc, f0); sb();
         lds_wait<0>(f1);  // every read of stage s is in: its slot may be refilled
-        if (s + 1 < nk) {
-            // issued so far: stages up to min(nk - 1, s + kStages - 1)
-            const int64_t last = nk - 1 < s + kStages - 1 ? nk - 1 : s + kStages - 1;
-            wait_stages_after(issued_after(s + 1, last));
-            __builtin_amdgcn_s_barrier();
-            if (s + kStages < nk)
-                stage_load(ra, rb, slot(s), slot(s) + kStageElems, K, (s + kStages) * kStageK);
-            const uint32_t nxt = lds_addr(slot(s + 1));
-            read_frags(f0, nxt + oa0, nxt + ob0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mma_frags(acc, f1);
-        __builtin_amdgcn_sched_barrier(0);
+        // stage s+1 has landed (issued so far: stages up to min(nk - 1, s + kStages - 1))
+        if (s + 1 < nk) wait_stages_after(issued_after(s + 1, nk - 1 < s + kStages - 1 ? nk - 1 : s + kStages - 1));
+        __builtin_amdgcn_s_barrier();
+        sb();
+        const uint32_t na = lds_addr(slot(s + 1)) + oa0, nb = lds_addr(slot(s + 1)) + ob0;
+        uint16_t* const st = slot(s);
+        const int64_t k0 = (s + kStages) * kStageK;
+        const bool refill = s + kStages < nk;
+        mma_one<0>(acc, f1); sb(); if (refill) stage_load_part<0>(ra, rb, st, st + kStageElems, K, k0); sb();
+        mma_one<1>(acc, f1); sb(); if (refill) stage_load_part<1>(ra, rb, st, st + kStageElems, K, k0); sb();
+        mma_one<2>(acc, f1); sb(); if (refill) stage_load_part<2>(ra, rb, st, st + kStageElems, K, k0); sb();
+        mma_one<3>(acc, f1); sb(); if (refill) stage_load_part<3>(ra, rb, st, st + kStageElems, K, k0); sb();
+        mma_one<4>(acc, f1); sb(); read_frag<0>(f0, na, nb); sb(); read_frag<1>(f0, na, nb); sb();
+        mma_one<5>(acc, f1); sb(); read_frag<2>(f0, na, nb); sb(); read_frag<3>(f0, na, nb); sb();
+        mma_one<6>(acc, f1); sb(); read_frag<4>(f0, na, nb); sb(); read_frag<5>(f0, na, nb); sb();
+        mma_one<7>(acc, f1); sb();
     }
+    lds_wait<0>(f0);  // the reads past the last stage land before their registers are reused
     // epilogue: accumulator register e of block (x, y) holds row 8 (e/4) + 4 (lane/32) + e%4,
     // column lane % 32 of the block.  (The empty asm makes the output pointer opaque
     // here, so that the compiler does not hoist the epilogue's addresses above the
