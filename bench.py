@@ -310,6 +310,31 @@ def alltoallv_leg(steps):
         heap.close()
 
 
+def copy_ceiling(nbytes, steps):
+    """The practical ceiling for copy-shaped traffic: torch's device copy of one
+    contiguous buffer of `nbytes` into another, over NSETS rotated pairs so that,
+    as in the timed combine, no step finds its data in the 256 MB MALL."""
+    import torch
+
+    pairs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+              torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(NSETS)]
+    st = torch.cuda.current_stream()
+    for k in range(2 * NSETS):
+        pairs[k % NSETS][1].copy_(pairs[k % NSETS][0])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for k in range(steps):
+        pairs[k % NSETS][1].copy_(pairs[k % NSETS][0])
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    del pairs
+    return {"what": f"torch copy of {nbytes >> 20} MiB, {NSETS} rotated buffer pairs (cold in the MALL)",
+            "ms": round(ms, 5), "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -559,6 +584,7 @@ def main():
         rec["put_copy"] = {"bytes_moved": 2 * W * nb, "launches": W,
                            "ms": round(ctx["put_copy"], 5),
                            "GBps": round(2 * W * nb / (ctx["put_copy"] * 1e-3) / 1e9, 2)}
+        rec["copy_ceiling"] = copy_ceiling(W * nb, args.steps)
     heap.close()
     if args.legs == "all":
         rec["ag_gemm"] = ag_gemm_leg(args.steps // 5 + 3)
