@@ -15,6 +15,8 @@
 // release writes the L2 back and the GEMM tile acquires device-wide instead.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "ag_gemm_geom.h"
 #include "gemm_rs_geom.h"
 #include "common.h"
@@ -138,13 +140,28 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
 
 // Wait until at most N of this wave's LDS reads are outstanding; the fragments
 // are tied to the wait so that no use of them is scheduled above it.
+template <int KA, int KB> struct FragTie;
+template <> struct FragTie<2, 4> {
+    template <int N>
+    static __device__ __forceinline__ void wait(bf16x8* a, bf16x8* b) {
+        asm volatile("s_waitcnt lgkmcnt(%6)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+                     : "i"(N));
+    }
+};
+template <> struct FragTie<4, 4> {
+    template <int N>
+    static __device__ __forceinline__ void wait(bf16x8* a, bf16x8* b) {
+        asm volatile("s_waitcnt lgkmcnt(%8)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                       "+v"(b[2]), "+v"(b[3])
+                     : "i"(N));
+    }
+};
+
 template <int N>
 __device__ __forceinline__ void lds_wait(Frags& f) {
-    static_assert(kBlkA == 2 && kBlkB == 4, "lds_wait ties 2 + 4 fragments");
-    asm volatile("s_waitcnt lgkmcnt(%6)"
-                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]),
-                   "+v"(f.b[3])
-                 : "i"(N));
+    FragTie<kBlkA, kBlkB>::template wait<N>(f.a, f.b);
 }
 
 // LDS byte address of a stage slot's first element.
@@ -162,24 +179,25 @@ __device__ __forceinline__ uint32_t frag_offset(int row0, int kk) {
     return 2u * (uint32_t)(row * kStageK + 8 * swz(row, 2 * kk + (l >> 5)));
 }
 
-__device__ __forceinline__ void read_frags(Frags& f, uint32_t a_addr, uint32_t b_addr) {
-    constexpr int kBlk = 32 * kStageK * 2;  // bytes between fragment blocks
-    f.a[0] = lds_read16<0>(a_addr);
-    f.a[1] = lds_read16<kBlk>(a_addr);
-    f.b[0] = lds_read16<0>(b_addr);
-    f.b[1] = lds_read16<kBlk>(b_addr);
-    f.b[2] = lds_read16<2 * kBlk>(b_addr);
-    f.b[3] = lds_read16<3 * kBlk>(b_addr);
-}
-
-// Fragment I of read_frags alone (0, 1: A blocks; 2 .. 5: B blocks).
+// Fragment I of read_frags alone (I < kBlkA: A blocks; then the B blocks).
 template <int I>
 __device__ __forceinline__ void read_frag(Frags& f, uint32_t a_addr, uint32_t b_addr) {
-    constexpr int kBlk = 32 * kStageK * 2;
-    if (I < kBlkA)
-        f.a[I < kBlkA ? I : 0] = lds_read16<(I < kBlkA ? I : 0) * kBlk>(a_addr);
+    constexpr int kBlk = 32 * kStageK * 2;  // bytes between fragment blocks
+    if constexpr (I < kBlkA)
+        f.a[I] = lds_read16<I * kBlk>(a_addr);
     else
-        f.b[I >= kBlkA ? I - kBlkA : 0] = lds_read16<(I >= kBlkA ? I - kBlkA : 0) * kBlk>(b_addr);
+        f.b[I - kBlkA] = lds_read16<(I - kBlkA) * kBlk>(b_addr);
+}
+
+template <int... Is>
+__device__ __forceinline__ void read_frags_seq(Frags& f, uint32_t a_addr, uint32_t b_addr,
+                                               std::integer_sequence<int, Is...>) {
+    (read_frag<Is>(f, a_addr, b_addr), ...);
+}
+
+// Every fragment of one k16 step: kBlkA A blocks, then kBlkB B blocks.
+__device__ __forceinline__ void read_frags(Frags& f, uint32_t a_addr, uint32_t b_addr) {
+    read_frags_seq(f, a_addr, b_addr, std::make_integer_sequence<int, kBlkA + kBlkB>{});
 }
 
 // MFMA I of mma_frags alone (block x = I / kBlkB, y = I mod kBlkB).
@@ -190,6 +208,66 @@ __device__ __forceinline__ void mma_one(f32x16 (&acc)[kBlkA][kBlkB], const Frags
 }
 
 __device__ __forceinline__ void sb() { __builtin_amdgcn_sched_barrier(0); }
+
+// The interleaving of a half-stage: kMfma MFMAs, and after MFMA i the memory
+// operations j (of n in all) with j * kMfma / n == i, so they spread evenly and
+// the earliest ones come first.
+constexpr int kMfma = kBlkA * kBlkB;
+constexpr int kReads = kBlkA + kBlkB;
+constexpr int op_slot(int j, int n) { return j * kMfma / n; }
+
+// Before the barrier: the MFMAs of f0(s), with the reads of f1(s) between them.
+struct PreCtx {
+    Frags* fr;
+    uint32_t a, b;
+};
+template <int I, int J>
+__device__ __forceinline__ void pre_op(const PreCtx& c) {
+    if constexpr (op_slot(J, kReads) == I) {
+        read_frag<J>(*c.fr, c.a, c.b);
+        sb();
+    }
+}
+template <int I, int... Js>
+__device__ __forceinline__ void pre_ops(const PreCtx& c, std::integer_sequence<int, Js...>) {
+    (pre_op<I, Js>(c), ...);
+}
+template <int... Is>
+__device__ __forceinline__ void pre_half(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PreCtx& c,
+                                         std::integer_sequence<int, Is...>) {
+    ((mma_one<Is>(acc, fm), sb(), pre_ops<Is>(c, std::make_integer_sequence<int, kReads>{})), ...);
+}
+
+// After the barrier: the MFMAs of f1(s), with the reads of f0(s+1) and then
+// (when `refill`) the loads refilling the freed slot between them.
+struct PostCtx {
+    Frags* fr;
+    uint32_t a, b;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint16_t* st;
+    int64_t K, k0;
+    bool refill;
+};
+template <int I, int J>
+__device__ __forceinline__ void post_op(const PostCtx& c) {
+    if constexpr (op_slot(J, kReads + kDmaPerStage) == I) {
+        if constexpr (J < kReads) {
+            read_frag<J>(*c.fr, c.a, c.b);
+        } else {
+            if (c.refill) stage_load_part<J - kReads>(c.ra, c.rb, c.st, c.st + kStageElems, c.K, c.k0);
+        }
+        sb();
+    }
+}
+template <int I, int... Js>
+__device__ __forceinline__ void post_ops(const PostCtx& c, std::integer_sequence<int, Js...>) {
+    (post_op<I, Js>(c), ...);
+}
+template <int... Is>
+__device__ __forceinline__ void post_half(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PostCtx& c,
+                                          std::integer_sequence<int, Is...>) {
+    ((mma_one<Is>(acc, fm), sb(), post_ops<Is>(c, std::make_integer_sequence<int, kReads + kDmaPerStage>{})), ...);
+}
 
 __device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Frags& f) {
 #pragma unroll
@@ -225,9 +303,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
         stage_load(ra, rb, st, st + kStageElems, K, s * kStageK);
     }
     // Software pipeline over stages, one stage of LDS loads ahead of the reads:
-    //   MFMAs of f0(s), each followed by one read of f1(s) | wait for f1(s),
-    //   wait for stage s+1, barrier | MFMAs of f1(s), each followed by one LDS
-    //   load refilling the slot of stage s with stage s+4 or one read of f0(s+1)
+    //   MFMAs of f0(s), the reads of f1(s) spread between them | wait for f1(s),
+    //   wait for stage s+1, barrier | MFMAs of f1(s), the reads of f0(s+1) and
+    //   then the LDS loads refilling the slot of stage s with stage s+4 spread
+    //   between them
     // so the LDS latency of each half hides under the other half's MFMAs, and the
     // memory instructions issue while the matrix core works (one MFMA, then one
     // memory instruction: the MFMA runs on while the next instruction issues).  A
@@ -248,22 +327,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
     const uint32_t oa0 = frag_offset(kWaveRows * wm, 0), oa1 = frag_offset(kWaveRows * wm, 1);
     const uint32_t ob0 = frag_offset(kWaveCols * wn, 0) + 2u * kStageElems;
     const uint32_t ob1 = frag_offset(kWaveCols * wn, 1) + 2u * kStageElems;
-    static_assert(kBlkA * kBlkB == 8 && kBlkA + kBlkB == 6 && kDmaPerStage == 4,
-                  "the interleaving below pairs 8 MFMAs with 6 reads or 4 loads + 6 reads");
     Frags f0, f1;
     read_frags(f0, lds_addr(slot(0)) + oa0, lds_addr(slot(0)) + ob0);
     for (int64_t s = 0; s < nk; ++s) {
         const uint32_t ca = lds_addr(slot(s)) + oa1, cb = lds_addr(slot(s)) + ob1;
         lds_wait<0>(f0);  // the only LDS reads in flight here are f0(s)'s
         sb();
-        mma_one<0>(acc, f0); sb(); read_frag<0>(f1, ca, cb); sb();
-        mma_one<1>(acc, f0); sb(); read_frag<1>(f1, ca, cb); sb();
-        mma_one<2>(acc, f0); sb(); read_frag<2>(f1, ca, cb); sb();
-        mma_one<3>(acc, f0); sb(); read_frag<3>(f1, ca, cb); sb();
-        mma_one<4>(acc, f0); sb(); read_frag<4>(f1, ca, cb); sb();
-        mma_one<5>(acc, f0); sb(); read_frag<5>(f1, ca, cb); sb();
-        mma_one<6>(acc, f0); sb();
-        mma_one<7>(acc, f0); sb();
+        pre_half(acc, f0, PreCtx{&f1, ca, cb}, std::make_integer_sequence<int, kMfma>{});
         lds_wait<0>(f1);  // every read of stage s is in: its slot may be refilled
         // stage s+1 has landed (issued so far: stages up to min(nk - 1, s + kStages - 1))
         if (s + 1 < nk) wait_stages_after(issued_after(s + 1, nk - 1 < s + kStages - 1 ? nk - 1 : s + kStages - 1));
@@ -273,14 +343,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
         uint16_t* const st = slot(s);
         const int64_t k0 = (s + kStages) * kStageK;
         const bool refill = s + kStages < nk;
-        mma_one<0>(acc, f1); sb(); if (refill) stage_load_part<0>(ra, rb, st, st + kStageElems, K, k0); sb();
-        mma_one<1>(acc, f1); sb(); if (refill) stage_load_part<1>(ra, rb, st, st + kStageElems, K, k0); sb();
-        mma_one<2>(acc, f1); sb(); if (refill) stage_load_part<2>(ra, rb, st, st + kStageElems, K, k0); sb();
-        mma_one<3>(acc, f1); sb(); if (refill) stage_load_part<3>(ra, rb, st, st + kStageElems, K, k0); sb();
-        mma_one<4>(acc, f1); sb(); read_frag<0>(f0, na, nb); sb(); read_frag<1>(f0, na, nb); sb();
-        mma_one<5>(acc, f1); sb(); read_frag<2>(f0, na, nb); sb(); read_frag<3>(f0, na, nb); sb();
-        mma_one<6>(acc, f1); sb(); read_frag<4>(f0, na, nb); sb(); read_frag<5>(f0, na, nb); sb();
-        mma_one<7>(acc, f1); sb();
+        post_half(acc, f1, PostCtx{&f0, na, nb, ra, rb, st, K, k0, refill},
+                  std::make_integer_sequence<int, kMfma>{});
     }
     lds_wait<0>(f0);  // the reads past the last stage land before their registers are reused
     // epilogue: accumulator register e of block (x, y) holds row 8 (e/4) + 4 (lane/32) + e%4,
