@@ -18,6 +18,8 @@ SHAPES = [
     (16, 2048, 64, 264),
     (5, 5 * 700, 16, 1000),
     (8, 8 * 257, 8, 257),
+    (2, 2 * 2048, 64, 2304),   # 72 tiles per destination: three queue blocks, the last ragged
+    (3, 3 * 4096, 8, 4096),    # 256 tiles per destination: eight full blocks
 ]
 
 

@@ -71,6 +71,7 @@ EXACT = [
     (16, 16 * 130, 64, 264),  # more ranks than XCDs, ragged tiles
     (2, 2 * 520, 1032, 776),
     (5, 5 * 40, 4096, 16),   # long K, narrow N
+    (2, 2 * 2048, 64, 2304),  # 72 tiles per destination: several queue blocks, the last ragged
 ]
 
 
