@@ -28,7 +28,10 @@ from combine_harness import say  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-def run_gemm_rs(a_bits, bt_bits, flags=0, dirty_signals=False):
+def run_gemm_rs(a_bits, bt_bits, flags=0, dirty_signals=False, calls=1, caller_reset=False):
+    """Run `calls` back-to-back calls on the same buffers (the signal array keeps
+    the previous call's values unless the call resets it); with caller_reset the
+    signals are zeroed by ra2a_signal_reset and the calls pass RS_SKIP_RESET."""
     W = len(a_bits)
     m, K = a_bits[0].shape
     N = bt_bits[0].shape[0]
@@ -48,8 +51,14 @@ def run_gemm_rs(a_bits, bt_bits, flags=0, dirty_signals=False):
             if dirty_signals:
                 heap.view(osg, (nsig * 128,), torch.uint8, r).fill_(0x5A)
         torch.cuda.synchronize()
-        ra2a.gemm_rs(heap.ptr(oa), heap.ptr(ob), heap.ptr(op), heap.ptr(oo), heap.ptr(osg), W, m,
-                     K, N, flags, torch.cuda.current_stream())
+        st = torch.cuda.current_stream()
+        for _ in range(calls):
+            f = flags
+            if caller_reset:
+                ra2a.signal_reset(heap.handle, heap.ptr(osg), nsig, st)
+                f |= ra2a.RS_SKIP_RESET
+            ra2a.gemm_rs(heap.ptr(oa), heap.ptr(ob), heap.ptr(op), heap.ptr(oo), heap.ptr(osg), W, m,
+                         K, N, f, st)
         torch.cuda.synchronize()
         rc = ra2a.check(heap.handle)
         assert rc == ra2a.OK, ra2a.last_error()
@@ -89,6 +98,20 @@ def test_integer_inputs_bit_exact(W, m, K, N, flags):
     for j in range(W):
         np.testing.assert_array_equal(outs[j], gemm.f64_to_bf16_rne_bits(ref[j]),
                                       err_msg=f"rank {j}")
+        assert (sigs[j] == 1).all(), sigs[j]
+
+
+@pytest.mark.parametrize("caller_reset", [False, True])
+def test_back_to_back_calls_and_caller_reset(caller_reset):
+    """Three calls in a row on one signal array (each reset by the library, or by
+    the caller with RS_SKIP_RESET): the output and the signals are those of one call."""
+    W, m, K, N = 4, 4 * 300, 136, 520
+    say(f"[case] gemm_rs back-to-back caller_reset={caller_reset}")
+    a, bt = synthgen.make_gemm_rs_inputs(m=m, K=K, N=N, W=W, integer=True)
+    outs, sigs = run_gemm_rs(a, bt, 0, dirty_signals=True, calls=3, caller_reset=caller_reset)
+    ref = gemm.gemm_rs_ref(a, bt)
+    for j in range(W):
+        np.testing.assert_array_equal(outs[j], gemm.f64_to_bf16_rne_bits(ref[j]), err_msg=f"rank {j}")
         assert (sigs[j] == 1).all(), sigs[j]
 
 
