@@ -40,6 +40,12 @@ constexpr int kStages = 4;         // LDS ring depth (3 stages in flight)
 constexpr int kStageElems = kGemmBM * kStageK;  // bf16 per operand per stage (16 KiB)
 constexpr int kRowsPerWave = kGemmBM / kGemmWaves;        // operand rows each wave loads
 constexpr int kDmaPerStage = 2 * (kRowsPerWave / 16);      // its LDS loads per stage (A and B)
+// bf16 epilogue: the 256 x 256 output tile staged in LDS, rows padded by 16 bytes so
+// that the two rows one write instruction touches fall in different banks
+constexpr int kEpiPitch = kGemmBM * 2 + 16;                  // bytes per staged row
+constexpr int kLdsElems = (kStages * 2 * kStageElems) > (kGemmBM * kEpiPitch / 2)
+                              ? (kStages * 2 * kStageElems)
+                              : (kGemmBM * kEpiPitch / 2);   // uint16 elements of the LDS array
 
 // float -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -354,23 +360,57 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
     uint64_t cbase = reinterpret_cast<uint64_t>(c);
     asm volatile("" : "+v"(cbase));
     const int lane = (int)threadIdx.x & 63;
+    if constexpr (F32OUT) {
 #pragma unroll
-    for (int x = 0; x < kBlkA; ++x)
+        for (int x = 0; x < kBlkA; ++x)
 #pragma unroll
-        for (int y = 0; y < kBlkB; ++y) {
-            const int64_t col = kWaveCols * wn + 32 * y + (lane & 31);
+            for (int y = 0; y < kBlkB; ++y) {
+                const int64_t col = kWaveCols * wn + 32 * y + (lane & 31);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (row < rows_valid && col < cols_valid) {
-                    if (F32OUT)
+                for (int e = 0; e < 16; ++e) {
+                    const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (row < rows_valid && col < cols_valid)
                         reinterpret_cast<float*>(cbase)[(int64_t)row * ldc + col] = acc[x][y][e];
-                    else
-                        reinterpret_cast<uint16_t*>(cbase)[(int64_t)row * ldc + col] =
-                            (uint16_t)bf16_rne(acc[x][y][e]);
                 }
             }
+    } else {
+        // bf16: round into the LDS tile (row pitch kEpiPitch), then write it out as
+        // 16-byte row pieces -- 16 stores per lane instead of 128 two-byte ones.
+        // Every wave's reads of the ring are complete (its own waits above); the
+        // barrier makes that true for all of them before the ring is overwritten.
+        __builtin_amdgcn_s_barrier();
+        uint8_t* const t = reinterpret_cast<uint8_t*>(lds);
+#pragma unroll
+        for (int x = 0; x < kBlkA; ++x)
+#pragma unroll
+            for (int y = 0; y < kBlkB; ++y) {
+                const int col = kWaveCols * wn + 32 * y + (lane & 31);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    *reinterpret_cast<uint16_t*>(t + row * kEpiPitch + col * 2) =
+                        (uint16_t)bf16_rne(acc[x][y][e]);
+                }
+            }
+        __syncthreads();
+        // 16-byte pieces need a 16-byte aligned output and a row stride of whole pieces
+        const bool vec = (cbase & 15u) == 0 && (ldc & 7) == 0;
+        constexpr int kPieces = kGemmBM * kGemmBM / 8;  // 8 bf16 per piece
+        for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
+            const int row = i / (kGemmBM / 8);
+            const int col0 = (i - row * (kGemmBM / 8)) * 8;
+            if (row >= rows_valid || col0 >= cols_valid) continue;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(t + row * kEpiPitch + col0 * 2);
+            uint16_t* const dst = reinterpret_cast<uint16_t*>(cbase) + (int64_t)row * ldc + col0;
+            if (vec && col0 + 8 <= cols_valid) {
+                *reinterpret_cast<u32x4*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (col0 + k < cols_valid) dst[k] = (uint16_t)(v[k >> 1] >> (16 * (k & 1)));
+            }
         }
+    }
     __builtin_amdgcn_s_barrier();  // the LDS ring is free for the next tile
 }
 
@@ -410,7 +450,7 @@ hipError_t launch_transpose_b(const uint16_t* b, uint16_t* bt, int64_t K, int64_
 
 template <int SYNC>
 __global__ void __launch_bounds__(kGemmThreads, 1) ag_gemm_kernel(AgGemmArgs a) {
-    __shared__ uint16_t lds[kStages * 2 * kStageElems];  // 4 stages x (A, B^T), 128 KiB
+    __shared__ uint16_t lds[kLdsElems];  // 4 stages x (A, B^T), 128 KiB, or the staged output tile
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
     constexpr bool kOwned = SYNC == kSyncXcd;
@@ -553,7 +593,7 @@ __device__ __forceinline__ void rs_reduce_tile(const GemmRsArgs& a, int j, int t
 
 template <int SYNC, bool F32P>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_rs_kernel(GemmRsArgs a) {
-    __shared__ uint16_t lds[kStages * 2 * kStageElems];
+    __shared__ uint16_t lds[kLdsElems];
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
     constexpr bool kOwned = SYNC == kSyncXcd;
