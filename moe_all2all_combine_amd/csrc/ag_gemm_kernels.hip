@@ -46,6 +46,12 @@ constexpr int kEpiPitch = kGemmBM * 2 + 16;                  // bytes per staged
 constexpr int kLdsElems = (kStages * 2 * kStageElems) > (kGemmBM * kEpiPitch / 2)
                               ? (kStages * 2 * kStageElems)
                               : (kGemmBM * kEpiPitch / 2);   // uint16 elements of the LDS array
+// fp32 epilogue: half the tile's rows at a time, rows padded by 32 bytes (the two
+// rows one write instruction touches then fall in the two halves of the banks)
+constexpr int kEpiRows32 = kGemmBM / 2;
+constexpr int kEpiPitch32 = kGemmBM * 4 + 32;
+static_assert(kEpiRows32 * kEpiPitch32 <= 2 * kLdsElems, "the fp32 half tile must fit the LDS array");
+static_assert(kWaveRows <= kEpiRows32 && kEpiRows32 % kWaveRows == 0, "a wave's rows lie in one half");
 
 // float -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -361,18 +367,46 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
     asm volatile("" : "+v"(cbase));
     const int lane = (int)threadIdx.x & 63;
     if constexpr (F32OUT) {
+        // fp32: through LDS half a tile at a time (rows [128 h, 128 h + 128)), written
+        // out as 16-byte row pieces.  Each wave's rows lie in one half; waves of the
+        // other half only help with the stores.
+        uint8_t* const t = reinterpret_cast<uint8_t*>(lds);
+        const bool vec = (cbase & 15u) == 0 && (ldc & 3) == 0;
+        constexpr int kPieces = kEpiRows32 * kGemmBM / 4;  // 4 floats per piece
+        const int my_half = kWaveRows * wm / kEpiRows32;
+        for (int h = 0; h < kGemmBM / kEpiRows32; ++h) {
+            __builtin_amdgcn_s_barrier();  // the ring, or the previous half, is free
+            if (my_half == h) {
 #pragma unroll
-        for (int x = 0; x < kBlkA; ++x)
+                for (int x = 0; x < kBlkA; ++x)
 #pragma unroll
-            for (int y = 0; y < kBlkB; ++y) {
-                const int64_t col = kWaveCols * wn + 32 * y + (lane & 31);
+                    for (int y = 0; y < kBlkB; ++y) {
+                        const int col = kWaveCols * wn + 32 * y + (lane & 31);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    if (row < rows_valid && col < cols_valid)
-                        reinterpret_cast<float*>(cbase)[(int64_t)row * ldc + col] = acc[x][y][e];
+                        for (int e = 0; e < 16; ++e) {
+                            const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                            *reinterpret_cast<float*>(t + (row - kEpiRows32 * h) * kEpiPitch32 + col * 4) =
+                                acc[x][y][e];
+                        }
+                    }
+            }
+            __syncthreads();
+            for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
+                const int lrow = i / (kGemmBM / 4);
+                const int col0 = (i - lrow * (kGemmBM / 4)) * 4;
+                const int row = kEpiRows32 * h + lrow;
+                if (row >= rows_valid || col0 >= cols_valid) continue;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(t + lrow * kEpiPitch32 + col0 * 4);
+                float* const dst = reinterpret_cast<float*>(cbase) + (int64_t)row * ldc + col0;
+                if (vec && col0 + 4 <= cols_valid) {
+                    *reinterpret_cast<u32x4*>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (col0 + k < cols_valid) dst[k] = __uint_as_float(v[k]);
                 }
             }
+        }
     } else {
         // bf16: round into the LDS tile (row pitch kEpiPitch), then write it out as
         // 16-byte row pieces -- 16 stores per lane instead of 128 two-byte ones.
