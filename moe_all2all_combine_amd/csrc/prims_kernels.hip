@@ -26,11 +26,17 @@ constexpr int64_t kSmallPut = 256 * 1024;
 
 }  // namespace
 
+// A wide put: workgroup k copies segments k, k + grid, ... of kPutSeg * V bytes
+// (8 vectors per lane, all in flight), streamed past the caches.
+constexpr int kPutSeg = kThreads * 8;  // vectors per segment
 template <int V>
 __global__ void __launch_bounds__(kThreads) put_kernel(uint8_t* dst, const uint8_t* src,
                                                       int64_t bytes) {
-    copy_flat<V, 8>(src, dst, bytes, (int64_t)blockIdx.x * kThreads + threadIdx.x,
-                    (int64_t)gridDim.x * kThreads);
+    const int64_t seg = (int64_t)kPutSeg * V;
+    for (int64_t o = (int64_t)blockIdx.x * seg; o < bytes; o += (int64_t)gridDim.x * seg) {
+        const int64_t n = bytes - o < seg ? bytes - o : seg;
+        copy_flat<V, 8, true>(src + o, dst + o, n, threadIdx.x, kThreads);
+    }
 }
 
 // One workgroup: copy, fence (every wave), barrier, then one lane signals.
