@@ -139,3 +139,23 @@ def test_library_owned_heap():
         assert torch.equal(back, src)
     finally:
         ra2a.symm_heap_destroy(h)
+
+
+@pytest.mark.parametrize("nbytes", [(100 << 20) + 48, (33 << 20) + 3])
+def test_wide_put_loops_over_segments(nbytes):
+    """Puts large enough that each of the 2048 workgroups copies several segments
+    (16-byte vectors, and 1-byte vectors for an odd size), with a ragged tail."""
+    say(f"[case] wide put nbytes={nbytes}")
+    h = ra2a.SymmHeap(2, nbytes + (1 << 20))
+    try:
+        dst = h.alloc(nbytes)
+        g = torch.Generator(device="cuda").manual_seed(nbytes % 1000)
+        src = torch.randint(0, 256, (nbytes + 1,), dtype=torch.uint8, generator=g, device="cuda")
+        h.view(dst, (nbytes,), torch.uint8, 1).fill_(0)
+        off = nbytes % 2  # odd sizes also start one byte in: 1-byte vectors
+        ra2a.put(h.handle, h.ptr(dst), src.data_ptr() + off, nbytes, 1)
+        torch.cuda.synchronize()
+        assert ra2a.check(h.handle) == ra2a.OK
+        assert torch.equal(h.view(dst, (nbytes,), torch.uint8, 1), src[off:off + nbytes])
+    finally:
+        h.close()
