@@ -237,7 +237,10 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
         p->regionB = 0;
         p->ring_bytes = (int64_t)W * S * H * D * e;
     }
-    p->wg_per_cu = o->wg_per_cu > 0 ? o->wg_per_cu : 2;
+    // measured on the W=8, S=512, H=16, D=128 bf16 shape: the combine runs best with
+    // two persistent workgroups per compute unit, the dispatch (strided reads,
+    // contiguous writes) with one (51.1 against 55.0 us)
+    p->wg_per_cu = o->wg_per_cu > 0 ? o->wg_per_cu : (p->inverse ? 1 : 2);
     p->lookahead = o->lookahead;
     // the kernels index tiles, pieces and work items with 32-bit arithmetic
     const double tasks = (double)W * p->nbs * p->nhb * p->ndb * ((double)W + p->csplit * W);
