@@ -497,7 +497,7 @@ int ra2a_alltoallv_signal_slots(int W, int64_t *slots);
  *   recv_counts slice j: int64[W + 1]: [r] = rows received from rank r, [W] = the
  *               total, written once every segment has arrived (8-byte aligned);
  *   signals     slice j: ra2a_alltoallv_signal_slots' slots (8-byte aligned).
- * chunk_bytes: bytes per data task (0: 256 KiB; else a positive multiple of 16).
+ * chunk_bytes: bytes per data task (0: 44 KiB; else a positive multiple of 16).
  * The signals are zeroed by a reset launch first unless RA2A_A2V_SKIP_RESET.
  * Checked on the device (ra2a_check then reports RA2A_EDATA): a sender with a
  * negative count, or more rows in total than in_rows, sends nothing (its counts

@@ -26,7 +26,7 @@ CASES = [
 
 
 def chunks(rows, row_bytes, chunk):
-    chunk = chunk or 256 << 10
+    chunk = chunk or 44 << 10
     b = rows * row_bytes
     return max(1, -(-b // chunk))
 

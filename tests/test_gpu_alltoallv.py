@@ -71,7 +71,7 @@ def check_all(case, ins, counts, chunk):
     W, rb = case.W, case.rb
     want, want_rc = a2av.alltoallv(ins, counts)
     roff = a2av.receive_offsets(counts)
-    chunk_b = chunk or 256 << 10
+    chunk_b = chunk or 44 << 10
     for j in range(W):
         n = want[j].shape[0]
         o = case.out(j)
