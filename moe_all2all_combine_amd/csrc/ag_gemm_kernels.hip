@@ -562,6 +562,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) ag_gemm_kernel(AgGemmArgs a) 
 // partial_j[r] of the tile (bf16, or with F32P fp32), added in fp32 and rounded
 // to bf16 (nearest even).  The partials are read with device-scope loads (never
 // from the CU's L1).  V columns per lane: V partial elements form one load.
+constexpr int kRsGroup = 8;  // partial loads in flight per lane in a reduce task
+
 template <bool F32P, int V>
 __device__ __forceinline__ void rs_reduce_cols(const GemmRsArgs& a, uint8_t* slice, int64_t row0,
                                                int64_t col0, int rows, int cols) {
@@ -580,17 +582,31 @@ __device__ __forceinline__ void rs_reduce_cols(const GemmRsArgs& a, uint8_t* sli
         float s[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) s[v] = 0.f;
-        for (int src = 0; src < a.W; ++src) {
-            const auto x = Load::go(rp, off + (uint32_t)src * plane);
-            if constexpr (V == 1) {
-                s[0] += F32P ? __uint_as_float((uint32_t)x) : __uint_as_float((uint32_t)x << 16);
-            } else {
+        // the sources in groups of kRsGroup: every load of a group is issued before
+        // the first add (a short group loads the last source again and skips the
+        // add), then the adds run in rank order
+        for (int src0 = 0; src0 < a.W; src0 += kRsGroup) {
+            decltype(Load::go(rp, 0u)) x[kRsGroup];
 #pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    if constexpr (F32P)
-                        s[v] += __uint_as_float(x[v]);
-                    else
-                        s[v] += __uint_as_float(v & 1 ? x[v >> 1] & 0xFFFF0000u : x[v >> 1] << 16);
+            for (int g = 0; g < kRsGroup; ++g) {
+                const int src = src0 + g < a.W ? src0 + g : a.W - 1;
+                x[g] = Load::go(rp, off + (uint32_t)src * plane);
+            }
+#pragma unroll
+            for (int g = 0; g < kRsGroup; ++g) {
+                // a select, not a branch: every loaded value is used, so no load is
+                // sunk behind a test and the group's loads stay in flight together
+                const bool live = src0 + g < a.W;
+                if constexpr (V == 1) {
+                    const float t = F32P ? __uint_as_float((uint32_t)x[g]) : __uint_as_float((uint32_t)x[g] << 16);
+                    s[0] = live ? s[0] + t : s[0];
+                } else {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        const float t = F32P ? __uint_as_float(x[g][v])
+                                             : __uint_as_float(v & 1 ? x[g][v >> 1] & 0xFFFF0000u : x[g][v >> 1] << 16);
+                        s[v] = live ? s[v] + t : s[v];
+                    }
                 }
             }
         }

@@ -27,11 +27,12 @@
 namespace ra2a {
 
 constexpr int kRsTile = 256;   // output tile edge
-// Output tiles per queue block.  A reduce task reads W partial tiles through one
-// compute unit (about 2 MB with fp32 partials at W = 8), several times a GEMM
-// tile's time, so reduces placed among the GEMM tasks in small blocks hold up
-// compute: measured at W = 8, m = 8192, K = 896, N = 4096, blocks of 8 / 16 /
-// 32 / 64 tiles take 1.105 / 1.017 / 0.991 / 0.994 ms.
+// Output tiles per queue block.  Measured at W = 8, m = 8192, K = 896, N = 4096
+// (fp32 partials): while a reduce task waited for each partial load before
+// issuing the next, blocks of 8 / 16 / 32 / 64 tiles took 1.105 / 1.017 / 0.991
+// / 0.994 ms (a slow reduce among the GEMM tasks held compute up); with the loads
+// of a reduce in flight together, 8 / 16 / 32 take 0.914 / 0.940 / 0.923-0.942 ms,
+// the same within the run-to-run spread.
 constexpr int kRsBlock = 32;
 
 struct GemmRsArgs {
