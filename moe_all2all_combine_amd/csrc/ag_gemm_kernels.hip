@@ -3,8 +3,8 @@
 //   * AllGather part: copy a few rows of shard w (slice w) into G (slice rank),
 //     release, count the part; the tile's last part sets its signal to 1
 //     (put_with_signal per tile, the HyperParallel RFC section 六 / 十);
-//   * GEMM tile: wait until every tile covering its 256 rows is signalled,
-//     then C[256 x 256] = G[rows, :] @ B[:, cols] on the matrix cores (bf16 in,
+//   * GEMM tile: wait until every tile covering its kGemmBM rows is signalled,
+//     then C[kGemmBM x kGemmBN] = G[rows, :] @ B[:, cols] on the matrix cores (bf16 in,
 //     fp32 accumulation, bf16 out rounded to nearest even) -- "Triton-distributed
 //     Semantics", sections "Producer-Consumer Model" and "AllGather + GEMM
 //     Overlapping": the consumer waits only for its own tile.
@@ -29,27 +29,37 @@ namespace ra2a {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmWaves = 8;      // 2 per SIMD: one issues MFMAs while the other waits
+constexpr int kTileM = kGemmBM;   // output rows of a tile (rows of A)
+constexpr int kTileN = kGemmBN;   // output columns of a tile (rows of B^T)
+constexpr int kGemmWaves = kTileM / 32;  // waves (wm, wn), wm = wave / 2, wn = wave mod 2
 constexpr int kGemmThreads = 64 * kGemmWaves;
-constexpr int kWaveRows = 64;      // each wave owns 64 x 128 outputs of the tile:
-constexpr int kWaveCols = 128;     //   waves (wm, wn), wm = wave / 2, wn = wave mod 2
+constexpr int kGemmWgPerCu = 512 / kGemmThreads;  // two waves per SIMD in all
+constexpr int kWaveRows = 64;      // each wave owns 64 x 128 outputs of the tile
+constexpr int kWaveCols = 128;
+static_assert(kWaveRows * (kGemmWaves / 2) == kTileM && kWaveCols * 2 == kTileN,
+              "the waves tile the output tile");
 constexpr int kBlkA = kWaveRows / 32;  // 32 x 32 MFMA blocks per wave along rows
 constexpr int kBlkB = kWaveCols / 32;  // ... and along columns
 constexpr int kStageK = 32;        // k per pipeline stage
-constexpr int kStages = 4;         // LDS ring depth (3 stages in flight)
-constexpr int kStageElems = kGemmBM * kStageK;  // bf16 per operand per stage (16 KiB)
-constexpr int kRowsPerWave = kGemmBM / kGemmWaves;        // operand rows each wave loads
-constexpr int kDmaPerStage = 2 * (kRowsPerWave / 16);      // its LDS loads per stage (A and B)
-// bf16 epilogue: the 256 x 256 output tile staged in LDS, rows padded by 16 bytes so
-// that the two rows one write instruction touches fall in different banks
-constexpr int kEpiPitch = kGemmBM * 2 + 16;                  // bytes per staged row
-constexpr int kLdsElems = (kStages * 2 * kStageElems) > (kGemmBM * kEpiPitch / 2)
-                              ? (kStages * 2 * kStageElems)
-                              : (kGemmBM * kEpiPitch / 2);   // uint16 elements of the LDS array
+constexpr int kStages = kGemmWgPerCu == 1 ? 4 : 3;  // LDS ring depth (kStages - 1 in flight)
+constexpr int kStageA = kTileM * kStageK;  // bf16 of A per stage
+constexpr int kStageB = kTileN * kStageK;  // bf16 of B^T per stage
+constexpr int kSlotElems = kStageA + kStageB;
+constexpr int kRowsA = kTileM / kGemmWaves;  // A rows each wave loads per stage
+constexpr int kRowsB = kTileN / kGemmWaves;  // B^T rows each wave loads per stage
+constexpr int kDmaA = kRowsA / 16, kDmaB = kRowsB / 16;  // its LDS loads (16 rows each)
+constexpr int kDmaPerStage = kDmaA + kDmaB;
+static_assert(kRowsA % 16 == 0 && kRowsB % 16 == 0, "whole 16-row LDS loads");
+// bf16 epilogue: the output tile staged in LDS, rows padded by 16 bytes so that the
+// two rows one write instruction touches fall in different banks
+constexpr int kEpiPitch = kTileN * 2 + 16;                   // bytes per staged row
+constexpr int kLdsElems = (kStages * kSlotElems) > (kTileM * kEpiPitch / 2)
+                              ? (kStages * kSlotElems)
+                              : (kTileM * kEpiPitch / 2);    // uint16 elements of the LDS array
 // fp32 epilogue: half the tile's rows at a time, rows padded by 32 bytes (the two
 // rows one write instruction touches then fall in the two halves of the banks)
-constexpr int kEpiRows32 = kGemmBM / 2;
-constexpr int kEpiPitch32 = kGemmBM * 4 + 32;
+constexpr int kEpiRows32 = kTileM / 2;
+constexpr int kEpiPitch32 = kTileN * 4 + 32;
 static_assert(kEpiRows32 * kEpiPitch32 <= 2 * kLdsElems, "the fp32 half tile must fit the LDS array");
 static_assert(kWaveRows <= kEpiRows32 && kEpiRows32 % kWaveRows == 0, "a wave's rows lie in one half");
 
@@ -60,7 +70,7 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// LDS stage layout of an operand: 256 rows x 32 k (64 bytes per row, four 16-byte
+// LDS stage layout of an operand: its tile rows x 32 k (64 bytes per row, four 16-byte
 // chunks).  Chunk c of row r is stored at position c ^ g(r), g(r) = (r >> 2) & 3.
 // Of the XOR patterns measured with the LDS bank-conflict counter on gfx950 for
 // these fragment reads (32 consecutive rows at one chunk, and the same rows at
@@ -71,48 +81,40 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 // Offset sent for a chunk that must read as zero: past any buffer's range.
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
-// Load one stage (k0 .. k0 + 32) of both operands straight into LDS.  Each wave
-// instruction fills 1 KiB of LDS, lane l landing at byte 16 l: 16 rows x 4
-// chunks; the lane therefore fetches the logical chunk that belongs at its
-// swizzled position.  Rows past the operand's buffer and k past K read as 0.
-__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                           uint16_t* lds_a, uint16_t* lds_b, int64_t K,
-                                           int64_t k0) {
-    const int w = (int)threadIdx.x >> 6;
-    const int l = (int)threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave / 16; ++i) {
-        const int rbase = kRowsPerWave * w + 16 * i;
-        const int row = rbase + (l >> 2);
-        const int c = swz(row, l & 3);
-        const int64_t k = k0 + 8 * c;
-        const uint32_t off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(lds_a + rbase * kStageK), 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (__attribute__((address_space(3))) void*)(lds_b + rbase * kStageK), 16, off, 0, 0, 0);
-    }
-}
-
-// One of the kDmaPerStage LDS loads of stage_load: part p = 2 i + (0: A, 1: B).
+// One of the kDmaPerStage LDS loads of a stage (k0 .. k0 + 32): parts 0 .. kDmaA-1
+// load this wave's A rows, the others its B^T rows, into the stage's slot (A
+// first, then B^T).  Each wave instruction fills 1 KiB of LDS, lane l landing at
+// byte 16 l: 16 rows x 4 chunks; the lane therefore fetches the logical chunk
+// that belongs at its swizzled position.  Rows past the operand's buffer and k
+// past K read as 0.
 template <int P>
 __device__ __forceinline__ void stage_load_part(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                uint16_t* lds_a, uint16_t* lds_b, int64_t K,
-                                                int64_t k0) {
-    static_assert(P >= 0 && P < kDmaPerStage, "stage_load has kDmaPerStage parts");
+                                                uint16_t* slot, int64_t K, int64_t k0) {
+    static_assert(P >= 0 && P < kDmaPerStage, "a stage has kDmaPerStage parts");
+    constexpr bool kA = P < kDmaA;
     const int w = (int)threadIdx.x >> 6;
     const int l = (int)threadIdx.x & 63;
-    const int rbase = kRowsPerWave * w + 16 * (P >> 1);
+    const int rbase = kA ? kRowsA * w + 16 * P : kRowsB * w + 16 * (P - kDmaA);
     const int row = rbase + (l >> 2);
     const int c = swz(row, l & 3);
     const int64_t k = k0 + 8 * c;
     const uint32_t off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : kOutOfRange;
-    if (P & 1)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (__attribute__((address_space(3))) void*)(lds_b + rbase * kStageK), 16, off, 0, 0, 0);
-    else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(lds_a + rbase * kStageK), 16, off, 0, 0, 0);
+    uint16_t* const dst = (kA ? slot : slot + kStageA) + rbase * kStageK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kA ? ra : rb, (__attribute__((address_space(3))) void*)dst,
+                                             16, off, 0, 0, 0);
+}
+
+template <int... Ps>
+__device__ __forceinline__ void stage_load_seq(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                               uint16_t* slot, int64_t K, int64_t k0,
+                                               std::integer_sequence<int, Ps...>) {
+    (stage_load_part<Ps>(ra, rb, slot, K, k0), ...);
+}
+
+// Every load of one stage into its slot.
+__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                           uint16_t* slot, int64_t K, int64_t k0) {
+    stage_load_seq(ra, rb, slot, K, k0, std::make_integer_sequence<int, kDmaPerStage>{});
 }
 
 // Wait until at most n of this wave's vector memory operations are outstanding
@@ -266,7 +268,7 @@ __device__ __forceinline__ void post_op(const PostCtx& c) {
         if constexpr (J < kReads) {
             read_frag<J>(*c.fr, c.a, c.b);
         } else {
-            if (c.refill) stage_load_part<J - kReads>(c.ra, c.rb, c.st, c.st + kStageElems, c.K, c.k0);
+            if (c.refill) stage_load_part<J - kReads>(c.ra, c.rb, c.st, c.K, c.k0);
         }
         sb();
     }
@@ -289,7 +291,7 @@ __device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Fra
             acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
 }
 
-// One 256 x 256 output tile: C[i, n] = sum_k A[i, k] B^T[n, k] for the
+// One kTileM x kTileN output tile: C[i, n] = sum_k A[i, k] B^T[n, k] for the
 // rows_valid rows of A at a_rows and the cols_valid rows of B^T at bt_rows (both
 // K-contiguous bf16), stored at c (row stride ldc elements) as bf16 rounded to
 // nearest even, or (F32OUT) as the fp32 accumulators themselves.
@@ -311,8 +313,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only this tile's LDS loads in flight below
     // Stage s lives in slot s mod kStages; only stages that exist are loaded.
     for (int64_t s = 0; s < nk && s < kStages - 1; ++s) {
-        uint16_t* st = lds + s * 2 * kStageElems;
-        stage_load(ra, rb, st, st + kStageElems, K, s * kStageK);
+        stage_load(ra, rb, lds + s * kSlotElems, K, s * kStageK);
     }
     // Software pipeline over stages, one stage of LDS loads ahead of the reads:
     //   MFMAs of f0(s), the reads of f1(s) spread between them | wait for f1(s),
@@ -327,18 +328,17 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
     // (a slot's stale contents, never used): those reads are drained after the
     // loop.  Every branch below is uniform and guards loads only, so the MFMA
     // sequence is the same on every path.
-    auto slot = [&](int64_t s) { return lds + (s % kStages) * 2 * kStageElems; };
+    auto slot = [&](int64_t s) { return lds + (s % kStages) * kSlotElems; };
     // stages issued after stage s when the last one issued is `last`
     auto issued_after = [&](int64_t s, int64_t last) { return (int)(last - s); };
     wait_stages_after(issued_after(0, nk - 1 < kStages - 2 ? nk - 1 : kStages - 2));
     __builtin_amdgcn_s_barrier();
-    if (kStages - 1 < nk) stage_load(ra, rb, slot(kStages - 1), slot(kStages - 1) + kStageElems, K,
-                                     (int64_t)(kStages - 1) * kStageK);
+    if (kStages - 1 < nk) stage_load(ra, rb, slot(kStages - 1), K, (int64_t)(kStages - 1) * kStageK);
     const int wave = (int)threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const uint32_t oa0 = frag_offset(kWaveRows * wm, 0), oa1 = frag_offset(kWaveRows * wm, 1);
-    const uint32_t ob0 = frag_offset(kWaveCols * wn, 0) + 2u * kStageElems;
-    const uint32_t ob1 = frag_offset(kWaveCols * wn, 1) + 2u * kStageElems;
+    const uint32_t ob0 = frag_offset(kWaveCols * wn, 0) + 2u * kStageA;
+    const uint32_t ob1 = frag_offset(kWaveCols * wn, 1) + 2u * kStageA;
     Frags f0, f1;
     read_frags(f0, lds_addr(slot(0)) + oa0, lds_addr(slot(0)) + ob0);
     for (int64_t s = 0; s < nk; ++s) {
@@ -372,9 +372,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
         // other half only help with the stores.
         uint8_t* const t = reinterpret_cast<uint8_t*>(lds);
         const bool vec = (cbase & 15u) == 0 && (ldc & 3) == 0;
-        constexpr int kPieces = kEpiRows32 * kGemmBM / 4;  // 4 floats per piece
+        constexpr int kPieces = kEpiRows32 * kTileN / 4;  // 4 floats per piece
         const int my_half = kWaveRows * wm / kEpiRows32;
-        for (int h = 0; h < kGemmBM / kEpiRows32; ++h) {
+        for (int h = 0; h < kTileM / kEpiRows32; ++h) {
             __builtin_amdgcn_s_barrier();  // the ring, or the previous half, is free
             if (my_half == h) {
 #pragma unroll
@@ -392,8 +392,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
             }
             __syncthreads();
             for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
-                const int lrow = i / (kGemmBM / 4);
-                const int col0 = (i - lrow * (kGemmBM / 4)) * 4;
+                const int lrow = i / (kTileN / 4);
+                const int col0 = (i - lrow * (kTileN / 4)) * 4;
                 const int row = kEpiRows32 * h + lrow;
                 if (row >= rows_valid || col0 >= cols_valid) continue;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(t + lrow * kEpiPitch32 + col0 * 4);
@@ -429,10 +429,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
         __syncthreads();
         // 16-byte pieces need a 16-byte aligned output and a row stride of whole pieces
         const bool vec = (cbase & 15u) == 0 && (ldc & 7) == 0;
-        constexpr int kPieces = kGemmBM * kGemmBM / 8;  // 8 bf16 per piece
+        constexpr int kPieces = kTileM * kTileN / 8;  // 8 bf16 per piece
         for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
-            const int row = i / (kGemmBM / 8);
-            const int col0 = (i - row * (kGemmBM / 8)) * 8;
+            const int row = i / (kTileN / 8);
+            const int col0 = (i - row * (kTileN / 8)) * 8;
             if (row >= rows_valid || col0 >= cols_valid) continue;
             const u32x4 v = *reinterpret_cast<const u32x4*>(t + row * kEpiPitch + col0 * 2);
             uint16_t* const dst = reinterpret_cast<uint16_t*>(cbase) + (int64_t)row * ldc + col0;
@@ -483,7 +483,7 @@ hipError_t launch_transpose_b(const uint16_t* b, uint16_t* bt, int64_t K, int64_
 }
 
 template <int SYNC>
-__global__ void __launch_bounds__(kGemmThreads, 1) ag_gemm_kernel(AgGemmArgs a) {
+__global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) ag_gemm_kernel(AgGemmArgs a) {
     __shared__ uint16_t lds[kLdsElems];  // 4 stages x (A, B^T), 128 KiB, or the staged output tile
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
@@ -629,9 +629,9 @@ template <bool F32P>
 __device__ __forceinline__ void rs_reduce_tile(const GemmRsArgs& a, int j, int tile) {
     int mb, nb;
     grs_tile(a, tile, &mb, &nb);
-    const int64_t row0 = (int64_t)mb * kRsTile, col0 = (int64_t)nb * kRsTile;
-    const int rows = a.mj - row0 < kRsTile ? (int)(a.mj - row0) : kRsTile;
-    const int cols = a.N - col0 < kRsTile ? (int)(a.N - col0) : kRsTile;
+    const int64_t row0 = (int64_t)mb * kRsTileM, col0 = (int64_t)nb * kRsTileN;
+    const int rows = a.mj - row0 < kRsTileM ? (int)(a.mj - row0) : kRsTileM;
+    const int cols = a.N - col0 < kRsTileN ? (int)(a.N - col0) : kRsTileN;
     uint8_t* const slice = a.base + (int64_t)j * a.stride;
     // 16-byte loads where every row of a tile splits into whole vectors
     constexpr int V = F32P ? 4 : 8;
@@ -642,7 +642,7 @@ __device__ __forceinline__ void rs_reduce_tile(const GemmRsArgs& a, int j, int t
 }
 
 template <int SYNC, bool F32P>
-__global__ void __launch_bounds__(kGemmThreads, 1) gemm_rs_kernel(GemmRsArgs a) {
+__global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(GemmRsArgs a) {
     __shared__ uint16_t lds[kLdsElems];
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
@@ -678,9 +678,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_rs_kernel(GemmRsArgs a) 
                     // rows nb*256 .. of x2_r^T, into slot r of j's receive area
                     int mb, nb;
                     grs_tile(a, t.tile, &mb, &nb);
-                    const int64_t row0 = (int64_t)mb * kRsTile, col0 = (int64_t)nb * kRsTile;
-                    const int rows = a.mj - row0 < kRsTile ? (int)(a.mj - row0) : kRsTile;
-                    const int cols = a.N - col0 < kRsTile ? (int)(a.N - col0) : kRsTile;
+                    const int64_t row0 = (int64_t)mb * kRsTileM, col0 = (int64_t)nb * kRsTileN;
+                    const int rows = a.mj - row0 < kRsTileM ? (int)(a.mj - row0) : kRsTileM;
+                    const int cols = a.N - col0 < kRsTileN ? (int)(a.N - col0) : kRsTileN;
                     const uint8_t* const src_slice = a.base + (int64_t)t.r * a.stride;
                     const uint16_t* x1 = reinterpret_cast<const uint16_t*>(src_slice + a.a_off) +
                                          ((int64_t)t.j * a.mj + row0) * a.K;

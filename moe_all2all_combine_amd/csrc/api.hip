@@ -1057,8 +1057,8 @@ int plan_gemm_rs(int W, int64_t m, int64_t K, int64_t N, int nxcd, int flags,
     a->mj = m / W;
     a->K = K;
     a->N = N;
-    a->ntm = (int)cdiv(a->mj, ra2a::kRsTile);
-    a->ntn = (int)cdiv(N, ra2a::kRsTile);
+    a->ntm = (int)cdiv(a->mj, ra2a::kRsTileM);
+    a->ntn = (int)cdiv(N, ra2a::kRsTileN);
     a->ntiles = a->ntm * a->ntn;
     a->nblocks = (int)cdiv(a->ntiles, ra2a::kRsBlock);
     a->NG = std::max(1, std::min(nxcd, ra2a::kNumXcd));
@@ -1069,7 +1069,7 @@ int plan_gemm_rs(int W, int64_t m, int64_t K, int64_t N, int nxcd, int flags,
     if ((double)a->ntasks_dest * a->dpg >= 2147483647.0 - 65536.0)
         return fail(RA2A_EINVAL, "GEMM+ReduceScatter too large for 32-bit task indices");
     // a GEMM tile's operand rows and the receive area are addressed with 32-bit buffer offsets
-    if ((double)ra2a::kRsTile * K * 2 >= 4294967295.0 - 65536.0)
+    if ((double)ra2a::kRsTileN * K * 2 >= 4294967295.0 - 65536.0)
         return fail(RA2A_EINVAL, "K too large for 32-bit operand offsets");
     if ((double)W * a->mj * N * gemm_rs_elem(*a) >= 4294967295.0 - 65536.0)
         return fail(RA2A_EINVAL, "receive area of 4 GiB or more per slice");

@@ -6,7 +6,7 @@
 // Semantics", section "GEMM + ReduceScatter Overlapping".)  Rank r holds x1_r
 // (m x K) and x2_r, passed transposed as x2_r^T (N x K); output =
 // ReduceScatter(x1 @ x2): rank j receives out_j = rows [j*mj, (j+1)*mj) of
-// sum_r x1_r @ x2_r, mj = m / W.  Producer tasks compute one 256 x 256 tile of
+// sum_r x1_r @ x2_r, mj = m / W.  Producer tasks compute one kRsTileM x kRsTileN tile of
 // rank r's partial for destination j and store it into j's receive area (slot
 // r), then set the (tile, r) signal; the receiver's reduce task waits for the W
 // partials of a tile, adds them in rank order in fp32 and stores the bf16 result.
@@ -18,6 +18,8 @@
 
 #include <stdint.h>
 
+#include "ag_gemm_geom.h"
+
 #if defined(__HIPCC__)
 #define GRS_HD __host__ __device__ __forceinline__
 #else
@@ -26,7 +28,10 @@
 
 namespace ra2a {
 
-constexpr int kRsTile = 256;   // output tile edge
+// Output tiles are the GEMM tile of the matrix-core routine: kRsTileM rows of
+// out_j by kRsTileN columns.
+constexpr int kRsTileM = kGemmBM;
+constexpr int kRsTileN = kGemmBN;
 // Output tiles per queue block.  Measured at W = 8, m = 8192, K = 896, N = 4096
 // (fp32 partials): while a reduce task waited for each partial load before
 // issuing the next, blocks of 8 / 16 / 32 / 64 tiles took 1.105 / 1.017 / 0.991
