@@ -1100,11 +1100,9 @@ RA2A_API int ra2a_gemm_rs(const void* x1, const void* x2t, void* partial, void* 
     if (h->world != W) return fail(RA2A_EINVAL, "W=%d but the heap has %d slices", W, h->world);
     if (!in_heap(h, x2t) || !in_heap(h, partial) || !in_heap(h, out) || !in_heap(h, signals))
         return fail(RA2A_EINVAL, "x2t, partial, out and signals must be inside the heap of x1");
-    int nxcd = 1;
-    int rc = xcd_count(&nxcd);
-    if (rc) return rc;
+    // every argument check before the first device query
     ra2a::GemmRsArgs a{};
-    rc = plan_gemm_rs(W, m, K, N, nxcd, flags, &a);
+    int rc = plan_gemm_rs(W, m, K, N, ra2a::kNumXcd, flags, &a);
     if (rc) return rc;
     const size_t o_a = sym_offset(h, x1), o_b = sym_offset(h, x2t), o_p = sym_offset(h, partial);
     const size_t o_o = sym_offset(h, out), o_s = sym_offset(h, signals);
@@ -1123,6 +1121,11 @@ RA2A_API int ra2a_gemm_rs(const void* x1, const void* x2t, void* partial, void* 
             if (offs[i] < offs[k2] + lens[k2] && offs[k2] < offs[i] + lens[i])
                 return fail(RA2A_EINVAL, "x1, x2t, partial, out and signals must not overlap");
     }
+    int nxcd = 1;
+    rc = xcd_count(&nxcd);
+    if (rc) return rc;
+    rc = plan_gemm_rs(W, m, K, N, nxcd, flags, &a);  // the queues of this device's XCDs
+    if (rc) return rc;
     rc = ensure_err(h);
     if (rc) return rc;
     a.base = h->base;

@@ -193,3 +193,48 @@ def test_dispatch_signal_slots():
     o = ra2a.Opts(direction=ra2a.DIR_DISPATCH)
     assert ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", o) == (
         8 * 16 * 8, 0, ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS)
+
+
+# ---- argument checks of the AllToAll and GEMM+ReduceScatter entry points ----------
+# (all rejected before any device call, on an attached address range never dereferenced)
+
+def _a2v(h, inp, cnt, out, rc, sig, W=4, row_bytes=64, in_rows=100, out_rows=100, chunk=0, flags=0):
+    return ra2a.lib().ra2a_alltoallv(inp, cnt, out, rc, sig, W, row_bytes, in_rows, out_rows, chunk,
+                                     flags, None)
+
+
+def test_alltoallv_rejects_bad_arguments(fake_heap):
+    b = FAKE_BASE
+    inp, out, cnt, rc, sig = b, b + (1 << 20), b + (2 << 20), b + (2 << 20) + 256, b + (3 << 20)
+    E = ra2a.EINVAL
+    assert _a2v(fake_heap, 0x1000, cnt, out, rc, sig) == E                      # in outside any heap
+    assert _a2v(fake_heap, inp, cnt, out, rc, 0x1000) == E                      # signals outside
+    assert _a2v(fake_heap, inp, cnt, out, rc, sig, W=3) == E                    # W != slices
+    assert _a2v(fake_heap, inp, cnt, out, rc, sig, W=33) == E                   # W above 32
+    assert _a2v(fake_heap, inp + 8, cnt, out, rc, sig) == E                     # in not 16-aligned
+    assert _a2v(fake_heap, inp, cnt + 4, out, rc, sig) == E                     # counts not 8-aligned
+    assert _a2v(fake_heap, inp, cnt, inp + 4096, rc, sig) == E                  # out overlaps in
+    assert _a2v(fake_heap, inp, cnt, out, rc, sig, out_rows=1 << 20) == E       # out past the slice
+    assert _a2v(fake_heap, inp, cnt, out, rc, sig, chunk=24) == E               # chunk not 16-multiple
+    assert _a2v(fake_heap, inp, cnt, out, rc, sig, flags=2) == E                # unknown flag
+    assert _a2v(fake_heap, inp, cnt, out, rc, sig, row_bytes=0) == E
+    assert _a2v(fake_heap, 0, cnt, out, rc, sig) == E                           # NULL
+
+
+def _grs(h, x1, x2t, p, out, sig, W=4, m=64, K=64, N=64, flags=0):
+    return ra2a.lib().ra2a_gemm_rs(x1, x2t, p, out, sig, W, m, K, N, flags, None)
+
+
+def test_gemm_rs_rejects_bad_arguments(fake_heap):
+    b = FAKE_BASE
+    x1, x2t, p, out, sig = b, b + (1 << 18), b + (1 << 19), b + (1 << 20), b + (2 << 20)
+    E = ra2a.EINVAL
+    assert _grs(fake_heap, 0x1000, x2t, p, out, sig) == E                        # x1 outside the heap
+    assert _grs(fake_heap, x1, x2t, p, out, sig, W=2) == E                       # W != slices
+    assert _grs(fake_heap, x1, x2t, p, out, sig, m=66) == E                      # m not divisible by W
+    assert _grs(fake_heap, x1, x2t, p, out, sig, K=12) == E                      # K not a multiple of 8
+    assert _grs(fake_heap, x1, x2t, p + 8, out, sig) == E                        # partial not 16-aligned
+    assert _grs(fake_heap, x1, x1 + 4096, p, out, sig) == E                      # x2t overlaps x1
+    assert _grs(fake_heap, x1, x2t, p, out, b + (4 << 20) - 64) == E             # signals past the slice
+    assert _grs(fake_heap, x1, x2t, p, out, sig, flags=8) == E                   # unknown flag
+    assert _grs(fake_heap, x1, x2t, 0, out, sig) == E                            # NULL
