@@ -331,7 +331,10 @@ int ra2a_rev_all2all_workspace_bytes(int W, int64_t S, int64_t H, int64_t D, int
  * complete, copies the ring into out_j and hands the ring slot back.
  * Afterwards every region-A slot holds W (ADD) or 1 (SET) and every region-B
  * slot the number of consumer work items that used it.  Staging (staged mode)
- * comes from the heap (see workspace_bytes).
+ * comes from the heap (see workspace_bytes).  Under stream capture (a HIP graph)
+ * the reset is always a launch of its own, so replays stay correct; make one call
+ * outside capture first (the first call on a heap allocates its error word and
+ * probes the device's XCDs).
  * Errors: EINVAL, ENOMEM (heap too small for the staging ring), EHIP.           */
 int ra2a_rev_all2all(const void *in, void *out, uint64_t *signals, int W, int64_t S, int64_t H,
                      int64_t D, int dtype, void *stream);

@@ -520,10 +520,15 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     const int64_t nstamps = a.stamps ? (int64_t)W * pl.regionA : 0;
     // In-launch reset: direct mode, unless asked for a separate launch, and only
     // when the occupancy leaves room for the zeroing workgroups beside the
-    // persistent ones (they must run whatever those do).
+    // persistent ones (they must run whatever those do).  Not under stream capture:
+    // a replayed launch would carry the tag it was captured with, the reset flags
+    // would already hold it, and producers could signal before the zeroing.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    he = hipStreamIsCapturing(st, &cap);
+    if (he != hipSuccess) return hip_fail(he, "hipStreamIsCapturing");
     const int per_cu = grid / std::max(1, ncu);
     const bool in_launch = pl.direct && !(opts && opts->separate_reset) && occ > per_cu &&
-                           (!skip || nstamps > 0);
+                           (!skip || nstamps > 0) && cap == hipStreamCaptureStatusNone;
     if (in_launch) {
         // about 16 slots per thread and zeroing workgroup, at most kResetFlags of them
         const int64_t work = (skip ? 0 : reset_slots * W) + nstamps;  // words to zero

@@ -239,6 +239,42 @@ def test_direct_reset_clears_dirty_signals(reset):
         case.close()
 
 
+@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
+def test_graph_capture_and_replay(mode):
+    """A combine captured in a HIP graph and replayed three times, with eager work
+    between the replays (outputs poisoned, signal arrays and control words filled
+    with garbage): every replay's output equals the oracle's and its signals the
+    eager call's.  Under capture the reset is a launch of its own."""
+    W, S, H, D = 4, 96, 4, 64
+    wl = synthgen.small_workload(W, S, H, D, "bf16", seed=31, tile=(32, 1, 64))
+    case = CombineCase(wl, opts_for(wl, mode=mode, consumer_split=2))
+    say(f"[case] graph capture and replay, mode={mode}")
+    try:
+        ins = synthgen.make_inputs(wl)
+        want = oracle.combine(ins)
+        case.upload(ins)
+        case.run_pipelined()  # the first call on the heap, outside capture
+        torch.cuda.synchronize()
+        case.check_device()
+        eager_sig = [case.signals(j) for j in range(W)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            case.run_pipelined()
+        for rep in range(3):
+            case.fill_out(0xA5)
+            case.fill_signals(0x5A)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            case.check_device()
+            for j in range(W):
+                assert case.download(j).tobytes() == want[j].tobytes(), f"replay {rep}, rank {j}"
+                np.testing.assert_array_equal(case.signals(j), eager_sig[j], err_msg=f"replay {rep}")
+        del g
+    finally:
+        case.close()
+
+
 @pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED, ra2a.MODE_BULK, ra2a.MODE_PULL])
 def test_straggler_timestamps(mode):
     """Per-tile completion clocks under a delayed source: every tile is stamped
