@@ -294,8 +294,11 @@ __device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Fra
 // One kTileM x kTileN output tile: C[i, n] = sum_k A[i, k] B^T[n, k] for the
 // rows_valid rows of A at a_rows and the cols_valid rows of B^T at bt_rows (both
 // K-contiguous bf16), stored at c (row stride ldc elements) as bf16 rounded to
-// nearest even, or (F32OUT) as the fp32 accumulators themselves.
-template <bool F32OUT>
+// nearest even, or (F32OUT) as the fp32 accumulators themselves; with NTOUT the
+// output's 16-byte pieces are stored non-temporally (GEMM+ReduceScatter partials,
+// read back only by reduce tasks much later: 3-5 % faster there, measured; the
+// AllGather+GEMM output keeps ordinary stores, 1-3 % faster for it).
+template <bool F32OUT, bool NTOUT = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid,
                                           const uint16_t* bt_rows, int cols_valid, int64_t K,
                                           void* c, int64_t ldc, uint16_t* lds) {
@@ -399,6 +402,12 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
                 const u32x4 v = *reinterpret_cast<const u32x4*>(t + lrow * kEpiPitch32 + col0 * 4);
                 float* const dst = reinterpret_cast<float*>(cbase) + (int64_t)row * ldc + col0;
                 if (vec && col0 + 4 <= cols_valid) {
+                    if (NTOUT)
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+                    else
+                        if (NTOUT)
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+                else
                     *reinterpret_cast<u32x4*>(dst) = v;
                 } else {
 #pragma unroll
@@ -688,7 +697,7 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
                                           col0 * a.K;
                     uint8_t* const part = dst_slice + a.p_off +
                                           (((int64_t)t.r * a.mj + row0) * a.N + col0) * (F32P ? 4 : 2);
-                    gemm_tile<F32P>(x1, rows, x2t, cols, a.K, part, a.N, lds);
+                    gemm_tile<F32P, true>(x1, rows, x2t, cols, a.K, part, a.N, lds);
                     group_release<SYNC>();
                     if (threadIdx.x == 0)
                         sig_update(sig + grs_sig_slot(a, t.tile, t.r) * kSigStrideU64, 1ull, kSigSet);
