@@ -198,6 +198,7 @@ template <> struct Vec<1> { using T = uint8_t; };
 // and the hardware range-checks every access against the descriptor's size
 // (an out-of-range load returns 0 instead of touching other memory).
 constexpr int kPolicySc1 = 16;  // device scope: never served from the CU's L1
+constexpr int kPolicyNt = 2;    // non-temporal: streamed, evicted first
 constexpr uint32_t kBufferDword3 = 0x00020000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
