@@ -405,10 +405,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
                     if (NTOUT)
                         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
                     else
-                        if (NTOUT)
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-                else
-                    *reinterpret_cast<u32x4*>(dst) = v;
+                        *reinterpret_cast<u32x4*>(dst) = v;
                 } else {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
