@@ -40,22 +40,32 @@ static_assert(kWaveRows * (kGemmWaves / 2) == kTileM && kWaveCols * 2 == kTileN,
               "the waves tile the output tile");
 constexpr int kBlkA = kWaveRows / 32;  // 32 x 32 MFMA blocks per wave along rows
 constexpr int kBlkB = kWaveCols / 32;  // ... and along columns
-constexpr int kStageK = 32;        // k per pipeline stage
-constexpr int kStages = kGemmWgPerCu == 1 ? 4 : 3;  // LDS ring depth (kStages - 1 in flight)
+// k per pipeline stage: 64 bf16 = 128 bytes of an operand row, one whole cache
+// line, so that each LDS load instruction fetches 8 whole lines.  With 32-k
+// stages an instruction fetched 16 half lines and the loads filled LDS at 21 B
+// per clock per CU against 36 B with whole lines (measured): below the 32 B per
+// clock the matrix cores need at their peak for a 256 x 256 tile.
+constexpr int kStageK = 64;
+constexpr int kChunks = kStageK / 8;       // 16-byte chunks per operand row of a stage
+constexpr int kStages = 2;                 // LDS ring depth: one stage computed, one landing
 constexpr int kStageA = kTileM * kStageK;  // bf16 of A per stage
 constexpr int kStageB = kTileN * kStageK;  // bf16 of B^T per stage
 constexpr int kSlotElems = kStageA + kStageB;
 constexpr int kRowsA = kTileM / kGemmWaves;  // A rows each wave loads per stage
 constexpr int kRowsB = kTileN / kGemmWaves;  // B^T rows each wave loads per stage
-constexpr int kDmaA = kRowsA / 16, kDmaB = kRowsB / 16;  // its LDS loads (16 rows each)
+constexpr int kDmaRows = 64 / kChunks;       // rows per LDS load instruction (1 KiB)
+constexpr int kDmaA = kRowsA / kDmaRows, kDmaB = kRowsB / kDmaRows;  // a wave's LDS loads per stage
 constexpr int kDmaPerStage = kDmaA + kDmaB;
-static_assert(kRowsA % 16 == 0 && kRowsB % 16 == 0, "whole 16-row LDS loads");
+static_assert(kRowsA % kDmaRows == 0 && kRowsB % kDmaRows == 0, "whole LDS load instructions");
+constexpr int kKSteps = kStageK / 16;      // k16 MFMA steps per stage
+static_assert(kKSteps == 4, "the main loop runs four k16 quarters per stage");
 // bf16 epilogue: the output tile staged in LDS, rows padded by 16 bytes so that the
 // two rows one write instruction touches fall in different banks
 constexpr int kEpiPitch = kTileN * 2 + 16;                   // bytes per staged row
 constexpr int kLdsElems = (kStages * kSlotElems) > (kTileM * kEpiPitch / 2)
                               ? (kStages * kSlotElems)
                               : (kTileM * kEpiPitch / 2);    // uint16 elements of the LDS array
+static_assert(2 * kLdsElems * kGemmWgPerCu + 1024 <= 160 * 1024, "the LDS of a CU holds its workgroups");
 // fp32 epilogue: half the tile's rows at a time, rows padded by 32 bytes (the two
 // rows one write instruction touches then fall in the two halves of the banks)
 constexpr int kEpiRows32 = kTileM / 2;
@@ -70,21 +80,24 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// LDS stage layout of an operand: its tile rows x 32 k (64 bytes per row, four 16-byte
-// chunks).  Chunk c of row r is stored at position c ^ g(r), g(r) = (r >> 2) & 3.
-// Of the XOR patterns measured with the LDS bank-conflict counter on gfx950 for
-// these fragment reads (32 consecutive rows at one chunk, and the same rows at
-// the next chunk), this one is the only conflict-free one: (r >> 1) & 3 and
-// ((r >> 1) ^ (r >> 3)) & 3 stall 4 cycles per read, r & 3 and no swizzle 12.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+// LDS stage layout of an operand: its tile rows x 64 k (128 bytes per row, eight
+// 16-byte chunks).  Chunk c of row r is stored at position c ^ g(r),
+// g(r) = (r ^ ((r >> 3) & 3)) & 7.  A fragment read takes 32 consecutive rows at
+// one chunk (lanes 0-31) and the same rows at the next chunk (lanes 32-63).  With
+// 64 banks serving 16 lanes a clock (the model the bank-conflict counter bore
+// out for 64-byte rows) the even rows of any 16 then cover the 8 chunk positions
+// once, and so do the odd rows; with 32 banks serving 8 lanes a clock, any 8
+// consecutive rows cover them once.  g depends on r mod 32 only, so the blocks
+// of a wave (rows + 32 x) sit at fixed offsets.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ ((r >> 3) & 3)) & 7); }
 
 // Offset sent for a chunk that must read as zero: past any buffer's range.
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
-// One of the kDmaPerStage LDS loads of a stage (k0 .. k0 + 32): parts 0 .. kDmaA-1
+// One of the kDmaPerStage LDS loads of a stage (k0 .. k0 + 64): parts 0 .. kDmaA-1
 // load this wave's A rows, the others its B^T rows, into the stage's slot (A
 // first, then B^T).  Each wave instruction fills 1 KiB of LDS, lane l landing at
-// byte 16 l: 16 rows x 4 chunks; the lane therefore fetches the logical chunk
+// byte 16 l: 8 rows x 8 chunks; the lane therefore fetches the logical chunk
 // that belongs at its swizzled position.  Rows past the operand's buffer and k
 // past K read as 0.
 template <int P>
@@ -94,9 +107,9 @@ __device__ __forceinline__ void stage_load_part(__amdgpu_buffer_rsrc_t ra, __amd
     constexpr bool kA = P < kDmaA;
     const int w = (int)threadIdx.x >> 6;
     const int l = (int)threadIdx.x & 63;
-    const int rbase = kA ? kRowsA * w + 16 * P : kRowsB * w + 16 * (P - kDmaA);
-    const int row = rbase + (l >> 2);
-    const int c = swz(row, l & 3);
+    const int rbase = kA ? kRowsA * w + kDmaRows * P : kRowsB * w + kDmaRows * (P - kDmaA);
+    const int row = rbase + l / kChunks;
+    const int c = swz(row, l % kChunks);
     const int64_t k = k0 + 8 * c;
     const uint32_t off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : kOutOfRange;
     uint16_t* const dst = (kA ? slot : slot + kStageA) + rbase * kStageK;
@@ -115,18 +128,6 @@ __device__ __forceinline__ void stage_load_seq(__amdgpu_buffer_rsrc_t ra, __amdg
 __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                            uint16_t* slot, int64_t K, int64_t k0) {
     stage_load_seq(ra, rb, slot, K, k0, std::make_integer_sequence<int, kDmaPerStage>{});
-}
-
-// Wait until at most n of this wave's vector memory operations are outstanding
-// (they complete in issue order): the LDS loads of the stages issued after the
-// one about to be read.
-__device__ __forceinline__ void wait_stages_after(int n) {
-    if (n >= 2)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * kDmaPerStage) : "memory");
-    else if (n == 1)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kDmaPerStage) : "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Matrix-core work: wave (wm, wn) owns rows kWaveRows wm .. + kWaveRows and
@@ -184,7 +185,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
 }
 
 // Lane byte offsets, inside an operand's stage slot, of the lane's fragment of
-// block 0 for k16 step kk: row row0 + (l mod 32), chunk swz(row, 2 kk + l / 32).
+// block 0 for k16 step kk (0 .. 3): row row0 + (l mod 32), chunk swz(row, 2 kk + l / 32).
 // The swizzle depends only on the row mod 32, so the other blocks (rows + 32 x)
 // sit at fixed offsets of 32 x 64 bytes.
 __device__ __forceinline__ uint32_t frag_offset(int row0, int kk) {
@@ -223,14 +224,15 @@ __device__ __forceinline__ void mma_one(f32x16 (&acc)[kBlkA][kBlkB], const Frags
 
 __device__ __forceinline__ void sb() { __builtin_amdgcn_sched_barrier(0); }
 
-// The interleaving of a half-stage: kMfma MFMAs, and after MFMA i the memory
+// The interleaving of a k16 step: kMfma MFMAs, and after MFMA i the memory
 // operations j (of n in all) with j * kMfma / n == i, so they spread evenly and
 // the earliest ones come first.
 constexpr int kMfma = kBlkA * kBlkB;
 constexpr int kReads = kBlkA + kBlkB;
 constexpr int op_slot(int j, int n) { return j * kMfma / n; }
 
-// Before the barrier: the MFMAs of f0(s), with the reads of f1(s) between them.
+// A k16 step before the barrier: the MFMAs of one fragment set, with the reads of
+// the next step's fragments (into the other set) between them.
 struct PreCtx {
     Frags* fr;
     uint32_t a, b;
@@ -247,13 +249,14 @@ __device__ __forceinline__ void pre_ops(const PreCtx& c, std::integer_sequence<i
     (pre_op<I, Js>(c), ...);
 }
 template <int... Is>
-__device__ __forceinline__ void pre_half(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PreCtx& c,
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PreCtx& c,
                                          std::integer_sequence<int, Is...>) {
     ((mma_one<Is>(acc, fm), sb(), pre_ops<Is>(c, std::make_integer_sequence<int, kReads>{})), ...);
 }
 
-// After the barrier: the MFMAs of f1(s), with the reads of f0(s+1) and then
-// (when `refill`) the loads refilling the freed slot between them.
+// The last k16 step of a stage, after the barrier: its MFMAs, with the reads of
+// the next stage's first fragments and then (when `refill`) the loads refilling
+// the freed slot between them.
 struct PostCtx {
     Frags* fr;
     uint32_t a, b;
@@ -278,7 +281,7 @@ __device__ __forceinline__ void post_ops(const PostCtx& c, std::integer_sequence
     (post_op<I, Js>(c), ...);
 }
 template <int... Is>
-__device__ __forceinline__ void post_half(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PostCtx& c,
+__device__ __forceinline__ void mma_step_refill(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PostCtx& c,
                                           std::integer_sequence<int, Is...>) {
     ((mma_one<Is>(acc, fm), sb(), post_ops<Is>(c, std::make_integer_sequence<int, kReads + kDmaPerStage>{})), ...);
 }
@@ -314,52 +317,64 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
         for (int y = 0; y < kBlkB; ++y) acc[x][y] = f32x16{};
     const int64_t nk = (K + kStageK - 1) / kStageK;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only this tile's LDS loads in flight below
-    // Stage s lives in slot s mod kStages; only stages that exist are loaded.
-    for (int64_t s = 0; s < nk && s < kStages - 1; ++s) {
-        stage_load(ra, rb, lds + s * kSlotElems, K, s * kStageK);
+    // Stage s lives in slot s mod 2.  Both slots are loaded up front (the second
+    // only if its stage exists); stage 0 lands before the first reads.
+    stage_load(ra, rb, lds, K, 0);
+    if (nk > 1) {
+        stage_load(ra, rb, lds + kSlotElems, K, kStageK);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kDmaPerStage) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    // Software pipeline over stages, one stage of LDS loads ahead of the reads:
-    //   MFMAs of f0(s), the reads of f1(s) spread between them | wait for f1(s),
-    //   wait for stage s+1, barrier | MFMAs of f1(s), the reads of f0(s+1) and
-    //   then the LDS loads refilling the slot of stage s with stage s+4 spread
-    //   between them
-    // so the LDS latency of each half hides under the other half's MFMAs, and the
-    // memory instructions issue while the matrix core works (one MFMA, then one
+    __builtin_amdgcn_s_barrier();
+    // Software pipeline over stages of four k16 steps, the fragments of step q+1
+    // read into the other register set while the MFMAs of step q run:
+    //   q0: MFMAs of f0 = (s, 0), reads of f1 = (s, 1)
+    //   q1: MFMAs of f1,          reads of f0 = (s, 2)
+    //   q2: MFMAs of f0,          reads of f1 = (s, 3)
+    //   wait for f1 (every read of stage s is in) and for stage s+1 (the only
+    //   LDS loads in flight), barrier
+    //   q3: MFMAs of f1,          reads of f0 = (s+1, 0), then the loads
+    //       refilling slot s mod 2 with stage s+2
+    // so the LDS latency of each step hides under the previous step's MFMAs, and
+    // the memory instructions issue while the matrix core works (one MFMA, then one
     // memory instruction: the MFMA runs on while the next instruction issues).  A
     // slot is refilled only after the barrier that follows every wave's wait for
-    // its own reads of it.  The last iteration reads f0 of a stage past the end
-    // (a slot's stale contents, never used): those reads are drained after the
-    // loop.  Every branch below is uniform and guards loads only, so the MFMA
-    // sequence is the same on every path.
-    auto slot = [&](int64_t s) { return lds + (s % kStages) * kSlotElems; };
-    // stages issued after stage s when the last one issued is `last`
-    auto issued_after = [&](int64_t s, int64_t last) { return (int)(last - s); };
-    wait_stages_after(issued_after(0, nk - 1 < kStages - 2 ? nk - 1 : kStages - 2));
-    __builtin_amdgcn_s_barrier();
-    if (kStages - 1 < nk) stage_load(ra, rb, slot(kStages - 1), K, (int64_t)(kStages - 1) * kStageK);
+    // its own reads of it; stage s+2 then has q3 of stage s and q0..q2 of stage
+    // s+1 to land.  The last iteration reads f0 of a stage past the end (a slot's
+    // stale contents, never used): those reads are drained after the loop.  Every
+    // branch below is uniform and guards loads only, so the MFMA sequence is the
+    // same on every path.
+    auto slot = [&](int64_t s) { return lds + (s & 1) * kSlotElems; };
     const int wave = (int)threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const uint32_t oa0 = frag_offset(kWaveRows * wm, 0), oa1 = frag_offset(kWaveRows * wm, 1);
-    const uint32_t ob0 = frag_offset(kWaveCols * wn, 0) + 2u * kStageA;
-    const uint32_t ob1 = frag_offset(kWaveCols * wn, 1) + 2u * kStageA;
+    // Step q's fragments sit at step 0's offsets XOR (q << 5): the chunk index
+    // 2 q + lane / 32, XORed with g(row), only moves in bits 1-2 with q, which are
+    // bits 5-6 of the byte offset (rows are 128 bytes).
+    static_assert(kStageK * 2 == 128, "rows of 128 bytes");
+    const uint32_t oa = frag_offset(kWaveRows * wm, 0);
+    const uint32_t ob = frag_offset(kWaveCols * wn, 0) + 2u * kStageA;
+    constexpr auto kSeq = std::make_integer_sequence<int, kMfma>{};
     Frags f0, f1;
-    read_frags(f0, lds_addr(slot(0)) + oa0, lds_addr(slot(0)) + ob0);
+    read_frags(f0, lds_addr(slot(0)) + oa, lds_addr(slot(0)) + ob);
     for (int64_t s = 0; s < nk; ++s) {
-        const uint32_t ca = lds_addr(slot(s)) + oa1, cb = lds_addr(slot(s)) + ob1;
-        lds_wait<0>(f0);  // the only LDS reads in flight here are f0(s)'s
+        const uint32_t cs = lds_addr(slot(s));
+        lds_wait<0>(f0);  // the only LDS reads in flight here are f0's
         sb();
-        pre_half(acc, f0, PreCtx{&f1, ca, cb}, std::make_integer_sequence<int, kMfma>{});
+        mma_step(acc, f0, PreCtx{&f1, cs + (oa ^ (1u << 5)), cs + (ob ^ (1u << 5))}, kSeq);
+        lds_wait<0>(f1);
+        sb();
+        mma_step(acc, f1, PreCtx{&f0, cs + (oa ^ (2u << 5)), cs + (ob ^ (2u << 5))}, kSeq);
+        lds_wait<0>(f0);
+        sb();
+        mma_step(acc, f0, PreCtx{&f1, cs + (oa ^ (3u << 5)), cs + (ob ^ (3u << 5))}, kSeq);
         lds_wait<0>(f1);  // every read of stage s is in: its slot may be refilled
-        // stage s+1 has landed (issued so far: stages up to min(nk - 1, s + kStages - 1))
-        if (s + 1 < nk) wait_stages_after(issued_after(s + 1, nk - 1 < s + kStages - 1 ? nk - 1 : s + kStages - 1));
+        if (s + 1 < nk) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stage s+1 has landed
         __builtin_amdgcn_s_barrier();
         sb();
-        const uint32_t na = lds_addr(slot(s + 1)) + oa0, nb = lds_addr(slot(s + 1)) + ob0;
-        uint16_t* const st = slot(s);
-        const int64_t k0 = (s + kStages) * kStageK;
-        const bool refill = s + kStages < nk;
-        post_half(acc, f1, PostCtx{&f0, na, nb, ra, rb, st, K, k0, refill},
-                  std::make_integer_sequence<int, kMfma>{});
+        const uint32_t ns = lds_addr(slot(s + 1));
+        mma_step_refill(acc, f1, PostCtx{&f0, ns + oa, ns + ob, ra, rb, slot(s), K, (s + 2) * kStageK, s + 2 < nk},
+                  kSeq);
     }
     lds_wait<0>(f0);  // the reads past the last stage land before their registers are reused
     // epilogue: accumulator register e of block (x, y) holds row 8 (e/4) + 4 (lane/32) + e%4,
