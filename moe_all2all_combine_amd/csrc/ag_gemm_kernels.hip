@@ -505,7 +505,7 @@ hipError_t launch_transpose_b(const uint16_t* b, uint16_t* bt, int64_t K, int64_
 
 template <int SYNC>
 __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) ag_gemm_kernel(AgGemmArgs a) {
-    __shared__ uint16_t lds[kLdsElems];  // 4 stages x (A, B^T), 128 KiB, or the staged output tile
+    __shared__ uint16_t lds[kLdsElems];  // 2 stages x (A, B^T), 128 KiB, or the staged output tile
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
     constexpr bool kOwned = SYNC == kSyncXcd;
