@@ -87,7 +87,22 @@ def cpu_baseline(wl, ins, budget_s=12.0):
     gbs = wl.algorithmic_bytes * reps / el / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full combines of the {wl.name} workload "
-                      f"({wl.algorithmic_bytes >> 20} MiB moved each), one thread, {el:.1f} s"}
+                      f"({wl.algorithmic_bytes >> 20} MiB moved each), one thread, {el:.1f} s",
+            "host": host_cpu()}
+
+
+def host_cpu():
+    """The host the CPU baseline ran on: CPU model, cores this process may use, cores online."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity": len(os.sched_getaffinity(0)), "online": os.cpu_count()}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0

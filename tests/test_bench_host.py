@@ -29,3 +29,12 @@ def test_traffic_record_is_tied_to_the_kernel_sources():
     t = bench.load_traffic()
     # either the committed counters match the current kernel sources, or no traffic is claimed
     assert t is None or t > synthgen.WORKLOADS[bench.WORKLOAD].algorithmic_bytes * 0.9
+
+
+def test_host_cpu_description():
+    import bench
+
+    h = bench.host_cpu()
+    assert set(h) == {"cpu_model", "affinity", "online"}
+    assert 1 <= h["affinity"] <= h["online"]
+    assert isinstance(h["cpu_model"], str) and h["cpu_model"]
