@@ -100,34 +100,63 @@ constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 // byte 16 l: 8 rows x 8 chunks; the lane therefore fetches the logical chunk
 // that belongs at its swizzled position.  Rows past the operand's buffer and k
 // past K read as 0.
-template <int P>
+//
+// Two ways to address the load, equal in result, chosen per kernel by measurement:
+//  * SM (scalar M0): the wave index is read as a scalar, so the LDS destination
+//    (M0) is scalar arithmetic, and row x K x 2 splits into a scalar part and
+//    lane_rows = (l / kChunks) x K x 2, a per-lane term common to every load of the
+//    tile (lane_rows_of), so no multiply is left in the loop; k is 32-bit (the
+//    host rejects K with tile rows x K x 2 bytes at 4 GiB or more).  GEMM +
+//    ReduceScatter (K = 896): fp32 partials 0.84 -> 0.79 ms, bf16 0.76 -> 0.74 ms;
+//  * otherwise the destination comes from the vector wave index through a
+//    readfirstlane per load and the offset from 64-bit arithmetic the compiler
+//    strength-reduces: AllGather + GEMM (K = 7168) 0.49 against 0.51 ms with SM.
+template <int P, bool SM>
 __device__ __forceinline__ void stage_load_part(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                uint16_t* slot, int64_t K, int64_t k0) {
+                                                uint16_t* slot, int64_t K, int64_t k0, uint32_t lane_rows) {
     static_assert(P >= 0 && P < kDmaPerStage, "a stage has kDmaPerStage parts");
     constexpr bool kA = P < kDmaA;
-    const int w = (int)threadIdx.x >> 6;
     const int l = (int)threadIdx.x & 63;
-    const int rbase = kA ? kRowsA * w + kDmaRows * P : kRowsB * w + kDmaRows * (P - kDmaA);
-    const int row = rbase + l / kChunks;
-    const int c = swz(row, l % kChunks);
-    const int64_t k = k0 + 8 * c;
-    const uint32_t off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : kOutOfRange;
+    uint32_t off;
+    int rbase;
+    if constexpr (SM) {
+        const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        rbase = kA ? kRowsA * w + kDmaRows * P : kRowsB * w + kDmaRows * (P - kDmaA);
+        const int row = rbase + l / kChunks;
+        const int k = (int)k0 + 8 * swz(row, l % kChunks);
+        off = k < (int)K ? (uint32_t)rbase * (uint32_t)K * 2u + lane_rows + (uint32_t)k * 2u : kOutOfRange;
+    } else {
+        const int w = (int)threadIdx.x >> 6;
+        rbase = kA ? kRowsA * w + kDmaRows * P : kRowsB * w + kDmaRows * (P - kDmaA);
+        const int row = rbase + l / kChunks;
+        const int64_t k = k0 + 8 * swz(row, l % kChunks);
+        off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : kOutOfRange;
+    }
     uint16_t* const dst = (kA ? slot : slot + kStageA) + rbase * kStageK;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kA ? ra : rb, (__attribute__((address_space(3))) void*)dst,
                                              16, off, 0, 0, 0);
 }
 
-template <int... Ps>
+template <bool SM, int... Ps>
 __device__ __forceinline__ void stage_load_seq(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                               uint16_t* slot, int64_t K, int64_t k0,
+                                               uint16_t* slot, int64_t K, int64_t k0, uint32_t lane_rows,
                                                std::integer_sequence<int, Ps...>) {
-    (stage_load_part<Ps>(ra, rb, slot, K, k0), ...);
+    (stage_load_part<Ps, SM>(ra, rb, slot, K, k0, lane_rows), ...);
 }
 
 // Every load of one stage into its slot.
+template <bool SM>
 __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                           uint16_t* slot, int64_t K, int64_t k0) {
-    stage_load_seq(ra, rb, slot, K, k0, std::make_integer_sequence<int, kDmaPerStage>{});
+                                           uint16_t* slot, int64_t K, int64_t k0, uint32_t lane_rows) {
+    stage_load_seq<SM>(ra, rb, slot, K, k0, lane_rows, std::make_integer_sequence<int, kDmaPerStage>{});
+}
+
+// The per-lane row term of the stage loads' offsets, computed once per tile and
+// made opaque so that the compiler cannot fold it back into a multiply per load.
+__device__ __forceinline__ uint32_t lane_rows_of(int64_t K) {
+    uint32_t v = (uint32_t)(((int)threadIdx.x & 63) / kChunks) * (uint32_t)K * 2u;
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 // Matrix-core work: wave (wm, wn) owns rows kWaveRows wm .. + kWaveRows and
@@ -264,26 +293,28 @@ struct PostCtx {
     uint16_t* st;
     int64_t K, k0;
     bool refill;
+    uint32_t lane_rows;
 };
-template <int I, int J>
+template <bool SM, int I, int J>
 __device__ __forceinline__ void post_op(const PostCtx& c) {
     if constexpr (op_slot(J, kReads + kDmaPerStage) == I) {
         if constexpr (J < kReads) {
             read_frag<J>(*c.fr, c.a, c.b);
         } else {
-            if (c.refill) stage_load_part<J - kReads>(c.ra, c.rb, c.st, c.K, c.k0);
+            if (c.refill) stage_load_part<J - kReads, SM>(c.ra, c.rb, c.st, c.K, c.k0, c.lane_rows);
         }
         sb();
     }
 }
-template <int I, int... Js>
+template <bool SM, int I, int... Js>
 __device__ __forceinline__ void post_ops(const PostCtx& c, std::integer_sequence<int, Js...>) {
-    (post_op<I, Js>(c), ...);
+    (post_op<SM, I, Js>(c), ...);
 }
-template <int... Is>
+template <bool SM, int... Is>
 __device__ __forceinline__ void mma_step_refill(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PostCtx& c,
-                                          std::integer_sequence<int, Is...>) {
-    ((mma_one<Is>(acc, fm), sb(), post_ops<Is>(c, std::make_integer_sequence<int, kReads + kDmaPerStage>{})), ...);
+                                                std::integer_sequence<int, Is...>) {
+    ((mma_one<Is>(acc, fm), sb(), post_ops<SM, Is>(c, std::make_integer_sequence<int, kReads + kDmaPerStage>{})),
+     ...);
 }
 
 __device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Frags& f) {
@@ -300,8 +331,9 @@ __device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Fra
 // nearest even, or (F32OUT) as the fp32 accumulators themselves; with NTOUT the
 // output's 16-byte pieces are stored non-temporally (GEMM+ReduceScatter partials,
 // read back only by reduce tasks much later: 3-5 % faster there, measured; the
-// AllGather+GEMM output keeps ordinary stores, 1-3 % faster for it).
-template <bool F32OUT, bool NTOUT = false>
+// AllGather+GEMM output keeps ordinary stores, 1-3 % faster for it).  SM selects the
+// stage loads' addressing (stage_load_part).
+template <bool F32OUT, bool NTOUT, bool SM>
 __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid,
                                           const uint16_t* bt_rows, int cols_valid, int64_t K,
                                           void* c, int64_t ldc, uint16_t* lds) {
@@ -319,9 +351,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only this tile's LDS loads in flight below
     // Stage s lives in slot s mod 2.  Both slots are loaded up front (the second
     // only if its stage exists); stage 0 lands before the first reads.
-    stage_load(ra, rb, lds, K, 0);
+    const uint32_t lane_rows = SM ? lane_rows_of(K) : 0u;
+    stage_load<SM>(ra, rb, lds, K, 0, lane_rows);
     if (nk > 1) {
-        stage_load(ra, rb, lds + kSlotElems, K, kStageK);
+        stage_load<SM>(ra, rb, lds + kSlotElems, K, kStageK, lane_rows);
         asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kDmaPerStage) : "memory");
     } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -373,8 +406,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
         __builtin_amdgcn_s_barrier();
         sb();
         const uint32_t ns = lds_addr(slot(s + 1));
-        mma_step_refill(acc, f1, PostCtx{&f0, ns + oa, ns + ob, ra, rb, slot(s), K, (s + 2) * kStageK, s + 2 < nk},
-                  kSeq);
+        mma_step_refill<SM>(
+            acc, f1, PostCtx{&f0, ns + oa, ns + ob, ra, rb, slot(s), K, (s + 2) * kStageK, s + 2 < nk, lane_rows},
+            kSeq);
     }
     lds_wait<0>(f0);  // the reads past the last stage land before their registers are reused
     // epilogue: accumulator register e of block (x, y) holds row 8 (e/4) + 4 (lane/32) + e%4,
@@ -561,7 +595,7 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) ag_gemm_kernel(AgG
                     const int rows_valid = rv < kGemmBM ? (int)rv : kGemmBM;
                     const int64_t n0 = (int64_t)t.nb * kGemmBN;
                     const int cols_valid = a.N - n0 < kGemmBN ? (int)(a.N - n0) : kGemmBN;
-                    gemm_tile<false>(G + row0 * a.K, rows_valid, a.bt + n0 * a.K, cols_valid, a.K,
+                    gemm_tile<false, false, false>(G + row0 * a.K, rows_valid, a.bt + n0 * a.K, cols_valid, a.K,
                                      a.c + row0 * a.N + n0, a.N, lds);
                 }
             }
@@ -712,7 +746,7 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
                                           col0 * a.K;
                     uint8_t* const part = dst_slice + a.p_off +
                                           (((int64_t)t.r * a.mj + row0) * a.N + col0) * (F32P ? 4 : 2);
-                    gemm_tile<F32P, true>(x1, rows, x2t, cols, a.K, part, a.N, lds);
+                    gemm_tile<F32P, true, true>(x1, rows, x2t, cols, a.K, part, a.N, lds);
                     group_release<SYNC>();
                     if (threadIdx.x == 0)
                         sig_update(sig + grs_sig_slot(a, t.tile, t.r) * kSigStrideU64, 1ull, kSigSet);
