@@ -85,6 +85,8 @@ EXACT = [
     (16, 129, 264, 264, 64, 7),    # more shards than XCDs
     (2, 520, 1032, 776, 1000, 1),  # a tile larger than a shard
     (8, 64, 4096, 8, 512, 3),      # N smaller than one column tile
+    (2, 96, 192, 136, 48, 1),      # three 64-k stages: the one refill of the ring
+    (4, 64, 128, 64, 32, 2),       # two whole stages, no refill
 ]
 
 

@@ -81,6 +81,8 @@ EXACT = [
     (2, 2 * 520, 1032, 776),
     (5, 5 * 40, 4096, 16),   # long K, narrow N
     (2, 2 * 2048, 64, 2304),  # 72 tiles per destination: several queue blocks, the last ragged
+    (3, 3 * 96, 192, 136),   # three 64-k stages: the one refill of the ring
+    (2, 2 * 64, 128, 64),    # two whole stages, no refill
 ]
 
 
