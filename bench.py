@@ -425,8 +425,8 @@ def main():
     # resets its signals before its combine starts (event order).
     done = [None] * NSETS
 
-    def step(k, o, overlap=True, reset=True):
-        oi, oo, osg = sets[k % NSETS]
+    def step(k, o, overlap=True, reset=True, nsets=NSETS):
+        oi, oo, osg = sets[k % nsets]
         if not reset:
             pass  # the combine zeroes its own signals
         elif overlap:
@@ -445,11 +445,11 @@ def main():
             fin.record(stream)
             done[k % NSETS] = fin
 
-    def timed(o, steps, warmup, overlap=True, reset=True):
+    def timed(o, steps, warmup, overlap=True, reset=True, nsets=NSETS):
         """Wall-clock ms per step, and ms per step between two HIP events recorded
         on the launch stream around the whole timed region."""
         for k in range(warmup):
-            step(k, o, overlap=overlap, reset=reset)
+            step(k, o, overlap=overlap, reset=reset, nsets=nsets)
         torch.cuda.synchronize()
         assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -457,7 +457,7 @@ def main():
         t0 = time.perf_counter()
         e0.record(stream)
         for k in range(steps):
-            step(k, o, overlap, reset)
+            step(k, o, overlap, reset, nsets)
         e1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -472,6 +472,9 @@ def main():
     inl_ms, kern_ms = timed(opts_lib, args.steps, args.warmup, overlap=False, reset=False)
     serial_ms, _ = timed(opts, args.steps, args.warmup, overlap=False)
     overlap_ms, _ = timed(opts, args.steps, args.warmup, overlap=True)
+    # warm, for context only: every step on one buffer set, whose 256 MiB the
+    # 256 MB MALL largely holds from one step to the next
+    warm_ms, warm_kern_ms = timed(opts_lib, args.steps, args.warmup, overlap=False, reset=False, nsets=1)
     variants = {"in_launch": inl_ms, "serial": serial_ms, "overlapped": overlap_ms}
     mode_used = min(variants, key=variants.get)
     ms_per_step = variants[mode_used]
@@ -531,6 +534,10 @@ def main():
         "overlapped": {"ms_per_step": round(overlap_ms, 5),
                        "note": "each reset launch on a side stream during the previous step's combine"},
         "kernel_timing": "HIP events on the launch stream around the in-launch timed region / launches"}
+    rec["warm"] = {"ms_per_step": round(warm_ms, 5), "value": round(alg / (warm_ms * 1e-3) / 1e9, 2),
+                   "kernel_ms": round(warm_kern_ms, 5),
+                   "note": "context, not the headline: in-launch steps on one buffer set, data left in "
+                           f"the MALL by the previous step; the headline rotates {NSETS} sets (cold)"}
     if args.legs == "all":
         st_ms, _ = timed(opts_st, args.steps, args.warmup, overlap=False)  # reset launch + combine
         st_ok = parity(args.steps - 1)
