@@ -458,11 +458,13 @@ int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int flags, int64_
  *           bf16 (16-byte aligned);
  *   out     slice j: out_j, m/W x N (8-byte aligned);
  *   signals slice j: ra2a_gemm_rs_sizes' slots at 128-byte spacing (8-byte aligned).
- * K must be a multiple of 8.  The signals are zeroed by a reset launch first
+ * K must be a multiple of 8, and 512 * K below 2^32 (a tile's operand rows are
+ * addressed with 32-bit offsets).  The signals are zeroed by a reset launch first
  * unless RA2A_RS_SKIP_RESET.  After the call every tile slot holds 1.  The
  * library owns the buffers until the stream reaches the end of the launch.
  * Errors: EINVAL (shapes, flags, alignment, overlap, a buffer outside the heap
- * or crossing the end of a slice, a receive area of 4 GiB or more), EHIP.      */
+ * or crossing the end of a slice, K too large, a receive area of 4 GiB or more),
+ * EHIP.                                                                        */
 int ra2a_gemm_rs(const void *x1, const void *x2t, void *partial, void *out, uint64_t *signals,
                  int W, int64_t m, int64_t K, int64_t N, int flags, void *stream);
 

@@ -63,3 +63,14 @@ def test_rejected_shapes(args):
     with pytest.raises(ra2a.Ra2aError) as e:
         ra2a.gemm_rs_sizes(*args)
     assert e.value.code == ra2a.EINVAL
+
+
+def test_k_limit_of_32_bit_operand_offsets():
+    """A tile's 256 operand rows of K bf16 are addressed with 32-bit offsets: the
+    largest K accepted keeps 256 * K * 2 bytes below 4 GiB (less a 64 KiB margin)."""
+    ok_k = (1 << 23) - 256           # 256 * K * 2 = 2^32 - 2^17
+    assert ra2a.gemm_rs_sizes(1, 1, ok_k, 8)[0] == 1
+    for K in ((1 << 23) - 128, 1 << 23):
+        with pytest.raises(ra2a.Ra2aError) as e:
+            ra2a.gemm_rs_sizes(1, 1, K, 8)
+        assert e.value.code == ra2a.EINVAL
