@@ -29,6 +29,7 @@ def test_plan_task_count_of_the_workload():
 @pytest.mark.parametrize("bad", [
     dict(W=0), dict(rank=8), dict(rank=-1), dict(m_local=0), dict(K=12), dict(N=4),
     dict(tile_rows=0),
+    dict(K=1 << 23),  # 256 rows x K x 2 bytes reach 4 GiB: past the tile's 32-bit offsets
 ])
 def test_plan_rejects_bad_arguments(bad):
     args = dict(W=8, rank=0, m_local=64, K=64, N=64, tile_rows=16)
@@ -43,3 +44,7 @@ def test_signal_slot_counts():
     assert ra2a.ag_gemm_signal_slots(8, 1024, 128) == (64, 64, ra2a.QUEUE_SLOTS)
     assert ra2a.ag_gemm_signal_slots(3, 300, 100) == (9, 9, ra2a.QUEUE_SLOTS)
     assert ra2a.ag_gemm_signal_slots(2, 5, 1000) == (2, 2, ra2a.QUEUE_SLOTS)  # one tile per shard
+
+
+def test_largest_k_within_32_bit_operand_offsets():
+    assert ra2a.debug_ag_gemm_plan(8, 0, 64, (1 << 23) - 256, 64, 16) > 0
