@@ -307,3 +307,237 @@ def explore_all(spec: ProtocolSpec, max_states: int = 2_000_000) -> Tuple[int, L
             nxt.step(ag)
             stack.append(nxt)
     return len(seen), violations, deadlock
+
+
+# ---------------------------------------------------------------------------
+# Row units: the combine's work cut into units that each fill whole output
+# rows with every source's data, completed per S-block by an arrival count.
+#
+# This is the push mode of the HyperParallel RFC (section 5.1) with one work
+# unit carrying all W sources of some token rows instead of one source's piece
+# of a tile.  The tile signal keeps the pages' meaning -- the tile is complete
+# once it reads W (ADD) or each of its (tile, source) slots reads 1 (SET) -- and
+# a block counter decides which unit may give it that value:
+#   * a unit writes its rows (all sources) into out_j, fences (publishes them),
+#     then adds 1 to the arrival counter of its S-block (j, b);
+#   * the unit whose add brings the counter to the block's unit count signals
+#     every tile of the block: ADD W on each tile slot, or SET 1 on each (tile,
+#     source) slot -- the values W per-source pieces would have left.
+# Readings where the pages say nothing (they have no row units): the counter is
+# a monotone count of arrivals zeroed with the signals before the launch, and
+# it ends at the block's unit count.  Visibility is modelled as above (a write
+# is pending until its writer's fence), so the model checks the counting logic;
+# the device-wide acquire/release pair the completing unit runs on the GPU is
+# what makes the other units' fences cumulative there.
+
+
+def row_unit_counts(S: int, BS: int, KU: int) -> List[int]:
+    """Units of each S-block: ceil(rows of the block / tokens per unit)."""
+    out = []
+    for b in range(-(-S // BS)):
+        rows = min(BS, S - b * BS)
+        out.append(-(-rows // KU))
+    return out
+
+
+def expected_final_block_counts(S: int, BS: int, KU: int) -> List[int]:
+    """Closed-form final arrival counters: each block's counter ends at its unit count."""
+    return row_unit_counts(S, BS, KU)
+
+
+@dataclasses.dataclass(frozen=True)
+class RowSpec:
+    W: int
+    units: Tuple[int, ...]   # unit count of each S-block
+    nstreams: int            # signal tiles per (destination, S-block)
+    protocol: str            # SET | ADD
+    n_workers: int = 2       # units are dealt round-robin, as the static schedule does
+    n_consumers: int = 2
+    # negative controls
+    skip_reset: bool = False          # counters and signals keep the previous launch's finals
+    count_before_fence: bool = False  # the arrival is counted before the rows are published
+    signal_every_unit: bool = False   # no counter: each unit signals its block on its own
+
+
+def row_units(spec: RowSpec) -> List[Tuple[int, int, int]]:
+    """All units (j, b, k), in the static schedule's order: block, unit, destination."""
+    return [(j, b, k) for b, n in enumerate(spec.units) for k in range(n) for j in range(spec.W)]
+
+
+def expected_row_finals(spec: RowSpec) -> Tuple[Dict[tuple, int], Dict[tuple, int]]:
+    """(tile signals, block counters) after a launch, in closed form."""
+    ps = ProtocolSpec(W=spec.W, nbs=len(spec.units), nstreams=spec.nstreams, R=1,
+                      protocol=spec.protocol)
+    cnt = {(j, b): n for j in range(spec.W) for b, n in enumerate(spec.units)}
+    return expected_final_signals(ps), cnt
+
+
+class _RowRun:
+    def __init__(self, spec: RowSpec):
+        self.spec = spec
+        us = row_units(spec)
+        self.work = [us[i::spec.n_workers] for i in range(spec.n_workers)]
+        cons = []
+        for b in range(len(spec.units)):
+            for j in range(spec.W):
+                for t in range(spec.nstreams):
+                    if spec.protocol == ADD:
+                        cons.append((j, t, b))
+                    else:
+                        cons.extend((j, t, b, r) for r in range(spec.W))
+        self.cons = [cons[i::spec.n_consumers] for i in range(spec.n_consumers)]
+        self.wpc = [[0, 0] for _ in self.work]
+        self.cpc = [[0, 0] for _ in self.cons]
+        sig0, cnt0 = expected_row_finals(spec) if spec.skip_reset else ({}, {})
+        self.sig: Dict[tuple, int] = dict(sig0)
+        self.cnt: Dict[tuple, int] = dict(cnt0)
+        self.last: Dict[tuple, bool] = {}
+        self.pending = set()   # (j, b, k) rows written, not yet published
+        self.visible = set()
+        self.violations: List[str] = []
+
+    def _steps(self):
+        if self.spec.signal_every_unit:
+            return ("write", "fence", "signal")
+        if self.spec.count_before_fence:
+            return ("write", "count", "fence", "signal")
+        return ("write", "fence", "count", "signal")
+
+    def _signal_block(self, j, b):
+        for t in range(self.spec.nstreams):
+            if self.spec.protocol == ADD:
+                self.sig[(j, t, b)] = self.sig.get((j, t, b), 0) + self.spec.W
+            else:
+                for r in range(self.spec.W):
+                    self.sig[(j, t, b, r)] = 1
+
+    def work_runnable(self, a):
+        return self.wpc[a][0] < len(self.work[a])
+
+    def work_step(self, a):
+        li, st = self.wpc[a]
+        u = self.work[a][li]
+        j, b, k = u
+        kind = self._steps()[st]
+        if kind == "write":
+            self.pending.add(u)
+        elif kind == "fence":
+            if u in self.pending:
+                self.pending.discard(u)
+                self.visible.add(u)
+        elif kind == "count":
+            c = self.cnt.get((j, b), 0) + 1
+            self.cnt[(j, b)] = c
+            self.last[u] = c == self.spec.units[b]
+        elif kind == "signal":
+            if self.spec.signal_every_unit or self.last.get(u, False):
+                self._signal_block(j, b)
+        st += 1
+        if st == len(self._steps()):
+            li, st = li + 1, 0
+        self.wpc[a] = [li, st]
+
+    def cons_runnable(self, a):
+        li, st = self.cpc[a]
+        if li >= len(self.cons[a]):
+            return False
+        if st:
+            return True
+        c = self.cons[a][li]
+        want = self.spec.W if self.spec.protocol == ADD else 1
+        return self.sig.get(c, 0) == want
+
+    def cons_step(self, a):
+        li, st = self.cpc[a]
+        c = self.cons[a][li]
+        j, b = c[0], c[2]
+        for k in range(self.spec.units[b]):
+            if (j, b, k) not in self.visible:
+                self.violations.append(f"consumer {c} read unpublished rows of unit {(j, b, k)}")
+        self.cpc[a] = [li + 1, 0]
+
+    def agents(self):
+        return [("w", a) for a in range(len(self.work))] + [("c", a) for a in range(len(self.cons))]
+
+    def runnable(self):
+        return [(k, a) for k, a in self.agents()
+                if (self.work_runnable(a) if k == "w" else self.cons_runnable(a))]
+
+    def step(self, ag):
+        k, a = ag
+        if k == "w":
+            self.work_step(a)
+        else:
+            self.cons_step(a)
+
+    def done(self):
+        return (all(pc[0] >= len(l) for pc, l in zip(self.wpc, self.work))
+                and all(pc[0] >= len(l) for pc, l in zip(self.cpc, self.cons)))
+
+    def key(self):
+        return (tuple(map(tuple, self.wpc)), tuple(map(tuple, self.cpc)),
+                tuple(sorted(self.sig.items())), tuple(sorted(self.cnt.items())),
+                tuple(sorted(self.last.items())), tuple(sorted(self.pending)),
+                tuple(sorted(self.visible)), bool(self.violations))
+
+    def clone(self):
+        c = _RowRun.__new__(_RowRun)
+        c.spec, c.work, c.cons = self.spec, self.work, self.cons
+        c.wpc = [list(x) for x in self.wpc]
+        c.cpc = [list(x) for x in self.cpc]
+        c.sig, c.cnt, c.last = dict(self.sig), dict(self.cnt), dict(self.last)
+        c.pending, c.visible = set(self.pending), set(self.visible)
+        c.violations = list(self.violations)
+        return c
+
+
+@dataclasses.dataclass
+class RowOutcome:
+    completed: bool
+    violations: List[str]
+    signals: Dict[tuple, int]
+    counters: Dict[tuple, int]
+
+
+def run_rows_random(spec: RowSpec, seed: int, max_steps: int = 1_000_000) -> RowOutcome:
+    """One execution of the row-unit protocol under a seeded random scheduler."""
+    rng = random.Random(seed)
+    run = _RowRun(spec)
+    for _ in range(max_steps):
+        if run.done():
+            break
+        ready = run.runnable()
+        if not ready:
+            break  # the remaining consumers spin until their bounded wait gives up
+        run.step(rng.choice(ready))
+    return RowOutcome(run.done(), run.violations, run.sig, run.cnt)
+
+
+def explore_rows(spec: RowSpec, max_states: int = 2_000_000) -> Tuple[int, List[str], bool]:
+    """Every interleaving of the row-unit protocol: (states, violations, some path stuck)."""
+    seen = set()
+    stack = [_RowRun(spec)]
+    violations: List[str] = []
+    stuck = False
+    while stack:
+        run = stack.pop()
+        k = run.key()
+        if k in seen:
+            continue
+        seen.add(k)
+        if len(seen) > max_states:
+            raise RuntimeError("state space too large for exhaustive exploration")
+        if run.violations:
+            violations.extend(run.violations)
+            continue
+        if run.done():
+            continue
+        ready = run.runnable()
+        if not ready:
+            stuck = True
+            continue
+        for ag in ready:
+            nxt = run.clone()
+            nxt.step(ag)
+            stack.append(nxt)
+    return len(seen), violations, stuck

@@ -99,3 +99,66 @@ def test_symm_at():
     assert oracle.symm_at(base, stride, world, p, -1) is None
     assert oracle.symm_at(base, stride, world, base + world * stride, 0) is None
     assert oracle.symm_at(base, stride, world, base - 1, 0) is None
+
+
+# ---- row units ---------------------------------------------------------------
+from oracle.protocol import (RowSpec, explore_rows, expected_final_block_counts,  # noqa: E402
+                             expected_row_finals, row_unit_counts, row_units, run_rows_random)
+
+
+def test_row_unit_counts_worked():
+    # S = 37 in S-blocks of 16: rows 16, 16, 5; units of 5 tokens: 4, 4, 1
+    assert row_unit_counts(37, 16, 5) == [4, 4, 1]
+    # units as large as the block: one each; units of one token: the block's rows
+    assert row_unit_counts(37, 16, 16) == [1, 1, 1]
+    assert row_unit_counts(37, 16, 1) == [16, 16, 5]
+    # the bench workload: 512 tokens in blocks of 64, 8-token units
+    assert row_unit_counts(512, 64, 8) == [8] * 8
+    assert expected_final_block_counts(37, 16, 5) == [4, 4, 1]
+
+
+def test_row_unit_counts_brute_force():
+    """Each block's unit count equals the number of distinct (block, unit) pairs
+    met when every token is assigned to unit (token mod BS) div KU of its block."""
+    for S in range(1, 40):
+        for BS in range(1, 12):
+            for KU in range(1, BS + 1):
+                seen = {}
+                for s in range(S):
+                    seen.setdefault(s // BS, set()).add((s % BS) // KU)
+                assert row_unit_counts(S, BS, KU) == [len(seen[b]) for b in sorted(seen)]
+
+
+def row_spec(protocol, **kw):
+    base = dict(W=2, units=(2, 1), nstreams=1, protocol=protocol, n_workers=2, n_consumers=1)
+    base.update(kw)
+    return RowSpec(**base)
+
+
+@pytest.mark.parametrize("workers", [2, 3])
+@pytest.mark.parametrize("protocol", [ADD, SET])
+def test_rows_exhaustive_no_violation(protocol, workers):
+    states, violations, stuck = explore_rows(row_spec(protocol, n_workers=workers))
+    assert states > 100
+    assert violations == [] and not stuck
+
+
+@pytest.mark.parametrize("protocol", [ADD, SET])
+def test_rows_seeded_schedules_match_closed_forms(protocol):
+    spec = row_spec(protocol, W=3, units=(3, 3, 1), nstreams=2, n_workers=4, n_consumers=3)
+    want_sig, want_cnt = expected_row_finals(spec)
+    for seed in range(200):
+        out = run_rows_random(spec, seed)
+        assert out.completed and out.violations == []
+        assert out.signals == want_sig and out.counters == want_cnt
+    # every unit is scheduled once
+    assert len(row_units(spec)) == 3 * 7
+
+
+@pytest.mark.parametrize("control", ["skip_reset", "count_before_fence", "signal_every_unit"])
+@pytest.mark.parametrize("protocol", [ADD, SET])
+def test_rows_negative_controls_fire(control, protocol):
+    # three workers: the two units of block 0 of each destination run on different ones
+    spec = row_spec(protocol, n_workers=3, **{control: True})
+    _, violations, _ = explore_rows(spec)
+    assert violations, f"{control} must let a consumer read unpublished rows"
