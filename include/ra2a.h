@@ -198,10 +198,11 @@ int ra2a_signal_reset(const ra2a_heap_t *heap, uint64_t *sig_sym, int64_t n_slot
 #define RA2A_DIR_DISPATCH 1 /* out_r[j*S + s, h, d] = in_j[s, r*H + h, d] (the inverse) */
 
 /* Where producers put their pieces (ra2a_opts_t.mode). */
-#define RA2A_MODE_DIRECT 1 /* push straight into out_j (default) */
+#define RA2A_MODE_DIRECT 1 /* one piece per (source, tile), straight into out_j */
 #define RA2A_MODE_STAGED 2 /* through a staging ring in slice j, reordered by consumers */
 #define RA2A_MODE_BULK 3   /* two-phase layout with fine-grained signals (see below) */
 #define RA2A_MODE_PULL 4   /* senders stage in their own slice, receivers pull (see below) */
+#define RA2A_MODE_ROWS 5   /* row units: whole rows of out_j, all sources (the default) */
 
 /* Work-queue words the pipelined combine keeps after the hand-back counters
  * (used in slice 0 only, staged mode only; direct mode leaves them 0): per
@@ -243,11 +244,28 @@ typedef struct ra2a_opts {
                                * at timestamps[j * tile_slots + u] (direct mode: the
                                * latest of its pieces' signals; staged mode: the end of
                                * its consumer copy) */
-    int32_t mode;             /* RA2A_MODE_DIRECT (or 0): producers store each piece
+    int32_t mode;             /* 0: RA2A_MODE_DIRECT.
+                               * RA2A_MODE_ROWS: each work unit fills unit_rows whole
+                               * token rows of out_j (the W sources' runs of H*D elements,
+                               * one contiguous range of out_j; W contiguous ranges of
+                               * the inputs) and adds 1 to its S-block's arrival counter
+                               * (region B: one per S-block); the unit that completes the
+                               * block marks every signal tile of the block complete
+                               * (ADD W, or SET 1 on each (tile, source) slot), the values
+                               * W pieces would leave.  Not for the dispatch, nor with a
+                               * straggler source (every unit carries all sources).
+                               * RA2A_MODE_DIRECT: producers store each piece (one
+                               * source's rows of a tile, or a part of them: piece_rows)
                                * straight into its final place in out_j (a symmetric
-                               * buffer) and signal the tile; out_j is complete once
-                               * every tile signal is; no ring, no consumer copy, no
-                               * hand-back, no work queue (a static schedule).
+                               * buffer) and signal the tile.
+                               * Both direct modes: no ring, no consumer copy, no
+                               * hand-back, no work queue (a static schedule); the data
+                               * is released device-wide before a signal, so a tile
+                               * whose signal reads its final value (W under ADD, 1 on
+                               * each of its slots under SET) is complete in out_j and
+                               * visible to any reader on the device that acquires the
+                               * signal (ra2a_wait_signal, or a later kernel), even
+                               * while the launch still runs.
                                * RA2A_MODE_STAGED: producers store into slice j's staging
                                * ring (the pages' window layout), consumers wait, copy
                                * ring -> out_j and hand the ring slot back.
@@ -293,16 +311,28 @@ typedef struct ra2a_opts {
                                * mode zeroes them inside the combine launch) */
     int32_t direction;        /* RA2A_DIR_COMBINE (0, the default) or RA2A_DIR_DISPATCH (the
                                * inverse map; see ra2a_all2all_dispatch) */
+    int32_t unit_rows;        /* RA2A_MODE_ROWS: tokens per row unit (0: the default,
+                               * max(1, 262144 / (W*H*D*e)) -- about 256 KiB of output;
+                               * always capped at tile_s, and a unit never straddles two
+                               * S-blocks) */
+    int32_t piece_rows;       /* RA2A_MODE_DIRECT: tokens per piece, at most tile_s (0:
+                               * the default -- a tile's rows of one source in one piece
+                               * up to 128 KiB, else cut into ceil(bytes / 128 KiB)
+                               * pieces of equal token counts).  With more than one
+                               * piece per tile and source, each tile counts its
+                               * pieces' arrivals in region B and the piece that
+                               * completes it signals it (ADD W, or SET 1 per source) */
     int32_t reserved[1];      /* must be zero */
 } ra2a_opts_t;
 
 /* Number of signal slots the combine needs per slice: `tile_slots` data
  * signals (region A: ADD, one per (s-block, head block, d block) in that
  * order; SET, one per (s-block, head block, d block, source r)), then
- * `credit_slots` ring hand-back counters (region B, staged mode only, 0 in
- * direct mode: ADD [ring slot][merged head block][d block]; SET [ring
- * slot][merged head block][d block][source], where a merged head block is
- * head_merge adjacent head blocks), then `queue_slots` control words
+ * `credit_slots` counters (region B; staged mode: ring hand-back counters, ADD
+ * [ring slot][merged head block][d block], SET [ring slot][merged head
+ * block][d block][source], where a merged head block is head_merge adjacent
+ * head blocks; RA2A_MODE_ROWS: one arrival counter per S-block; 0 in the
+ * other modes), then `queue_slots` control words
  * (RA2A_QUEUE_SLOTS work-queue words, then RA2A_RESET_FLAGS reset flags; 0 for
  * an empty problem).  The
  * `signals` array of a combine must hold the sum of the three in every slice.
@@ -311,26 +341,51 @@ int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t D, int dt
                                   const ra2a_opts_t *opts, int64_t *tile_slots,
                                   int64_t *credit_slots, int64_t *queue_slots);
 
+/* The tiling, mode and work a combine with these options resolves to (no GPU
+ * needed): what the defaults chose, so that callers and tests can predict the
+ * signal arrays.  The launch adds the schedule, which depends on the device:
+ * the direct modes claim their work items dynamically (a counter in the last
+ * RA2A_QUEUE_SLOTS word, slice 0, ending at work_items) when there are at least
+ * 8 per compute unit, else walk them statically (that word stays 0).          */
+typedef struct ra2a_plan {
+    int32_t mode;            /* RA2A_MODE_DIRECT, _ROWS, _STAGED, _BULK or _PULL */
+    int32_t protocol;        /* RA2A_PROTO_ADD or RA2A_PROTO_SET: the signal layout used */
+    int64_t tile_s, tile_h, tile_d;
+    int32_t head_merge;      /* signal tiles of adjacent head blocks moved together */
+    int32_t piece_rows;      /* direct mode: tokens per piece (tile_s in the staged modes) */
+    int32_t pieces_per_tile; /* direct mode: pieces per tile and source, ceil(tile_s /
+                              * piece_rows); > 1 means region B holds arrival counters */
+    int32_t unit_rows;       /* RA2A_MODE_ROWS: tokens per row unit (0 otherwise) */
+    int64_t tile_slots, credit_slots, queue_slots; /* as ra2a_rev_all2all_signal_slots */
+    int64_t work_items;      /* direct modes: pieces or row units per launch (0 otherwise) */
+    size_t workspace_bytes;  /* as ra2a_rev_all2all_workspace_bytes (pipelined) */
+} ra2a_plan_t;
+
+int ra2a_rev_all2all_plan(int W, int64_t S, int64_t H, int64_t D, int dtype,
+                          const ra2a_opts_t *opts, ra2a_plan_t *plan);
+
 /* Staging bytes per slice the library reserves from the heap on first use
  * (pipelined: the ring; two_phase != 0: a full (W, S, H, D) staging area).     */
 int ra2a_rev_all2all_workspace_bytes(int W, int64_t S, int64_t H, int64_t D, int dtype,
                                      const ra2a_opts_t *opts, int two_phase, size_t *bytes);
 
-/* The combine with the signal-pipelined persistent kernel and default options.
- * Every signal slot and work-queue word is zeroed before any producer of the
- * launch signals ("Host Side Modifications").  In direct mode (the default)
- * one launch does both: a few extra workgroups zero the slots and publish
- * their share through the reset flags, and the persistent workgroups walk the
- * producer pieces on a static schedule: each copies one source's part of a
- * tile with 16-byte stores straight into out_j, releases it and, once the
- * reset flags carry this launch's tag, signals the tile.  (Staged mode, or
- * separate_reset, or an occupancy without room for the zeroing workgroups:
- * the reset is a launch of its own before the combine's.)  In staged
+/* The combine with the signal-pipelined persistent kernel and default options
+ * (row units, RA2A_MODE_ROWS).  Every signal slot and work-queue word is zeroed
+ * before any producer of the launch signals ("Host Side Modifications").  In
+ * the direct modes one launch does both: its lowest-numbered workgroups zero the
+ * slots and publish their share through the reset flags (dispatched first, so
+ * no occupancy is needed beside them), and the persistent workgroups walk the
+ * row units (or, RA2A_MODE_DIRECT, the producer pieces) on a static schedule:
+ * each copies its rows with 16-byte stores straight into out_j, releases them
+ * device-wide and, once the reset flags carry this launch's tag, counts or
+ * signals its tiles.  (Staged, bulk and pull modes, or separate_reset: the
+ * reset is a launch of its own before the combine's.)  In staged
  * mode they take tasks from one work queue per XCD: producer pieces into the
  * staging ring, and consumer work, which waits until its tile's signal is
  * complete, copies the ring into out_j and hands the ring slot back.
- * Afterwards every region-A slot holds W (ADD) or 1 (SET) and every region-B
- * slot the number of consumer work items that used it.  Staging (staged mode)
+ * Afterwards every region-A slot holds W (ADD) or 1 (SET), and every region-B
+ * slot the number of consumer work items that used it (staged) or the number
+ * of row units of its S-block (row units).  Staging (staged mode)
  * comes from the heap (see workspace_bytes).  Under stream capture (a HIP graph)
  * the reset is always a launch of its own, so replays stay correct; make one call
  * outside capture first (the first call on a heap allocates its error word and

@@ -11,18 +11,20 @@ Functions keep the C names without the ``ra2a_`` prefix.  Failures raise
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import weakref
 from typing import Optional, Sequence, Tuple
 
 __all__ = [
     "Ra2aError", "Opts", "SymmHeap", "lib", "OK", "EINVAL", "ENOMEM", "EHIP", "ETIMEOUT",
     "EUNSUPPORTED", "EDATA", "A2V_SKIP_RESET", "alltoallv_signal_slots", "alltoallv", "debug_alltoallv_emulate", "SIG_SET", "SIG_ADD", "PROTO_ADD", "PROTO_SET", "MODE_DIRECT", "MODE_STAGED",
-    "QUEUE_SLOTS", "RS_AGENT_SYNC", "RS_SKIP_RESET", "RS_BF16_PARTIALS", "gemm_rs_sizes", "gemm_rs", "debug_gemm_rs_plan", "MODE_BULK", "MODE_PULL", "DIR_COMBINE", "DIR_DISPATCH", "all2all_dispatch", "all2all_dispatch_ex", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
+    "QUEUE_SLOTS", "RS_AGENT_SYNC", "RS_SKIP_RESET", "RS_BF16_PARTIALS", "gemm_rs_sizes", "gemm_rs", "debug_gemm_rs_plan", "MODE_BULK", "MODE_PULL", "MODE_ROWS", "DIR_COMBINE", "DIR_DISPATCH", "all2all_dispatch", "all2all_dispatch_ex", "RESET_FLAGS", "CMP_EQ", "CMP_NE", "CMP_GT", "CMP_GE", "CMP_LT",
     "CMP_LE", "SIG_STRIDE_BYTES", "DTYPES", "symm_heap_create", "symm_heap_attach",
     "symm_heap_destroy", "symm_malloc", "symm_heap_info", "symm_at", "put", "get",
     "put_with_signal", "signal_op", "wait_signal", "signal_reset", "rev_all2all",
-    "rev_all2all_ex", "rev_all2all_two_phase", "rev_all2all_signal_slots",
+    "rev_all2all_ex", "rev_all2all_two_phase", "rev_all2all_plan", "Plan", "rev_all2all_signal_slots",
     "rev_all2all_workspace_bytes", "check", "last_error", "version", "ag_gemm",
     "ag_gemm_signal_slots", "debug_ag_gemm_plan", "AG_AGENT_SYNC", "AG_SKIP_RESET",
     "AG_B_TRANSPOSED",
@@ -37,6 +39,7 @@ PROTO_ADD, PROTO_SET = 1, 2
 MODE_DIRECT, MODE_STAGED = 1, 2
 MODE_BULK = 3
 MODE_PULL = 4
+MODE_ROWS = 5
 QUEUE_SLOTS = 18
 DIR_COMBINE = 0
 DIR_DISPATCH = 1
@@ -68,7 +71,8 @@ class Opts(ctypes.Structure):
         ("consumer_split", ctypes.c_int32), ("skip_reset", ctypes.c_int32),
         ("stream_batch", ctypes.c_int32), ("agent_sync", ctypes.c_int32),
         ("head_merge", ctypes.c_int32), ("separate_reset", ctypes.c_int32),
-        ("direction", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
+        ("direction", ctypes.c_int32), ("unit_rows", ctypes.c_int32),
+        ("piece_rows", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
     ]
 
     def __init__(self, **kw):
@@ -112,6 +116,7 @@ def lib():
         "ra2a_signal_reset": (i32, [vp, vp, i64, vp]),
         "ra2a_rev_all2all_signal_slots": (i32, [i32, i64, i64, i64, i32, vp, ctypes.POINTER(i64),
                                                 ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "ra2a_rev_all2all_plan": (i32, [i32, i64, i64, i64, i32, vp, vp]),
         "ra2a_rev_all2all_workspace_bytes": (i32, [i32, i64, i64, i64, i32, vp, i32,
                                                    ctypes.POINTER(sz)]),
         "ra2a_rev_all2all": (i32, [vp, vp, vp, i32, i64, i64, i64, i32, vp]),
@@ -186,19 +191,50 @@ def _opts(opts):
 
 # ---- heap -------------------------------------------------------------------
 
+# Heaps still open when the interpreter exits are closed by an atexit hook,
+# while torch and the HIP runtime are intact.  (Left to object finalizers or to
+# the library's own unload, their device synchronize and frees would run in
+# whatever order the process tears down torch, the runtime and a profiler.)
+# The hook is registered again when the first torch-backed heap is made, after
+# torch is imported, so that it runs before torch's own exit handlers (atexit
+# runs handlers last-registered first).
+_open_handles = set()
+_torch_heaps = weakref.WeakSet()
+_hook_after_torch = False
+
+
+def _close_all_heaps() -> None:
+    for h in list(_torch_heaps):
+        try:
+            h.close()
+        except Exception:
+            pass
+    for handle in list(_open_handles):
+        try:
+            symm_heap_destroy(handle)
+        except Exception:
+            _open_handles.discard(handle)
+
+
+atexit.register(_close_all_heaps)
+
+
 def symm_heap_create(world: int, slice_bytes: int) -> int:
     h = ctypes.c_void_p()
     _ok(lib().ra2a_symm_heap_create(world, slice_bytes, ctypes.byref(h)))
+    _open_handles.add(h.value)
     return h.value
 
 
 def symm_heap_attach(base: int, world: int, stride: int) -> int:
     h = ctypes.c_void_p()
     _ok(lib().ra2a_symm_heap_attach(base, world, stride, ctypes.byref(h)))
+    _open_handles.add(h.value)
     return h.value
 
 
 def symm_heap_destroy(heap: int) -> None:
+    _open_handles.discard(heap)
     _ok(lib().ra2a_symm_heap_destroy(heap))
 
 
@@ -270,6 +306,26 @@ def rev_all2all_signal_slots(W: int, S: int, H: int, D: int, dtype,
     _ok(lib().ra2a_rev_all2all_signal_slots(W, S, H, D, _dtype(dtype), _opts(opts),
                                             ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+class Plan(ctypes.Structure):
+    """Mirror of ``ra2a_plan_t``: what a combine with given options resolves to."""
+
+    _fields_ = [
+        ("mode", ctypes.c_int32), ("protocol", ctypes.c_int32),
+        ("tile_s", ctypes.c_int64), ("tile_h", ctypes.c_int64), ("tile_d", ctypes.c_int64),
+        ("head_merge", ctypes.c_int32), ("piece_rows", ctypes.c_int32),
+        ("pieces_per_tile", ctypes.c_int32), ("unit_rows", ctypes.c_int32),
+        ("tile_slots", ctypes.c_int64), ("credit_slots", ctypes.c_int64),
+        ("queue_slots", ctypes.c_int64), ("work_items", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def rev_all2all_plan(W: int, S: int, H: int, D: int, dtype, opts=None) -> Plan:
+    pl = Plan()
+    _ok(lib().ra2a_rev_all2all_plan(W, S, H, D, _dtype(dtype), _opts(opts), ctypes.byref(pl)))
+    return pl
 
 
 def rev_all2all_workspace_bytes(W: int, S: int, H: int, D: int, dtype, opts=None,
@@ -367,6 +423,10 @@ class SymmHeap:
 
     def __init__(self, world: int, slice_bytes: int, device=None):
         import torch
+        global _hook_after_torch
+        if not _hook_after_torch:  # see _close_all_heaps
+            atexit.register(_close_all_heaps)
+            _hook_after_torch = True
         align = 2 << 20
         self.world = world
         self.stride = (slice_bytes + align - 1) // align * align
@@ -376,6 +436,7 @@ class SymmHeap:
         self.pad = (-raw) % 256
         self.base = raw + self.pad
         self.handle = symm_heap_attach(self.base, world, self.stride)
+        _torch_heaps.add(self)
 
     def alloc(self, nbytes: int, align: int = 256) -> int:
         return symm_malloc(self.handle, nbytes, align)
@@ -393,9 +454,11 @@ class SymmHeap:
         return self.mem[start:start + nbytes].view(dtype).view(*shape)
 
     def close(self) -> None:
+        """Destroy the heap handle, then drop the torch memory it lived in."""
         if self.handle:
             symm_heap_destroy(self.handle)
             self.handle = None
+        self.mem = None
 
     def __del__(self):
         try:

@@ -42,8 +42,18 @@ namespace {
 constexpr size_t kSliceAlign = size_t(2) << 20;
 constexpr uint64_t kDefaultTimeoutUs = 5000000ull;
 thread_local std::string g_err;
-std::mutex g_reg_mu;
-std::vector<ra2a_heap*> g_heaps;
+// The heap registry lives until the process ends (never destroyed: no exit
+// handler can find it half torn down).
+std::mutex& g_reg_mu = *new std::mutex;
+std::vector<ra2a_heap*>& g_heaps = *new std::vector<ra2a_heap*>;
+
+// Set when the library is unloaded at process exit.  From then on the HIP
+// runtime, the profiler's hooks and torch's allocator may already be gone, so a
+// heap destroyed that late frees host state only and leaves its device memory
+// to the runtime (callers should close heaps before exit; the Python binding
+// does so from an atexit hook).
+std::atomic<bool> g_exiting{false};
+__attribute__((destructor)) void mark_exiting() { g_exiting.store(true); }
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -123,6 +133,17 @@ int ensure_err(ra2a_heap* h) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Default output bytes per row unit (RA2A_MODE_ROWS): the unit_rows default is
+// max(1, kRowUnitBytes / (W*H*D*e)) tokens, at most the S-block.
+constexpr int64_t kRowUnitBytes = 256 << 10;
+// Default bytes per direct-mode piece: a tile's rows of one source larger than
+// this are cut into ceil(bytes / kPieceBytes) pieces of equal token counts.
+constexpr int64_t kPieceBytes = 128 << 10;
+// Direct modes: with at least this many pieces (or row units) per compute unit,
+// the persistent workgroups claim them dynamically, one workgroup per compute
+// unit by default; with fewer, a static schedule with two per compute unit.
+constexpr int64_t kDynPiecesPerCu = 8;
+
 int lowbit_vec(uint64_t m) {
     if ((m & 15u) == 0) return 16;
     if ((m & 7u) == 0) return 8;
@@ -143,6 +164,9 @@ struct Plan {
     int stream_batch;       // 0 = derive from the L2 budget
     int agent_sync;
     int direct;             // 1: direct push (no staging), 0: staged through the ring
+    int rows;               // 1 (with direct): row units -- whole rows of out_j per unit
+    int KU, upb;            // row units: tokens per unit, units per full S-block
+    int PR, nsub;           // direct pieces: tokens per piece, pieces per tile and source
     int inverse;            // 1: the dispatch (the combine's inverse map)
     int bulk;               // 1: two-phase staging layout with fine-grained signals
     int pull;               // 1 (with bulk): staging in the sender's slice, pulled by the receiver
@@ -163,8 +187,14 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (o->separate_reset != 0 && o->separate_reset != 1)
         return fail(RA2A_EINVAL, "separate_reset must be 0 or 1");
     if (o->mode != 0 && o->mode != RA2A_MODE_DIRECT && o->mode != RA2A_MODE_STAGED &&
-        o->mode != RA2A_MODE_BULK && o->mode != RA2A_MODE_PULL)
-        return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_DIRECT, _STAGED, _BULK or _PULL");
+        o->mode != RA2A_MODE_BULK && o->mode != RA2A_MODE_PULL && o->mode != RA2A_MODE_ROWS)
+        return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_ROWS, _DIRECT, _STAGED, _BULK or _PULL");
+    if (o->mode == RA2A_MODE_ROWS && o->direction == RA2A_DIR_DISPATCH)
+        return fail(RA2A_EINVAL, "row units are a combine mode (the dispatch runs in direct mode)");
+    if (o->mode == RA2A_MODE_ROWS && o->straggler_rank >= 0 && o->straggler_delay > 0)
+        return fail(RA2A_EINVAL, "a straggler source needs per-source pieces: every row unit "
+                                 "carries all sources (use RA2A_MODE_DIRECT)");
+    if (o->unit_rows < 0) return fail(RA2A_EINVAL, "unit_rows must be >= 0");
     p->BS = o->tile_s > 0 ? o->tile_s : std::min<int64_t>(S, 64);
     p->TH = o->tile_h > 0 ? o->tile_h : 1;
     p->TD = o->tile_d > 0 ? o->tile_d : D;
@@ -216,6 +246,8 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     p->stream_batch = o->stream_batch;
     p->agent_sync = o->agent_sync ? 1 : 0;
     p->direct = (o->mode == RA2A_MODE_STAGED || p->bulk) ? 0 : 1;
+    // row units only when asked for; the default direct mode moves per-source pieces
+    p->rows = o->mode == RA2A_MODE_ROWS ? 1 : 0;
     p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);
     if (o->consumer_split < 0 || o->wg_per_cu < 0 || o->lookahead < -1)
         return fail(RA2A_EINVAL, "negative option");
@@ -231,6 +263,38 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
         p->ring_bytes = 0;
         p->csplit = 1;
     }
+    // Tokens per piece.  In the staged modes a piece is a whole tile's rows of one
+    // source.  In direct mode the rows of a tile may be cut into nsub parts, each
+    // a piece of its own (about kPieceBytes by default), whose arrivals the tile
+    // counts in region B (one counter per moved tile, per source under SET).
+    p->PR = (int)p->BS;
+    p->nsub = 1;
+    if (o->piece_rows < 0) return fail(RA2A_EINVAL, "piece_rows must be >= 0");
+    if (p->direct && !p->rows) {
+        int64_t pr = p->BS;
+        if (o->piece_rows > 0) {
+            pr = std::min<int64_t>(o->piece_rows, p->BS);
+        } else if (p->piece_bytes > kPieceBytes) {
+            const int64_t parts = cdiv(p->piece_bytes, kPieceBytes);
+            pr = cdiv(p->BS, parts);
+        }
+        p->PR = (int)pr;
+        p->nsub = (int)cdiv(p->BS, pr);
+        if (p->nsub > 1) p->regionB = (int64_t)p->nbs * p->nmhb * p->ndb * perW;
+    }
+    p->KU = 1;
+    p->upb = 1;
+    if (p->rows) {
+        // tokens per row unit (default: about kRowUnitBytes of output, at least one
+        // token, at most the S-block); region B holds one arrival counter per S-block
+        const int64_t row_bytes = (int64_t)W * H * D * e;
+        int64_t ku = o->unit_rows > 0 ? o->unit_rows : std::max<int64_t>(1, kRowUnitBytes / row_bytes);
+        ku = std::min(ku, p->BS);
+        p->KU = (int)ku;
+        p->upb = (int)cdiv(p->BS, ku);
+        p->regionB = p->nbs;
+        p->unit_bytes = ku * row_bytes;
+    }
     if (p->bulk) {
         // every sender's whole segment has a place: no ring reuse, no hand-back
         p->R = std::max(p->nbs, 1);
@@ -240,13 +304,17 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     // measured on the W=8, S=512, H=16, D=128 bf16 shape: the combine runs best with
     // two persistent workgroups per compute unit, the dispatch (strided reads,
     // contiguous writes) with one (51.1 against 55.0 us)
-    p->wg_per_cu = o->wg_per_cu > 0 ? o->wg_per_cu : (p->inverse ? 1 : 2);
+    p->wg_per_cu = o->wg_per_cu;  // 0: resolved with the schedule at launch (prepare_pipelined)
     p->lookahead = o->lookahead;
     // the kernels index tiles, pieces and work items with 32-bit arithmetic
     const double tasks = (double)W * p->nbs * p->nhb * p->ndb * ((double)W + p->csplit * W);
     if (tasks >= 2147483647.0 - 65536.0) return fail(RA2A_EINVAL, "too many tiles");
     // per-launch index arithmetic uses 32-bit vector counts inside one unit
     if (p->unit_bytes >= (int64_t(1) << 31) - 65536) return fail(RA2A_EINVAL, "tile too large");
+    // the direct modes store through a buffer descriptor per piece / unit, whose
+    // range (at most one S-block of out_j rows) must stay below 2^32 bytes
+    if (p->direct && (double)p->BS * W * H * D * e >= 4294967296.0 - 65536.0)
+        return fail(RA2A_EINVAL, "an S-block of output rows (tile_s * W*H*D*e) reaches 4 GiB");
     // consumers address the staging ring with 32-bit buffer offsets
     if (p->ring_bytes >= (int64_t(1) << 32) && !(p->bulk && p->agent_sync))
         return fail(RA2A_EINVAL, "staging above 4 GiB per slice (the bulk mode allows it with "
@@ -382,12 +450,14 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     a->R = pl.R;
     a->protocol = pl.protocol;
     const int nstreams = W * pl.nmhb * pl.ndb;
-    const int per_cu = std::max(1, std::min(blocks_per_cu, pl.wg_per_cu));
     // one stream group (and work queue) per XCD
     a->NG = std::max(1, std::min(nxcd, ra2a::kNumXcd));
     a->nstreams = nstreams;
     // XCD-local sync needs one group per XCD (XCC_ID mod NG must identify the XCD)
-    a->sync = (pl.agent_sync || nxcd > ra2a::kNumXcd) ? ra2a::kSyncAgent : ra2a::kSyncXcd;
+    // Direct mode publishes every tile device-wide: a tile's W pieces come from
+    // workgroups on any XCD, and its consumer may run on any other.
+    a->sync = (pl.agent_sync || pl.direct || nxcd > ra2a::kNumXcd) ? ra2a::kSyncAgent
+                                                                   : ra2a::kSyncXcd;
     {
         const int ns_max = (nstreams + a->NG - 1) / a->NG;
         int kb = pl.stream_batch;
@@ -403,6 +473,11 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     a->regionB = pl.regionB;
     a->ring_bytes = pl.ring_bytes;
     a->direct = pl.direct;
+    a->rows = pl.rows;
+    a->KU = pl.KU;
+    a->upb = pl.upb;
+    a->PR = pl.PR;
+    a->nsub = pl.nsub;
     a->inverse = pl.inverse;
     a->bulk = pl.bulk;
     a->pull = pl.pull;
@@ -413,7 +488,27 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     // vector width: every offset, stride and run is a multiple of it
     const uint64_t m = (uint64_t)(D * e0) | (uint64_t)(pl.TD * e0) | in_off | out_off | stg_off;
     *V = lowbit_vec(m);
+    // Schedule of the direct modes: dynamic claims when the pieces (row units)
+    // are many per compute unit, else static; workgroups per compute unit as
+    // asked, else one (dynamic) or two (static; the dispatch, whose reads are
+    // strided, one).  The staged modes keep two by default.
+    int64_t work = 0;
+    if (pl.rows) {
+        a->nunits = ra2a::total_row_units(*a);
+        if (a->nunits >= (int64_t(1) << 31) - 65536) return fail(RA2A_EINVAL, "too many row units");
+        work = a->nunits;
+    } else if (pl.direct) {
+        work = ra2a::total_pieces(*a);
+    }
+    a->dyn = pl.direct && work >= kDynPiecesPerCu * (int64_t)ncu ? 1 : 0;
+    int wpc = pl.wg_per_cu;
+    if (wpc <= 0) wpc = !pl.direct ? 2 : (a->dyn || pl.inverse) ? 1 : 2;
+    const int per_cu = std::max(1, std::min(blocks_per_cu, wpc));
     *grid = per_cu * ncu;
+    if (pl.direct) *grid = (int)std::min<int64_t>(*grid, work);  // no workgroup without work
+    // the claim counter: the spare queue word (slice 0), zeroed with the signals
+    a->claim_off = (int64_t)sig_off + (pl.regionA + pl.regionB + ra2a::kQueueSlots - 1) *
+                                          RA2A_SIG_STRIDE_BYTES;
     if (*grid < 1) return fail(RA2A_EUNSUPPORTED, "no compute units");
     return RA2A_OK;
 }
@@ -501,7 +596,8 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     const uint64_t m = (uint64_t)(D * e0) | (uint64_t)(pl.TD * e0) | c.in_off | c.out_off | stg;
     int occ = 0;
     hipError_t he = ra2a::pipelined_blocks_per_cu(
-        lowbit_vec(m), pl.agent_sync ? ra2a::kSyncAgent : ra2a::kSyncXcd, pl.direct, &occ);
+        lowbit_vec(m), (pl.agent_sync || pl.direct) ? ra2a::kSyncAgent : ra2a::kSyncXcd, pl.direct,
+        &occ);
     if (he != hipSuccess) return hip_fail(he, "occupancy query");
     ra2a::PipeArgs a{};
     int V = 16, grid = 0;
@@ -518,16 +614,16 @@ int combine_pipelined(const void* in, void* out, uint64_t* signals, int W, int64
     const bool skip = opts && opts->skip_reset;
     const int64_t reset_slots = pl.regionA + pl.regionB + ra2a::kQueueSlots;
     const int64_t nstamps = a.stamps ? (int64_t)W * pl.regionA : 0;
-    // In-launch reset: direct mode, unless asked for a separate launch, and only
-    // when the occupancy leaves room for the zeroing workgroups beside the
-    // persistent ones (they must run whatever those do).  Not under stream capture:
-    // a replayed launch would carry the tag it was captured with, the reset flags
-    // would already hold it, and producers could signal before the zeroing.
+    // In-launch reset: direct mode, unless asked for a separate launch.  The
+    // zeroing workgroups take the launch's lowest block ids, so they are
+    // dispatched before any workgroup that waits for them, whatever else occupies
+    // the device.  Not under stream capture: a replayed launch would carry the tag
+    // it was captured with, the reset flags would already hold it, and producers
+    // could signal before the zeroing.
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     he = hipStreamIsCapturing(st, &cap);
     if (he != hipSuccess) return hip_fail(he, "hipStreamIsCapturing");
-    const int per_cu = grid / std::max(1, ncu);
-    const bool in_launch = pl.direct && !(opts && opts->separate_reset) && occ > per_cu &&
+    const bool in_launch = pl.direct && !(opts && opts->separate_reset) &&
                            (!skip || nstamps > 0) && cap == hipStreamCaptureStatusNone;
     if (in_launch) {
         // about 16 slots per thread and zeroing workgroup, at most kResetFlags of them
@@ -630,6 +726,10 @@ RA2A_API int ra2a_symm_heap_destroy(ra2a_heap_t* h) {
         auto it = std::find(g_heaps.begin(), g_heaps.end(), h);
         if (it == g_heaps.end()) return fail(RA2A_EINVAL, "not a live heap");
         g_heaps.erase(it);
+    }
+    if (g_exiting.load()) {  // too late for HIP calls (see mark_exiting)
+        delete h;
+        return ok();
     }
     const bool touched = h->owned || h->err || h->bt_ws;
     hipError_t e = touched ? hipDeviceSynchronize() : hipSuccess;
@@ -811,6 +911,44 @@ RA2A_API int ra2a_rev_all2all_signal_slots(int W, int64_t S, int64_t H, int64_t 
     if (tile_slots) *tile_slots = a;
     if (credit_slots) *credit_slots = b;
     if (queue_slots) *queue_slots = (a + b) > 0 ? ra2a::kQueueSlots + ra2a::kResetFlags : 0;
+    return ok();
+}
+
+RA2A_API int ra2a_rev_all2all_plan(int W, int64_t S, int64_t H, int64_t D, int dtype,
+                                   const ra2a_opts_t* opts, ra2a_plan_t* plan) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(RA2A_EINVAL, "unknown dtype %d", dtype);
+    if (!plan) return fail(RA2A_EINVAL, "plan must be non-NULL");
+    if (W < 1 || S < 1 || H < 1 || D < 1) return fail(RA2A_EINVAL, "bad dimensions");
+    Plan p{};
+    int rc = make_plan(W, S, H, D, e, opts, &p);
+    if (rc) return rc;
+    std::memset(plan, 0, sizeof *plan);
+    plan->mode = p.rows ? RA2A_MODE_ROWS
+                 : p.direct ? RA2A_MODE_DIRECT
+                 : p.pull   ? RA2A_MODE_PULL
+                 : p.bulk   ? RA2A_MODE_BULK
+                            : RA2A_MODE_STAGED;
+    plan->protocol = p.protocol == RA2A_SIG_SET ? RA2A_PROTO_SET : RA2A_PROTO_ADD;
+    plan->tile_s = p.BS;
+    plan->tile_h = p.TH;
+    plan->tile_d = p.TD;
+    plan->head_merge = p.MH;
+    plan->piece_rows = p.PR;
+    plan->pieces_per_tile = p.nsub;
+    plan->unit_rows = p.rows ? p.KU : 0;
+    plan->tile_slots = p.regionA;
+    plan->credit_slots = p.regionB;
+    plan->queue_slots = ra2a::kQueueSlots + ra2a::kResetFlags;
+    plan->workspace_bytes = (size_t)p.ring_bytes;
+    if (p.direct) {
+        ra2a::PipeArgs a{};
+        int V = 16, grid = 0;
+        rc = prepare_pipelined(W, S, H, D, e, p, opts, int64_t(1) << 40, 0, 0, 0, 0, 256, 8, 8, &a,
+                               &V, &grid);
+        if (rc) return rc;
+        plan->work_items = p.rows ? a.nunits : ra2a::total_pieces(a);
+    }
     return ok();
 }
 
@@ -1542,35 +1680,102 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
 
     const bool add = a.protocol == ra2a::kSigAdd;
     const int64_t sigA_len = pl.regionA * RA2A_SIG_STRIDE_BYTES;
-    if (pl.direct) {
+    if (pl.rows) {
+        // Row units as the kernel runs them: every unit once in its global order;
+        // each fills whole output rows, adds 1 to its block's arrival counter, and
+        // the unit that completes the block marks its signal tiles.  Every output
+        // row must be written by exactly one unit.
+        const int64_t total = ra2a::total_row_units(a);
+        if (total != a.nunits) return fail(RA2A_EINVAL, "row unit count mismatch");
+        std::vector<uint8_t> rowhit((size_t)(W * S), 0);
+        const int64_t sigB_len = pl.regionB * RA2A_SIG_STRIDE_BYTES;
+        for (int64_t u = 0; u < total; ++u) {
+            const ra2a::RowUnit q = ra2a::row_unit(a, u);
+            if (q.j < 0 || q.j >= W || q.b < 0 || q.b >= a.nbs || q.rows < 1 || q.k < 0 ||
+                q.k >= q.nub)
+                return fail(RA2A_EINVAL, "row unit %lld out of range", (long long)u);
+            const int64_t s0 = (int64_t)q.b * a.BS + (int64_t)q.k * a.KU;
+            for (int64_t t = s0; t < s0 + q.rows; ++t) {
+                if (t >= S || t >= (int64_t)(q.b + 1) * a.BS)
+                    return fail(RA2A_EINVAL, "row unit %lld leaves its S-block", (long long)u);
+                rowhit[(size_t)(q.j * S + t)]++;
+            }
+            std::vector<std::pair<int64_t, int64_t>> offs;
+            rc = walk_plan(q.pl, V, 0, ra2a::plan_vectors(q.pl, V), &offs);
+            if (rc) return rc;
+            for (const auto& o : offs) {
+                if (o.second < 0 || o.second + V > (int64_t)ra2a::plan_span(q.pl))
+                    return fail(RA2A_EINVAL, "row unit store outside its descriptor's range");
+                const int64_t so = q.src + o.first;
+                const int r = (int)(so / stride);
+                if (r < 0 || r >= W || !inside(so, V, r, in_off, nb))
+                    return fail(RA2A_EINVAL, "row unit reads outside every input");
+                if (!inside(q.dst + o.second, V, q.j, out_off, nb))
+                    return fail(RA2A_EINVAL, "row unit writes outside out of rank %d", q.j);
+                std::memcpy(&heap[(size_t)(q.dst + o.second)], &heap[(size_t)so], (size_t)V);
+            }
+            if (!inside(q.cnt, 8, q.j, sig_off + sigA_len, sigB_len))
+                return fail(RA2A_EINVAL, "row unit counter outside region B");
+            *u64(q.cnt) += 1;
+            if (*u64(q.cnt) > (uint64_t)q.nub)
+                return fail(RA2A_EINVAL, "block counter beyond its unit count");
+            if (*u64(q.cnt) == (uint64_t)q.nub)  // the unit that completes the block
+                for (int k = 0; k < q.nsig; ++k) {
+                    const int64_t sg = q.sig + (int64_t)k * RA2A_SIG_STRIDE_BYTES;
+                    if (!inside(sg, 8, q.j, sig_off, sigA_len))
+                        return fail(RA2A_EINVAL, "row unit signal outside region A");
+                    *u64(sg) = add ? *u64(sg) + (uint64_t)W : 1;
+                }
+        }
+        for (uint8_t x : rowhit)
+            if (x != 1) return fail(RA2A_EINVAL, "row units do not write every output row once");
+    } else if (pl.direct) {
         // Direct mode as the kernel runs it: every piece once in its global order,
         // no waits, no hand-back counters.
         const int64_t total = ra2a::total_pieces(a);
-        std::vector<uint8_t> seen((size_t)total, 0);  // by (stream, S-block, source)
+        std::vector<int64_t> seen((size_t)a.nstreams * a.nbs * W, 0);  // rows per (stream, S-block, source)
         for (int64_t gp = 0; gp < total; ++gp) {
             const ra2a::Piece p = ra2a::direct_piece(a, gp);
-            if (p.sid < 0 || p.sid >= a.nstreams || p.b < 0 || p.b >= a.nbs || p.r < 0 || p.r >= W)
+            if (p.sid < 0 || p.sid >= a.nstreams || p.b < 0 || p.b >= a.nbs || p.r < 0 || p.r >= W ||
+                p.sub < 0 || p.sub >= p.nsub || p.nsub > a.nsub || p.pl.A < 1)
                 return fail(RA2A_EINVAL, "direct piece %lld out of range", (long long)gp);
-            seen[(size_t)(((int64_t)p.sid * a.nbs + p.b) * W + p.r)]++;
+            seen[(size_t)(((int64_t)p.sid * a.nbs + p.b) * W + p.r)] += p.pl.A;
             std::vector<std::pair<int64_t, int64_t>> offs;
             rc = walk_plan(p.pl, V, 0, ra2a::plan_vectors(p.pl, V), &offs);
             if (rc) return rc;
             for (const auto& o : offs) {
+                if (o.second < 0 || o.second + V > (int64_t)ra2a::plan_span(p.pl))
+                    return fail(RA2A_EINVAL, "piece store outside its descriptor's range");
                 if (!inside(p.src + o.first, V, p.r, in_off, nb))
                     return fail(RA2A_EINVAL, "piece reads outside in of rank %d", p.r);
                 if (!inside(p.dst + o.second, V, p.j, out_off, nb))
                     return fail(RA2A_EINVAL, "piece writes outside out of rank %d", p.j);
                 std::memcpy(&heap[(size_t)(p.dst + o.second)], &heap[(size_t)(p.src + o.first)], (size_t)V);
             }
-            for (int k = 0; k < p.nsig; ++k) {
+            bool last = true;  // one piece per tile and source: it signals itself
+            uint64_t val = 1;
+            if (a.nsub > 1) {  // count the arrival; the last one signals for all
+                if (!inside(p.cnt, 8, p.j, sig_off + sigA_len, pl.regionB * RA2A_SIG_STRIDE_BYTES))
+                    return fail(RA2A_EINVAL, "piece counter outside region B");
+                *u64(p.cnt) += 1;
+                if (*u64(p.cnt) > p.cnt_need) return fail(RA2A_EINVAL, "tile counter beyond its need");
+                last = *u64(p.cnt) == p.cnt_need;
+                val = add ? (uint64_t)W : 1;
+            }
+            for (int k = 0; k < p.nsig && last; ++k) {
                 const int64_t sg = p.sig + k * p.sig_step;
                 if (!inside(sg, 8, p.j, sig_off, sigA_len))
                     return fail(RA2A_EINVAL, "piece signal outside region A");
-                *u64(sg) = add ? *u64(sg) + 1 : 1;
+                *u64(sg) = add ? *u64(sg) + val : 1;
             }
         }
-        for (uint8_t x : seen)
-            if (x != 1) return fail(RA2A_EINVAL, "direct schedule does not hold every piece once");
+        // every (stream, S-block, source) moved each of its rows exactly once
+        for (int sid = 0; sid < a.nstreams; ++sid)
+            for (int b = 0; b < a.nbs; ++b)
+                for (int r = 0; r < W; ++r)
+                    if (seen[(size_t)(((int64_t)sid * a.nbs + b) * W + r)] !=
+                        std::min<int64_t>(a.BS, S - (int64_t)b * a.BS))
+                        return fail(RA2A_EINVAL, "direct schedule does not move every row once");
     }
     // Staged mode: each group's queue run strictly in queue order, one task at a
     // time: every wait must already hold when its task comes up (the kernel's

@@ -74,6 +74,13 @@ struct RowPlan {
 
 RA2A_HD int plan_vectors(const RowPlan& p, int V) { return p.A * p.B * p.C * (p.run / V); }
 
+// Bytes from a plan's first destination byte to one past its last (the range a
+// buffer descriptor for the destination must cover; the host keeps it below 2^32).
+RA2A_HD uint32_t plan_span(const RowPlan& p) {
+    return (uint32_t)((int64_t)(p.A - 1) * p.da + (int64_t)(p.B - 1) * p.db +
+                      (int64_t)(p.C - 1) * p.dc + p.run);
+}
+
 // Digits of vector index idx in the plan's mixed radix: idx = ((ia * B + ib) *
 // C + ic) * vpr + col, with vpr = run / V vectors per row.
 struct PlanDigits {
@@ -202,6 +209,9 @@ RA2A_HD void tile_of(const PipeArgs& a, int ns, int64_t t, int* b, int* k) {
 // Producer piece pc of group g: source r = pc mod W of tile pc div W.
 struct Piece {
     int32_t b, r, j, slot, nsig;
+    int32_t sub, nsub;    // direct mode: the piece's rows are part `sub` of nsub of the tile's
+    int64_t cnt;          // direct mode, nsub > 1: the tile's arrival counter (slice j)
+    uint64_t cnt_need;    // arrivals that complete the tile (W * nsub under ADD, nsub under SET)
     int64_t src;          // absolute byte offset from the heap base (slice r)
     int64_t dst;          // absolute byte offset (slice j: staging ring, or out if direct)
     RowPlan pl;
@@ -213,21 +223,25 @@ struct Piece {
     int64_t unit_index;   // first data-signal slot index within slice j (timestamp row)
 };
 
-// The piece of source r in S-block b of stream sid.
-RA2A_HD Piece piece_at(const PipeArgs& a, int sid, int b, int r) {
+// The piece of source r in S-block b of stream sid: its rows [sub * PR, (sub + 1)
+// * PR) of the block (all of them in the staged modes, where PR = BS).
+RA2A_HD Piece piece_at(const PipeArgs& a, int sid, int b, int r, int sub = 0) {
     Piece p;
     const int64_t e = a.e;
     p.r = r;
     p.b = b;
     p.sid = sid;
+    p.sub = sub;
     const Stream st = stream_of(a, p.sid);
     p.j = st.j;
     const uint32_t cycle = (uint32_t)p.b / (uint32_t)a.R;  // uses of this ring slot before b
     p.slot = (int)((uint32_t)p.b - cycle * (uint32_t)a.R);
     const bool add = a.protocol == kSigAdd;
     const int64_t HWDe = a.H * (int64_t)a.W * a.D * e;
-    const int64_t s0 = (int64_t)p.b * a.BS;
-    const int bs = (int)geom_min(a.BS, a.S - s0);
+    const int64_t blk = geom_min(a.BS, a.S - (int64_t)p.b * a.BS);  // rows of the block
+    p.nsub = (int)((blk + a.PR - 1) / a.PR);
+    const int64_t s0 = (int64_t)p.b * a.BS + (int64_t)sub * a.PR;
+    const int bs = (int)geom_min(a.PR, blk - (int64_t)sub * a.PR);
     RowPlan& pl = p.pl;
     pl.A = bs;
     if (a.inverse) {
@@ -282,6 +296,12 @@ RA2A_HD Piece piece_at(const PipeArgs& a, int sid, int b, int r) {
     if (!add) ci = ci * a.W + p.r;
     p.credit = sig_base + (a.regionA + ci) * kSigStrideU64 * 8;
     p.credit_need = (uint64_t)cycle * (uint64_t)a.csplit;
+    // direct mode with several pieces per tile and source: one arrival counter per
+    // moved tile (b, merged head block, d block) -- per source under SET -- in region B
+    int64_t ti = ((int64_t)p.b * a.nmhb + st.mhb) * a.ndb + st.db;
+    if (!add) ti = ti * a.W + p.r;
+    p.cnt = sig_base + (a.regionA + ti) * kSigStrideU64 * 8;
+    p.cnt_need = (uint64_t)p.nsub * (add ? (uint64_t)a.W : 1ull);
     return p;
 }
 
@@ -300,18 +320,101 @@ RA2A_HD int64_t group_pieces(const PipeArgs& a, int g) {
     return (int64_t)a.nbs * group_streams(a, g).ns * a.W;
 }
 
+// Direct mode: pieces per source in one stream: nsub for every S-block but the
+// last, which has ceil(its rows / PR).
+RA2A_HD int64_t stream_subtiles(const PipeArgs& a) {
+    const int64_t last = a.S - (int64_t)(a.nbs - 1) * a.BS;
+    return (int64_t)(a.nbs - 1) * a.nsub + (last + a.PR - 1) / a.PR;
+}
+
 // Direct mode: piece gp of the whole combine, in the order (stream, S-block,
-// source) with the source fastest, so that the pieces in flight together fill
-// a few destinations' outputs and read contiguous row ranges of every input.
+// part, source) with the source fastest, so that the pieces in flight together
+// fill a few destinations' outputs and read contiguous row ranges of every input.
 RA2A_HD Piece direct_piece(const PipeArgs& a, int64_t gp) {
     const uint32_t t = (uint32_t)gp / (uint32_t)a.W;
     const int r = (int)((uint32_t)gp - t * (uint32_t)a.W);
-    const uint32_t sid = t / (uint32_t)a.nbs;
-    return piece_at(a, (int)sid, (int)(t - sid * (uint32_t)a.nbs), r);
+    const uint32_t spt = (uint32_t)stream_subtiles(a);
+    const uint32_t sid = t / spt;
+    const uint32_t rem = t - sid * spt;
+    uint32_t b = rem / (uint32_t)a.nsub;
+    if (b > (uint32_t)a.nbs - 1u) b = (uint32_t)a.nbs - 1u;  // the last block may be short
+    return piece_at(a, (int)sid, (int)b, r, (int)(rem - b * (uint32_t)a.nsub));
 }
 
 RA2A_HD int64_t total_pieces(const PipeArgs& a) {
-    return (int64_t)a.nbs * a.nstreams * a.W;
+    return stream_subtiles(a) * a.nstreams * a.W;
+}
+
+// Row units (direct mode, the default combine).  A row unit fills rows
+// [s0, s0 + rows) of out_j completely: for each of those tokens the W sources'
+// runs of H*D elements, which are contiguous in out_j (columns r*H .. r*H + H - 1
+// for r = 0 .. W-1 make up a whole output row) and contiguous, token after token,
+// in each in_r (rows j*S + s0 ..).  So a unit writes one contiguous range of out_j
+// and reads W contiguous ranges.  The signal tiles of S-block b are complete once
+// every unit of b has stored its rows: each unit releases its stores device-wide
+// and adds 1 to the block's arrival counter (region B of slice j); the unit that
+// brings it to `nub` (the block's unit count) acquires and releases, then marks
+// every signal tile of the block complete -- ADD W on the tile's slot, or SET 1 on
+// each (tile, source) slot -- exactly the values W pieces would have left.
+// Units are ordered S-block first, then the unit inside the block, then the
+// destination, so that early tiles of every destination complete first.
+struct RowUnit {
+    int32_t j, b, k, rows, nub;
+    int64_t src;          // absolute byte offset of in_0[j*S + s0] (slice 0); source r is
+                          // r slices further (the plan's middle digit)
+    int64_t dst;          // absolute byte offset of out_j[s0] (slice j)
+    RowPlan pl;
+    int64_t sig;          // absolute byte offset of the block's first data signal (slice j)
+    int32_t nsig;         // data-signal slots of the block (consecutive, one slot apart)
+    int64_t cnt;          // absolute byte offset of the block's arrival counter (slice j)
+    int64_t unit_index;   // slot index of the block's first data signal (timestamp row)
+};
+
+// Row units of S-block b (of any destination).
+RA2A_HD int32_t row_units_of_block(const PipeArgs& a, int b) {
+    const int64_t bs = geom_min(a.BS, a.S - (int64_t)b * a.BS);
+    return (int32_t)((bs + a.KU - 1) / a.KU);
+}
+
+RA2A_HD int64_t total_row_units(const PipeArgs& a) {
+    return ((int64_t)(a.nbs - 1) * a.upb + row_units_of_block(a, a.nbs - 1)) * a.W;
+}
+
+RA2A_HD RowUnit row_unit(const PipeArgs& a, int64_t u) {
+    RowUnit q;
+    const int64_t e = a.e;
+    const uint32_t per_block = (uint32_t)a.upb * (uint32_t)a.W;  // units of a full S-block
+    uint32_t b = (uint32_t)u / per_block;
+    if (b > (uint32_t)a.nbs - 1u) b = (uint32_t)a.nbs - 1u;      // the last block may be short
+    const uint32_t rem = (uint32_t)u - b * per_block;
+    const uint32_t k = rem / (uint32_t)a.W;
+    q.b = (int)b;
+    q.k = (int)k;
+    q.j = (int)(rem - k * (uint32_t)a.W);
+    q.nub = row_units_of_block(a, q.b);
+    const int64_t bs = geom_min(a.BS, a.S - (int64_t)q.b * a.BS);
+    const int64_t s0 = (int64_t)q.b * a.BS + (int64_t)q.k * a.KU;
+    q.rows = (int)geom_min(a.KU, bs - (int64_t)q.k * a.KU);
+    const int64_t run = a.H * a.D * e;  // one source's part of a token row
+    q.src = a.in_off + ((int64_t)q.j * a.S + s0) * run;
+    q.dst = (int64_t)q.j * a.stride + a.out_off + s0 * run * a.W;
+    RowPlan& pl = q.pl;
+    pl.A = q.rows;      // tokens
+    pl.sa = run;
+    pl.da = run * a.W;
+    pl.B = a.W;         // sources, source-major inside an output row
+    pl.sb = a.stride;
+    pl.db = run;
+    pl.C = 1;
+    pl.sc = pl.dc = 0;
+    pl.run = (int)run;
+    const int64_t per_block_slots = (int64_t)a.nhb * a.ndb * (a.protocol == kSigAdd ? 1 : a.W);
+    const int64_t sig_base = (int64_t)q.j * a.stride + a.sig_off;
+    q.unit_index = (int64_t)q.b * per_block_slots;
+    q.sig = sig_base + q.unit_index * kSigStrideU64 * 8;
+    q.nsig = (int32_t)per_block_slots;
+    q.cnt = sig_base + (a.regionA + q.b) * kSigStrideU64 * 8;
+    return q;
 }
 
 // Consumer work item `it` of group g: part `part` of a unit (ADD: a tile with

@@ -142,6 +142,80 @@ __device__ __forceinline__ void copy_plan(const uint8_t* __restrict__ src, uint8
     }
 }
 
+// The same with device-scope write-through stores (kPolicyDevNt) through a
+// buffer descriptor `dst` whose range covers the plan's destination (32-bit
+// plan offsets): how the direct modes write out_j, so that a drain publishes
+// the data device-wide (device.h).  Loads are non-temporal (the input is read
+// once).
+template <int V, int U>
+__device__ __forceinline__ void copy_plan_wt(const uint8_t* __restrict__ src,
+                                             __amdgpu_buffer_rsrc_t dst, const RowPlan& p, int lo,
+                                             int hi) {
+    using T = typename Vec<V>::T;
+    constexpr int kRound = U * kThreads;
+    const int vpr = p.run / V;
+    const int nfull = hi > lo ? (hi - lo) / kRound : 0;
+    int idx = lo + (int)threadIdx.x;
+    auto get = [](const uint8_t* s) { return load_nt(reinterpret_cast<const T*>(s)); };
+    auto put = [&](const T& v, uint32_t off) { BufStore<V, kPolicyDevNt>::go(v, dst, off); };
+    if (p.B * p.C == 1 && lo == 0 && kThreads % vpr == 0) {
+        // whole rows per step: both offsets advance by constants
+        const int rows = kThreads / vpr;
+        const int row = idx / vpr, col = idx - row * vpr;
+        const uint8_t* s0 = src + row * p.sa + (int64_t)col * V;
+        uint32_t d0 = (uint32_t)(row * p.da + (int64_t)col * V);
+        const int64_t ds = rows * p.sa;
+        const uint32_t dd = (uint32_t)(rows * p.da);
+        for (int k = 0; k < nfull; ++k) {
+            T v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = get(s0 + u * ds);
+#pragma unroll
+            for (int u = 0; u < U; ++u) put(v[u], d0 + (uint32_t)u * dd);
+            s0 += U * ds;
+            d0 += (uint32_t)U * dd;
+        }
+        idx += nfull * kRound;
+        if (idx < hi) {
+            T v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (idx + u * kThreads < hi) v[u] = get(s0 + u * ds);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (idx + u * kThreads < hi) put(v[u], d0 + (uint32_t)u * dd);
+        }
+        return;
+    }
+    PlanCursor c = cursor_start(p, V, vpr, (uint32_t)idx, kThreads);
+    for (int k = 0; k < nfull; ++k) {
+        T v[U];
+        uint32_t doff[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            v[u] = get(src + c.so);
+            doff[u] = (uint32_t)c.dofs;
+            cursor_advance(c, p, vpr);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) put(v[u], doff[u]);
+    }
+    idx += nfull * kRound;
+    if (idx < hi) {
+        T v[U];
+        uint32_t doff[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (idx + u * kThreads < hi) v[u] = get(src + c.so);
+            doff[u] = (uint32_t)c.dofs;
+            cursor_advance(c, p, vpr);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (idx + u * kThreads < hi) put(v[u], doff[u]);
+    }
+}
+
 // The same, reading the source through a buffer descriptor with cache policy
 // POLICY at 32-bit offsets src_off + (plan offset).
 template <int V, int U, int POLICY, bool NTS>
@@ -237,7 +311,8 @@ __device__ __forceinline__ bool piece_wait(const PipeArgs& a, const Piece& p, in
         return false;
     if (p.r == a.straggler && a.delay) {
         if (threadIdx.x == 0) {
-            const uint64_t id = ((uint64_t)p.b * (uint64_t)a.nstreams + p.sid) * a.W + p.r;
+            const uint64_t id =
+                ((((uint64_t)p.b * (uint64_t)a.nstreams + p.sid) * (uint64_t)a.nsub + p.sub) * a.W) + p.r;
             const uint64_t n = a.delay + splitmix64(a.seed, id) % ((uint64_t)a.delay + 1ull);
             for (uint64_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
         }
@@ -341,47 +416,167 @@ __device__ __forceinline__ bool reset_published(const PipeArgs& a) {
     return __syncthreads_and(ok ? 1 : 0) != 0;
 }
 
-// Direct mode.  Producers store straight into out_j, so no consumer has data to
-// move: a tile is complete when its signal reaches W (ADD) or each of its W
-// slots reads 1 (SET), and the optional completion stamp of a tile is the
-// latest of its producers' stamps (an atomic max each).  The only wait is for
-// the in-launch reset's flags (above), so a static schedule (workgroup k takes
-// pieces k, k + piece_grid, ... of the direct_piece order) needs no queue.  The
-// reset runs on reset_nz workgroups launched after the piece_grid ones, and the
-// host launches it only when the occupancy leaves room for them beside the
-// persistent workgroups: they run whatever those do and wait on nothing, so
-// the wait always ends.  Every atomic is issued without a return value, so no
-// drain waits for a round trip.  A piece's geometry is 32-bit scalar arithmetic: the inline 64-bit
-// division sequences it replaced delayed every piece's first load measurably.
-// (Measured too: issuing the next piece's loads before this piece's release is
-// slower here, not faster.)
+// Work distribution of the direct modes.  Persistent workgroup k first takes
+// piece (or row unit) k.  With a static schedule (dyn == 0) it then takes k +
+// piece_grid, k + 2 piece_grid, ...; with dyn == 1 each further one is claimed
+// from a counter in the spare queue word (zeroed by the reset, so the first
+// claim waits until the reset is published), issued when the previous piece
+// starts so that the claim's round trip hides under its copy.  Claimed work
+// stays balanced when pieces are many and their speed varies with where in
+// HBM they lie.
+struct Claimer {
+    uint64_t* ctr;
+    int64_t grid;
+    int64_t next;   // lane 0: the claimed piece, or -1 if none is claimed yet
+};
+
+__device__ __forceinline__ Claimer claimer(const PipeArgs& a) {
+    Claimer c;
+    c.ctr = reinterpret_cast<uint64_t*>(a.base + a.claim_off);
+    c.grid = a.piece_grid;
+    c.next = -1;
+    return c;
+}
+
+// Lane 0 claims the piece after the current one (dynamic schedule, once the
+// reset is published).
+__device__ __forceinline__ void claim_ahead(const PipeArgs& a, Claimer& c, bool published) {
+    if (a.dyn && published && threadIdx.x == 0 && c.next < 0)
+        c.next = c.grid + (int64_t)__hip_atomic_fetch_add(c.ctr, 1ull, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The workgroup's next piece (uniform across it).
+__device__ __forceinline__ int64_t next_piece(const PipeArgs& a, Claimer& c, int64_t cur,
+                                              int64_t* lds_next) {
+    if (!a.dyn) return cur + c.grid;
+    if (threadIdx.x == 0) *lds_next = c.next;
+    c.next = -1;
+    __syncthreads();
+    const int64_t n = *lds_next;
+    __syncthreads();
+    return n;
+}
+
+// Wave 0: completion stamps (the device clock) of n signal tiles `step` slots apart.
+__device__ __forceinline__ void stamp_tiles(const PipeArgs& a, int j, int64_t first, int64_t step,
+                                            int n) {
+    if (a.stamps && threadIdx.x < 64) {
+        const uint64_t now = rtc_now();
+        for (int k = threadIdx.x; k < n; k += 64)
+            __hip_atomic_fetch_max(a.stamps + (int64_t)j * a.units_per_dest + first + k * step, now,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Lane 0 adds 1 to an arrival counter; true (uniformly) for the arrival that
+// brings it to `need`.
+__device__ __forceinline__ bool arrive(const PipeArgs& a, int64_t cnt, uint64_t need, int* lds_flag) {
+    if (threadIdx.x == 0) {
+        const uint64_t before = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(a.base + cnt), 1ull,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *lds_flag = before + 1ull == need ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = *lds_flag != 0;
+    __syncthreads();
+    return last;
+}
+
+// Direct mode, per-source pieces.  Producers store straight into out_j, so no
+// consumer has data to move.  A piece covers part `sub` of the tile's rows for
+// one source.  With one part per tile (nsub == 1) the piece signals its tiles
+// itself: ADD 1 (the tile is complete at W) or SET 1 on its (tile, source)
+// slot.  With several, each piece adds 1 to its tile's arrival counter (per
+// source under SET) and the piece that completes it signals as all W (or the
+// source's) pieces would have: ADD W, or SET 1.  Stores are device-scope
+// write-through (copy_plan_wt), so a drain and a barrier publish them on every
+// XCD before the signal or the count; the piece that reads the counter's last
+// arrival follows every other piece's drained stores.  The optional completion
+// stamp of a tile is the latest of its signalling pieces' stamps.  The only
+// wait is for the in-launch reset's flags.  The reset runs on the reset_nz
+// workgroups with the lowest block ids.  Those are dispatched first --
+// workgroups of one launch are dispatched in id order -- so they hold their
+// compute-unit slots before any workgroup that waits for them exists, whatever
+// else occupies the device; they wait on nothing, so the wait always ends.
 template <int V, int SYNC>
 __device__ __forceinline__ void direct_path(const PipeArgs& a, int* lds_flag) {
-    const int pg = a.piece_grid;
-    if ((int)blockIdx.x >= pg) {  // a zeroing workgroup of the in-launch reset
-        reset_share(a, (int)blockIdx.x - pg);
+    __shared__ int64_t lds_next;
+    const int nz = a.reset_nz;
+    if ((int)blockIdx.x < nz) {  // a zeroing workgroup of the in-launch reset
+        reset_share(a, (int)blockIdx.x);
         return;
     }
     bool published = a.reset_tag == 0ull;
     const int64_t total = total_pieces(a);
-    for (int64_t gp = blockIdx.x; gp < total; gp += pg) {
+    const int op = a.protocol == kSigAdd ? kSigAdd : kSigSet;
+    const uint64_t done_val = a.protocol == kSigAdd ? (uint64_t)a.W : 1ull;
+    Claimer cl = claimer(a);
+    for (int64_t gp = (int)blockIdx.x - nz; gp < total;) {
+        claim_ahead(a, cl, published);
         const Piece p = direct_piece(a, gp);
         if (!piece_wait(a, p, lds_flag)) return;
-        // final place: stream the stores past the L2
-        copy_plan<V, 8, true, true>(a.base + p.src, a.base + p.dst, p.pl, 0, plan_vectors(p.pl, V));
-        group_release<SYNC>();
+        // final place: device-scope write-through stores, so the drain publishes them
+        copy_plan_wt<V, 8>(a.base + p.src, make_rsrc_uniform(a.base + p.dst, plan_span(p.pl)), p.pl,
+                           0, plan_vectors(p.pl, V));
+        group_release_written_through();
         if (!published) {
             if (!reset_published(a)) return;
             published = true;
+            claim_ahead(a, cl, published);
         }
-        piece_signal(a, p.sig, p.sig_step, p.nsig);
-        if (a.stamps && threadIdx.x < 64) {
-            const uint64_t now = rtc_now();
-            const int64_t step = slot_step(a);
+        const int64_t step = slot_step(a);
+        if (a.nsub == 1) {
+            piece_signal(a, p.sig, p.sig_step, p.nsig);
+            stamp_tiles(a, p.j, p.unit_index, step, p.nsig);
+        } else if (arrive(a, p.cnt, p.cnt_need, lds_flag) && threadIdx.x < 64) {
             for (int k = threadIdx.x; k < p.nsig; k += 64)
-                __hip_atomic_fetch_max(a.stamps + (int64_t)p.j * a.units_per_dest + p.unit_index + k * step,
-                                       now, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sig_update(reinterpret_cast<uint64_t*>(a.base + p.sig + k * p.sig_step), done_val, op);
+            stamp_tiles(a, p.j, p.unit_index, step, p.nsig);
         }
+        gp = next_piece(a, cl, gp, &lds_next);
+    }
+}
+
+// Direct mode with row units (RA2A_MODE_ROWS; combine_geom.h row_unit).  A
+// unit copies its rows of every source into out_j with device-scope
+// write-through stores (the destination one contiguous range), drains them, and
+// adds 1 to the S-block's arrival counter; the unit that completes the block
+// marks every signal tile of the block complete.  Every other unit of the block
+// drained its stores before its add, and the completing unit read the counter
+// after all of them: the block's rows are performed device-wide before these
+// signals.  Counter and signals are zeroed by the in-launch reset, so both
+// wait for its flags.  Work is distributed as in direct_path.
+template <int V>
+__device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
+    __shared__ int64_t lds_next;
+    const int nz = a.reset_nz;
+    if ((int)blockIdx.x < nz) {  // a zeroing workgroup of the in-launch reset
+        reset_share(a, (int)blockIdx.x);
+        return;
+    }
+    const int op = a.protocol == kSigAdd ? kSigAdd : kSigSet;
+    const uint64_t val = a.protocol == kSigAdd ? (uint64_t)a.W : 1ull;
+    bool published = a.reset_tag == 0ull;
+    Claimer cl = claimer(a);
+    for (int64_t u = (int)blockIdx.x - nz; u < a.nunits;) {
+        claim_ahead(a, cl, published);
+        const RowUnit q = row_unit(a, u);
+        copy_plan_wt<V, 8>(a.base + q.src, make_rsrc_uniform(a.base + q.dst, plan_span(q.pl)), q.pl,
+                           0, plan_vectors(q.pl, V));
+        group_release_written_through();
+        if (!published) {
+            if (!reset_published(a)) return;
+            published = true;
+            claim_ahead(a, cl, published);
+        }
+        if (arrive(a, q.cnt, (uint64_t)q.nub, lds_flag) && threadIdx.x < 64) {
+            for (int k = threadIdx.x; k < q.nsig; k += 64)
+                sig_update(reinterpret_cast<uint64_t*>(a.base + q.sig) + (int64_t)k * kSigStrideU64,
+                           val, op);
+            stamp_tiles(a, q.j, q.unit_index, 1, q.nsig);
+        }
+        u = next_piece(a, cl, u, &lds_next);
     }
 }
 
@@ -390,7 +585,10 @@ __global__ void __launch_bounds__(kThreads) rev_a2a_pipelined_kernel(PipeArgs a)
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
     if (DIRECT) {
-        direct_path<V, SYNC>(a, &lds_flag);
+        if (a.rows)
+            rows_path<V>(a, &lds_flag);
+        else
+            direct_path<V, SYNC>(a, &lds_flag);
         return;
     }
     // Staged mode.  XCD-local sync binds each group to one XCD (queue.h); with

@@ -54,6 +54,15 @@ struct PipeArgs {
     int64_t regionB;    // ring hand-back slots per slice (work counters follow, slice 0)
     int64_t ring_bytes; // staging bytes per slice
     int32_t direct;     // 1: pieces go straight to out_j, no staging
+    int32_t PR;         // tokens per piece (direct mode: <= BS; staged modes: BS)
+    int32_t nsub;       // pieces per full S-block and source (ceil(BS / PR)); > 1: the
+                        // pieces of a tile count their arrivals in region B
+    int32_t dyn;        // 1: persistent workgroups claim pieces / units from a counter
+    int64_t claim_off;  // absolute byte offset of that counter (slice 0, the spare queue word)
+    int32_t rows;       // 1 (with direct): row units -- whole rows of out_j, every source
+    int32_t KU;         // row units: tokens per unit (a unit never straddles S-blocks)
+    int32_t upb;        // row units per full S-block: ceil(BS / KU)
+    int64_t nunits;     // row units in total
     int32_t inverse;    // 1: the dispatch (the combine's inverse map), direct mode only
     int32_t bulk;       // 1: staging in the two-phase layout [W][S][H][D], no ring
     int32_t pull;       // 1 (with bulk): the staging lives in the sender's slice, [j][S][H][D]
@@ -61,10 +70,11 @@ struct PipeArgs {
     uint32_t delay;     // busy-loop base n0
     uint64_t seed;      // SplitMix64 seed of the delays
     int64_t units_per_dest;  // consumer units per destination (timestamps row)
-    // in-launch signal reset (direct mode): reset_nz extra workgroups, after the
-    // piece_grid workgroups that move pieces, zero slots [0, reset_slots) of every
-    // slice (reset_chunk each) and their share of the timestamps (stamp_chunk
-    // each), then set their reset flag to reset_tag; 0 = no in-launch reset
+    // in-launch signal reset (direct mode): reset_nz extra workgroups, the launch's
+    // lowest block ids (before the piece_grid workgroups that move data), zero
+    // slots [0, reset_slots) of every slice (reset_chunk each) and their share of
+    // the timestamps (stamp_chunk each), then set their reset flag to reset_tag;
+    // 0 = no in-launch reset
     uint64_t reset_tag;
     int32_t reset_nz;
     int32_t piece_grid;

@@ -245,6 +245,51 @@ template <int POLICY> struct BufLoad<1, POLICY> {
     }
 };
 
+// Buffer stores with cache policy POLICY.  kPolicyDevNt (device scope +
+// non-temporal) is how the direct combine writes its output: a device-scope
+// store is written through to the device's point of coherence -- it is what a
+// relaxed device-scope atomic store compiles to on gfx950 (`sc1`, with no L2
+// write-back around it) -- so once the wave has drained it (s_waitcnt
+// vmcnt(0)) the data is visible to every XCD, and no L2 write-back
+// (`buffer_wbl2`) is needed before the signal.  A reader still acquires
+// (invalidates its own stale L1/L2 lines) after it sees the signal.
+constexpr int kPolicyDevNt = kPolicySc1 | kPolicyNt;
+
+template <int V, int POLICY> struct BufStore;
+template <int POLICY> struct BufStore<16, POLICY> {
+    static __device__ __forceinline__ void go(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, POLICY);
+    }
+};
+template <int POLICY> struct BufStore<8, POLICY> {
+    static __device__ __forceinline__ void go(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, POLICY);
+    }
+};
+template <int POLICY> struct BufStore<4, POLICY> {
+    static __device__ __forceinline__ void go(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, POLICY);
+    }
+};
+template <int POLICY> struct BufStore<2, POLICY> {
+    static __device__ __forceinline__ void go(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, POLICY);
+    }
+};
+template <int POLICY> struct BufStore<1, POLICY> {
+    static __device__ __forceinline__ void go(uint8_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, POLICY);
+    }
+};
+
+// Release of data written with device-scope stores (kPolicyDevNt): every wave
+// drains its own stores -- each is then performed device-wide -- and the
+// workgroup barrier orders them all before the signal wave 0 issues next.
+__device__ __forceinline__ void group_release_written_through() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
 template <typename T>
 __device__ __forceinline__ T load_nt(const T* p) { return __builtin_nontemporal_load(p); }
 template <typename T>

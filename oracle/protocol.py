@@ -541,3 +541,12 @@ def explore_rows(spec: RowSpec, max_states: int = 2_000_000) -> Tuple[int, List[
             nxt.step(ag)
             stack.append(nxt)
     return len(seen), violations, stuck
+
+
+def expected_final_piece_counts(S: int, BS: int, PR: int, W: int, protocol: str) -> List[int]:
+    """Direct mode with tiles cut into pieces of PR tokens: the arrival counter of a
+    tile ends at the number of pieces that fed it -- ceil(rows of its S-block / PR)
+    from each of the W sources under ADD (one counter per tile), from its one source
+    under SET (one counter per tile and source).  Per S-block."""
+    per_source = row_unit_counts(S, BS, PR)
+    return [n * W for n in per_source] if protocol == ADD else per_source

@@ -7,15 +7,33 @@ import math
 import numpy as np
 
 import moe_all2all_combine_amd as ra2a
-from oracle.protocol import ADD, SET, ProtocolSpec, expected_final_credits, expected_final_signals
+from oracle.protocol import (ADD, SET, ProtocolSpec, expected_final_block_counts,
+                             expected_final_credits, expected_final_piece_counts,
+                             expected_final_signals)
+
+ELEM = {"u8": 1, "bf16": 2, "f16": 2, "i32": 4, "f32": 4, "i64": 8, "f64": 8}
+
+
+def row_mode(opts) -> bool:
+    """Whether the options select row units."""
+    return opts.mode == ra2a.MODE_ROWS
+
+
+def unit_rows(W, S, H, D, opts, dtype="bf16") -> int:
+    """Tokens per row unit as the header documents it."""
+    tile_s = opts.tile_s or min(S, 64)
+    ku = opts.unit_rows or max(1, 262144 // (W * H * D * ELEM[dtype]))
+    return min(ku, tile_s)
 
 
 def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):
     """Data signals (one per signal tile) then hand-back counters (one per ring
-    slot of each moved stream, a stream being head_merge adjacent head blocks)."""
-    nbs = math.ceil(S / opts.tile_s)
-    nhb = math.ceil(H / opts.tile_h)
-    ndb = math.ceil(D / opts.tile_d)
+    slot of each moved stream, a stream being head_merge adjacent head blocks),
+    or, with row units, one arrival counter per S-block."""
+    tile_s = opts.tile_s or min(S, 64)
+    nbs = math.ceil(S / tile_s)
+    nhb = math.ceil(H / (opts.tile_h or 1))
+    ndb = math.ceil(D / (opts.tile_d or D))
     direct = opts.mode not in (ra2a.MODE_STAGED, ra2a.MODE_BULK, ra2a.MODE_PULL)
     bulk = opts.mode in (ra2a.MODE_BULK, ra2a.MODE_PULL)  # staged, but no ring: data signals only
     R = nbs if (direct or bulk) else min(opts.ring or 8, nbs)
@@ -27,16 +45,35 @@ def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):
     per = W if proto == SET else 1
     # merged head blocks: derived from the size of the hand-back region
     _, n_credit, _ = ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)
-    if direct or bulk:
-        # no ring (direct: no consumer work either): the data signals only
-        assert n_credit == 0
+    if row_mode(opts):
         tiles = ProtocolSpec(W=W, nbs=nbs, nstreams=nhb * ndb, R=R, protocol=proto)
         ns = nhb * ndb
         a = np.zeros(nbs * ns * per, dtype=np.int64)
         for k, v in expected_final_signals(tiles).items():
             if k[0] == 0:
                 a[(k[2] * ns + k[1]) * per + (k[3] if proto == SET else 0)] = v
-        return a
+        b = np.asarray(expected_final_block_counts(S, tile_s, unit_rows(W, S, H, D, opts, dtype)),
+                       dtype=np.int64)
+        assert n_credit == nbs
+        return np.concatenate([a, b])
+    if direct or bulk:
+        # no ring (direct: no consumer work either): the data signals, then (direct
+        # mode with tiles cut into several pieces) one arrival counter per moved tile
+        tiles = ProtocolSpec(W=W, nbs=nbs, nstreams=nhb * ndb, R=R, protocol=proto)
+        ns = nhb * ndb
+        a = np.zeros(nbs * ns * per, dtype=np.int64)
+        for k, v in expected_final_signals(tiles).items():
+            if k[0] == 0:
+                a[(k[2] * ns + k[1]) * per + (k[3] if proto == SET else 0)] = v
+        plan = ra2a.rev_all2all_plan(W, S, H, D, dtype, opts) if direct else None
+        if plan is None or plan.pieces_per_tile == 1:
+            assert n_credit == 0
+            return a
+        nm = n_credit // (nbs * per)  # moved tiles per S-block: merged head blocks x d blocks
+        assert nm * nbs * per == n_credit
+        cnt = expected_final_piece_counts(S, tile_s, plan.piece_rows, W, proto)
+        b = np.repeat(np.asarray(cnt, dtype=np.int64), nm * per)
+        return np.concatenate([a, b])
     nmhb = n_credit // (R * ndb * per)
     assert nmhb * R * ndb * per == n_credit
     # data signals: one per signal tile, the model's closed form

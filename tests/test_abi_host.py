@@ -80,8 +80,16 @@ def test_signal_slots_and_workspace():
     Q = ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS  # control words: queue words, then reset flags
     # 64-token x 1-head x 128 tiles, ADD: one slot per (S-block, head) per slice
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
-    # direct mode (the default): no ring, so no hand-back counters
+    # direct mode (the default): one piece per tile and source (128 KiB), so no
+    # counters in region B
     assert (a, b, q) == (8 * 16, 0, Q)
+    # row units: region B holds one arrival counter per S-block
+    a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", ra2a.Opts(mode=ra2a.MODE_ROWS))
+    assert (a, b, q) == (8 * 16, 8, Q)
+    # pieces of 16 tokens: 4 per tile and source, so one arrival counter per moved tile
+    # (S-block, merged head block of 8)
+    a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", ra2a.Opts(piece_rows=16))
+    assert (a, b, q) == (8 * 16, 8 * 2, Q)
     # staged: ring of 8 = every S-block; 256-B heads would merge 16 at a time into
     # 4 KiB runs, but that leaves only 512 pieces, so 8 at a time (1024 pieces):
     # 2 moved streams per destination
@@ -102,8 +110,15 @@ def test_signal_slots_and_workspace():
     a, b, _ = ra2a.rev_all2all_signal_slots(8, 4096, 1, 7168, "bf16",
                                             ra2a.Opts(tile_s=32, mode=ra2a.MODE_STAGED))
     assert (a, b) == (128, 8)
+    # 448 KiB of one source per tile: four pieces of 8 tokens, a counter per tile
     a, b, _ = ra2a.rev_all2all_signal_slots(8, 4096, 1, 7168, "bf16", ra2a.Opts(tile_s=32))
+    assert (a, b) == (128, 128)
+    a, b, _ = ra2a.rev_all2all_signal_slots(8, 4096, 1, 7168, "bf16",
+                                            ra2a.Opts(tile_s=32, piece_rows=32))
     assert (a, b) == (128, 0)
+    pl = ra2a.rev_all2all_plan(8, 4096, 1, 7168, "bf16", ra2a.Opts(tile_s=32))
+    assert (pl.mode, pl.piece_rows, pl.pieces_per_tile, pl.work_items) == (
+        ra2a.MODE_DIRECT, 8, 4, 8 * 128 * 4 * 8)
     # ragged: S=37 in tiles of 16 -> 3 blocks; D=40 in tiles of 16 -> 3 d blocks
     a, b, _ = ra2a.rev_all2all_signal_slots(3, 37, 2, 40, "bf16",
                                             ra2a.Opts(tile_s=16, tile_d=16, mode=ra2a.MODE_STAGED))
@@ -238,3 +253,23 @@ def test_gemm_rs_rejects_bad_arguments(fake_heap):
     assert _grs(fake_heap, x1, x2t, p, out, b + (4 << 20) - 64) == E             # signals past the slice
     assert _grs(fake_heap, x1, x2t, p, out, sig, flags=8) == E                   # unknown flag
     assert _grs(fake_heap, x1, x2t, 0, out, sig) == E                            # NULL
+
+
+def test_exit_hook_closes_open_heaps():
+    """A process that exits with attached heaps open ends normally: the binding
+    tracks them and its exit hook destroys them (no GPU involved: an attached
+    heap that never ran makes no HIP call)."""
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import moe_all2all_combine_amd as ra2a\n"
+            "h = ra2a.symm_heap_attach(0x7f0000000000, 2, 1 << 20)\n"
+            "assert h in ra2a._open_handles\n"
+            "ra2a._close_all_heaps()\n"
+            "assert not ra2a._open_handles\n"
+            "h2 = ra2a.symm_heap_attach(0x7f0000000000, 2, 1 << 20)\n"
+            "print('ok', flush=True)\n") % root
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr

@@ -103,11 +103,48 @@ def test_emulated_lookahead(lookahead, W, S, H, D, tile, proto, ring, stream_bat
 def test_emulated_direct_mode(W, S, H, D, dtype, tile, proto):
     opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2],
                      protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD)
-    assert opts.mode == 0  # the default is the direct mode
+    assert opts.mode == 0  # the default: direct mode, per-source pieces
     assert ra2a.rev_all2all_workspace_bytes(W, S, H, D, dtype, opts) == 0
     check_emulation(W, S, H, D, dtype, opts, 1, seed=3)
     opts.mode = ra2a.MODE_DIRECT
     check_emulation(W, S, H, D, dtype, opts, 1, seed=3)
+    for pr in (1, 3, tile[0] // 2 or 1):  # tiles cut into pieces: arrival counters
+        opts.piece_rows = pr
+        check_emulation(W, S, H, D, dtype, opts, 1, seed=3)
+
+
+@pytest.mark.parametrize("unit_rows", [0, 1, 2, 3, 5, 64, 1000])
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto", [
+    (3, 37, 2, 40, "bf16", (16, 1, 16), P_ADD), (3, 37, 2, 40, "bf16", (16, 1, 16), P_SET),
+    (8, 512, 16, 128, "bf16", (64, 1, 128), P_ADD), (16, 64, 32, 128, "f32", (64, 1, 128), P_SET),
+    (2, 8, 4, 16, "i32", (8, 4, 16), P_SET), (1, 9, 3, 7, "u8", (4, 2, 3), P_ADD),
+    (8, 96, 1, 7168, "bf16", (32, 1, 7168), P_ADD), (5, 33, 3, 12, "u8", (7, 2, 5), P_SET),
+])
+def test_emulated_row_units(unit_rows, W, S, H, D, dtype, tile, proto):
+    """Row units: every output row written once by one unit, the bytes equal the
+    oracle's, every signal tile ends at W (ADD) or 1 (SET) and every S-block's
+    arrival counter at its unit count (the protocol model's closed forms)."""
+    opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2], unit_rows=unit_rows,
+                     mode=ra2a.MODE_ROWS,
+                     protocol=ra2a.PROTO_SET if proto == P_SET else ra2a.PROTO_ADD)
+    check_emulation(W, S, H, D, dtype, opts, 1, seed=5)
+
+
+def test_row_units_rejected_for_dispatch_and_straggler():
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16",
+                                      ra2a.Opts(mode=ra2a.MODE_ROWS, direction=ra2a.DIR_DISPATCH))
+    assert e.value.code == ra2a.EINVAL
+    with pytest.raises(ra2a.Ra2aError) as e:
+        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16",
+                                      ra2a.Opts(mode=ra2a.MODE_ROWS, straggler_rank=1,
+                                                straggler_delay=10))
+    assert e.value.code == ra2a.EINVAL
+    with pytest.raises(ra2a.Ra2aError):
+        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", ra2a.Opts(unit_rows=-1))
+    with pytest.raises(ra2a.Ra2aError):
+        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", ra2a.Opts(piece_rows=-1))
+    assert ra2a.rev_all2all_plan(4, 64, 2, 64, "bf16", ra2a.Opts(mode=ra2a.MODE_ROWS)).credit_slots == 1
 
 
 @pytest.mark.parametrize("head_merge", [1, 2, 3, 16])
@@ -143,8 +180,9 @@ DISPATCH_CASES = [
 @pytest.mark.parametrize("W,S,H,D,dtype,tile", DISPATCH_CASES)
 @pytest.mark.parametrize("head_merge", [0, 1, 3])
 def test_emulated_dispatch_matches_oracle(W, S, H, D, dtype, tile, head_merge):
-    """The kernel's dispatch geometry moves exactly the oracle's bytes, and every
-    (tile, source) signal ends at 1."""
+    """The kernel's dispatch geometry moves exactly the oracle's bytes, every
+    (tile, source) signal ends at 1, and (tiles cut into pieces) every arrival
+    counter at its closed form."""
     opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2], head_merge=head_merge,
                      direction=ra2a.DIR_DISPATCH)
     wl = synthgen.small_workload(W, S, H, D, dtype, seed=S + 3 * W, tile=tile)
@@ -152,7 +190,9 @@ def test_emulated_dispatch_matches_oracle(W, S, H, D, dtype, tile, head_merge):
     outs, sigs = ra2a.debug_emulate_pipelined(ins, W, S, H, D, dtype, opts)
     want = oracle.dispatch(ins)
     exp = expected_signal_array(W, S, H, D, opts, 1, dtype)
-    assert (exp == 1).all() and len(exp) == W * -(-S // tile[0]) * -(-H // tile[1]) * -(-D // tile[2])
+    n_a = W * -(-S // tile[0]) * -(-H // tile[1]) * -(-D // tile[2])
+    assert (exp[:n_a] == 1).all()
+    assert len(exp) == n_a + ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)[1]
     for r in range(W):
         assert outs[r].tobytes() == want[r].tobytes(), f"rank {r}"
         np.testing.assert_array_equal(sigs[r][:len(exp)].astype(np.int64), exp)
@@ -166,7 +206,7 @@ def test_dispatch_rejects_staged_mode(mode):
         ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", opts)
     assert e.value.code == ra2a.EINVAL
     with pytest.raises(ra2a.Ra2aError):
-        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", ra2a.Opts(mode=5))
+        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", ra2a.Opts(mode=6))
     with pytest.raises(ra2a.Ra2aError):
         ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16", ra2a.Opts(direction=2))
 

@@ -36,8 +36,11 @@ def check_queue_words(q, opts):
     q = q.astype(np.uint64)
     assert len(q) == ra2a.QUEUE_SLOTS == 18
     if opts.mode not in QUEUED:
-        # the direct mode runs a static schedule: no queue words are touched
-        assert not q.any(), q
+        # the direct modes touch only the last word: the claim counter of a dynamic
+        # schedule, which ends at the number of work items (or stays 0: static)
+        assert not q[:17].any(), q
+        work = ra2a.rev_all2all_plan(*opts._shape, opts).work_items if hasattr(opts, "_shape") else None
+        assert int(q[17]) == 0 or work is None or int(q[17]) == work, (int(q[17]), work)
         return
     assert int(q[16]) == 0xFF and int(q[17]) == 0, q[16:]
     for g, (head, taker) in enumerate(q[:16].reshape(8, 2)):
@@ -52,6 +55,7 @@ def check_queue_words(q, opts):
 
 def run_and_check(wl, opts, variant="pipelined", inputs=None, want=None, check_signals=True,
                   csplit=None):
+    opts._shape = (wl.W, wl.S, wl.H, wl.D, wl.dtype)
     say(f"[case] {variant} {wl.name} W={wl.W} S={wl.S} H={wl.H} D={wl.D} {wl.dtype} "
         f"tile=({opts.tile_s},{opts.tile_h},{opts.tile_d}) proto={opts.protocol} ring={opts.ring}")
     case = CombineCase(wl, opts, two_phase=(variant == "two_phase"))
@@ -104,10 +108,15 @@ def test_small_staged(W, S, H, D, dtype, tile, proto, ring, csplit):
 
 
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL)
-@pytest.mark.parametrize("agent", [0, 1])
-def test_small_direct(W, S, H, D, dtype, tile, proto, ring, agent):
+@pytest.mark.parametrize("knobs", [dict(), dict(piece_rows=1), dict(piece_rows=3),
+                                   dict(piece_rows=5, wg_per_cu=1),
+                                   dict(mode=ra2a.MODE_ROWS), dict(mode=ra2a.MODE_ROWS, unit_rows=1),
+                                   dict(mode=ra2a.MODE_ROWS, unit_rows=3)])
+def test_small_direct(W, S, H, D, dtype, tile, proto, ring, knobs):
+    """The direct modes: per-source pieces (the default; whole tiles, or tiles cut
+    into pieces of a few tokens with arrival counters) and row units."""
     wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S + 2, tile=tile, protocol=proto)
-    opts = opts_for(wl, agent_sync=agent)
+    opts = opts_for(wl, **knobs)
     run_and_check(wl, opts, csplit=1)
 
 
@@ -137,7 +146,7 @@ def test_small_two_phase(W, S, H, D, dtype, tile, proto, ring):
     run_and_check(wl, opts_for(wl), variant="two_phase")
 
 
-@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
+@pytest.mark.parametrize("mode", [0, ra2a.MODE_ROWS, ra2a.MODE_STAGED])
 def test_iota_w2_worked_case(mode):
     wl = synthgen.WORKLOADS["iota_w2_s8_h4_d16_i32"]
     opts = opts_for(wl, consumer_split=1, mode=mode)
@@ -194,17 +203,19 @@ def test_back_to_back_launches_reset_signals():
 DIRTY = 0x5A  # byte pattern left in the signal array before a launch
 
 
-@pytest.mark.parametrize("reset", ["in_launch", "separate", "no_room"])
-def test_direct_reset_clears_dirty_signals(reset):
-    """Direct mode zeroes the signals inside the combine launch (with
-    separate_reset, or when the occupancy leaves no room for the zeroing
-    workgroups, in a launch of its own): whatever the signal array held, the
-    data signals end at their counts and the queue words at 0, launch after
-    launch; each in-launch reset leaves its own tag in the reset flags."""
+@pytest.mark.parametrize("mode", [0, ra2a.MODE_ROWS])
+@pytest.mark.parametrize("reset", ["in_launch", "separate", "full_grid"])
+def test_direct_reset_clears_dirty_signals(reset, mode):
+    """The direct modes zero the signals inside the combine launch (with
+    separate_reset, in a launch of its own), also when the persistent grid fills
+    every slot the occupancy allows: whatever the signal array held, the data
+    signals and counters end at their closed forms and the queue words at 0,
+    launch after launch; each in-launch reset leaves its own tag in the reset
+    flags."""
     wl = synthgen.small_workload(8, 96, 4, 64, "bf16", seed=11, tile=(16, 1, 64),
                                  protocol=synthgen.PROTOCOL_ADD)
-    knobs = {"in_launch": {}, "separate": dict(separate_reset=1), "no_room": dict(wg_per_cu=64)}
-    opts = opts_for(wl, **knobs[reset])
+    knobs = {"in_launch": {}, "separate": dict(separate_reset=1), "full_grid": dict(wg_per_cu=64)}
+    opts = opts_for(wl, mode=mode, **knobs[reset])
     case = CombineCase(wl, opts)
     dirty = int.from_bytes(bytes([DIRTY]) * 8, "little")
     try:
@@ -226,20 +237,20 @@ def test_direct_reset_clears_dirty_signals(reset):
                 np.testing.assert_array_equal(case.signals(j), exp, err_msg=f"signals of rank {j}")
             assert not case.queue_words().any()
             f = [int(x) & (2**64 - 1) for x in case.reset_flags()]
-            if reset == "in_launch":
+            if reset != "separate":
                 nz = next((k for k in range(1, len(f)) if f[k] != f[0]), len(f))
                 assert f[0] not in (0, dirty), hex(f[0])
                 assert all(x == dirty for x in f[nz:]), "flags past the zeroing workgroups moved"
                 tags.append(f[0])
             else:
                 assert all(x == dirty for x in f), "a separate reset launch leaves the flags alone"
-        if reset == "in_launch":
+        if reset != "separate":
             assert len(set(tags)) == len(tags), "every launch has a tag of its own"
     finally:
         case.close()
 
 
-@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
+@pytest.mark.parametrize("mode", [0, ra2a.MODE_ROWS, ra2a.MODE_STAGED])
 def test_graph_capture_and_replay(mode):
     """A combine captured in a HIP graph and replayed three times, with eager work
     between the replays (outputs poisoned, signal arrays and control words filled
@@ -299,7 +310,7 @@ def test_straggler_timestamps(mode):
     assert t[:, :, lag].mean() > t[:, :, others].mean(), (t[:, :, lag].mean(), t[:, :, others].mean())
 
 
-@pytest.mark.parametrize("mode", [ra2a.MODE_DIRECT, ra2a.MODE_STAGED])
+@pytest.mark.parametrize("mode", [0, ra2a.MODE_ROWS, ra2a.MODE_STAGED])
 def test_pipelined_equals_two_phase_bitwise(mode):
     """The barrier-synchronised variant as a differential for the signal-pipelined one."""
     wl = synthgen.small_workload(8, 300, 4, 72, "f16", seed=9, tile=(24, 1, 72))
@@ -352,6 +363,12 @@ def full_case(name, variant, **kw):
     if variant in ("staged", "bulk", "pull"):
         kw["mode"] = {"staged": ra2a.MODE_STAGED, "bulk": ra2a.MODE_BULK, "pull": ra2a.MODE_PULL}[variant]
         variant = "pipelined"
+    elif variant == "rows":
+        kw["mode"] = ra2a.MODE_ROWS
+        variant = "pipelined"
+    elif variant == "whole_tiles":  # one piece per tile and source
+        kw["piece_rows"] = wl.tile_s
+        variant = "pipelined"
     else:
         kw.pop("consumer_split", None)
     opts = opts_for(wl, consumer_split=kw.pop("consumer_split", 1), **kw)
@@ -359,12 +376,13 @@ def full_case(name, variant, **kw):
                   csplit=None if opts.mode in QUEUED else 1)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "pull", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "rows", "staged", "bulk", "pull", "two_phase"])
 def test_full_ep_combine_w8_bf16(variant):
     full_case("ep_combine_w8_s512_h16_d128_bf16", variant)
 
 
-@pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "pull", "two_phase"])
+@pytest.mark.parametrize("variant", ["pipelined", "whole_tiles", "rows", "staged", "bulk", "pull",
+                                     "two_phase"])
 def test_full_moe_combine_w8_d7168(variant):
     full_case("moe_combine_w8_s4096_h1_d7168_bf16", variant, consumer_split=4)
 
@@ -374,3 +392,10 @@ def test_full_straggler_w16_f32(variant):
     wl = synthgen.WORKLOADS["straggler_w16_s2048_h32_d128_f32"]
     full_case("straggler_w16_s2048_h32_d128_f32", variant,
               straggler_rank=synthgen.straggler_rank(wl), straggler_delay=200, straggler_seed=2)
+
+
+@pytest.mark.parametrize("variant", ["pipelined", "rows"])
+def test_full_straggler_w16_f32_undelayed(variant):
+    """The C4 shape without the delay (SET per (tile, source)): the default direct
+    mode (dynamically claimed pieces, arrival counters) and row units."""
+    full_case("straggler_w16_s2048_h32_d128_f32", variant)

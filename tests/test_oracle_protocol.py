@@ -162,3 +162,12 @@ def test_rows_negative_controls_fire(control, protocol):
     spec = row_spec(protocol, n_workers=3, **{control: True})
     _, violations, _ = explore_rows(spec)
     assert violations, f"{control} must let a consumer read unpublished rows"
+
+
+def test_piece_counts_worked():
+    from oracle.protocol import expected_final_piece_counts
+    # the MoE-combine shape: 32-token tiles cut into 8-token pieces, 8 sources, ADD
+    assert expected_final_piece_counts(4096, 32, 8, 8, ADD) == [32] * 128
+    # ragged: S = 37, tiles of 16, pieces of 6 -> parts 3, 3, 1; SET counts per source
+    assert expected_final_piece_counts(37, 16, 6, 3, SET) == [3, 3, 1]
+    assert expected_final_piece_counts(37, 16, 6, 3, ADD) == [9, 9, 3]
