@@ -515,9 +515,10 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
 
 // Number of XCDs of the current device (the largest XCC_ID a probe launch of
 // 4096 workgroups observed, plus one), measured once per device.
+std::mutex& g_xcd_mu = *new std::mutex;
+int g_xcd_n[64];  // per device: measured XCD count, 0 = not measured yet
+
 int xcd_count(int* nxcd) {
-    static std::mutex mu;
-    static int cached_n[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -525,7 +526,8 @@ int xcd_count(int* nxcd) {
         *nxcd = 1;
         return RA2A_OK;
     }
-    std::lock_guard<std::mutex> g(mu);
+    std::lock_guard<std::mutex> g(g_xcd_mu);
+    int* cached_n = g_xcd_n;
     if (!cached_n[dev]) {
         const int n = 4096;
         uint32_t* d = nullptr;
@@ -1089,9 +1091,12 @@ RA2A_API int ra2a_ag_gemm_signal_slots(int W, int64_t m_local, int tile_rows, in
     return ok();
 }
 
-RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, void* c,
-                          uint64_t* signals, int W, int rank, int64_t m_local, int64_t K, int64_t N,
-                          int tile_rows, int flags, void* stream) {
+namespace {
+
+// The AllGather+GEMM's host side: validation, planning, the B^T workspace, launches.
+int ag_gemm_run(const void* a_shards, void* gathered, const void* b, void* c, uint64_t* signals,
+                int W, int rank, int64_t m_local, int64_t K, int64_t N, int tile_rows, int flags,
+                void* stream) {
     if (flags & ~(RA2A_AG_AGENT_SYNC | RA2A_AG_SKIP_RESET | RA2A_AG_B_TRANSPOSED))
         return fail(RA2A_EINVAL, "unknown flags");
     if (!a_shards || !gathered || !b || !c || !signals) return fail(RA2A_EINVAL, "NULL pointer");
@@ -1101,10 +1106,12 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
     if (!in_heap(h, gathered) || !in_heap(h, signals))
         return fail(RA2A_EINVAL, "gathered and signals must be inside the heap of a_shards");
     int nxcd = 1;
-    int rc = xcd_count(&nxcd);
+    int rc = RA2A_OK;
+    const bool agent = (flags & RA2A_AG_AGENT_SYNC) != 0;
+    rc = xcd_count(&nxcd);
     if (rc) return rc;
     ra2a::AgGemmArgs a{};
-    rc = plan_ag_gemm(W, rank, m_local, K, N, tile_rows, nxcd, (flags & RA2A_AG_AGENT_SYNC) != 0, &a);
+    rc = plan_ag_gemm(W, rank, m_local, K, N, tile_rows, nxcd, agent, &a);
     if (rc) return rc;
     const size_t a_off = sym_offset(h, a_shards), g_off = sym_offset(h, gathered);
     const size_t s_off = sym_offset(h, signals);
@@ -1120,6 +1127,14 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
     if (overlap(a_off, shard_bytes, g_off, g_bytes) || overlap(a_off, shard_bytes, s_off, s_bytes) ||
         overlap(g_off, g_bytes, s_off, s_bytes))
         return fail(RA2A_EINVAL, "a_shards, gathered and signals overlap");
+    // XCD-local synchronisation reads G through the CU's L1, and a GEMM row block
+    // waits only for the AllGather tiles of its own rows.  If a 128-byte line of G
+    // held rows of two row blocks, a block could cache the line before the next
+    // block's rows arrive and a later tile on the same CU read them stale.  Row
+    // blocks start at g_off + (w*m_local + 256*mb)*K*2 bytes; unless every such
+    // start is 128-byte aligned, synchronise device-wide (the acquire drops L1).
+    if (a.sync == ra2a::kSyncXcd && (g_off % 128 != 0 || shard_bytes % 128 != 0))
+        a.sync = ra2a::kSyncAgent;
     rc = ensure_err(h);
     if (rc) return rc;
     a.base = h->base;
@@ -1131,8 +1146,9 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
     if (flags & RA2A_AG_B_TRANSPOSED) {
         a.bt = static_cast<const uint16_t*>(b);
     } else {
-        // B^T into the heap's workspace (the matrix cores take both operands k-contiguous)
+        // B^T into a workspace (the matrix cores take both operands k-contiguous)
         const size_t need = (size_t)(K * N * 2);
+        uint16_t* bt = nullptr;
         {
             std::lock_guard<std::mutex> lk(h->mu);
             if (h->bt_bytes < need) {
@@ -1152,11 +1168,11 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
                 h->bt_ws = p;
                 h->bt_bytes = need;
             }
+            bt = static_cast<uint16_t*>(h->bt_ws);
         }
-        hipError_t e = ra2a::launch_transpose_b(static_cast<const uint16_t*>(b),
-                                                static_cast<uint16_t*>(h->bt_ws), K, N, st);
+        hipError_t e = ra2a::launch_transpose_b(static_cast<const uint16_t*>(b), bt, K, N, st);
         if (e != hipSuccess) return hip_fail(e, "B transpose launch");
-        a.bt = static_cast<const uint16_t*>(h->bt_ws);
+        a.bt = bt;
     }
     a.c = static_cast<uint16_t*>(c);
     a.err = h->err;
@@ -1175,6 +1191,15 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
     he = ra2a::launch_ag_gemm(a, occ * ncu, st);
     if (he != hipSuccess) return hip_fail(he, "AllGather+GEMM launch");
     return ok();
+}
+
+}  // namespace
+
+RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, void* c,
+                          uint64_t* signals, int W, int rank, int64_t m_local, int64_t K, int64_t N,
+                          int tile_rows, int flags, void* stream) {
+    return ag_gemm_run(a_shards, gathered, b, c, signals, W, rank, m_local, K, N, tile_rows, flags,
+                       stream);
 }
 
 // ===========================================================================
@@ -1580,13 +1605,21 @@ RA2A_API int ra2a_check(const ra2a_heap_t* h) {
     if (!h) return fail(RA2A_EINVAL, "heap must be non-NULL");
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-    if (!h->err) return ok();
+    // the heap's error word, if it exists: read and cleared
     uint32_t w = 0;
-    e = hipMemcpy(&w, h->err, sizeof w, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_fail(e, "reading the error word");
+    uint32_t* words[1] = {h->err};
+    for (uint32_t* word : words) {
+        if (!word) continue;
+        uint32_t x = 0;
+        e = hipMemcpy(&x, word, sizeof x, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "reading an error word");
+        if (x) {
+            e = hipMemset(word, 0, sizeof x);
+            if (e != hipSuccess) return hip_fail(e, "clearing an error word");
+        }
+        w |= x;
+    }
     if (w) {
-        e = hipMemset(h->err, 0, sizeof w);
-        if (e != hipSuccess) return hip_fail(e, "clearing the error word");
         if (w & (ra2a::kErrCounts | ra2a::kErrOverflow))
             return fail(RA2A_EDATA, "device-side data check failed (error word 0x%x:%s%s%s)", w,
                         (w & ra2a::kErrCounts) ? " a sender's counts were unusable" : "",

@@ -34,8 +34,11 @@ def parts_per_tile(m_local, K, tile_rows):
     return [math.ceil(tr / rpp)] * (ntiles - 1) + [math.ceil(rows_last / rpp)]
 
 
-def run_ag_gemm(shards, b, tile_rows, rank=0, flags=0):
-    """b is B (K x N), or B^T (N x K) when flags has AG_B_TRANSPOSED."""
+def run_ag_gemm(shards, b, tile_rows, rank=0, flags=0, entry=None, g_pad=0):
+    """b is B (K x N), or B^T (N x K) when flags has AG_B_TRANSPOSED.  `entry`:
+    the binding function to call (ra2a.ag_gemm by default); g_pad: bytes of
+    padding before G in its slice (an offset that is not a multiple of 128)."""
+    entry = entry or ra2a.ag_gemm
     W = len(shards)
     m_local, K = shards[0].shape
     N = b.shape[0] if flags & ra2a.AG_B_TRANSPOSED else b.shape[1]
@@ -45,7 +48,9 @@ def run_ag_gemm(shards, b, tile_rows, rank=0, flags=0):
     heap = ra2a.SymmHeap(W, shard_bytes + W * shard_bytes + nsig * 128 + (1 << 16))
     try:
         off_a = heap.alloc(shard_bytes)
-        off_g = heap.alloc(W * shard_bytes)
+        if g_pad:
+            heap.alloc(g_pad, 16)
+        off_g = heap.alloc(W * shard_bytes, 16)
         off_s = heap.alloc(nsig * 128)
         for w in range(W):
             heap.view(off_a, (m_local, K), torch.int16, w).copy_(
@@ -54,9 +59,9 @@ def run_ag_gemm(shards, b, tile_rows, rank=0, flags=0):
         bt = torch.from_numpy(b.view(np.int16)).cuda()
         ct = torch.full((W * m_local, N), 0x7FC1, dtype=torch.int16, device="cuda")
         torch.cuda.synchronize()
-        ra2a.ag_gemm(heap.ptr(off_a), heap.ptr(off_g), bt.data_ptr(), ct.data_ptr(),
-                     heap.ptr(off_s), W, rank, m_local, K, N, tile_rows, flags,
-                     torch.cuda.current_stream())
+        entry(heap.ptr(off_a), heap.ptr(off_g), bt.data_ptr(), ct.data_ptr(),
+              heap.ptr(off_s), W, rank, m_local, K, N, tile_rows, flags,
+              torch.cuda.current_stream())
         torch.cuda.synchronize()
         rc = ra2a.check(heap.handle)
         assert rc == ra2a.OK, ra2a.last_error()
@@ -87,6 +92,8 @@ EXACT = [
     (8, 64, 4096, 8, 512, 3),      # N smaller than one column tile
     (2, 96, 192, 136, 48, 1),      # three 64-k stages: the one refill of the ring
     (4, 64, 128, 64, 32, 2),       # two whole stages, no refill
+    (2, 601, 8, 40, 128, 0),       # shard starts off the 128-byte grid: device-wide sync
+    (3, 601, 72, 64, 128, 1),
 ]
 
 
@@ -139,3 +146,28 @@ def test_full_workload_sampled_rows():
     err = gemm.rel_error(gemm.bf16_bits_to_f64(c[rows]), ref)
     say(f"[full] rel error {err:.3e}")
     assert err <= 1e-2, err
+
+
+@pytest.mark.parametrize("g_pad", [16, 48])
+def test_gathered_matrix_off_the_line_grid(g_pad):
+    """G starting 16 or 48 bytes past a 128-byte line: row blocks share lines with
+    their neighbours, so the launch synchronises device-wide; bit-exact."""
+    W, m_local, K, N = 4, 520, 64, 96
+    say(f"[case] ag_gemm G offset by {g_pad} bytes")
+    shards, b = synthgen.make_integer_ag_gemm_inputs(W, m_local, K, N, seed=17)
+    c, g, sig, counts = run_ag_gemm(shards, b, 128, 1, 0, g_pad=g_pad)
+    check_common(shards, b, 128, c, g, sig, counts)
+    np.testing.assert_array_equal(c, gemm.f64_to_bf16_rne_bits(gemm.ag_gemm_ref(shards, b)))
+
+
+def test_full_workload_integer_inputs_bit_exact():
+    """The AllGather+GEMM workload's full shape (W=8 shards of 1024 x 7168, B 7168 x
+    4096) with integer inputs in {-1, 0, 1}: every output element bit for bit."""
+    wl = synthgen.AG_GEMM
+    say("[case] ag_gemm full shape, integer inputs, whole output")
+    shards, b = synthgen.make_integer_ag_gemm_inputs(wl.W, wl.m_local, wl.K, wl.N, seed=23)
+    c, g, sig, counts = run_ag_gemm(shards, b, wl.tile_rows, 0)
+    check_common(shards, b, wl.tile_rows, c, g, sig, counts)
+    say("[full] fp64 reference")
+    ref = gemm.ag_gemm_ref(shards, b)
+    np.testing.assert_array_equal(c, gemm.f64_to_bf16_rne_bits(ref))
