@@ -465,6 +465,25 @@ int ra2a_ag_gemm(const void *a_shards, void *gathered, const void *b, void *c, u
                  int W, int rank, int64_t m_local, int64_t K, int64_t N, int tile_rows, int flags,
                  void *stream);
 
+/* The same AllGather+GEMM for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It calls no hipMalloc, hipFree or other allocating routine.  Arguments,
+ * results and errors as ra2a_ag_gemm; the kernels are the same.  Differences:
+ *   - B^T (unless RA2A_AG_B_TRANSPOSED) goes to a static device array of the
+ *     library, 64 MiB per GPU (K * N * 2 bytes at most, EINVAL beyond), which
+ *     each GPU the library runs on holds until the process ends;
+ *   - the device error word is in that array too: ra2a_check on any heap of
+ *     the device reports (and clears) a wait that gave up;
+ *   - unless an earlier allocating call on the device has measured its XCDs,
+ *     producers and consumers synchronise device-wide (as RA2A_AG_AGENT_SYNC).
+ * Every call on one GPU shares that array, which keeps the last call's B^T:
+ * calls that overlap in time on one GPU (other streams, other threads) race on
+ * it; order them on one stream.  The first call on a device looks up the
+ * array's address (once per device; make it outside graph capture).          */
+int ra2a_ag_gemm_noalloc(const void *a_shards, void *gathered, const void *b, void *c,
+                         uint64_t *signals, int W, int rank, int64_t m_local, int64_t K,
+                         int64_t N, int tile_rows, int flags, void *stream);
+
 /* Host check of the AllGather+GEMM work queues for a device of `num_xcd` XCDs
  * (no GPU needed): every part and GEMM tile queued exactly once, parts cover
  * each shard's rows once without straddling tiles, and every GEMM tile queued

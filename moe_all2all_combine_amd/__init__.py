@@ -26,7 +26,7 @@ __all__ = [
     "put_with_signal", "signal_op", "wait_signal", "signal_reset", "rev_all2all",
     "rev_all2all_ex", "rev_all2all_two_phase", "rev_all2all_plan", "Plan", "rev_all2all_signal_slots",
     "rev_all2all_workspace_bytes", "check", "last_error", "version", "ag_gemm",
-    "ag_gemm_signal_slots", "debug_ag_gemm_plan", "AG_AGENT_SYNC", "AG_SKIP_RESET",
+    "ag_gemm_signal_slots", "ag_gemm_noalloc", "debug_ag_gemm_plan", "AG_AGENT_SYNC", "AG_SKIP_RESET",
     "AG_B_TRANSPOSED",
 ]
 
@@ -128,6 +128,7 @@ def lib():
         "ra2a_ag_gemm_signal_slots": (i32, [i32, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                             ctypes.POINTER(i64)]),
         "ra2a_ag_gemm": (i32, [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp]),
+        "ra2a_ag_gemm_noalloc": (i32, [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp]),
         "ra2a_debug_ag_gemm_plan": (i32, [i32, i32, i64, i64, i64, i32, i32, ctypes.POINTER(i64)]),
         "ra2a_gemm_rs_sizes": (i32, [i32, i64, i64, i64, i32, ctypes.POINTER(i64),
                                      ctypes.POINTER(i64), ctypes.POINTER(sz)]),
@@ -401,6 +402,14 @@ def ag_gemm(a_shards: int, gathered: int, b: int, c: int, signals: int, W: int, 
             m_local: int, K: int, N: int, tile_rows: int = 128, flags: int = 0, stream=None) -> None:
     _ok(lib().ra2a_ag_gemm(a_shards, gathered, b, c, signals, W, rank, m_local, K, N, tile_rows,
                            flags, _stream(stream)))
+
+
+def ag_gemm_noalloc(a_shards: int, gathered: int, b: int, c: int, signals: int, W: int, rank: int,
+                    m_local: int, K: int, N: int, tile_rows: int = 128, flags: int = 0,
+                    stream=None) -> None:
+    """ra2a_ag_gemm_noalloc: the AllGather+GEMM without any device allocation."""
+    _ok(lib().ra2a_ag_gemm_noalloc(a_shards, gathered, b, c, signals, W, rank, m_local, K, N,
+                                   tile_rows, flags, _stream(stream)))
 
 
 def debug_ag_gemm_plan(W: int, rank: int, m_local: int, K: int, N: int, tile_rows: int,

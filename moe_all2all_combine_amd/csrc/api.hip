@@ -65,6 +65,19 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
+// Set while an allocation-free entry point runs on this thread: the library's
+// own allocations (error words, workspaces, the XCD probe) refuse to run then.
+thread_local bool g_no_alloc = false;
+struct NoAllocScope {
+    NoAllocScope() { g_no_alloc = true; }
+    ~NoAllocScope() { g_no_alloc = false; }
+};
+
+int no_alloc_refused(const char* what) {
+    return fail(RA2A_EUNSUPPORTED, "internal: %s would allocate inside an allocation-free entry point",
+                what);
+}
+
 int hip_fail(hipError_t e, const char* what) {
     return fail(RA2A_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
@@ -119,6 +132,7 @@ uint64_t timeout_ticks(const ra2a_heap* h) {
 int ensure_err(ra2a_heap* h) {
     std::lock_guard<std::mutex> g(h->mu);
     if (h->err) return RA2A_OK;
+    if (g_no_alloc) return no_alloc_refused("the heap's error word");
     void* ew = nullptr;
     hipError_t e = hipMalloc(&ew, 256);
     if (e == hipSuccess) e = hipMemset(ew, 0, 256);
@@ -386,6 +400,7 @@ int heap_alloc(ra2a_heap* h, size_t bytes, size_t align, size_t* off) {
 
 // Staging area of at least `bytes` per slice, cached per heap.
 int staging(ra2a_heap* h, bool full, size_t bytes, size_t* off) {
+    if (g_no_alloc) return no_alloc_refused("staging");
     std::lock_guard<std::mutex> g(h->mu);
     size_t& co = full ? h->full_off : h->ring_off;
     size_t& cb = full ? h->full_bytes : h->ring_bytes;
@@ -529,6 +544,7 @@ int xcd_count(int* nxcd) {
     std::lock_guard<std::mutex> g(g_xcd_mu);
     int* cached_n = g_xcd_n;
     if (!cached_n[dev]) {
+        if (g_no_alloc) return no_alloc_refused("the XCD probe");
         const int n = 4096;
         uint32_t* d = nullptr;
         e = hipMalloc(&d, n * sizeof(uint32_t));
@@ -545,6 +561,16 @@ int xcd_count(int* nxcd) {
     }
     *nxcd = cached_n[dev];
     return RA2A_OK;
+}
+
+// The current device's XCD count if an earlier call measured it (no probe).
+bool xcd_count_known(int* nxcd) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    std::lock_guard<std::mutex> g(g_xcd_mu);
+    if (!g_xcd_n[dev]) return false;
+    *nxcd = g_xcd_n[dev];
+    return true;
 }
 
 // Tag of one in-launch reset: a process-wide counter starting at a random
@@ -1093,10 +1119,44 @@ RA2A_API int ra2a_ag_gemm_signal_slots(int W, int64_t m_local, int tile_rows, in
 
 namespace {
 
-// The AllGather+GEMM's host side: validation, planning, the B^T workspace, launches.
+// The allocation-free entry points keep their workspace and error word in one
+// static device array per GPU (`scratch`): the first kScratchErrBytes hold the
+// error word, the rest the B^T workspace of ra2a_ag_gemm_noalloc.  Host code
+// never passes the array's name to a kernel or a copy (on the host it is only
+// a stand-in): it uses the device address hipGetSymbolAddress gives for the
+// current device, looked up once per device and kept in g_scratch.
+constexpr size_t kScratchErrBytes = 256;
+constexpr size_t kScratchBtBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchErrBytes + kScratchBtBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex& g_scratch_mu = *new std::mutex;
+uint8_t* g_scratch[kMaxDevices];  // per device: scratch's device address, or null
+
+// The current device's scratch address (looked up on first use).
+int scratch_address(uint8_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(RA2A_EUNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch[dev] = static_cast<uint8_t*>(p);
+    }
+    *out = g_scratch[dev];
+    return RA2A_OK;
+}
+
+// Shared by ra2a_ag_gemm and ra2a_ag_gemm_noalloc.  `no_alloc`: B^T goes to the
+// device's scratch array (at most kScratchBtBytes) and errors to its error word;
+// the XCD count is used only if an earlier call measured it (else device-wide
+// synchronisation, which needs no placement knowledge).
 int ag_gemm_run(const void* a_shards, void* gathered, const void* b, void* c, uint64_t* signals,
                 int W, int rank, int64_t m_local, int64_t K, int64_t N, int tile_rows, int flags,
-                void* stream) {
+                void* stream, bool no_alloc) {
     if (flags & ~(RA2A_AG_AGENT_SYNC | RA2A_AG_SKIP_RESET | RA2A_AG_B_TRANSPOSED))
         return fail(RA2A_EINVAL, "unknown flags");
     if (!a_shards || !gathered || !b || !c || !signals) return fail(RA2A_EINVAL, "NULL pointer");
@@ -1107,9 +1167,13 @@ int ag_gemm_run(const void* a_shards, void* gathered, const void* b, void* c, ui
         return fail(RA2A_EINVAL, "gathered and signals must be inside the heap of a_shards");
     int nxcd = 1;
     int rc = RA2A_OK;
-    const bool agent = (flags & RA2A_AG_AGENT_SYNC) != 0;
-    rc = xcd_count(&nxcd);
-    if (rc) return rc;
+    bool agent = (flags & RA2A_AG_AGENT_SYNC) != 0;
+    if (no_alloc) {
+        if (!xcd_count_known(&nxcd)) agent = true;
+    } else {
+        rc = xcd_count(&nxcd);
+        if (rc) return rc;
+    }
     ra2a::AgGemmArgs a{};
     rc = plan_ag_gemm(W, rank, m_local, K, N, tile_rows, nxcd, agent, &a);
     if (rc) return rc;
@@ -1135,8 +1199,14 @@ int ag_gemm_run(const void* a_shards, void* gathered, const void* b, void* c, ui
     // start is 128-byte aligned, synchronise device-wide (the acquire drops L1).
     if (a.sync == ra2a::kSyncXcd && (g_off % 128 != 0 || shard_bytes % 128 != 0))
         a.sync = ra2a::kSyncAgent;
-    rc = ensure_err(h);
-    if (rc) return rc;
+    uint8_t* scr = nullptr;
+    if (no_alloc) {
+        rc = scratch_address(&scr);
+        if (rc) return rc;
+    } else {
+        rc = ensure_err(h);
+        if (rc) return rc;
+    }
     a.base = h->base;
     a.stride = (int64_t)h->stride;
     a.a_off = (int64_t)a_off;
@@ -1149,7 +1219,13 @@ int ag_gemm_run(const void* a_shards, void* gathered, const void* b, void* c, ui
         // B^T into a workspace (the matrix cores take both operands k-contiguous)
         const size_t need = (size_t)(K * N * 2);
         uint16_t* bt = nullptr;
-        {
+        if (no_alloc) {
+            if (need > kScratchBtBytes)
+                return fail(RA2A_EINVAL, "B^T of %zu bytes exceeds the %zu-byte scratch of the "
+                                         "allocation-free entry point (pass B transposed)", need,
+                            kScratchBtBytes);
+            bt = reinterpret_cast<uint16_t*>(scr + kScratchErrBytes);
+        } else {
             std::lock_guard<std::mutex> lk(h->mu);
             if (h->bt_bytes < need) {
                 if (h->bt_ws) {
@@ -1175,7 +1251,7 @@ int ag_gemm_run(const void* a_shards, void* gathered, const void* b, void* c, ui
         a.bt = bt;
     }
     a.c = static_cast<uint16_t*>(c);
-    a.err = h->err;
+    a.err = no_alloc ? reinterpret_cast<uint32_t*>(scr) : h->err;
     a.timeout = timeout_ticks(h);
     int ncu = 0;
     rc = device_cus(&ncu);
@@ -1199,7 +1275,15 @@ RA2A_API int ra2a_ag_gemm(const void* a_shards, void* gathered, const void* b, v
                           uint64_t* signals, int W, int rank, int64_t m_local, int64_t K, int64_t N,
                           int tile_rows, int flags, void* stream) {
     return ag_gemm_run(a_shards, gathered, b, c, signals, W, rank, m_local, K, N, tile_rows, flags,
-                       stream);
+                       stream, false);
+}
+
+RA2A_API int ra2a_ag_gemm_noalloc(const void* a_shards, void* gathered, const void* b, void* c,
+                                  uint64_t* signals, int W, int rank, int64_t m_local, int64_t K,
+                                  int64_t N, int tile_rows, int flags, void* stream) {
+    NoAllocScope guard;
+    return ag_gemm_run(a_shards, gathered, b, c, signals, W, rank, m_local, K, N, tile_rows, flags,
+                       stream, true);
 }
 
 // ===========================================================================
@@ -1605,9 +1689,17 @@ RA2A_API int ra2a_check(const ra2a_heap_t* h) {
     if (!h) return fail(RA2A_EINVAL, "heap must be non-NULL");
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-    // the heap's error word, if it exists: read and cleared
+    // the heap's error word, and the current device's scratch error word (used by
+    // the allocation-free entry points), if either exists; both read and cleared
     uint32_t w = 0;
-    uint32_t* words[1] = {h->err};
+    uint32_t* words[2] = {h->err, nullptr};
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+            std::lock_guard<std::mutex> g(g_scratch_mu);
+            words[1] = reinterpret_cast<uint32_t*>(g_scratch[dev]);
+        }
+    }
     for (uint32_t* word : words) {
         if (!word) continue;
         uint32_t x = 0;
