@@ -98,6 +98,28 @@ def combine_dest(inputs: Sequence[np.ndarray], j: int) -> np.ndarray:
     return out
 
 
+def combine_dest_rows(inputs: Sequence[np.ndarray], out_j: np.ndarray, j: int, s0: int,
+                      s1: int) -> None:
+    """Rows [s0, s1) of out_j (a preallocated (S, H*W, D) array), written in place.
+
+    The definition restricted to those rows is itself a combine of the same form:
+    destination 0 of a problem with S' = s1 - s0 whose sources are in_r rows
+    [j*S + s0, j*S + s1), so the same C function computes it from offset pointers
+    (no other arithmetic).  Lets a caller split one combine over threads by (j, s)."""
+    W, S, H, D, dt = _check_inputs(inputs)
+    if not (0 <= s0 <= s1 <= S) or out_j.shape != (S, H * W, D) or out_j.dtype != dt \
+            or not out_j.flags.c_contiguous:
+        raise ValueError("bad row range or output array")
+    if s1 == s0:
+        return
+    e = dt.itemsize
+    sub = (ctypes.c_void_p * W)(*[a.ctypes.data + (j * S + s0) * H * D * e for a in inputs])
+    rc = _load().oracle_combine_dest(sub, out_j.ctypes.data + s0 * H * W * D * e, 0, W, s1 - s0,
+                                     H, D, e)
+    if rc:
+        raise ValueError("oracle_combine_dest rejected its arguments")
+
+
 def combine(inputs: Sequence[np.ndarray]) -> List[np.ndarray]:
     """All W outputs, each of shape (S, H*W, D)."""
     W = len(inputs)

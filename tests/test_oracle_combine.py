@@ -181,3 +181,21 @@ def test_planted_mistakes_are_caught():
                     if not np.array_equal(got, closed_form(j, W, S, H, D)):
                         caught = True
             assert caught, f"planted mistake '{name}' was not caught by the closed-form pin"
+
+
+def test_combine_dest_rows_assembles_the_destination():
+    """Row ranges of a destination computed separately (as a threaded caller would)
+    assemble exactly the whole destination, for ranges of every size, including
+    empty ones."""
+    rng = np.random.default_rng(3)
+    W, S, H, D = 3, 11, 2, 5
+    ins = [rng.integers(0, 2**16, size=(S * W, H, D), dtype=np.uint16) for _ in range(W)]
+    for j in range(W):
+        want = oracle.combine_dest(ins, j)
+        for cuts in ([0, S], [0, 4, 4, 9, S], [0, 1, 2, 3, 5, 8, S]):
+            out = np.zeros((S, H * W, D), dtype=np.uint16)
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                oracle.combine_dest_rows(ins, out, j, a, b)
+            assert out.tobytes() == want.tobytes()
+    with pytest.raises(ValueError):
+        oracle.combine_dest_rows(ins, np.zeros((S, H * W, D), dtype=np.uint16), 0, 5, 3)
