@@ -42,8 +42,9 @@ sys.path.insert(0, ROOT)
 WORKLOAD = "ep_combine_w8_s512_h16_d128_bf16"
 HBM_PEAK_GBS = 8000.0
 NSETS = 6
-KERNEL = "rev_a2a_pipelined_kernel (direct mode)"
+KERNEL = "rev_a2a_pipelined_kernel (direct mode: per-source pieces, write-through stores)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rev_a2a_pipelined_direct_ep_combine_w8.json")
+TRAFFIC_FILE_MOE = os.path.join(ROOT, "profiles", "traffic_rev_a2a_pipelined_direct_moe_combine_w8.json")
 
 
 def log(msg):
@@ -59,50 +60,106 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic():
+def load_traffic(path=TRAFFIC_FILE):
     """HBM bytes per launch of the persistent kernel from the committed rocprofv3
     counter runs, if they were taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         rec = json.load(fh)
     if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, ins, budget_s=12.0):
-    """The CPU oracle as it stands (one thread) on repeated full combines."""
-    import oracle
+def cpu_baseline(wl, ins, run_s=2.5):
+    """The CPU oracle as it stands on the host cores: repeated full combines of the
+    workload, timed on one thread and on every core this process may use (the
+    combine split over (destination, token range) with the oracle's row-range
+    entry; ctypes releases the GIL during each C call), median of 3 runs each;
+    plus the fp64 GEMM oracle (numpy on all cores) on a bounded sample of the
+    AllGather+GEMM workload."""
+    import concurrent.futures as cf
 
-    oracle.combine(ins)  # warm
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.combine(ins)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    gbs = wl.algorithmic_bytes * reps / el / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full combines of the {wl.name} workload "
-                      f"({wl.algorithmic_bytes >> 20} MiB moved each), one thread, {el:.1f} s",
+    import numpy as np
+
+    import oracle
+    from oracle import gemm
+
+    W, S = wl.W, wl.S
+    nthreads = len(os.sched_getaffinity(0))
+    outs = [np.empty((S, wl.H * W, wl.D), dtype=ins[0].dtype) for _ in range(W)]
+    per = max(1, -(-nthreads // W))  # token ranges per destination
+    cuts = [S * k // per for k in range(per + 1)]
+    tasks = [(j, cuts[k], cuts[k + 1]) for j in range(W) for k in range(per)]
+
+    def one_thread():
+        for j in range(W):
+            oracle.combine_dest_rows(ins, outs[j], j, 0, S)
+
+    pool = cf.ThreadPoolExecutor(max_workers=nthreads)
+
+    def all_threads():
+        list(pool.map(lambda t: oracle.combine_dest_rows(ins, outs[t[0]], *t), tasks))
+
+    def rate(fn):
+        t0 = time.perf_counter()
+        fn()
+        one = time.perf_counter() - t0
+        reps = max(1, int(run_s / max(one, 1e-6)))
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+            runs.append(wl.algorithmic_bytes * reps / (time.perf_counter() - t0) / 1e9)
+        return float(np.median(runs)), reps
+
+    v1, r1 = rate(one_thread)
+    vn, rn = rate(all_threads)
+    pool.shutdown()
+    ok = all(outs[j].tobytes() == oracle.combine_dest(ins, j).tobytes() for j in range(W))
+    # the fp64 GEMM oracle on the first 256 rows of every shard of the AllGather+GEMM
+    import synthgen
+    g = synthgen.AG_GEMM
+    shards, b = synthgen.make_ag_gemm_inputs(g, m_local=256)
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        gemm.ag_gemm_ref(shards, b)
+        runs.append(2.0 * g.W * 256 * g.K * g.N / (time.perf_counter() - t0) / 1e9)
+    return {"value": round(vn, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{rn} full combines of the {wl.name} workload per run "
+                      f"({wl.algorithmic_bytes >> 20} MiB moved each), split over {len(tasks)} "
+                      f"(destination, token range) tasks on {nthreads} threads; median of 3 runs",
+            "one_thread": {"value": round(v1, 3), "unit": "GB/s", "cores": 1,
+                           "sample": f"{r1} full combines per run, median of 3 runs"},
+            "parity_with_oracle": ok,
+            "gemm_fp64": {"value": round(float(np.median(runs)), 2), "unit": "GFLOP/s",
+                          "cores": nthreads, "sample": f"{g.name} restricted to 256 rows per shard "
+                          f"({g.W * 256} x {g.K} x {g.N}), numpy float64, median of 3 runs"},
             "host": host_cpu()}
 
 
 def host_cpu():
-    """The host the CPU baseline ran on: CPU model, cores this process may use, cores online."""
-    model = "unknown"
+    """The host the CPU baseline ran on: the CPU model string and its family /
+    model / stepping numbers (/proc/cpuinfo), cores this process may use, cores
+    online."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
+                k, _, v = line.partition(":")
+                k = k.strip()
+                if k in ("model name", "cpu family", "model", "stepping", "cpu MHz") and k not in info:
+                    info[k] = v.strip()
+                if not line.strip() and info:
                     break
     except OSError:
         pass
-    return {"cpu_model": model, "affinity": len(os.sched_getaffinity(0)), "online": os.cpu_count()}
+    return {"cpu_model": info.get("model name", "unknown"),
+            "cpu_family_model_stepping": [info.get("cpu family"), info.get("model"), info.get("stepping")],
+            "affinity": len(os.sched_getaffinity(0)), "online": os.cpu_count()}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -168,7 +225,30 @@ def ag_gemm_leg(steps):
         bt_ms = e0.elapsed_time(e1) / steps
         assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
         ktf = flops / (bt_ms * 1e-3) / 1e12
+        # the unfused library sequence on the same inputs: gather the shards into G
+        # (device copies), then torch.matmul(G, B)
+        shards_t = [heap.view(oa, (m, K), torch.bfloat16, w) for w in range(W)]
+        gbuf = torch.empty(W * m, K, dtype=torch.bfloat16, device="cuda")
+        cl = torch.empty(W * m, N, dtype=torch.bfloat16, device="cuda")
+
+        def lib_seq():
+            for w in range(W):
+                gbuf[w * m:(w + 1) * m].copy_(shards_t[w])
+            torch.matmul(gbuf, b, out=cl)
+
+        for _ in range(3):
+            lib_seq()
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(steps):
+            lib_seq()
+        e1.record(st)
+        torch.cuda.synchronize()
+        lib_ms = e0.elapsed_time(e1) / steps
         return {"workload": g.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                "library_sequence": {"ms": round(lib_ms, 4),
+                                     "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 1),
+                                     "what": "W shard copies into G, then torch.matmul(G, B) (bf16)"},
                 "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "calls": steps,
                 "note": "one call = B transposed into the workspace + signal reset + persistent launch",
                 "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
@@ -325,6 +405,219 @@ def alltoallv_leg(steps):
         heap.close()
 
 
+def put_calibration(heap, src_off, dst_off, nbytes, calls=8):
+    """Counter calibration: the library's put kernel copying a known `nbytes`
+    (slice 0 -> slice 0), so that a counter pass over the same process reads
+    what FETCH_SIZE / WRITE_SIZE report for exactly nbytes read and written."""
+    import torch
+
+    import moe_all2all_combine_amd as ra2a
+
+    for _ in range(calls):
+        ra2a.put(heap.handle, heap.ptr(dst_off), heap.ptr(src_off), nbytes, 0,
+                 torch.cuda.current_stream())
+    torch.cuda.synchronize()
+
+
+def device_inputs(heap, off, wl, bits):
+    """The workload's inputs generated on the device from its seed: the same
+    distribution as synthgen's recipe (uniform(-1, 1) or normal(0, std), then
+    rounded to the element type), from torch's device generator, so that the
+    multi-GiB workloads need no host generation."""
+    import torch
+
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[wl.dtype]
+    for r in range(wl.W):
+        v = heap.view(off, (wl.S * wl.W, wl.H, wl.D), dt, r)
+        if wl.dist == "normal":
+            v.copy_(torch.randn(v.shape, generator=gen, device="cuda") * wl.std)
+        else:
+            v.copy_(torch.rand(v.shape, generator=gen, device="cuda") * 2 - 1)
+
+
+def combine_views_match(heap, oi, oo, wl, bits):
+    """The definition out_j[s, r*H + h, d] = in_r[j*S + s, h, d], checked on the
+    device as bits with torch views."""
+    import torch
+
+    W, S, H, D = wl.W, wl.S, wl.H, wl.D
+    return all(torch.equal(heap.view(oo, (S, W, H, D), bits, j)[:, r],
+                           heap.view(oi, (W, S, H, D), bits, r)[j])
+               for j in range(W) for r in range(W))
+
+
+def moe_leg(steps, profile=False):
+    """The MoE-combine-shaped workload (W=8, S=4096, H=1, D=7168 bf16, 32-token
+    tiles, ADD): one step = one combine with the library defaults (in-launch
+    reset, one launch), on one buffer set (7.5 GB, far beyond the 256 MB MALL).
+    Its own roofline: algorithmic bytes / the launch's average duration (HIP
+    events on the launch stream around the timed steps).  Row units and whole-
+    tile pieces for context."""
+    import torch
+
+    import moe_all2all_combine_amd as ra2a
+    import synthgen
+
+    wl = synthgen.WORKLOADS["moe_combine_w8_s4096_h1_d7168_bf16"]
+    W, S, H, D = wl.W, wl.S, wl.H, wl.D
+    tiles = dict(tile_s=wl.tile_s, tile_h=wl.tile_h, tile_d=wl.tile_d, protocol=ra2a.PROTO_ADD)
+    variants = {"default": ra2a.Opts(**tiles), "rows": ra2a.Opts(mode=ra2a.MODE_ROWS, **tiles),
+                "whole_tile_pieces": ra2a.Opts(piece_rows=wl.tile_s, **tiles)}
+    if profile:  # counter runs: the default variant only, and a calibration copy
+        variants = {"default": variants["default"]}
+    nsig = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o)) for o in variants.values())
+    nb = wl.bytes_per_rank
+    heap = ra2a.SymmHeap(W, 2 * nb + nsig * 128 + (4 << 20))
+    try:
+        oi, oo, osg = heap.alloc(nb), heap.alloc(nb), heap.alloc(nsig * 128)
+        bits = torch.int16
+        device_inputs(heap, oi, wl, bits)
+        st = torch.cuda.current_stream()
+        if profile:
+            put_calibration(heap, oi, oo, 16 << 20)
+        res = {}
+        for name, o in variants.items():
+            def call():
+                ra2a.rev_all2all_ex(heap.ptr(oi), heap.ptr(oo), heap.ptr(osg), W, S, H, D, wl.dtype, o,
+                                    st)
+            for _ in range(2):
+                call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for _ in range(steps):
+                call()
+            e1.record(st)
+            torch.cuda.synchronize()
+            assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
+            ms = e0.elapsed_time(e1) / steps
+            # parity of this variant: output poisoned, one more call, the definition
+            for j in range(W):
+                heap.view(oo, (nb,), torch.uint8, j).fill_(0xA5)
+            call()
+            torch.cuda.synchronize()
+            ok = ra2a.check(heap.handle) == ra2a.OK and combine_views_match(heap, oi, oo, wl, bits)
+            res[name] = (ms, ok)
+        alg = wl.algorithmic_bytes
+        ms, ok = res["default"]
+        gbs = alg / (ms * 1e-3) / 1e9
+        pl = ra2a.rev_all2all_plan(W, S, H, D, wl.dtype, variants["default"])
+        out = {"workload": wl.name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+               "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "parity": ok, "steps": steps,
+               "algorithmic_bytes": alg,
+               "plan": {"piece_rows": pl.piece_rows, "pieces_per_tile": pl.pieces_per_tile,
+                        "pieces": pl.work_items},
+               "note": "one step = one launch (in-launch reset + combine), inputs generated on the "
+                       "device from seed 1 (normal(0, 1) in bf16)",
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "traffic": load_traffic(TRAFFIC_FILE_MOE),
+                            "kernel": KERNEL, "kernel_ms": round(ms, 5)}}
+        for name in [n for n in ("rows", "whole_tile_pieces") if n in res]:
+            m2, ok2 = res[name]
+            g2 = alg / (m2 * 1e-3) / 1e9
+            out[name] = {"ms": round(m2, 4), "GB/s": round(g2, 1),
+                         "pct_hbm_peak": round(100 * g2 / HBM_PEAK_GBS, 2), "parity": ok2}
+        return out
+    finally:
+        heap.close()
+
+
+def straggler_leg():
+    """The straggler workload (W=16, S=2048, H=32, D=128 fp32, 64 x 1 x 128 tiles,
+    SET per (tile, source)): before each of its pieces, the source slice drawn
+    from seed 2 waits n0 + u ticks of the 100 MHz device clock (u uniform in
+    [0, n0], SplitMix64 from seed 2).  n0 is calibrated once, here, from the
+    undelayed launch: a piece then holds its workgroup for t_piece = launch time
+    x workgroups / pieces on average, and n0 = t_piece / 1.5 makes the mean wait
+    (1.5 n0) equal to t_piece, so a delayed slice's pieces take about twice an
+    unperturbed slice's.  Then, in direct and staged mode: the launch time with
+    and without the delay, and the per-tile completion times (device clock stamps,
+    microseconds from the launch's first stamp) of the delayed source against the
+    others -- a consumer waits tile by tile, only for its own tile's source."""
+    import numpy as np
+    import torch
+
+    import moe_all2all_combine_amd as ra2a
+    import synthgen
+
+    wl = synthgen.WORKLOADS["straggler_w16_s2048_h32_d128_f32"]
+    W, S, H, D = wl.W, wl.S, wl.H, wl.D
+    lag = synthgen.straggler_rank(wl)
+    base = dict(tile_s=wl.tile_s, tile_h=wl.tile_h, tile_d=wl.tile_d, protocol=ra2a.PROTO_SET)
+    o_st = ra2a.Opts(mode=ra2a.MODE_STAGED, consumer_split=1, **base)
+    nt = ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, ra2a.Opts(**base))[0]
+    nsig = max(sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
+               for o in (ra2a.Opts(**base), o_st))
+    ring = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, o_st)
+    nb = wl.bytes_per_rank
+    heap = ra2a.SymmHeap(W, 2 * nb + ring + nsig * 128 + (4 << 20))
+    try:
+        oi, oo, osg = heap.alloc(nb), heap.alloc(nb), heap.alloc(nsig * 128)
+        device_inputs(heap, oi, wl, torch.int32)
+        stamps = torch.zeros(W * nt, dtype=torch.int64, device="cuda")
+        st = torch.cuda.current_stream()
+
+        def opts(n0, mode):
+            return ra2a.Opts(mode=mode, consumer_split=1, straggler_rank=lag if n0 else -1,
+                             straggler_delay=n0, straggler_seed=wl.seed,
+                             timestamps=stamps.data_ptr(), **base)
+
+        def run(n0, mode=0, reps=3):
+            o = opts(n0, mode)
+            call = lambda: ra2a.rev_all2all_ex(heap.ptr(oi), heap.ptr(oo), heap.ptr(osg), W, S, H,
+                                               D, wl.dtype, o, st)
+            call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for _ in range(reps):
+                call()
+            e1.record(st)
+            torch.cuda.synchronize()
+            assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
+            t = stamps.cpu().numpy().view(np.uint64).reshape(W, nt // W, W).astype(np.float64)
+            t = (t - t.min()) / 100.0  # the 100 MHz device clock -> microseconds
+            return e0.elapsed_time(e1) / reps, t[:, :, lag], np.delete(t, lag, axis=2)
+
+        # calibration from the undelayed default launch
+        plan = ra2a.rev_all2all_plan(W, S, H, D, wl.dtype, opts(0, 0))
+        props = torch.cuda.get_device_properties(0)
+        ms0, _, _ = run(0)
+        wg = min(plan.work_items, props.multi_processor_count)  # one workgroup per CU (dynamic)
+        t_piece_us = ms0 * 1e3 * wg / plan.work_items
+        n0 = max(1, int(round(t_piece_us * 100 / 1.5)))
+
+        def q(a):
+            return {"p50": round(float(np.percentile(a, 50)), 1),
+                    "p90": round(float(np.percentile(a, 90)), 1), "max": round(float(a.max()), 1)}
+
+        out = {"workload": wl.name, "straggler_rank": lag, "n0": n0,
+               "calibration": {"undelayed_ms": round(ms0, 4), "pieces": plan.work_items,
+                               "workgroups": wg, "t_piece_us": round(t_piece_us, 3),
+                               "rule": "n0 = t_piece / 1.5 ticks of 10 ns: a delayed piece waits "
+                                       "t_piece on average, taking about twice a clean one"},
+               "note": "per-tile completion stamps (device clock), microseconds from the launch's "
+                       "first stamp; SET per (tile, source): each source's tiles separately"}
+        for name, mode in (("direct", 0), ("staged", ra2a.MODE_STAGED)):
+            msu, lag_u, oth_u = run(0, mode)
+            ms, lagged, others = run(n0, mode)
+            out[name] = {
+                "ms_delayed": round(ms, 4), "ms_undelayed": round(msu, 4),
+                "delayed_source_us": q(lagged), "other_sources_us": q(others),
+                "undelayed": {"that_source_us": q(lag_u), "other_sources_us": q(oth_u)},
+                "median_lag_us": round(float(np.median(lagged) - np.median(others)), 1),
+                # behind a barrier every tile would complete after the last piece of
+                # every source; with per-tile signals this share of the other
+                # sources' tiles is complete before the delayed source's last tile
+                "other_tiles_done_before_delayed_last": round(float((others < lagged.max()).mean()), 4)}
+        out["parity"] = combine_views_match(heap, oi, oo, wl, torch.int32)
+        return out
+    finally:
+        heap.close()
+
+
 def copy_ceiling(nbytes, steps):
     """The practical ceiling for copy-shaped traffic: torch's device copy of one
     contiguous buffer of `nbytes` into another, over NSETS rotated pairs so that,
@@ -356,7 +649,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--legs", choices=["all", "main", "ag_gemm", "gemm_rs", "alltoallv"], default="all")
+    ap.add_argument("--legs", choices=["all", "main", "moe", "straggler", "ag_gemm", "gemm_rs",
+                                       "alltoallv"], default="all")
     ap.add_argument("--workload", default=WORKLOAD)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -381,6 +675,14 @@ def main():
     if args.legs == "alltoallv":  # only the variable-size AllToAll leg (for counter runs)
         torch.cuda.set_device(0)
         print(json.dumps({"alltoallv": alltoallv_leg(args.steps)}), flush=True)
+        return
+    if args.legs == "moe":  # only the MoE-combine-shaped leg's default (for counter runs)
+        torch.cuda.set_device(0)
+        print(json.dumps({"moe_combine": moe_leg(args.steps, profile=True)}), flush=True)
+        return
+    if args.legs == "straggler":
+        torch.cuda.set_device(0)
+        print(json.dumps({"straggler": straggler_leg()}), flush=True)
         return
 
     wl = synthgen.WORKLOADS[args.workload]
@@ -464,6 +766,8 @@ def main():
         assert ra2a.check(hs) == ra2a.OK, ra2a.last_error()
         return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
+    if args.legs == "main":  # counter runs: a copy of known size in the same process
+        put_calibration(heap, sets[0][0], sets[0][1], nb)
     # No timing events between launches (a timestamped event between two kernels
     # costs microseconds per step on this stack).  An in-launch step is exactly
     # one launch of the persistent kernel, so the events around its timed region
@@ -494,7 +798,19 @@ def main():
                                   == W).all()) for j in range(W))
         return ok
 
-    ok = parity(args.steps - 1)
+    def poison(k):
+        """Outputs and signal array of buffer set k filled with garbage."""
+        _, oo, osg = sets[k % NSETS]
+        for j in range(W):
+            heap.view(oo, (nb,), torch.uint8, j).fill_(0xA5)
+            heap.view(osg, (nsig * 128,), torch.uint8, j).fill_(0x5A)
+        torch.cuda.synchronize()
+
+    # parity of the headline variant itself: set 0 poisoned, one more in-launch step
+    poison(0)
+    step(0, opts_lib, overlap=False, reset=False)
+    torch.cuda.synchronize()
+    ok = ra2a.check(hs) == ra2a.OK and parity(0)
     log(f"[bench] combine {ms_per_step * 1e3:.1f} us/step, kernel {kern_ms * 1e3:.1f} us, "
         f"parity {ok}")
     alg = wl.algorithmic_bytes
@@ -517,7 +833,7 @@ def main():
         "parity": ok,
         "config": {"workload": wl.name, "W": W, "S": S, "H": H, "D": D, "dtype": wl.dtype,
                    "tile": [wl.tile_s, wl.tile_h, wl.tile_d], "protocol": wl.protocol,
-                   "variant": "signal-pipelined persistent kernel, direct mode",
+                   "variant": "signal-pipelined persistent kernel, direct mode (per-source pieces)",
                    "step": "signal reset + combine", "steps_issued": mode_used,
                    "buffer_sets": NSETS,
                    "algorithmic_bytes": alg},
@@ -540,18 +856,27 @@ def main():
                            f"the MALL by the previous step; the headline rotates {NSETS} sets (cold)"}
     if args.legs == "all":
         st_ms, _ = timed(opts_st, args.steps, args.warmup, overlap=False)  # reset launch + combine
-        st_ok = parity(args.steps - 1)
+        poison(0)
+        step(0, opts_st, overlap=False)
+        torch.cuda.synchronize()
+        st_ok = ra2a.check(hs) == ra2a.OK and parity(0)
         rec["staged"] = {"ms_per_step": round(st_ms, 5),
                          "value": round(alg / (st_ms * 1e-3) / 1e9, 2), "parity": st_ok}
         bk_ms, _ = timed(opts_bk, args.steps, args.warmup, overlap=False)  # reset launch + combine
+        poison(0)
+        step(0, opts_bk, overlap=False)
+        torch.cuda.synchronize()
         rec["bulk"] = {"ms_per_step": round(bk_ms, 5),
                        "value": round(alg / (bk_ms * 1e-3) / 1e9, 2),
-                       "parity": parity(args.steps - 1, check_signals=False),
+                       "parity": ra2a.check(hs) == ra2a.OK and parity(0, check_signals=False),
                        "note": "two-phase layout with per-(S-block, sender) signals"}
         pl_ms, _ = timed(opts_pl, args.steps, args.warmup, overlap=False)  # reset launch + combine
+        poison(0)
+        step(0, opts_pl, overlap=False)
+        torch.cuda.synchronize()
         rec["pull"] = {"ms_per_step": round(pl_ms, 5),
                        "value": round(alg / (pl_ms * 1e-3) / 1e9, 2),
-                       "parity": parity(args.steps - 1, check_signals=False),
+                       "parity": ra2a.check(hs) == ra2a.OK and parity(0, check_signals=False),
                        "note": "pull mode: senders stage in their own slice, receivers pull"}
 
         # forward All2All (dispatch, the combine's inverse) on the same buffers
@@ -609,6 +934,11 @@ def main():
         rec["copy_ceiling"] = copy_ceiling(W * nb, args.steps)
     heap.close()
     if args.legs == "all":
+        log("[bench] MoE-combine-shaped leg")
+        rec["moe_combine"] = moe_leg(10)
+        log("[bench] straggler leg")
+        rec["straggler"] = straggler_leg()
+        log("[bench] GEMM legs")
         rec["ag_gemm"] = ag_gemm_leg(args.steps // 5 + 3)
         rec["gemm_rs"] = gemm_rs_leg(args.steps // 5 + 3)
         rec["alltoallv"] = alltoallv_leg(args.steps // 5 + 3)

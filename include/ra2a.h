@@ -235,8 +235,10 @@ typedef struct ra2a_opts {
                          * every piece first when no slot is reused; -1: every piece
                          * first); always capped so that no wait points forward */
     int32_t straggler_rank;   /* source slice whose producers are delayed, -1 = none */
-    uint32_t straggler_delay; /* busy-loop base n0: each delayed piece spins n0 + u
-                               * iterations, u uniform in [0, n0] from SplitMix64 */
+    uint32_t straggler_delay; /* busy-wait base n0: before each of its pieces the
+                               * delayed source waits n0 + u ticks of the 100 MHz
+                               * device clock, u uniform in [0, n0] from SplitMix64
+                               * (Steele, Lea and Flood 2014) indexed by the piece */
     uint64_t straggler_seed;  /* seed of that SplitMix64 sequence */
     uint64_t *timestamps;     /* optional device array, zeroed by the caller: for each
                                * destination slice j and data-signal slot u, the device

@@ -310,11 +310,14 @@ __device__ __forceinline__ bool piece_wait(const PipeArgs& a, const Piece& p, in
                            p.credit_need, a.timeout, a.err, lds_flag))
         return false;
     if (p.r == a.straggler && a.delay) {
+        // a busy wait of n0 + u ticks of the 100 MHz device clock, u uniform in
+        // [0, n0] from SplitMix64 indexed by the piece
         if (threadIdx.x == 0) {
             const uint64_t id =
                 ((((uint64_t)p.b * (uint64_t)a.nstreams + p.sid) * (uint64_t)a.nsub + p.sub) * a.W) + p.r;
             const uint64_t n = a.delay + splitmix64(a.seed, id) % ((uint64_t)a.delay + 1ull);
-            for (uint64_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
+            const uint64_t t0 = rtc_now();
+            while (rtc_now() - t0 < n) __builtin_amdgcn_s_sleep(1);
         }
         __syncthreads();
     }

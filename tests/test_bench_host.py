@@ -35,6 +35,19 @@ def test_host_cpu_description():
     import bench
 
     h = bench.host_cpu()
-    assert set(h) == {"cpu_model", "affinity", "online"}
+    assert set(h) == {"cpu_model", "cpu_family_model_stepping", "affinity", "online"}
     assert 1 <= h["affinity"] <= h["online"]
     assert isinstance(h["cpu_model"], str) and h["cpu_model"]
+
+
+def test_cpu_baseline_on_a_tiny_workload():
+    """The CPU baseline's threaded oracle split reproduces the oracle and reports
+    one-thread and all-core rates with the host description."""
+    import bench
+    import synthgen
+
+    wl = synthgen.small_workload(4, 64, 2, 64, "bf16", seed=1, tile=(16, 1, 64))
+    rec = bench.cpu_baseline(wl, synthgen.make_inputs(wl), run_s=0.05)
+    assert rec["parity_with_oracle"] is True
+    assert rec["kind"] == "oracle" and rec["value"] > 0 and rec["one_thread"]["value"] > 0
+    assert rec["cores"] == rec["host"]["affinity"] and rec["gemm_fp64"]["value"] > 0
