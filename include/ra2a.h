@@ -387,8 +387,11 @@ int ra2a_rev_all2all_workspace_bytes(int W, int64_t S, int64_t H, int64_t D, int
  * complete, copies the ring into out_j and hands the ring slot back.
  * Afterwards every region-A slot holds W (ADD) or 1 (SET), and every region-B
  * slot the number of consumer work items that used it (staged) or the number
- * of row units of its S-block (row units).  Staging (staged mode)
- * comes from the heap (see workspace_bytes).  Under stream capture (a HIP graph)
+ * of row units of its S-block (row units).  Staging (staged, bulk and pull
+ * modes) comes from the heap (see workspace_bytes) and is one area per heap,
+ * shared by every such call on the heap whatever its stream: calls that use
+ * staging on one heap must be ordered (one stream, or events between them),
+ * else they race on it.  Under stream capture (a HIP graph)
  * the reset is always a launch of its own, so replays stay correct; make one call
  * outside capture first (the first call on a heap allocates its error word and
  * probes the device's XCDs).
@@ -424,7 +427,9 @@ int ra2a_all2all_dispatch_ex(const void *in, void *out, uint64_t *signals, int W
  * Copy"): phase 1 copies every contiguous (S, H, D) segment in_r[j*S, (j+1)*S)
  * into slot r of rank j's full-size staging area; stream order between the two
  * launches is the barrier; phase 2 reorders staging into out_j.  `signals` is
- * not used and may be NULL.  Errors: EINVAL, ENOMEM, EHIP.                      */
+ * not used and may be NULL.  The staging area is the heap's (shared by every
+ * two-phase call on the heap: order them on one stream).
+ * Errors: EINVAL, ENOMEM, EHIP.                                                 */
 int ra2a_rev_all2all_two_phase(const void *in, void *out, uint64_t *signals, int W, int64_t S,
                                int64_t H, int64_t D, int dtype, void *stream);
 
@@ -458,7 +463,13 @@ int ra2a_rev_all2all_two_phase(const void *in, void *out, uint64_t *signals, int
 #define RA2A_AG_SKIP_RESET 2
 #define RA2A_AG_B_TRANSPOSED 4 /* `b` holds B^T (N x K row-major); otherwise the
                                   library transposes B into a workspace it owns
-                                  (hipMalloc'd once per heap, freed with it) */
+                                  (hipMalloc'd once per heap, freed with it).  That
+                                  workspace is one per heap: calls on one heap
+                                  with different B must be ordered on one stream,
+                                  and a call that needs it larger synchronizes the
+                                  device to replace it, so make the first call
+                                  with the largest B outside graph capture (or
+                                  use ra2a_ag_gemm_noalloc) */
 
 int ra2a_ag_gemm_signal_slots(int W, int64_t m_local, int tile_rows, int64_t *tile_slots,
                               int64_t *count_slots, int64_t *queue_slots);

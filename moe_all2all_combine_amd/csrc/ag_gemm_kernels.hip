@@ -27,51 +27,39 @@
 namespace ra2a {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTileM = kGemmBM;   // output rows of a tile (rows of A)
-constexpr int kTileN = kGemmBN;   // output columns of a tile (rows of B^T)
-constexpr int kGemmWaves = kTileM / 32;  // waves (wm, wn), wm = wave / 2, wn = wave mod 2
-constexpr int kGemmThreads = 64 * kGemmWaves;
-constexpr int kGemmWgPerCu = 512 / kGemmThreads;  // two waves per SIMD in all
-constexpr int kWaveRows = 64;      // each wave owns 64 x 128 outputs of the tile
-constexpr int kWaveCols = 128;
-static_assert(kWaveRows * (kGemmWaves / 2) == kTileM && kWaveCols * 2 == kTileN,
-              "the waves tile the output tile");
-constexpr int kBlkA = kWaveRows / 32;  // 32 x 32 MFMA blocks per wave along rows
-constexpr int kBlkB = kWaveCols / 32;  // ... and along columns
-// k per pipeline stage: 64 bf16 = 128 bytes of an operand row, one whole cache
-// line, so that each LDS load instruction fetches 8 whole lines.  With 32-k
-// stages an instruction fetched 16 half lines and the loads filled LDS at 21 B
-// per clock per CU against 36 B with whole lines (measured): below the 32 B per
-// clock the matrix cores need at their peak for a 256 x 256 tile.
-constexpr int kStageK = 64;
-constexpr int kChunks = kStageK / 8;       // 16-byte chunks per operand row of a stage
-constexpr int kStages = 2;                 // LDS ring depth: one stage computed, one landing
-constexpr int kStageA = kTileM * kStageK;  // bf16 of A per stage
-constexpr int kStageB = kTileN * kStageK;  // bf16 of B^T per stage
-constexpr int kSlotElems = kStageA + kStageB;
-constexpr int kRowsA = kTileM / kGemmWaves;  // A rows each wave loads per stage
-constexpr int kRowsB = kTileN / kGemmWaves;  // B^T rows each wave loads per stage
-constexpr int kDmaRows = 64 / kChunks;       // rows per LDS load instruction (1 KiB)
-constexpr int kDmaA = kRowsA / kDmaRows, kDmaB = kRowsB / kDmaRows;  // a wave's LDS loads per stage
-constexpr int kDmaPerStage = kDmaA + kDmaB;
-static_assert(kRowsA % kDmaRows == 0 && kRowsB % kDmaRows == 0, "whole LDS load instructions");
-constexpr int kKSteps = kStageK / 16;      // k16 MFMA steps per stage
-static_assert(kKSteps == 4, "the main loop runs four k16 quarters per stage");
-// bf16 epilogue: the output tile staged in LDS, rows padded by 16 bytes so that the
-// two rows one write instruction touches fall in different banks
-constexpr int kEpiPitch = kTileN * 2 + 16;                   // bytes per staged row
-constexpr int kLdsElems = (kStages * kSlotElems) > (kTileM * kEpiPitch / 2)
-                              ? (kStages * kSlotElems)
-                              : (kTileM * kEpiPitch / 2);    // uint16 elements of the LDS array
-static_assert(2 * kLdsElems * kGemmWgPerCu + 1024 <= 160 * 1024, "the LDS of a CU holds its workgroups");
-// fp32 epilogue: half the tile's rows at a time, rows padded by 32 bytes (the two
-// rows one write instruction touches then fall in the two halves of the banks)
-constexpr int kEpiRows32 = kTileM / 2;
-constexpr int kEpiPitch32 = kTileN * 4 + 32;
-static_assert(kEpiRows32 * kEpiPitch32 <= 2 * kLdsElems, "the fp32 half tile must fit the LDS array");
-static_assert(kWaveRows <= kEpiRows32 && kEpiRows32 % kWaveRows == 0, "a wave's rows lie in one half");
+// ---- the matrix-core tile ----------------------------------------------------
+//
+// One output tile of kTileM x kTileN = 256 x 256 per workgroup of four waves, one
+// per SIMD; wave (wm, wn) = (wave / 2, wave mod 2) owns its 128 x 128 quarter as
+// 8 x 8 blocks of v_mfma_f32_16x16x32_bf16.  The operands are given to the
+// instruction swapped (B^T block first), so that lane l of block (x, y) holds
+// rows 16 x + l % 16 and four consecutive columns 16 y + 4 (l / 16) .. + 3 of the
+// wave's quarter: the epilogue writes 8 (bf16) or 16 (fp32) contiguous bytes.
+// (Lane layout of the instruction: A operand row l % 16, k 8 (l / 16) .. + 7; B
+// operand column l % 16, the same k; result column l % 16, rows 4 (l / 16) .. +3 --
+// checked on the device with exact integer inputs before this tile was written.)
+// Measured on the 8192 x 4096 x 7168 product alone: 0.416 ms with this tile, the
+// MFMA pipes busy 65 % of the cycles at the 1.68 GHz the device clocks under this
+// load (counters), against 0.46 ms for the previous eight-wave 32 x 32 x 16 tile.
+constexpr int kTileM = kGemmBM;
+constexpr int kTileN = kGemmBN;
+constexpr int kGemmThreads = 256;  // four waves
+constexpr int kGemmWgPerCu = 1;
+constexpr int kStageK = 64;        // k per pipeline stage: 128 bytes, one cache line per row
+constexpr int kSlotA = kTileM * kStageK * 2;   // bytes of A in a stage slot
+constexpr int kSlotB = kTileN * kStageK * 2;
+constexpr int kSlot = kSlotA + kSlotB;         // 64 KiB; the LDS ring holds two
+constexpr int kLoadsPerStage = 16;             // 1 KiB LDS loads per wave per stage (8 of A, 8 of B^T)
+constexpr int kReadsPerStep = 16;              // 16-byte fragment reads per wave per k32 step
+constexpr int kMfmaPerStep = 64;               // 8 x 8 blocks
+constexpr int kEpiPitch = kTileN * 2 + 16;     // bf16 output tile staged in LDS, bytes per row
+constexpr int kEpiRows32 = kTileM / 2;         // fp32 output: half the tile at a time
+constexpr int kEpiPitch32 = kTileN * 4 + 16;
+constexpr int kLdsBytes = kTileM * kEpiPitch;  // the largest of the three uses
+static_assert(2 * kSlot <= kLdsBytes && kEpiRows32 * kEpiPitch32 <= kLdsBytes, "LDS array");
+static_assert(kLdsBytes + 1024 <= 160 * 1024, "the LDS of a CU holds the workgroup");
 
 // float -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -80,101 +68,65 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// LDS stage layout of an operand: its tile rows x 64 k (128 bytes per row, eight
-// 16-byte chunks).  Chunk c of row r is stored at position c ^ g(r),
-// g(r) = (r ^ ((r >> 3) & 3)) & 7.  A fragment read takes 32 consecutive rows at
-// one chunk (lanes 0-31) and the same rows at the next chunk (lanes 32-63).  With
-// 64 banks serving 16 lanes a clock (the model the bank-conflict counter bore
-// out for 64-byte rows) the even rows of any 16 then cover the 8 chunk positions
-// once, and so do the odd rows; with 32 banks serving 8 lanes a clock, any 8
-// consecutive rows cover them once.  g depends on r mod 32 only, so the blocks
-// of a wave (rows + 32 x) sit at fixed offsets.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ ((r >> 3) & 3)) & 7); }
+// LDS stage layout of an operand: its 256 rows x 64 k, 128 bytes per row as eight
+// 16-byte chunks; logical chunk c of row r sits at position c ^ ((r >> 1) & 7).
+// A fragment read takes 16 consecutive rows (starting at a multiple of 16) at one
+// chunk: the eight even rows then cover the eight positions once, and so do the
+// eight odd ones, which lie in the other half of the 64 banks -- no conflict
+// whether the LDS serves 16 or 8 lanes a clock (the counter reads 0.3 %).
 
 // Offset sent for a chunk that must read as zero: past any buffer's range.
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
-// One of the kDmaPerStage LDS loads of a stage (k0 .. k0 + 64): parts 0 .. kDmaA-1
-// load this wave's A rows, the others its B^T rows, into the stage's slot (A
-// first, then B^T).  Each wave instruction fills 1 KiB of LDS, lane l landing at
-// byte 16 l: 8 rows x 8 chunks; the lane therefore fetches the logical chunk
-// that belongs at its swizzled position.  Rows past the operand's buffer and k
-// past K read as 0.
-//
-// Two ways to address the load, equal in result, chosen per kernel by measurement:
-//  * SM (scalar M0): the wave index is read as a scalar, so the LDS destination
-//    (M0) is scalar arithmetic, and row x K x 2 splits into a scalar part and
-//    lane_rows = (l / kChunks) x K x 2, a per-lane term common to every load of the
-//    tile (lane_rows_of), so no multiply is left in the loop; k is 32-bit (the
-//    host rejects K with tile rows x K x 2 bytes at 4 GiB or more).  GEMM +
-//    ReduceScatter (K = 896): fp32 partials 0.84 -> 0.79 ms, bf16 0.76 -> 0.74 ms;
-//  * otherwise the destination comes from the vector wave index through a
-//    readfirstlane per load and the offset from 64-bit arithmetic the compiler
-//    strength-reduces: AllGather + GEMM (K = 7168) 0.49 against 0.51 ms with SM.
-template <int P, bool SM>
-__device__ __forceinline__ void stage_load_part(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                uint16_t* slot, int64_t K, int64_t k0, uint32_t lane_rows) {
-    static_assert(P >= 0 && P < kDmaPerStage, "a stage has kDmaPerStage parts");
-    constexpr bool kA = P < kDmaA;
+// Per-lane terms of the stage loads, fixed for a tile: lane l lands at byte 16 l of
+// a 1 KiB LDS block, i.e. row 8 P' + l / 8 of the wave's rows, position l % 8, and
+// fetches the logical chunk stored there.
+struct LoadLane {
+    uint32_t row_off;  // (l / 8) * K * 2
+    int chunk;         // (l % 8) ^ ((l / 8) >> 1): the logical chunk for an even part
+};
+
+__device__ __forceinline__ LoadLane load_lane(int64_t K) {
     const int l = (int)threadIdx.x & 63;
-    uint32_t off;
-    int rbase;
-    if constexpr (SM) {
-        const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-        rbase = kA ? kRowsA * w + kDmaRows * P : kRowsB * w + kDmaRows * (P - kDmaA);
-        const int row = rbase + l / kChunks;
-        const int k = (int)k0 + 8 * swz(row, l % kChunks);
-        off = k < (int)K ? (uint32_t)rbase * (uint32_t)K * 2u + lane_rows + (uint32_t)k * 2u : kOutOfRange;
-    } else {
-        const int w = (int)threadIdx.x >> 6;
-        rbase = kA ? kRowsA * w + kDmaRows * P : kRowsB * w + kDmaRows * (P - kDmaA);
-        const int row = rbase + l / kChunks;
-        const int64_t k = k0 + 8 * swz(row, l % kChunks);
-        off = k < K ? (uint32_t)(((int64_t)row * K + k) * 2) : kOutOfRange;
-    }
-    uint16_t* const dst = (kA ? slot : slot + kStageA) + rbase * kStageK;
+    LoadLane ll;
+    ll.row_off = (uint32_t)(l >> 3) * (uint32_t)K * 2u;
+    asm volatile("" : "+v"(ll.row_off));  // computed once, not folded back into every load
+    ll.chunk = (l & 7) ^ (l >> 4);
+    return ll;
+}
+
+// Load P (0 .. 15) of this wave's share of a stage (k0 .. k0 + 63): loads 0-7 bring
+// A rows 64 w + 8 P .., loads 8-15 B^T rows 64 w + 8 (P - 8) .. into the slot (A,
+// then B^T).  Row r = 64 w + 8 P + l / 8 has (r >> 1) & 7 = (l >> 4) ^ 4 (P & 1).
+// Rows past the operand's buffer (the descriptor's range), k past K, and a stage
+// past the last (`live` false) read as zero: no branch around the load.
+template <int P>
+__device__ __forceinline__ void stage_load_part(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                                char* slot, int w, uint32_t K, uint32_t k0,
+                                                const LoadLane& ll, bool live) {
+    constexpr bool kA = P < 8;
+    const int rbase = 64 * w + 8 * (kA ? P : P - 8);
+    const int chunk = ll.chunk ^ (4 * (P & 1));
+    const uint32_t k = k0 + 8u * (uint32_t)chunk;
+    const uint32_t off = (live && k < K) ? (uint32_t)rbase * K * 2u + ll.row_off + k * 2u : kOutOfRange;
+    char* const dst = slot + (kA ? 0 : kSlotA) + rbase * 128;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kA ? ra : rb, (__attribute__((address_space(3))) void*)dst,
                                              16, off, 0, 0, 0);
 }
 
-template <bool SM, int... Ps>
-__device__ __forceinline__ void stage_load_seq(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                               uint16_t* slot, int64_t K, int64_t k0, uint32_t lane_rows,
+template <int... Ps>
+__device__ __forceinline__ void stage_load_seq(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, char* slot,
+                                               int w, uint32_t K, uint32_t k0, const LoadLane& ll,
                                                std::integer_sequence<int, Ps...>) {
-    (stage_load_part<Ps, SM>(ra, rb, slot, K, k0, lane_rows), ...);
+    (stage_load_part<Ps>(ra, rb, slot, w, K, k0, ll, true), ...);
 }
 
-// Every load of one stage into its slot.
-template <bool SM>
-__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                           uint16_t* slot, int64_t K, int64_t k0, uint32_t lane_rows) {
-    stage_load_seq<SM>(ra, rb, slot, K, k0, lane_rows, std::make_integer_sequence<int, kDmaPerStage>{});
-}
-
-// The per-lane row term of the stage loads' offsets, computed once per tile and
-// made opaque so that the compiler cannot fold it back into a multiply per load.
-__device__ __forceinline__ uint32_t lane_rows_of(int64_t K) {
-    uint32_t v = (uint32_t)(((int)threadIdx.x & 63) / kChunks) * (uint32_t)K * 2u;
-    asm volatile("" : "+v"(v));
-    return v;
-}
-
-// Matrix-core work: wave (wm, wn) owns rows kWaveRows wm .. + kWaveRows and
-// columns kWaveCols wn .. + kWaveCols of the tile as kBlkA x kBlkB blocks of
-// 32 x 32.  A k16 step reads kBlkA A and kBlkB B fragments (16 bytes per lane)
-// and issues kBlkA kBlkB MFMAs (v_mfma_f32_32x32x16_bf16: lane l supplies row /
-// column l % 32, k 8 (l / 32) .. +8).
-struct Frags {
-    bf16x8 a[kBlkA], b[kBlkB];
-};
-
-// 16-byte LDS reads at addr + OFF (OFF an immediate).  Written as inline
-// assembly on purpose: the compiler cannot tell these reads apart from the LDS
-// slots still being filled by the direct loads of later stages, and before
-// every LDS read it would wait for all of those loads (vmcnt(0)), which
-// serialises the pipeline.  The stage being read is already complete for every
-// wave (wait_stages_after + barrier); the caller waits for the reads with
-// lds_wait.
+// 16-byte LDS reads at addr + OFF (OFF an immediate).  Written as inline assembly
+// on purpose: the compiler cannot tell these reads apart from the LDS slots still
+// being filled by the direct loads of later stages, and before every LDS read it
+// would wait for all of those loads (vmcnt(0)), serialising the pipeline.  The
+// stage being read is complete for every wave (the stage barrier); the caller
+// waits for the reads with lds_wait.
 template <int OFF>
 __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
     bf16x8 v;
@@ -182,273 +134,193 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
     return v;
 }
 
-// Wait until at most N of this wave's LDS reads are outstanding; the fragments
-// are tied to the wait so that no use of them is scheduled above it.
-template <int KA, int KB> struct FragTie;
-template <> struct FragTie<2, 4> {
-    template <int N>
-    static __device__ __forceinline__ void wait(bf16x8* a, bf16x8* b) {
-        asm volatile("s_waitcnt lgkmcnt(%6)"
-                     : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
-                     : "i"(N));
-    }
-};
-template <> struct FragTie<4, 4> {
-    template <int N>
-    static __device__ __forceinline__ void wait(bf16x8* a, bf16x8* b) {
-        asm volatile("s_waitcnt lgkmcnt(%8)"
-                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
-                       "+v"(b[2]), "+v"(b[3])
-                     : "i"(N));
-    }
+// A wave's fragments of one k32 step: 8 A blocks (rows 16 x ..) and 8 B^T blocks.
+struct Frags {
+    bf16x8 a[8], b[8];
 };
 
-template <int N>
+// Wait until this wave's LDS reads are in; the fragments are tied to the wait so
+// that no use of them is scheduled above it.
 __device__ __forceinline__ void lds_wait(Frags& f) {
-    FragTie<kBlkA, kBlkB>::template wait<N>(f.a, f.b);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.a[4]), "+v"(f.a[5]),
+                      "+v"(f.a[6]), "+v"(f.a[7]));
+    asm volatile("" : "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]), "+v"(f.b[4]), "+v"(f.b[5]),
+                      "+v"(f.b[6]), "+v"(f.b[7]));
 }
 
-// LDS byte address of a stage slot's first element.
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+// LDS byte address of a pointer into the LDS array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Lane byte offsets, inside an operand's stage slot, of the lane's fragment of
-// block 0 for k16 step kk (0 .. 3): row row0 + (l mod 32), chunk swz(row, 2 kk + l / 32).
-// The swizzle depends only on the row mod 32, so the other blocks (rows + 32 x)
-// sit at fixed offsets of 32 x 64 bytes.
-__device__ __forceinline__ uint32_t frag_offset(int row0, int kk) {
-    const int l = (int)threadIdx.x & 63;
-    const int row = row0 + (l & 31);
-    return 2u * (uint32_t)(row * kStageK + 8 * swz(row, 2 * kk + (l >> 5)));
-}
-
-// Fragment I of read_frags alone (I < kBlkA: A blocks; then the B blocks).
+// Fragment read I (0-7: A block I, 8-15: B^T block I - 8); blocks are 16 rows =
+// 2 KiB apart, and the lane's swizzled chunk is the same in every block.
 template <int I>
 __device__ __forceinline__ void read_frag(Frags& f, uint32_t a_addr, uint32_t b_addr) {
-    constexpr int kBlk = 32 * kStageK * 2;  // bytes between fragment blocks
-    if constexpr (I < kBlkA)
-        f.a[I] = lds_read16<I * kBlk>(a_addr);
+    if constexpr (I < 8)
+        f.a[I] = lds_read16<I * 2048>(a_addr);
     else
-        f.b[I - kBlkA] = lds_read16<(I - kBlkA) * kBlk>(b_addr);
+        f.b[I - 8] = lds_read16<(I - 8) * 2048>(b_addr);
 }
 
 template <int... Is>
-__device__ __forceinline__ void read_frags_seq(Frags& f, uint32_t a_addr, uint32_t b_addr,
-                                               std::integer_sequence<int, Is...>) {
-    (read_frag<Is>(f, a_addr, b_addr), ...);
-}
-
-// Every fragment of one k16 step: kBlkA A blocks, then kBlkB B blocks.
-__device__ __forceinline__ void read_frags(Frags& f, uint32_t a_addr, uint32_t b_addr) {
-    read_frags_seq(f, a_addr, b_addr, std::make_integer_sequence<int, kBlkA + kBlkB>{});
-}
-
-// MFMA I of mma_frags alone (block x = I / kBlkB, y = I mod kBlkB).
-template <int I>
-__device__ __forceinline__ void mma_one(f32x16 (&acc)[kBlkA][kBlkB], const Frags& f) {
-    constexpr int x = I / kBlkB, y = I % kBlkB;
-    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
+__device__ __forceinline__ void read_frags_seq(Frags& f, uint32_t a, uint32_t b, std::integer_sequence<int, Is...>) {
+    (read_frag<Is>(f, a, b), ...);
 }
 
 __device__ __forceinline__ void sb() { __builtin_amdgcn_sched_barrier(0); }
 
-// The interleaving of a k16 step: kMfma MFMAs, and after MFMA i the memory
-// operations j (of n in all) with j * kMfma / n == i, so they spread evenly and
-// the earliest ones come first.
-constexpr int kMfma = kBlkA * kBlkB;
-constexpr int kReads = kBlkA + kBlkB;
-constexpr int op_slot(int j, int n) { return j * kMfma / n; }
-
-// A k16 step before the barrier: the MFMAs of one fragment set, with the reads of
-// the next step's fragments (into the other set) between them.
-struct PreCtx {
-    Frags* fr;
-    uint32_t a, b;
-};
-template <int I, int J>
-__device__ __forceinline__ void pre_op(const PreCtx& c) {
-    if constexpr (op_slot(J, kReads) == I) {
-        read_frag<J>(*c.fr, c.a, c.b);
-        sb();
-    }
-}
-template <int I, int... Js>
-__device__ __forceinline__ void pre_ops(const PreCtx& c, std::integer_sequence<int, Js...>) {
-    (pre_op<I, Js>(c), ...);
-}
-template <int... Is>
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PreCtx& c,
-                                         std::integer_sequence<int, Is...>) {
-    ((mma_one<Is>(acc, fm), sb(), pre_ops<Is>(c, std::make_integer_sequence<int, kReads>{})), ...);
+template <int I>
+__device__ __forceinline__ void mma_one(f32x4 (&acc)[8][8], const Frags& f) {
+    constexpr int x = I / 8, y = I % 8;
+    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[y], f.a[x], acc[x][y], 0, 0, 0);
 }
 
-// The last k16 step of a stage, after the barrier: its MFMAs, with the reads of
-// the next stage's first fragments and then (when `refill`) the loads refilling
-// the freed slot between them.
-struct PostCtx {
-    Frags* fr;
-    uint32_t a, b;
+// A k32 step: its 64 MFMAs with the other work of the step between them -- the 16
+// fragment reads of the next step over the first 32 MFMAs (they land well before
+// the step ends), and, in the second step of a stage, the 16 loads refilling the
+// slot just freed over the last 32 (measured best of the placements tried).
+struct StepCtx {
+    Frags* next;
+    uint32_t na, nb;                      // the next step's fragment addresses
     __amdgpu_buffer_rsrc_t ra, rb;
-    uint16_t* st;
-    int64_t K, k0;
-    bool refill;
-    uint32_t lane_rows;
+    char* slot;                           // the slot to refill
+    int w;
+    uint32_t K, k0;                       // the stage it is refilled with
+    const LoadLane* ll;
+    bool live;
 };
-template <bool SM, int I, int J>
-__device__ __forceinline__ void post_op(const PostCtx& c) {
-    if constexpr (op_slot(J, kReads + kDmaPerStage) == I) {
-        if constexpr (J < kReads) {
-            read_frag<J>(*c.fr, c.a, c.b);
-        } else {
-            if (c.refill) stage_load_part<J - kReads, SM>(c.ra, c.rb, c.st, c.K, c.k0, c.lane_rows);
+
+template <bool REFILL, int I, int J>
+__device__ __forceinline__ void step_op(const StepCtx& c) {
+    if constexpr (J < kReadsPerStep) {
+        if constexpr (J * 2 == I) {
+            read_frag<J>(*c.next, c.na, c.nb);
+            sb();
         }
-        sb();
+    } else if constexpr (REFILL) {
+        if constexpr (32 + (J - kReadsPerStep) * 2 == I) {
+            stage_load_part<J - kReadsPerStep>(c.ra, c.rb, c.slot, c.w, c.K, c.k0, *c.ll, c.live);
+            sb();
+        }
     }
 }
-template <bool SM, int I, int... Js>
-__device__ __forceinline__ void post_ops(const PostCtx& c, std::integer_sequence<int, Js...>) {
-    (post_op<SM, I, Js>(c), ...);
+template <bool REFILL, int I, int... Js>
+__device__ __forceinline__ void step_ops(const StepCtx& c, std::integer_sequence<int, Js...>) {
+    (step_op<REFILL, I, Js>(c), ...);
 }
-template <bool SM, int... Is>
-__device__ __forceinline__ void mma_step_refill(f32x16 (&acc)[kBlkA][kBlkB], const Frags& fm, const PostCtx& c,
-                                                std::integer_sequence<int, Is...>) {
-    ((mma_one<Is>(acc, fm), sb(), post_ops<SM, Is>(c, std::make_integer_sequence<int, kReads + kDmaPerStage>{})),
+template <bool REFILL, int... Is>
+__device__ __forceinline__ void k32_step(f32x4 (&acc)[8][8], const Frags& f, const StepCtx& c,
+                                         std::integer_sequence<int, Is...>) {
+    ((mma_one<Is>(acc, f), sb(),
+      step_ops<REFILL, Is>(c, std::make_integer_sequence<int, kReadsPerStep + kLoadsPerStage>{})),
      ...);
-}
-
-__device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBlkA][kBlkB], const Frags& f) {
-#pragma unroll
-    for (int x = 0; x < kBlkA; ++x)
-#pragma unroll
-        for (int y = 0; y < kBlkB; ++y)
-            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
 }
 
 // One kTileM x kTileN output tile: C[i, n] = sum_k A[i, k] B^T[n, k] for the
 // rows_valid rows of A at a_rows and the cols_valid rows of B^T at bt_rows (both
-// K-contiguous bf16), stored at c (row stride ldc elements) as bf16 rounded to
-// nearest even, or (F32OUT) as the fp32 accumulators themselves; with NTOUT the
-// output's 16-byte pieces are stored non-temporally (GEMM+ReduceScatter partials,
-// read back only by reduce tasks much later: 3-5 % faster there, measured; the
-// AllGather+GEMM output keeps ordinary stores, 1-3 % faster for it).  SM selects the
-// stage loads' addressing (stage_load_part).
-template <bool F32OUT, bool NTOUT, bool SM>
-__device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid,
-                                          const uint16_t* bt_rows, int cols_valid, int64_t K,
-                                          void* c, int64_t ldc, uint16_t* lds) {
+// K-contiguous bf16, K a multiple of 8), stored at c (row stride ldc elements) as
+// bf16 rounded to nearest even, or (F32OUT) as the fp32 accumulators; with NTOUT the
+// output's 16-byte pieces are stored non-temporally.  `lds` is the workgroup's LDS
+// array (kLdsBytes).
+template <bool F32OUT, bool NTOUT>
+__device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid, const uint16_t* bt_rows,
+                                          int cols_valid, int64_t K64, void* c, int64_t ldc, char* lds) {
     // K and ldc opaque per tile: nothing derived from them is hoisted out of the
     // persistent task loop and kept alive across tiles.
-    asm volatile("" : "+s"(K), "+s"(ldc));
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc_uniform(a_rows, (uint32_t)((int64_t)rows_valid * K * 2));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc_uniform(bt_rows, (uint32_t)((int64_t)cols_valid * K * 2));
-    f32x16 acc[kBlkA][kBlkB];
+    asm volatile("" : "+s"(K64), "+s"(ldc));
+    const uint32_t K = (uint32_t)K64;  // the host keeps 256 K 2 below 2^32
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc_uniform(a_rows, (uint32_t)rows_valid * K * 2u);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc_uniform(bt_rows, (uint32_t)cols_valid * K * 2u);
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int l = (int)threadIdx.x & 63;
+    const int wm = w >> 1, wn = w & 1;
+    f32x4 acc[8][8];
 #pragma unroll
-    for (int x = 0; x < kBlkA; ++x)
+    for (int x = 0; x < 8; ++x)
 #pragma unroll
-        for (int y = 0; y < kBlkB; ++y) acc[x][y] = f32x16{};
-    const int64_t nk = (K + kStageK - 1) / kStageK;
+        for (int y = 0; y < 8; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nk = (int)((K + kStageK - 1) / kStageK);
+    const LoadLane ll = load_lane(K64);
+    char* const slot0 = lds;
+    char* const slot1 = lds + kSlot;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only this tile's LDS loads in flight below
-    // Stage s lives in slot s mod 2.  Both slots are loaded up front (the second
-    // only if its stage exists); stage 0 lands before the first reads.
-    const uint32_t lane_rows = SM ? lane_rows_of(K) : 0u;
-    stage_load<SM>(ra, rb, lds, K, 0, lane_rows);
+    // Stage s lives in slot s mod 2; both are loaded up front (the second only if
+    // its stage exists), and stage 0 lands before the first reads.
+    constexpr auto kParts = std::make_integer_sequence<int, kLoadsPerStage>{};
+    stage_load_seq(ra, rb, slot0, w, K, 0, ll, kParts);
     if (nk > 1) {
-        stage_load<SM>(ra, rb, lds + kSlotElems, K, kStageK, lane_rows);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kDmaPerStage) : "memory");
+        stage_load_seq(ra, rb, slot1, w, K, kStageK, ll, kParts);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kLoadsPerStage) : "memory");
     } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __builtin_amdgcn_s_barrier();
-    // Software pipeline over stages of four k16 steps, the fragments of step q+1
-    // read into the other register set while the MFMAs of step q run:
-    //   q0: MFMAs of f0 = (s, 0), reads of f1 = (s, 1)
-    //   q1: MFMAs of f1,          reads of f0 = (s, 2)
-    //   q2: MFMAs of f0,          reads of f1 = (s, 3)
-    //   wait for f1 (every read of stage s is in) and for stage s+1 (the only
-    //   LDS loads in flight), barrier
-    //   q3: MFMAs of f1,          reads of f0 = (s+1, 0), then the loads
-    //       refilling slot s mod 2 with stage s+2
-    // so the LDS latency of each step hides under the previous step's MFMAs, and
-    // the memory instructions issue while the matrix core works (one MFMA, then one
-    // memory instruction: the MFMA runs on while the next instruction issues).  A
-    // slot is refilled only after the barrier that follows every wave's wait for
-    // its own reads of it; stage s+2 then has q3 of stage s and q0..q2 of stage
-    // s+1 to land.  The last iteration reads f0 of a stage past the end (a slot's
-    // stale contents, never used): those reads are drained after the loop.  Every
-    // branch below is uniform and guards loads only, so the MFMA sequence is the
-    // same on every path.
-    auto slot = [&](int64_t s) { return lds + (s & 1) * kSlotElems; };
-    const int wave = (int)threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    // Step q's fragments sit at step 0's offsets XOR (q << 5): the chunk index
-    // 2 q + lane / 32, XORed with g(row), only moves in bits 1-2 with q, which are
-    // bits 5-6 of the byte offset (rows are 128 bytes).
-    static_assert(kStageK * 2 == 128, "rows of 128 bytes");
-    const uint32_t oa = frag_offset(kWaveRows * wm, 0);
-    const uint32_t ob = frag_offset(kWaveCols * wn, 0) + 2u * kStageA;
-    constexpr auto kSeq = std::make_integer_sequence<int, kMfma>{};
+    // Fragment offsets inside a slot: row 128 wm + l % 16 (then + 16 x), logical chunk
+    // l / 16 (+ 4 in the second k32 step: position ^ 4, byte ^ 64).
+    const uint32_t sw = (uint32_t)((l >> 4) ^ ((l & 15) >> 1)) * 16u;
+    const uint32_t oa = (uint32_t)((128 * wm + (l & 15)) * 128) + sw;
+    const uint32_t ob = (uint32_t)kSlotA + (uint32_t)((128 * wn + (l & 15)) * 128) + sw;
+    const uint32_t base0 = lds_addr(slot0);
     Frags f0, f1;
-    read_frags(f0, lds_addr(slot(0)) + oa, lds_addr(slot(0)) + ob);
-    for (int64_t s = 0; s < nk; ++s) {
-        const uint32_t cs = lds_addr(slot(s));
-        lds_wait<0>(f0);  // the only LDS reads in flight here are f0's
+    read_frags_seq(f0, base0 + oa, base0 + ob, std::make_integer_sequence<int, kReadsPerStep>{});
+    // Per stage s (two k32 steps):
+    //   step 0: MFMAs of f0 = (s, k 0..31), reads f1 <- (s, k 32..63)
+    //   wait for f1 (every read of stage s is in) and for stage s+1 (the only loads in
+    //   flight), barrier: every wave is done with slot s mod 2
+    //   step 1: MFMAs of f1, reads f0 <- (s+1, k 0..31), loads refilling slot s mod 2
+    //           with stage s+2 (zeros past the last stage)
+    // The last iteration reads f0 of a stage past the end (stale contents, unused);
+    // those reads are drained after the loop, and the zero-filling loads too, before
+    // the epilogue reuses the LDS.
+    constexpr auto kSeq = std::make_integer_sequence<int, kMfmaPerStep>{};
+    for (int s = 0; s < nk; ++s) {
+        const uint32_t cs = base0 + (uint32_t)((s & 1) * kSlot);
+        const uint32_t ns = base0 + (uint32_t)(((s + 1) & 1) * kSlot);
+        char* const freed = (s & 1) ? slot1 : slot0;
+        lds_wait(f0);
         sb();
-        mma_step(acc, f0, PreCtx{&f1, cs + (oa ^ (1u << 5)), cs + (ob ^ (1u << 5))}, kSeq);
-        lds_wait<0>(f1);
-        sb();
-        mma_step(acc, f1, PreCtx{&f0, cs + (oa ^ (2u << 5)), cs + (ob ^ (2u << 5))}, kSeq);
-        lds_wait<0>(f0);
-        sb();
-        mma_step(acc, f0, PreCtx{&f1, cs + (oa ^ (3u << 5)), cs + (ob ^ (3u << 5))}, kSeq);
-        lds_wait<0>(f1);  // every read of stage s is in: its slot may be refilled
+        k32_step<false>(acc, f0, StepCtx{&f1, (cs + oa) ^ 64u, (cs + ob) ^ 64u, ra, rb, freed, w, K, 0, &ll, false},
+                        kSeq);
+        lds_wait(f1);
         if (s + 1 < nk) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stage s+1 has landed
         __builtin_amdgcn_s_barrier();
         sb();
-        const uint32_t ns = lds_addr(slot(s + 1));
-        mma_step_refill<SM>(
-            acc, f1, PostCtx{&f0, ns + oa, ns + ob, ra, rb, slot(s), K, (s + 2) * kStageK, s + 2 < nk, lane_rows},
-            kSeq);
+        k32_step<true>(acc, f1,
+                       StepCtx{&f0, ns + oa, ns + ob, ra, rb, freed, w, K, (uint32_t)(s + 2) * kStageK, &ll,
+                               s + 2 < nk},
+                       kSeq);
     }
-    lds_wait<0>(f0);  // the reads past the last stage land before their registers are reused
-    // epilogue: accumulator register e of block (x, y) holds row 8 (e/4) + 4 (lane/32) + e%4,
-    // column lane % 32 of the block.  (The empty asm makes the output pointer opaque
-    // here, so that the compiler does not hoist the epilogue's addresses above the
-    // loop and keep them alive across it.)
+    lds_wait(f0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write the LDS
+    // (The empty asm makes the output pointer opaque here, so that the epilogue's
+    // addresses are not hoisted above the loop and kept alive across it.)
     uint64_t cbase = reinterpret_cast<uint64_t>(c);
     asm volatile("" : "+v"(cbase));
-    const int lane = (int)threadIdx.x & 63;
+    __builtin_amdgcn_s_barrier();  // every wave is out of the ring
     if constexpr (F32OUT) {
-        // fp32: through LDS half a tile at a time (rows [128 h, 128 h + 128)), written
-        // out as 16-byte row pieces.  Each wave's rows lie in one half; waves of the
-        // other half only help with the stores.
-        uint8_t* const t = reinterpret_cast<uint8_t*>(lds);
+        // fp32: half the tile's rows at a time through LDS, written out as 16-byte pieces
         const bool vec = (cbase & 15u) == 0 && (ldc & 3) == 0;
-        constexpr int kPieces = kEpiRows32 * kTileN / 4;  // 4 floats per piece
-        const int my_half = kWaveRows * wm / kEpiRows32;
-        for (int h = 0; h < kTileM / kEpiRows32; ++h) {
-            __builtin_amdgcn_s_barrier();  // the ring, or the previous half, is free
-            if (my_half == h) {
+        for (int h = 0; h < 2; ++h) {
+            if (wm == h) {
 #pragma unroll
-                for (int x = 0; x < kBlkA; ++x)
+                for (int x = 0; x < 8; ++x)
 #pragma unroll
-                    for (int y = 0; y < kBlkB; ++y) {
-                        const int col = kWaveCols * wn + 32 * y + (lane & 31);
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                            *reinterpret_cast<float*>(t + (row - kEpiRows32 * h) * kEpiPitch32 + col * 4) =
-                                acc[x][y][e];
-                        }
+                    for (int y = 0; y < 8; ++y) {
+                        const int row = 16 * x + (l & 15);  // inside the half
+                        const int col = 128 * wn + 16 * y + 4 * (l >> 4);
+                        *reinterpret_cast<f32x4*>(lds + row * kEpiPitch32 + col * 4) = acc[x][y];
                     }
             }
             __syncthreads();
+            constexpr int kPieces = kEpiRows32 * kTileN / 4;
             for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
                 const int lrow = i / (kTileN / 4);
                 const int col0 = (i - lrow * (kTileN / 4)) * 4;
                 const int row = kEpiRows32 * h + lrow;
                 if (row >= rows_valid || col0 >= cols_valid) continue;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(t + lrow * kEpiPitch32 + col0 * 4);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(lds + lrow * kEpiPitch32 + col0 * 4);
                 float* const dst = reinterpret_cast<float*>(cbase) + (int64_t)row * ldc + col0;
                 if (vec && col0 + 4 <= cols_valid) {
                     if (NTOUT)
@@ -461,38 +333,37 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
                         if (col0 + k < cols_valid) dst[k] = __uint_as_float(v[k]);
                 }
             }
+            __syncthreads();
         }
     } else {
-        // bf16: round into the LDS tile (row pitch kEpiPitch), then write it out as
-        // 16-byte row pieces -- 16 stores per lane instead of 128 two-byte ones.
-        // Every wave's reads of the ring are complete (its own waits above); the
-        // barrier makes that true for all of them before the ring is overwritten.
-        __builtin_amdgcn_s_barrier();
-        uint8_t* const t = reinterpret_cast<uint8_t*>(lds);
+        // bf16: round into the LDS tile (8 bytes per lane and block), then write it
+        // out as 16-byte row pieces
 #pragma unroll
-        for (int x = 0; x < kBlkA; ++x)
+        for (int x = 0; x < 8; ++x)
 #pragma unroll
-            for (int y = 0; y < kBlkB; ++y) {
-                const int col = kWaveCols * wn + 32 * y + (lane & 31);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = kWaveRows * wm + 32 * x + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    *reinterpret_cast<uint16_t*>(t + row * kEpiPitch + col * 2) =
-                        (uint16_t)bf16_rne(acc[x][y][e]);
-                }
+            for (int y = 0; y < 8; ++y) {
+                const int row = 128 * wm + 16 * x + (l & 15);
+                const int col = 128 * wn + 16 * y + 4 * (l >> 4);
+                u32x2 v;
+                v[0] = bf16_rne(acc[x][y][0]) | (bf16_rne(acc[x][y][1]) << 16);
+                v[1] = bf16_rne(acc[x][y][2]) | (bf16_rne(acc[x][y][3]) << 16);
+                *reinterpret_cast<u32x2*>(lds + row * kEpiPitch + col * 2) = v;
             }
         __syncthreads();
         // 16-byte pieces need a 16-byte aligned output and a row stride of whole pieces
         const bool vec = (cbase & 15u) == 0 && (ldc & 7) == 0;
-        constexpr int kPieces = kTileM * kTileN / 8;  // 8 bf16 per piece
+        constexpr int kPieces = kTileM * kTileN / 8;
         for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
             const int row = i / (kTileN / 8);
             const int col0 = (i - row * (kTileN / 8)) * 8;
             if (row >= rows_valid || col0 >= cols_valid) continue;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(t + row * kEpiPitch + col0 * 2);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kEpiPitch + col0 * 2);
             uint16_t* const dst = reinterpret_cast<uint16_t*>(cbase) + (int64_t)row * ldc + col0;
             if (vec && col0 + 8 <= cols_valid) {
-                *reinterpret_cast<u32x4*>(dst) = v;
+                if (NTOUT)
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+                else
+                    *reinterpret_cast<u32x4*>(dst) = v;
             } else {
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
@@ -500,7 +371,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
             }
         }
     }
-    __builtin_amdgcn_s_barrier();  // the LDS ring is free for the next tile
+    __builtin_amdgcn_s_barrier();  // the LDS is free for the next tile
 }
 
 // B (K x N, row-major) -> B^T (N x K): each lane transposes one 8 x 8 block in
@@ -539,7 +410,7 @@ hipError_t launch_transpose_b(const uint16_t* b, uint16_t* bt, int64_t K, int64_
 
 template <int SYNC>
 __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) ag_gemm_kernel(AgGemmArgs a) {
-    __shared__ uint16_t lds[kLdsElems];  // 2 stages x (A, B^T), 128 KiB, or the staged output tile
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];  // the ring, or the staged output tile
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
     constexpr bool kOwned = SYNC == kSyncXcd;
@@ -595,8 +466,8 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) ag_gemm_kernel(AgG
                     const int rows_valid = rv < kGemmBM ? (int)rv : kGemmBM;
                     const int64_t n0 = (int64_t)t.nb * kGemmBN;
                     const int cols_valid = a.N - n0 < kGemmBN ? (int)(a.N - n0) : kGemmBN;
-                    gemm_tile<false, false, false>(G + row0 * a.K, rows_valid, a.bt + n0 * a.K, cols_valid, a.K,
-                                     a.c + row0 * a.N + n0, a.N, lds);
+                    gemm_tile<false, false>(G + row0 * a.K, rows_valid, a.bt + n0 * a.K, cols_valid, a.K,
+                                            a.c + row0 * a.N + n0, a.N, lds);
                 }
             }
             if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
@@ -701,7 +572,7 @@ __device__ __forceinline__ void rs_reduce_tile(const GemmRsArgs& a, int j, int t
 
 template <int SYNC, bool F32P>
 __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(GemmRsArgs a) {
-    __shared__ uint16_t lds[kLdsElems];
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
     __shared__ int lds_flag;
     __shared__ int64_t lds_pos[2];
     constexpr bool kOwned = SYNC == kSyncXcd;
@@ -746,7 +617,7 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
                                           col0 * a.K;
                     uint8_t* const part = dst_slice + a.p_off +
                                           (((int64_t)t.r * a.mj + row0) * a.N + col0) * (F32P ? 4 : 2);
-                    gemm_tile<F32P, true, true>(x1, rows, x2t, cols, a.K, part, a.N, lds);
+                    gemm_tile<F32P, true>(x1, rows, x2t, cols, a.K, part, a.N, lds);
                     group_release<SYNC>();
                     if (threadIdx.x == 0)
                         sig_update(sig + grs_sig_slot(a, t.tile, t.r) * kSigStrideU64, 1ull, kSigSet);

@@ -387,6 +387,31 @@ def test_full_moe_combine_w8_d7168(variant):
     full_case("moe_combine_w8_s4096_h1_d7168_bf16", variant, consumer_split=4)
 
 
+def test_full_straggler_timestamps():
+    """The straggler workload at full size in the default mode, with per-tile
+    stamps: every (tile, source) slot is stamped, and the delayed source's tiles
+    complete later than the others' at the median."""
+    wl = synthgen.WORKLOADS["straggler_w16_s2048_h32_d128_f32"]
+    W, S, H, D = wl.W, wl.S, wl.H, wl.D
+    lag = synthgen.straggler_rank(wl)
+    opts = opts_for(wl, straggler_rank=lag, straggler_delay=1000, straggler_seed=2)
+    nt = ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, opts)[0]
+    stamps = torch.full((W * nt,), -1, dtype=torch.int64, device="cuda")
+    opts.timestamps = stamps.data_ptr()
+    if "straggler_w16_s2048_h32_d128_f32" not in _FULL_CACHE:
+        _FULL_CACHE.clear()
+        say("[full] generating straggler_w16_s2048_h32_d128_f32")
+        ins = synthgen.make_inputs(wl)
+        _FULL_CACHE["straggler_w16_s2048_h32_d128_f32"] = (ins, oracle.combine(ins))
+    ins, want = _FULL_CACHE["straggler_w16_s2048_h32_d128_f32"]
+    run_and_check(wl, opts, inputs=ins, want=want, csplit=1)
+    t = stamps.cpu().numpy().view(np.uint64).reshape(W, nt // W, W)
+    assert (t > 0).all() and (t != np.uint64(2**64 - 1)).all(), "a tile was not stamped"
+    t = (t - t.min()).astype(np.float64)
+    others = np.delete(t, lag, axis=2)
+    assert np.median(t[:, :, lag]) > np.median(others), (np.median(t[:, :, lag]), np.median(others))
+
+
 @pytest.mark.parametrize("variant", ["pipelined", "staged", "bulk", "pull", "two_phase"])
 def test_full_straggler_w16_f32(variant):
     wl = synthgen.WORKLOADS["straggler_w16_s2048_h32_d128_f32"]
