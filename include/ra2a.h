@@ -510,20 +510,22 @@ int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t
  * Semantics", section "GEMM + ReduceScatter Overlapping".)  output =
  * ReduceScatter(x1 @ x2): rank r holds x1_r (m x K) and x2_r (K x N); rank j
  * receives out_j = rows [j*m/W, (j+1)*m/W) of sum_r x1_r @ x2_r (m must be
- * divisible by W).  One persistent launch: producer tasks compute 256 x 256
- * tiles of rank r's partial product for destination j, store them into j's
- * receive area at slot r and SET the (tile, r) signal in j's slice; the
- * receiver's reduce task waits for the W partials of its tile, adds them in
- * rank order 0..W-1 in fp32 and stores bf16 (round to nearest even).  A partial
- * is the fp32 accumulator tile of x1_r @ x2_r (one rounding in all, to bf16 at
- * the end), or with RA2A_RS_BF16_PARTIALS that product as the bf16 tensor a
- * framework's matmul returns (rounded to nearest even): half the receive area
- * and its traffic, at the cost of W more roundings, so that where the partials
- * cancel the elementwise error is no longer bounded by the result's magnitude
- * but by 2^-8 * sum_r |partial_r|.  Producers
- * for destination j visit the sources in the RFC's rotation ((j - t) mod W at
- * step t, so rank r works for rank (r + t) mod W).  bf16 operands, fp32
- * accumulation.  Every wait is bounded (ra2a_check reports RA2A_ETIMEOUT).    */
+ * divisible by W).  One persistent launch of tasks, each a 256 x 256 tile of
+ * rank r's partial product for destination j.  The tasks of the W - 1 other
+ * ranks store their tiles into j's receive area at slot r and SET the (tile, r)
+ * signal in j's slice; rank j's own task keeps its tile in its accumulators,
+ * waits for those W - 1 signals, adds the partials in rank order 0..W-1 (its
+ * own in its place) in fp32, stores bf16 (round to nearest even) and SETs
+ * (tile, j).  A partial is the fp32 accumulator tile of x1_r @ x2_r (one
+ * rounding in all, to bf16 at the end), or with RA2A_RS_BF16_PARTIALS that
+ * product as the bf16 tensor a framework's matmul returns (rounded to nearest
+ * even, rank j's own too): half the receive area and its traffic, at the cost
+ * of W more roundings, so that where the partials cancel the elementwise error
+ * is no longer bounded by the result's magnitude but by 2^-8 * sum_r
+ * |partial_r|.  Tasks for destination j visit the sources in a rotation
+ * ((j + 1 + s) mod W at step s, so rank r works for rank (r - 1 - s) mod W and
+ * j's own task comes last).  bf16 operands, fp32 accumulation.  Every wait is
+ * bounded (ra2a_check reports RA2A_ETIMEOUT).                                */
 #define RA2A_RS_AGENT_SYNC 1 /* device-wide release/acquire instead of the XCD-local protocol */
 #define RA2A_RS_SKIP_RESET 2 /* the caller zeroed the signals; no reset launch */
 #define RA2A_RS_BF16_PARTIALS 4 /* partials rounded to bf16 instead of kept in fp32 */
@@ -531,9 +533,11 @@ int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t
 /* Sizes for (W, m, K, N): `tile_slots` = (output tiles of out_j) * W signal slots
  * per slice, then `queue_slots` (RA2A_QUEUE_SLOTS) queue words (slice 0); the
  * `signals` array must hold their sum per slice.  `partial_bytes` = bytes of the
- * receive area per slice: [W][m/W][N] fp32, or bf16 if `flags` holds
- * RA2A_RS_BF16_PARTIALS (the other flags do not change the sizes).  Any output
- * pointer may be NULL.  Errors: EINVAL.                                        */
+ * receive area per slice: W slots of one 256 x 256 partial tile per output tile,
+ * fp32, or bf16 if `flags` holds RA2A_RS_BF16_PARTIALS (the other flags do not
+ * change the sizes); its layout is the library's own (the accumulators in the
+ * order the matrix-core lanes hold them).  Any output pointer may be NULL.
+ * Errors: EINVAL.                                                               */
 int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int flags, int64_t *tile_slots,
                        int64_t *queue_slots, size_t *partial_bytes);
 
@@ -541,8 +545,8 @@ int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int flags, int64_
  * offsets in every slice (row-major, bf16 unless stated):
  *   x1      slice r: x1_r, m x K (16-byte aligned);
  *   x2t     slice r: x2_r transposed, N x K (16-byte aligned);
- *   partial slice j: the receive area, [W][m/W][N] fp32 or (RA2A_RS_BF16_PARTIALS)
- *           bf16 (16-byte aligned);
+ *   partial slice j: the receive area, ra2a_gemm_rs_sizes' partial_bytes
+ *           (16-byte aligned; scratch, its contents are the library's);
  *   out     slice j: out_j, m/W x N (8-byte aligned);
  *   signals slice j: ra2a_gemm_rs_sizes' slots at 128-byte spacing (8-byte aligned).
  * K must be a multiple of 8, and 512 * K below 2^32 (a tile's operand rows are
@@ -556,8 +560,8 @@ int ra2a_gemm_rs(const void *x1, const void *x2t, void *partial, void *out, uint
                  int W, int64_t m, int64_t K, int64_t N, int flags, void *stream);
 
 /* Host check of the GEMM+ReduceScatter work queues for a device of num_xcd
- * XCDs: every (destination, tile, source) GEMM task and every reduce task once,
- * each reduce task after the W GEMM tasks it waits for.  tasks_per_group
+ * XCDs: every (destination, tile, source) task once, and each receiver's task
+ * (source == destination) after the W - 1 tasks it waits for.  tasks_per_group
  * (optional) receives the queue length.  Returns EINVAL with a message on a
  * violation.                                                                   */
 int ra2a_debug_gemm_rs_plan(int W, int64_t m, int64_t K, int64_t N, int num_xcd,

@@ -55,10 +55,8 @@ constexpr int kLoadsPerStage = 16;             // 1 KiB LDS loads per wave per s
 constexpr int kReadsPerStep = 16;              // 16-byte fragment reads per wave per k32 step
 constexpr int kMfmaPerStep = 64;               // 8 x 8 blocks
 constexpr int kEpiPitch = kTileN * 2 + 16;     // bf16 output tile staged in LDS, bytes per row
-constexpr int kEpiRows32 = kTileM / 2;         // fp32 output: half the tile at a time
-constexpr int kEpiPitch32 = kTileN * 4 + 16;
-constexpr int kLdsBytes = kTileM * kEpiPitch;  // the largest of the three uses
-static_assert(2 * kSlot <= kLdsBytes && kEpiRows32 * kEpiPitch32 <= kLdsBytes, "LDS array");
+constexpr int kLdsBytes = kTileM * kEpiPitch;  // the larger of the two uses
+static_assert(2 * kSlot <= kLdsBytes, "LDS array");
 static_assert(kLdsBytes + 1024 <= 160 * 1024, "the LDS of a CU holds the workgroup");
 
 // float -> bf16, round to nearest even (NaN stays NaN).
@@ -218,25 +216,25 @@ __device__ __forceinline__ void k32_step(f32x4 (&acc)[8][8], const Frags& f, con
      ...);
 }
 
-// One kTileM x kTileN output tile: C[i, n] = sum_k A[i, k] B^T[n, k] for the
-// rows_valid rows of A at a_rows and the cols_valid rows of B^T at bt_rows (both
-// K-contiguous bf16, K a multiple of 8), stored at c (row stride ldc elements) as
-// bf16 rounded to nearest even, or (F32OUT) as the fp32 accumulators; with NTOUT the
-// output's 16-byte pieces are stored non-temporally.  `lds` is the workgroup's LDS
-// array (kLdsBytes).
-template <bool F32OUT, bool NTOUT>
-__device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid, const uint16_t* bt_rows,
-                                          int cols_valid, int64_t K64, void* c, int64_t ldc, char* lds) {
-    // K and ldc opaque per tile: nothing derived from them is hoisted out of the
-    // persistent task loop and kept alive across tiles.
-    asm volatile("" : "+s"(K64), "+s"(ldc));
+// Main loop of one kTileM x kTileN output tile: acc = the fp32 accumulators of
+// C[i, n] = sum_k A[i, k] B^T[n, k] for the rows_valid rows of A at a_rows and the
+// cols_valid rows of B^T at bt_rows (both K-contiguous bf16, K a multiple of 8);
+// rows and columns past those counts accumulate zeros.  Lane l of wave (wm, wn)
+// holds in acc[x][y] the rows 128 wm + 16 x + l % 16, columns 128 wn + 16 y +
+// 4 (l / 16) .. + 3.  `lds` is the workgroup's LDS array (kLdsBytes); on return
+// every wave is out of it and no load is in flight.
+__device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][8], const uint16_t* a_rows, int rows_valid,
+                                              const uint16_t* bt_rows, int cols_valid, int64_t K64,
+                                              char* lds) {
+    // K opaque per tile: nothing derived from it is hoisted out of the persistent
+    // task loop and kept alive across tiles.
+    asm volatile("" : "+s"(K64));
     const uint32_t K = (uint32_t)K64;  // the host keeps 256 K 2 below 2^32
     const __amdgpu_buffer_rsrc_t ra = make_rsrc_uniform(a_rows, (uint32_t)rows_valid * K * 2u);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc_uniform(bt_rows, (uint32_t)cols_valid * K * 2u);
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int l = (int)threadIdx.x & 63;
     const int wm = w >> 1, wn = w & 1;
-    f32x4 acc[8][8];
 #pragma unroll
     for (int x = 0; x < 8; ++x)
 #pragma unroll
@@ -294,84 +292,67 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid
     }
     lds_wait(f0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write the LDS
+    __builtin_amdgcn_s_barrier();  // every wave is out of the ring
+}
+
+// Epilogue: the tile's rows_valid x cols_valid corner of acc, rounded to bf16
+// (nearest even), stored at c (row stride ldc elements) through the LDS; with
+// NTOUT the 16-byte pieces are stored non-temporally.
+template <bool NTOUT>
+__device__ __forceinline__ void epi_bf16(const f32x4 (&acc)[8][8], int rows_valid, int cols_valid, void* c,
+                                         int64_t ldc, char* lds) {
+    asm volatile("" : "+s"(ldc));
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int l = (int)threadIdx.x & 63;
+    const int wm = w >> 1, wn = w & 1;
     // (The empty asm makes the output pointer opaque here, so that the epilogue's
-    // addresses are not hoisted above the loop and kept alive across it.)
+    // addresses are not hoisted above the main loop and kept alive across it.)
     uint64_t cbase = reinterpret_cast<uint64_t>(c);
     asm volatile("" : "+v"(cbase));
-    __builtin_amdgcn_s_barrier();  // every wave is out of the ring
-    if constexpr (F32OUT) {
-        // fp32: half the tile's rows at a time through LDS, written out as 16-byte pieces
-        const bool vec = (cbase & 15u) == 0 && (ldc & 3) == 0;
-        for (int h = 0; h < 2; ++h) {
-            if (wm == h) {
+    // bf16: round into the LDS tile (8 bytes per lane and block), then write it
+    // out as 16-byte row pieces
 #pragma unroll
-                for (int x = 0; x < 8; ++x)
+    for (int x = 0; x < 8; ++x)
 #pragma unroll
-                    for (int y = 0; y < 8; ++y) {
-                        const int row = 16 * x + (l & 15);  // inside the half
-                        const int col = 128 * wn + 16 * y + 4 * (l >> 4);
-                        *reinterpret_cast<f32x4*>(lds + row * kEpiPitch32 + col * 4) = acc[x][y];
-                    }
-            }
-            __syncthreads();
-            constexpr int kPieces = kEpiRows32 * kTileN / 4;
-            for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
-                const int lrow = i / (kTileN / 4);
-                const int col0 = (i - lrow * (kTileN / 4)) * 4;
-                const int row = kEpiRows32 * h + lrow;
-                if (row >= rows_valid || col0 >= cols_valid) continue;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(lds + lrow * kEpiPitch32 + col0 * 4);
-                float* const dst = reinterpret_cast<float*>(cbase) + (int64_t)row * ldc + col0;
-                if (vec && col0 + 4 <= cols_valid) {
-                    if (NTOUT)
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-                    else
-                        *reinterpret_cast<u32x4*>(dst) = v;
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (col0 + k < cols_valid) dst[k] = __uint_as_float(v[k]);
-                }
-            }
-            __syncthreads();
+        for (int y = 0; y < 8; ++y) {
+            const int row = 128 * wm + 16 * x + (l & 15);
+            const int col = 128 * wn + 16 * y + 4 * (l >> 4);
+            u32x2 v;
+            v[0] = bf16_rne(acc[x][y][0]) | (bf16_rne(acc[x][y][1]) << 16);
+            v[1] = bf16_rne(acc[x][y][2]) | (bf16_rne(acc[x][y][3]) << 16);
+            *reinterpret_cast<u32x2*>(lds + row * kEpiPitch + col * 2) = v;
         }
-    } else {
-        // bf16: round into the LDS tile (8 bytes per lane and block), then write it
-        // out as 16-byte row pieces
+    __syncthreads();
+    // 16-byte pieces need a 16-byte aligned output and a row stride of whole pieces
+    const bool vec = (cbase & 15u) == 0 && (ldc & 7) == 0;
+    constexpr int kPieces = kTileM * kTileN / 8;
+    for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
+        const int row = i / (kTileN / 8);
+        const int col0 = (i - row * (kTileN / 8)) * 8;
+        if (row >= rows_valid || col0 >= cols_valid) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kEpiPitch + col0 * 2);
+        uint16_t* const dst = reinterpret_cast<uint16_t*>(cbase) + (int64_t)row * ldc + col0;
+        if (vec && col0 + 8 <= cols_valid) {
+            if (NTOUT)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+            else
+                *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-#pragma unroll
-            for (int y = 0; y < 8; ++y) {
-                const int row = 128 * wm + 16 * x + (l & 15);
-                const int col = 128 * wn + 16 * y + 4 * (l >> 4);
-                u32x2 v;
-                v[0] = bf16_rne(acc[x][y][0]) | (bf16_rne(acc[x][y][1]) << 16);
-                v[1] = bf16_rne(acc[x][y][2]) | (bf16_rne(acc[x][y][3]) << 16);
-                *reinterpret_cast<u32x2*>(lds + row * kEpiPitch + col * 2) = v;
-            }
-        __syncthreads();
-        // 16-byte pieces need a 16-byte aligned output and a row stride of whole pieces
-        const bool vec = (cbase & 15u) == 0 && (ldc & 7) == 0;
-        constexpr int kPieces = kTileM * kTileN / 8;
-        for (int i = (int)threadIdx.x; i < kPieces; i += kGemmThreads) {
-            const int row = i / (kTileN / 8);
-            const int col0 = (i - row * (kTileN / 8)) * 8;
-            if (row >= rows_valid || col0 >= cols_valid) continue;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kEpiPitch + col0 * 2);
-            uint16_t* const dst = reinterpret_cast<uint16_t*>(cbase) + (int64_t)row * ldc + col0;
-            if (vec && col0 + 8 <= cols_valid) {
-                if (NTOUT)
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-                else
-                    *reinterpret_cast<u32x4*>(dst) = v;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (col0 + k < cols_valid) dst[k] = (uint16_t)(v[k >> 1] >> (16 * (k & 1)));
-            }
+            for (int k = 0; k < 8; ++k)
+                if (col0 + k < cols_valid) dst[k] = (uint16_t)(v[k >> 1] >> (16 * (k & 1)));
         }
     }
     __builtin_amdgcn_s_barrier();  // the LDS is free for the next tile
+}
+
+// One output tile, stored as bf16.
+template <bool NTOUT>
+__device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid, const uint16_t* bt_rows,
+                                          int cols_valid, int64_t K, void* c, int64_t ldc, char* lds) {
+    f32x4 acc[8][8];
+    gemm_mainloop(acc, a_rows, rows_valid, bt_rows, cols_valid, K, lds);
+    epi_bf16<NTOUT>(acc, rows_valid, cols_valid, c, ldc, lds);
 }
 
 // B (K x N, row-major) -> B^T (N x K): each lane transposes one 8 x 8 block in
@@ -466,7 +447,7 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) ag_gemm_kernel(AgG
                     const int rows_valid = rv < kGemmBM ? (int)rv : kGemmBM;
                     const int64_t n0 = (int64_t)t.nb * kGemmBN;
                     const int cols_valid = a.N - n0 < kGemmBN ? (int)(a.N - n0) : kGemmBN;
-                    gemm_tile<false, false>(G + row0 * a.K, rows_valid, a.bt + n0 * a.K, cols_valid, a.K,
+                    gemm_tile<false>(G + row0 * a.K, rows_valid, a.bt + n0 * a.K, cols_valid, a.K,
                                             a.c + row0 * a.N + n0, a.N, lds);
                 }
             }
@@ -481,93 +462,124 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) ag_gemm_kernel(AgG
 // ---------------------------------------------------------------------------
 // GEMM + ReduceScatter (gemm_rs_geom.h): one persistent launch over one work
 // queue per XCD.  Destination j's tasks form group j mod NG, bound to one XCD
-// like the AllGather's, so the partials a reduce task reads were written into
-// the L2 it reads through.
+// like the AllGather's, so the partials the receiver's task reads were written
+// into the L2 it reads through.
 
-// Reduce task: out_j tile = sum over r = 0..W-1 (in that order) of the partials
-// partial_j[r] of the tile (bf16, or with F32P fp32), added in fp32 and rounded
-// to bf16 (nearest even).  The partials are read with device-scope loads (never
-// from the CU's L1).  V columns per lane: V partial elements form one load.
-constexpr int kRsGroup = 8;  // partial loads in flight per lane in a reduce task
+// A partial tile in the lanes' own order: thread t's 16-byte piece number b --
+// block (x, y), b = 8 x + y, as fp32; or blocks (x, 2 p) and (x, 2 p + 1), b =
+// 4 x + p, as bf16 rounded to nearest even -- at byte 4096 b + 16 t of the
+// tile's slot.  Stored non-temporally: each partial is read once, by the
+// receiver's task.
+constexpr int kRsPieceBytes = kGemmThreads * 16;
 
-template <bool F32P, int V>
-__device__ __forceinline__ void rs_reduce_cols(const GemmRsArgs& a, uint8_t* slice, int64_t row0,
-                                               int64_t col0, int rows, int cols) {
-    constexpr int E = F32P ? 4 : 2;  // bytes per partial element
-    // device scope (never the CU's L1) and non-temporal: each partial is read once,
-    // and streaming it keeps the L2 for the GEMM tiles' operands (fp32 partials
-    // 0.86 -> 0.785 ms at W = 8, m = 8192, K = 896, N = 4096, measured)
-    using Load = BufLoad<V * E, kPolicySc1 | kPolicyNt>;
-    const __amdgpu_buffer_rsrc_t rp =
-        make_rsrc_uniform(slice + a.p_off, (uint32_t)((int64_t)a.W * a.mj * a.N * E));
-    uint16_t* const out = reinterpret_cast<uint16_t*>(slice + a.out_off);
-    const uint32_t plane = (uint32_t)(a.mj * a.N * E);  // bytes of one source's partial
-    const int vc = cols / V;
-    for (int i = threadIdx.x; i < rows * vc; i += kGemmThreads) {
-        const int r = i / vc;
-        const int c = (i - r * vc) * V;
-        const int64_t el = (row0 + r) * a.N + col0 + c;
-        const uint32_t off = (uint32_t)(el * E);
-        float s[V];
+__device__ __forceinline__ u32x4 bits(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
+
+template <bool F32P>
+__device__ __forceinline__ void rs_store_partial(const f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t rp,
+                                                 uint32_t slot) {
+    const uint32_t off = slot + threadIdx.x * 16u;
+    if constexpr (F32P) {
 #pragma unroll
-        for (int v = 0; v < V; ++v) s[v] = 0.f;
-        // the sources in groups of kRsGroup: every load of a group is issued before
-        // the first add (a short group loads the last source again and skips the
-        // add), then the adds run in rank order
-        for (int src0 = 0; src0 < a.W; src0 += kRsGroup) {
-            decltype(Load::go(rp, 0u)) x[kRsGroup];
+        for (int b = 0; b < 64; ++b)
+            BufStore<16, kPolicyNt>::go(bits(acc[b >> 3][b & 7]), rp, off + (uint32_t)(b * kRsPieceBytes));
+    } else {
 #pragma unroll
-            for (int g = 0; g < kRsGroup; ++g) {
-                const int src = src0 + g < a.W ? src0 + g : a.W - 1;
-                x[g] = Load::go(rp, off + (uint32_t)src * plane);
-            }
-#pragma unroll
-            for (int g = 0; g < kRsGroup; ++g) {
-                // a select, not a branch: every loaded value is used, so no load is
-                // sunk behind a test and the group's loads stay in flight together
-                const bool live = src0 + g < a.W;
-                if constexpr (V == 1) {
-                    const float t = F32P ? __uint_as_float((uint32_t)x[g]) : __uint_as_float((uint32_t)x[g] << 16);
-                    s[0] = live ? s[0] + t : s[0];
-                } else {
-#pragma unroll
-                    for (int v = 0; v < V; ++v) {
-                        const float t = F32P ? __uint_as_float(x[g][v])
-                                             : __uint_as_float(v & 1 ? x[g][v >> 1] & 0xFFFF0000u : x[g][v >> 1] << 16);
-                        s[v] = live ? s[v] + t : s[v];
-                    }
-                }
-            }
-        }
-        if constexpr (V == 1) {
-            out[el] = (uint16_t)bf16_rne(s[0]);
-        } else {
-            // V bf16 results as V/4 8-byte stores (out is 8-byte aligned, V*2 bytes per lane)
-#pragma unroll
-            for (int q = 0; q < V / 4; ++q) {
-                u32x2 o;
-                o[0] = bf16_rne(s[4 * q]) | (bf16_rne(s[4 * q + 1]) << 16);
-                o[1] = bf16_rne(s[4 * q + 2]) | (bf16_rne(s[4 * q + 3]) << 16);
-                *reinterpret_cast<u32x2*>(out + el + 4 * q) = o;
-            }
+        for (int b = 0; b < 32; ++b) {
+            const f32x4 u = acc[b >> 2][2 * (b & 3)], v = acc[b >> 2][2 * (b & 3) + 1];
+            const u32x4 o = {bf16_rne(u[0]) | (bf16_rne(u[1]) << 16), bf16_rne(u[2]) | (bf16_rne(u[3]) << 16),
+                             bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
+            BufStore<16, kPolicyNt>::go(o, rp, off + (uint32_t)(b * kRsPieceBytes));
         }
     }
 }
 
+// The receiver's own partial as the sum takes it: its accumulators, or those
+// rounded to bf16 like every other partial.
 template <bool F32P>
-__device__ __forceinline__ void rs_reduce_tile(const GemmRsArgs& a, int j, int tile) {
-    int mb, nb;
-    grs_tile(a, tile, &mb, &nb);
-    const int64_t row0 = (int64_t)mb * kRsTileM, col0 = (int64_t)nb * kRsTileN;
-    const int rows = a.mj - row0 < kRsTileM ? (int)(a.mj - row0) : kRsTileM;
-    const int cols = a.N - col0 < kRsTileN ? (int)(a.N - col0) : kRsTileN;
-    uint8_t* const slice = a.base + (int64_t)j * a.stride;
-    // 16-byte loads where every row of a tile splits into whole vectors
-    constexpr int V = F32P ? 4 : 8;
-    if (a.N % V == 0)
-        rs_reduce_cols<F32P, V>(a, slice, row0, col0, rows, cols);
-    else
-        rs_reduce_cols<F32P, 1>(a, slice, row0, col0, rows, cols);
+__device__ __forceinline__ f32x4 rs_own(f32x4 v) {
+    if constexpr (F32P) {
+        return v;
+    } else {
+        return f32x4{__uint_as_float(bf16_rne(v[0]) << 16), __uint_as_float(bf16_rne(v[1]) << 16),
+                     __uint_as_float(bf16_rne(v[2]) << 16), __uint_as_float(bf16_rne(v[3]) << 16)};
+    }
+}
+
+// Half h of a bf16 piece: the four values of one block.
+__device__ __forceinline__ f32x4 rs_unpack_bf16(u32x4 x, int h) {
+    const uint32_t lo = x[2 * h], hi = x[2 * h + 1];
+    return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u), __uint_as_float(hi << 16),
+                 __uint_as_float(hi & 0xFFFF0000u)};
+}
+
+// The receiver's task: acc <- sum over r = 0..W-1, in that order, of the tile's
+// partials in fp32, its own (acc, see rs_own) in place r == j; slot r at byte
+// tile_off + r src_stride of the receive area.  The partials are read with
+// device-scope non-temporal loads (never from the CU's L1); the loads of
+// kFoldPieces pieces of up to kFoldSrc sources are in flight together (a source
+// past W, or j itself, is sent out of range and reads zero without touching
+// memory; a select, not a branch, drops it, so no load waits behind a test).
+constexpr int kFoldSrc = 8;
+constexpr int kFoldPieces = 4;
+
+// Pieces P0 .. P0 + kFoldPieces - 1 (a template parameter, so that every index
+// into acc is a constant and acc stays in registers).
+template <bool F32P, int P0>
+__device__ __forceinline__ void rs_fold_group(f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
+                                              uint32_t src_stride, int j, int W) {
+    constexpr int kBlk = F32P ? 1 : 2;  // blocks per piece
+    using Load = BufLoad<16, kPolicySc1 | kPolicyNt>;
+    const uint32_t t16 = threadIdx.x * 16u;
+    f32x4 s[kFoldPieces * kBlk];
+#pragma unroll
+    for (int i = 0; i < kFoldPieces * kBlk; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int src0 = 0; src0 < W; src0 += kFoldSrc) {
+        u32x4 x[kFoldSrc][kFoldPieces];
+#pragma unroll
+        for (int g = 0; g < kFoldSrc; ++g) {
+            const int src = src0 + g;
+            const bool load = src < W && src != j;
+            const uint32_t base = tile_off + (uint32_t)src * src_stride + t16;
+#pragma unroll
+            for (int q = 0; q < kFoldPieces; ++q)
+                x[g][q] = Load::go(rp, load ? base + (uint32_t)((P0 + q) * kRsPieceBytes) : kOutOfRange);
+        }
+#pragma unroll
+        for (int g = 0; g < kFoldSrc; ++g) {
+            const int src = src0 + g;
+#pragma unroll
+            for (int q = 0; q < kFoldPieces; ++q)
+#pragma unroll
+                for (int h = 0; h < kBlk; ++h) {
+                    const int b = (P0 + q) * kBlk + h;  // block 8 x + y
+                    const f32x4 v = src == j ? rs_own<F32P>(acc[b >> 3][b & 7])
+                                             : (F32P ? __builtin_bit_cast(f32x4, x[g][q]) : rs_unpack_bf16(x[g][q], h));
+                    f32x4& t = s[q * kBlk + h];
+                    t = src < W ? t + v : t;
+                }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kFoldPieces; ++q)
+#pragma unroll
+        for (int h = 0; h < kBlk; ++h) {
+            const int b = (P0 + q) * kBlk + h;
+            acc[b >> 3][b & 7] = s[q * kBlk + h];
+        }
+}
+
+template <bool F32P, int... Gs>
+__device__ __forceinline__ void rs_fold_groups(f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
+                                               uint32_t src_stride, int j, int W, std::integer_sequence<int, Gs...>) {
+    (rs_fold_group<F32P, Gs * kFoldPieces>(acc, rp, tile_off, src_stride, j, W), ...);
+}
+
+template <bool F32P>
+__device__ __forceinline__ void rs_fold(f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
+                                        uint32_t src_stride, int j, int W) {
+    constexpr int kPieces = F32P ? 64 : 32;
+    rs_fold_groups<F32P>(acc, rp, tile_off, src_stride, j, W,
+                         std::make_integer_sequence<int, kPieces / kFoldPieces>{});
 }
 
 template <int SYNC, bool F32P>
@@ -580,6 +592,9 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
     const uint32_t xcc = xcc_id();
     const int home = SYNC == kSyncXcd ? (int)(xcc % (uint32_t)a.NG) : (int)(blockIdx.x % a.NG);
     const int64_t total = a.ntasks_dest * a.dpg;
+    // the receive area (W slots of ntiles partial tiles) is below 4 GiB (host check)
+    const uint32_t src_stride = (uint32_t)grs_part_offset(a, 1, 0);
+    const uint32_t area = (uint32_t)grs_part_offset(a, a.W, 0);
     QueueClaim qc;
     int k = 0;
     for (int gi = 0; gi < a.NG; ++gi) {
@@ -600,33 +615,42 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
             if (threadIdx.x == 0) nxt = queue_next(qc);
             const RsTask t = grs_group_task(a, g, pos);
             if (t.j < a.W) {
+                // rank r's partial of the tile: rows j*mj + mb*256 .. of x1_r, rows
+                // nb*256 .. of x2_r^T
                 uint8_t* const dst_slice = a.base + (int64_t)t.j * a.stride;
                 uint64_t* const sig = reinterpret_cast<uint64_t*>(dst_slice + a.sig_off);
-                if (!t.reduce) {
-                    // rank r's partial of the tile: rows j*mj + mb*256 .. of x1_r,
-                    // rows nb*256 .. of x2_r^T, into slot r of j's receive area
-                    int mb, nb;
-                    grs_tile(a, t.tile, &mb, &nb);
-                    const int64_t row0 = (int64_t)mb * kRsTileM, col0 = (int64_t)nb * kRsTileN;
-                    const int rows = a.mj - row0 < kRsTileM ? (int)(a.mj - row0) : kRsTileM;
-                    const int cols = a.N - col0 < kRsTileN ? (int)(a.N - col0) : kRsTileN;
-                    const uint8_t* const src_slice = a.base + (int64_t)t.r * a.stride;
-                    const uint16_t* x1 = reinterpret_cast<const uint16_t*>(src_slice + a.a_off) +
-                                         ((int64_t)t.j * a.mj + row0) * a.K;
-                    const uint16_t* x2t = reinterpret_cast<const uint16_t*>(src_slice + a.bt_off) +
-                                          col0 * a.K;
-                    uint8_t* const part = dst_slice + a.p_off +
-                                          (((int64_t)t.r * a.mj + row0) * a.N + col0) * (F32P ? 4 : 2);
-                    gemm_tile<F32P, true>(x1, rows, x2t, cols, a.K, part, a.N, lds);
+                int mb, nb;
+                grs_tile(a, t.tile, &mb, &nb);
+                const int64_t row0 = (int64_t)mb * kRsTileM, col0 = (int64_t)nb * kRsTileN;
+                const int rows = a.mj - row0 < kRsTileM ? (int)(a.mj - row0) : kRsTileM;
+                const int cols = a.N - col0 < kRsTileN ? (int)(a.N - col0) : kRsTileN;
+                const uint8_t* const src_slice = a.base + (int64_t)t.r * a.stride;
+                const uint16_t* x1 = reinterpret_cast<const uint16_t*>(src_slice + a.a_off) +
+                                     ((int64_t)t.j * a.mj + row0) * a.K;
+                const uint16_t* x2t = reinterpret_cast<const uint16_t*>(src_slice + a.bt_off) + col0 * a.K;
+                f32x4 acc[8][8];
+                gemm_mainloop(acc, x1, rows, x2t, cols, a.K, lds);
+                const __amdgpu_buffer_rsrc_t rp = make_rsrc_uniform(dst_slice + a.p_off, area);
+                if (t.r != t.j) {
+                    // into slot r of j's receive area, then the (tile, r) signal
+                    rs_store_partial<F32P>(acc, rp, (uint32_t)grs_part_offset(a, t.r, t.tile));
                     group_release<SYNC>();
                     if (threadIdx.x == 0)
                         sig_update(sig + grs_sig_slot(a, t.tile, t.r) * kSigStrideU64, 1ull, kSigSet);
                 } else {
-                    if (!group_wait_all<SYNC == kSyncAgent>(sig + grs_sig_slot(a, t.tile, 0) * kSigStrideU64,
-                                                            kSigStrideU64 * 8, a.W, kCmpEq, 1ull,
+                    // the other sources' partials: signals (tile, 0 .. j-1), (tile, j+1 .. W-1)
+                    uint64_t* const s0 = sig + grs_sig_slot(a, t.tile, 0) * kSigStrideU64;
+                    if (!group_wait_all<SYNC == kSyncAgent>(s0, kSigStrideU64 * 8, t.j, kCmpEq, 1ull, a.timeout,
+                                                            a.err, &lds_flag) ||
+                        !group_wait_all<SYNC == kSyncAgent>(s0 + (int64_t)(t.j + 1) * kSigStrideU64,
+                                                            kSigStrideU64 * 8, a.W - 1 - t.j, kCmpEq, 1ull,
                                                             a.timeout, a.err, &lds_flag))
                         return;
-                    rs_reduce_tile<F32P>(a, t.j, t.tile);
+                    rs_fold<F32P>(acc, rp, (uint32_t)grs_part_offset(a, 0, t.tile), src_stride, t.j, a.W);
+                    epi_bf16<true>(acc, rows, cols, dst_slice + a.out_off + (row0 * a.N + col0) * 2, a.N, lds);
+                    group_release<SYNC>();
+                    if (threadIdx.x == 0)
+                        sig_update(sig + grs_sig_slot(a, t.tile, t.j) * kSigStrideU64, 1ull, kSigSet);
                 }
             }
             if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;

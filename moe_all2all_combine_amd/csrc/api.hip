@@ -1291,8 +1291,8 @@ RA2A_API int ra2a_ag_gemm_noalloc(const void* a_shards, void* gathered, const vo
 
 namespace {
 
-// bytes per element of the receive area
-size_t gemm_rs_elem(const ra2a::GemmRsArgs& a) { return a.f32p ? 4u : 2u; }
+// bytes of the receive area: W slots of ntiles partial tiles (fp32 or bf16)
+size_t gemm_rs_area(const ra2a::GemmRsArgs& a) { return (size_t)ra2a::grs_part_offset(a, a.W, 0); }
 
 int plan_gemm_rs(int W, int64_t m, int64_t K, int64_t N, int nxcd, int flags,
                  ra2a::GemmRsArgs* a) {
@@ -1317,13 +1317,13 @@ int plan_gemm_rs(int W, int64_t m, int64_t K, int64_t N, int nxcd, int flags,
     a->dpg = (int)cdiv(W, a->NG);
     a->sync = ((flags & RA2A_RS_AGENT_SYNC) || nxcd > ra2a::kNumXcd) ? ra2a::kSyncAgent : ra2a::kSyncXcd;
     a->f32p = (flags & RA2A_RS_BF16_PARTIALS) ? 0 : 1;
-    a->ntasks_dest = (int64_t)a->ntiles * (W + 1);
+    a->ntasks_dest = (int64_t)a->ntiles * W;
     if ((double)a->ntasks_dest * a->dpg >= 2147483647.0 - 65536.0)
         return fail(RA2A_EINVAL, "GEMM+ReduceScatter too large for 32-bit task indices");
     // a GEMM tile's operand rows and the receive area are addressed with 32-bit buffer offsets
     if ((double)ra2a::kRsTileN * K * 2 >= 4294967295.0 - 65536.0)
         return fail(RA2A_EINVAL, "K too large for 32-bit operand offsets");
-    if ((double)W * a->mj * N * gemm_rs_elem(*a) >= 4294967295.0 - 65536.0)
+    if ((double)W * a->ntiles * ra2a::kRsPartElems * (a->f32p ? 4 : 2) >= 4294967295.0 - 65536.0)
         return fail(RA2A_EINVAL, "receive area of 4 GiB or more per slice");
     return RA2A_OK;
 }
@@ -1337,7 +1337,7 @@ RA2A_API int ra2a_gemm_rs_sizes(int W, int64_t m, int64_t K, int64_t N, int flag
     if (rc) return rc;
     if (tile_slots) *tile_slots = (int64_t)a.ntiles * W;
     if (queue_slots) *queue_slots = ra2a::kQueueSlots;
-    if (partial_bytes) *partial_bytes = (size_t)W * (size_t)a.mj * (size_t)N * gemm_rs_elem(a);
+    if (partial_bytes) *partial_bytes = gemm_rs_area(a);
     return ok();
 }
 
@@ -1359,7 +1359,7 @@ RA2A_API int ra2a_gemm_rs(const void* x1, const void* x2t, void* partial, void* 
     const size_t o_a = sym_offset(h, x1), o_b = sym_offset(h, x2t), o_p = sym_offset(h, partial);
     const size_t o_o = sym_offset(h, out), o_s = sym_offset(h, signals);
     const size_t n_a = (size_t)(m * K * 2), n_b = (size_t)(N * K * 2);
-    const size_t n_p = (size_t)W * (size_t)a.mj * (size_t)N * gemm_rs_elem(a), n_o = (size_t)(a.mj * N * 2);
+    const size_t n_p = gemm_rs_area(a), n_o = (size_t)(a.mj * N * 2);
     const int64_t nslots = ra2a::grs_queue_slot(a) + ra2a::kQueueSlots;
     const size_t n_s = (size_t)nslots * RA2A_SIG_STRIDE_BYTES;
     if (o_a % 16 || o_b % 16 || o_p % 16 || o_o % 8 || o_s % 8)
@@ -1411,36 +1411,30 @@ RA2A_API int ra2a_debug_gemm_rs_plan(int W, int64_t m, int64_t K, int64_t N, int
     ra2a::GemmRsArgs a{};
     int rc = plan_gemm_rs(W, m, K, N, std::max(1, num_xcd), 0, &a);
     if (rc) return rc;
-    // every destination's queue: each (source, tile) GEMM task and each reduce task
-    // exactly once, and every reduce task after the W GEMM tasks it waits for
+    // every destination's queue: each (source, tile) task exactly once, and the
+    // receiver's task of a tile (r == j, which waits) after the W - 1 it waits for
     for (int g = 0; g < a.NG; ++g) {
         const int64_t total = a.ntasks_dest * a.dpg;
-        std::vector<int> done((size_t)W * a.ntiles * W, 0), red((size_t)W * a.ntiles, 0);
+        std::vector<int> done((size_t)W * a.ntiles * W, 0);
         for (int64_t pos = 0; pos < total; ++pos) {
             const ra2a::RsTask t = ra2a::grs_group_task(a, g, pos);
             if (t.j < 0 || t.tile < 0 || t.tile >= a.ntiles || t.r < 0 || t.r >= W ||
                 t.j % a.NG != g)
                 return fail(RA2A_EINVAL, "group %d position %lld: task out of range", g, (long long)pos);
             if (t.j >= W) continue;  // padding of the last group
-            if (!t.reduce) {
-                int& d = done[((size_t)t.j * a.ntiles + t.tile) * W + t.r];
-                if (d++) return fail(RA2A_EINVAL, "GEMM task (j=%d, tile=%d, r=%d) twice", t.j, t.tile, t.r);
-            } else {
+            if (t.r == t.j)
                 for (int r = 0; r < W; ++r)
-                    if (!done[((size_t)t.j * a.ntiles + t.tile) * W + r])
-                        return fail(RA2A_EINVAL, "group %d position %lld: reduce of tile %d waits for "
-                                    "a GEMM task queued after it", g, (long long)pos, t.tile);
-                if (red[(size_t)t.j * a.ntiles + t.tile]++)
-                    return fail(RA2A_EINVAL, "reduce task twice");
-            }
+                    if (r != t.j && !done[((size_t)t.j * a.ntiles + t.tile) * W + r])
+                        return fail(RA2A_EINVAL, "group %d position %lld: the receiver's task of tile %d "
+                                    "waits for a task queued after it", g, (long long)pos, t.tile);
+            int& d = done[((size_t)t.j * a.ntiles + t.tile) * W + t.r];
+            if (d++) return fail(RA2A_EINVAL, "task (j=%d, tile=%d, r=%d) twice", t.j, t.tile, t.r);
         }
         for (int j = g; j < W; j += a.NG)
-            for (int t = 0; t < a.ntiles; ++t) {
-                if (!red[(size_t)j * a.ntiles + t]) return fail(RA2A_EINVAL, "a reduce task is missing");
+            for (int t = 0; t < a.ntiles; ++t)
                 for (int r = 0; r < W; ++r)
                     if (!done[((size_t)j * a.ntiles + t) * W + r])
-                        return fail(RA2A_EINVAL, "a GEMM task is missing");
-            }
+                        return fail(RA2A_EINVAL, "a task is missing");
     }
     if (tasks_per_group) *tasks_per_group = a.ntasks_dest * a.dpg;
     return ok();

@@ -1,8 +1,8 @@
 """Host checks of the GEMM+ReduceScatter work queues (no GPU): the kernel's own
-task decode (gemm_rs_geom.h) holds every (destination, tile, source) GEMM task
-and every reduce task once per queue, each reduce task after the W GEMM tasks it
-waits for (the deadlock-freedom argument), and the argument checks reject what
-the kernel cannot run."""
+task decode (gemm_rs_geom.h) holds every (destination, tile, source) task once
+per queue, and the receiver's task of each tile (source == destination, the one
+that waits and adds) after the W - 1 tasks it waits for (the deadlock-freedom
+argument); the argument checks reject what the kernel cannot run."""
 import pytest
 
 import moe_all2all_combine_amd as ra2a
@@ -29,10 +29,13 @@ def test_queues_hold_every_task_once_and_waits_point_backwards(W, m, K, N, num_x
     n = ra2a.debug_gemm_rs_plan(W, m, K, N, num_xcd)
     tiles = -(-(m // W) // 256) * -(-N // 256)
     groups = min(num_xcd, 8)
-    assert n == tiles * (W + 1) * -(-W // groups)
+    assert n == tiles * W * -(-W // groups)
 
 
 def test_sizes():
+    # the receive area holds W slots of one whole 256 x 256 tile per output tile
+    t, q, p = ra2a.gemm_rs_sizes(3, 300, 72, 202)
+    assert (t, q, p) == (1 * 1 * 3, ra2a.QUEUE_SLOTS, 3 * 1 * 256 * 256 * 4)
     t, q, p = ra2a.gemm_rs_sizes(8, 8192, 896, 4096)
     assert (t, q, p) == (4 * 16 * 8, ra2a.QUEUE_SLOTS, 8 * 1024 * 4096 * 4)
     t, q, p = ra2a.gemm_rs_sizes(8, 8192, 896, 4096, ra2a.RS_BF16_PARTIALS)
@@ -49,7 +52,7 @@ def test_unknown_flags_rejected():
 
 
 def test_f32_partials_hit_the_4gib_limit_first():
-    # 8 x 8000 x 24576 elements: 3.1 GB in bf16, 6.3 GB in fp32
+    # 8 slots of 32 x 96 tiles of 256 x 256: 3.2 GB in bf16, 6.4 GB in fp32
     ra2a.gemm_rs_sizes(8, 8 * 8000, 8, 24576, ra2a.RS_BF16_PARTIALS)
     with pytest.raises(ra2a.Ra2aError):
         ra2a.gemm_rs_sizes(8, 8 * 8000, 8, 24576)

@@ -74,7 +74,7 @@ EXACT = [
     # W, m, K, N
     (8, 512, 512, 512),
     (3, 300, 72, 200),
-    (3, 300, 72, 202),       # N not a multiple of 4: the reduce's one-column path
+    (3, 300, 72, 202),       # N not a multiple of 4: the epilogue's one-column path
     (3, 300, 72, 204),       # N a multiple of 4, not of 8: fp32 vectors, bf16 one column
     (1, 5, 8, 8),            # W = 1: a plain GEMM
     (16, 16 * 130, 64, 264),  # more ranks than XCDs, ragged tiles
@@ -182,4 +182,19 @@ def test_full_workload_sampled_rows(flags):
         ref = gemm.gemm_rs_rows_ref(a, bt, j, rows)
         err = check_outputs(a, bt, outs, flags, j, rows, ref)
         say(f"[full] rank {j} error measure {err:.3e}")
+        assert (sigs[j] == 1).all()
+
+
+@pytest.mark.parametrize("flags", [0, BF16P])
+def test_full_workload_integer_whole_output(flags):
+    """The workload's shape with inputs in {-1, 0, 1}: every fp32 accumulation and
+    sum is an exact integer (|value| <= 8 * 896), so the whole of every out_j
+    equals the oracle's fp64 sum rounded to bf16, bit for bit."""
+    wl = synthgen.GEMM_RS
+    say(f"[case] gemm_rs full {wl.name} integer flags={flags} (whole output)")
+    a, bt = synthgen.make_gemm_rs_inputs(wl, integer=True)
+    outs, sigs = run_gemm_rs(a, bt, flags)
+    ref = gemm.gemm_rs_ref(a, bt, round_partials=bool(flags & BF16P))
+    for j in range(wl.W):
+        np.testing.assert_array_equal(outs[j], gemm.f64_to_bf16_rne_bits(ref[j]), err_msg=f"rank {j}")
         assert (sigs[j] == 1).all()
