@@ -419,6 +419,61 @@ def put_calibration(heap, src_off, dst_off, nbytes, calls=8):
     torch.cuda.synchronize()
 
 
+def staged_ring_leg(steps, warmup, tile_s, ring):
+    """The staged mode on the EP-combine workload with a given tile_s and ring
+    depth (S-blocks), over the rotated buffer sets, for counter runs on how much
+    of the staging reaches HBM: one launch per step (reset launch + combine),
+    parity of the last step, then the put-kernel copy of one rank's bytes that
+    calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    import moe_all2all_combine_amd as ra2a
+    import synthgen
+
+    wl = synthgen.WORKLOADS[WORKLOAD]
+    W, S, H, D = wl.W, wl.S, wl.H, wl.D
+    proto = ra2a.PROTO_SET if wl.protocol == synthgen.PROTOCOL_SET else ra2a.PROTO_ADD
+    o = ra2a.Opts(tile_s=tile_s, tile_h=wl.tile_h, tile_d=wl.tile_d, protocol=proto,
+                  mode=ra2a.MODE_STAGED, ring=ring)
+    nb = wl.bytes_per_rank
+    nsig = sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
+    work = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, o)
+    heap = ra2a.SymmHeap(W, NSETS * (2 * nb + nsig * 128 + 4096) + work + (4 << 20))
+    try:
+        sets = [(heap.alloc(nb), heap.alloc(nb), heap.alloc(nsig * 128)) for _ in range(NSETS)]
+        for oi, _, _ in sets:
+            device_inputs(heap, oi, wl, torch.int16)
+        st = torch.cuda.current_stream()
+
+        def step(k):
+            oi, oo, osg = sets[k % NSETS]
+            ra2a.rev_all2all_ex(heap.ptr(oi), heap.ptr(oo), heap.ptr(osg), W, S, H, D, wl.dtype, o, st)
+
+        for k in range(warmup):
+            step(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for k in range(steps):
+            step(k)
+        e1.record(st)
+        torch.cuda.synchronize()
+        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
+        ms = e0.elapsed_time(e1) / steps
+        oi, oo, _ = sets[(steps - 1) % NSETS]
+        ok = all(torch.equal(heap.view(oo, (S, W, H, D), torch.int16, j)[:, r],
+                             heap.view(oi, (W, S, H, D), torch.int16, r)[j])
+                 for j in range(W) for r in range(W))
+        put_calibration(heap, sets[0][0], sets[0][1], nb)
+        gbs = wl.algorithmic_bytes / (ms * 1e-3) / 1e9
+        return {"workload": wl.name, "tile_s": tile_s, "ring": ring, "ring_bytes_per_slice": work,
+                "ms_per_step": round(ms, 5), "GB/s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / 8000, 2), "parity": ok,
+                "step": "reset launch + staged combine", "calibration_put_bytes": nb}
+    finally:
+        heap.close()
+
+
 def device_inputs(heap, off, wl, bits):
     """The workload's inputs generated on the device from its seed: the same
     distribution as synthgen's recipe (uniform(-1, 1) or normal(0, std), then
@@ -650,7 +705,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--legs", choices=["all", "main", "moe", "straggler", "ag_gemm", "gemm_rs",
-                                       "alltoallv"], default="all")
+                                       "alltoallv", "staged_ring"], default="all")
+    ap.add_argument("--tile-s", type=int, default=64, help="staged_ring leg: tokens per tile")
+    ap.add_argument("--ring", type=int, default=8, help="staged_ring leg: ring depth in S-blocks")
     ap.add_argument("--workload", default=WORKLOAD)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -679,6 +736,11 @@ def main():
     if args.legs == "moe":  # only the MoE-combine-shaped leg's default (for counter runs)
         torch.cuda.set_device(0)
         print(json.dumps({"moe_combine": moe_leg(args.steps, profile=True)}), flush=True)
+        return
+    if args.legs == "staged_ring":  # the staged mode at one ring size (for counter runs)
+        torch.cuda.set_device(0)
+        print(json.dumps({"staged_ring": staged_ring_leg(args.steps, args.warmup, args.tile_s, args.ring)}),
+              flush=True)
         return
     if args.legs == "straggler":
         torch.cuda.set_device(0)
