@@ -245,10 +245,32 @@ def ag_gemm_leg(steps):
         e1.record(st)
         torch.cuda.synchronize()
         lib_ms = e0.elapsed_time(e1) / steps
+
+        # the same with B given transposed (N x K, a linear layer's weight layout):
+        # the library multiplies by the transposed view, no copy
+        def lib_seq_bt():
+            for w in range(W):
+                gbuf[w * m:(w + 1) * m].copy_(shards_t[w])
+            torch.mm(gbuf, bt.t(), out=cl)
+
+        for _ in range(3):
+            lib_seq_bt()
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(steps):
+            lib_seq_bt()
+        e1.record(st)
+        torch.cuda.synchronize()
+        lib_bt_ms = e0.elapsed_time(e1) / steps
         return {"workload": g.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
                 "library_sequence": {"ms": round(lib_ms, 4),
                                      "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 1),
                                      "what": "W shard copies into G, then torch.matmul(G, B) (bf16)"},
+                "b_transposed": {"ms": round(bt_ms, 4),
+                                 "what": "one call with B passed as B^T (N x K): reset + persistent launch",
+                                 "library_sequence_ms": round(lib_bt_ms, 4),
+                                 "library_sequence": "W shard copies into G, then torch.mm(G, B^T viewed "
+                                                     "transposed) (bf16)"},
                 "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "calls": steps,
                 "note": "one call = B transposed into the workspace + signal reset + persistent launch",
                 "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
