@@ -165,6 +165,32 @@ def host_cpu():
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def steady_times(fns, steps, stream, warm=12, rounds=2):
+    """Milliseconds per call of each callable in `fns` (name -> fn) in steady state:
+    every one is first called `warm` times (first calls of a library pick and load
+    their kernels, and the clocks settle), then timed `rounds` times over `steps`
+    calls with HIP events on `stream`, the callables taking turns; the best round
+    counts."""
+    import torch
+
+    for fn in fns.values():
+        for _ in range(warm):
+            fn()
+    torch.cuda.synchronize()
+    best = {k: float("inf") for k in fns}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(rounds):
+        for k, fn in fns.items():
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best[k] = min(best[k], e0.elapsed_time(e1) / steps)
+    return best
+
+
 def ag_gemm_leg(steps):
     """The AllGather+GEMM workload (W=8 shards of 1024 x 7168 gathered, times a
     7168 x 4096 B; bf16 in, fp32 accumulation, bf16 out), for context: one call
@@ -194,39 +220,18 @@ def ag_gemm_leg(steps):
             ra2a.ag_gemm(heap.ptr(oa), heap.ptr(og), b.data_ptr(), c.data_ptr(), heap.ptr(osg),
                          W, 0, m, K, N, tr, 0, st)
 
-        for _ in range(3):
-            call()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            call()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
-        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
-        flops = 2.0 * W * m * N * K
-        tf = flops / (ms * 1e-3) / 1e12
-        # the persistent kernel alone, from HIP events on the launch stream around
-        # calls with B already transposed (one launch each, after a reset launch)
+        # with B already transposed (one launch each, after a reset launch): the
+        # persistent kernel's roofline
         bt = b.t().contiguous()
 
         def call_bt():
             ra2a.ag_gemm(heap.ptr(oa), heap.ptr(og), bt.data_ptr(), c.data_ptr(), heap.ptr(osg),
                          W, 0, m, K, N, tr, ra2a.AG_B_TRANSPOSED, st)
 
-        for _ in range(3):
-            call_bt()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(st)
-        for _ in range(steps):
-            call_bt()
-        e1.record(st)
-        torch.cuda.synchronize()
-        bt_ms = e0.elapsed_time(e1) / steps
-        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
-        ktf = flops / (bt_ms * 1e-3) / 1e12
         # the unfused library sequence on the same inputs: gather the shards into G
-        # (device copies), then torch.matmul(G, B)
+        # (device copies), then the library GEMM, with B as K x N and with B given
+        # transposed (N x K, a linear layer's weight layout: the library multiplies
+        # by the transposed view, no copy)
         shards_t = [heap.view(oa, (m, K), torch.bfloat16, w) for w in range(W)]
         gbuf = torch.empty(W * m, K, dtype=torch.bfloat16, device="cuda")
         cl = torch.empty(W * m, N, dtype=torch.bfloat16, device="cuda")
@@ -236,32 +241,17 @@ def ag_gemm_leg(steps):
                 gbuf[w * m:(w + 1) * m].copy_(shards_t[w])
             torch.matmul(gbuf, b, out=cl)
 
-        for _ in range(3):
-            lib_seq()
-        torch.cuda.synchronize()
-        e0.record(st)
-        for _ in range(steps):
-            lib_seq()
-        e1.record(st)
-        torch.cuda.synchronize()
-        lib_ms = e0.elapsed_time(e1) / steps
-
-        # the same with B given transposed (N x K, a linear layer's weight layout):
-        # the library multiplies by the transposed view, no copy
         def lib_seq_bt():
             for w in range(W):
                 gbuf[w * m:(w + 1) * m].copy_(shards_t[w])
             torch.mm(gbuf, bt.t(), out=cl)
 
-        for _ in range(3):
-            lib_seq_bt()
-        torch.cuda.synchronize()
-        e0.record(st)
-        for _ in range(steps):
-            lib_seq_bt()
-        e1.record(st)
-        torch.cuda.synchronize()
-        lib_bt_ms = e0.elapsed_time(e1) / steps
+        t = steady_times({"call": call, "call_bt": call_bt, "lib": lib_seq, "lib_bt": lib_seq_bt}, steps, st)
+        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
+        ms, bt_ms, lib_ms, lib_bt_ms = t["call"], t["call_bt"], t["lib"], t["lib_bt"]
+        flops = 2.0 * W * m * N * K
+        tf = flops / (ms * 1e-3) / 1e12
+        ktf = flops / (bt_ms * 1e-3) / 1e12
         return {"workload": g.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
                 "library_sequence": {"ms": round(lib_ms, 4),
                                      "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 1),
@@ -272,7 +262,9 @@ def ag_gemm_leg(steps):
                                  "library_sequence": "W shard copies into G, then torch.mm(G, B^T viewed "
                                                      "transposed) (bf16)"},
                 "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "calls": steps,
-                "note": "one call = B transposed into the workspace + signal reset + persistent launch",
+                "note": "one call = B transposed into the workspace + signal reset + persistent launch; "
+                        "steady state: every variant called 12 times first, then two rounds of "
+                        "timed calls taking turns, the best round (HIP events)",
                 "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -315,22 +307,6 @@ def gemm_rs_leg(steps):
             ra2a.gemm_rs(heap.ptr(oa), heap.ptr(ob), heap.ptr(op), heap.ptr(oo), heap.ptr(osg),
                          W, m, K, N, flags, st)
 
-        def timed(fn):
-            for _ in range(3):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(st)
-            for _ in range(steps):
-                fn()
-            e1.record(st)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / steps
-
-        ms = timed(call)
-        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
-        bf16p_ms = timed(lambda: call(ra2a.RS_BF16_PARTIALS))
-        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
         # the library sequence, on the same inputs
         x1 = [heap.view(oa, (m, K), torch.bfloat16, r) for r in range(W)]
         x2 = [heap.view(ob, (N, K), torch.bfloat16, r).t() for r in range(W)]
@@ -342,11 +318,15 @@ def gemm_rs_leg(steps):
                 torch.mm(x1[r], x2[r], out=part[r])
             torch.sum(part, dim=0, dtype=torch.float32, out=out)
 
-        lib_ms = timed(lib)
+        t = steady_times({"f32": call, "bf16": lambda: call(ra2a.RS_BF16_PARTIALS), "lib": lib}, steps, st)
+        assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
+        ms, bf16p_ms, lib_ms = t["f32"], t["bf16"], t["lib"]
         flops = 2.0 * W * m * N * K
         tf = flops / (ms * 1e-3) / 1e12
         return {"workload": g.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "calls": steps,
-                "note": "one call = signal reset + persistent launch; fp32 partials",
+                "note": "one call = signal reset + persistent launch; fp32 partials; steady state: "
+                        "every variant called 12 times first, then two rounds of timed calls taking "
+                        "turns, the best round (HIP events)",
                 "bf16_partials": {"ms": round(bf16p_ms, 4),
                                   "TFLOP/s": round(flops / (bf16p_ms * 1e-3) / 1e12, 1)},
                 "library_sequence": {"ms": round(lib_ms, 4),
