@@ -240,8 +240,10 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     } else if (p->TD == D) {
         // adjacent head blocks are contiguous: merge up to ~4 KiB runs, but keep at
         // least kMinPieces pieces, so that each of the (about 512) persistent
-        // workgroups gets two or more
-        constexpr int64_t kMinPieces = 1024;
+        // workgroups of the combine gets two or more, and each of the dispatch's one
+        // or more (measured on the W=8, S=512, H=16, D=128 bf16 shape: the dispatch's
+        // strided reads run best as whole 4 KiB runs, 51.1 against 53.0 us with 2 KiB)
+        const int64_t kMinPieces = p->inverse ? 512 : 1024;
         int64_t mh = std::max<int64_t>(1, std::min<int64_t>(p->nhb, 4096 / std::max<int64_t>(1, p->TH * D * e)));
         const int64_t per_mh = (int64_t)W * p->nbs * W;  // pieces per merged head block
         while (mh > 1 && per_mh * cdiv(p->nhb, mh) < kMinPieces) mh /= 2;
@@ -315,9 +317,6 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
         p->regionB = 0;
         p->ring_bytes = (int64_t)W * S * H * D * e;
     }
-    // measured on the W=8, S=512, H=16, D=128 bf16 shape: the combine runs best with
-    // two persistent workgroups per compute unit, the dispatch (strided reads,
-    // contiguous writes) with one (51.1 against 55.0 us)
     p->wg_per_cu = o->wg_per_cu;  // 0: resolved with the schedule at launch (prepare_pipelined)
     p->lookahead = o->lookahead;
     // the kernels index tiles, pieces and work items with 32-bit arithmetic
@@ -505,8 +504,9 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     *V = lowbit_vec(m);
     // Schedule of the direct modes: dynamic claims when the pieces (row units)
     // are many per compute unit, else static; workgroups per compute unit as
-    // asked, else one (dynamic) or two (static; the dispatch, whose reads are
-    // strided, one).  The staged modes keep two by default.
+    // asked, else one (dynamic) or two (static; on the W=8, S=512, H=16, D=128
+    // bf16 shape the dispatch measured 51.1 us with two against 53.1 with one).
+    // The staged modes keep two by default.
     int64_t work = 0;
     if (pl.rows) {
         a->nunits = ra2a::total_row_units(*a);
@@ -517,7 +517,7 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     }
     a->dyn = pl.direct && work >= kDynPiecesPerCu * (int64_t)ncu ? 1 : 0;
     int wpc = pl.wg_per_cu;
-    if (wpc <= 0) wpc = !pl.direct ? 2 : (a->dyn || pl.inverse) ? 1 : 2;
+    if (wpc <= 0) wpc = (pl.direct && a->dyn) ? 1 : 2;
     const int per_cu = std::max(1, std::min(blocks_per_cu, wpc));
     *grid = per_cu * ncu;
     if (pl.direct) *grid = (int)std::min<int64_t>(*grid, work);  // no workgroup without work

@@ -204,8 +204,16 @@ def test_opts_layout_matches_the_header(tmp_path):
 
 
 def test_dispatch_signal_slots():
-    """One slot per (signal tile, source) in every slice; no hand-back counters."""
+    """One slot per (signal tile, source) in every slice.  The dispatch merges all 16
+    heads into 4 KiB runs, so a piece (64 tokens) is 256 KiB and moves as two parts
+    of 32 tokens: one arrival counter per (S-block, source) in region B."""
     o = ra2a.Opts(direction=ra2a.DIR_DISPATCH)
+    assert ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", o) == (
+        8 * 16 * 8, 8 * 8, ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS)
+    p = ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16", o)
+    assert (p.piece_rows, p.pieces_per_tile) == (32, 2)
+    # with heads kept in 2 KiB runs the pieces are 128 KiB, one part each
+    o = ra2a.Opts(direction=ra2a.DIR_DISPATCH, head_merge=8)
     assert ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", o) == (
         8 * 16 * 8, 0, ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS)
 
