@@ -52,9 +52,10 @@ def log(msg):
 
 
 def kernel_source_hash():
-    """Hash of the sources the persistent kernel is compiled from."""
+    """Hash of the sources the persistent kernel is compiled from and of the host
+    code that plans its launches (piece shapes, schedule)."""
     h = hashlib.sha256()
-    for f in ("combine_kernels.hip", "combine_geom.h", "device.h", "common.h", "queue.h"):
+    for f in ("combine_kernels.hip", "combine_geom.h", "device.h", "common.h", "queue.h", "api.hip"):
         with open(os.path.join(ROOT, "moe_all2all_combine_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

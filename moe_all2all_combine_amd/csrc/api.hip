@@ -239,11 +239,14 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
         p->MH = std::min(o->head_merge, p->nhb);
     } else if (p->TD == D) {
         // adjacent head blocks are contiguous: merge up to ~4 KiB runs, but keep at
-        // least kMinPieces pieces, so that each of the (about 512) persistent
-        // workgroups of the combine gets two or more, and each of the dispatch's one
-        // or more (measured on the W=8, S=512, H=16, D=128 bf16 shape: the dispatch's
-        // strided reads run best as whole 4 KiB runs, 51.1 against 53.0 us with 2 KiB)
-        const int64_t kMinPieces = p->inverse ? 512 : 1024;
+        // least kMinPieces pieces.  The direct modes need one for each of the (about
+        // 512) persistent workgroups, since pieces above kPieceBytes move in parts
+        // (measured on the W=8, S=512, H=16, D=128 bf16 shape, whole 4 KiB runs in
+        // 256 KiB pieces of two parts against 2 KiB runs: the combine 48.2 against
+        // 48.9 us, the dispatch, whose reads are the strided side, 51.1 against 53.0
+        // us); the staged modes, whose pieces are not cut, two each.
+        const bool direct_mode = !(o->mode == RA2A_MODE_STAGED || p->bulk);
+        const int64_t kMinPieces = direct_mode ? 512 : 1024;
         int64_t mh = std::max<int64_t>(1, std::min<int64_t>(p->nhb, 4096 / std::max<int64_t>(1, p->TH * D * e)));
         const int64_t per_mh = (int64_t)W * p->nbs * W;  // pieces per merged head block
         while (mh > 1 && per_mh * cdiv(p->nhb, mh) < kMinPieces) mh /= 2;

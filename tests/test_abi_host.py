@@ -80,15 +80,21 @@ def test_signal_slots_and_workspace():
     Q = ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS  # control words: queue words, then reset flags
     # 64-token x 1-head x 128 tiles, ADD: one slot per (S-block, head) per slice
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
-    # direct mode (the default): one piece per tile and source (128 KiB), so no
-    # counters in region B
+    # direct mode (the default): 16 heads merged into 4 KiB runs, so a piece (one
+    # source's 64 tokens) is 256 KiB and moves as two parts of 32 tokens: one arrival
+    # counter per moved tile (S-block) in region B
+    assert (a, b, q) == (8 * 16, 8, Q)
+    p = ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16")
+    assert (p.head_merge, p.piece_rows, p.pieces_per_tile) == (16, 32, 2)
+    # with heads merged 8 at a time (2 KiB runs) a piece is 128 KiB, one part
+    a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", ra2a.Opts(head_merge=8))
     assert (a, b, q) == (8 * 16, 0, Q)
     # row units: region B holds one arrival counter per S-block
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", ra2a.Opts(mode=ra2a.MODE_ROWS))
     assert (a, b, q) == (8 * 16, 8, Q)
     # pieces of 16 tokens: 4 per tile and source, so one arrival counter per moved tile
     # (S-block, merged head block of 8)
-    a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", ra2a.Opts(piece_rows=16))
+    a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", ra2a.Opts(piece_rows=16, head_merge=8))
     assert (a, b, q) == (8 * 16, 8 * 2, Q)
     # staged: ring of 8 = every S-block; 256-B heads would merge 16 at a time into
     # 4 KiB runs, but that leaves only 512 pieces, so 8 at a time (1024 pieces):
