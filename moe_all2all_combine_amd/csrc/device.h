@@ -299,8 +299,9 @@ __device__ __forceinline__ void store_nt(T v, T* p) { __builtin_nontemporal_stor
 // Full rounds keep U vectors per thread in flight (all loads, then all
 // stores, no bounds checks so the values stay in registers); the remainder
 // goes one vector at a time.
-// NT: non-temporal loads and stores (streamed past the caches).
-template <int V, int U, bool NT = false>
+// NT: non-temporal loads (streamed past the caches); NTS: the same for the
+// stores (by default as NT).
+template <int V, int U, bool NT = false, bool NTS = NT>
 __device__ __forceinline__ void copy_flat(const uint8_t* __restrict__ src,
                                           uint8_t* __restrict__ dst, int64_t bytes, int64_t tid0,
                                           int64_t nthr) {
@@ -315,17 +316,18 @@ __device__ __forceinline__ void copy_flat(const uint8_t* __restrict__ src,
         for (int u = 0; u < U; ++u) v[u] = NT ? load_nt(s + idx + u * nthr) : s[idx + u * nthr];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (NT)
+            if (NTS)
                 store_nt(v[u], d + idx + u * nthr);
             else
                 d[idx + u * nthr] = v[u];
         }
     }
     for (; idx < total; idx += nthr) {
-        if (NT)
-            store_nt(load_nt(s + idx), d + idx);
+        const T v = NT ? load_nt(s + idx) : s[idx];
+        if (NTS)
+            store_nt(v, d + idx);
         else
-            d[idx] = s[idx];
+            d[idx] = v;
     }
 }
 
