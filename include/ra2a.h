@@ -307,7 +307,9 @@ typedef struct ra2a_opts {
     int32_t head_merge;       /* signal tiles of adjacent head blocks moved together by one
                                * piece / unit (each keeps its own signal); default, when a
                                * tile spans all of D: runs of up to 4 KiB, halved until the
-                               * combine has at least 1024 pieces */
+                               * call has at least 512 pieces (direct modes; their pieces
+                               * above 128 KiB then move in parts, see piece_rows) or 1024
+                               * (staged modes) */
     int32_t separate_reset;   /* 1: zero the signals with a launch of their own before the
                                * combine's, also in direct mode (0, the default: direct
                                * mode zeroes them inside the combine launch) */
