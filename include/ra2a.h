@@ -228,8 +228,9 @@ typedef struct ra2a_opts {
                          * (source r, tile), set to 1; the consumer waits for each piece. */
     int32_t ring;       /* staged mode: staging ring depth in S-blocks (default 8; >= the
                          * number of S-blocks means no slot is reused) */
-    int32_t wg_per_cu;  /* persistent workgroups per compute unit (default 2 for the
-                         * combine, 1 for the dispatch; capped at the kernel's occupancy) */
+    int32_t wg_per_cu;  /* persistent workgroups per compute unit (default 2, or 1 when
+                         * the direct modes claim their pieces dynamically -- 8 or more
+                         * per compute unit; capped at the kernel's occupancy) */
     int32_t lookahead;  /* staged mode: tiles whose pieces are queued ahead of a tile's
                          * consumer work (0: default -- half of what the ring allows, or
                          * every piece first when no slot is reused; -1: every piece
