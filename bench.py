@@ -192,6 +192,32 @@ def steady_times(fns, steps, stream, warm=12, rounds=2):
     return best
 
 
+def cold_times(fns, calls, stream, flush_bytes=512 << 20):
+    """Milliseconds per call of each callable with the Infinity Cache cold: before
+    every call a copy of `flush_bytes` (twice the 256 MB cache) evicts what the
+    previous call left there; HIP events around each call alone, the mean over
+    `calls` calls (after one untimed call each)."""
+    import torch
+
+    a = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for k, fn in fns.items():
+        fn()
+        tot = 0.0
+        for _ in range(calls):
+            b.copy_(a)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            tot += e0.elapsed_time(e1)
+        out[k] = tot / calls
+    del a, b
+    return out
+
+
 def ag_gemm_leg(steps):
     """The AllGather+GEMM workload (W=8 shards of 1024 x 7168 gathered, times a
     7168 x 4096 B; bf16 in, fp32 accumulation, bf16 out), for context: one call
@@ -248,6 +274,7 @@ def ag_gemm_leg(steps):
             torch.mm(gbuf, bt.t(), out=cl)
 
         t = steady_times({"call": call, "call_bt": call_bt, "lib": lib_seq, "lib_bt": lib_seq_bt}, steps, st)
+        cold = cold_times({"call_bt": call_bt, "lib_bt": lib_seq_bt}, 10, st)
         assert ra2a.check(heap.handle) == ra2a.OK, ra2a.last_error()
         ms, bt_ms, lib_ms, lib_bt_ms = t["call"], t["call_bt"], t["lib"], t["lib_bt"]
         flops = 2.0 * W * m * N * K
@@ -261,7 +288,11 @@ def ag_gemm_leg(steps):
                                  "what": "one call with B passed as B^T (N x K): reset + persistent launch",
                                  "library_sequence_ms": round(lib_bt_ms, 4),
                                  "library_sequence": "W shard copies into G, then torch.mm(G, B^T viewed "
-                                                     "transposed) (bf16)"},
+                                                     "transposed) (bf16)",
+                                 "cold": {"ms": round(cold["call_bt"], 4),
+                                          "library_sequence_ms": round(cold["lib_bt"], 4),
+                                          "what": "each call after a 512 MiB copy that evicts the "
+                                                  "Infinity Cache (events around each call)"}},
                 "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "calls": steps,
                 "note": "one call = B transposed into the workspace + signal reset + persistent launch; "
                         "steady state: every variant called 12 times first, then two rounds of "
