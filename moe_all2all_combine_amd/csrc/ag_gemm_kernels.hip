@@ -31,29 +31,30 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---- the matrix-core tile ----------------------------------------------------
 //
-// One output tile of kTileM x kTileN = 256 x 256 per workgroup of four waves, one
-// per SIMD; wave (wm, wn) = (wave / 2, wave mod 2) owns its 128 x 128 quarter as
-// 8 x 8 blocks of v_mfma_f32_16x16x32_bf16.  The operands are given to the
+// One output tile of kTileM x kTileN = 256 x 256 per workgroup of eight waves, two
+// per SIMD; wave (wm, wn) = (wave / 4, wave mod 4) owns 128 rows x 64 columns as
+// 8 x 4 blocks of v_mfma_f32_16x16x32_bf16.  The operands are given to the
 // instruction swapped (B^T block first), so that lane l of block (x, y) holds
 // rows 16 x + l % 16 and four consecutive columns 16 y + 4 (l / 16) .. + 3 of the
-// wave's quarter: the epilogue writes 8 (bf16) or 16 (fp32) contiguous bytes.
+// wave's part: the epilogue writes 8 (bf16) or 16 (fp32) contiguous bytes.
 // (Lane layout of the instruction: A operand row l % 16, k 8 (l / 16) .. + 7; B
 // operand column l % 16, the same k; result column l % 16, rows 4 (l / 16) .. +3 --
 // checked on the device with exact integer inputs before this tile was written.)
-// Measured on the 8192 x 4096 x 7168 product alone: 0.416 ms with this tile, the
-// MFMA pipes busy 65 % of the cycles at the 1.68 GHz the device clocks under this
-// load (counters), against 0.46 ms for the previous eight-wave 32 x 32 x 16 tile.
+// Measured on the product alone, in one box call: 8192 x 4096 x 7168 in 0.418-0.423
+// ms against 0.428-0.436 ms with four waves of 128 x 128 (one per SIMD), and
+// 8192 x 4096 x 896 in 0.065-0.066 against 0.077-0.078 ms: with two waves per SIMD
+// one wave's prologue, waits and epilogue overlap the other's matrix work.
 constexpr int kTileM = kGemmBM;
 constexpr int kTileN = kGemmBN;
-constexpr int kGemmThreads = 256;  // four waves
+constexpr int kGemmThreads = 512;  // eight waves
 constexpr int kGemmWgPerCu = 1;
 constexpr int kStageK = 64;        // k per pipeline stage: 128 bytes, one cache line per row
 constexpr int kSlotA = kTileM * kStageK * 2;   // bytes of A in a stage slot
 constexpr int kSlotB = kTileN * kStageK * 2;
 constexpr int kSlot = kSlotA + kSlotB;         // 64 KiB; the LDS ring holds two
-constexpr int kLoadsPerStage = 16;             // 1 KiB LDS loads per wave per stage (8 of A, 8 of B^T)
-constexpr int kReadsPerStep = 16;              // 16-byte fragment reads per wave per k32 step
-constexpr int kMfmaPerStep = 64;               // 8 x 8 blocks
+constexpr int kLoadsPerStage = 8;              // 1 KiB LDS loads per wave per stage (4 of A, 4 of B^T)
+constexpr int kReadsPerStep = 12;              // 16-byte fragment reads per wave per k32 step (8 A, 4 B^T)
+constexpr int kMfmaPerStep = 32;               // 8 x 4 blocks
 constexpr int kEpiPitch = kTileN * 2 + 16;     // bf16 output tile staged in LDS, bytes per row
 constexpr int kLdsBytes = kTileM * kEpiPitch;  // the larger of the two uses
 static_assert(2 * kSlot <= kLdsBytes, "LDS array");
@@ -93,17 +94,17 @@ __device__ __forceinline__ LoadLane load_lane(int64_t K) {
     return ll;
 }
 
-// Load P (0 .. 15) of this wave's share of a stage (k0 .. k0 + 63): loads 0-7 bring
-// A rows 64 w + 8 P .., loads 8-15 B^T rows 64 w + 8 (P - 8) .. into the slot (A,
-// then B^T).  Row r = 64 w + 8 P + l / 8 has (r >> 1) & 7 = (l >> 4) ^ 4 (P & 1).
+// Load P (0 .. 7) of this wave's share of a stage (k0 .. k0 + 63): loads 0-3 bring
+// A rows 32 w + 8 P .., loads 4-7 B^T rows 32 w + 8 (P - 4) .. into the slot (A,
+// then B^T).  Row r = 32 w + 8 P + l / 8 has (r >> 1) & 7 = (l >> 4) ^ 4 (P & 1).
 // Rows past the operand's buffer (the descriptor's range), k past K, and a stage
 // past the last (`live` false) read as zero: no branch around the load.
 template <int P>
 __device__ __forceinline__ void stage_load_part(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                                 char* slot, int w, uint32_t K, uint32_t k0,
                                                 const LoadLane& ll, bool live) {
-    constexpr bool kA = P < 8;
-    const int rbase = 64 * w + 8 * (kA ? P : P - 8);
+    constexpr bool kA = P < 4;
+    const int rbase = 32 * w + 8 * (kA ? P : P - 4);
     const int chunk = ll.chunk ^ (4 * (P & 1));
     const uint32_t k = k0 + 8u * (uint32_t)chunk;
     const uint32_t off = (live && k < K) ? (uint32_t)rbase * K * 2u + ll.row_off + k * 2u : kOutOfRange;
@@ -132,9 +133,9 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
     return v;
 }
 
-// A wave's fragments of one k32 step: 8 A blocks (rows 16 x ..) and 8 B^T blocks.
+// A wave's fragments of one k32 step: 8 A blocks (rows 16 x ..) and 4 B^T blocks.
 struct Frags {
-    bf16x8 a[8], b[8];
+    bf16x8 a[8], b[4];
 };
 
 // Wait until this wave's LDS reads are in; the fragments are tied to the wait so
@@ -143,8 +144,7 @@ __device__ __forceinline__ void lds_wait(Frags& f) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     asm volatile("" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.a[4]), "+v"(f.a[5]),
                       "+v"(f.a[6]), "+v"(f.a[7]));
-    asm volatile("" : "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]), "+v"(f.b[4]), "+v"(f.b[5]),
-                      "+v"(f.b[6]), "+v"(f.b[7]));
+    asm volatile("" : "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
 }
 
 // LDS byte address of a pointer into the LDS array.
@@ -152,7 +152,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Fragment read I (0-7: A block I, 8-15: B^T block I - 8); blocks are 16 rows =
+// Fragment read I (0-7: A block I, 8-11: B^T block I - 8); blocks are 16 rows =
 // 2 KiB apart, and the lane's swizzled chunk is the same in every block.
 template <int I>
 __device__ __forceinline__ void read_frag(Frags& f, uint32_t a_addr, uint32_t b_addr) {
@@ -170,15 +170,15 @@ __device__ __forceinline__ void read_frags_seq(Frags& f, uint32_t a, uint32_t b,
 __device__ __forceinline__ void sb() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int I>
-__device__ __forceinline__ void mma_one(f32x4 (&acc)[8][8], const Frags& f) {
-    constexpr int x = I / 8, y = I % 8;
+__device__ __forceinline__ void mma_one(f32x4 (&acc)[8][4], const Frags& f) {
+    constexpr int x = I / 4, y = I % 4;
     acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[y], f.a[x], acc[x][y], 0, 0, 0);
 }
 
-// A k32 step: its 64 MFMAs with the other work of the step between them -- the 16
-// fragment reads of the next step over the first 32 MFMAs (they land well before
-// the step ends), and, in the second step of a stage, the 16 loads refilling the
-// slot just freed over the last 32 (measured best of the placements tried).
+// A k32 step: its 32 MFMAs with the other work of the step between them -- the 12
+// fragment reads of the next step on every second of the first 24 MFMAs (they land
+// well before the step ends), and, in the second step of a stage, the 8 loads
+// refilling the slot just freed on every second of the last 16.
 struct StepCtx {
     Frags* next;
     uint32_t na, nb;                      // the next step's fragment addresses
@@ -198,7 +198,7 @@ __device__ __forceinline__ void step_op(const StepCtx& c) {
             sb();
         }
     } else if constexpr (REFILL) {
-        if constexpr (32 + (J - kReadsPerStep) * 2 == I) {
+        if constexpr (16 + (J - kReadsPerStep) * 2 == I) {
             stage_load_part<J - kReadsPerStep>(c.ra, c.rb, c.slot, c.w, c.K, c.k0, *c.ll, c.live);
             sb();
         }
@@ -209,7 +209,7 @@ __device__ __forceinline__ void step_ops(const StepCtx& c, std::integer_sequence
     (step_op<REFILL, I, Js>(c), ...);
 }
 template <bool REFILL, int... Is>
-__device__ __forceinline__ void k32_step(f32x4 (&acc)[8][8], const Frags& f, const StepCtx& c,
+__device__ __forceinline__ void k32_step(f32x4 (&acc)[8][4], const Frags& f, const StepCtx& c,
                                          std::integer_sequence<int, Is...>) {
     ((mma_one<Is>(acc, f), sb(),
       step_ops<REFILL, Is>(c, std::make_integer_sequence<int, kReadsPerStep + kLoadsPerStage>{})),
@@ -223,7 +223,7 @@ __device__ __forceinline__ void k32_step(f32x4 (&acc)[8][8], const Frags& f, con
 // holds in acc[x][y] the rows 128 wm + 16 x + l % 16, columns 128 wn + 16 y +
 // 4 (l / 16) .. + 3.  `lds` is the workgroup's LDS array (kLdsBytes); on return
 // every wave is out of it and no load is in flight.
-__device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][8], const uint16_t* a_rows, int rows_valid,
+__device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][4], const uint16_t* a_rows, int rows_valid,
                                               const uint16_t* bt_rows, int cols_valid, int64_t K64,
                                               char* lds) {
     // K opaque per tile: nothing derived from it is hoisted out of the persistent
@@ -234,11 +234,11 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][8], const uint16_t
     const __amdgpu_buffer_rsrc_t rb = make_rsrc_uniform(bt_rows, (uint32_t)cols_valid * K * 2u);
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int l = (int)threadIdx.x & 63;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w >> 2, wn = w & 3;
 #pragma unroll
     for (int x = 0; x < 8; ++x)
 #pragma unroll
-        for (int y = 0; y < 8; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nk = (int)((K + kStageK - 1) / kStageK);
     const LoadLane ll = load_lane(K64);
     char* const slot0 = lds;
@@ -259,7 +259,7 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][8], const uint16_t
     // l / 16 (+ 4 in the second k32 step: position ^ 4, byte ^ 64).
     const uint32_t sw = (uint32_t)((l >> 4) ^ ((l & 15) >> 1)) * 16u;
     const uint32_t oa = (uint32_t)((128 * wm + (l & 15)) * 128) + sw;
-    const uint32_t ob = (uint32_t)kSlotA + (uint32_t)((128 * wn + (l & 15)) * 128) + sw;
+    const uint32_t ob = (uint32_t)kSlotA + (uint32_t)((64 * wn + (l & 15)) * 128) + sw;
     const uint32_t base0 = lds_addr(slot0);
     Frags f0, f1;
     read_frags_seq(f0, base0 + oa, base0 + ob, std::make_integer_sequence<int, kReadsPerStep>{});
@@ -299,12 +299,12 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][8], const uint16_t
 // (nearest even), stored at c (row stride ldc elements) through the LDS; with
 // NTOUT the 16-byte pieces are stored non-temporally.
 template <bool NTOUT>
-__device__ __forceinline__ void epi_bf16(const f32x4 (&acc)[8][8], int rows_valid, int cols_valid, void* c,
+__device__ __forceinline__ void epi_bf16(const f32x4 (&acc)[8][4], int rows_valid, int cols_valid, void* c,
                                          int64_t ldc, char* lds) {
     asm volatile("" : "+s"(ldc));
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int l = (int)threadIdx.x & 63;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w >> 2, wn = w & 3;
     // (The empty asm makes the output pointer opaque here, so that the epilogue's
     // addresses are not hoisted above the main loop and kept alive across it.)
     uint64_t cbase = reinterpret_cast<uint64_t>(c);
@@ -314,9 +314,9 @@ __device__ __forceinline__ void epi_bf16(const f32x4 (&acc)[8][8], int rows_vali
 #pragma unroll
     for (int x = 0; x < 8; ++x)
 #pragma unroll
-        for (int y = 0; y < 8; ++y) {
+        for (int y = 0; y < 4; ++y) {
             const int row = 128 * wm + 16 * x + (l & 15);
-            const int col = 128 * wn + 16 * y + 4 * (l >> 4);
+            const int col = 64 * wn + 16 * y + 4 * (l >> 4);
             u32x2 v;
             v[0] = bf16_rne(acc[x][y][0]) | (bf16_rne(acc[x][y][1]) << 16);
             v[1] = bf16_rne(acc[x][y][2]) | (bf16_rne(acc[x][y][3]) << 16);
@@ -350,7 +350,7 @@ __device__ __forceinline__ void epi_bf16(const f32x4 (&acc)[8][8], int rows_vali
 template <bool NTOUT>
 __device__ __forceinline__ void gemm_tile(const uint16_t* a_rows, int rows_valid, const uint16_t* bt_rows,
                                           int cols_valid, int64_t K, void* c, int64_t ldc, char* lds) {
-    f32x4 acc[8][8];
+    f32x4 acc[8][4];
     gemm_mainloop(acc, a_rows, rows_valid, bt_rows, cols_valid, K, lds);
     epi_bf16<NTOUT>(acc, rows_valid, cols_valid, c, ldc, lds);
 }
@@ -469,26 +469,26 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) ag_gemm_kernel(AgG
 // into the L2 it reads through.
 
 // A partial tile in the lanes' own order: thread t's 16-byte piece number b --
-// block (x, y), b = 8 x + y, as fp32; or blocks (x, 2 p) and (x, 2 p + 1), b =
-// 4 x + p, as bf16 rounded to nearest even -- at byte 4096 b + 16 t of the
-// tile's slot.  Stored non-temporally: each partial is read once, by the
+// block (x, y), b = 4 x + y, as fp32; or blocks (x, 2 p) and (x, 2 p + 1), b =
+// 2 x + p, as bf16 rounded to nearest even -- at byte 8192 b + 16 t of the
+// tile's slot (512 threads).  Stored non-temporally: each partial is read once, by the
 // receiver's task.
 constexpr int kRsPieceBytes = kGemmThreads * 16;
 
 __device__ __forceinline__ u32x4 bits(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
 
 template <bool F32P>
-__device__ __forceinline__ void rs_store_partial(const f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t rp,
+__device__ __forceinline__ void rs_store_partial(const f32x4 (&acc)[8][4], __amdgpu_buffer_rsrc_t rp,
                                                  uint32_t slot) {
     const uint32_t off = slot + threadIdx.x * 16u;
     if constexpr (F32P) {
 #pragma unroll
-        for (int b = 0; b < 64; ++b)
-            BufStore<16, kPolicyNt>::go(bits(acc[b >> 3][b & 7]), rp, off + (uint32_t)(b * kRsPieceBytes));
+        for (int b = 0; b < 32; ++b)
+            BufStore<16, kPolicyNt>::go(bits(acc[b >> 2][b & 3]), rp, off + (uint32_t)(b * kRsPieceBytes));
     } else {
 #pragma unroll
-        for (int b = 0; b < 32; ++b) {
-            const f32x4 u = acc[b >> 2][2 * (b & 3)], v = acc[b >> 2][2 * (b & 3) + 1];
+        for (int b = 0; b < 16; ++b) {
+            const f32x4 u = acc[b >> 1][2 * (b & 1)], v = acc[b >> 1][2 * (b & 1) + 1];
             const u32x4 o = {bf16_rne(u[0]) | (bf16_rne(u[1]) << 16), bf16_rne(u[2]) | (bf16_rne(u[3]) << 16),
                              bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
             BufStore<16, kPolicyNt>::go(o, rp, off + (uint32_t)(b * kRsPieceBytes));
@@ -523,12 +523,12 @@ __device__ __forceinline__ f32x4 rs_unpack_bf16(u32x4 x, int h) {
 // past W, or j itself, is sent out of range and reads zero without touching
 // memory; a select, not a branch, drops it, so no load waits behind a test).
 constexpr int kFoldSrc = 8;
-constexpr int kFoldPieces = 4;
+constexpr int kFoldPieces = 2;
 
 // Pieces P0 .. P0 + kFoldPieces - 1 (a template parameter, so that every index
 // into acc is a constant and acc stays in registers).
 template <bool F32P, int P0>
-__device__ __forceinline__ void rs_fold_group(f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
+__device__ __forceinline__ void rs_fold_group(f32x4 (&acc)[8][4], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
                                               uint32_t src_stride, int j, int W) {
     constexpr int kBlk = F32P ? 1 : 2;  // blocks per piece
     using Load = BufLoad<16, kPolicySc1 | kPolicyNt>;
@@ -554,8 +554,8 @@ __device__ __forceinline__ void rs_fold_group(f32x4 (&acc)[8][8], __amdgpu_buffe
             for (int q = 0; q < kFoldPieces; ++q)
 #pragma unroll
                 for (int h = 0; h < kBlk; ++h) {
-                    const int b = (P0 + q) * kBlk + h;  // block 8 x + y
-                    const f32x4 v = src == j ? rs_own<F32P>(acc[b >> 3][b & 7])
+                    const int b = (P0 + q) * kBlk + h;  // block 4 x + y
+                    const f32x4 v = src == j ? rs_own<F32P>(acc[b >> 2][b & 3])
                                              : (F32P ? __builtin_bit_cast(f32x4, x[g][q]) : rs_unpack_bf16(x[g][q], h));
                     f32x4& t = s[q * kBlk + h];
                     t = src < W ? t + v : t;
@@ -567,20 +567,20 @@ __device__ __forceinline__ void rs_fold_group(f32x4 (&acc)[8][8], __amdgpu_buffe
 #pragma unroll
         for (int h = 0; h < kBlk; ++h) {
             const int b = (P0 + q) * kBlk + h;
-            acc[b >> 3][b & 7] = s[q * kBlk + h];
+            acc[b >> 2][b & 3] = s[q * kBlk + h];
         }
 }
 
 template <bool F32P, int... Gs>
-__device__ __forceinline__ void rs_fold_groups(f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
+__device__ __forceinline__ void rs_fold_groups(f32x4 (&acc)[8][4], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
                                                uint32_t src_stride, int j, int W, std::integer_sequence<int, Gs...>) {
     (rs_fold_group<F32P, Gs * kFoldPieces>(acc, rp, tile_off, src_stride, j, W), ...);
 }
 
 template <bool F32P>
-__device__ __forceinline__ void rs_fold(f32x4 (&acc)[8][8], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
+__device__ __forceinline__ void rs_fold(f32x4 (&acc)[8][4], __amdgpu_buffer_rsrc_t rp, uint32_t tile_off,
                                         uint32_t src_stride, int j, int W) {
-    constexpr int kPieces = F32P ? 64 : 32;
+    constexpr int kPieces = F32P ? 32 : 16;
     rs_fold_groups<F32P>(acc, rp, tile_off, src_stride, j, W,
                          std::make_integer_sequence<int, kPieces / kFoldPieces>{});
 }
@@ -631,7 +631,7 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
                 const uint16_t* x1 = reinterpret_cast<const uint16_t*>(src_slice + a.a_off) +
                                      ((int64_t)t.j * a.mj + row0) * a.K;
                 const uint16_t* x2t = reinterpret_cast<const uint16_t*>(src_slice + a.bt_off) + col0 * a.K;
-                f32x4 acc[8][8];
+                f32x4 acc[8][4];
                 gemm_mainloop(acc, x1, rows, x2t, cols, a.K, lds);
                 const __amdgpu_buffer_rsrc_t rp = make_rsrc_uniform(dst_slice + a.p_off, area);
                 if (t.r != t.j) {

@@ -40,8 +40,8 @@ constexpr int kRsTileN = kGemmBN;
 constexpr int kRsBlock = 32;
 
 // A partial tile in the receive area: the 256 x 256 accumulators in the lanes'
-// own order (fp32: [8 x 8 blocks][256 threads][4 values]; bf16: [8 x 4 block
-// pairs][256 threads][2 x 4 values]), so that every store and load of a wave is
+// own order (fp32: [8 x 4 blocks][512 threads][4 values]; bf16: [8 x 2 block
+// pairs][512 threads][2 x 4 values]), so that every store and load of a wave is
 // 1 KiB contiguous and no LDS pass is needed on either side.  Rows and columns
 // past the matrix hold zeros.
 constexpr int64_t kRsPartElems = (int64_t)kRsTileM * kRsTileN;
