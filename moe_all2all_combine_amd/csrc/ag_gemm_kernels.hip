@@ -522,8 +522,9 @@ __device__ __forceinline__ f32x4 rs_unpack_bf16(u32x4 x, int h) {
 // kFoldPieces pieces of up to kFoldSrc sources are in flight together (a source
 // past W, or j itself, is sent out of range and reads zero without touching
 // memory; a select, not a branch, drops it, so no load waits behind a test).
-constexpr int kFoldSrc = 8;
-constexpr int kFoldPieces = 2;
+// (4 sources x 4 pieces measured 1.5-2.5 % faster than 8 x 2 and 8 x 1, in one box call)
+constexpr int kFoldSrc = 4;
+constexpr int kFoldPieces = 4;
 
 // Pieces P0 .. P0 + kFoldPieces - 1 (a template parameter, so that every index
 // into acc is a constant and acc stays in registers).
