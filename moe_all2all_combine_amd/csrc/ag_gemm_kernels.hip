@@ -223,9 +223,14 @@ __device__ __forceinline__ void k32_step(f32x4 (&acc)[8][4], const Frags& f, con
 // holds in acc[x][y] the rows 128 wm + 16 x + l % 16, columns 128 wn + 16 y +
 // 4 (l / 16) .. + 3.  `lds` is the workgroup's LDS array (kLdsBytes); on return
 // every wave is out of it and no load is in flight.
+//
+// Stores the caller issued before are not waited for first: the first stage's wait
+// (vector memory operations complete in issue order) and barrier cover them, after
+// which, if `pend` is set, wave 0 publishes them (with `agent`, an L2 write-back
+// first) by setting the signal at `pend` to 1.
 __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][4], const uint16_t* a_rows, int rows_valid,
                                               const uint16_t* bt_rows, int cols_valid, int64_t K64,
-                                              char* lds) {
+                                              char* lds, uint64_t* pend = nullptr, bool agent = false) {
     // K opaque per tile: nothing derived from it is hoisted out of the persistent
     // task loop and kept alive across tiles.
     asm volatile("" : "+s"(K64));
@@ -243,7 +248,6 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][4], const uint16_t
     const LoadLane ll = load_lane(K64);
     char* const slot0 = lds;
     char* const slot1 = lds + kSlot;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only this tile's LDS loads in flight below
     // Stage s lives in slot s mod 2; both are loaded up front (the second only if
     // its stage exists), and stage 0 lands before the first reads.
     constexpr auto kParts = std::make_integer_sequence<int, kLoadsPerStage>{};
@@ -255,6 +259,10 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[8][4], const uint16_t
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __builtin_amdgcn_s_barrier();
+    if (pend != nullptr) {  // every wave's earlier stores are complete
+        if (agent && threadIdx.x < 64) fence_release_agent();
+        if (threadIdx.x == 0) sig_update(pend, 1ull, kSigSet);
+    }
     // Fragment offsets inside a slot: row 128 wm + l % 16 (then + 16 x), logical chunk
     // l / 16 (+ 4 in the second k32 step: position ^ 4, byte ^ 64).
     const uint32_t sw = (uint32_t)((l >> 4) ^ ((l & 15) >> 1)) * 16u;
@@ -601,6 +609,10 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
     const uint32_t area = (uint32_t)grs_part_offset(a, a.W, 0);
     QueueClaim qc;
     int k = 0;
+    // The (tile, r) signal of the partial this workgroup stored last, not set yet: its
+    // stores drain under the next task's first loads, whose wait covers them
+    // (gemm_mainloop sets it), or at the latest before the workgroup leaves a queue.
+    uint64_t* pend = nullptr;
     for (int gi = 0; gi < a.NG; ++gi) {
         const int g = (home + gi) % a.NG;
         if (threadIdx.x == 0) lds_pos[k & 1] = queue_first<kOwned>(qw, g, gi, xcc, qc);
@@ -612,6 +624,11 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
             // the group's queue: dpg destinations of ntasks_dest each (the last
             // group may have fewer real destinations; their tasks are skipped)
             if (pos >= total) {
+                if (pend != nullptr) {
+                    group_release<SYNC>();
+                    if (threadIdx.x == 0) sig_update(pend, 1ull, kSigSet);
+                    pend = nullptr;
+                }
                 if (threadIdx.x == 0) queue_drained(qw, g, pos, total, qc);
                 break;
             }
@@ -633,14 +650,14 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
                                      ((int64_t)t.j * a.mj + row0) * a.K;
                 const uint16_t* x2t = reinterpret_cast<const uint16_t*>(src_slice + a.bt_off) + col0 * a.K;
                 f32x4 acc[8][4];
-                gemm_mainloop(acc, x1, rows, x2t, cols, a.K, lds);
+                gemm_mainloop(acc, x1, rows, x2t, cols, a.K, lds, pend, SYNC == kSyncAgent);
+                pend = nullptr;
                 const __amdgpu_buffer_rsrc_t rp = make_rsrc_uniform(dst_slice + a.p_off, area);
                 if (t.r != t.j) {
-                    // into slot r of j's receive area, then the (tile, r) signal
+                    // into slot r of j's receive area; the (tile, r) signal follows once
+                    // the stores have drained
                     rs_store_partial<F32P>(acc, rp, (uint32_t)grs_part_offset(a, t.r, t.tile));
-                    group_release<SYNC>();
-                    if (threadIdx.x == 0)
-                        sig_update(sig + grs_sig_slot(a, t.tile, t.r) * kSigStrideU64, 1ull, kSigSet);
+                    pend = sig + grs_sig_slot(a, t.tile, t.r) * kSigStrideU64;
                 } else {
                     // the other sources' partials: signals (tile, 0 .. j-1), (tile, j+1 .. W-1)
                     uint64_t* const s0 = sig + grs_sig_slot(a, t.tile, 0) * kSigStrideU64;
