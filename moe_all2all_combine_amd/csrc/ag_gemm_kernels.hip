@@ -669,9 +669,8 @@ __global__ void __launch_bounds__(kGemmThreads, kGemmWgPerCu) gemm_rs_kernel(Gem
                         return;
                     rs_fold<F32P>(acc, rp, (uint32_t)grs_part_offset(a, 0, t.tile), src_stride, t.j, a.W);
                     epi_bf16<true>(acc, rows, cols, dst_slice + a.out_off + (row0 * a.N + col0) * 2, a.N, lds);
-                    group_release<SYNC>();
-                    if (threadIdx.x == 0)
-                        sig_update(sig + grs_sig_slot(a, t.tile, t.j) * kSigStrideU64, 1ull, kSigSet);
+                    // (tile, j): the tile of out_j is complete, once its stores have drained
+                    pend = sig + grs_sig_slot(a, t.tile, t.j) * kSigStrideU64;
                 }
             }
             if (threadIdx.x == 0) lds_pos[k & 1] = (int64_t)nxt;
