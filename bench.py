@@ -363,7 +363,10 @@ def gemm_rs_leg(steps):
                                   "TFLOP/s": round(flops / (bf16p_ms * 1e-3) / 1e12, 1)},
                 "library_sequence": {"ms": round(lib_ms, 4),
                                      "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 1),
-                                     "what": "W torch.mm (bf16 out) + fp32 sum over sources"},
+                                     "what": "W torch.mm (bf16 out) + fp32 sum over sources",
+                                     "same_arithmetic_as": "bf16_partials (each rank's product "
+                                                           "rounded to bf16, summed in fp32)",
+                                     "bf16_partials_over_library": round(bf16p_ms / lib_ms, 4)},
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
