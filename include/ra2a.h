@@ -519,8 +519,10 @@ int ra2a_debug_ag_gemm_plan(int W, int rank, int64_t m_local, int64_t K, int64_t
  * signal in j's slice; rank j's own task keeps its tile in its accumulators,
  * waits for those W - 1 signals, adds the partials in rank order 0..W-1 (its
  * own in its place) in fp32, stores bf16 (round to nearest even) and SETs
- * (tile, j).  A partial is the fp32 accumulator tile of x1_r @ x2_r (one
- * rounding in all, to bf16 at the end), or with RA2A_RS_BF16_PARTIALS that
+ * (tile, j).  The signals order the tasks inside the launch; out_j is complete,
+ * for any reader, when the launch is (stream order).  A partial is the fp32
+ * accumulator tile of x1_r @ x2_r (one rounding in all, to bf16 at the end), or
+ * with RA2A_RS_BF16_PARTIALS that
  * product as the bf16 tensor a framework's matmul returns (rounded to nearest
  * even, rank j's own too): half the receive area and its traffic, at the cost
  * of W more roundings, so that where the partials cancel the elementwise error
