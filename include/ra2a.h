@@ -202,7 +202,7 @@ int ra2a_signal_reset(const ra2a_heap_t *heap, uint64_t *sig_sym, int64_t n_slot
 #define RA2A_MODE_STAGED 2 /* through a staging ring in slice j, reordered by consumers */
 #define RA2A_MODE_BULK 3   /* two-phase layout with fine-grained signals (see below) */
 #define RA2A_MODE_PULL 4   /* senders stage in their own slice, receivers pull (see below) */
-#define RA2A_MODE_ROWS 5   /* row units: whole rows of out_j, all sources (the default) */
+#define RA2A_MODE_ROWS 5   /* row units: whole rows of out_j, all sources */
 
 /* Work-queue words the pipelined combine keeps after the hand-back counters
  * (used in slice 0 only, staged mode only; direct mode leaves them 0): per
@@ -247,16 +247,26 @@ typedef struct ra2a_opts {
                                * at timestamps[j * tile_slots + u] (direct mode: the
                                * latest of its pieces' signals; staged mode: the end of
                                * its consumer copy) */
-    int32_t mode;             /* 0: RA2A_MODE_DIRECT.
+    int32_t mode;             /* 0: the default -- RA2A_MODE_ROWS for the combine when
+                               * one source's run of a token row, H*D*e bytes, is at
+                               * most 8 KiB and none of a delayed straggler source,
+                               * head_merge or piece_rows is set; RA2A_MODE_DIRECT
+                               * otherwise (always for the dispatch).
                                * RA2A_MODE_ROWS: each work unit fills unit_rows whole
                                * token rows of out_j (the W sources' runs of H*D elements,
                                * one contiguous range of out_j; W contiguous ranges of
-                               * the inputs) and adds 1 to its S-block's arrival counter
-                               * (region B: one per S-block); the unit that completes the
-                               * block marks every signal tile of the block complete
-                               * (ADD W, or SET 1 on each (tile, source) slot), the values
+                               * the inputs, read source after source) and adds 1 to its
+                               * S-block's arrival counter (region B: one per S-block).
+                               * Under ADD with W a multiple of the block's unit count
+                               * nub, each unit also adds W / nub to every signal tile of
+                               * its block once its rows are released (a tile reaches W
+                               * when all nub units have stored); otherwise the unit that
+                               * completes the block's count marks every signal tile of
+                               * the block complete (ADD W, or SET 1 on each (tile,
+                               * source) slot).  Either way the final values are the ones
                                * W pieces would leave.  Not for the dispatch, nor with a
-                               * straggler source (every unit carries all sources).
+                               * delayed straggler source (every unit carries all
+                               * sources).
                                * RA2A_MODE_DIRECT: producers store each piece (one
                                * source's rows of a tile, or a part of them: piece_rows)
                                * straight into its final place in out_j (a symmetric

@@ -350,7 +350,10 @@ RA2A_HD int64_t total_pieces(const PipeArgs& a) {
 // runs of H*D elements, which are contiguous in out_j (columns r*H .. r*H + H - 1
 // for r = 0 .. W-1 make up a whole output row) and contiguous, token after token,
 // in each in_r (rows j*S + s0 ..).  So a unit writes one contiguous range of out_j
-// and reads W contiguous ranges.  The signal tiles of S-block b are complete once
+// and reads W contiguous ranges.  It copies source by source (one source's rows,
+// then the next source's): on gfx950 reading each range in order while the
+// output fills as W interleaved streams measured faster than filling the output
+// token by token (W = 8, S = 512, H = 16, D = 128 bf16: 47 against 60 us).  The signal tiles of S-block b are complete once
 // every unit of b has stored its rows: each unit releases its stores device-wide
 // and adds 1 to the block's arrival counter (region B of slice j); the unit that
 // brings it to `nub` (the block's unit count) acquires and releases, then marks
@@ -399,12 +402,12 @@ RA2A_HD RowUnit row_unit(const PipeArgs& a, int64_t u) {
     q.src = a.in_off + ((int64_t)q.j * a.S + s0) * run;
     q.dst = (int64_t)q.j * a.stride + a.out_off + s0 * run * a.W;
     RowPlan& pl = q.pl;
-    pl.A = q.rows;      // tokens
-    pl.sa = run;
-    pl.da = run * a.W;
-    pl.B = a.W;         // sources, source-major inside an output row
-    pl.sb = a.stride;
-    pl.db = run;
+    pl.A = a.W;         // sources: each one's rows are read in one contiguous range
+    pl.sa = a.stride;
+    pl.da = run;
+    pl.B = q.rows;      // tokens
+    pl.sb = run;
+    pl.db = run * a.W;
     pl.C = 1;
     pl.sc = pl.dc = 0;
     pl.run = (int)run;

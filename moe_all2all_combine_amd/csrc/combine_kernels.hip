@@ -5,6 +5,7 @@
 //
 // Combine ("Reverse All2All (EP MoE Distributed Kernel)", section "Reverse
 // All2All Operator Semantics"): out_j[s, r*H + h, d] = in_r[j*S + s, h, d].
+#include <type_traits>
 #include <hip/hip_runtime.h>
 
 #include "combine_geom.h"
@@ -216,6 +217,99 @@ __device__ __forceinline__ void copy_plan_wt(const uint8_t* __restrict__ src,
     }
 }
 
+// Copy of the runs (a, b) of a plan with C == 1 and sb == run, so that each a's
+// B runs are one contiguous source range: run (a, b) goes from src + a*sa +
+// b*run to dst + a*da + b*db.  The range is moved in rounds of kThreads * V
+// contiguous bytes (lane t takes bytes [t*V, t*V + V) of each), U rounds in
+// flight, all loads before any store, one a at a time; device-scope
+// write-through stores as in copy_plan_wt.  Two run shapes (run_shape_ok):
+//  - a run of m whole rounds: a round lies in one run, so its destination is the
+//    same for the whole workgroup (scalar registers) plus the lane's column;
+//  - k runs per round (kThreads * V = k * run): a lane's run inside the round
+//    and column inside the run are fixed, so its destination is round q's first
+//    run (q*k) plus a per-lane constant; a last, partial round is predicated.
+// `mid()` runs once, when the middle a starts, so that what it issues
+// completes under the rest of the copy.
+template <int V>
+__device__ __forceinline__ bool run_shape_ok(const RowPlan& p) {
+    constexpr int kChunk = kThreads * V;
+    return p.C == 1 && p.sb == p.run && p.run > 0 &&
+           (p.run % kChunk == 0 || kChunk % p.run == 0);
+}
+
+template <int V, int U, typename Mid>
+__device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
+                                             __amdgpu_buffer_rsrc_t dst, const RowPlan& p,
+                                             Mid&& mid) {
+    using T = typename Vec<V>::T;
+    constexpr int kChunk = kThreads * V;
+    const bool whole = p.run >= kChunk;             // runs of m whole rounds
+    const int m = whole ? p.run / kChunk : 1;        // rounds per run
+    const int k = whole ? 1 : kChunk / p.run;        // runs per round
+    const int nq = whole ? p.B * m : p.B / k;        // full rounds per a
+    const int rem = whole ? 0 : p.B - nq * k;        // runs of a last, partial round
+    const uint32_t lane = threadIdx.x * V;
+    const uint32_t db = (uint32_t)p.db;
+    // k runs per round: the lane's run inside a round and its column in that run
+    const uint32_t lrun = whole ? 0u : lane / (uint32_t)p.run;
+    const uint32_t lane_dst = whole ? lane : lrun * db + (lane - lrun * (uint32_t)p.run);
+    const uint32_t round_db = (uint32_t)k * db;     // destination step per round (k runs)
+    for (int a0 = 0; a0 < p.A; ++a0) {
+        if (a0 == p.A / 2) mid();
+        const uint8_t* const s0 = src + (int64_t)a0 * p.sa + lane;
+        // destination of round q: run q / m, chunk q % m (whole runs, tracked
+        // without divisions), or runs q*k .. (k runs per round)
+        uint32_t dof = (uint32_t)((int64_t)a0 * p.da) + lane_dst;
+        int c = 0;
+        auto next = [&]() {
+            dof += kChunk;
+            if (++c == m) {
+                c = 0;
+                dof += db - (uint32_t)m * kChunk;
+            }
+        };
+        int q = 0;
+        // K rounds from round q on: all loads, then all stores.  STEP: every
+        // round advances the destination by round_db (k runs per round, or one
+        // round per run); otherwise by the whole-run tracking.
+        auto group = [&](auto kc, auto step) {
+            constexpr int K = decltype(kc)::value;
+            constexpr bool STEP = decltype(step)::value;
+            T v[K];
+            uint32_t d[K];
+#pragma unroll
+            for (int u = 0; u < K; ++u)
+                v[u] = load_nt(reinterpret_cast<const T*>(s0 + (int64_t)(q + u) * kChunk));
+#pragma unroll
+            for (int u = 0; u < K; ++u) {
+                if (STEP) {
+                    d[u] = dof + (uint32_t)u * round_db;
+                } else {
+                    d[u] = dof;
+                    next();
+                }
+            }
+            if (STEP) dof += (uint32_t)K * round_db;
+#pragma unroll
+            for (int u = 0; u < K; ++u) BufStore<V, kPolicyDevNt>::go(v[u], dst, d[u]);
+            q += K;
+        };
+        auto rounds = [&](auto step) {
+            while (q + U <= nq) group(std::integral_constant<int, U>{}, step);
+            if (U >= 4 && q + U / 2 <= nq) group(std::integral_constant<int, (U >= 4 ? U / 2 : 1)>{}, step);
+            while (q < nq) group(std::integral_constant<int, 1>{}, step);
+        };
+        if (m == 1)
+            rounds(std::true_type{});
+        else
+            rounds(std::false_type{});
+        if (rem > 0 && lrun < (uint32_t)rem) {
+            const T v = load_nt(reinterpret_cast<const T*>(s0 + (int64_t)nq * kChunk));
+            BufStore<V, kPolicyDevNt>::go(v, dst, dof);
+        }
+    }
+}
+
 // The same, reading the source through a buffer descriptor with cache policy
 // POLICY at 32-bit offsets src_off + (plan offset).
 template <int V, int U, int POLICY, bool NTS>
@@ -406,15 +500,18 @@ __device__ __forceinline__ void reset_share(const PipeArgs& a, int k) {
                            a.reset_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ const uint64_t* reset_flag(const PipeArgs& a, int k) {
+    return reinterpret_cast<const uint64_t*>(a.base + a.flag_off) + (int64_t)k * kSigStrideU64;
+}
+
 // Before a workgroup's first signal: every reset flag carries this launch's tag
-// (lane k of wave 0 polls flag k), then wave 0 -- the one that signals and
-// stamps -- acquires.  False, uniformly, if a bounded wait gave up.
-__device__ __forceinline__ bool reset_published(const PipeArgs& a) {
+// (lane k of wave 0 polls flag k; `early`, lane k's earlier read of it, spares
+// the poll when it already held the tag), then wave 0 -- the one that signals
+// and stamps -- acquires.  False, uniformly, if a bounded wait gave up.
+__device__ __forceinline__ bool reset_published(const PipeArgs& a, uint64_t early = 0ull) {
     bool ok = true;
-    if ((int)threadIdx.x < a.reset_nz)
-        ok = spin_until(reinterpret_cast<const uint64_t*>(a.base + a.flag_off) +
-                            (int64_t)threadIdx.x * kSigStrideU64,
-                        kCmpEq, a.reset_tag, a.timeout, a.err);
+    if ((int)threadIdx.x < a.reset_nz && early != a.reset_tag)
+        ok = spin_until(reset_flag(a, (int)threadIdx.x), kCmpEq, a.reset_tag, a.timeout, a.err);
     if (threadIdx.x < 64) fence_acquire_agent();
     return __syncthreads_and(ok ? 1 : 0) != 0;
 }
@@ -544,12 +641,15 @@ __device__ __forceinline__ void direct_path(const PipeArgs& a, int* lds_flag) {
 // Direct mode with row units (RA2A_MODE_ROWS; combine_geom.h row_unit).  A
 // unit copies its rows of every source into out_j with device-scope
 // write-through stores (the destination one contiguous range), drains them, and
-// adds 1 to the S-block's arrival counter; the unit that completes the block
-// marks every signal tile of the block complete.  Every other unit of the block
-// drained its stores before its add, and the completing unit read the counter
-// after all of them: the block's rows are performed device-wide before these
-// signals.  Counter and signals are zeroed by the in-launch reset, so both
-// wait for its flags.  Work is distributed as in direct_path.
+// adds 1 to the S-block's arrival counter.  Under ADD, when W is a multiple of
+// the block's unit count nub, each unit also adds W / nub to every signal tile
+// of the block, after its own drain: a tile reaches W exactly when all nub units
+// have stored.  Otherwise the unit that completes the block's count marks every
+// signal tile of the block complete: every other unit of the block drained its
+// stores before its add, and the completing unit read the counter after all of
+// them, so the block's rows are performed device-wide before these signals.
+// Counter and signals are zeroed by the in-launch reset, so both wait for its
+// flags.  Work is distributed as in direct_path.
 template <int V>
 __device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
     __shared__ int64_t lds_next;
@@ -558,22 +658,48 @@ __device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
         reset_share(a, (int)blockIdx.x);
         return;
     }
-    const int op = a.protocol == kSigAdd ? kSigAdd : kSigSet;
-    const uint64_t val = a.protocol == kSigAdd ? (uint64_t)a.W : 1ull;
+    const bool add = a.protocol == kSigAdd;
+    const int op = add ? kSigAdd : kSigSet;
+    const uint64_t val = add ? (uint64_t)a.W : 1ull;
     bool published = a.reset_tag == 0ull;
     Claimer cl = claimer(a);
     for (int64_t u = (int)blockIdx.x - nz; u < a.nunits;) {
         claim_ahead(a, cl, published);
         const RowUnit q = row_unit(a, u);
-        copy_plan_wt<V, 8>(a.base + q.src, make_rsrc_uniform(a.base + q.dst, plan_span(q.pl)), q.pl,
-                           0, plan_vectors(q.pl, V));
+        const __amdgpu_buffer_rsrc_t dst = make_rsrc_uniform(a.base + q.dst, plan_span(q.pl));
+        // Until the reset is known to be published, lane k < nz of wave 0 reads
+        // reset flag k during the copy; the check after it then has nothing left
+        // to wait for unless that read came too early.
+        uint64_t early = 0ull;
+        auto poll = [&]() {
+            if (!published && (int)threadIdx.x < nz) early = sig_load(reset_flag(a, (int)threadIdx.x));
+        };
+        if (run_shape_ok<V>(q.pl)) {
+            copy_runs_wt<V, 8>(a.base + q.src, dst, q.pl, poll);
+        } else {
+            poll();
+            copy_plan_wt<V, 8>(a.base + q.src, dst, q.pl, 0, plan_vectors(q.pl, V));
+        }
         group_release_written_through();
         if (!published) {
-            if (!reset_published(a)) return;
+            if (!reset_published(a, early)) return;
             published = true;
             claim_ahead(a, cl, published);
         }
-        if (arrive(a, q.cnt, (uint64_t)q.nub, lds_flag) && threadIdx.x < 64) {
+        // ADD protocol with W a multiple of the block's unit count: every unit
+        // adds its share W / nub to each tile of the block (a tile reaches W once
+        // all of them have stored their rows) and counts itself, with nothing to
+        // wait for.  Otherwise the unit that completes the count signals for all.
+        const uint64_t share = add && a.W % q.nub == 0 ? (uint64_t)(a.W / q.nub) : 0ull;
+        if (share != 0ull) {
+            if (threadIdx.x < 64) {
+                if (threadIdx.x == 0) sig_update(reinterpret_cast<uint64_t*>(a.base + q.cnt), 1ull, kSigAdd);
+                for (int k = threadIdx.x; k < q.nsig; k += 64)
+                    sig_update(reinterpret_cast<uint64_t*>(a.base + q.sig) + (int64_t)k * kSigStrideU64,
+                               share, kSigAdd);
+                stamp_tiles(a, q.j, q.unit_index, 1, q.nsig);
+            }
+        } else if (arrive(a, q.cnt, (uint64_t)q.nub, lds_flag) && threadIdx.x < 64) {
             for (int k = threadIdx.x; k < q.nsig; k += 64)
                 sig_update(reinterpret_cast<uint64_t*>(a.base + q.sig) + (int64_t)k * kSigStrideU64,
                            val, op);

@@ -14,9 +14,10 @@ from oracle.protocol import (ADD, SET, ProtocolSpec, expected_final_block_counts
 ELEM = {"u8": 1, "bf16": 2, "f16": 2, "i32": 4, "f32": 4, "i64": 8, "f64": 8}
 
 
-def row_mode(opts) -> bool:
-    """Whether the options select row units."""
-    return opts.mode == ra2a.MODE_ROWS
+def row_mode(W, S, H, D, opts, dtype="bf16") -> bool:
+    """Whether the combine resolves these options to row units (asked for, or
+    mode 0 on a shape whose default is row units): the plan the library reports."""
+    return ra2a.rev_all2all_plan(W, S, H, D, dtype, opts).mode == ra2a.MODE_ROWS
 
 
 def unit_rows(W, S, H, D, opts, dtype="bf16") -> int:
@@ -45,7 +46,7 @@ def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):
     per = W if proto == SET else 1
     # merged head blocks: derived from the size of the hand-back region
     _, n_credit, _ = ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)
-    if row_mode(opts):
+    if row_mode(W, S, H, D, opts, dtype):
         tiles = ProtocolSpec(W=W, nbs=nbs, nstreams=nhb * ndb, R=R, protocol=proto)
         ns = nhb * ndb
         a = np.zeros(nbs * ns * per, dtype=np.int64)

@@ -79,13 +79,21 @@ def test_attach_rejects_overlap_and_misalignment(fake_heap):
 def test_signal_slots_and_workspace():
     Q = ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS  # control words: queue words, then reset flags
     # 64-token x 1-head x 128 tiles, ADD: one slot per (S-block, head) per slice
+    # the default on this shape (a source's run of a token row is 4 KiB, at most
+    # 8 KiB): row units of 8 tokens (256 KiB of output), one arrival counter per
+    # S-block in region B
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
-    # direct mode (the default): 16 heads merged into 4 KiB runs, so a piece (one
-    # source's 64 tokens) is 256 KiB and moves as two parts of 32 tokens: one arrival
-    # counter per moved tile (S-block) in region B
     assert (a, b, q) == (8 * 16, 8, Q)
     p = ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16")
-    assert (p.head_merge, p.piece_rows, p.pieces_per_tile) == (16, 32, 2)
+    assert (p.mode, p.unit_rows, p.work_items) == (ra2a.MODE_ROWS, 8, 8 * 64)
+    # per-source pieces: 16 heads merged into 4 KiB runs, so a piece (one source's 64
+    # tokens) is 256 KiB and moves as two parts of 32 tokens: one arrival counter per
+    # moved tile (S-block) in region B
+    direct = ra2a.Opts(mode=ra2a.MODE_DIRECT)
+    a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", direct)
+    assert (a, b, q) == (8 * 16, 8, Q)
+    p = ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16", direct)
+    assert (p.mode, p.head_merge, p.piece_rows, p.pieces_per_tile) == (ra2a.MODE_DIRECT, 16, 32, 2)
     # with heads merged 8 at a time (2 KiB runs) a piece is 128 KiB, one part
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", ra2a.Opts(head_merge=8))
     assert (a, b, q) == (8 * 16, 0, Q)

@@ -120,6 +120,31 @@ def test_small_direct(W, S, H, D, dtype, tile, proto, ring, knobs):
     run_and_check(wl, opts, csplit=1)
 
 
+# Row units whose per-source run (H*D*e bytes) relates to the 4 KiB round of
+# 256 lanes x 16 bytes in each way the row copy handles: whole rounds per run
+# (8 KiB: two; 4 KiB: one), several runs per round (2 KiB, 512 B, with a last,
+# partial round when the unit's tokens do not fill it) and neither (6 KiB, 96 B:
+# the general plan walk).
+ROW_RUNS = [
+    (3, 21, 4, 1024, "bf16", (8, 1, 1024), synthgen.PROTOCOL_ADD),
+    (4, 19, 2, 1024, "bf16", (8, 2, 1024), synthgen.PROTOCOL_SET),
+    (8, 24, 8, 128, "bf16", (8, 1, 128), synthgen.PROTOCOL_ADD),
+    (5, 23, 4, 128, "f32", (16, 1, 64), synthgen.PROTOCOL_ADD),
+    (4, 30, 2, 128, "bf16", (8, 1, 128), synthgen.PROTOCOL_SET),
+    (3, 17, 3, 512, "f32", (8, 1, 512), synthgen.PROTOCOL_ADD),
+    (4, 13, 3, 16, "bf16", (4, 1, 16), synthgen.PROTOCOL_ADD),
+]
+
+
+@pytest.mark.parametrize("W,S,H,D,dtype,tile,proto", ROW_RUNS)
+@pytest.mark.parametrize("unit_rows", [0, 1, 3, 5])
+def test_row_units_run_shapes(W, S, H, D, dtype, tile, proto, unit_rows):
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 31 + S + unit_rows, tile=tile,
+                                 protocol=proto)
+    opts = opts_for(wl, mode=ra2a.MODE_ROWS, unit_rows=unit_rows)
+    run_and_check(wl, opts, csplit=1)
+
+
 @pytest.mark.parametrize("W,S,H,D,dtype,tile,proto,ring", SMALL[:6])
 def test_small_staged_agent_sync(W, S, H, D, dtype, tile, proto, ring):
     wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S + 1, tile=tile, protocol=proto)
