@@ -41,8 +41,17 @@ sys.path.insert(0, ROOT)
 
 WORKLOAD = "ep_combine_w8_s512_h16_d128_bf16"
 HBM_PEAK_GBS = 8000.0
+# what ra2a_rev_all2all_plan reports as the mode a combine resolves to
+MODE_NAMES = {1: "per-source pieces", 2: "staged", 3: "bulk", 4: "pull",
+              5: "row units (whole out_j rows, all sources)"}
 NSETS = 6
-KERNEL = "rev_a2a_pipelined_kernel (direct mode: per-source pieces, write-through stores)"
+BIG_ALIGN = 2 << 20  # placement of the combine's inputs and outputs in a slice
+
+
+def kernel_label(mode):
+    """The dominant kernel of a combine leg, named with the mode its plan resolves to."""
+    return (f"rev_a2a_pipelined_kernel (direct mode: {MODE_NAMES.get(mode, '?')}, "
+            "write-through stores)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rev_a2a_pipelined_direct_ep_combine_w8.json")
 TRAFFIC_FILE_MOE = os.path.join(ROOT, "profiles", "traffic_rev_a2a_pipelined_direct_moe_combine_w8.json")
 
@@ -475,9 +484,10 @@ def staged_ring_leg(steps, warmup, tile_s, ring):
     nb = wl.bytes_per_rank
     nsig = sum(ra2a.rev_all2all_signal_slots(W, S, H, D, wl.dtype, o))
     work = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, o)
-    heap = ra2a.SymmHeap(W, NSETS * (2 * nb + nsig * 128 + 4096) + work + (4 << 20))
+    heap = ra2a.SymmHeap(W, NSETS * (2 * nb + nsig * 128 + 4096 + 2 * BIG_ALIGN) + work + (4 << 20))
     try:
-        sets = [(heap.alloc(nb), heap.alloc(nb), heap.alloc(nsig * 128)) for _ in range(NSETS)]
+        sets = [(heap.alloc(nb, BIG_ALIGN), heap.alloc(nb, BIG_ALIGN), heap.alloc(nsig * 128))
+                for _ in range(NSETS)]
         for oi, _, _ in sets:
             device_inputs(heap, oi, wl, torch.int16)
         st = torch.cuda.current_stream()
@@ -605,7 +615,7 @@ def moe_leg(steps, profile=False):
                "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                             "traffic": load_traffic(TRAFFIC_FILE_MOE),
-                            "kernel": KERNEL, "kernel_ms": round(ms, 5)}}
+                            "kernel": kernel_label(pl.mode), "kernel_ms": round(ms, 5)}}
         for name in [n for n in ("rows", "whole_tile_pieces") if n in res]:
             m2, ok2 = res[name]
             g2 = alg / (m2 * 1e-3) / 1e9
@@ -805,9 +815,11 @@ def main():
     ring = sum(ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, o) for o in (opts_st, opts_bk))
     full = ra2a.rev_all2all_workspace_bytes(W, S, H, D, wl.dtype, None, True)
     nb = wl.bytes_per_rank
-    slice_bytes = NSETS * (2 * nb + nsig * 128 + 4096) + ring + full + (4 << 20)
+    # inputs and outputs on 2 MiB boundaries (the header's placement note)
+    slice_bytes = NSETS * (2 * nb + nsig * 128 + 4096 + 2 * BIG_ALIGN) + ring + full + (4 << 20)
     heap = ra2a.SymmHeap(W, slice_bytes)
-    sets = [(heap.alloc(nb), heap.alloc(nb), heap.alloc(nsig * 128)) for _ in range(NSETS)]
+    sets = [(heap.alloc(nb, BIG_ALIGN), heap.alloc(nb, BIG_ALIGN), heap.alloc(nsig * 128))
+            for _ in range(NSETS)]
     log(f"[bench] generating {wl.name}")
     ins = synthgen.make_inputs(wl)
     bits = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[wl.elem_bytes]
@@ -932,13 +944,15 @@ def main():
         "parity": ok,
         "config": {"workload": wl.name, "W": W, "S": S, "H": H, "D": D, "dtype": wl.dtype,
                    "tile": [wl.tile_s, wl.tile_h, wl.tile_d], "protocol": wl.protocol,
-                   "variant": "signal-pipelined persistent kernel, direct mode (per-source pieces)",
+                   "variant": "signal-pipelined persistent kernel, direct mode, " + MODE_NAMES.get(
+                       ra2a.rev_all2all_plan(W, S, H, D, wl.dtype, opts_lib).mode, "?"),
                    "step": "signal reset + combine", "steps_issued": mode_used,
                    "buffer_sets": NSETS,
                    "algorithmic_bytes": alg},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(), "kernel": KERNEL,
+                     "traffic": load_traffic(),
+                     "kernel": kernel_label(ra2a.rev_all2all_plan(W, S, H, D, wl.dtype, opts_lib).mode),
                      "kernel_ms": round(kern_ms, 5)},
     }
     rec["step_variants"] = {
@@ -954,6 +968,16 @@ def main():
                    "note": "context, not the headline: in-launch steps on one buffer set, data left in "
                            f"the MALL by the previous step; the headline rotates {NSETS} sets (cold)"}
     if args.legs == "all":
+        # the other direct mode, in-launch reset as the headline
+        opts_pc = ra2a.Opts(mode=ra2a.MODE_DIRECT, **tiles)
+        pc_ms, pc_kern_ms = timed(opts_pc, args.steps, args.warmup, overlap=False, reset=False)
+        poison(0)
+        step(0, opts_pc, overlap=False, reset=False)
+        torch.cuda.synchronize()
+        rec["pieces"] = {"ms_per_step": round(pc_ms, 5), "kernel_ms": round(pc_kern_ms, 5),
+                         "value": round(alg / (pc_ms * 1e-3) / 1e9, 2),
+                         "parity": ra2a.check(hs) == ra2a.OK and parity(0),
+                         "note": "RA2A_MODE_DIRECT: per-source pieces, in-launch reset"}
         st_ms, _ = timed(opts_st, args.steps, args.warmup, overlap=False)  # reset launch + combine
         poison(0)
         step(0, opts_st, overlap=False)

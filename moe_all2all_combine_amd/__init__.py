@@ -239,7 +239,7 @@ def symm_heap_destroy(heap: int) -> None:
     _ok(lib().ra2a_symm_heap_destroy(heap))
 
 
-def symm_malloc(heap: int, nbytes: int, align: int = 256) -> int:
+def symm_malloc(heap: int, nbytes: int, align: int = 0) -> int:
     off = ctypes.c_size_t()
     _ok(lib().ra2a_symm_malloc(heap, nbytes, align, ctypes.byref(off)))
     return off.value
@@ -447,7 +447,7 @@ class SymmHeap:
         self.handle = symm_heap_attach(self.base, world, self.stride)
         _torch_heaps.add(self)
 
-    def alloc(self, nbytes: int, align: int = 256) -> int:
+    def alloc(self, nbytes: int, align: int = 0) -> int:
         return symm_malloc(self.handle, nbytes, align)
 
     def ptr(self, offset: int, rank: int = 0) -> int:

@@ -148,8 +148,17 @@ int ensure_err(ra2a_heap* h) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Default output bytes per row unit (RA2A_MODE_ROWS): the unit_rows default is
-// max(1, kRowUnitBytes / (W*H*D*e)) tokens, at most the S-block.
+// max(1, kRowUnitBytes / (W*H*D*e)) tokens, at most the S-block -- or twice
+// that when a source's run (H*D*e) is at least kRowWholeRun (a 4 KiB round of
+// 256 lanes x 16 B lies in one run) and the call still has kRowUnitsMin units
+// (one per compute unit of the 256 of gfx950).  Measured (bf16, tile_s 64,
+// 256 KiB against 512 KiB units): W=8, S=512, H=16, D=128 47.8 against 47.1 us;
+// W=16, S=256, H=16, D=128 96.1 against 91.8; W=8, S=1024, H=8, D=128 (2 KiB
+// runs) 48.2 against 51.7; W=4, S=1024, H=16, D=128 (128 units) 27.5 against
+// 31.6.
 constexpr int64_t kRowUnitBytes = 256 << 10;
+constexpr int64_t kRowWholeRun = 4 << 10;
+constexpr int64_t kRowUnitsMin = 256;
 // Mode 0 moves row units when one source's run of a token row (H*D*e bytes) is at
 // most this, per-source pieces above it.  Measured on gfx950 (bf16, tile_s 64,
 // percent of 8 TB/s, row units against pieces): runs of 1 KiB (W=8, S=2048, H=4,
@@ -325,6 +334,14 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
         const int64_t row_bytes = (int64_t)W * H * D * e;
         int64_t ku = o->unit_rows > 0 ? o->unit_rows : std::max<int64_t>(1, kRowUnitBytes / row_bytes);
         ku = std::min(ku, p->BS);
+        if (o->unit_rows == 0 && H * D * e >= kRowWholeRun) {
+            // runs of whole rounds: twice the bytes per unit while every compute
+            // unit still gets one
+            const int64_t ku2 = std::min<int64_t>(std::max<int64_t>(1, 2 * kRowUnitBytes / row_bytes), p->BS);
+            const int64_t units2 = ((int64_t)(p->nbs - 1) * cdiv(p->BS, ku2) +
+                                    cdiv(S - (int64_t)(p->nbs - 1) * p->BS, ku2)) * W;
+            if (units2 >= kRowUnitsMin) ku = ku2;
+        }
         p->KU = (int)ku;
         p->upb = (int)cdiv(p->BS, ku);
         p->regionB = p->nbs;
@@ -405,7 +422,9 @@ int check_combine(const void* in, const void* out, const void* signals, int W, i
 
 // Bump allocation under the heap's lock.
 int heap_alloc(ra2a_heap* h, size_t bytes, size_t align, size_t* off) {
-    if (align == 0) align = 256;
+    // default: 4 KiB for buffers of 4 KiB or more (runs of 4 KiB, a round of
+    // 256 lanes x 16 B, then keep to 4 KiB pages), 256 B below
+    if (align == 0) align = bytes >= 4096 ? 4096 : 256;
     if (align & (align - 1)) return fail(RA2A_EINVAL, "align must be a power of two");
     const size_t start = (h->bump + align - 1) & ~(align - 1);
     if (start > h->stride || bytes > h->stride - start)
@@ -427,7 +446,7 @@ int staging(ra2a_heap* h, bool full, size_t bytes, size_t* off) {
         return RA2A_OK;
     }
     size_t o = 0;
-    int rc = heap_alloc(h, std::max<size_t>(bytes, 256), 256, &o);
+    int rc = heap_alloc(h, std::max<size_t>(bytes, 256), 0, &o);
     if (rc) return fail(RA2A_ENOMEM, "staging of %zu bytes per slice does not fit the heap: %s",
                         bytes, g_err.c_str());
     co = o;
@@ -509,6 +528,11 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     a->rows = pl.rows;
     a->KU = pl.KU;
     a->upb = pl.upb;
+    // Row units: four rounds in flight per lane when each source's range in a
+    // unit is at least 64 KiB, else eight (gfx950, bf16: W=8, S=512, H=16,
+    // D=128, 64 KiB ranges, 46.3 against 46.9 us; D=256 91.2 against 93.5; W=16,
+    // S=256, H=16, D=128, 32 KiB ranges, 92.4 against 90.2).
+    a->ru = pl.rows && (int64_t)pl.KU * H * D * e0 >= (64 << 10) ? 4 : 8;
     a->PR = pl.PR;
     a->nsub = pl.nsub;
     a->inverse = pl.inverse;
@@ -521,11 +545,11 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     // vector width: every offset, stride and run is a multiple of it
     const uint64_t m = (uint64_t)(D * e0) | (uint64_t)(pl.TD * e0) | in_off | out_off | stg_off;
     *V = lowbit_vec(m);
-    // Schedule of the direct modes: dynamic claims when the pieces (row units)
-    // are many per compute unit, else static; workgroups per compute unit as
-    // asked, else one (dynamic) or two (static; on the W=8, S=512, H=16, D=128
-    // bf16 shape the dispatch measured 51.1 us with two against 53.1 with one).
-    // The staged modes keep two by default.
+    // Schedule of the direct modes: for pieces, dynamic claims when they are many
+    // per compute unit, else static; workgroups per compute unit as asked, else
+    // one (dynamic, and row units) or two (static pieces; on the W=8, S=512, H=16,
+    // D=128 bf16 shape the dispatch measured 51.1 us with two against 53.1 with
+    // one).  The staged modes keep two by default.
     int64_t work = 0;
     if (pl.rows) {
         a->nunits = ra2a::total_row_units(*a);
@@ -534,9 +558,13 @@ int prepare_pipelined(int W, int64_t S, int64_t H, int64_t D, int e0, const Plan
     } else if (pl.direct) {
         work = ra2a::total_pieces(*a);
     }
-    a->dyn = pl.direct && work >= kDynPiecesPerCu * (int64_t)ncu ? 1 : 0;
+    // Row units keep the static schedule with one workgroup per compute unit:
+    // on gfx950 fewer copies in flight fill HBM better here (W=8, S=4096, H=16,
+    // D=128 bf16, 256 KiB units: 350 us static against 378 claimed; W=8, S=512:
+    // 47.5 against 48.0 us with two per compute unit).
+    a->dyn = pl.direct && !pl.rows && work >= kDynPiecesPerCu * (int64_t)ncu ? 1 : 0;
     int wpc = pl.wg_per_cu;
-    if (wpc <= 0) wpc = (pl.direct && a->dyn) ? 1 : 2;
+    if (wpc <= 0) wpc = (pl.rows || (pl.direct && a->dyn)) ? 1 : 2;
     const int per_cu = std::max(1, std::min(blocks_per_cu, wpc));
     *grid = per_cu * ncu;
     if (pl.direct) *grid = (int)std::min<int64_t>(*grid, work);  // no workgroup without work

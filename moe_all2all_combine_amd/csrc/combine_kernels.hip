@@ -219,17 +219,20 @@ __device__ __forceinline__ void copy_plan_wt(const uint8_t* __restrict__ src,
 
 // Copy of the runs (a, b) of a plan with C == 1 and sb == run, so that each a's
 // B runs are one contiguous source range: run (a, b) goes from src + a*sa +
-// b*run to dst + a*da + b*db.  The range is moved in rounds of kThreads * V
-// contiguous bytes (lane t takes bytes [t*V, t*V + V) of each), U rounds in
-// flight, all loads before any store, one a at a time; device-scope
-// write-through stores as in copy_plan_wt.  Two run shapes (run_shape_ok):
+// b*run to dst + a*da + b*db.  The ranges are moved in rounds of kThreads * V
+// contiguous bytes (lane t takes bytes [t*V, t*V + V) of each), a after a, U
+// rounds in flight (all loads, then all stores; a group may span several a);
+// device-scope write-through stores as in copy_plan_wt.  Two run shapes
+// (run_shape_ok):
 //  - a run of m whole rounds: a round lies in one run, so its destination is the
 //    same for the whole workgroup (scalar registers) plus the lane's column;
 //  - k runs per round (kThreads * V = k * run): a lane's run inside the round
 //    and column inside the run are fixed, so its destination is round q's first
-//    run (q*k) plus a per-lane constant; a last, partial round is predicated.
-// `mid()` runs once, when the middle a starts, so that what it issues
-// completes under the rest of the copy.
+//    run (q*k) plus a per-lane constant; each a's last, partial round (B not a
+//    multiple of k) moves in a second pass, by the lanes whose run it holds.
+// Round offsets advance with selects, not branches, so that a group's loads
+// issue back to back.  `mid()` runs once, about half-way (before the first group
+// past the middle), so that what it issues completes under the rest of the copy.
 template <int V>
 __device__ __forceinline__ bool run_shape_ok(const RowPlan& p) {
     constexpr int kChunk = kThreads * V;
@@ -250,63 +253,74 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
     const int rem = whole ? 0 : p.B - nq * k;        // runs of a last, partial round
     const uint32_t lane = threadIdx.x * V;
     const uint32_t db = (uint32_t)p.db;
-    // k runs per round: the lane's run inside a round and its column in that run
+    // k runs per round: the lane's run inside a round, and its destination offset
     const uint32_t lrun = whole ? 0u : lane / (uint32_t)p.run;
     const uint32_t lane_dst = whole ? lane : lrun * db + (lane - lrun * (uint32_t)p.run);
-    const uint32_t round_db = (uint32_t)k * db;     // destination step per round (k runs)
-    for (int a0 = 0; a0 < p.A; ++a0) {
-        if (a0 == p.A / 2) mid();
-        const uint8_t* const s0 = src + (int64_t)a0 * p.sa + lane;
-        // destination of round q: run q / m, chunk q % m (whole runs, tracked
-        // without divisions), or runs q*k .. (k runs per round)
-        uint32_t dof = (uint32_t)((int64_t)a0 * p.da) + lane_dst;
-        int c = 0;
-        auto next = [&]() {
-            dof += kChunk;
-            if (++c == m) {
-                c = 0;
-                dof += db - (uint32_t)m * kChunk;
-            }
-        };
-        int q = 0;
-        // K rounds from round q on: all loads, then all stores.  STEP: every
-        // round advances the destination by round_db (k runs per round, or one
-        // round per run); otherwise by the whole-run tracking.
-        auto group = [&](auto kc, auto step) {
+    // destination steps: to the next round of the same run, to the first round of
+    // the next run of the same a, and from the last round of an a to the first of
+    // the next (modulo 2^32, like the offsets)
+    const uint32_t next_run = whole ? db - (uint32_t)(m - 1) * kChunk : (uint32_t)k * db;
+    const uint32_t next_a = whole ? (uint32_t)p.da - ((uint32_t)(p.B - 1) * db + (uint32_t)(m - 1) * kChunk)
+                                  : (uint32_t)p.da - (uint32_t)(nq - 1) * (uint32_t)k * db;
+    const int64_t src_next_a = p.sa - (int64_t)(nq - 1) * kChunk;
+    const int total = p.A * nq;
+    const uint8_t* const s_lane = src + lane;
+    int q = 0, c = 0;
+    int64_t so = 0;
+    uint32_t dof = lane_dst;
+    auto advance = [&]() {
+        const bool end_run = c + 1 == m;
+        const bool end_a = q + 1 == nq;
+        so += end_a ? src_next_a : (int64_t)kChunk;
+        dof += end_a ? next_a : (end_run ? next_run : (uint32_t)kChunk);
+        c = end_run ? 0 : c + 1;
+        q = end_a ? 0 : q + 1;
+    };
+    bool mid_done = false;
+    int f = 0;
+    auto group = [&](auto kc) {
+        constexpr int K = decltype(kc)::value;
+        if (!mid_done && 2 * f >= total) {
+            mid();
+            mid_done = true;
+        }
+        int64_t sofs[K];
+        uint32_t d[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            sofs[u] = so;
+            d[u] = dof;
+            advance();
+        }
+        T v[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u) v[u] = load_nt(reinterpret_cast<const T*>(s_lane + sofs[u]));
+#pragma unroll
+        for (int u = 0; u < K; ++u) BufStore<V, kPolicyDevNt>::go(v[u], dst, d[u]);
+        f += K;
+    };
+    while (f + U <= total) group(std::integral_constant<int, U>{});
+    if (U >= 4 && f + U / 2 <= total) group(std::integral_constant<int, (U >= 4 ? U / 2 : 1)>{});
+    while (f < total) group(std::integral_constant<int, 1>{});
+    if (!mid_done) mid();
+    // the partial rounds (k runs per round, B % k of them left per a), one per a
+    if (rem > 0 && lrun < (uint32_t)rem) {
+        const int64_t s_part = (int64_t)nq * kChunk;
+        const uint32_t d_part = (uint32_t)nq * (uint32_t)k * db + lane_dst;
+        int a0 = 0;
+        auto part = [&](auto kc) {
             constexpr int K = decltype(kc)::value;
-            constexpr bool STEP = decltype(step)::value;
             T v[K];
-            uint32_t d[K];
 #pragma unroll
             for (int u = 0; u < K; ++u)
-                v[u] = load_nt(reinterpret_cast<const T*>(s0 + (int64_t)(q + u) * kChunk));
+                v[u] = load_nt(reinterpret_cast<const T*>(s_lane + (int64_t)(a0 + u) * p.sa + s_part));
 #pragma unroll
-            for (int u = 0; u < K; ++u) {
-                if (STEP) {
-                    d[u] = dof + (uint32_t)u * round_db;
-                } else {
-                    d[u] = dof;
-                    next();
-                }
-            }
-            if (STEP) dof += (uint32_t)K * round_db;
-#pragma unroll
-            for (int u = 0; u < K; ++u) BufStore<V, kPolicyDevNt>::go(v[u], dst, d[u]);
-            q += K;
+            for (int u = 0; u < K; ++u)
+                BufStore<V, kPolicyDevNt>::go(v[u], dst, (uint32_t)((int64_t)(a0 + u) * p.da) + d_part);
+            a0 += K;
         };
-        auto rounds = [&](auto step) {
-            while (q + U <= nq) group(std::integral_constant<int, U>{}, step);
-            if (U >= 4 && q + U / 2 <= nq) group(std::integral_constant<int, (U >= 4 ? U / 2 : 1)>{}, step);
-            while (q < nq) group(std::integral_constant<int, 1>{}, step);
-        };
-        if (m == 1)
-            rounds(std::true_type{});
-        else
-            rounds(std::false_type{});
-        if (rem > 0 && lrun < (uint32_t)rem) {
-            const T v = load_nt(reinterpret_cast<const T*>(s0 + (int64_t)nq * kChunk));
-            BufStore<V, kPolicyDevNt>::go(v, dst, dof);
-        }
+        while (a0 + U <= p.A) part(std::integral_constant<int, U>{});
+        while (a0 < p.A) part(std::integral_constant<int, 1>{});
     }
 }
 
@@ -675,7 +689,10 @@ __device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
             if (!published && (int)threadIdx.x < nz) early = sig_load(reset_flag(a, (int)threadIdx.x));
         };
         if (run_shape_ok<V>(q.pl)) {
-            copy_runs_wt<V, 8>(a.base + q.src, dst, q.pl, poll);
+            if (a.ru == 4)
+                copy_runs_wt<V, 4>(a.base + q.src, dst, q.pl, poll);
+            else
+                copy_runs_wt<V, 8>(a.base + q.src, dst, q.pl, poll);
         } else {
             poll();
             copy_plan_wt<V, 8>(a.base + q.src, dst, q.pl, 0, plan_vectors(q.pl, V));

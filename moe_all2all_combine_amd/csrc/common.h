@@ -62,6 +62,7 @@ struct PipeArgs {
     int32_t rows;       // 1 (with direct): row units -- whole rows of out_j, every source
     int32_t KU;         // row units: tokens per unit (a unit never straddles S-blocks)
     int32_t upb;        // row units per full S-block: ceil(BS / KU)
+    int32_t ru;         // row units: rounds in flight per lane (4 or 8)
     int64_t nunits;     // row units in total
     int32_t inverse;    // 1: the dispatch (the combine's inverse map), direct mode only
     int32_t bulk;       // 1: staging in the two-phase layout [W][S][H][D], no ring

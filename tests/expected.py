@@ -22,9 +22,16 @@ def row_mode(W, S, H, D, opts, dtype="bf16") -> bool:
 
 def unit_rows(W, S, H, D, opts, dtype="bf16") -> int:
     """Tokens per row unit as the header documents it."""
-    tile_s = opts.tile_s or min(S, 64)
-    ku = opts.unit_rows or max(1, 262144 // (W * H * D * ELEM[dtype]))
-    return min(ku, tile_s)
+    tile_s = min(opts.tile_s or min(S, 64), S)
+    row = W * H * D * ELEM[dtype]
+    ku = min(opts.unit_rows or max(1, 262144 // row), tile_s)
+    if not opts.unit_rows and H * D * ELEM[dtype] >= 4096:
+        ku2 = min(max(1, 524288 // row), tile_s)
+        nbs = math.ceil(S / tile_s)
+        units2 = ((nbs - 1) * math.ceil(tile_s / ku2) + math.ceil((S - (nbs - 1) * tile_s) / ku2)) * W
+        if units2 >= 256:
+            ku = ku2
+    return ku
 
 
 def expected_signal_array(W, S, H, D, opts, csplit, dtype="bf16"):

@@ -60,6 +60,11 @@ def test_symm_malloc_bump_and_exhaustion(fake_heap):
     a = ra2a.symm_malloc(fake_heap, 100)
     b = ra2a.symm_malloc(fake_heap, 10, 4096)
     assert a == 0 and b == 4096
+    # default alignment: 256 B below 4 KiB, 4 KiB from 4 KiB on
+    c = ra2a.symm_malloc(fake_heap, 100)
+    d = ra2a.symm_malloc(fake_heap, 8192)
+    e2 = ra2a.symm_malloc(fake_heap, 100, 16)
+    assert (c, d, e2) == (4096 + 256, 8192, 16384)
     with pytest.raises(ra2a.Ra2aError) as e:
         ra2a.symm_malloc(fake_heap, 4 << 20)
     assert e.value.code == ra2a.ENOMEM
@@ -80,12 +85,28 @@ def test_signal_slots_and_workspace():
     Q = ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS  # control words: queue words, then reset flags
     # 64-token x 1-head x 128 tiles, ADD: one slot per (S-block, head) per slice
     # the default on this shape (a source's run of a token row is 4 KiB, at most
-    # 8 KiB): row units of 8 tokens (256 KiB of output), one arrival counter per
-    # S-block in region B
+    # 8 KiB): row units; the run is a whole 4 KiB round and 512 KiB units still
+    # number 256, so 16 tokens per unit; one arrival counter per S-block in region B
     a, b, q = ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16")
     assert (a, b, q) == (8 * 16, 8, Q)
     p = ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16")
-    assert (p.mode, p.unit_rows, p.work_items) == (ra2a.MODE_ROWS, 8, 8 * 64)
+    assert (p.mode, p.unit_rows, p.work_items) == (ra2a.MODE_ROWS, 16, 8 * 4 * 8)
+    # 256 KiB units: runs shorter than a round (2 KiB), or too few 512 KiB units (128)
+    p = ra2a.rev_all2all_plan(8, 1024, 8, 128, "bf16")
+    assert (p.mode, p.unit_rows, p.work_items) == (ra2a.MODE_ROWS, 16, 16 * 4 * 8)
+    p = ra2a.rev_all2all_plan(4, 1024, 16, 128, "bf16")
+    assert (p.mode, p.unit_rows, p.work_items) == (ra2a.MODE_ROWS, 16, 16 * 4 * 4)
+    # 8 KiB runs: 512 KiB units (8 tokens), 256 of them
+    p = ra2a.rev_all2all_plan(8, 256, 32, 128, "bf16")
+    assert (p.mode, p.unit_rows, p.work_items) == (ra2a.MODE_ROWS, 8, 4 * 8 * 8)
+    # runs above 8 KiB, the dispatch, a delayed straggler source: per-source pieces
+    assert ra2a.rev_all2all_plan(8, 256, 1, 7168, "bf16").mode == ra2a.MODE_DIRECT
+    assert ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16",
+                                 ra2a.Opts(direction=ra2a.DIR_DISPATCH)).mode == ra2a.MODE_DIRECT
+    assert ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16",
+                                 ra2a.Opts(straggler_rank=2, straggler_delay=100)).mode == ra2a.MODE_DIRECT
+    assert ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16",
+                                 ra2a.Opts(straggler_rank=2)).mode == ra2a.MODE_ROWS
     # per-source pieces: 16 heads merged into 4 KiB runs, so a piece (one source's 64
     # tokens) is 256 KiB and moves as two parts of 32 tokens: one arrival counter per
     # moved tile (S-block) in region B
