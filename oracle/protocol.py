@@ -323,6 +323,10 @@ def explore_all(spec: ProtocolSpec, max_states: int = 2_000_000) -> Tuple[int, L
 #   * the unit whose add brings the counter to the block's unit count signals
 #     every tile of the block: ADD W on each tile slot, or SET 1 on each (tile,
 #     source) slot -- the values W per-source pieces would have left.
+# Variant (share): under ADD, in a block whose unit count n divides W, every
+# unit adds W / n to each tile of its block after its own fence, and still
+# counts itself; a tile then reads W exactly when all n units have published
+# their rows, with no unit waiting for the count.
 # Readings where the pages say nothing (they have no row units): the counter is
 # a monotone count of arrivals zeroed with the signals before the launch, and
 # it ends at the block's unit count.  Visibility is modelled as above (a write
@@ -357,6 +361,9 @@ class RowSpec:
     skip_reset: bool = False          # counters and signals keep the previous launch's finals
     count_before_fence: bool = False  # the arrival is counted before the rows are published
     signal_every_unit: bool = False   # no counter: each unit signals its block on its own
+    share: bool = False               # ADD, n | W: each unit adds W / n after its fence
+    share_full: bool = False          # negative control: each sharing unit adds all of W
+    share_before_fence: bool = False  # negative control: the share is added before the fence
 
 
 def row_units(spec: RowSpec) -> List[Tuple[int, int, int]]:
@@ -396,17 +403,23 @@ class _RowRun:
         self.visible = set()
         self.violations: List[str] = []
 
-    def _steps(self):
+    def _shares(self, b):
+        """Whether the units of block b add shares (ADD, unit count divides W)."""
+        return self.spec.share and self.spec.protocol == ADD and self.spec.W % self.spec.units[b] == 0
+
+    def _steps(self, b=0):
         if self.spec.signal_every_unit:
             return ("write", "fence", "signal")
+        if self._shares(b) and self.spec.share_before_fence:
+            return ("write", "signal", "fence", "count")
         if self.spec.count_before_fence:
             return ("write", "count", "fence", "signal")
         return ("write", "fence", "count", "signal")
 
-    def _signal_block(self, j, b):
+    def _signal_block(self, j, b, amount=None):
         for t in range(self.spec.nstreams):
             if self.spec.protocol == ADD:
-                self.sig[(j, t, b)] = self.sig.get((j, t, b), 0) + self.spec.W
+                self.sig[(j, t, b)] = self.sig.get((j, t, b), 0) + (self.spec.W if amount is None else amount)
             else:
                 for r in range(self.spec.W):
                     self.sig[(j, t, b, r)] = 1
@@ -418,7 +431,8 @@ class _RowRun:
         li, st = self.wpc[a]
         u = self.work[a][li]
         j, b, k = u
-        kind = self._steps()[st]
+        steps = self._steps(b)
+        kind = steps[st]
         if kind == "write":
             self.pending.add(u)
         elif kind == "fence":
@@ -430,10 +444,13 @@ class _RowRun:
             self.cnt[(j, b)] = c
             self.last[u] = c == self.spec.units[b]
         elif kind == "signal":
-            if self.spec.signal_every_unit or self.last.get(u, False):
+            if self._shares(b):
+                n = self.spec.units[b]
+                self._signal_block(j, b, self.spec.W if self.spec.share_full else self.spec.W // n)
+            elif self.spec.signal_every_unit or self.last.get(u, False):
                 self._signal_block(j, b)
         st += 1
-        if st == len(self._steps()):
+        if st == len(steps):
             li, st = li + 1, 0
         self.wpc[a] = [li, st]
 

@@ -164,6 +164,36 @@ def test_rows_negative_controls_fire(control, protocol):
     assert violations, f"{control} must let a consumer read unpublished rows"
 
 
+@pytest.mark.parametrize("workers", [2, 3])
+@pytest.mark.parametrize("units", [(2, 1), (1, 2), (2, 2)])
+def test_rows_share_exhaustive_no_violation(units, workers):
+    """ADD shares (each unit of a block with n | W units adds W / n): no consumer
+    reads unpublished rows in any interleaving, and the finals are the closed
+    forms."""
+    spec = row_spec(ADD, units=units, n_workers=workers, share=True)
+    states, violations, stuck = explore_rows(spec)
+    assert states > 100
+    assert violations == [] and not stuck
+
+
+def test_rows_share_seeded_schedules_match_closed_forms():
+    # W = 4: blocks of 4 and 2 units share (4 / 4 = 1, 4 / 2 = 2), 3 units count
+    spec = row_spec(ADD, W=4, units=(4, 2, 3, 1), nstreams=2, n_workers=5, n_consumers=3,
+                    share=True)
+    want_sig, want_cnt = expected_row_finals(spec)
+    for seed in range(100):
+        out = run_rows_random(spec, seed)
+        assert out.completed and out.violations == []
+        assert out.signals == want_sig and out.counters == want_cnt
+
+
+@pytest.mark.parametrize("control", ["share_full", "share_before_fence"])
+def test_rows_share_negative_controls_fire(control):
+    spec = row_spec(ADD, units=(2, 1), n_workers=3, share=True, **{control: True})
+    _, violations, _ = explore_rows(spec)
+    assert violations, f"{control} must let a consumer read unpublished rows"
+
+
 def test_piece_counts_worked():
     from oracle.protocol import expected_final_piece_counts
     # the MoE-combine shape: 32-token tiles cut into 8-token pieces, 8 sources, ADD
