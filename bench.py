@@ -1,7 +1,8 @@
 """Benchmark of the Reverse All2All combine on one MI355X.
 
 One step = one whole combine: the signal reset, then the signal-pipelined
-persistent kernel (direct mode, the library default), over the EP-combine
+persistent kernel (the library default: direct mode with row units on this
+shape), over the EP-combine
 workload: W=8 simulated ranks (slices of one symmetric heap), S=512 tokens,
 H=16 heads, D=128, bf16 values uniform(-1, 1) from seed 0, 64 x 1 x 128
 signal tiles with ADD-to-W tile signals.  Inputs are resident in HBM before
@@ -17,9 +18,10 @@ step's reset launch on a side stream while the previous step's combine runs
 
 Prints one JSON line: metric and value (GB/s of algorithmic bytes: every input
 element read once and every output element written once, per step), the
-roofline of the persistent kernel (its duration from HIP events around every
-launch, on the launch stream, in a separate pass over the same steps: events
-between kernels slow the steps themselves), and for context the staged mode, the two-phase variant, a
+roofline of the persistent kernel (its average launch duration: HIP events on
+the launch stream around the in-launch timed region, one launch per step, no
+events between launches), and for context per-source pieces, the staged mode,
+the two-phase variant, a
 plain copy of the same bytes with the library's put kernel, the bulk mode
 (two-phase layout with per-(S-block, sender) signals), the pull mode, the forward
 All2All (dispatch, the combine's inverse map) on the same buffers, and the CPU
@@ -748,8 +750,8 @@ def copy_ceiling(nbytes, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--legs", choices=["all", "main", "moe", "straggler", "ag_gemm", "gemm_rs",
                                        "alltoallv", "staged_ring"], default="all")
