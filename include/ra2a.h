@@ -254,9 +254,10 @@ typedef struct ra2a_opts {
                                * its consumer copy) */
     int32_t mode;             /* 0: the default -- RA2A_MODE_ROWS for the combine when
                                * one source's run of a token row, H*D*e bytes, is at
-                               * most 8 KiB and none of a delayed straggler source,
-                               * head_merge or piece_rows is set; RA2A_MODE_DIRECT
-                               * otherwise (always for the dispatch).
+                               * most 8 KiB and divides or is a multiple of 4096, and
+                               * none of a delayed straggler source, head_merge or
+                               * piece_rows is set; RA2A_MODE_DIRECT otherwise (always
+                               * for the dispatch).
                                * RA2A_MODE_ROWS: each work unit fills unit_rows whole
                                * token rows of out_j (the W sources' runs of H*D elements,
                                * one contiguous range of out_j; W contiguous ranges of

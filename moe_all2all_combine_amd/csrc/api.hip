@@ -160,12 +160,14 @@ constexpr int64_t kRowUnitBytes = 256 << 10;
 constexpr int64_t kRowWholeRun = 4 << 10;
 constexpr int64_t kRowUnitsMin = 256;
 // Mode 0 moves row units when one source's run of a token row (H*D*e bytes) is at
-// most this, per-source pieces above it.  Measured on gfx950 (bf16, tile_s 64,
-// percent of 8 TB/s, row units against pieces): runs of 1 KiB (W=8, S=2048, H=4,
-// D=128) 69 against 57, 4 KiB (W=8, S=512, H=16, D=128) 71 against 69, 4 KiB at
-// W=16 71 against 67, 8 KiB (W=8, S=512, H=16, D=256) 71 against 66, equal at
-// 4 KiB and 1 GiB (W=8, S=4096, H=16, D=128); 14 KiB (W=8, S=4096, H=1,
-// D=7168) 72 against 74 and 16 KiB (W=16, S=2048, H=32, D=128 f32) 70 against 76.
+// most this and divides or is a multiple of the 4 KiB round (kRowWholeRun),
+// per-source pieces otherwise.  Measured on gfx950 (bf16, tile_s 64, percent of
+// 8 TB/s, row units against pieces): runs of 1 KiB (W=8, S=2048, H=4, D=128) 70
+// against 57, 4 KiB (W=8, S=512, H=16, D=128) 72 against 69, 4 KiB at W=16 74
+// against 67, 8 KiB (W=8, S=512, H=16, D=256) 73 against 66, 4 KiB at 1 GiB
+// (W=8, S=4096, H=16, D=128) 77 against 75; but 3 KiB (D=96) 58 against 63,
+// 6 KiB (H=24) 62 against 64, 14 KiB (W=8, S=4096, H=1, D=7168) 69 against 74
+// and 16 KiB (W=16, S=2048, H=32, D=128 f32) 67 against 76.
 constexpr int64_t kRowsMaxRun = 8 << 10;
 // Default bytes per direct-mode piece: a tile's rows of one source larger than
 // this are cut into ceil(bytes / kPieceBytes) pieces of equal token counts.
@@ -283,13 +285,16 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     p->agent_sync = o->agent_sync ? 1 : 0;
     p->direct = (o->mode == RA2A_MODE_STAGED || p->bulk) ? 0 : 1;
     // Row units when asked for, and by default for the combine when a source's
-    // run of a token row (H*D*e) is at most kRowsMaxRun and nothing asks for
-    // per-source pieces (a delayed straggler source, head merging or piece sizes
-    // set by the caller); otherwise per-source pieces.
+    // run of a token row (H*D*e) is at most kRowsMaxRun, divides or is a multiple
+    // of the 4 KiB round, and nothing asks for per-source pieces (a delayed
+    // straggler source, head merging or piece sizes set by the caller); otherwise
+    // per-source pieces.
     const bool pieces_asked = (o->straggler_rank >= 0 && o->straggler_delay > 0) ||
                               o->head_merge > 0 || o->piece_rows > 0;
-    p->rows = (o->mode == RA2A_MODE_ROWS ||
-               (o->mode == 0 && !p->inverse && !pieces_asked && H * D * e <= kRowsMaxRun))
+    const int64_t run = H * D * e;
+    const bool rows_run = run <= kRowsMaxRun && run > 0 &&
+                          (run % kRowWholeRun == 0 || kRowWholeRun % run == 0);
+    p->rows = (o->mode == RA2A_MODE_ROWS || (o->mode == 0 && !p->inverse && !pieces_asked && rows_run))
                   ? 1
                   : 0;
     p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);

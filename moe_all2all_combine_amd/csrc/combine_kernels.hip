@@ -218,26 +218,24 @@ __device__ __forceinline__ void copy_plan_wt(const uint8_t* __restrict__ src,
 }
 
 // Copy of the runs (a, b) of a plan with C == 1 and sb == run, so that each a's
-// B runs are one contiguous source range: run (a, b) goes from src + a*sa +
-// b*run to dst + a*da + b*db.  The ranges are moved in rounds of kThreads * V
-// contiguous bytes (lane t takes bytes [t*V, t*V + V) of each), a after a, U
-// rounds in flight (all loads, then all stores; a group may span several a);
-// device-scope write-through stores as in copy_plan_wt.  Two run shapes
-// (run_shape_ok):
-//  - a run of m whole rounds: a round lies in one run, so its destination is the
-//    same for the whole workgroup (scalar registers) plus the lane's column;
-//  - k runs per round (kThreads * V = k * run): a lane's run inside the round
-//    and column inside the run are fixed, so its destination is round q's first
-//    run (q*k) plus a per-lane constant; each a's last, partial round (B not a
-//    multiple of k) moves in a second pass, by the lanes whose run it holds.
-// Round offsets advance with selects, not branches, so that a group's loads
-// issue back to back.  `mid()` runs once, about half-way (before the first group
-// past the middle), so that what it issues completes under the rest of the copy.
-template <int V>
+// B runs are one contiguous source range of B*run bytes: run (a, b) goes from
+// src + a*sa + b*run to dst + a*da + b*db.  The ranges are moved in rounds of
+// kThreads * V contiguous bytes (lane t takes bytes [t*V, t*V + V) of each), a
+// after a, U rounds in flight (all loads, then all stores; a group may span
+// several a); device-scope write-through stores as in copy_plan_wt.  The
+// source offset of a round is the same for the whole workgroup (scalar
+// registers) plus the lane's column.  The destination:
+//  - runs of whole rounds: a round lies in one run, so its destination is also
+//    workgroup-uniform plus the lane's column;
+//  - any other run: each lane keeps its own (column in the run, destination),
+//    advanced by the round's kThreads * V bytes with one wrap test per round.
+// Each a's last, partial round (B*run not a multiple of the round) moves in a
+// second pass, by the lanes whose bytes it holds.  Round offsets advance with
+// selects, not branches, so that a group's loads issue back to back.  `mid()`
+// runs once, about half-way (before the first group past the middle), so that
+// what it issues completes under the rest of the copy.
 __device__ __forceinline__ bool run_shape_ok(const RowPlan& p) {
-    constexpr int kChunk = kThreads * V;
-    return p.C == 1 && p.sb == p.run && p.run > 0 &&
-           (p.run % kChunk == 0 || kChunk % p.run == 0);
+    return p.C == 1 && p.sb == p.run && p.run > 0;
 }
 
 template <int V, int U, typename Mid>
@@ -246,39 +244,55 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
                                              Mid&& mid) {
     using T = typename Vec<V>::T;
     constexpr int kChunk = kThreads * V;
-    const bool whole = p.run >= kChunk;             // runs of m whole rounds
-    const int m = whole ? p.run / kChunk : 1;        // rounds per run
-    const int k = whole ? 1 : kChunk / p.run;        // runs per round
-    const int nq = whole ? p.B * m : p.B / k;        // full rounds per a
-    const int rem = whole ? 0 : p.B - nq * k;        // runs of a last, partial round
+    const uint32_t R = (uint32_t)p.run;
+    const bool whole = R % kChunk == 0;              // runs of m whole rounds
+    const int m = whole ? (int)(R / kChunk) : 1;     // rounds per run
+    const int64_t len = (int64_t)p.B * R;            // bytes per a
+    const int nq = (int)(len / kChunk);              // full rounds per a
+    const uint32_t remb = (uint32_t)(len - (int64_t)nq * kChunk);  // bytes of a partial round
     const uint32_t lane = threadIdx.x * V;
-    const uint32_t db = (uint32_t)p.db;
-    // k runs per round: the lane's run inside a round, and its destination offset
-    const uint32_t lrun = whole ? 0u : lane / (uint32_t)p.run;
-    const uint32_t lane_dst = whole ? lane : lrun * db + (lane - lrun * (uint32_t)p.run);
-    // destination steps: to the next round of the same run, to the first round of
-    // the next run of the same a, and from the last round of an a to the first of
-    // the next (modulo 2^32, like the offsets)
-    const uint32_t next_run = whole ? db - (uint32_t)(m - 1) * kChunk : (uint32_t)k * db;
-    const uint32_t next_a = whole ? (uint32_t)p.da - ((uint32_t)(p.B - 1) * db + (uint32_t)(m - 1) * kChunk)
-                                  : (uint32_t)p.da - (uint32_t)(nq - 1) * (uint32_t)k * db;
+    const uint32_t db = (uint32_t)p.db, da = (uint32_t)p.da;
+    // other runs: the lane's column in its run and destination in round 0, and
+    // the per-round steps (kThreads * V = sr runs + sc bytes)
+    const uint32_t col0 = whole ? lane : lane % R;
+    const uint32_t lane_dst = whole ? lane : (lane / R) * db + col0;
+    const uint32_t sc = whole ? 0u : (uint32_t)kChunk % R;
+    const uint32_t step = whole ? 0u : ((uint32_t)kChunk / R) * db + sc;
+    // whole runs: destination steps to the next round of the same run, to the
+    // next run of the same a, and from an a's last round to the next a's first
+    // (modulo 2^32, like the offsets)
+    const uint32_t next_run = db - (uint32_t)(m - 1) * kChunk;
+    const uint32_t next_a = da - ((uint32_t)(p.B - 1) * db + (uint32_t)(m - 1) * kChunk);
     const int64_t src_next_a = p.sa - (int64_t)(nq - 1) * kChunk;
     const int total = p.A * nq;
     const uint8_t* const s_lane = src + lane;
     int q = 0, c = 0;
     int64_t so = 0;
-    uint32_t dof = lane_dst;
-    auto advance = [&]() {
-        const bool end_run = c + 1 == m;
+    uint32_t dof = lane_dst;  // whole runs: the destination; others: relative to abase
+    uint32_t abase = 0, col = col0;
+    auto advance = [&](auto whole_c) {
+        constexpr bool WHOLE = decltype(whole_c)::value;
         const bool end_a = q + 1 == nq;
         so += end_a ? src_next_a : (int64_t)kChunk;
-        dof += end_a ? next_a : (end_run ? next_run : (uint32_t)kChunk);
-        c = end_run ? 0 : c + 1;
+        if (WHOLE) {
+            const bool end_run = c + 1 == m;
+            dof += end_a ? next_a : (end_run ? next_run : (uint32_t)kChunk);
+            c = end_run ? 0 : c + 1;
+        } else {
+            col += sc;
+            dof += step;
+            const bool wrap = col >= R;
+            col = wrap ? col - R : col;
+            dof = wrap ? dof + (db - R) : dof;
+            col = end_a ? col0 : col;
+            dof = end_a ? lane_dst : dof;
+            abase = end_a ? abase + da : abase;
+        }
         q = end_a ? 0 : q + 1;
     };
     bool mid_done = false;
     int f = 0;
-    auto group = [&](auto kc) {
+    auto group = [&](auto kc, auto whole_c) {
         constexpr int K = decltype(kc)::value;
         if (!mid_done && 2 * f >= total) {
             mid();
@@ -289,8 +303,8 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             sofs[u] = so;
-            d[u] = dof;
-            advance();
+            d[u] = abase + dof;
+            advance(whole_c);
         }
         T v[K];
 #pragma unroll
@@ -299,14 +313,23 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
         for (int u = 0; u < K; ++u) BufStore<V, kPolicyDevNt>::go(v[u], dst, d[u]);
         f += K;
     };
-    while (f + U <= total) group(std::integral_constant<int, U>{});
-    if (U >= 4 && f + U / 2 <= total) group(std::integral_constant<int, (U >= 4 ? U / 2 : 1)>{});
-    while (f < total) group(std::integral_constant<int, 1>{});
+    auto rounds = [&](auto whole_c) {
+        while (f + U <= total) group(std::integral_constant<int, U>{}, whole_c);
+        if (U >= 4 && f + U / 2 <= total)
+            group(std::integral_constant<int, (U >= 4 ? U / 2 : 1)>{}, whole_c);
+        while (f < total) group(std::integral_constant<int, 1>{}, whole_c);
+    };
+    if (whole)
+        rounds(std::true_type{});
+    else
+        rounds(std::false_type{});
     if (!mid_done) mid();
-    // the partial rounds (k runs per round, B % k of them left per a), one per a
-    if (rem > 0 && lrun < (uint32_t)rem) {
+    // the partial rounds, one per a: bytes nq*kChunk + lane of each a's range
+    if (remb > 0 && lane < remb) {
+        const uint32_t o = (uint32_t)nq * kChunk + lane;
+        const uint32_t ri = o / R;
         const int64_t s_part = (int64_t)nq * kChunk;
-        const uint32_t d_part = (uint32_t)nq * (uint32_t)k * db + lane_dst;
+        const uint32_t d_part = ri * db + (o - ri * R);
         int a0 = 0;
         auto part = [&](auto kc) {
             constexpr int K = decltype(kc)::value;
@@ -316,7 +339,7 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
                 v[u] = load_nt(reinterpret_cast<const T*>(s_lane + (int64_t)(a0 + u) * p.sa + s_part));
 #pragma unroll
             for (int u = 0; u < K; ++u)
-                BufStore<V, kPolicyDevNt>::go(v[u], dst, (uint32_t)((int64_t)(a0 + u) * p.da) + d_part);
+                BufStore<V, kPolicyDevNt>::go(v[u], dst, (uint32_t)(a0 + u) * da + d_part);
             a0 += K;
         };
         while (a0 + U <= p.A) part(std::integral_constant<int, U>{});
@@ -688,7 +711,7 @@ __device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
         auto poll = [&]() {
             if (!published && (int)threadIdx.x < nz) early = sig_load(reset_flag(a, (int)threadIdx.x));
         };
-        if (run_shape_ok<V>(q.pl)) {
+        if (run_shape_ok(q.pl)) {
             if (a.ru == 4)
                 copy_runs_wt<V, 4>(a.base + q.src, dst, q.pl, poll);
             else

@@ -99,8 +99,12 @@ def test_signal_slots_and_workspace():
     # 8 KiB runs: 512 KiB units (8 tokens), 256 of them
     p = ra2a.rev_all2all_plan(8, 256, 32, 128, "bf16")
     assert (p.mode, p.unit_rows, p.work_items) == (ra2a.MODE_ROWS, 8, 4 * 8 * 8)
-    # runs above 8 KiB, the dispatch, a delayed straggler source: per-source pieces
+    # runs above 8 KiB, runs that neither divide nor are a multiple of 4 KiB (3 and
+    # 6 KiB), the dispatch, a delayed straggler source: per-source pieces
     assert ra2a.rev_all2all_plan(8, 256, 1, 7168, "bf16").mode == ra2a.MODE_DIRECT
+    assert ra2a.rev_all2all_plan(8, 512, 16, 96, "bf16").mode == ra2a.MODE_DIRECT
+    assert ra2a.rev_all2all_plan(8, 512, 24, 128, "bf16").mode == ra2a.MODE_DIRECT
+    assert ra2a.rev_all2all_plan(8, 512, 4, 64, "bf16").mode == ra2a.MODE_ROWS  # 512 B runs
     assert ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16",
                                  ra2a.Opts(direction=ra2a.DIR_DISPATCH)).mode == ra2a.MODE_DIRECT
     assert ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16",
