@@ -252,12 +252,12 @@ typedef struct ra2a_opts {
                                * at timestamps[j * tile_slots + u] (direct mode: the
                                * latest of its pieces' signals; staged mode: the end of
                                * its consumer copy) */
-    int32_t mode;             /* 0: the default -- RA2A_MODE_ROWS for the combine when
-                               * one source's run of a token row, H*D*e bytes, is at
-                               * most 8 KiB and divides or is a multiple of 4096, and
-                               * none of a delayed straggler source, head_merge or
-                               * piece_rows is set; RA2A_MODE_DIRECT otherwise (always
-                               * for the dispatch).
+    int32_t mode;             /* 0: the default -- RA2A_MODE_ROWS when one source's run
+                               * of a token row, H*D*e bytes, is at most 8 KiB and
+                               * divides or is a multiple of 4096, and none of a
+                               * delayed straggler source, head_merge or piece_rows is
+                               * set; RA2A_MODE_DIRECT otherwise (the combine and the
+                               * dispatch alike).
                                * RA2A_MODE_ROWS: each work unit fills unit_rows whole
                                * token rows of out_j (the W sources' runs of H*D elements,
                                * one contiguous range of out_j; W contiguous ranges of
@@ -270,7 +270,12 @@ typedef struct ra2a_opts {
                                * completes the block's count marks every signal tile of
                                * the block complete (ADD W, or SET 1 on each (tile,
                                * source) slot).  Either way the final values are the ones
-                               * W pieces would leave.  Not for the dispatch, nor with a
+                               * W pieces would leave.  The dispatch's unit is the mirror
+                               * image: source j's unit_rows rows of in_j, read whole,
+                               * give each destination r one contiguous range (rows
+                               * j*S + s0 .. of out_r), and the unit that completes the
+                               * block's count (region B of slice j) sets the block's
+                               * (tile, j) slot in every destination's slice.  Not with a
                                * delayed straggler source (every unit carries all
                                * sources).
                                * RA2A_MODE_DIRECT: producers store each piece (one
@@ -435,7 +440,8 @@ int ra2a_rev_all2all_ex(const void *in, void *out, uint64_t *signals, int W, int
  * combine: the signal tile (source j's S-block b, head block, d block) of
  * destination r has one slot per source (the SET layout,
  * ra2a_rev_all2all_signal_slots with direction = RA2A_DIR_DISPATCH), and each
- * ends at 1.  Staged mode is rejected (EINVAL).  _ex takes the combine's
+ * ends at 1.  Row units and per-source pieces as for the combine (the same
+ * default rule); staged mode is rejected (EINVAL).  _ex takes the combine's
  * options (direction is forced to RA2A_DIR_DISPATCH).
  * Errors: EINVAL, EHIP.                                                         */
 int ra2a_all2all_dispatch(const void *in, void *out, uint64_t *signals, int W, int64_t S,

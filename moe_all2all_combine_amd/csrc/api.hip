@@ -222,8 +222,6 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     if (o->mode != 0 && o->mode != RA2A_MODE_DIRECT && o->mode != RA2A_MODE_STAGED &&
         o->mode != RA2A_MODE_BULK && o->mode != RA2A_MODE_PULL && o->mode != RA2A_MODE_ROWS)
         return fail(RA2A_EINVAL, "mode must be 0, RA2A_MODE_ROWS, _DIRECT, _STAGED, _BULK or _PULL");
-    if (o->mode == RA2A_MODE_ROWS && o->direction == RA2A_DIR_DISPATCH)
-        return fail(RA2A_EINVAL, "row units are a combine mode (the dispatch runs in direct mode)");
     if (o->mode == RA2A_MODE_ROWS && o->straggler_rank >= 0 && o->straggler_delay > 0)
         return fail(RA2A_EINVAL, "a straggler source needs per-source pieces: every row unit "
                                  "carries all sources (use RA2A_MODE_DIRECT)");
@@ -284,19 +282,17 @@ int make_plan(int W, int64_t S, int64_t H, int64_t D, int e, const ra2a_opts_t* 
     p->stream_batch = o->stream_batch;
     p->agent_sync = o->agent_sync ? 1 : 0;
     p->direct = (o->mode == RA2A_MODE_STAGED || p->bulk) ? 0 : 1;
-    // Row units when asked for, and by default for the combine when a source's
-    // run of a token row (H*D*e) is at most kRowsMaxRun, divides or is a multiple
-    // of the 4 KiB round, and nothing asks for per-source pieces (a delayed
-    // straggler source, head merging or piece sizes set by the caller); otherwise
-    // per-source pieces.
+    // Row units when asked for, and by default (the combine and the dispatch)
+    // when a source's run of a token row (H*D*e) is at most kRowsMaxRun, divides
+    // or is a multiple of the 4 KiB round, and nothing asks for per-source pieces
+    // (a delayed straggler source, head merging or piece sizes set by the
+    // caller); otherwise per-source pieces.
     const bool pieces_asked = (o->straggler_rank >= 0 && o->straggler_delay > 0) ||
                               o->head_merge > 0 || o->piece_rows > 0;
     const int64_t run = H * D * e;
     const bool rows_run = run <= kRowsMaxRun && run > 0 &&
                           (run % kRowWholeRun == 0 || kRowWholeRun % run == 0);
-    p->rows = (o->mode == RA2A_MODE_ROWS || (o->mode == 0 && !p->inverse && !pieces_asked && rows_run))
-                  ? 1
-                  : 0;
+    p->rows = (o->mode == RA2A_MODE_ROWS || (o->mode == 0 && !pieces_asked && rows_run)) ? 1 : 0;
     p->unit_bytes = p->piece_bytes * (p->protocol == RA2A_SIG_SET ? 1 : W);
     if (o->consumer_split < 0 || o->wg_per_cu < 0 || o->lookahead < -1)
         return fail(RA2A_EINVAL, "negative option");
@@ -1874,16 +1870,26 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
             std::vector<std::pair<int64_t, int64_t>> offs;
             rc = walk_plan(q.pl, V, 0, ra2a::plan_vectors(q.pl, V), &offs);
             if (rc) return rc;
+            // the dispatch stores to every destination r through r's own descriptor,
+            // which covers the unit's rows of out_r (rows * run bytes)
+            const int64_t run_b = (int64_t)q.pl.run;
             for (const auto& o : offs) {
-                if (o.second < 0 || o.second + V > (int64_t)ra2a::plan_span(q.pl))
-                    return fail(RA2A_EINVAL, "row unit store outside its descriptor's range");
                 const int64_t so = q.src + o.first;
                 const int r = (int)(so / stride);
                 if (r < 0 || r >= W || !inside(so, V, r, in_off, nb))
                     return fail(RA2A_EINVAL, "row unit reads outside every input");
-                if (!inside(q.dst + o.second, V, q.j, out_off, nb))
-                    return fail(RA2A_EINVAL, "row unit writes outside out of rank %d", q.j);
-                std::memcpy(&heap[(size_t)(q.dst + o.second)], &heap[(size_t)so], (size_t)V);
+                const int64_t dabs = q.dst + o.second;
+                const int rd = (int)(dabs / stride);
+                if (pl.inverse) {
+                    const int64_t rel = dabs - (int64_t)rd * stride - q.dst;
+                    if (rd < 0 || rd >= W || rel < 0 || rel + V > (int64_t)q.rows * run_b)
+                        return fail(RA2A_EINVAL, "row unit store outside its descriptor's range");
+                } else if (o.second < 0 || o.second + V > (int64_t)ra2a::plan_span(q.pl)) {
+                    return fail(RA2A_EINVAL, "row unit store outside its descriptor's range");
+                }
+                if (!inside(dabs, V, pl.inverse ? rd : q.j, out_off, nb))
+                    return fail(RA2A_EINVAL, "row unit writes outside out of rank %d", rd);
+                std::memcpy(&heap[(size_t)dabs], &heap[(size_t)so], (size_t)V);
             }
             if (!inside(q.cnt, 8, q.j, sig_off + sigA_len, sigB_len))
                 return fail(RA2A_EINVAL, "row unit counter outside region B");
@@ -1891,12 +1897,14 @@ RA2A_API int ra2a_debug_emulate_pipelined(const void* const* in, void* const* ou
             if (*u64(q.cnt) > (uint64_t)q.nub)
                 return fail(RA2A_EINVAL, "block counter beyond its unit count");
             if (*u64(q.cnt) == (uint64_t)q.nub)  // the unit that completes the block
-                for (int k = 0; k < q.nsig; ++k) {
-                    const int64_t sg = q.sig + (int64_t)k * RA2A_SIG_STRIDE_BYTES;
-                    if (!inside(sg, 8, q.j, sig_off, sigA_len))
-                        return fail(RA2A_EINVAL, "row unit signal outside region A");
-                    *u64(sg) = add ? *u64(sg) + (uint64_t)W : 1;
-                }
+                for (int d = 0; d < q.nd; ++d)
+                    for (int k = 0; k < q.nsig; ++k) {
+                        const int64_t sg = q.sig + (int64_t)d * stride + (int64_t)k * q.sig_step;
+                        const int rs = q.nd == 1 ? q.j : d;
+                        if (!inside(sg, 8, rs, sig_off, sigA_len))
+                            return fail(RA2A_EINVAL, "row unit signal outside region A");
+                        *u64(sg) = add ? *u64(sg) + (uint64_t)W : 1;
+                    }
         }
         for (uint8_t x : rowhit)
             if (x != 1) return fail(RA2A_EINVAL, "row units do not write every output row once");

@@ -345,32 +345,41 @@ RA2A_HD int64_t total_pieces(const PipeArgs& a) {
     return stream_subtiles(a) * a.nstreams * a.W;
 }
 
-// Row units (direct mode, the default combine).  A row unit fills rows
-// [s0, s0 + rows) of out_j completely: for each of those tokens the W sources'
-// runs of H*D elements, which are contiguous in out_j (columns r*H .. r*H + H - 1
-// for r = 0 .. W-1 make up a whole output row) and contiguous, token after token,
-// in each in_r (rows j*S + s0 ..).  So a unit writes one contiguous range of out_j
+// Row units (direct mode).  A combine row unit fills rows [s0, s0 + rows) of
+// out_j completely: for each of those tokens the W sources' runs of H*D
+// elements, which are contiguous in out_j (columns r*H .. r*H + H - 1 for
+// r = 0 .. W-1 make up a whole output row) and contiguous, token after token, in
+// each in_r (rows j*S + s0 ..).  So a unit writes one contiguous range of out_j
 // and reads W contiguous ranges.  It copies source by source (one source's rows,
 // then the next source's): on gfx950 reading each range in order while the
 // output fills as W interleaved streams measured faster than filling the output
-// token by token (W = 8, S = 512, H = 16, D = 128 bf16: 47 against 60 us).  The signal tiles of S-block b are complete once
-// every unit of b has stored its rows: each unit releases its stores device-wide
-// and adds 1 to the block's arrival counter (region B of slice j); the unit that
-// brings it to `nub` (the block's unit count) acquires and releases, then marks
-// every signal tile of the block complete -- ADD W on the tile's slot, or SET 1 on
-// each (tile, source) slot -- exactly the values W pieces would have left.
-// Units are ordered S-block first, then the unit inside the block, then the
-// destination, so that early tiles of every destination complete first.
+// token by token (W = 8, S = 512, H = 16, D = 128 bf16: 47 against 60 us).
+// The dispatch's row unit is the mirror image: source j's rows [s0, s0 + rows)
+// of in_j, read whole, give each destination r one contiguous range, rows
+// j*S + s0 .. of out_r, destination by destination.
+// The signal tiles of S-block b are complete once every unit of b has stored
+// its rows: each unit releases its stores device-wide and adds 1 to the block's
+// arrival counter (region B of slice j); the unit that brings it to `nub` (the
+// block's unit count) marks every signal tile of the block complete -- ADD W on
+// the tile's slot, or SET 1 on each (tile, source) slot (the dispatch: in every
+// destination's slice) -- exactly the values W pieces would have left; or, under
+// ADD with nub dividing W, every unit adds W / nub itself (the kernel's choice).
+// Units are ordered S-block first, then the unit inside the block, then j, so
+// that early tiles of every destination complete first.
 struct RowUnit {
     int32_t j, b, k, rows, nub;
     int64_t src;          // absolute byte offset of in_0[j*S + s0] (slice 0); source r is
                           // r slices further (the plan's middle digit)
     int64_t dst;          // absolute byte offset of out_j[s0] (slice j)
     RowPlan pl;
-    int64_t sig;          // absolute byte offset of the block's first data signal (slice j)
-    int32_t nsig;         // data-signal slots of the block (consecutive, one slot apart)
-    int64_t cnt;          // absolute byte offset of the block's arrival counter (slice j)
+    int64_t sig;          // absolute byte offset of the block's first data signal (slice j;
+                          // the dispatch: in destination slice 0)
+    int32_t nsig;         // data-signal slots of the block, per destination
+    int64_t sig_step;     // bytes between consecutive ones
+    int32_t nd;           // destinations signalled: 1 (the combine: j) or W (the dispatch)
     int64_t unit_index;   // slot index of the block's first data signal (timestamp row)
+    int64_t unit_step;    // slot distance between consecutive ones
+    int64_t cnt;          // absolute byte offset of the block's arrival counter (slice j)
 };
 
 // Row units of S-block b (of any destination).
@@ -399,9 +408,35 @@ RA2A_HD RowUnit row_unit(const PipeArgs& a, int64_t u) {
     const int64_t s0 = (int64_t)q.b * a.BS + (int64_t)q.k * a.KU;
     q.rows = (int)geom_min(a.KU, bs - (int64_t)q.k * a.KU);
     const int64_t run = a.H * a.D * e;  // one source's part of a token row
+    RowPlan& pl = q.pl;
+    const int64_t sig_j = (int64_t)q.j * a.stride + a.sig_off;
+    q.cnt = sig_j + (a.regionA + q.b) * kSigStrideU64 * 8;
+    if (a.inverse) {
+        // the dispatch: unit (source j, rows s0 ..) reads whole rows of in_j
+        // ([H*W][D] columns) and gives each destination r its run, rows j*S + s0 ..
+        // of out_r: destination by destination, each one contiguous range
+        q.src = (int64_t)q.j * a.stride + a.in_off + s0 * run * a.W;
+        q.dst = a.out_off + ((int64_t)q.j * a.S + s0) * run;  // destination r: r slices further
+        pl.A = a.W;       // destinations
+        pl.sa = run;
+        pl.da = a.stride;
+        pl.B = q.rows;    // tokens
+        pl.sb = run * a.W;
+        pl.db = run;
+        pl.C = 1;
+        pl.sc = pl.dc = 0;
+        pl.run = (int)run;
+        // SET per (tile, source j) in each destination's slice
+        q.unit_index = tile_slot(a, q.b, 0, 0, q.j);
+        q.unit_step = a.W;
+        q.sig = a.sig_off + q.unit_index * kSigStrideU64 * 8;
+        q.nsig = a.nhb * a.ndb;
+        q.sig_step = (int64_t)a.W * kSigStrideU64 * 8;
+        q.nd = a.W;
+        return q;
+    }
     q.src = a.in_off + ((int64_t)q.j * a.S + s0) * run;
     q.dst = (int64_t)q.j * a.stride + a.out_off + s0 * run * a.W;
-    RowPlan& pl = q.pl;
     pl.A = a.W;         // sources: each one's rows are read in one contiguous range
     pl.sa = a.stride;
     pl.da = run;
@@ -412,11 +447,12 @@ RA2A_HD RowUnit row_unit(const PipeArgs& a, int64_t u) {
     pl.sc = pl.dc = 0;
     pl.run = (int)run;
     const int64_t per_block_slots = (int64_t)a.nhb * a.ndb * (a.protocol == kSigAdd ? 1 : a.W);
-    const int64_t sig_base = (int64_t)q.j * a.stride + a.sig_off;
     q.unit_index = (int64_t)q.b * per_block_slots;
-    q.sig = sig_base + q.unit_index * kSigStrideU64 * 8;
+    q.unit_step = 1;
+    q.sig = sig_j + q.unit_index * kSigStrideU64 * 8;
     q.nsig = (int32_t)per_block_slots;
-    q.cnt = sig_base + (a.regionA + q.b) * kSigStrideU64 * 8;
+    q.sig_step = kSigStrideU64 * 8;
+    q.nd = 1;
     return q;
 }
 

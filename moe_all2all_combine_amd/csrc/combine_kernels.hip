@@ -347,6 +347,104 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
     }
 }
 
+// The mirror image of copy_runs_wt, for the dispatch's row units: each a's B
+// runs are one contiguous destination range (db == run) at dst + a*da (another
+// slice for every a, so each round takes its own descriptor), and the source
+// holds them at src + a*sa + b*sb.  Rounds walk the destination range; the
+// source offset is workgroup-uniform for runs of whole rounds, else tracked per
+// lane as copy_runs_wt tracks its destination.
+template <int V, int U, typename Mid>
+__device__ __forceinline__ void copy_runs_inv_wt(const uint8_t* __restrict__ src, uint8_t* dst,
+                                                 const RowPlan& p, Mid&& mid) {
+    using T = typename Vec<V>::T;
+    constexpr int kChunk = kThreads * V;
+    const uint32_t R = (uint32_t)p.run;
+    const bool whole = R % kChunk == 0;
+    const int m = whole ? (int)(R / kChunk) : 1;
+    const int64_t len = (int64_t)p.B * R;            // bytes per a (its destination range)
+    const int nq = (int)(len / kChunk);
+    const uint32_t remb = (uint32_t)(len - (int64_t)nq * kChunk);
+    const uint32_t lane = threadIdx.x * V;
+    const uint32_t sb = (uint32_t)p.sb, sa = (uint32_t)p.sa;
+    const uint32_t col0 = whole ? lane : lane % R;
+    const uint32_t lane_src = whole ? lane : (lane / R) * sb + col0;
+    const uint32_t sc = whole ? 0u : (uint32_t)kChunk % R;
+    const uint32_t step = whole ? 0u : ((uint32_t)kChunk / R) * sb + sc;
+    const uint32_t next_run = sb - (uint32_t)(m - 1) * kChunk;
+    const uint32_t next_a = sa - ((uint32_t)(p.B - 1) * sb + (uint32_t)(m - 1) * kChunk);
+    const uint32_t span = (uint32_t)len;
+    const int total = p.A * nq;
+    int q = 0, c = 0, a0 = 0;
+    uint32_t sof = lane_src, abase = 0, col = col0;
+    auto advance = [&](auto whole_c) {
+        constexpr bool WHOLE = decltype(whole_c)::value;
+        const bool end_a = q + 1 == nq;
+        if (WHOLE) {
+            const bool end_run = c + 1 == m;
+            sof += end_a ? next_a : (end_run ? next_run : (uint32_t)kChunk);
+            c = end_run ? 0 : c + 1;
+        } else {
+            col += sc;
+            sof += step;
+            const bool wrap = col >= R;
+            col = wrap ? col - R : col;
+            sof = wrap ? sof + (sb - R) : sof;
+            col = end_a ? col0 : col;
+            sof = end_a ? lane_src : sof;
+            abase = end_a ? abase + sa : abase;
+        }
+        a0 = end_a ? a0 + 1 : a0;
+        q = end_a ? 0 : q + 1;
+    };
+    bool mid_done = false;
+    int f = 0;
+    auto group = [&](auto kc, auto whole_c) {
+        constexpr int K = decltype(kc)::value;
+        if (!mid_done && 2 * f >= total) {
+            mid();
+            mid_done = true;
+        }
+        uint32_t s_off[K], d_off[K];
+        int a_u[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            s_off[u] = abase + sof;
+            d_off[u] = (uint32_t)q * kChunk + lane;
+            a_u[u] = a0;
+            advance(whole_c);
+        }
+        T v[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u) v[u] = load_nt(reinterpret_cast<const T*>(src + s_off[u]));
+#pragma unroll
+        for (int u = 0; u < K; ++u)
+            BufStore<V, kPolicyDevNt>::go(v[u], make_rsrc_uniform(dst + (int64_t)a_u[u] * p.da, span),
+                                          d_off[u]);
+        f += K;
+    };
+    auto rounds = [&](auto whole_c) {
+        while (f + U <= total) group(std::integral_constant<int, U>{}, whole_c);
+        if (U >= 4 && f + U / 2 <= total)
+            group(std::integral_constant<int, (U >= 4 ? U / 2 : 1)>{}, whole_c);
+        while (f < total) group(std::integral_constant<int, 1>{}, whole_c);
+    };
+    if (whole)
+        rounds(std::true_type{});
+    else
+        rounds(std::false_type{});
+    if (!mid_done) mid();
+    // the partial rounds, one per a: bytes nq*kChunk + lane of each destination range
+    if (remb > 0 && lane < remb) {
+        const uint32_t o = (uint32_t)nq * kChunk + lane;
+        const uint32_t ri = o / R;
+        const uint32_t s_part = ri * sb + (o - ri * R);
+        for (int a1 = 0; a1 < p.A; ++a1) {
+            const T v = load_nt(reinterpret_cast<const T*>(src + (uint32_t)a1 * sa + s_part));
+            BufStore<V, kPolicyDevNt>::go(v, make_rsrc_uniform(dst + (int64_t)a1 * p.da, span), o);
+        }
+    }
+}
+
 // The same, reading the source through a buffer descriptor with cache policy
 // POLICY at 32-bit offsets src_off + (plan offset).
 template <int V, int U, int POLICY, bool NTS>
@@ -703,7 +801,9 @@ __device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
     for (int64_t u = (int)blockIdx.x - nz; u < a.nunits;) {
         claim_ahead(a, cl, published);
         const RowUnit q = row_unit(a, u);
-        const __amdgpu_buffer_rsrc_t dst = make_rsrc_uniform(a.base + q.dst, plan_span(q.pl));
+        // (the combine's destination: one slice, one descriptor)
+        const __amdgpu_buffer_rsrc_t dst =
+            make_rsrc_uniform(a.base + q.dst, a.inverse ? 0u : plan_span(q.pl));
         // Until the reset is known to be published, lane k < nz of wave 0 reads
         // reset flag k during the copy; the check after it then has nothing left
         // to wait for unless that read came too early.
@@ -711,7 +811,12 @@ __device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
         auto poll = [&]() {
             if (!published && (int)threadIdx.x < nz) early = sig_load(reset_flag(a, (int)threadIdx.x));
         };
-        if (run_shape_ok(q.pl)) {
+        if (a.inverse) {
+            if (a.ru == 4)
+                copy_runs_inv_wt<V, 4>(a.base + q.src, a.base + q.dst, q.pl, poll);
+            else
+                copy_runs_inv_wt<V, 8>(a.base + q.src, a.base + q.dst, q.pl, poll);
+        } else if (run_shape_ok(q.pl)) {
             if (a.ru == 4)
                 copy_runs_wt<V, 4>(a.base + q.src, dst, q.pl, poll);
             else
@@ -731,19 +836,25 @@ __device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
         // all of them have stored their rows) and counts itself, with nothing to
         // wait for.  Otherwise the unit that completes the count signals for all.
         const uint64_t share = add && a.W % q.nub == 0 ? (uint64_t)(a.W / q.nub) : 0ull;
+        // (the dispatch signals every destination's slice: nd = W, one slice apart)
+        const int nall = q.nd * q.nsig;
+        auto signal_all = [&](uint64_t v, int sop) {
+            for (int i = threadIdx.x; i < nall; i += 64) {
+                const int d = i / q.nsig, k = i - d * q.nsig;
+                sig_update(reinterpret_cast<uint64_t*>(a.base + q.sig + (int64_t)d * a.stride +
+                                                       (int64_t)k * q.sig_step),
+                           v, sop);
+            }
+            for (int d = 0; d < q.nd; ++d)
+                stamp_tiles(a, q.nd == 1 ? q.j : d, q.unit_index, q.unit_step, q.nsig);
+        };
         if (share != 0ull) {
             if (threadIdx.x < 64) {
                 if (threadIdx.x == 0) sig_update(reinterpret_cast<uint64_t*>(a.base + q.cnt), 1ull, kSigAdd);
-                for (int k = threadIdx.x; k < q.nsig; k += 64)
-                    sig_update(reinterpret_cast<uint64_t*>(a.base + q.sig) + (int64_t)k * kSigStrideU64,
-                               share, kSigAdd);
-                stamp_tiles(a, q.j, q.unit_index, 1, q.nsig);
+                signal_all(share, kSigAdd);
             }
         } else if (arrive(a, q.cnt, (uint64_t)q.nub, lds_flag) && threadIdx.x < 64) {
-            for (int k = threadIdx.x; k < q.nsig; k += 64)
-                sig_update(reinterpret_cast<uint64_t*>(a.base + q.sig) + (int64_t)k * kSigStrideU64,
-                           val, op);
-            stamp_tiles(a, q.j, q.unit_index, 1, q.nsig);
+            signal_all(val, op);
         }
         u = next_piece(a, cl, u, &lds_next);
     }

@@ -100,12 +100,15 @@ def test_signal_slots_and_workspace():
     p = ra2a.rev_all2all_plan(8, 256, 32, 128, "bf16")
     assert (p.mode, p.unit_rows, p.work_items) == (ra2a.MODE_ROWS, 8, 4 * 8 * 8)
     # runs above 8 KiB, runs that neither divide nor are a multiple of 4 KiB (3 and
-    # 6 KiB), the dispatch, a delayed straggler source: per-source pieces
+    # 6 KiB), a delayed straggler source: per-source pieces; the dispatch follows
+    # the same run rule
     assert ra2a.rev_all2all_plan(8, 256, 1, 7168, "bf16").mode == ra2a.MODE_DIRECT
     assert ra2a.rev_all2all_plan(8, 512, 16, 96, "bf16").mode == ra2a.MODE_DIRECT
     assert ra2a.rev_all2all_plan(8, 512, 24, 128, "bf16").mode == ra2a.MODE_DIRECT
     assert ra2a.rev_all2all_plan(8, 512, 4, 64, "bf16").mode == ra2a.MODE_ROWS  # 512 B runs
     assert ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16",
+                                 ra2a.Opts(direction=ra2a.DIR_DISPATCH)).mode == ra2a.MODE_ROWS
+    assert ra2a.rev_all2all_plan(8, 256, 1, 7168, "bf16",
                                  ra2a.Opts(direction=ra2a.DIR_DISPATCH)).mode == ra2a.MODE_DIRECT
     assert ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16",
                                  ra2a.Opts(straggler_rank=2, straggler_delay=100)).mode == ra2a.MODE_DIRECT
@@ -243,10 +246,16 @@ def test_opts_layout_matches_the_header(tmp_path):
 
 
 def test_dispatch_signal_slots():
-    """One slot per (signal tile, source) in every slice.  The dispatch merges all 16
-    heads into 4 KiB runs, so a piece (64 tokens) is 256 KiB and moves as two parts
-    of 32 tokens: one arrival counter per (S-block, source) in region B."""
+    """One slot per (signal tile, source) in every slice.  By default the dispatch
+    runs row units here (4 KiB runs): one arrival counter per S-block of the
+    slice's own rows in region B.  With per-source pieces it merges all 16 heads
+    into 4 KiB runs, so a piece (64 tokens) is 256 KiB and moves as two parts of
+    32 tokens: one arrival counter per (S-block, source) in region B."""
     o = ra2a.Opts(direction=ra2a.DIR_DISPATCH)
+    assert ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", o) == (
+        8 * 16 * 8, 8, ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS)
+    assert ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16", o).mode == ra2a.MODE_ROWS
+    o = ra2a.Opts(direction=ra2a.DIR_DISPATCH, mode=ra2a.MODE_DIRECT)
     assert ra2a.rev_all2all_signal_slots(8, 512, 16, 128, "bf16", o) == (
         8 * 16 * 8, 8 * 8, ra2a.QUEUE_SLOTS + ra2a.RESET_FLAGS)
     p = ra2a.rev_all2all_plan(8, 512, 16, 128, "bf16", o)

@@ -130,11 +130,11 @@ def test_emulated_row_units(unit_rows, W, S, H, D, dtype, tile, proto):
     check_emulation(W, S, H, D, dtype, opts, 1, seed=5)
 
 
-def test_row_units_rejected_for_dispatch_and_straggler():
-    with pytest.raises(ra2a.Ra2aError) as e:
-        ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16",
-                                      ra2a.Opts(mode=ra2a.MODE_ROWS, direction=ra2a.DIR_DISPATCH))
-    assert e.value.code == ra2a.EINVAL
+def test_row_units_rejected_for_straggler():
+    # row units serve the dispatch too; a delayed straggler source needs pieces
+    p = ra2a.rev_all2all_plan(4, 64, 2, 64, "bf16",
+                              ra2a.Opts(mode=ra2a.MODE_ROWS, direction=ra2a.DIR_DISPATCH))
+    assert p.mode == ra2a.MODE_ROWS
     with pytest.raises(ra2a.Ra2aError) as e:
         ra2a.rev_all2all_signal_slots(4, 64, 2, 64, "bf16",
                                       ra2a.Opts(mode=ra2a.MODE_ROWS, straggler_rank=1,
@@ -193,6 +193,28 @@ def test_emulated_dispatch_matches_oracle(W, S, H, D, dtype, tile, head_merge):
     n_a = W * -(-S // tile[0]) * -(-H // tile[1]) * -(-D // tile[2])
     assert (exp[:n_a] == 1).all()
     assert len(exp) == n_a + ra2a.rev_all2all_signal_slots(W, S, H, D, dtype, opts)[1]
+    for r in range(W):
+        assert outs[r].tobytes() == want[r].tobytes(), f"rank {r}"
+        np.testing.assert_array_equal(sigs[r][:len(exp)].astype(np.int64), exp)
+        assert not sigs[r][len(exp):].any()
+
+
+@pytest.mark.parametrize("W,S,H,D,dtype,tile", DISPATCH_CASES)
+@pytest.mark.parametrize("unit_rows", [0, 1, 3, 5])
+def test_emulated_dispatch_row_units(W, S, H, D, dtype, tile, unit_rows):
+    """Dispatch row units (source j's rows, every destination's run): the
+    oracle's bytes, every (tile, source) signal at 1 in every destination's
+    slice, every S-block counter at its unit count."""
+    opts = ra2a.Opts(tile_s=tile[0], tile_h=tile[1], tile_d=tile[2], unit_rows=unit_rows,
+                     mode=ra2a.MODE_ROWS, direction=ra2a.DIR_DISPATCH)
+    assert ra2a.rev_all2all_plan(W, S, H, D, dtype, opts).mode == ra2a.MODE_ROWS
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=S + 5 * W + unit_rows, tile=tile)
+    ins = [x.reshape(S, H * W, D) for x in synthgen.make_inputs(wl)]
+    outs, sigs = ra2a.debug_emulate_pipelined(ins, W, S, H, D, dtype, opts)
+    want = oracle.dispatch(ins)
+    exp = expected_signal_array(W, S, H, D, opts, 1, dtype)
+    n_a = W * -(-S // tile[0]) * -(-H // tile[1]) * -(-D // tile[2])
+    assert (exp[:n_a] == 1).all() and len(exp) == n_a + -(-S // tile[0])
     for r in range(W):
         assert outs[r].tobytes() == want[r].tobytes(), f"rank {r}"
         np.testing.assert_array_equal(sigs[r][:len(exp)].astype(np.int64), exp)

@@ -62,14 +62,28 @@ def test_small_dispatch(W, S, H, D, dtype, tile, knobs):
     run_dispatch(wl, opts_for(wl, direction=ra2a.DIR_DISPATCH, **knobs))
 
 
+@pytest.mark.parametrize("W,S,H,D,dtype,tile", SMALL)
+@pytest.mark.parametrize("unit_rows", [1, 3, 0])
+def test_small_dispatch_row_units(W, S, H, D, dtype, tile, unit_rows):
+    """Row units for the dispatch (source j's rows read whole, every destination's
+    run written as one contiguous range), on every run shape of SMALL."""
+    wl = synthgen.small_workload(W, S, H, D, dtype, seed=W * 100 + S + 19 + unit_rows, tile=tile)
+    run_dispatch(wl, opts_for(wl, direction=ra2a.DIR_DISPATCH, mode=ra2a.MODE_ROWS,
+                              unit_rows=unit_rows))
+
+
 def test_dispatch_clears_dirty_signals():
     wl = synthgen.small_workload(8, 96, 4, 64, "bf16", seed=17, tile=(16, 1, 64))
     run_dispatch(wl, opts_for(wl, direction=ra2a.DIR_DISPATCH), fill_signals=0x5A)
 
 
-def test_full_ep_combine_shape_dispatch():
+@pytest.mark.parametrize("mode", [0, ra2a.MODE_DIRECT])
+def test_full_ep_combine_shape_dispatch(mode):
     wl = synthgen.WORKLOADS["ep_combine_w8_s512_h16_d128_bf16"]
-    run_dispatch(wl, opts_for(wl, direction=ra2a.DIR_DISPATCH))
+    opts = opts_for(wl, direction=ra2a.DIR_DISPATCH, mode=mode)
+    if mode == 0:  # the default on this shape: row units
+        assert ra2a.rev_all2all_plan(wl.W, wl.S, wl.H, wl.D, wl.dtype, opts).mode == ra2a.MODE_ROWS
+    run_dispatch(wl, opts)
 
 
 @pytest.mark.parametrize("name", ["ep_combine_w8_s512_h16_d128_bf16",
