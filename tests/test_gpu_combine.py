@@ -335,6 +335,26 @@ def test_straggler_timestamps(mode):
     assert t[:, :, lag].mean() > t[:, :, others].mean(), (t[:, :, lag].mean(), t[:, :, others].mean())
 
 
+@pytest.mark.parametrize("proto", [synthgen.PROTOCOL_ADD, synthgen.PROTOCOL_SET])
+@pytest.mark.parametrize("unit_rows", [4, 3])
+def test_row_units_stamp_every_tile(proto, unit_rows):
+    """Row units with completion stamps: every signal tile is stamped, under ADD
+    with units adding their shares (4 units per S-block, W = 4) or counting to the
+    block's completion (3 units: 16 = 3 + 3 + 3 + 3 + 3 + 1 rows, 6 units), and
+    under SET; garbage left in the stamp array is cleared."""
+    W, S, H, D = 4, 128, 4, 64
+    wl = synthgen.small_workload(W, S, H, D, "f32", seed=23 + unit_rows, tile=(16, 1, 64),
+                                 protocol=proto)
+    opts = opts_for(wl, mode=ra2a.MODE_ROWS, unit_rows=unit_rows)
+    nt = ra2a.rev_all2all_signal_slots(W, S, H, D, "f32", opts)[0]
+    stamps = torch.full((W * nt,), -1, dtype=torch.int64, device="cuda")
+    opts.timestamps = stamps.data_ptr()
+    say(f"[case] row-unit stamps proto={proto} unit_rows={unit_rows}")
+    run_and_check(wl, opts, csplit=1)
+    t = stamps.cpu().numpy().view(np.uint64)
+    assert (t > 0).all() and (t != np.uint64(2**64 - 1)).all(), "a tile was not stamped"
+
+
 @pytest.mark.parametrize("mode", [0, ra2a.MODE_ROWS, ra2a.MODE_STAGED])
 def test_pipelined_equals_two_phase_bitwise(mode):
     """The barrier-synchronised variant as a differential for the signal-pipelined one."""

@@ -72,6 +72,22 @@ def test_small_dispatch_row_units(W, S, H, D, dtype, tile, unit_rows):
                               unit_rows=unit_rows))
 
 
+@pytest.mark.parametrize("mode", [ra2a.MODE_ROWS, ra2a.MODE_DIRECT])
+def test_dispatch_stamps_every_tile(mode):
+    """Completion stamps of the dispatch: every (tile, source) slot of every
+    destination is stamped, row units (stamped by the unit that completes its
+    block, in each destination's row) and pieces alike."""
+    W, S, H, D = 4, 96, 4, 64
+    wl = synthgen.small_workload(W, S, H, D, "bf16", seed=29, tile=(16, 1, 64))
+    opts = opts_for(wl, direction=ra2a.DIR_DISPATCH, mode=mode, unit_rows=5)
+    nt = ra2a.rev_all2all_signal_slots(W, S, H, D, "bf16", opts)[0]
+    stamps = torch.full((W * nt,), -1, dtype=torch.int64, device="cuda")
+    opts.timestamps = stamps.data_ptr()
+    run_dispatch(wl, opts)
+    t = stamps.cpu().numpy().view(np.uint64)
+    assert (t > 0).all() and (t != np.uint64(2**64 - 1)).all(), "a tile was not stamped"
+
+
 def test_dispatch_clears_dirty_signals():
     wl = synthgen.small_workload(8, 96, 4, 64, "bf16", seed=17, tile=(16, 1, 64))
     run_dispatch(wl, opts_for(wl, direction=ra2a.DIR_DISPATCH), fill_signals=0x5A)
