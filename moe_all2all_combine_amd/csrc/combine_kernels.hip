@@ -231,17 +231,18 @@ __device__ __forceinline__ void copy_plan_wt(const uint8_t* __restrict__ src,
 //    advanced by the round's kThreads * V bytes with one wrap test per round.
 // Each a's last, partial round (B*run not a multiple of the round) moves in a
 // second pass, by the lanes whose bytes it holds.  Round offsets advance with
-// selects, not branches, so that a group's loads issue back to back.  `mid()`
-// runs once, about half-way (before the first group past the middle), so that
-// what it issues completes under the rest of the copy.
+// selects, not branches, so that a group's loads issue back to back.  `late()`
+// runs once, right after the loads of the last round group: a load it issues
+// (a read of the reset flags) is younger than every copy load, so no store of
+// the copy waits for it, and it completes under the last stores.
 __device__ __forceinline__ bool run_shape_ok(const RowPlan& p) {
     return p.C == 1 && p.sb == p.run && p.run > 0;
 }
 
-template <int V, int U, typename Mid>
+template <int V, int U, typename Late>
 __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
                                              __amdgpu_buffer_rsrc_t dst, const RowPlan& p,
-                                             Mid&& mid) {
+                                             Late&& late) {
     using T = typename Vec<V>::T;
     constexpr int kChunk = kThreads * V;
     const uint32_t R = (uint32_t)p.run;
@@ -290,14 +291,9 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
         }
         q = end_a ? 0 : q + 1;
     };
-    bool mid_done = false;
     int f = 0;
     auto group = [&](auto kc, auto whole_c) {
         constexpr int K = decltype(kc)::value;
-        if (!mid_done && 2 * f >= total) {
-            mid();
-            mid_done = true;
-        }
         int64_t sofs[K];
         uint32_t d[K];
 #pragma unroll
@@ -309,6 +305,7 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
         T v[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) v[u] = load_nt(reinterpret_cast<const T*>(s_lane + sofs[u]));
+        if (f + K == total) late();
 #pragma unroll
         for (int u = 0; u < K; ++u) BufStore<V, kPolicyDevNt>::go(v[u], dst, d[u]);
         f += K;
@@ -323,7 +320,7 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
         rounds(std::true_type{});
     else
         rounds(std::false_type{});
-    if (!mid_done) mid();
+    if (total == 0) late();
     // the partial rounds, one per a: bytes nq*kChunk + lane of each a's range
     if (remb > 0 && lane < remb) {
         const uint32_t o = (uint32_t)nq * kChunk + lane;
@@ -353,9 +350,9 @@ __device__ __forceinline__ void copy_runs_wt(const uint8_t* __restrict__ src,
 // holds them at src + a*sa + b*sb.  Rounds walk the destination range; the
 // source offset is workgroup-uniform for runs of whole rounds, else tracked per
 // lane as copy_runs_wt tracks its destination.
-template <int V, int U, typename Mid>
+template <int V, int U, typename Late>
 __device__ __forceinline__ void copy_runs_inv_wt(const uint8_t* __restrict__ src, uint8_t* dst,
-                                                 const RowPlan& p, Mid&& mid) {
+                                                 const RowPlan& p, Late&& late) {
     using T = typename Vec<V>::T;
     constexpr int kChunk = kThreads * V;
     const uint32_t R = (uint32_t)p.run;
@@ -396,14 +393,9 @@ __device__ __forceinline__ void copy_runs_inv_wt(const uint8_t* __restrict__ src
         a0 = end_a ? a0 + 1 : a0;
         q = end_a ? 0 : q + 1;
     };
-    bool mid_done = false;
     int f = 0;
     auto group = [&](auto kc, auto whole_c) {
         constexpr int K = decltype(kc)::value;
-        if (!mid_done && 2 * f >= total) {
-            mid();
-            mid_done = true;
-        }
         uint32_t s_off[K], d_off[K];
         int a_u[K];
 #pragma unroll
@@ -416,6 +408,7 @@ __device__ __forceinline__ void copy_runs_inv_wt(const uint8_t* __restrict__ src
         T v[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) v[u] = load_nt(reinterpret_cast<const T*>(src + s_off[u]));
+        if (f + K == total) late();
 #pragma unroll
         for (int u = 0; u < K; ++u)
             BufStore<V, kPolicyDevNt>::go(v[u], make_rsrc_uniform(dst + (int64_t)a_u[u] * p.da, span),
@@ -432,7 +425,7 @@ __device__ __forceinline__ void copy_runs_inv_wt(const uint8_t* __restrict__ src
         rounds(std::true_type{});
     else
         rounds(std::false_type{});
-    if (!mid_done) mid();
+    if (total == 0) late();
     // the partial rounds, one per a: bytes nq*kChunk + lane of each destination range
     if (remb > 0 && lane < remb) {
         const uint32_t o = (uint32_t)nq * kChunk + lane;
@@ -805,8 +798,10 @@ __device__ __forceinline__ void rows_path(const PipeArgs& a, int* lds_flag) {
         const __amdgpu_buffer_rsrc_t dst =
             make_rsrc_uniform(a.base + q.dst, a.inverse ? 0u : plan_span(q.pl));
         // Until the reset is known to be published, lane k < nz of wave 0 reads
-        // reset flag k during the copy; the check after it then has nothing left
-        // to wait for unless that read came too early.
+        // reset flag k at the end of the copy, behind its last loads (a read in
+        // the middle held up the next round's stores, which wait in order behind
+        // it); the check after the drain then has nothing left to wait for unless
+        // that read came too early.
         uint64_t early = 0ull;
         auto poll = [&]() {
             if (!published && (int)threadIdx.x < nz) early = sig_load(reset_flag(a, (int)threadIdx.x));
