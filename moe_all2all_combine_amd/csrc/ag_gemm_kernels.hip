@@ -176,9 +176,11 @@ __device__ __forceinline__ void mma_one(f32x4 (&acc)[8][4], const Frags& f) {
 }
 
 // A k32 step: its 32 MFMAs with the other work of the step between them -- the 12
-// fragment reads of the next step on every second of the first 24 MFMAs (they land
-// well before the step ends), and, in the second step of a stage, the 8 loads
-// refilling the slot just freed on every second of the last 16.
+// fragment reads of the next step after MFMAs 1, 3, .., 23 (they land well before
+// the step ends), and, in the second step of a stage, the 8 loads refilling the
+// slot just freed after MFMAs 0, 2, .., 14: as early as the slot is free, which
+// gives them the most time before the wait for them one step later (1.5-3 %
+// faster than refills on the last 16 MFMAs, same box).
 struct StepCtx {
     Frags* next;
     uint32_t na, nb;                      // the next step's fragment addresses
@@ -193,12 +195,12 @@ struct StepCtx {
 template <bool REFILL, int I, int J>
 __device__ __forceinline__ void step_op(const StepCtx& c) {
     if constexpr (J < kReadsPerStep) {
-        if constexpr (J * 2 == I) {
+        if constexpr (J * 2 + 1 == I) {
             read_frag<J>(*c.next, c.na, c.nb);
             sb();
         }
     } else if constexpr (REFILL) {
-        if constexpr (16 + (J - kReadsPerStep) * 2 == I) {
+        if constexpr ((J - kReadsPerStep) * 2 == I) {
             stage_load_part<J - kReadsPerStep>(c.ra, c.rb, c.slot, c.w, c.K, c.k0, *c.ll, c.live);
             sb();
         }
