@@ -176,11 +176,12 @@ __device__ __forceinline__ void mma_one(f32x4 (&acc)[8][4], const Frags& f) {
 }
 
 // A k32 step: its 32 MFMAs with the other work of the step between them -- the 12
-// fragment reads of the next step after MFMAs 1, 3, .., 23 (they land well before
-// the step ends), and, in the second step of a stage, the 8 loads refilling the
-// slot just freed after MFMAs 0, 2, .., 14: as early as the slot is free, which
-// gives them the most time before the wait for them one step later (1.5-3 %
-// faster than refills on the last 16 MFMAs, same box).
+// fragment reads of the next step after MFMAs 0 .. 11 (they land well before the
+// step ends), and, in the second step of a stage, the 8 loads refilling the slot
+// just freed after MFMAs 0, 2, .., 14: as early as the slot is free, which gives
+// them the most time before the wait for them one step later (1.5-3 % faster than
+// refills on the last 16 MFMAs, same box; the reads on MFMAs 0 .. 11 rather than
+// on every second MFMA, another 0.5-1 %).
 struct StepCtx {
     Frags* next;
     uint32_t na, nb;                      // the next step's fragment addresses
@@ -195,7 +196,7 @@ struct StepCtx {
 template <bool REFILL, int I, int J>
 __device__ __forceinline__ void step_op(const StepCtx& c) {
     if constexpr (J < kReadsPerStep) {
-        if constexpr (J * 2 + 1 == I) {
+        if constexpr (J == I) {
             read_frag<J>(*c.next, c.na, c.nb);
             sb();
         }
