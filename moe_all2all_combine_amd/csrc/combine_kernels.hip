@@ -148,10 +148,19 @@ __device__ __forceinline__ void copy_plan(const uint8_t* __restrict__ src, uint8
 // plan offsets): how the direct modes write out_j, so that a drain publishes
 // the data device-wide (device.h).  Loads are non-temporal (the input is read
 // once).
-template <int V, int U>
+//
+// `early(n)` runs once: right after the first full round's loads, with n = U of
+// them the youngest memory operations in flight, or with n = 0 before the
+// remainder when there is no full round.
+struct NoEarly {
+    template <class N>
+    __device__ __forceinline__ void operator()(N) const {}
+};
+
+template <int V, int U, class Early = NoEarly>
 __device__ __forceinline__ void copy_plan_wt(const uint8_t* __restrict__ src,
                                              __amdgpu_buffer_rsrc_t dst, const RowPlan& p, int lo,
-                                             int hi) {
+                                             int hi, Early&& early = Early{}) {
     using T = typename Vec<V>::T;
     constexpr int kRound = U * kThreads;
     const int vpr = p.run / V;
@@ -171,11 +180,13 @@ __device__ __forceinline__ void copy_plan_wt(const uint8_t* __restrict__ src,
             T v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) v[u] = get(s0 + u * ds);
+            if (k == 0) early(std::integral_constant<int, U>{});
 #pragma unroll
             for (int u = 0; u < U; ++u) put(v[u], d0 + (uint32_t)u * dd);
             s0 += U * ds;
             d0 += (uint32_t)U * dd;
         }
+        if (nfull == 0) early(std::integral_constant<int, 0>{});
         idx += nfull * kRound;
         if (idx < hi) {
             T v[U];
@@ -198,9 +209,11 @@ __device__ __forceinline__ void copy_plan_wt(const uint8_t* __restrict__ src,
             doff[u] = (uint32_t)c.dofs;
             cursor_advance(c, p, vpr);
         }
+        if (k == 0) early(std::integral_constant<int, U>{});
 #pragma unroll
         for (int u = 0; u < U; ++u) put(v[u], doff[u]);
     }
+    if (nfull == 0) early(std::integral_constant<int, 0>{});
     idx += nfull * kRound;
     if (idx < hi) {
         T v[U];
@@ -719,7 +732,8 @@ __device__ __forceinline__ bool arrive(const PipeArgs& a, int64_t cnt, uint64_t 
 // source under SET) and the piece that completes it signals as all W (or the
 // source's) pieces would have: ADD W, or SET 1.  Stores are device-scope
 // write-through (copy_plan_wt), so a drain and a barrier publish them on every
-// XCD before the signal or the count; the piece that reads the counter's last
+// XCD before the signal or the count (the drain of one piece's stores is the wait
+// for the next piece's first loads); the piece that reads the counter's last
 // arrival follows every other piece's drained stores.  The optional completion
 // stamp of a tile is the latest of its signalling pieces' stamps.  The only
 // wait is for the in-launch reset's flags.  The reset runs on the reset_nz
@@ -739,30 +753,68 @@ __device__ __forceinline__ void direct_path(const PipeArgs& a, int* lds_flag) {
     const int64_t total = total_pieces(a);
     const int op = a.protocol == kSigAdd ? kSigAdd : kSigSet;
     const uint64_t done_val = a.protocol == kSigAdd ? (uint64_t)a.W : 1ull;
+    const int64_t step = slot_step(a);
     Claimer cl = claimer(a);
+    // The piece whose stores are issued but not yet published (`pend`): its signal,
+    // or its arrival, goes out once those stores have drained -- right after the
+    // next piece's first loads, whose wait then covers them (vector memory
+    // operations complete in issue order), or at the end.  So no workgroup sits in a
+    // drain between two pieces with nothing in flight.
+    bool pend = false;
+    Piece q{};
+    // wave 0, once every wave's stores of q have drained
+    auto publish = [&]() {
+        if (a.nsub == 1) {
+            piece_signal(a, q.sig, q.sig_step, q.nsig);
+            stamp_tiles(a, q.j, q.unit_index, step, q.nsig);
+        } else if (threadIdx.x < 64) {
+            uint64_t before = 0ull;
+            if (threadIdx.x == 0)
+                before = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(a.base + q.cnt), 1ull,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)before);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(before >> 32));
+            if ((((uint64_t)hi << 32) | lo) + 1ull == q.cnt_need) {
+                for (int k = threadIdx.x; k < q.nsig; k += 64)
+                    sig_update(reinterpret_cast<uint64_t*>(a.base + q.sig + k * q.sig_step), done_val, op);
+                stamp_tiles(a, q.j, q.unit_index, step, q.nsig);
+            }
+        }
+    };
     for (int64_t gp = (int)blockIdx.x - nz; gp < total;) {
         claim_ahead(a, cl, published);
         const Piece p = direct_piece(a, gp);
+        // a delayed (straggler) piece waits before its copy: publish the pending
+        // piece first, so that its tiles are not held up by the delay
+        if (pend && p.r == a.straggler && a.delay) {
+            group_release_written_through();
+            publish();
+            pend = false;
+        }
         if (!piece_wait(a, p, lds_flag)) return;
-        // final place: device-scope write-through stores, so the drain publishes them
+        auto early = [&](auto n) {
+            if (pend) {
+                asm volatile("s_waitcnt vmcnt(%0)" ::"i"(decltype(n)::value) : "memory");
+                __syncthreads();  // every wave's stores of q have drained
+                publish();
+                pend = false;
+            }
+        };
+        // final place: device-scope write-through stores, so a drain publishes them
         copy_plan_wt<V, 8>(a.base + p.src, make_rsrc_uniform(a.base + p.dst, plan_span(p.pl)), p.pl,
-                           0, plan_vectors(p.pl, V));
-        group_release_written_through();
-        if (!published) {
+                           0, plan_vectors(p.pl, V), early);
+        if (!published) {  // before any signal (the first is the next piece's)
             if (!reset_published(a)) return;
             published = true;
             claim_ahead(a, cl, published);
         }
-        const int64_t step = slot_step(a);
-        if (a.nsub == 1) {
-            piece_signal(a, p.sig, p.sig_step, p.nsig);
-            stamp_tiles(a, p.j, p.unit_index, step, p.nsig);
-        } else if (arrive(a, p.cnt, p.cnt_need, lds_flag) && threadIdx.x < 64) {
-            for (int k = threadIdx.x; k < p.nsig; k += 64)
-                sig_update(reinterpret_cast<uint64_t*>(a.base + p.sig + k * p.sig_step), done_val, op);
-            stamp_tiles(a, p.j, p.unit_index, step, p.nsig);
-        }
+        q = p;
+        pend = true;
         gp = next_piece(a, cl, gp, &lds_next);
+    }
+    if (pend) {
+        group_release_written_through();
+        publish();
     }
 }
 
